@@ -1,0 +1,21 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an AMD MI355X (gfx950) GPU and the HIP library")
+
+
+@pytest.fixture(scope="session")
+def orc():
+    """The fp64 CPU oracle (built on demand if liboracle.so is missing)."""
+    import oracle
+
+    oracle.lib()
+    return oracle

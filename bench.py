@@ -1,0 +1,383 @@
+"""Benchmark of the particle-to-grid deposition hot path on one MI355X.
+
+Default (the headline): 3-D CIC current deposit on a 128^3 periodic grid with
+32 particles per cell (67,108,864 particles), tile edge 8, drift 1, 2% of the
+particles pushed 2-4 cells so the escape valve runs.  One "step" is one pass of
+the whole path over that batch, as a PIC step runs it:
+    zero J; deposit_currents(pushed particles, previous layout) -> J;
+    pcg_tile_sort(pushed particles) -> new layout + permuted SoA arrays.
+Inputs are resident in HBM before timing starts; W warm-up steps, then K timed
+steps between a device synchronisation on each side (HIP events on the
+library's stream).  Per-kernel durations come from the library's event tap
+(events recorded around every launch, on the launch stream) during the same
+timed steps.
+
+Other workloads (--config): 2 (2-D CIC 512^2), 4 (3-D TSC clustered, T from
+--tile), 5 (ECSIM mass matrix 64^3: cell sort + MFMA assembly), 1 (1-D sweep).
+
+Prints ONE JSON line (rank 0).  Only one GPU is used: --gpus above 1 exits.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
+
+METRIC = "deposited particles/s (3D CIC 128^3, 32 ppc) + % of HBM roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--tile", type=int, default=0, help="tile edge T (0 = the workload's)")
+    ap.add_argument("--block", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--no-flat", action="store_true", help="skip the flat-path comparison")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------- helpers
+
+def kernel_times(pcg, names):
+    out = {}
+    for nm in names:
+        ms, n = pcg.pcg_timing_read(nm)
+        if n:
+            out[nm] = dict(total_ms=ms, launches=n, avg_us=1000.0 * ms / n)
+    return out
+
+
+def time_steps(torch, pcg, step, steps, warmup):
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    pcg.pcg_timing_reset()
+    pcg.pcg_timing_enable(True)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pcg.pcg_timing_enable(False)
+    ms = ev0.elapsed_time(ev1) / steps
+    kt = kernel_times(pcg, pcg.pcg_timing_names())
+    return ms, wall, kt
+
+
+def time_plain(torch, fn, reps):
+    """Average ms of fn over reps (events on the current stream, after one warm-up)."""
+    fn()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        fn()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / reps
+
+
+def roofline_entry(kt, name, bytes_per_launch=None, flops_per_launch=None):
+    k = kt.get(name)
+    if not k:
+        return None
+    sec = k["avg_us"] * 1e-6
+    if flops_per_launch is not None:
+        achieved = flops_per_launch / sec / 1e12
+        return dict(bound="mfma", achieved=round(achieved, 3), peak=MFMA_FP32_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=round(achieved / MFMA_FP32_PEAK_TFLOPS, 4),
+                    traffic=None, kernel=name, avg_us=round(k["avg_us"], 2))
+    achieved = bytes_per_launch / sec / 1e9
+    return dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None, kernel=name,
+                avg_us=round(k["avg_us"], 2))
+
+
+def cpu_baseline_deposit(wl, order, T, target_s):
+    """The fp64 oracle as it stands (single thread) on a bounded prefix sample of
+    the same particles: its tile sort (keys + stable counting sort) and deposit."""
+    import numpy as np
+
+    import oracle
+
+    def run(m):
+        x = [a[:m] for a in wl.x_next]
+        t0 = time.perf_counter()
+        oracle.tile_sort(wl.dim, wl.n, order, T, x)
+        oracle.deposit(wl.dim, wl.n, order, x, [v[:m] for v in wl.v], wl.q[:m], wl.w[:m])
+        return time.perf_counter() - t0
+
+    cal = min(wl.count, 1 << 20)
+    per = run(cal) / cal
+    m = int(min(wl.count, max(cal, target_s / per)))
+    sec = run(m)
+    return dict(value=round(m / sec, 1), unit="particles/s", cores=1, kind="oracle",
+                sample=f"first {m} of {wl.count} particles of the step input: oracle tile sort "
+                       f"(keys + stable counting sort) + fp64 deposit, {sec:.1f} s, 1 thread")
+
+
+# ----------------------------------------------------------------- deposit family
+
+def bench_deposit(args, torch, pcg, k):
+    import numpy as np
+
+    import synthetic
+
+    info = synthetic.CONFIG_INFO[k]
+    order = info["order"]
+    T = args.tile or (info.get("T") or 8)
+    D = info["D"]
+    wl = synthetic.config(k)
+    n, dim, cnt = wl.n, wl.dim, wl.count
+    dev = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    # previous step's state: sorted on x, pushed to x_next (library sort, untimed)
+    x0 = [t(a) for a in wl.x]
+    arrays = [t(a) for a in wl.x_next] + [t(a) for a in wl.v] + [t(wl.q), t(wl.w)]
+    _, _, off0, cur = pcg.pcg_tile_sort(dim, n, order, T, x0, arrays)
+    del x0, arrays
+    torch.cuda.synchronize()
+    nt = pcg.ntiles(dim, n, T)
+    J = torch.zeros(3, n[2], n[1], n[0], dtype=torch.float32, device=dev)
+    esc = torch.zeros(1, dtype=torch.int64, device=dev)
+    lay = pcg.Layout(T=T, order=order, tile_offsets=off0, n_partitioned=cnt, drift=D,
+                     block=args.block)
+    dws = torch.empty(max(pcg.pcg_deposit_workspace_bytes(dim, n, lay), 256), dtype=torch.uint8,
+                      device=dev)
+    # sort outputs (the next step's state), preallocated
+    perm = torch.empty(cnt, dtype=torch.int32, device=dev)
+    keys = torch.empty(cnt, dtype=torch.int32, device=dev)
+    off1 = torch.empty(nt + 1, dtype=torch.int32, device=dev)
+    nxt = [torch.empty_like(a) for a in cur]
+    sws = torch.empty(pcg.pcg_sort_workspace_bytes(dim, n, cnt, T), dtype=torch.uint8, device=dev)
+    xs, vs, q, w = cur[:dim], cur[dim:dim + 3], cur[dim + 3], cur[dim + 4]
+
+    def deposit():
+        pcg.deposit_currents(dim, n, order, xs, vs, q, w, J, lay, esc, dws)
+
+    def step():
+        J.zero_()
+        deposit()
+        pcg.pcg_tile_sort(dim, n, order, T, xs, cur, outs=nxt, perm=perm, sorted_keys=keys,
+                          tile_offsets=off1, workspace=sws)
+
+    ms, wall, kt = time_steps(torch, pcg, step, args.steps, args.warmup)
+    # escape count of one deposit of this input
+    esc.zero_()
+    deposit()
+    torch.cuda.synchronize()
+    n_esc = int(esc.item())
+
+    # algorithmic bytes per launch (SoA fp32 fields the kernel must move)
+    jbytes = 3 * n[0] * n[1] * n[2] * 4
+    pbytes = (dim + 5) * 4
+    alg = {
+        "deposit_tiled": cnt * pbytes + 2 * jbytes,
+        "sort_keys": cnt * (dim * 4 + 4),
+        "sort_permute": cnt * (4 + 2 * (dim + 5) * 4),
+        "sort_offsets": cnt * 4 + (nt + 1) * 4,
+    }
+    kernels = {}
+    for nm, kk in kt.items():
+        e = dict(avg_us=round(kk["avg_us"], 2), launches_per_step=kk["launches"] / args.steps)
+        if nm in alg:
+            e["alg_bytes"] = alg[nm]
+            e["GBps"] = round(alg[nm] / (kk["avg_us"] * 1e-6) / 1e9, 1)
+        kernels[nm] = e
+    dominant = max(kt, key=lambda nm: kt[nm]["total_ms"])
+    roof = roofline_entry(kt, "deposit_tiled", bytes_per_launch=alg["deposit_tiled"])
+    roof_dom = (roofline_entry(kt, dominant, bytes_per_launch=alg[dominant])
+                if dominant in alg else None)
+
+    extra = {}
+    dep_ms = time_plain(torch, lambda: (J.zero_(), deposit()), args.steps)
+    extra["deposit_only_particles_per_s"] = round(cnt / (dep_ms * 1e-3), 1)
+    extra["deposit_only_ms"] = round(dep_ms, 4)
+    if not args.no_flat:
+        def flat():
+            J.zero_()
+            pcg.deposit_currents(dim, n, order, xs, vs, q, w, J, None)
+        fl_ms = time_plain(torch, flat, max(3, args.steps // 4))
+        extra["flat_deposit_particles_per_s"] = round(cnt / (fl_ms * 1e-3), 1)
+        extra["tiled_speedup_vs_flat"] = round(fl_ms / dep_ms, 2)
+    sort_ms = time_plain(torch, lambda: pcg.pcg_tile_sort(
+        dim, n, order, T, xs, cur, outs=nxt, perm=perm, sorted_keys=keys, tile_offsets=off1,
+        workspace=sws), args.steps)
+    extra["sort_only_ms"] = round(sort_ms, 4)
+    extra["escaped_particles"] = n_esc
+    extra["deposit_roofline"] = roof
+    extra["dominant_kernel"] = dominant
+    wk = {2: "2-D CIC current deposit + tile sort, 512^2 periodic, 16 ppc",
+          3: "3-D CIC current deposit + tile sort, 128^3 periodic, 32 ppc, 2% pushed 2-4 cells",
+          4: "3-D TSC current deposit + tile sort, 128^3 periodic, clustered (Gaussian blob)"}[k]
+    config = dict(workload=wk, particles=cnt, grid=n[:dim], order=order, tile=T, drift=D,
+                  block=args.block or 256, step="zero J + tiled deposit + tile sort/permute")
+    cpu = None if args.no_cpu_baseline else cpu_baseline_deposit(wl, order, T, args.cpu_seconds)
+    return dict(value=cnt / (ms * 1e-3), ms=ms, wall=wall, dtype="f32", config=config,
+                roofline=roof_dom if roof_dom else roof, kernels=kernels, extra=extra,
+                cpu=cpu, unit="particles/s")
+
+
+# ----------------------------------------------------------------- mass matrix
+
+def bench_mass(args, torch, pcg):
+    import numpy as np
+
+    import synthetic
+
+    wl = synthetic.config(5)
+    n, cnt = wl.n, wl.count
+    dev = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    x = [t(a) for a in wl.x]
+    arrays = x + [t(b) for b in wl.B] + [t(wl.beta), t(wl.q), t(wl.w)]
+    M = torch.zeros(n[2], n[1], n[0], 27, 3, 3, dtype=torch.float32, device=dev)
+    nc = n[0] * n[1] * n[2]
+    perm = torch.empty(cnt, dtype=torch.int32, device=dev)
+    keys = torch.empty(cnt, dtype=torch.int32, device=dev)
+    off = torch.empty(nc + 1, dtype=torch.int32, device=dev)
+    outs = [torch.empty_like(a) for a in arrays]
+    sws = torch.empty(pcg.pcg_sort_workspace_bytes(3, n, cnt, 1), dtype=torch.uint8, device=dev)
+    cells = pcg.Layout(T=1, order=1, tile_offsets=off, n_partitioned=cnt, drift=0)
+
+    def step():
+        M.zero_()
+        pcg.pcg_tile_sort(3, n, 1, 1, x, arrays, outs=outs, perm=perm, sorted_keys=keys,
+                          tile_offsets=off, workspace=sws)
+        pcg.assemble_mass_matrix(n, outs[0:3], outs[3:6], outs[6], outs[7], outs[8], M, cells,
+                                 pcg.PCG_MASS_MFMA)
+
+    ms, wall, kt = time_steps(torch, pcg, step, args.steps, args.warmup)
+    flops = cnt * 1152.0     # dense 8x8 node pairs x 9 components x 2 flops
+    roof = roofline_entry(kt, "mass_mfma", flops_per_launch=flops)
+    mbytes = M.numel() * 4
+    kernels = {nm: dict(avg_us=round(kk["avg_us"], 2),
+                        launches_per_step=kk["launches"] / args.steps) for nm, kk in kt.items()}
+    extra = {}
+    for nm, var in (("valu", pcg.PCG_MASS_VALU), ("mfma", pcg.PCG_MASS_MFMA)):
+        mm = time_plain(torch, lambda: (M.zero_(), pcg.assemble_mass_matrix(
+            n, outs[0:3], outs[3:6], outs[6], outs[7], outs[8], M, cells, var)), 5)
+        extra[f"mass_{nm}_ms"] = round(mm, 4)
+    extra["mfma_speedup_vs_valu"] = round(extra["mass_valu_ms"] / extra["mass_mfma_ms"], 2)
+    if "mass_mfma" in kt:
+        sec = kt["mass_mfma"]["avg_us"] * 1e-6
+        hbm = (cnt * 36 + 2 * mbytes) / sec / 1e9
+        extra["mass_hbm_roofline"] = dict(bound="hbm", achieved=round(hbm, 1), peak=HBM_PEAK_GBS,
+                                          unit="GB/s", frac=round(hbm / HBM_PEAK_GBS, 4))
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        m = 1 << 20
+        t0 = time.perf_counter()
+        oracle.mass_matrix(n, [a[:m] for a in wl.x], [b[:m] for b in wl.B], wl.q[:m], wl.w[:m],
+                           wl.beta[:m])
+        per = (time.perf_counter() - t0) / m
+        m2 = int(min(cnt, max(m, args.cpu_seconds / per)))
+        t0 = time.perf_counter()
+        oracle.mass_matrix(n, [a[:m2] for a in wl.x], [b[:m2] for b in wl.B], wl.q[:m2],
+                           wl.w[:m2], wl.beta[:m2])
+        sec = time.perf_counter() - t0
+        cpu = dict(value=round(m2 / sec, 1), unit="particles/s", cores=1, kind="oracle",
+                   sample=f"first {m2} of {cnt} particles: fp64 per-particle outer products, "
+                          f"{sec:.1f} s, 1 thread")
+    config = dict(workload="ECSIM 3-D CIC mass matrix 64^3, 64 ppc (cell sort + MFMA assembly)",
+                  particles=cnt, grid=n, step="zero M + cell sort/permute + MFMA assembly")
+    return dict(value=cnt / (ms * 1e-3), ms=ms, wall=wall, dtype="f32", config=config,
+                roofline=roof, kernels=kernels, extra=extra, cpu=cpu, unit="particles/s")
+
+
+# ----------------------------------------------------------------- 1-D sweep
+
+def bench_sweep(args, torch, pcg):
+    import numpy as np
+
+    import synthetic
+
+    s = synthetic.config(1)
+    dev = torch.device("cuda:0")
+    x0 = torch.from_numpy(s.x0).to(dev)
+    v = torch.from_numpy(s.v).to(dev)
+    H = torch.empty(s.nb, dtype=torch.float32, device=dev)
+    step = lambda: pcg.deposit_sweep1d(s.nb, x0, v, s.T, s.dt, s.hw, H)
+    ms, wall, kt = time_steps(torch, pcg, step, args.steps, args.warmup)
+    kernels = {nm: dict(avg_us=round(kk["avg_us"], 2)) for nm, kk in kt.items()}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        reps = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 2.0:
+            oracle.sweep1d(s.nb, s.x0, s.v, s.T, s.dt, s.hw)
+            reps += 1
+        sec = (time.perf_counter() - t0) / reps
+        cpu = dict(value=round(s.x0.size * s.T / sec, 1), unit="particle-steps/s", cores=1,
+                   kind="oracle", sample=f"the whole workload, {reps} repetitions")
+    return dict(value=s.x0.size * s.T / (ms * 1e-3), ms=ms, wall=wall, dtype="f64",
+                config=dict(workload="1-D windowed CIC sweep, 2000 particles, 50 steps, 1024 bins"),
+                roofline=None, kernels=kernels, extra={}, cpu=cpu, unit="particle-steps/s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
+              "supported (the multi-GPU split is a design note only)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import particle_cell_grid_amd as pcg
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.config in (2, 3, 4):
+        r = bench_deposit(args, torch, pcg, args.config)
+    elif args.config == 5:
+        r = bench_mass(args, torch, pcg)
+    else:
+        r = bench_sweep(args, torch, pcg)
+    line = {
+        "metric": METRIC if args.config == 3 else f"config {args.config}: {r['unit']}",
+        "value": round(r["value"], 1),
+        "unit": r["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": r["dtype"],
+        "data": "synthetic",
+        "config": r["config"],
+        "roofline": r["roofline"],
+        "cpu_baseline": r["cpu"],
+        "kernels": r["kernels"],
+        "extra": r["extra"],
+        "wall_s_timed": round(r["wall"], 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,217 @@
+/*
+ * pcg.h -- C ABI of the particle-to-grid scatter-deposition library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every array pointer is a DEVICE pointer owned by the caller; the
+ *   library never allocates, frees or retains device memory.  Struct arguments
+ *   and the small pointer arrays that carry device pointers are host memory,
+ *   read during the call only.
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
+ *   stream).  Every call only enqueues work on that stream and returns; results
+ *   are ready once the stream is synchronised.  Calls on different streams that
+ *   write the same output race.
+ * Layouts.  Particles are structure-of-arrays fp32.  Grids are periodic and
+ *   node-centred with unit spacing: node g sits at integer coordinate g and
+ *   cell g spans [g, g+1), so positions are in cell units with
+ *   0 <= x_k < n_k.  Grid arrays are x-fastest (linear node
+ *   g = gx + n_x*(gy + n_y*gz)).  Unused axes of a 1-D or 2-D grid have n_k = 1.
+ * Accumulation.  deposit_currents and assemble_mass_matrix ADD into their
+ *   output (the caller zeroes it); deposit_sweep1d OVERWRITES its output.
+ * Errors.  Every entry point returns a pcg_status.  Arguments are validated on
+ *   the host before anything is enqueued; on failure nothing is launched and
+ *   pcg_last_error() gives a message (per host thread).  A launch failure
+ *   reported by the HIP runtime returns PCG_EHIP.  Positions outside [0, n_k)
+ *   or non-finite break the precondition: the kernels clamp and wrap every
+ *   index so such input cannot make them access memory out of bounds, but the
+ *   values they deposit are then unspecified.
+ *
+ * Sources cited below:
+ *   [TD] Entity wiki, "Tiled current deposit".
+ *   [MM] Pennati & Markidis, "Mass Matrix Assembly on Tensor Cores for Implicit
+ *        Particle-In-Cell Methods" (arXiv:2604.19286).
+ *   [CS] WEANJ examples, "03. Compaction and scatter-add".
+ */
+#ifndef PCG_H
+#define PCG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pcg_status;
+#define PCG_OK 0
+#define PCG_EINVAL (-1)        /* bad argument (null pointer, size, range)      */
+#define PCG_EUNSUPPORTED (-2)  /* valid but not built (dim/order/variant combo) */
+#define PCG_ELDS (-3)          /* scratch tile does not fit the 160 KiB LDS     */
+#define PCG_EWORKSPACE (-4)    /* workspace missing or too small                */
+#define PCG_EHIP (-6)          /* the HIP runtime reported a launch error       */
+
+/* Periodic grid: dim in {1,2,3}; n[k] nodes (= cells) per axis, n[k] = 1 for
+ * k >= dim. */
+typedef struct pcg_grid {
+    int32_t dim;
+    int32_t n[3];
+} pcg_grid;
+
+/* Particles, SoA fp32 device arrays of `count` entries (count < 2^31).
+ * x[k] is used for k < dim (others may be NULL); v[0..2] are always the three
+ * velocity components (unused by assemble_mass_matrix, may be NULL there). */
+typedef struct pcg_particles {
+    int64_t count;
+    const float *x[3];
+    const float *v[3];
+    const float *q;
+    const float *w;
+} pcg_particles;
+
+/* A tile layout ([TD] "How a tile deposit runs", "The tile-based spatial
+ * sort"), as written by pcg_tile_sort.  Tile t owns the particle slice
+ * [tile_offsets[t], tile_offsets[t+1]); particles [n_partitioned, count) are an
+ * unsorted tail handled by the flat kernel ([TD] "Coverage: the tail pass").
+ *   T          tile edge in nodes on every used axis (1 = a cell layout).
+ *   order      shape order the layout was keyed with (1 CIC, 2 TSC).
+ *   drift      halo budget D >= 0 in cells ([TD] "Halo sizing"): the scratch
+ *              tile spans TE = T + order + 2*D nodes per used axis.
+ *   block      work-group size; 0 = automatic, otherwise clamped to [64, 1024]
+ *              and rounded down to a multiple of 64 ([TD] team size knob).
+ *   tile_offsets  device uint32 [ntiles + 1], ntiles = prod_k (n_k / T). */
+typedef struct pcg_tile {
+    int32_t T;
+    int32_t order;
+    int32_t drift;
+    int32_t block;
+    int64_t n_partitioned;
+    const uint32_t *tile_offsets;
+} pcg_tile;
+
+/* ------------------------------------------------------------------------ */
+/* Tile sort  ([TD] "The tile-based spatial sort")                           */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace pcg_tile_sort needs for `count` particles.  Returns
+ * 0 if the arguments are invalid. */
+size_t pcg_sort_workspace_bytes(const pcg_grid *grid, int64_t count, int32_t T);
+
+/* Stable tile sort.
+ * Key: the tile (edge T nodes per used axis, n_k % T == 0) holding each
+ *   particle's first support node -- the cell's lower node for order 1, and for
+ *   order 2 the node below it when the fractional coordinate is < 1/2 ([MM]
+ *   §2.3) -- wrapped periodically; key = t_x + nt_x*(t_y + nt_y*t_z).  With
+ *   T = 1 the key is the cell index (a cell sort, [MM] §3.1).
+ * Output: perm[j] (device uint32 [count]; may be NULL when count == 0) is the
+ *   input index of the particle
+ *   placed in slot j: ascending key, ties in ascending input index (stable, so
+ *   the result is unique).  sorted_keys (device uint32 [count], or NULL) gets
+ *   the keys in slot order.  tile_offsets (device uint32 [ntiles+1]) gets
+ *   tile_offsets[t] = number of particles with key < t.
+ *   out_arrays[i][j] = in_arrays[i][perm[j]] for i < n_arrays (0..16 fp32
+ *   device arrays of `count` entries; out-of-place, out != in).  The keys are
+ *   computed from key_x[k], k < dim.
+ * workspace: device memory of at least pcg_sort_workspace_bytes(), 256-byte
+ *   aligned, contents undefined on entry and exit. */
+pcg_status pcg_tile_sort(const pcg_grid *grid, int32_t order, int32_t T, int64_t count,
+                         const float *const key_x[3], int32_t n_arrays,
+                         const float *const in_arrays[], float *const out_arrays[],
+                         uint32_t *perm, uint32_t *sorted_keys, uint32_t *tile_offsets,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Current deposit  ([TD]; [MM] §2.3 Eq.(12) shape functions)                */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace deposit_currents needs for this layout (tile may
+ * be NULL: then 0). */
+size_t pcg_deposit_workspace_bytes(const pcg_grid *grid, const pcg_tile *tile);
+
+/* J_c(g) += q_p w_p v_{p,c} W(x_p - x_g) for every particle p, every node g of
+ * its order-`order` B-spline support (CIC = 1: 2^dim nodes, TSC = 2: 3^dim
+ * nodes) and c = x, y, z; node indices wrap periodically.
+ * J: device fp32 [3][n_z][n_y][n_x], accumulated.
+ * tile: the layout from pcg_tile_sort keyed with the same order (tile->order
+ *   must equal order), or NULL.  With a layout, one work-group per tile (heavy
+ *   tiles split into chunks) accumulates into an LDS scratch tile of
+ *   TE = T + order + 2*drift nodes per used axis and flushes it once with
+ *   global atomics; a particle whose stencil does not fit the window takes the
+ *   escape valve to global atomics ([TD] "Correctness is independent of the
+ *   halo").  The tail [n_partitioned, count) and the tile == NULL case use the
+ *   flat one-thread-per-particle global-atomic kernel ([TD] "Coverage").
+ *   Requires n_k % T == 0 and drift + order < n_k on used axes, and
+ *   3*TE^dim*4 bytes <= 160 KiB (else PCG_ELDS).
+ * n_escaped: optional device uint64 counter; the number of escaped particles
+ *   is ADDED to it.  workspace: pcg_deposit_workspace_bytes() bytes (may be
+ *   NULL when that is 0). */
+pcg_status deposit_currents(const pcg_grid *grid, const pcg_particles *particles, int32_t order,
+                            const pcg_tile *tile, float *J, unsigned long long *n_escaped,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* ECSIM mass matrix  ([MM] §2.1 Eq.(4)-(6), §2.2 Eq.(9)-(11), §3)           */
+/* ------------------------------------------------------------------------ */
+
+#define PCG_MASS_AUTO 0   /* the matrix-core path                                  */
+#define PCG_MASS_MFMA 1   /* per-cell contraction on fp32 MFMA (16x16x4)           */
+#define PCG_MASS_VALU 2   /* the same per-cell contraction with vector FMAs         */
+#define PCG_MASS_FLAT 3   /* one thread per particle, 576 global atomics each      */
+
+/* M^{ij}_{g, g+o} += q_p w_p alpha_p^{ij} W_{pg} W_{p,g+o} over every ordered
+ * pair of the 8 CIC support nodes of every particle, with
+ * alpha_p = (I - C(omega) + omega omega^T) / (1 + |omega|^2), C(omega)u = omega x u,
+ * omega = beta_p B_p ([MM] Eq.(5), c = 1; the prefactor of Eq.(4) is 1).
+ * 3-D, CIC, every n_k >= 3.
+ * M: device fp32 [n_z][n_y][n_x][27][3][3], accumulated; row g, stencil offset
+ *   o = (dx+1) + 3(dy+1) + 9(dz+1) for the node g + (dx,dy,dz) (wrapped).
+ * B[3], beta: device fp32 per-particle magnetic field and beta = q dt / (2m).
+ * cells: a T = 1, order = 1 layout from pcg_tile_sort (cell c owns its slice;
+ *   [MM] §3.1 assumes particles sorted by cell), or NULL (flat path).  A
+ *   particle found in the slice of a cell it is not in is deposited by the
+ *   flat path; the tail [n_partitioned, count) likewise.
+ * variant: PCG_MASS_*; VALU and MFMA need `cells`. */
+pcg_status assemble_mass_matrix(const pcg_grid *grid, const pcg_particles *particles,
+                                const float *const B[3], const float *beta,
+                                const pcg_tile *cells, int32_t variant, float *M, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* 1-D windowed sweep  ([CS] "The problem", "Code")                          */
+/* ------------------------------------------------------------------------ */
+
+/* H is overwritten with the fused result of `steps` windowed CIC deposits on
+ * the periodic interval [0,1) split into nb bins (1 <= nb <= 16384): for
+ * t = 1..steps, x = x0 + v (t dt) wrapped as x - floor(x), window centre
+ * c = t/steps, minimum-image d = (x-c) - rint(x-c); if |d| < half_width the
+ * particle deposits weight (1 - |d|/half_width)^2 split linearly between bins
+ * floor(x nb - 1/2) and the next one (mod nb).  Positions and weights are
+ * computed in fp64 without fused multiply-adds; H is fp32 [nb].
+ * x0, v: device fp64 [count]. */
+pcg_status deposit_sweep1d(int32_t nb, int64_t count, const double *x0, const double *v,
+                           int32_t steps, double dt, double half_width, float *H, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Diagnostics and measurement                                               */
+/* ------------------------------------------------------------------------ */
+
+const char *pcg_status_string(pcg_status status);
+/* Message of the last failed call on this host thread ("" if none). */
+const char *pcg_last_error(void);
+/* Library version string. */
+const char *pcg_version(void);
+
+/* Kernel timing tap, for measurement.  While enabled, every kernel launch is
+ * bracketed by a pair of HIP events recorded on its launch stream.
+ * pcg_timing_read synchronises the recorded events of the named kernel (e.g.
+ * "deposit_tiled") and returns their summed elapsed time in ms and the number
+ * of launches since the last reset.  pcg_timing_names writes a comma-separated
+ * list of the kernel names seen into buf (truncated to len). */
+pcg_status pcg_timing_enable(int32_t enable);
+pcg_status pcg_timing_reset(void);
+pcg_status pcg_timing_read(const char *kernel, double *total_ms, int64_t *launches);
+pcg_status pcg_timing_names(char *buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PCG_H */

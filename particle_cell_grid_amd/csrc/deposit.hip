@@ -1,0 +1,459 @@
+// deposit.hip -- current deposit J_c += q w v_c W(x - x_g) ([TD] Entity wiki
+// "Tiled current deposit"; B-spline weights from the mass-matrix paper §2.3
+// Eq.(12)).
+//
+// Tiled path ([TD] "How a tile deposit runs"): one work-group per tile (or per
+// chunk of a heavy tile) zeroes an LDS scratch window of TE = T + order + 2D
+// nodes per used axis (D nodes of drift below the tile origin, D + order
+// above), adds every particle of its slice into it with LDS float atomics, then
+// adds each non-zero scratch value to J with one global atomic, wrapping node
+// indices periodically.  A particle whose support does not fit the window is
+// deposited directly to J with global atomics (the escape valve, [TD]
+// "Correctness is independent of the halo").
+// Flat path ([TD] "The two paths", flat column): one thread per particle,
+// (order+1)^dim x 3 global atomics -- used with no layout and for the tail.
+#include <algorithm>
+#include <climits>
+
+#include "common.hpp"
+
+namespace pcg {
+namespace {
+
+struct DepArgs {
+    int n[3];
+    float nf[3];
+    int T, D, TE;
+    int nt[3];
+    uint32_t ntiles;
+    int vol;  // TE^dim
+    const float *x[3];
+    const float *v[3];
+    const float *q;
+    const float *w;
+    float *J;
+    int64_t ng;
+    const uint32_t *tile_offsets;
+    int64_t n_part;
+    const uint32_t *chunk_cum;
+    uint32_t chunk;
+    unsigned long long *n_escaped;
+};
+
+// One axis of the shape: first support node b (wrapped) and order+1 weights.
+template <int ORDER>
+__device__ inline int shape_axis(float xraw, float nf, int n, float *W)
+{
+    const float x = clamp_coord(xraw, nf);
+    const float fl = floorf(x);
+    const float xi = x - fl;
+    int b = (int)fl;
+    if (ORDER == 1) {
+        W[0] = 1.0f - xi;
+        W[1] = xi;
+    } else {
+        float d;
+        if (xi < 0.5f) {
+            b -= 1;
+            d = xi;
+        } else {
+            d = xi - 1.0f;
+        }
+        const float lo = 0.5f - d, hi = 0.5f + d;
+        W[0] = 0.5f * lo * lo;
+        W[1] = 0.75f - d * d;
+        W[2] = 0.5f * hi * hi;
+    }
+    return wrap_index(b, n);
+}
+
+// All (order+1)^dim global atomics of one particle.
+template <int DIM, int ORDER>
+__device__ inline void deposit_global(const DepArgs &a, const int *b, float W[3][ORDER + 1],
+                                      const float *amp)
+{
+    constexpr int M = ORDER + 1;
+    constexpr int MY = DIM > 1 ? M : 1, MZ = DIM > 2 ? M : 1;
+#pragma unroll
+    for (int az = 0; az < MZ; ++az) {
+        const int gz = DIM > 2 ? wrap_index(b[2] + az, a.n[2]) : 0;
+#pragma unroll
+        for (int ay = 0; ay < MY; ++ay) {
+            const int gy = DIM > 1 ? wrap_index(b[1] + ay, a.n[1]) : 0;
+            const float wyz = (DIM > 1 ? W[1][ay] : 1.0f) * (DIM > 2 ? W[2][az] : 1.0f);
+#pragma unroll
+            for (int ax = 0; ax < M; ++ax) {
+                const int gx = wrap_index(b[0] + ax, a.n[0]);
+                const int64_t g = gx + (int64_t)a.n[0] * (gy + (int64_t)a.n[1] * gz);
+                const float wt = W[0][ax] * wyz;
+#pragma unroll
+                for (int c = 0; c < 3; ++c)
+                    atomic_add_f32(&a.J[c * a.ng + g], amp[c] * wt);
+            }
+        }
+    }
+}
+
+template <int DIM, int ORDER>
+__global__ __launch_bounds__(1024) void k_deposit_flat(DepArgs a, int64_t begin, int64_t end)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t p = begin + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < end; p += stride) {
+        float W[3][ORDER + 1];
+        int b[3] = {0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < DIM; ++k)
+            b[k] = shape_axis<ORDER>(a.x[k][p], a.nf[k], a.n[k], W[k]);
+        const float qw = a.q[p] * a.w[p];
+        const float amp[3] = {qw * a.v[0][p], qw * a.v[1][p], qw * a.v[2][p]};
+        deposit_global<DIM, ORDER>(a, b, W, amp);
+    }
+}
+
+template <int DIM, int ORDER>
+__global__ __launch_bounds__(1024) void k_deposit_tiled(DepArgs a)
+{
+    extern __shared__ float scratch[];  // [3][TE^dim]
+    __shared__ uint32_t s_tile, s_lo, s_hi, s_esc;
+    constexpr int M = ORDER + 1;
+
+    if (threadIdx.x == 0) {
+        const uint32_t item = blockIdx.x;
+        const uint32_t total = a.chunk_cum[a.ntiles];
+        s_esc = 0;
+        if (item >= total) {
+            s_tile = UINT_MAX;
+        } else {
+            // largest t with chunk_cum[t] <= item (empty tiles own no items)
+            uint32_t lo = 0, hi = a.ntiles - 1;
+            while (lo < hi) {
+                const uint32_t mid = (lo + hi + 1) >> 1;
+                if (a.chunk_cum[mid] <= item)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            const uint32_t t = lo;
+            const uint32_t nch = a.chunk_cum[t + 1] - a.chunk_cum[t];
+            const uint32_t c = item - a.chunk_cum[t];
+            const uint64_t p0 = std::min<uint64_t>(a.tile_offsets[t], (uint64_t)a.n_part);
+            const uint64_t p1 = std::min<uint64_t>(a.tile_offsets[t + 1], (uint64_t)a.n_part);
+            const uint64_t len = p1 > p0 ? p1 - p0 : 0;
+            s_lo = (uint32_t)(p0 + len * c / nch);
+            s_hi = (uint32_t)(p0 + len * (c + 1) / nch);
+            s_tile = t;
+        }
+    }
+    __syncthreads();
+    const uint32_t tile = s_tile;
+    if (tile == UINT_MAX)
+        return;
+    const uint32_t lo = s_lo, hi = s_hi;
+    int origin[3] = {0, 0, 0};
+    {
+        uint32_t t = tile;
+#pragma unroll
+        for (int k = 0; k < DIM; ++k) {
+            origin[k] = (int)(t % (uint32_t)a.nt[k]) * a.T;
+            t /= (uint32_t)a.nt[k];
+        }
+    }
+    const int TE = a.TE, vol = a.vol, D = a.D;
+    for (int i = threadIdx.x; i < 3 * vol; i += blockDim.x)
+        scratch[i] = 0.0f;
+    __syncthreads();
+
+    const int last = a.T - 1 + 2 * D;  // largest scratch start that keeps the stencil inside
+    for (uint32_t p = lo + threadIdx.x; p < hi; p += blockDim.x) {
+        float W[3][M];
+        int b[3] = {0, 0, 0};
+        int s[3] = {0, 0, 0};
+        bool esc = false;
+#pragma unroll
+        for (int k = 0; k < DIM; ++k) {
+            b[k] = shape_axis<ORDER>(a.x[k][p], a.nf[k], a.n[k], W[k]);
+            // scratch start: periodic offset of the base node from the window's low edge
+            s[k] = wrap_index(b[k] - origin[k] + D, a.n[k]);
+            esc |= s[k] > last;
+        }
+        const float qw = a.q[p] * a.w[p];
+        const float amp[3] = {qw * a.v[0][p], qw * a.v[1][p], qw * a.v[2][p]};
+        if (!esc) {
+            constexpr int MY = DIM > 1 ? M : 1, MZ = DIM > 2 ? M : 1;
+#pragma unroll
+            for (int az = 0; az < MZ; ++az) {
+#pragma unroll
+                for (int ay = 0; ay < MY; ++ay) {
+                    const int row = DIM == 3 ? ((s[2] + az) * TE + (s[1] + ay)) * TE
+                                             : (DIM == 2 ? (s[1] + ay) * TE : 0);
+                    const float wyz = (DIM > 1 ? W[1][ay] : 1.0f) * (DIM > 2 ? W[2][az] : 1.0f);
+#pragma unroll
+                    for (int ax = 0; ax < M; ++ax) {
+                        const int idx = row + s[0] + ax;
+                        const float wt = W[0][ax] * wyz;
+#pragma unroll
+                        for (int c = 0; c < 3; ++c)
+                            __hip_atomic_fetch_add(&scratch[c * vol + idx], amp[c] * wt,
+                                                   __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+                    }
+                }
+            }
+        } else {
+            deposit_global<DIM, ORDER>(a, b, W, amp);
+            atomicAdd(&s_esc, 1u);
+        }
+    }
+    __syncthreads();
+
+    // flush: one global atomic per non-zero scratch value, node indices wrapped
+    for (int i = threadIdx.x; i < vol; i += blockDim.x) {
+        int sx = i, sy = 0, sz = 0;
+        if (DIM > 1) {
+            sx = i % TE;
+            const int r = i / TE;
+            sy = DIM > 2 ? r % TE : r;
+            sz = DIM > 2 ? r / TE : 0;
+        }
+        const int gx = wrap_index(origin[0] - D + sx, a.n[0]);
+        const int gy = DIM > 1 ? wrap_index(origin[1] - D + sy, a.n[1]) : 0;
+        const int gz = DIM > 2 ? wrap_index(origin[2] - D + sz, a.n[2]) : 0;
+        const int64_t g = gx + (int64_t)a.n[0] * (gy + (int64_t)a.n[1] * gz);
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+            const float val = scratch[c * vol + i];
+            if (val != 0.0f)
+                atomic_add_f32(&a.J[c * a.ng + g], val);
+        }
+    }
+    if (threadIdx.x == 0 && s_esc && a.n_escaped)
+        atomicAdd(a.n_escaped, (unsigned long long)s_esc);
+}
+
+// Work items per tile: ceil(len/chunk) (0 for an empty tile), exclusive prefix
+// over tiles into cum[0..ntiles]; one work-group.
+__global__ __launch_bounds__(1024) void k_chunk_cum(const uint32_t *__restrict__ off,
+                                                    uint32_t ntiles, int64_t n_part,
+                                                    uint32_t chunk, uint32_t *__restrict__ cum)
+{
+    __shared__ uint32_t wsum[1024 / WAVE];
+    const uint32_t per = (ntiles + 1023) / 1024;
+    const uint32_t t0 = threadIdx.x * per;
+    const uint32_t t1 = min(t0 + per, ntiles);
+    auto items = [&](uint32_t t) -> uint32_t {
+        const uint64_t p0 = std::min<uint64_t>(off[t], (uint64_t)n_part);
+        const uint64_t p1 = std::min<uint64_t>(off[t + 1], (uint64_t)n_part);
+        return p1 > p0 ? (uint32_t)((p1 - p0 + chunk - 1) / chunk) : 0u;
+    };
+    uint32_t s = 0;
+    for (uint32_t t = t0; t < t1; ++t)
+        s += items(t);
+    // block exclusive scan of s
+    const int wave = threadIdx.x / WAVE, lane = lane_id();
+    uint32_t inc = s;
+#pragma unroll
+    for (int o = 1; o < WAVE; o <<= 1) {
+        const uint32_t u = __shfl_up(inc, o, WAVE);
+        if (lane >= o)
+            inc += u;
+    }
+    if (lane == WAVE - 1)
+        wsum[wave] = inc;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+    for (int w = 0; w < 1024 / WAVE; ++w) {
+        before += w < wave ? wsum[w] : 0u;
+        all += wsum[w];
+    }
+    uint32_t run = before + inc - s;
+    for (uint32_t t = t0; t < t1; ++t) {
+        cum[t] = run;
+        run += items(t);
+    }
+    if (threadIdx.x == 0)
+        cum[ntiles] = all;
+}
+
+template <int DIM, int ORDER>
+pcg_status launch_flat(const DepArgs &a, int64_t begin, int64_t end, hipStream_t st)
+{
+    if (end <= begin)
+        return PCG_OK;
+    const int64_t blocks = std::min<int64_t>((end - begin + 255) / 256, (int64_t)device_cus() * 32);
+    return launch("deposit_flat", k_deposit_flat<DIM, ORDER>, dim3((unsigned)blocks), dim3(256), 0,
+                  st, a, begin, end);
+}
+
+template <int DIM, int ORDER>
+pcg_status launch_tiled(const DepArgs &a, uint32_t nwork, int block, size_t lds, hipStream_t st)
+{
+    auto kern = k_deposit_tiled<DIM, ORDER>;
+    if (lds > 65536) {
+        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds) != hipSuccess)
+            return fail(PCG_EHIP, "deposit_currents: cannot raise dynamic LDS to %zu bytes", lds);
+    }
+    return launch("deposit_tiled", kern, dim3(nwork), dim3(block), lds, st, a);
+}
+
+pcg_status dispatch(int dim, int order, bool tiled, const DepArgs &a, int64_t begin, int64_t end,
+                    uint32_t nwork, int block, size_t lds, hipStream_t st)
+{
+    const int key = dim * 10 + order;
+    if (tiled) {
+        switch (key) {
+        case 11: return launch_tiled<1, 1>(a, nwork, block, lds, st);
+        case 12: return launch_tiled<1, 2>(a, nwork, block, lds, st);
+        case 21: return launch_tiled<2, 1>(a, nwork, block, lds, st);
+        case 22: return launch_tiled<2, 2>(a, nwork, block, lds, st);
+        case 31: return launch_tiled<3, 1>(a, nwork, block, lds, st);
+        case 32: return launch_tiled<3, 2>(a, nwork, block, lds, st);
+        }
+    } else {
+        switch (key) {
+        case 11: return launch_flat<1, 1>(a, begin, end, st);
+        case 12: return launch_flat<1, 2>(a, begin, end, st);
+        case 21: return launch_flat<2, 1>(a, begin, end, st);
+        case 22: return launch_flat<2, 2>(a, begin, end, st);
+        case 31: return launch_flat<3, 1>(a, begin, end, st);
+        case 32: return launch_flat<3, 2>(a, begin, end, st);
+        }
+    }
+    return fail(PCG_EUNSUPPORTED, "deposit_currents: dim %d order %d", dim, order);
+}
+
+uint32_t tile_count(const pcg_grid *grid, int T)
+{
+    uint64_t nt = 1;
+    for (int k = 0; k < grid->dim; ++k)
+        nt *= (uint64_t)(grid->n[k] / T);
+    return (uint32_t)nt;
+}
+
+}  // namespace
+}  // namespace pcg
+
+using namespace pcg;
+
+extern "C" {
+
+size_t pcg_deposit_workspace_bytes(const pcg_grid *grid, const pcg_tile *tile)
+{
+    if (!tile || !grid || check_grid(grid, "pcg_deposit_workspace_bytes") != PCG_OK || tile->T < 1)
+        return 0;
+    for (int k = 0; k < grid->dim; ++k)
+        if (grid->n[k] % tile->T)
+            return 0;
+    return align_up(((size_t)tile_count(grid, tile->T) + 1) * sizeof(uint32_t), 256);
+}
+
+pcg_status deposit_currents(const pcg_grid *grid, const pcg_particles *particles, int32_t order,
+                            const pcg_tile *tile, float *J, unsigned long long *n_escaped,
+                            void *workspace, size_t workspace_bytes, void *stream)
+{
+    const char *who = "deposit_currents";
+    clear_error();
+    PCG_TRY(check_grid(grid, who));
+    if (!particles)
+        return fail(PCG_EINVAL, "%s: particles is NULL", who);
+    if (order != 1 && order != 2)
+        return fail(PCG_EUNSUPPORTED, "%s: order %d not in {1,2}", who, order);
+    const int64_t count = particles->count;
+    if (count < 0 || count >= (int64_t(1) << 31))
+        return fail(PCG_EINVAL, "%s: count %lld outside [0, 2^31)", who, (long long)count);
+    if (!J)
+        return fail(PCG_EINVAL, "%s: J is NULL", who);
+    if (count > 0) {
+        for (int k = 0; k < grid->dim; ++k)
+            if (!particles->x[k])
+                return fail(PCG_EINVAL, "%s: x[%d] is NULL", who, k);
+        for (int c = 0; c < 3; ++c)
+            if (!particles->v[c])
+                return fail(PCG_EINVAL, "%s: v[%d] is NULL", who, c);
+        if (!particles->q || !particles->w)
+            return fail(PCG_EINVAL, "%s: q or w is NULL", who);
+    }
+    DepArgs a{};
+    for (int k = 0; k < 3; ++k) {
+        a.n[k] = grid->n[k];
+        a.nf[k] = (float)grid->n[k];
+        a.x[k] = k < grid->dim ? particles->x[k] : nullptr;
+        a.v[k] = particles->v[k];
+        a.nt[k] = 1;
+    }
+    a.q = particles->q;
+    a.w = particles->w;
+    a.J = J;
+    a.ng = (int64_t)grid->n[0] * grid->n[1] * grid->n[2];
+    a.n_escaped = n_escaped;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (count == 0)
+        return PCG_OK;
+
+    if (!tile)  // no layout yet: flat path ([TD] "First step / tiny species")
+        return dispatch(grid->dim, order, false, a, 0, count, 0, 0, 0, st);
+
+    const int T = tile->T, D = tile->drift;
+    if (T < 1)
+        return fail(PCG_EINVAL, "%s: tile T = %d < 1", who, T);
+    if (tile->order != order)
+        return fail(PCG_EINVAL, "%s: layout keyed with order %d, deposit order %d", who,
+                    tile->order, order);
+    if (D < 0)
+        return fail(PCG_EINVAL, "%s: drift %d < 0", who, D);
+    for (int k = 0; k < grid->dim; ++k) {
+        if (grid->n[k] % T)
+            return fail(PCG_EINVAL, "%s: n[%d] = %d is not a multiple of T = %d", who, k,
+                        grid->n[k], T);
+        if (D + order >= grid->n[k])
+            return fail(PCG_EINVAL, "%s: drift %d + order %d must be < n[%d] = %d", who, D,
+                        order, k, grid->n[k]);
+    }
+    if (tile->n_partitioned < 0 || tile->n_partitioned > count)
+        return fail(PCG_EINVAL, "%s: n_partitioned %lld outside [0, count]", who,
+                    (long long)tile->n_partitioned);
+    if (!tile->tile_offsets)
+        return fail(PCG_EINVAL, "%s: tile_offsets is NULL", who);
+    const int TE = T + order + 2 * D;
+    int64_t vol = 1;
+    for (int k = 0; k < grid->dim; ++k)
+        vol *= TE;
+    const size_t lds = (size_t)vol * 3 * sizeof(float);
+    if (lds > 160 * 1024)
+        return fail(PCG_ELDS, "%s: scratch tile %d^%d x 3 fp32 = %zu bytes exceeds 160 KiB", who,
+                    TE, grid->dim, lds);
+    const size_t need = pcg_deposit_workspace_bytes(grid, tile);
+    if (!workspace || workspace_bytes < need)
+        return fail(PCG_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, need,
+                    workspace_bytes);
+    int block = tile->block;
+    if (block <= 0)
+        block = 256;
+    block = std::max(64, std::min(1024, block)) / 64 * 64;
+
+    a.T = T;
+    a.D = D;
+    a.TE = TE;
+    a.vol = (int)vol;
+    for (int k = 0; k < grid->dim; ++k)
+        a.nt[k] = grid->n[k] / T;
+    a.ntiles = tile_count(grid, T);
+    a.tile_offsets = tile->tile_offsets;
+    a.n_part = tile->n_partitioned;
+    a.chunk_cum = static_cast<const uint32_t *>(workspace);
+    // a tile holding more than `chunk` particles is split over several
+    // work-groups (each with its own scratch and flush) to balance load
+    const int64_t target = (count + (int64_t)device_cus() * 4 - 1) / ((int64_t)device_cus() * 4);
+    a.chunk = (uint32_t)std::max<int64_t>(2048, target);
+    const uint64_t nwork = (uint64_t)a.ntiles + ((uint64_t)a.n_part + a.chunk - 1) / a.chunk;
+    if (nwork >= (uint64_t(1) << 31))
+        return fail(PCG_EINVAL, "%s: too many work-groups", who);
+
+    PCG_TRY(launch("deposit_chunks", k_chunk_cum, dim3(1), dim3(1024), 0, st, a.tile_offsets,
+                   a.ntiles, a.n_part, a.chunk, static_cast<uint32_t *>(workspace)));
+    PCG_TRY(dispatch(grid->dim, order, true, a, 0, 0, (uint32_t)nwork, block, lds, st));
+    // tail pass ([TD] "Coverage: the tail pass")
+    return dispatch(grid->dim, order, false, a, tile->n_partitioned, count, 0, 0, 0, st);
+}
+
+}  // extern "C"

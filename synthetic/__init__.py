@@ -7,9 +7,12 @@ particle arrays.
 
 Recipe (numpy ``Generator(PCG64(seed))``, draws made in this order):
   1. positions, 2. velocities, 3. charges (deterministic), 4. weights,
-  5. magnetic field, 6. the far-displaced subset, 7. the shuffle.
-Values are drawn in fp64 and stored as fp32; a coordinate that rounds up to
-the grid edge n_k is mapped to 0 (positions live in [0, n_k)).
+  5. magnetic field, 6. the far-displaced subset.
+Particles come out in a random order (as a shuffled particle array would be):
+uniform loadings deal every cell exactly ppc times in a random order, and every
+other per-particle quantity is drawn i.i.d. in that final order, so no array is
+ever gathered.  Draws are fp32 except the 1-D workload (fp64); a coordinate that
+rounds up to the grid edge n_k is mapped to 0 (positions live in [0, n_k)).
 
 Workloads (see ``config``):
   1  1-D windowed sweep: 2000 particles, x0 ~ U[0,1), v ~ N(0, 0.05) (fp64),
@@ -41,15 +44,16 @@ def rng(seed: int) -> np.random.Generator:
 
 
 def to_grid_f32(xd: np.ndarray, nk: int) -> np.ndarray:
-    """Cast fp64 coordinates in [0, nk) to fp32, mapping a round-up to nk onto 0."""
-    x = xd.astype(F32)
-    x[x >= F32(nk)] = F32(0.0)
+    """Cast coordinates in [0, nk] to fp32, mapping a round-up to nk onto 0."""
+    x = np.asarray(xd, dtype=F32).copy()
+    x[(x >= F32(nk)) | (x < 0)] = F32(0.0)
     return x
 
 
 def periodic_shift(x: np.ndarray, delta: np.ndarray, nk: int) -> np.ndarray:
-    """Input preparation (a push, not part of the deposit): x + delta wrapped into [0, nk)."""
-    y = np.mod(x.astype(np.float64) + delta, float(nk))
+    """Input preparation (a push, not part of the deposit): x + delta wrapped into
+    [0, nk), in fp32."""
+    y = np.mod(x.astype(F32) + np.asarray(delta, dtype=F32), F32(nk))
     return to_grid_f32(y, nk)
 
 
@@ -83,32 +87,31 @@ class Workload:
 
 
 def _uniform_per_cell(r, n3, dim, ppc):
-    """Exactly ppc particles per cell, uniform inside the cell (cell-major order)."""
+    """Exactly ppc particles per cell, uniform inside the cell, in random order."""
     ncell = int(np.prod(n3[:dim]))
-    cells = np.repeat(np.arange(ncell, dtype=np.int64), ppc)
-    offs = r.random((dim, cells.size))
+    cells = r.permutation(ncell * ppc) // ppc      # every cell dealt ppc times
+    offs = r.random((dim, cells.size), dtype=F32)
     xs = []
     rem = cells
     for k in range(dim):
-        ck = rem % n3[k]
+        ck = (rem % n3[k]).astype(F32)
         rem = rem // n3[k]
-        xd = ck.astype(np.float64) + offs[k]
-        x = xd.astype(F32)
+        x = ck + offs[k]
         # keep the particle inside its cell when fp32 rounds up to the next node
-        up = x >= (ck + 1).astype(F32)
+        up = x >= ck + F32(1)
         if up.any():
-            x[up] = np.nextafter((ck[up] + 1).astype(F32), F32(0.0))
+            x[up] = np.nextafter(ck[up] + F32(1), F32(0.0))
         x[x >= F32(n3[k])] = F32(0.0)
         xs.append(x)
     return xs
 
 
 def _velocities(r, npart, sigma):
-    v = r.normal(0.0, sigma, (3, npart))
+    v = r.standard_normal((3, npart), dtype=F32) * F32(sigma)
     speed = np.sqrt((v * v).sum(axis=0))
     big = speed >= 1.0
     if big.any():
-        v[:, big] *= (1.0 - 2.0 ** -20) / speed[big]
+        v[:, big] *= (F32(1.0 - 2.0 ** -20) / speed[big])
     return v
 
 
@@ -121,10 +124,12 @@ def deposit_workload(dim, n, ppc=None, count=None, sigma_v=0.1, w_uniform=False,
     """Particles for a 2-D/3-D current deposit.
 
     Either ``ppc`` (exactly that many per cell, uniform in-cell) or ``blob``
-    (dict(sigma, overdensity) with ``count`` particles) sets the positions.
-    The push displaces every particle by its velocity (one cell per unit
-    speed), except a ``far_fraction`` subset displaced by a random direction
-    times a length drawn from ``far_range`` cells.
+    (dict(sigma, overdensity) with ``count`` particles: each particle belongs to
+    a Gaussian blob at the centre with the probability that gives the stated
+    peak overdensity over the uniform background, else to the background) sets
+    the positions.  The push displaces every particle by its velocity (one cell
+    per unit speed), except a ``far_fraction`` subset displaced by a random
+    direction times a length drawn from ``far_range`` cells.
     """
     n3 = list(n) + [1] * (3 - len(n))
     r = rng(seed)
@@ -136,36 +141,31 @@ def deposit_workload(dim, n, ppc=None, count=None, sigma_v=0.1, w_uniform=False,
         amp = float(blob["overdensity"])
         vol = float(np.prod(n3[:dim]))
         blob_mass = amp * (2.0 * math.pi * sig * sig) ** (dim / 2.0)
-        nb = int(round(count * blob_mass / (blob_mass + vol)))
-        centre = [nk / 2.0 for nk in n3[:dim]]
-        g = r.normal(0.0, sig, (dim, nb))
-        u = r.random((dim, count - nb))
+        in_blob = r.random(count, dtype=F32) < F32(blob_mass / (blob_mass + vol))
         xs = []
         for k in range(dim):
-            xd = np.concatenate([np.mod(centre[k] + g[k], n3[k]), u[k] * n3[k]])
+            g = r.standard_normal(count, dtype=F32) * F32(sig) + F32(n3[k] / 2.0)
+            u = r.random(count, dtype=F32) * F32(n3[k])
+            xd = np.where(in_blob, np.mod(g, F32(n3[k])), u)
             xs.append(to_grid_f32(xd, n3[k]))
     npart = xs[0].size
     # 2. velocities, 3. charges, 4. weights
     v = _velocities(r, npart, sigma_v)
     q = _charges(npart)
     w = r.uniform(0.5, 1.5, npart).astype(F32) if w_uniform else np.ones(npart, F32)
-    # 6. displacement: v * (1 cell per unit speed), a subset displaced far
+    # 6. displacement: v * (1 cell per unit speed); the order is random, so the
+    #    first n_far particles are a random subset, displaced far instead
     delta = v[:dim].copy()
     n_far = int(round(far_fraction * npart))
     if n_far:
-        idx = r.choice(npart, n_far, replace=False)
-        d = r.normal(0.0, 1.0, (3, n_far))
+        d = r.standard_normal((3, n_far), dtype=F32)
         d /= np.sqrt((d * d).sum(axis=0))
-        length = r.uniform(far_range[0], far_range[1], n_far)
-        delta[:, idx] = (d * length)[:dim]
+        length = r.uniform(far_range[0], far_range[1], n_far).astype(F32)
+        delta[:, :n_far] = (d * length)[:dim]
     x_next = [periodic_shift(xs[k], delta[k], n3[k]) for k in range(dim)]
-    # 7. shuffle
-    perm = r.permutation(npart)
-    wl = Workload(dim, n3, [a[perm] for a in xs], [a[perm] for a in x_next],
-                  [v[c].astype(F32)[perm] for c in range(3)], q[perm], w[perm],
-                  meta=dict(ppc=ppc, count=npart, sigma_v=sigma_v, far_fraction=far_fraction,
-                            n_far=n_far, seed=seed))
-    return wl
+    return Workload(dim, n3, xs, x_next, [v[c] for c in range(3)], q, w,
+                    meta=dict(ppc=ppc, count=npart, sigma_v=sigma_v, far_fraction=far_fraction,
+                              n_far=n_far, seed=seed))
 
 
 def mass_workload(n, ppc, dt=0.1, w_uniform=False, seed=0):
@@ -179,13 +179,10 @@ def mass_workload(n, ppc, dt=0.1, w_uniform=False, seed=0):
     q = _charges(npart)                                     # 3. charges
     w = (r.uniform(0.5, 1.5, npart).astype(F32) if w_uniform  # 4. weights
          else np.ones(npart, F32))
-    B = r.normal(0.0, 1.0, (3, npart))                      # 5. magnetic field
+    B = r.standard_normal((3, npart), dtype=F32)            # 5. magnetic field
     beta = (q.astype(np.float64) * dt / 2.0).astype(F32)
-    perm = r.permutation(npart)                             # 7. shuffle
-    return Workload(3, n3, [a[perm] for a in xs], [a[perm] for a in xs],
-                    [v[c].astype(F32)[perm] for c in range(3)], q[perm], w[perm],
-                    [B[c].astype(F32)[perm] for c in range(3)], beta[perm],
-                    meta=dict(ppc=ppc, count=npart, dt=dt, seed=seed))
+    return Workload(3, n3, xs, xs, [v[c] for c in range(3)], q, w, [B[c] for c in range(3)],
+                    beta, meta=dict(ppc=ppc, count=npart, dt=dt, seed=seed))
 
 
 @dataclass

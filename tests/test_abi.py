@@ -1,0 +1,193 @@
+"""The C-ABI library: it loads, exports every function include/pcg.h declares,
+and rejects invalid arguments on the host with the documented status codes
+before anything is enqueued (so these run without a GPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "particle_cell_grid_amd", "libpcg.so")
+HEADER = os.path.join(ROOT, "include", "pcg.h")
+
+EINVAL, EUNSUPPORTED, ELDS, EWORKSPACE = -1, -2, -3, -4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        import subprocess
+        import sys
+
+        subprocess.check_call([sys.executable, os.path.join(ROOT, "particle_cell_grid_amd",
+                                                            "csrc", "build.py")])
+    return C.CDLL(LIB)
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["pcg_tile_sort", "pcg_sort_workspace_bytes", "deposit_currents",
+              "pcg_deposit_workspace_bytes", "assemble_mass_matrix", "deposit_sweep1d",
+              "pcg_status_string", "pcg_last_error", "pcg_version", "pcg_timing_enable",
+              "pcg_timing_reset", "pcg_timing_read", "pcg_timing_names"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"libpcg.so does not export {n}"
+
+
+class Grid(C.Structure):
+    _fields_ = [("dim", C.c_int32), ("n", C.c_int32 * 3)]
+
+
+class Particles(C.Structure):
+    _fields_ = [("count", C.c_int64), ("x", C.c_void_p * 3), ("v", C.c_void_p * 3),
+                ("q", C.c_void_p), ("w", C.c_void_p)]
+
+
+class Tile(C.Structure):
+    _fields_ = [("T", C.c_int32), ("order", C.c_int32), ("drift", C.c_int32),
+                ("block", C.c_int32), ("n_partitioned", C.c_int64), ("tile_offsets", C.c_void_p)]
+
+
+FAKE = 0x10000  # never dereferenced: validation fails before any launch
+
+
+def grid(dim, n):
+    return Grid(dim, (C.c_int32 * 3)(*(list(n) + [1] * (3 - len(n)))))
+
+
+def particles(count):
+    P = Particles()
+    P.count = count
+    for k in range(3):
+        P.x[k] = FAKE
+        P.v[k] = FAKE
+    P.q = FAKE
+    P.w = FAKE
+    return P
+
+
+def test_status_strings(lib):
+    lib.pcg_status_string.restype = C.c_char_p
+    lib.pcg_version.restype = C.c_char_p
+    assert b"EINVAL" in lib.pcg_status_string(EINVAL)
+    assert b"LDS" in lib.pcg_status_string(ELDS)
+    assert b"gfx950" in lib.pcg_version()
+
+
+def test_sort_workspace_size(lib):
+    lib.pcg_sort_workspace_bytes.restype = C.c_size_t
+    g = grid(3, [128, 128, 128])
+    ws = lib.pcg_sort_workspace_bytes(C.byref(g), C.c_int64(1 << 20), 8)
+    assert ws >= 5 * 4 * (1 << 20)
+    assert lib.pcg_sort_workspace_bytes(C.byref(g), C.c_int64(100), 7) == 0   # 128 % 7
+    bad = grid(4, [8, 8, 8])
+    assert lib.pcg_sort_workspace_bytes(C.byref(bad), C.c_int64(100), 1) == 0
+
+
+def test_deposit_validation(lib):
+    lib.pcg_last_error.restype = C.c_char_p
+    dc = lib.deposit_currents
+    P = particles(1000)
+    J = C.c_void_p(FAKE)
+
+    def call(g, order=1, tile=None, J=J, ws=C.c_void_p(FAKE), wsb=1 << 30, P=P):
+        return dc(C.byref(g), C.byref(P), order, C.byref(tile) if tile else None, J, None, ws,
+                  C.c_size_t(wsb), None)
+
+    assert call(grid(0, [1, 1, 1])) == EINVAL
+    assert call(grid(2, [8, 8, 8])) == EINVAL                     # unused axis not 1
+    assert call(grid(3, [8, 8, 8]), order=3) == EUNSUPPORTED
+    assert call(grid(3, [8, 8, 8]), J=None) == EINVAL
+    P2 = particles(1000)
+    P2.q = None
+    assert call(grid(3, [8, 8, 8]), P=P2) == EINVAL
+    assert call(grid(3, [8, 8, 8]), P=particles(-1)) == EINVAL
+    g = grid(3, [64, 64, 64])
+    t = Tile(8, 2, 1, 0, 1000, FAKE)
+    assert call(g, order=1, tile=t) == EINVAL                     # layout keyed with TSC
+    assert b"order" in lib.pcg_last_error()
+    t = Tile(6, 1, 1, 0, 1000, FAKE)
+    assert call(g, tile=t) == EINVAL                              # 64 % 6
+    t = Tile(8, 1, -1, 0, 1000, FAKE)
+    assert call(g, tile=t) == EINVAL                              # negative drift
+    t = Tile(8, 1, 1, 0, 1001, FAKE)
+    assert call(g, tile=t) == EINVAL                              # n_partitioned > count
+    t = Tile(8, 1, 1, 0, 1000, None)
+    assert call(g, tile=t) == EINVAL                              # no offsets
+    t = Tile(16, 2, 8, 0, 1000, FAKE)                             # TE = 34: 34^3*12 B > 160 KiB
+    assert call(g, order=2, tile=t) == ELDS
+    t = Tile(8, 1, 1, 0, 1000, FAKE)
+    assert call(g, tile=t, ws=None) == EWORKSPACE
+    assert call(g, tile=t, wsb=16) == EWORKSPACE
+    small = grid(3, [4, 4, 4])
+    t = Tile(4, 1, 3, 0, 1000, FAKE)                              # drift + order >= n
+    assert call(small, tile=t) == EINVAL
+
+
+def test_deposit_workspace_size(lib):
+    lib.pcg_deposit_workspace_bytes.restype = C.c_size_t
+    g = grid(3, [128, 128, 128])
+    t = Tile(8, 1, 1, 0, 0, FAKE)
+    assert lib.pcg_deposit_workspace_bytes(C.byref(g), C.byref(t)) >= 4097 * 4
+    assert lib.pcg_deposit_workspace_bytes(C.byref(g), None) == 0
+
+
+def test_tile_sort_validation(lib):
+    ts = lib.pcg_tile_sort
+    g = grid(3, [32, 32, 32])
+    kx = (C.c_void_p * 3)(FAKE, FAKE, FAKE)
+    arr = (C.c_void_p * 1)(FAKE)
+    arr2 = (C.c_void_p * 1)(FAKE + 4096)
+
+    def call(g=g, order=1, T=8, count=100, n_arrays=1, outs=arr2, perm=FAKE, off=FAKE, ws=FAKE,
+             wsb=1 << 30):
+        return ts(C.byref(g), order, T, C.c_int64(count), kx, n_arrays, arr, outs,
+                  C.c_void_p(perm), None, C.c_void_p(off), C.c_void_p(ws), C.c_size_t(wsb), None)
+
+    assert call(T=0) == EINVAL
+    assert call(T=5) == EINVAL
+    assert call(order=0) == EUNSUPPORTED
+    assert call(count=-5) == EINVAL
+    assert call(n_arrays=17) == EINVAL
+    assert call(outs=arr) == EINVAL                               # in place
+    assert call(perm=0) == EINVAL
+    assert call(off=0) == EINVAL
+    assert call(ws=0) == EWORKSPACE
+    assert call(wsb=10) == EWORKSPACE
+    assert call(ws=FAKE + 8) == EWORKSPACE                        # misaligned
+
+
+def test_mass_and_sweep_validation(lib):
+    am = lib.assemble_mass_matrix
+    P = particles(100)
+    B = (C.c_void_p * 3)(FAKE, FAKE, FAKE)
+    assert am(C.byref(grid(2, [8, 8])), C.byref(P), B, C.c_void_p(FAKE), None, 0,
+              C.c_void_p(FAKE), None) == EUNSUPPORTED
+    assert am(C.byref(grid(3, [2, 8, 8])), C.byref(P), B, C.c_void_p(FAKE), None, 0,
+              C.c_void_p(FAKE), None) == EINVAL
+    assert am(C.byref(grid(3, [8, 8, 8])), C.byref(P), B, C.c_void_p(FAKE), None, 9,
+              C.c_void_p(FAKE), None) == EINVAL
+    assert am(C.byref(grid(3, [8, 8, 8])), C.byref(P), B, C.c_void_p(FAKE), None, 1,
+              C.c_void_p(FAKE), None) == EINVAL                   # MFMA needs cells
+    t = Tile(2, 1, 0, 0, 100, FAKE)
+    assert am(C.byref(grid(3, [8, 8, 8])), C.byref(P), B, C.c_void_p(FAKE), C.byref(t), 1,
+              C.c_void_p(FAKE), None) == EINVAL                   # not a cell layout
+    sw = lib.deposit_sweep1d
+    sw.argtypes = [C.c_int32, C.c_int64, C.c_void_p, C.c_void_p, C.c_int32, C.c_double,
+                   C.c_double, C.c_void_p, C.c_void_p]
+    assert sw(0, 10, FAKE, FAKE, 50, 0.02, 0.005, FAKE, None) == EINVAL
+    assert sw(1 << 15, 10, FAKE, FAKE, 50, 0.02, 0.005, FAKE, None) == EINVAL
+    assert sw(1024, 10, FAKE, FAKE, 50, 0.02, 0.0, FAKE, None) == EINVAL
+    assert sw(1024, 10, None, FAKE, 50, 0.02, 0.005, FAKE, None) == EINVAL

@@ -77,8 +77,9 @@ typedef struct pcg_particles {
  *   order      shape order the layout was keyed with (1 CIC, 2 TSC).
  *   drift      halo budget D >= 0 in cells ([TD] "Halo sizing"): the scratch
  *              tile spans TE = T + order + 2*D nodes per used axis.
- *   block      work-group size; 0 = automatic, otherwise clamped to [64, 1024]
- *              and rounded down to a multiple of 64 ([TD] team size knob).
+ *   block      work-group size; 0 = automatic (256), otherwise clamped to
+ *              [64, 256] and rounded down to a multiple of 64 ([TD] team size
+ *              knob).
  *   tile_offsets  device uint32 [ntiles + 1], ntiles = prod_k (n_k / T). */
 typedef struct pcg_tile {
     int32_t T;
@@ -138,7 +139,11 @@ size_t pcg_deposit_workspace_bytes(const pcg_grid *grid, const pcg_tile *tile);
  *   TE = T + order + 2*drift nodes per used axis and flushes it once with
  *   global atomics; a particle whose stencil does not fit the window takes the
  *   escape valve to global atomics ([TD] "Correctness is independent of the
- *   halo").  The tail [n_partitioned, count) and the tile == NULL case use the
+ *   halo").  The scratch holds int64 fixed-point sums scaled per work-group
+ *   (exact, order-independent in-tile accumulation of the fp32 products); a
+ *   particle whose |q w v| lies far outside its work-group's scale also takes
+ *   the valve but is not counted in n_escaped.  When the int64 scratch
+ *   (3*TE^dim*8 bytes) exceeds the LDS, fp32 scratch is used instead.  The tail [n_partitioned, count) and the tile == NULL case use the
  *   flat one-thread-per-particle global-atomic kernel ([TD] "Coverage").
  *   Requires n_k % T == 0 and drift + order < n_k on used axes, and
  *   3*TE^dim*4 bytes <= 160 KiB (else PCG_ELDS).

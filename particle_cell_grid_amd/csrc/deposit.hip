@@ -5,9 +5,9 @@
 // Tiled path ([TD] "How a tile deposit runs"): one work-group per tile (or per
 // chunk of a heavy tile) zeroes an LDS scratch window of TE = T + order + 2D
 // nodes per used axis (D nodes of drift below the tile origin, D + order
-// above), adds every particle of its slice into it with LDS float atomics, then
-// adds each non-zero scratch value to J with one global atomic, wrapping node
-// indices periodically.  A particle whose support does not fit the window is
+// above), adds every particle of its slice into it with LDS atomics (exact
+// int64 fixed-point sums, see k_deposit_tiled), then adds each non-zero scratch
+// value to J with one global atomic, wrapping node indices periodically.  A particle whose support does not fit the window is
 // deposited directly to J with global atomics (the escape valve, [TD]
 // "Correctness is independent of the halo").
 // Flat path ([TD] "The two paths", flat column): one thread per particle,
@@ -19,6 +19,8 @@
 
 namespace pcg {
 namespace {
+
+constexpr size_t LDS_LIMIT = 160 * 1024;
 
 struct DepArgs {
     int n[3];
@@ -110,17 +112,31 @@ __global__ __launch_bounds__(1024) void k_deposit_flat(DepArgs a, int64_t begin,
     }
 }
 
-template <int DIM, int ORDER>
-__global__ __launch_bounds__(1024) void k_deposit_tiled(DepArgs a)
+// LDS float atomics (ds_add_f32) are ~30x slower than integer LDS atomics on
+// gfx950, so the scratch tile normally holds int64 fixed-point sums: a
+// work-group picks a power-of-two scale 2^S from the largest |q w v_c| of its
+// first 256 particles (S puts that value near 2^23), every product
+// q w v_c W * 2^S is rounded once to an integer and added with ds_add_u64.
+// The sums are then exact and independent of the order of the adds.  A
+// particle whose largest |q w v_c| * 2^S is outside [2^8, 2^30) would overflow
+// or lose precision there, so it takes the escape valve like a particle that
+// left the window (only the latter are counted as escapes).  When the int64
+// scratch does not fit the LDS, FIXED = false keeps fp32 LDS atomics.
+template <int DIM, int ORDER, bool FIXED>
+__global__ __launch_bounds__(256) void k_deposit_tiled(DepArgs a)
 {
-    extern __shared__ float scratch[];  // [3][TE^dim]
-    __shared__ uint32_t s_tile, s_lo, s_hi, s_esc;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    unsigned long long *acc64 = reinterpret_cast<unsigned long long *>(smem);  // [3][vol]
+    float *acc32 = reinterpret_cast<float *>(smem);                          // [3][vol]
+    __shared__ uint32_t s_tile, s_lo, s_hi, s_esc, s_maxbits;
     constexpr int M = ORDER + 1;
+    constexpr int MY = DIM > 1 ? M : 1, MZ = DIM > 2 ? M : 1;
 
     if (threadIdx.x == 0) {
         const uint32_t item = blockIdx.x;
         const uint32_t total = a.chunk_cum[a.ntiles];
         s_esc = 0;
+        s_maxbits = 0;
         if (item >= total) {
             s_tile = UINT_MAX;
         } else {
@@ -159,27 +175,77 @@ __global__ __launch_bounds__(1024) void k_deposit_tiled(DepArgs a)
         }
     }
     const int TE = a.TE, vol = a.vol, D = a.D;
-    for (int i = threadIdx.x; i < 3 * vol; i += blockDim.x)
-        scratch[i] = 0.0f;
+    if (FIXED) {
+        for (int i = threadIdx.x; i < 3 * vol; i += blockDim.x)
+            acc64[i] = 0ull;
+        // scale from the first batch: largest |q w v_c|
+        float m = 0.0f;
+        const uint32_t p = lo + threadIdx.x;
+        if (p < hi) {
+            const float qw = fabsf(a.q[p] * a.w[p]);
+            m = qw * fmaxf(fabsf(a.v[0][p]), fmaxf(fabsf(a.v[1][p]), fabsf(a.v[2][p])));
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1)
+            m = fmaxf(m, __shfl_xor(m, o, WAVE));
+        if (lane_id() == 0 && m > 0.0f && m <= 3.0e38f)
+            atomicMax(&s_maxbits, __float_as_uint(m));  // non-negative: int order = float order
+    } else {
+        for (int i = threadIdx.x; i < 3 * vol; i += blockDim.x)
+            acc32[i] = 0.0f;
+    }
     __syncthreads();
+    float scale = 1.0f, inv_scale = 1.0f;
+    if (FIXED) {
+        const float m = __uint_as_float(s_maxbits);
+        int S = 0;
+        if (m > 0.0f)
+            S = 23 - ilogbf(m);
+        S = max(-100, min(100, S));
+        scale = ldexpf(1.0f, S);
+        inv_scale = ldexpf(1.0f, -S);
+    }
+    const float lo_ok = 256.0f, hi_ok = 1073741824.0f;  // 2^8 and 2^30 (scaled)
 
     const int last = a.T - 1 + 2 * D;  // largest scratch start that keeps the stencil inside
     for (uint32_t p = lo + threadIdx.x; p < hi; p += blockDim.x) {
+        // all loads first, so they are in flight together
+        float xs[3], vv[3];
+#pragma unroll
+        for (int k = 0; k < DIM; ++k)
+            xs[k] = a.x[k][p];
+#pragma unroll
+        for (int c = 0; c < 3; ++c)
+            vv[c] = a.v[c][p];
+        const float qw = a.q[p] * a.w[p];
+
         float W[3][M];
         int b[3] = {0, 0, 0};
         int s[3] = {0, 0, 0};
         bool esc = false;
 #pragma unroll
         for (int k = 0; k < DIM; ++k) {
-            b[k] = shape_axis<ORDER>(a.x[k][p], a.nf[k], a.n[k], W[k]);
+            b[k] = shape_axis<ORDER>(xs[k], a.nf[k], a.n[k], W[k]);
             // scratch start: periodic offset of the base node from the window's low edge
             s[k] = wrap_index(b[k] - origin[k] + D, a.n[k]);
             esc |= s[k] > last;
         }
-        const float qw = a.q[p] * a.w[p];
-        const float amp[3] = {qw * a.v[0][p], qw * a.v[1][p], qw * a.v[2][p]};
-        if (!esc) {
-            constexpr int MY = DIM > 1 ? M : 1, MZ = DIM > 2 ? M : 1;
+        float amp[3] = {qw * vv[0], qw * vv[1], qw * vv[2]};
+        bool in_lds = !esc;
+        if (FIXED) {
+            const float amax =
+                fmaxf(fabsf(amp[0]), fmaxf(fabsf(amp[1]), fabsf(amp[2]))) * scale;
+            if (amax == 0.0f) {  // deposits nothing, but an escape is still an escape
+                if (esc)
+                    atomicAdd(&s_esc, 1u);
+                continue;
+            }
+            in_lds = in_lds && amax >= lo_ok && amax < hi_ok;
+#pragma unroll
+            for (int c = 0; c < 3; ++c)
+                amp[c] *= scale;
+        }
+        if (in_lds) {
 #pragma unroll
             for (int az = 0; az < MZ; ++az) {
 #pragma unroll
@@ -192,16 +258,30 @@ __global__ __launch_bounds__(1024) void k_deposit_tiled(DepArgs a)
                         const int idx = row + s[0] + ax;
                         const float wt = W[0][ax] * wyz;
 #pragma unroll
-                        for (int c = 0; c < 3; ++c)
-                            __hip_atomic_fetch_add(&scratch[c * vol + idx], amp[c] * wt,
-                                                   __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+                        for (int c = 0; c < 3; ++c) {
+                            if (FIXED) {
+                                const long long f = (long long)__float2int_rn(amp[c] * wt);
+                                __hip_atomic_fetch_add(&acc64[c * vol + idx],
+                                                       (unsigned long long)f, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+                            } else {
+                                __hip_atomic_fetch_add(&acc32[c * vol + idx], amp[c] * wt,
+                                                       __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+                            }
+                        }
                     }
                 }
             }
         } else {
+            if (FIXED) {
+#pragma unroll
+                for (int c = 0; c < 3; ++c)
+                    amp[c] *= inv_scale;  // exact: power-of-two scale
+            }
             deposit_global<DIM, ORDER>(a, b, W, amp);
-            atomicAdd(&s_esc, 1u);
+            if (esc)
+                atomicAdd(&s_esc, 1u);
         }
     }
     __syncthreads();
@@ -221,7 +301,11 @@ __global__ __launch_bounds__(1024) void k_deposit_tiled(DepArgs a)
         const int64_t g = gx + (int64_t)a.n[0] * (gy + (int64_t)a.n[1] * gz);
 #pragma unroll
         for (int c = 0; c < 3; ++c) {
-            const float val = scratch[c * vol + i];
+            float val;
+            if (FIXED)
+                val = (float)((double)(long long)acc64[c * vol + i] * (double)inv_scale);
+            else
+                val = acc32[c * vol + i];
             if (val != 0.0f)
                 atomic_add_f32(&a.J[c * a.ng + g], val);
         }
@@ -284,16 +368,27 @@ pcg_status launch_flat(const DepArgs &a, int64_t begin, int64_t end, hipStream_t
                   st, a, begin, end);
 }
 
-template <int DIM, int ORDER>
-pcg_status launch_tiled(const DepArgs &a, uint32_t nwork, int block, size_t lds, hipStream_t st)
+template <int DIM, int ORDER, bool FIXED>
+pcg_status launch_tiled_impl(const DepArgs &a, uint32_t nwork, int block, size_t lds,
+                             hipStream_t st)
 {
-    auto kern = k_deposit_tiled<DIM, ORDER>;
+    auto kern = k_deposit_tiled<DIM, ORDER, FIXED>;
     if (lds > 65536) {
         if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)lds) != hipSuccess)
             return fail(PCG_EHIP, "deposit_currents: cannot raise dynamic LDS to %zu bytes", lds);
     }
     return launch("deposit_tiled", kern, dim3(nwork), dim3(block), lds, st, a);
+}
+
+template <int DIM, int ORDER>
+pcg_status launch_tiled(const DepArgs &a, uint32_t nwork, int block, size_t lds,
+                        hipStream_t st)
+{
+    // int64 fixed-point scratch when it fits, else fp32 scratch (lds is the fp32 size)
+    if (2 * lds <= LDS_LIMIT)
+        return launch_tiled_impl<DIM, ORDER, true>(a, nwork, block, 2 * lds, st);
+    return launch_tiled_impl<DIM, ORDER, false>(a, nwork, block, lds, st);
 }
 
 pcg_status dispatch(int dim, int order, bool tiled, const DepArgs &a, int64_t begin, int64_t end,
@@ -429,7 +524,7 @@ pcg_status deposit_currents(const pcg_grid *grid, const pcg_particles *particles
     int block = tile->block;
     if (block <= 0)
         block = 256;
-    block = std::max(64, std::min(1024, block)) / 64 * 64;
+    block = std::max(64, std::min(256, block)) / 64 * 64;
 
     a.T = T;
     a.D = D;

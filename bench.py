@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--no-flat", action="store_true", help="skip the flat-path comparison")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device-to-device copy (known bytes) so hardware "
+                         "traffic counters can be scaled")
     return ap.parse_args()
 
 
@@ -172,11 +175,15 @@ def bench_deposit(args, torch, pcg, k):
     def deposit():
         pcg.deposit_currents(dim, n, order, xs, vs, q, w, J, lay, esc, dws)
 
+    def resort():
+        # the pushed particles are grouped by the previous layout: re-sort from it
+        pcg.pcg_tile_sort(dim, n, order, T, xs, cur, outs=nxt, want_perm=False,
+                          want_keys=False, tile_offsets=off1, workspace=sws, prev=lay)
+
     def step():
         J.zero_()
         deposit()
-        pcg.pcg_tile_sort(dim, n, order, T, xs, cur, outs=nxt, perm=perm, sorted_keys=keys,
-                          tile_offsets=off1, workspace=sws)
+        resort()
 
     ms, wall, kt = time_steps(torch, pcg, step, args.steps, args.warmup)
     # escape count of one deposit of this input
@@ -217,9 +224,11 @@ def bench_deposit(args, torch, pcg, k):
         fl_ms = time_plain(torch, flat, max(3, args.steps // 4))
         extra["flat_deposit_particles_per_s"] = round(cnt / (fl_ms * 1e-3), 1)
         extra["tiled_speedup_vs_flat"] = round(fl_ms / dep_ms, 2)
-    sort_ms = time_plain(torch, lambda: pcg.pcg_tile_sort(
+    sort_ms = time_plain(torch, resort, args.steps)
+    cold_ms = time_plain(torch, lambda: pcg.pcg_tile_sort(
         dim, n, order, T, xs, cur, outs=nxt, perm=perm, sorted_keys=keys, tile_offsets=off1,
-        workspace=sws), args.steps)
+        workspace=sws), max(3, args.steps // 4))
+    extra["sort_without_prev_layout_ms"] = round(cold_ms, 4)
     extra["sort_only_ms"] = round(sort_ms, 4)
     extra["escaped_particles"] = n_esc
     extra["deposit_roofline"] = roof
@@ -350,6 +359,13 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.config in (2, 3, 4):
         r = bench_deposit(args, torch, pcg, args.config)
     elif args.config == 5:

@@ -104,7 +104,7 @@ size_t pcg_sort_workspace_bytes(const pcg_grid *grid, int64_t count, int32_t T);
  *   order 2 the node below it when the fractional coordinate is < 1/2 ([MM]
  *   §2.3) -- wrapped periodically; key = t_x + nt_x*(t_y + nt_y*t_z).  With
  *   T = 1 the key is the cell index (a cell sort, [MM] §3.1).
- * Output: perm[j] (device uint32 [count]; may be NULL when count == 0) is the
+ * Output: perm[j] (device uint32 [count], or NULL when not wanted) is the
  *   input index of the particle
  *   placed in slot j: ascending key, ties in ascending input index (stable, so
  *   the result is unique).  sorted_keys (device uint32 [count], or NULL) gets
@@ -113,13 +113,23 @@ size_t pcg_sort_workspace_bytes(const pcg_grid *grid, int64_t count, int32_t T);
  *   out_arrays[i][j] = in_arrays[i][perm[j]] for i < n_arrays (0..16 fp32
  *   device arrays of `count` entries; out-of-place, out != in).  The keys are
  *   computed from key_x[k], k < dim.
+ * prev: optional; the layout the input is currently grouped by (the previous
+ *   sort's output, T and order equal to this call's, device offsets distinct
+ *   from tile_offsets).  When it covers all particles, the sort runs as a
+ *   single-pass counting sort over the 27 neighbouring tiles of each particle's
+ *   previous tile -- the every-step case of [TD] "Halo sizing", where particles
+ *   move at most one cell between sorts.  If the offsets are not a partition of
+ *   [0, count) or any particle moved further, the general radix path runs
+ *   instead, decided on the device (the call stays asynchronous).  The output
+ *   is identical either way.
  * workspace: device memory of at least pcg_sort_workspace_bytes(), 256-byte
  *   aligned, contents undefined on entry and exit. */
 pcg_status pcg_tile_sort(const pcg_grid *grid, int32_t order, int32_t T, int64_t count,
                          const float *const key_x[3], int32_t n_arrays,
                          const float *const in_arrays[], float *const out_arrays[],
                          uint32_t *perm, uint32_t *sorted_keys, uint32_t *tile_offsets,
-                         void *workspace, size_t workspace_bytes, void *stream);
+                         const pcg_tile *prev, void *workspace, size_t workspace_bytes,
+                         void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* Current deposit  ([TD]; [MM] §2.3 Eq.(12) shape functions)                */

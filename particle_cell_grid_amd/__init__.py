@@ -49,7 +49,7 @@ _lib.pcg_sort_workspace_bytes.argtypes = [_P(Grid), C.c_int64, C.c_int32]
 _lib.pcg_sort_workspace_bytes.restype = C.c_size_t
 _lib.pcg_tile_sort.argtypes = [_P(Grid), C.c_int32, C.c_int32, C.c_int64, C.c_void_p, C.c_int32,
                                C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
-                               C.c_void_p, C.c_size_t, C.c_void_p]
+                               C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
 _lib.pcg_tile_sort.restype = C.c_int32
 _lib.pcg_deposit_workspace_bytes.argtypes = [_P(Grid), _P(Tile)]
 _lib.pcg_deposit_workspace_bytes.restype = C.c_size_t
@@ -152,15 +152,19 @@ def pcg_tile_sort(dim: int, n: Sequence[int], order: int, T: int, key_x: List[to
                   arrays: Sequence[torch.Tensor] = (), outs: Optional[List[torch.Tensor]] = None,
                   perm: Optional[torch.Tensor] = None, sorted_keys: Optional[torch.Tensor] = None,
                   tile_offsets: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None):
+                  workspace: Optional[torch.Tensor] = None, prev: Optional["Layout"] = None,
+                  want_keys: bool = True, want_perm: bool = True):
     """Stable tile sort.  Returns (perm, sorted_keys, tile_offsets, outs);
-    output tensors are allocated when not given."""
+    output tensors are allocated when not given.  `prev` is the layout the
+    input is currently grouped by (enables the single-pass path); with
+    want_keys=False / want_perm=False (and no tensor given) the sorted keys /
+    the permutation are not written."""
     g = make_grid(dim, n)
     count = int(key_x[0].numel())
     dev = key_x[0].device
-    if perm is None:
+    if perm is None and want_perm:
         perm = torch.empty(count, dtype=torch.int32, device=dev)
-    if sorted_keys is None:
+    if sorted_keys is None and want_keys:
         sorted_keys = torch.empty(count, dtype=torch.int32, device=dev)
     if tile_offsets is None:
         tile_offsets = torch.empty(ntiles(dim, n, T) + 1, dtype=torch.int32, device=dev)
@@ -173,8 +177,10 @@ def pcg_tile_sort(dim: int, n: Sequence[int], order: int, T: int, key_x: List[to
     na = len(arrays)
     ins = (C.c_void_p * max(na, 1))(*[a.data_ptr() for a in arrays])
     ous = (C.c_void_p * max(na, 1))(*[o.data_ptr() for o in outs])
+    pt = prev.to_c() if prev is not None else None
     st = _lib.pcg_tile_sort(C.byref(g), int(order), int(T), count, kx, na, ins, ous,
-                            _ptr(perm), _ptr(sorted_keys), _ptr(tile_offsets), _ptr(workspace),
+                            _ptr(perm), _ptr(sorted_keys), _ptr(tile_offsets),
+                            C.byref(pt) if pt is not None else None, _ptr(workspace),
                             int(workspace.numel()), _stream())
     _check(st, "pcg_tile_sort")
     return perm, sorted_keys, tile_offsets, outs

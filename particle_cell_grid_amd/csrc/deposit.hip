@@ -16,6 +16,7 @@
 #include <climits>
 
 #include "common.hpp"
+#include "layout.hpp"
 
 namespace pcg {
 namespace {
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(1024) void k_deposit_flat(DepArgs a, int64_t begin,
 // or lose precision there, so it takes the escape valve like a particle that
 // left the window (only the latter are counted as escapes).  When the int64
 // scratch does not fit the LDS, FIXED = false keeps fp32 LDS atomics.
-template <int DIM, int ORDER, bool FIXED>
+template <int DIM, int ORDER, bool FIXED, int TEC>
 __global__ __launch_bounds__(256) void k_deposit_tiled(DepArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -133,32 +134,13 @@ __global__ __launch_bounds__(256) void k_deposit_tiled(DepArgs a)
     constexpr int MY = DIM > 1 ? M : 1, MZ = DIM > 2 ? M : 1;
 
     if (threadIdx.x == 0) {
-        const uint32_t item = blockIdx.x;
-        const uint32_t total = a.chunk_cum[a.ntiles];
+        const ChunkRange r = find_chunk(blockIdx.x, a.chunk_cum, a.ntiles, a.tile_offsets,
+                                        a.n_part);
+        s_tile = r.tile;
+        s_lo = r.lo;
+        s_hi = r.hi;
         s_esc = 0;
         s_maxbits = 0;
-        if (item >= total) {
-            s_tile = UINT_MAX;
-        } else {
-            // largest t with chunk_cum[t] <= item (empty tiles own no items)
-            uint32_t lo = 0, hi = a.ntiles - 1;
-            while (lo < hi) {
-                const uint32_t mid = (lo + hi + 1) >> 1;
-                if (a.chunk_cum[mid] <= item)
-                    lo = mid;
-                else
-                    hi = mid - 1;
-            }
-            const uint32_t t = lo;
-            const uint32_t nch = a.chunk_cum[t + 1] - a.chunk_cum[t];
-            const uint32_t c = item - a.chunk_cum[t];
-            const uint64_t p0 = std::min<uint64_t>(a.tile_offsets[t], (uint64_t)a.n_part);
-            const uint64_t p1 = std::min<uint64_t>(a.tile_offsets[t + 1], (uint64_t)a.n_part);
-            const uint64_t len = p1 > p0 ? p1 - p0 : 0;
-            s_lo = (uint32_t)(p0 + len * c / nch);
-            s_hi = (uint32_t)(p0 + len * (c + 1) / nch);
-            s_tile = t;
-        }
     }
     __syncthreads();
     const uint32_t tile = s_tile;
@@ -174,7 +156,11 @@ __global__ __launch_bounds__(256) void k_deposit_tiled(DepArgs a)
             t /= (uint32_t)a.nt[k];
         }
     }
-    const int TE = a.TE, vol = a.vol, D = a.D;
+    // TEC > 0: the scratch edge is a compile-time constant, so every node offset
+    // folds into the LDS instruction's immediate offset
+    const int TE = TEC > 0 ? TEC : a.TE;
+    const int vol = TEC > 0 ? (DIM == 3 ? TEC * TEC * TEC : (DIM == 2 ? TEC * TEC : TEC)) : a.vol;
+    const int D = a.D;
     if (FIXED) {
         for (int i = threadIdx.x; i < 3 * vol; i += blockDim.x)
             acc64[i] = 0ull;
@@ -208,16 +194,43 @@ __global__ __launch_bounds__(256) void k_deposit_tiled(DepArgs a)
     const float lo_ok = 256.0f, hi_ok = 1073741824.0f;  // 2^8 and 2^30 (scaled)
 
     const int last = a.T - 1 + 2 * D;  // largest scratch start that keeps the stencil inside
+    // software pipeline: the next particle's eight values load while this one
+    // is weighed and accumulated
+    float nx[3] = {0.f, 0.f, 0.f}, nv[3] = {0.f, 0.f, 0.f}, nq = 0.f, nw = 0.f;
+    {
+        const uint32_t p = lo + threadIdx.x;
+        if (p < hi) {
+#pragma unroll
+            for (int k = 0; k < DIM; ++k)
+                nx[k] = a.x[k][p];
+#pragma unroll
+            for (int c = 0; c < 3; ++c)
+                nv[c] = a.v[c][p];
+            nq = a.q[p];
+            nw = a.w[p];
+        }
+    }
     for (uint32_t p = lo + threadIdx.x; p < hi; p += blockDim.x) {
-        // all loads first, so they are in flight together
         float xs[3], vv[3];
 #pragma unroll
-        for (int k = 0; k < DIM; ++k)
-            xs[k] = a.x[k][p];
+        for (int k = 0; k < 3; ++k) {
+            xs[k] = nx[k];
+            vv[k] = nv[k];
+        }
+        const float qw = nq * nw;
+        {
+            const uint32_t pn = p + blockDim.x;
+            if (pn < hi) {
 #pragma unroll
-        for (int c = 0; c < 3; ++c)
-            vv[c] = a.v[c][p];
-        const float qw = a.q[p] * a.w[p];
+                for (int k = 0; k < DIM; ++k)
+                    nx[k] = a.x[k][pn];
+#pragma unroll
+                for (int c = 0; c < 3; ++c)
+                    nv[c] = a.v[c][pn];
+                nq = a.q[pn];
+                nw = a.w[pn];
+            }
+        }
 
         float W[3][M];
         int b[3] = {0, 0, 0};
@@ -246,26 +259,34 @@ __global__ __launch_bounds__(256) void k_deposit_tiled(DepArgs a)
                 amp[c] *= scale;
         }
         if (in_lds) {
+            // amp_c * W_x first, then one multiply per (node, component)
+            float ampx[3][M];
+#pragma unroll
+            for (int c = 0; c < 3; ++c)
+#pragma unroll
+                for (int ax = 0; ax < M; ++ax)
+                    ampx[c][ax] = amp[c] * W[0][ax];
+            const int base = DIM == 3 ? (s[2] * TE + s[1]) * TE + s[0]
+                                      : (DIM == 2 ? s[1] * TE + s[0] : s[0]);
 #pragma unroll
             for (int az = 0; az < MZ; ++az) {
 #pragma unroll
                 for (int ay = 0; ay < MY; ++ay) {
-                    const int row = DIM == 3 ? ((s[2] + az) * TE + (s[1] + ay)) * TE
-                                             : (DIM == 2 ? (s[1] + ay) * TE : 0);
+                    const int row = base + (DIM == 3 ? (az * TE + ay) * TE : ay * TE);
                     const float wyz = (DIM > 1 ? W[1][ay] : 1.0f) * (DIM > 2 ? W[2][az] : 1.0f);
 #pragma unroll
                     for (int ax = 0; ax < M; ++ax) {
-                        const int idx = row + s[0] + ax;
-                        const float wt = W[0][ax] * wyz;
+                        const int idx = row + ax;
 #pragma unroll
                         for (int c = 0; c < 3; ++c) {
+                            const float val = ampx[c][ax] * wyz;
                             if (FIXED) {
-                                const long long f = (long long)__float2int_rn(amp[c] * wt);
+                                const long long f = (long long)__float2int_rn(val);
                                 __hip_atomic_fetch_add(&acc64[c * vol + idx],
                                                        (unsigned long long)f, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_WORKGROUP);
                             } else {
-                                __hip_atomic_fetch_add(&acc32[c * vol + idx], amp[c] * wt,
+                                __hip_atomic_fetch_add(&acc32[c * vol + idx], val,
                                                        __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_WORKGROUP);
                             }
@@ -314,50 +335,6 @@ __global__ __launch_bounds__(256) void k_deposit_tiled(DepArgs a)
         atomicAdd(a.n_escaped, (unsigned long long)s_esc);
 }
 
-// Work items per tile: ceil(len/chunk) (0 for an empty tile), exclusive prefix
-// over tiles into cum[0..ntiles]; one work-group.
-__global__ __launch_bounds__(1024) void k_chunk_cum(const uint32_t *__restrict__ off,
-                                                    uint32_t ntiles, int64_t n_part,
-                                                    uint32_t chunk, uint32_t *__restrict__ cum)
-{
-    __shared__ uint32_t wsum[1024 / WAVE];
-    const uint32_t per = (ntiles + 1023) / 1024;
-    const uint32_t t0 = threadIdx.x * per;
-    const uint32_t t1 = min(t0 + per, ntiles);
-    auto items = [&](uint32_t t) -> uint32_t {
-        const uint64_t p0 = std::min<uint64_t>(off[t], (uint64_t)n_part);
-        const uint64_t p1 = std::min<uint64_t>(off[t + 1], (uint64_t)n_part);
-        return p1 > p0 ? (uint32_t)((p1 - p0 + chunk - 1) / chunk) : 0u;
-    };
-    uint32_t s = 0;
-    for (uint32_t t = t0; t < t1; ++t)
-        s += items(t);
-    // block exclusive scan of s
-    const int wave = threadIdx.x / WAVE, lane = lane_id();
-    uint32_t inc = s;
-#pragma unroll
-    for (int o = 1; o < WAVE; o <<= 1) {
-        const uint32_t u = __shfl_up(inc, o, WAVE);
-        if (lane >= o)
-            inc += u;
-    }
-    if (lane == WAVE - 1)
-        wsum[wave] = inc;
-    __syncthreads();
-    uint32_t before = 0, all = 0;
-    for (int w = 0; w < 1024 / WAVE; ++w) {
-        before += w < wave ? wsum[w] : 0u;
-        all += wsum[w];
-    }
-    uint32_t run = before + inc - s;
-    for (uint32_t t = t0; t < t1; ++t) {
-        cum[t] = run;
-        run += items(t);
-    }
-    if (threadIdx.x == 0)
-        cum[ntiles] = all;
-}
-
 template <int DIM, int ORDER>
 pcg_status launch_flat(const DepArgs &a, int64_t begin, int64_t end, hipStream_t st)
 {
@@ -368,11 +345,11 @@ pcg_status launch_flat(const DepArgs &a, int64_t begin, int64_t end, hipStream_t
                   st, a, begin, end);
 }
 
-template <int DIM, int ORDER, bool FIXED>
+template <int DIM, int ORDER, bool FIXED, int TEC>
 pcg_status launch_tiled_impl(const DepArgs &a, uint32_t nwork, int block, size_t lds,
                              hipStream_t st)
 {
-    auto kern = k_deposit_tiled<DIM, ORDER, FIXED>;
+    auto kern = k_deposit_tiled<DIM, ORDER, FIXED, TEC>;
     if (lds > 65536) {
         if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)lds) != hipSuccess)
@@ -381,14 +358,38 @@ pcg_status launch_tiled_impl(const DepArgs &a, uint32_t nwork, int block, size_t
     return launch("deposit_tiled", kern, dim3(nwork), dim3(block), lds, st, a);
 }
 
+constexpr size_t scratch_bytes(int dim, int te, int elem)
+{
+    return (size_t)3 * elem * (dim == 3 ? te * te * te : (dim == 2 ? te * te : te));
+}
+
+// A compile-time scratch edge: int64 fixed-point scratch when it fits the LDS.
+template <int DIM, int ORDER, int TEC>
+pcg_status launch_tiled_te(const DepArgs &a, uint32_t nwork, int block, hipStream_t st)
+{
+    constexpr bool fixed = scratch_bytes(DIM, TEC, 8) <= LDS_LIMIT;
+    return launch_tiled_impl<DIM, ORDER, fixed, TEC>(a, nwork, block,
+                                                     scratch_bytes(DIM, TEC, fixed ? 8 : 4), st);
+}
+
 template <int DIM, int ORDER>
 pcg_status launch_tiled(const DepArgs &a, uint32_t nwork, int block, size_t lds,
                         hipStream_t st)
 {
+    // the window shapes of tiles 4, 8, 16 with drift 1 are compiled with a
+    // constant edge; any other shape uses the runtime-edge kernel
+    if (DIM >= 2 && a.D == 1) {
+        switch (a.TE) {
+        case ORDER == 1 ? 7 : 8: return launch_tiled_te<DIM, ORDER, ORDER == 1 ? 7 : 8>(a, nwork, block, st);
+        case ORDER == 1 ? 11 : 12: return launch_tiled_te<DIM, ORDER, ORDER == 1 ? 11 : 12>(a, nwork, block, st);
+        case ORDER == 1 ? 19 : 20: return launch_tiled_te<DIM, ORDER, ORDER == 1 ? 19 : 20>(a, nwork, block, st);
+        default: break;
+        }
+    }
     // int64 fixed-point scratch when it fits, else fp32 scratch (lds is the fp32 size)
     if (2 * lds <= LDS_LIMIT)
-        return launch_tiled_impl<DIM, ORDER, true>(a, nwork, block, 2 * lds, st);
-    return launch_tiled_impl<DIM, ORDER, false>(a, nwork, block, lds, st);
+        return launch_tiled_impl<DIM, ORDER, true, 0>(a, nwork, block, 2 * lds, st);
+    return launch_tiled_impl<DIM, ORDER, false, 0>(a, nwork, block, lds, st);
 }
 
 pcg_status dispatch(int dim, int order, bool tiled, const DepArgs &a, int64_t begin, int64_t end,
@@ -545,7 +546,8 @@ pcg_status deposit_currents(const pcg_grid *grid, const pcg_particles *particles
         return fail(PCG_EINVAL, "%s: too many work-groups", who);
 
     PCG_TRY(launch("deposit_chunks", k_chunk_cum, dim3(1), dim3(1024), 0, st, a.tile_offsets,
-                   a.ntiles, a.n_part, a.chunk, static_cast<uint32_t *>(workspace)));
+                   a.ntiles, a.n_part, a.chunk, static_cast<uint32_t *>(workspace),
+                   (const uint32_t *)nullptr, 0u));
     PCG_TRY(dispatch(grid->dim, order, true, a, 0, 0, (uint32_t)nwork, block, lds, st));
     // tail pass ([TD] "Coverage: the tail pass")
     return dispatch(grid->dim, order, false, a, tile->n_partitioned, count, 0, 0, 0, st);

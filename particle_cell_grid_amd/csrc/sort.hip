@@ -2,19 +2,34 @@
 // deposit", section "The tile-based spatial sort"; with T = 1 the cell sort the
 // mass-matrix paper's §3.1 assumes).
 //
-// Pipeline on the caller's stream:
-//   1. k_tile_keys      key = tile of the first support node (uint32).
-//   2. LSD radix sort of (key, index) pairs, ceil(bits/8) passes of <= 8 bits:
-//        k_radix_hist     per-block digit histograms, digit-major [R][nblocks];
-//        scan             exclusive prefix over that array (3 kernels);
-//        k_radix_scatter  stable scatter: every wave ranks its 64 keys with
-//                         ballot-based peer masks, the block orders its waves
-//                         and items with per-(slot, digit) counts in LDS.
-//      Each pass is stable, so the composition sorts by key with ties in input
-//      order, i.e. the unique stable permutation.
-//   3. k_tile_offsets   offsets[t] = #keys < t, from key transitions.
-//   4. k_permute        out_a[j] = in_a[perm[j]] for each SoA array.
+// The result is the unique stable permutation by tile key; two paths reach it.
+//
+// Incremental path (the input was tile-sorted by `prev` and its particles have
+// since moved at most one tile -- [TD] "Halo sizing": at most one cell per
+// un-sorted step under CFL).  Every particle's new tile is then one of the 27
+// (fewer on a thin grid) neighbours of the tile whose slice holds it, so the
+// stable order is a counting sort over (source chunk, direction):
+//   k_inc_validate  prev is a partition of [0, count) (else fall back);
+//   k_chunk_cum     source slices split into balanced chunks;
+//   k_inc_count     per chunk, particles per direction (a particle that moved
+//                   further raises the fall-back flag);
+//   k_inc_totals    per new tile, the sum over its source (chunk, direction)s;
+//   scan            -> tile offsets;
+//   k_inc_bases     per new tile, running prefix over its sources in source
+//                   order -> output base of every (chunk, direction);
+//   k_inc_scatter   per chunk, stable ranks by direction (wave ballots), one
+//                   coalesced read and one write of every SoA array.
+// General path (no `prev`, or the flag is raised):
+//   k_tile_keys; LSD radix sort of (key, index) in ceil(bits/8) passes of
+//   <= 8 bits (per-block digit histograms, a scan, a stable scatter ranking
+//   each wave's keys with ballot peer masks); k_tile_offsets from key
+//   transitions; k_permute gathers the SoA arrays.
+// Both paths are enqueued when `prev` is given; a device flag makes the kernels
+// of the path not taken return at once, so the call stays asynchronous.
+#include <algorithm>
+
 #include "common.hpp"
+#include "layout.hpp"
 
 namespace pcg {
 namespace {
@@ -27,13 +42,37 @@ constexpr int SCAN_BLOCK = 256;
 constexpr int SCAN_IPT = 16;
 constexpr int SCAN_TILE = SCAN_BLOCK * SCAN_IPT;
 constexpr int MAX_ARRAYS = 16;
+constexpr int NDIR = 27;            // neighbour directions of the incremental path
+constexpr uint32_t INC_CHUNK = 2048;  // particles per chunk of the incremental path
+
+// A kernel runs only if `flag` is NULL or *flag == run.
+struct Gate {
+    const uint32_t *flag;
+    uint32_t run;
+};
+__device__ inline bool gated_off(const Gate &g) { return g.flag && *g.flag != g.run; }
 
 struct KeyGeom {
     int n[3];
+    float nf[3];
     int nt[3];
     int T;
     int T_shift;  // log2(T) if T is a power of two, else -1
 };
+
+// Tile coordinate of a particle along one axis: the tile holding its first
+// support node (wrapped).
+template <int ORDER>
+__device__ inline int tile_coord(float xraw, const KeyGeom &g, int k)
+{
+    const float xf = clamp_coord(xraw, g.nf[k]);
+    const float fl = floorf(xf);
+    int b = (int)fl;
+    if (ORDER == 2 && (xf - fl) < 0.5f)
+        b -= 1;
+    b = wrap_index(b, g.n[k]);
+    return g.T_shift >= 0 ? (b >> g.T_shift) : (b / g.T);
+}
 
 // ----------------------------------------------------------------- keys
 
@@ -41,22 +80,17 @@ template <int DIM, int ORDER>
 __global__ __launch_bounds__(256) void k_tile_keys(int64_t count, const float *__restrict__ x0,
                                                    const float *__restrict__ x1,
                                                    const float *__restrict__ x2, KeyGeom g,
-                                                   uint32_t *__restrict__ keys)
+                                                   uint32_t *__restrict__ keys, Gate gate)
 {
+    if (gated_off(gate))
+        return;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
         const float *xs[3] = {x0, x1, x2};
         uint32_t key = 0, mul = 1;
 #pragma unroll
         for (int k = 0; k < DIM; ++k) {
-            float xf = clamp_coord(xs[k][i], (float)g.n[k]);
-            float fl = floorf(xf);
-            int b = (int)fl;
-            if (ORDER == 2 && (xf - fl) < 0.5f)
-                b -= 1;
-            b = wrap_index(b, g.n[k]);
-            int t = g.T_shift >= 0 ? (b >> g.T_shift) : (b / g.T);
-            key += mul * (uint32_t)t;
+            key += mul * (uint32_t)tile_coord<ORDER>(xs[k][i], g, k);
             mul *= (uint32_t)g.nt[k];
         }
         keys[i] = key;
@@ -83,8 +117,10 @@ template <int BITS>
 __global__ __launch_bounds__(SORT_BLOCK) void k_radix_hist(const uint32_t *__restrict__ keys,
                                                            int64_t count, int shift,
                                                            uint32_t *__restrict__ counts,
-                                                           uint32_t nblocks)
+                                                           uint32_t nblocks, Gate gate)
 {
+    if (gated_off(gate))
+        return;
     constexpr uint32_t R = 1u << BITS;
     __shared__ uint32_t hist[R];
     for (uint32_t d = threadIdx.x; d < R; d += SORT_BLOCK)
@@ -110,8 +146,10 @@ template <int BITS>
 __global__ __launch_bounds__(SORT_BLOCK) void k_radix_scatter(
     const uint32_t *__restrict__ keys_in, const uint32_t *__restrict__ vals_in,
     uint32_t *__restrict__ keys_out, uint32_t *__restrict__ vals_out, int64_t count, int shift,
-    const uint32_t *__restrict__ offsets, uint32_t nblocks)
+    const uint32_t *__restrict__ offsets, uint32_t nblocks, Gate gate)
 {
+    if (gated_off(gate))
+        return;
     constexpr uint32_t R = 1u << BITS;
     __shared__ uint16_t cnt[SORT_SLOTS][R];  // items of digit d in wave-slot s, then prefix
     __shared__ uint32_t gbase[R];
@@ -206,8 +244,11 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t *total)
 
 __global__ __launch_bounds__(SCAN_BLOCK) void k_scan_reduce(const uint32_t *__restrict__ in,
                                                             size_t len,
-                                                            uint32_t *__restrict__ partial)
+                                                            uint32_t *__restrict__ partial,
+                                                            Gate gate)
 {
+    if (gated_off(gate))
+        return;
     const size_t base = (size_t)blockIdx.x * SCAN_TILE;
     uint32_t s = 0;
     for (int j = 0; j < SCAN_IPT; ++j) {
@@ -223,8 +264,10 @@ __global__ __launch_bounds__(SCAN_BLOCK) void k_scan_reduce(const uint32_t *__re
 
 // Single work-group exclusive scan of the partial sums (in place).
 __global__ __launch_bounds__(1024) void k_scan_partials(uint32_t *__restrict__ partial,
-                                                        uint32_t nparts)
+                                                        uint32_t nparts, Gate gate)
 {
+    if (gated_off(gate))
+        return;
     const uint32_t per = (nparts + 1023) / 1024;
     const uint32_t lo = threadIdx.x * per;
     const uint32_t hi = min(lo + per, nparts);
@@ -241,8 +284,11 @@ __global__ __launch_bounds__(1024) void k_scan_partials(uint32_t *__restrict__ p
 }
 
 __global__ __launch_bounds__(SCAN_BLOCK) void k_scan_down(uint32_t *__restrict__ data, size_t len,
-                                                          const uint32_t *__restrict__ partial)
+                                                          const uint32_t *__restrict__ partial,
+                                                          Gate gate)
 {
+    if (gated_off(gate))
+        return;
     // thread t owns SCAN_IPT consecutive elements of the block's tile
     const size_t base = (size_t)blockIdx.x * SCAN_TILE + (size_t)threadIdx.x * SCAN_IPT;
     uint32_t v[SCAN_IPT];
@@ -262,15 +308,16 @@ __global__ __launch_bounds__(SCAN_BLOCK) void k_scan_down(uint32_t *__restrict__
     }
 }
 
-pcg_status exclusive_scan(uint32_t *data, size_t len, uint32_t *partial, hipStream_t st)
+pcg_status exclusive_scan(uint32_t *data, size_t len, uint32_t *partial, Gate gate,
+                          hipStream_t st)
 {
     const uint32_t nparts = (uint32_t)((len + SCAN_TILE - 1) / SCAN_TILE);
     PCG_TRY(launch("sort_scan_reduce", k_scan_reduce, dim3(nparts), dim3(SCAN_BLOCK), 0, st,
-                   (const uint32_t *)data, len, partial));
+                   (const uint32_t *)data, len, partial, gate));
     PCG_TRY(launch("sort_scan_partials", k_scan_partials, dim3(1), dim3(1024), 0, st, partial,
-                   nparts));
+                   nparts, gate));
     PCG_TRY(launch("sort_scan_down", k_scan_down, dim3(nparts), dim3(SCAN_BLOCK), 0, st, data,
-                   len, (const uint32_t *)partial));
+                   len, (const uint32_t *)partial, gate));
     return PCG_OK;
 }
 
@@ -278,11 +325,13 @@ pcg_status exclusive_scan(uint32_t *data, size_t len, uint32_t *partial, hipStre
 
 __global__ __launch_bounds__(256) void k_tile_offsets(const uint32_t *__restrict__ sk,
                                                       int64_t count, uint32_t ntiles,
-                                                      uint32_t *__restrict__ off)
+                                                      uint32_t *__restrict__ off, Gate gate)
 {
+    if (gated_off(gate))
+        return;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i <= count; i += stride) {
-        // tiles t in (sk[i-1], sk[i]] start at slot i (with sk[-1] = -1, sk[count] = ntiles)
+        // tiles t in (sk[i-1], sk[i]] start at slot i (sk[-1] = -1, sk[count] = ntiles)
         const uint32_t lo = (i == 0) ? 0u : sk[i - 1] + 1u;
         const uint32_t hi = (i == count) ? ntiles : sk[i];
         for (uint32_t t = lo; t <= hi && t <= ntiles; ++t)
@@ -296,21 +345,360 @@ struct PermArgs {
     int n;
 };
 
+constexpr int PERM_EPT = 4;  // elements per thread: all index loads, then all gathers
+
 __global__ __launch_bounds__(256) void k_permute(PermArgs a, const uint32_t *__restrict__ perm,
-                                                 int64_t count)
+                                                 int64_t count, Gate gate)
 {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
-        const uint32_t p = min(perm[i], (uint32_t)(count - 1));  // perm is a permutation
-        float v[MAX_ARRAYS];
+    if (gated_off(gate))
+        return;
+    for (int64_t blk = blockIdx.x; blk * 256 * PERM_EPT < count; blk += gridDim.x) {
+    const int64_t i0 = (blk * PERM_EPT) * 256 + threadIdx.x;
+    uint32_t p[PERM_EPT];
 #pragma unroll
-        for (int k = 0; k < MAX_ARRAYS; ++k)
-            if (k < a.n)
-                v[k] = a.in[k][p];
+    for (int e = 0; e < PERM_EPT; ++e) {
+        const int64_t i = i0 + e * 256;
+        // perm is a permutation of [0, count); the clamp only keeps a broken one in bounds
+        p[e] = i < count ? min(perm[i], (uint32_t)(count - 1)) : 0u;
+    }
+    for (int k = 0; k < a.n; ++k) {
+        float v[PERM_EPT];
 #pragma unroll
-        for (int k = 0; k < MAX_ARRAYS; ++k)
-            if (k < a.n)
-                a.out[k][i] = v[k];
+        for (int e = 0; e < PERM_EPT; ++e)
+            v[e] = a.in[k][p[e]];
+#pragma unroll
+        for (int e = 0; e < PERM_EPT; ++e) {
+            const int64_t i = i0 + e * 256;
+            if (i < count)
+                a.out[k][i] = v[e];
+        }
+    }
+    }
+}
+
+// ----------------------------------------------------------------- incremental path
+
+__global__ void k_set_flag(uint32_t *flag, uint32_t v)
+{
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        *flag = v;
+}
+
+// prev must be a partition of [0, count): off[0] = 0, non-decreasing,
+// off[ntiles] = count.  Anything else falls back to the general path.
+__global__ __launch_bounds__(256) void k_inc_validate(const uint32_t *__restrict__ off,
+                                                      uint32_t ntiles, int64_t count,
+                                                      uint32_t *flag)
+{
+    const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t > ntiles)
+        return;
+    bool bad = false;
+    if (t == 0)
+        bad = off[0] != 0u;
+    else
+        bad = off[t] < off[t - 1];
+    if (t == ntiles)
+        bad = bad || (int64_t)off[ntiles] != count;
+    if (bad)
+        atomicOr(flag, 1u);
+}
+
+struct IncGeom {
+    KeyGeom g;
+    uint32_t ntiles;
+    const uint32_t *prev_off;
+    int64_t count;
+    const uint32_t *cum;
+    uint32_t *cnt;    // [nchunks][NDIR] particles per direction; then prefix over chunks
+    uint32_t *tcnt;   // [ntiles][NDIR] per source tile
+    uint32_t *tpre;   // [ntiles][NDIR] prefix over a new tile's sources
+    uint32_t *code;   // [count] direction << 27 | rank among the chunk's same-direction ones
+    uint32_t *flag;
+};
+
+// Direction index of the new tile coordinate t relative to source s on one
+// axis of nt tiles: 0, 1, 2 for -1, 0, +1; -1 if further.  On an axis of two
+// tiles only 0 and +1 are distinct, on an axis of one tile only 0.
+__device__ inline int axis_dir(int t, int s, int nt)
+{
+    int d = t - s;
+    if (d < 0)
+        d += nt;
+    if (d == 0)
+        return 1;
+    if (d == 1)
+        return 2;
+    if (d == nt - 1)
+        return 0;
+    return -1;
+}
+
+template <int DIM, int ORDER>
+__device__ inline int particle_dir(float x0, float x1, float x2, const KeyGeom &g, const int *sc)
+{
+    const float xs[3] = {x0, x1, x2};
+    int dir = 0, mul = 1;
+    bool far = false;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        int d = 1;  // unused axes: direction 0
+        if (k < DIM) {
+            d = axis_dir(tile_coord<ORDER>(xs[k], g, k), sc[k], g.nt[k]);
+            far |= d < 0;
+        }
+        dir += mul * (d < 0 ? 0 : d);
+        mul *= 3;
+    }
+    return far ? -1 : dir;
+}
+
+__device__ inline void tile_coords(uint32_t t, const KeyGeom &g, int *c)
+{
+    c[0] = (int)(t % (uint32_t)g.nt[0]);
+    c[1] = (int)((t / (uint32_t)g.nt[0]) % (uint32_t)g.nt[1]);
+    c[2] = (int)(t / ((uint32_t)g.nt[0] * (uint32_t)g.nt[1]));
+}
+
+__device__ inline uint32_t tile_index(const int *c, const KeyGeom &g)
+{
+    return (uint32_t)c[0] + (uint32_t)g.nt[0] * ((uint32_t)c[1] + (uint32_t)g.nt[1] * (uint32_t)c[2]);
+}
+
+// New tile reached from source coordinates sc by direction dir.
+__device__ inline uint32_t dest_tile(const int *sc, int dir, const KeyGeom &g)
+{
+    int c[3];
+    c[0] = wrap_index(sc[0] + dir % 3 - 1, g.nt[0]);
+    c[1] = wrap_index(sc[1] + (dir / 3) % 3 - 1, g.nt[1]);
+    c[2] = wrap_index(sc[2] + dir / 9 - 1, g.nt[2]);
+    return tile_index(c, g);
+}
+
+// One wave per chunk, walking it in order 64 particles at a time: every
+// particle gets its direction and its rank among the chunk's particles of that
+// direction (stable), and the chunk's per-direction totals are written.
+template <int DIM, int ORDER>
+__global__ __launch_bounds__(64) void k_inc_rank(IncGeom a, const float *x0, const float *x1,
+                                                 const float *x2)
+{
+    if (*a.flag != 0u)
+        return;
+    __shared__ uint32_t s_tile, s_lo, s_hi;
+    __shared__ uint32_t s_run[32];
+    if (threadIdx.x == 0) {
+        const ChunkRange r = find_chunk(blockIdx.x, a.cum, a.ntiles, a.prev_off, a.count);
+        s_tile = r.tile;
+        s_lo = r.lo;
+        s_hi = r.hi;
+    }
+    if (threadIdx.x < 32)
+        s_run[threadIdx.x] = 0;
+    __syncthreads();
+    if (s_tile == UINT_MAX)
+        return;
+    int sc[3];
+    tile_coords(s_tile, a.g, sc);
+    const uint32_t lo = s_lo, hi = s_hi;
+    bool far = false;
+    // software pipeline: the next batch's coordinates load while this one ranks
+    uint32_t p = lo + threadIdx.x;
+    float c0 = 0.f, c1 = 0.f, c2 = 0.f;
+    if (p < hi) {
+        c0 = x0[p];
+        c1 = DIM > 1 ? x1[p] : 0.f;
+        c2 = DIM > 2 ? x2[p] : 0.f;
+    }
+    for (uint32_t b = lo; b < hi; b += 64) {
+        const bool valid = p < hi;
+        const uint32_t pn = p + 64;
+        float n0 = 0.f, n1 = 0.f, n2 = 0.f;
+        if (pn < hi) {
+            n0 = x0[pn];
+            n1 = DIM > 1 ? x1[pn] : 0.f;
+            n2 = DIM > 2 ? x2[pn] : 0.f;
+        }
+        int dir = valid ? particle_dir<DIM, ORDER>(c0, c1, c2, a.g, sc) : 0;
+        far |= valid && dir < 0;
+        const bool ok = valid && dir >= 0;
+        if (!ok)
+            dir = 0;
+        const uint64_t peers = peer_mask<5>((uint32_t)dir, ok);
+        const uint32_t rank = (uint32_t)__popcll(peers & lanemask_lt());
+        // all lanes read the running counts, then each group's first lane
+        // advances its direction's count (a single wave: LDS runs in order)
+        const uint32_t before = s_run[dir];
+        __builtin_amdgcn_wave_barrier();
+        if (ok && rank == 0)
+            s_run[dir] = before + (uint32_t)__popcll(peers);
+        __builtin_amdgcn_wave_barrier();
+        if (ok)
+            a.code[p] = ((uint32_t)dir << 27) | (before + rank);
+        p = pn;
+        c0 = n0;
+        c1 = n1;
+        c2 = n2;
+    }
+    if (__ballot(far))
+        if (threadIdx.x == 0)
+            atomicOr(a.flag, 1u);
+    __syncthreads();
+    if (threadIdx.x < NDIR)
+        a.cnt[(size_t)blockIdx.x * NDIR + threadIdx.x] = s_run[threadIdx.x];
+}
+
+// Thread per (source tile, direction): exclusive prefix of the counts over the
+// tile's chunks (in place) and the tile's total.
+__global__ __launch_bounds__(256) void k_inc_chunk_prefix(IncGeom a)
+{
+    if (*a.flag != 0u)
+        return;
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= a.ntiles * (uint32_t)NDIR)
+        return;
+    const uint32_t s = i / NDIR, d = i % NDIR;
+    uint32_t run = 0;
+    for (uint32_t c = a.cum[s]; c < a.cum[s + 1]; ++c) {
+        const size_t j = (size_t)c * NDIR + d;
+        const uint32_t v = a.cnt[j];
+        a.cnt[j] = run;
+        run += v;
+    }
+    a.tcnt[i] = run;
+}
+
+// The distinct source coordinates of new-tile coordinate tc on one axis of nt
+// tiles, ascending, with the direction index (0, 1, 2 for -1, 0, +1) that
+// leads from each to tc.  Returns how many (1, 2 or 3).
+__device__ inline int axis_sources(int tc, int nt, int *c, int *d)
+{
+    if (nt == 1) {
+        c[0] = tc;
+        d[0] = 1;
+        return 1;
+    }
+    // source tc - delta for delta = +1, 0 (and -1 when nt >= 3)
+    int n = 0;
+    int cc[3], dd[3];
+    cc[n] = wrap_index(tc - 1, nt);
+    dd[n++] = 2;
+    cc[n] = tc;
+    dd[n++] = 1;
+    if (nt >= 3) {
+        cc[n] = wrap_index(tc + 1, nt);
+        dd[n++] = 0;
+    }
+    // sort <= 3 entries by coordinate
+    for (int i = 0; i < n; ++i)
+        for (int j = i + 1; j < n; ++j)
+            if (cc[j] < cc[i]) {
+                int t = cc[i];
+                cc[i] = cc[j];
+                cc[j] = t;
+                t = dd[i];
+                dd[i] = dd[j];
+                dd[j] = t;
+            }
+    for (int i = 0; i < n; ++i) {
+        c[i] = cc[i];
+        d[i] = dd[i];
+    }
+    return n;
+}
+
+// Thread per new tile: its particle count (scan input) and, in source order
+// (ascending linear index = lexicographic in z, y, x), the prefix of every
+// source's share.
+__global__ __launch_bounds__(256) void k_inc_tiles(IncGeom a, uint32_t *__restrict__ totals)
+{
+    if (*a.flag != 0u)
+        return;
+    const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t > a.ntiles)
+        return;
+    if (t == a.ntiles) {
+        totals[t] = 0;
+        return;
+    }
+    int tc[3];
+    tile_coords(t, a.g, tc);
+    int cx[3], dx[3], cy[3], dy[3], cz[3], dz[3];
+    const int nx = axis_sources(tc[0], a.g.nt[0], cx, dx);
+    const int ny = axis_sources(tc[1], a.g.nt[1], cy, dy);
+    const int nz = axis_sources(tc[2], a.g.nt[2], cz, dz);
+    uint32_t run = 0;
+    for (int iz = 0; iz < nz; ++iz)
+        for (int iy = 0; iy < ny; ++iy)
+            for (int ix = 0; ix < nx; ++ix) {
+                const int c[3] = {cx[ix], cy[iy], cz[iz]};
+                const size_t j = (size_t)tile_index(c, a.g) * NDIR + dx[ix] + 3 * dy[iy] + 9 * dz[iz];
+                a.tpre[j] = run;
+                run += a.tcnt[j];
+            }
+    totals[t] = run;
+}
+
+// One work-group per chunk, no ordering left: each particle's slot is
+// off[new tile] + tile prefix + chunk prefix + rank.
+template <int DIM>
+__global__ __launch_bounds__(256) void k_inc_move(IncGeom a, const uint32_t *__restrict__ off,
+                                                  PermArgs arr, uint32_t *__restrict__ perm,
+                                                  uint32_t *__restrict__ keys)
+{
+    if (*a.flag != 0u)
+        return;
+    __shared__ uint32_t s_tile, s_lo, s_hi;
+    __shared__ uint32_t s_base[NDIR], s_dest[NDIR];
+    if (threadIdx.x == 0) {
+        const ChunkRange r = find_chunk(blockIdx.x, a.cum, a.ntiles, a.prev_off, a.count);
+        s_tile = r.tile;
+        s_lo = r.lo;
+        s_hi = r.hi;
+    }
+    __syncthreads();
+    if (s_tile == UINT_MAX)
+        return;
+    if (threadIdx.x < NDIR) {
+        const int d = threadIdx.x;
+        int sc[3];
+        tile_coords(s_tile, a.g, sc);
+        const uint32_t t = dest_tile(sc, d, a.g);
+        const size_t j = (size_t)s_tile * NDIR + d;
+        s_dest[d] = t;
+        s_base[d] = off[t] + a.tpre[j] + a.cnt[(size_t)blockIdx.x * NDIR + d];
+    }
+    __syncthreads();
+    constexpr int EPT = 4;
+    for (uint32_t b = s_lo; b < s_hi; b += 256 * EPT) {
+        uint32_t pos[EPT], p[EPT];
+        bool ok[EPT];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            p[e] = b + e * 256 + threadIdx.x;
+            ok[e] = p[e] < s_hi;
+            const uint32_t c = ok[e] ? a.code[p[e]] : 0u;
+            const uint32_t d = c >> 27;
+            pos[e] = s_base[d < NDIR ? d : 0] + (c & ((1u << 27) - 1));
+            ok[e] = ok[e] && d < NDIR && pos[e] < (uint64_t)a.count;
+            if (ok[e] && keys)
+                keys[pos[e]] = s_dest[d];
+        }
+        if (perm) {
+#pragma unroll
+            for (int e = 0; e < EPT; ++e)
+                if (ok[e])
+                    perm[pos[e]] = p[e];
+        }
+        for (int k = 0; k < arr.n; ++k) {
+            float v[EPT];
+#pragma unroll
+            for (int e = 0; e < EPT; ++e)
+                v[e] = ok[e] ? arr.in[k][p[e]] : 0.f;
+#pragma unroll
+            for (int e = 0; e < EPT; ++e)
+                if (ok[e])
+                    arr.out[k][pos[e]] = v[e];
+        }
     }
 }
 
@@ -324,6 +712,7 @@ struct SortPlan {
     int bits = 1;
     uint32_t nblocks = 0;
     size_t counts_len = 0;
+    uint32_t nchunks_max = 0;
 };
 
 SortPlan make_plan(const pcg_grid *grid, int64_t count, int T)
@@ -342,11 +731,13 @@ SortPlan make_plan(const pcg_grid *grid, int64_t count, int T)
     p.bits = kb == 0 ? 1 : (kb + p.passes - 1) / p.passes;
     p.nblocks = (uint32_t)((count + SORT_TILE - 1) / SORT_TILE);
     p.counts_len = (size_t)(1u << p.bits) * p.nblocks;
+    p.nchunks_max = p.ntiles + (uint32_t)((count + INC_CHUNK - 1) / INC_CHUNK);
     return p;
 }
 
 struct SortBuffers {
-    uint32_t *k0, *ak, *av, *bv, *fk, *counts, *partial;
+    uint32_t *k0, *ak, *av, *bv, *fk, *pm, *counts, *partial;
+    uint32_t *flag, *cum, *cnt, *tcnt, *tpre;
 };
 
 size_t carve(const SortPlan &p, void *ws, SortBuffers *b)
@@ -358,8 +749,15 @@ size_t carve(const SortPlan &p, void *ws, SortBuffers *b)
     b->av = c.take<uint32_t>(n);
     b->bv = c.take<uint32_t>(n);
     b->fk = c.take<uint32_t>(n);
+    b->pm = c.take<uint32_t>(n);
     b->counts = c.take<uint32_t>(p.counts_len);
-    b->partial = c.take<uint32_t>((p.counts_len + SCAN_TILE - 1) / SCAN_TILE + 1);
+    const size_t scan_len = std::max(p.counts_len, (size_t)p.ntiles + 1);
+    b->partial = c.take<uint32_t>((scan_len + SCAN_TILE - 1) / SCAN_TILE + 1);
+    b->flag = c.take<uint32_t>(1);
+    b->cum = c.take<uint32_t>((size_t)p.ntiles + 1);
+    b->cnt = c.take<uint32_t>((size_t)p.nchunks_max * NDIR);
+    b->tcnt = c.take<uint32_t>((size_t)p.ntiles * NDIR);
+    b->tpre = c.take<uint32_t>((size_t)p.ntiles * NDIR);
     return c.used;
 }
 
@@ -379,42 +777,103 @@ pcg_status check_sort_args(const pcg_grid *grid, int64_t count, int T, const cha
 
 template <int BITS>
 pcg_status radix_pass(const SortPlan &p, int shift, const uint32_t *kin, const uint32_t *vin,
-                      uint32_t *kout, uint32_t *vout, const SortBuffers &b, hipStream_t st)
+                      uint32_t *kout, uint32_t *vout, const SortBuffers &b, Gate gate,
+                      hipStream_t st)
 {
     PCG_TRY(launch("sort_hist", k_radix_hist<BITS>, dim3(p.nblocks), dim3(SORT_BLOCK), 0, st,
-                   kin, p.count, shift, b.counts, p.nblocks));
-    PCG_TRY(exclusive_scan(b.counts, p.counts_len, b.partial, st));
+                   kin, p.count, shift, b.counts, p.nblocks, gate));
+    PCG_TRY(exclusive_scan(b.counts, p.counts_len, b.partial, gate, st));
     PCG_TRY(launch("sort_scatter", k_radix_scatter<BITS>, dim3(p.nblocks), dim3(SORT_BLOCK), 0,
                    st, kin, vin, kout, vout, p.count, shift, (const uint32_t *)b.counts,
-                   p.nblocks));
+                   p.nblocks, gate));
     return PCG_OK;
 }
 
 pcg_status radix_pass_dispatch(int bits, const SortPlan &p, int shift, const uint32_t *kin,
                                const uint32_t *vin, uint32_t *kout, uint32_t *vout,
-                               const SortBuffers &b, hipStream_t st)
+                               const SortBuffers &b, Gate gate, hipStream_t st)
 {
     switch (bits) {
-    case 1: return radix_pass<1>(p, shift, kin, vin, kout, vout, b, st);
-    case 2: return radix_pass<2>(p, shift, kin, vin, kout, vout, b, st);
-    case 3: return radix_pass<3>(p, shift, kin, vin, kout, vout, b, st);
-    case 4: return radix_pass<4>(p, shift, kin, vin, kout, vout, b, st);
-    case 5: return radix_pass<5>(p, shift, kin, vin, kout, vout, b, st);
-    case 6: return radix_pass<6>(p, shift, kin, vin, kout, vout, b, st);
-    case 7: return radix_pass<7>(p, shift, kin, vin, kout, vout, b, st);
-    case 8: return radix_pass<8>(p, shift, kin, vin, kout, vout, b, st);
+    case 1: return radix_pass<1>(p, shift, kin, vin, kout, vout, b, gate, st);
+    case 2: return radix_pass<2>(p, shift, kin, vin, kout, vout, b, gate, st);
+    case 3: return radix_pass<3>(p, shift, kin, vin, kout, vout, b, gate, st);
+    case 4: return radix_pass<4>(p, shift, kin, vin, kout, vout, b, gate, st);
+    case 5: return radix_pass<5>(p, shift, kin, vin, kout, vout, b, gate, st);
+    case 6: return radix_pass<6>(p, shift, kin, vin, kout, vout, b, gate, st);
+    case 7: return radix_pass<7>(p, shift, kin, vin, kout, vout, b, gate, st);
+    case 8: return radix_pass<8>(p, shift, kin, vin, kout, vout, b, gate, st);
     default: return fail(PCG_EUNSUPPORTED, "radix pass of %d bits", bits);
     }
 }
 
 template <int DIM, int ORDER>
 pcg_status launch_keys(int64_t count, const float *const x[3], const KeyGeom &g, uint32_t *keys,
-                       hipStream_t st)
+                       Gate gate, hipStream_t st)
 {
     const int64_t blocks = std::min<int64_t>((count + 255) / 256, (int64_t)device_cus() * 32);
     return launch("sort_keys", k_tile_keys<DIM, ORDER>, dim3((unsigned)std::max<int64_t>(blocks, 1)),
                   dim3(256), 0, st, count, x[0], DIM > 1 ? x[1] : nullptr,
-                  DIM > 2 ? x[2] : nullptr, g, keys);
+                  DIM > 2 ? x[2] : nullptr, g, keys, gate);
+}
+
+pcg_status general_path(const pcg_grid *grid, int order, const SortPlan &p, const KeyGeom &g,
+                        const float *const key_x[3], const PermArgs &arr, uint32_t *perm,
+                        uint32_t *sorted_keys, uint32_t *tile_offsets, const SortBuffers &b,
+                        Gate gate, hipStream_t st)
+{
+    const int64_t count = p.count;
+    const int key = grid->dim * 10 + order;
+    pcg_status s = PCG_OK;
+    switch (key) {
+    case 11: s = launch_keys<1, 1>(count, key_x, g, b.k0, gate, st); break;
+    case 12: s = launch_keys<1, 2>(count, key_x, g, b.k0, gate, st); break;
+    case 21: s = launch_keys<2, 1>(count, key_x, g, b.k0, gate, st); break;
+    case 22: s = launch_keys<2, 2>(count, key_x, g, b.k0, gate, st); break;
+    case 31: s = launch_keys<3, 1>(count, key_x, g, b.k0, gate, st); break;
+    case 32: s = launch_keys<3, 2>(count, key_x, g, b.k0, gate, st); break;
+    }
+    PCG_TRY(s);
+    uint32_t *final_keys = sorted_keys ? sorted_keys : b.fk;
+    if (!perm)
+        perm = b.pm;  // the last radix pass needs somewhere to put the permutation
+    const uint32_t *kin = b.k0;
+    const uint32_t *vin = nullptr;  // pass 0 ranks input indices
+    for (int pass = 0; pass < p.passes; ++pass) {
+        const bool last = pass == p.passes - 1;
+        uint32_t *kout = last ? final_keys : (pass % 2 == 0 ? b.ak : b.k0);
+        uint32_t *vout = last ? perm : (pass % 2 == 0 ? b.av : b.bv);
+        PCG_TRY(radix_pass_dispatch(p.bits, p, pass * p.bits, kin, vin, kout, vout, b, gate, st));
+        kin = kout;
+        vin = vout;
+    }
+    const int64_t oblocks = std::min<int64_t>((count + 1 + 255) / 256, (int64_t)device_cus() * 32);
+    PCG_TRY(launch("sort_offsets", k_tile_offsets, dim3((unsigned)oblocks), dim3(256), 0, st,
+                   (const uint32_t *)final_keys, count, p.ntiles, tile_offsets, gate));
+    if (arr.n > 0) {
+        const int64_t blocks = std::min<int64_t>((count + 256 * PERM_EPT - 1) / (256 * PERM_EPT),
+                                                 (int64_t)device_cus() * 32);
+        PCG_TRY(launch("sort_permute", k_permute, dim3((unsigned)blocks), dim3(256), 0, st, arr,
+                       (const uint32_t *)perm, count, gate));
+    }
+    return PCG_OK;
+}
+
+template <int DIM, int ORDER>
+pcg_status incremental_launch(const IncGeom &a, const float *const key_x[3], uint32_t nwork,
+                              const PermArgs &arr, uint32_t *perm, uint32_t *keys,
+                              uint32_t *tile_offsets, const SortBuffers &b, hipStream_t st)
+{
+    const float *x1 = DIM > 1 ? key_x[1] : nullptr, *x2 = DIM > 2 ? key_x[2] : nullptr;
+    PCG_TRY(launch("sort_inc_rank", k_inc_rank<DIM, ORDER>, dim3(nwork), dim3(64), 0, st, a,
+                   key_x[0], x1, x2));
+    PCG_TRY(launch("sort_inc_chunk_prefix", k_inc_chunk_prefix,
+                   dim3((a.ntiles * NDIR + 255) / 256), dim3(256), 0, st, a));
+    PCG_TRY(launch("sort_inc_tiles", k_inc_tiles, dim3((a.ntiles + 1 + 255) / 256), dim3(256), 0,
+                   st, a, tile_offsets));
+    PCG_TRY(exclusive_scan(tile_offsets, (size_t)a.ntiles + 1, b.partial, Gate{b.flag, 0u}, st));
+    PCG_TRY(launch("sort_inc_move", k_inc_move<DIM>, dim3(nwork), dim3(256), 0, st, a,
+                   (const uint32_t *)tile_offsets, arr, perm, keys));
+    return PCG_OK;
 }
 
 }  // namespace
@@ -437,7 +896,8 @@ pcg_status pcg_tile_sort(const pcg_grid *grid, int32_t order, int32_t T, int64_t
                          const float *const key_x[3], int32_t n_arrays,
                          const float *const in_arrays[], float *const out_arrays[],
                          uint32_t *perm, uint32_t *sorted_keys, uint32_t *tile_offsets,
-                         void *workspace, size_t workspace_bytes, void *stream)
+                         const pcg_tile *prev, void *workspace, size_t workspace_bytes,
+                         void *stream)
 {
     const char *who = "pcg_tile_sort";
     clear_error();
@@ -459,8 +919,17 @@ pcg_status pcg_tile_sort(const pcg_grid *grid, int32_t order, int32_t T, int64_t
         if ((const void *)in_arrays[i] == (const void *)out_arrays[i])
             return fail(PCG_EINVAL, "%s: array %d is permuted in place (out == in)", who, i);
     }
-    if ((!perm && count > 0) || !tile_offsets)
-        return fail(PCG_EINVAL, "%s: perm or tile_offsets is NULL", who);
+    if (!tile_offsets)
+        return fail(PCG_EINVAL, "%s: tile_offsets is NULL", who);
+    if (prev) {
+        if (prev->T != T || prev->order != order)
+            return fail(PCG_EINVAL, "%s: prev layout has T = %d, order = %d; sorting with T = %d,"
+                        " order = %d", who, prev->T, prev->order, T, order);
+        if (!prev->tile_offsets)
+            return fail(PCG_EINVAL, "%s: prev->tile_offsets is NULL", who);
+        if ((const void *)prev->tile_offsets == (const void *)tile_offsets)
+            return fail(PCG_EINVAL, "%s: prev->tile_offsets must differ from tile_offsets", who);
+    }
     SortPlan p = make_plan(grid, count, T);
     SortBuffers b;
     const size_t need = carve(p, nullptr, &b);
@@ -471,15 +940,17 @@ pcg_status pcg_tile_sort(const pcg_grid *grid, int32_t order, int32_t T, int64_t
         return fail(PCG_EWORKSPACE, "%s: workspace must be 256-byte aligned", who);
     carve(p, workspace, &b);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const Gate always{nullptr, 0u};
 
     if (count == 0) {
         return launch("sort_offsets", k_tile_offsets, dim3(1), dim3(256), 0, st,
-                      (const uint32_t *)nullptr, count, p.ntiles, tile_offsets);
+                      (const uint32_t *)nullptr, count, p.ntiles, tile_offsets, always);
     }
 
     KeyGeom g;
     for (int k = 0; k < 3; ++k) {
         g.n[k] = grid->n[k];
+        g.nf[k] = (float)grid->n[k];
         g.nt[k] = k < grid->dim ? grid->n[k] / T : 1;
     }
     g.T = T;
@@ -487,46 +958,51 @@ pcg_status pcg_tile_sort(const pcg_grid *grid, int32_t order, int32_t T, int64_t
     for (int s = 0; s < 31; ++s)
         if ((1 << s) == T)
             g.T_shift = s;
-    const int key = grid->dim * 10 + order;
-    pcg_status s = PCG_OK;
-    switch (key) {
-    case 11: s = launch_keys<1, 1>(count, key_x, g, b.k0, st); break;
-    case 12: s = launch_keys<1, 2>(count, key_x, g, b.k0, st); break;
-    case 21: s = launch_keys<2, 1>(count, key_x, g, b.k0, st); break;
-    case 22: s = launch_keys<2, 2>(count, key_x, g, b.k0, st); break;
-    case 31: s = launch_keys<3, 1>(count, key_x, g, b.k0, st); break;
-    case 32: s = launch_keys<3, 2>(count, key_x, g, b.k0, st); break;
+    PermArgs arr{};
+    for (int i = 0; i < n_arrays; ++i) {
+        arr.in[i] = in_arrays[i];
+        arr.out[i] = out_arrays[i];
     }
-    PCG_TRY(s);
+    arr.n = n_arrays;
 
-    uint32_t *final_keys = sorted_keys ? sorted_keys : b.fk;
-    const uint32_t *kin = b.k0;
-    const uint32_t *vin = nullptr;  // pass 0 ranks input indices
-    for (int pass = 0; pass < p.passes; ++pass) {
-        const bool last = pass == p.passes - 1;
-        uint32_t *kout = last ? final_keys : (pass % 2 == 0 ? b.ak : b.k0);
-        uint32_t *vout = last ? perm : (pass % 2 == 0 ? b.av : b.bv);
-        PCG_TRY(radix_pass_dispatch(p.bits, p, pass * p.bits, kin, vin, kout, vout, b, st));
-        kin = kout;
-        vin = vout;
-    }
-    {
-        const int64_t blocks = std::min<int64_t>((count + 1 + 255) / 256, (int64_t)device_cus() * 32);
-        PCG_TRY(launch("sort_offsets", k_tile_offsets, dim3((unsigned)blocks), dim3(256), 0, st,
-                       (const uint32_t *)final_keys, count, p.ntiles, tile_offsets));
-    }
-    if (n_arrays > 0) {
-        PermArgs a{};
-        for (int i = 0; i < n_arrays; ++i) {
-            a.in[i] = in_arrays[i];
-            a.out[i] = out_arrays[i];
+    // the incremental path needs a layout that covers every particle
+    const bool incremental = prev && prev->n_partitioned == count;
+    Gate gate = always;
+    if (incremental) {
+        IncGeom a;
+        a.g = g;
+        a.ntiles = p.ntiles;
+        a.prev_off = prev->tile_offsets;
+        a.count = count;
+        a.cum = b.cum;
+        a.cnt = b.cnt;
+        a.tcnt = b.tcnt;
+        a.tpre = b.tpre;
+        a.code = b.k0;  // the general path reuses it only if this path gave up
+        a.flag = b.flag;
+        const uint32_t chunk = INC_CHUNK;
+        const uint32_t nwork = p.nchunks_max;  // >= ntiles + ceil(count / chunk)
+        PCG_TRY(launch("sort_inc_flag", k_set_flag, dim3(1), dim3(64), 0, st, b.flag, 0u));
+        PCG_TRY(launch("sort_inc_validate", k_inc_validate, dim3((p.ntiles + 1 + 255) / 256),
+                       dim3(256), 0, st, prev->tile_offsets, p.ntiles, count, b.flag));
+        PCG_TRY(launch("sort_inc_chunks", k_chunk_cum, dim3(1), dim3(1024), 0, st,
+                       prev->tile_offsets, p.ntiles, count, chunk, b.cum,
+                       (const uint32_t *)b.flag, 0u));
+        const int key = grid->dim * 10 + order;
+        pcg_status s = PCG_OK;
+        switch (key) {
+        case 11: s = incremental_launch<1, 1>(a, key_x, nwork, arr, perm, sorted_keys, tile_offsets, b, st); break;
+        case 12: s = incremental_launch<1, 2>(a, key_x, nwork, arr, perm, sorted_keys, tile_offsets, b, st); break;
+        case 21: s = incremental_launch<2, 1>(a, key_x, nwork, arr, perm, sorted_keys, tile_offsets, b, st); break;
+        case 22: s = incremental_launch<2, 2>(a, key_x, nwork, arr, perm, sorted_keys, tile_offsets, b, st); break;
+        case 31: s = incremental_launch<3, 1>(a, key_x, nwork, arr, perm, sorted_keys, tile_offsets, b, st); break;
+        case 32: s = incremental_launch<3, 2>(a, key_x, nwork, arr, perm, sorted_keys, tile_offsets, b, st); break;
         }
-        a.n = n_arrays;
-        const int64_t blocks = std::min<int64_t>((count + 255) / 256, (int64_t)device_cus() * 64);
-        PCG_TRY(launch("sort_permute", k_permute, dim3((unsigned)blocks), dim3(256), 0, st, a,
-                       (const uint32_t *)perm, count));
+        PCG_TRY(s);
+        gate = Gate{b.flag, 1u};  // the general path runs only if the flag was raised
     }
-    return PCG_OK;
+    return general_path(grid, order, p, g, key_x, arr, perm, sorted_keys, tile_offsets, b, gate,
+                        st);
 }
 
 }  // extern "C"

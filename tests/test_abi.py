@@ -152,9 +152,10 @@ def test_tile_sort_validation(lib):
     arr2 = (C.c_void_p * 1)(FAKE + 4096)
 
     def call(g=g, order=1, T=8, count=100, n_arrays=1, outs=arr2, perm=FAKE, off=FAKE, ws=FAKE,
-             wsb=1 << 30):
+             wsb=1 << 30, prev=None):
         return ts(C.byref(g), order, T, C.c_int64(count), kx, n_arrays, arr, outs,
-                  C.c_void_p(perm), None, C.c_void_p(off), C.c_void_p(ws), C.c_size_t(wsb), None)
+                  C.c_void_p(perm), None, C.c_void_p(off), C.byref(prev) if prev else None,
+                  C.c_void_p(ws), C.c_size_t(wsb), None)
 
     assert call(T=0) == EINVAL
     assert call(T=5) == EINVAL
@@ -162,11 +163,14 @@ def test_tile_sort_validation(lib):
     assert call(count=-5) == EINVAL
     assert call(n_arrays=17) == EINVAL
     assert call(outs=arr) == EINVAL                               # in place
-    assert call(perm=0) == EINVAL
     assert call(off=0) == EINVAL
     assert call(ws=0) == EWORKSPACE
     assert call(wsb=10) == EWORKSPACE
     assert call(ws=FAKE + 8) == EWORKSPACE                        # misaligned
+    assert call(prev=Tile(4, 1, 1, 0, 100, FAKE)) == EINVAL       # prev keyed with another T
+    assert call(prev=Tile(8, 2, 1, 0, 100, FAKE)) == EINVAL       # or another order
+    assert call(prev=Tile(8, 1, 1, 0, 100, None)) == EINVAL       # no offsets
+    assert call(prev=Tile(8, 1, 1, 0, 100, FAKE)) == EINVAL       # offsets aliasing the output
 
 
 def test_mass_and_sweep_validation(lib):

@@ -90,3 +90,102 @@ def test_sort_full_size_config5_cells(orc):
     """16.8M particles into 262,144 cells (the mass-matrix layout)."""
     wl = full_config(5)
     _check_sort(orc, 3, wl.n, 1, 1, wl.x, [wl.beta])
+
+
+# ---------------------------------------------------------------- incremental path
+
+def _check_resort(orc, wl, order, T, prev_off, x, arrays, expect_same=True, n_part=None):
+    """Sort x (currently grouped by prev_off) with the previous layout given;
+    the result must equal the oracle's stable sort of x exactly."""
+    say("resort", wl.dim, wl.n, order, T, x[0].size)
+    cnt = x[0].size
+    prev = pcg.Layout(T=T, order=order, tile_offsets=dev(prev_off.view(np.int32)),
+                      n_partitioned=cnt if n_part is None else n_part)
+    perm, keys, off, outs = pcg.pcg_tile_sort(wl.dim, wl.n, order, T, [dev(a) for a in x],
+                                              [dev(a) for a in arrays], prev=prev)
+    torch.cuda.synchronize()
+    k_ref, p_ref, o_ref = orc.tile_sort(wl.dim, wl.n, order, T, x)
+    assert np.array_equal(u32(perm), p_ref)
+    assert np.array_equal(u32(keys), k_ref[p_ref])
+    assert np.array_equal(u32(off), o_ref)
+    for a, o in zip(arrays, outs):
+        assert np.array_equal(o.cpu().numpy(), a[p_ref])
+
+
+def _sorted_state(orc, wl, order, T):
+    _, p, o = orc.tile_sort(wl.dim, wl.n, order, T, wl.x)
+    return wl.take(p.astype(np.int64)), o
+
+
+@pytest.mark.parametrize("dim,n,order,T,ppc", [
+    (3, [32, 32, 32], 1, 8, 4),
+    (3, [32, 32, 32], 2, 4, 2),
+    (2, [64, 64], 1, 8, 6),
+    (2, [64, 32], 2, 16, 6),
+    (3, [16, 8, 64], 1, 8, 4),     # 2 and 1 tiles along x and y
+    (3, [24, 24, 24], 1, 1, 2),    # cell layout
+])
+def test_resort_steady_state(orc, dim, n, order, T, ppc):
+    wl = synthetic.deposit_workload(dim, n, ppc=ppc, far_fraction=0.02, seed=600 + T + dim)
+    s, off = _sorted_state(orc, wl, order, T)
+    _check_resort(orc, s, order, T, off, s.x_next, s.x_next + s.v + [s.q, s.w])
+
+
+def test_resort_far_moves_fall_back(orc):
+    """Particles that moved more than one tile raise the device flag; the radix
+    path then produces the same stable result."""
+    wl = synthetic.deposit_workload(3, [32, 32, 32], ppc=2, far_fraction=0.1, seed=610)
+    s, off = _sorted_state(orc, wl, 1, 2)   # tiles of 2 cells: 2-4 cell pushes leave the stencil
+    _check_resort(orc, s, 1, 2, off, s.x_next, [s.q])
+
+
+def test_resort_invalid_prev_falls_back(orc):
+    wl = synthetic.deposit_workload(3, [32, 32, 32], ppc=2, seed=611)
+    s, off = _sorted_state(orc, wl, 1, 8)
+    bad = off.copy()
+    bad[5], bad[6] = bad[6], bad[5]              # not monotone
+    _check_resort(orc, s, 1, 8, bad, s.x_next, [s.w])
+    bad = off.copy()
+    bad[-1] -= 3                                 # does not cover every particle
+    _check_resort(orc, s, 1, 8, bad, s.x_next, [s.w])
+
+
+def test_resort_with_tail_uses_general_path(orc):
+    wl = synthetic.deposit_workload(3, [32, 32, 32], ppc=2, seed=612)
+    s, off = _sorted_state(orc, wl, 1, 8)
+    _check_resort(orc, s, 1, 8, off, s.x_next, [s.w], n_part=s.count - 7)
+
+
+def test_resort_heavy_tiles(orc):
+    wl = synthetic.deposit_workload(3, [64, 64, 64], count=600_000,
+                                    blob=dict(sigma=3.0, overdensity=400.0), seed=613)
+    s, off = _sorted_state(orc, wl, 2, 8)
+    assert np.diff(off.astype(np.int64)).max() > 4 * 4096
+    _check_resort(orc, s, 2, 8, off, s.x_next, s.x_next + [s.q])
+
+
+def test_resort_full_size_config3(orc):
+    """The bench step's sort: 67.1M pushed particles re-sorted from their layout."""
+    wl = full_config(3)
+    s, off = _sorted_state(orc, wl, 1, 8)
+    _check_resort(orc, s, 1, 8, off, s.x_next, [s.x_next[0], s.q])
+
+
+@pytest.mark.parametrize("use_prev", [True, False])
+def test_sort_without_keys_or_perm(orc, use_prev):
+    """sorted_keys and perm are optional outputs: the same offsets and permuted
+    arrays without them, on both the single-pass and the radix path."""
+    wl = synthetic.deposit_workload(3, [32, 32, 32], ppc=3, seed=614)
+    s, off = _sorted_state(orc, wl, 1, 8)
+    prev = (pcg.Layout(T=8, order=1, tile_offsets=dev(off.view(np.int32)), n_partitioned=s.count)
+            if use_prev else None)
+    say("sort without keys/perm", use_prev)
+    perm, keys, o, outs = pcg.pcg_tile_sort(3, wl.n, 1, 8, [dev(a) for a in s.x_next],
+                                            [dev(s.q), dev(s.x_next[1])], prev=prev,
+                                            want_keys=False, want_perm=False)
+    torch.cuda.synchronize()
+    _, p_ref, o_ref = orc.tile_sort(3, wl.n, 1, 8, s.x_next)
+    assert keys is None and perm is None
+    assert np.array_equal(u32(o), o_ref)
+    assert np.array_equal(outs[0].cpu().numpy(), s.q[p_ref])
+    assert np.array_equal(outs[1].cpu().numpy(), s.x_next[1][p_ref])

@@ -12,8 +12,9 @@ library's stream).  Per-kernel durations come from the library's event tap
 (events recorded around every launch, on the launch stream) during the same
 timed steps.
 
-Other workloads (--config): 2 (2-D CIC 512^2), 4 (3-D TSC clustered, T from
---tile), 5 (ECSIM mass matrix 64^3: cell sort + MFMA assembly), 1 (1-D sweep).
+Other workloads (--workload): cic2d_512_ppc16 (2-D CIC 512^2), tsc3d_128_blob
+(3-D TSC clustered, T from --tile), mass_64_ppc64 (ECSIM mass matrix 64^3: cell
+sort + MFMA assembly), sweep1d_2000 (1-D windowed sweep).
 
 Prints ONE JSON line (rank 0).  Only one GPU is used: --gpus above 1 exits.
 """
@@ -29,7 +30,13 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
 
+# HBM bytes per dispatch measured by rocprofv3 FETCH_SIZE / WRITE_SIZE passes
+# (scaled by the copy calibration), with the digest of the kernel's sources at
+# the time the counters were taken.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
 METRIC = "deposited particles/s (3D CIC 128^3, 32 ppc) + % of HBM roofline"
+HEADLINE = "cic3d_128_ppc32"
 
 
 def parse():
@@ -37,20 +44,27 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", default=HEADLINE,
+                    choices=["sweep1d_2000", "cic2d_512_ppc16", "cic3d_128_ppc32",
+                             "tsc3d_128_blob", "mass_64_ppc64"])
     ap.add_argument("--tile", type=int, default=0, help="tile edge T (0 = the workload's)")
     ap.add_argument("--block", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--no-flat", action="store_true", help="skip the flat-path comparison")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a 1 GiB device-to-device copy (known bytes) so hardware "
-                         "traffic counters can be scaled")
+    ap.add_argument("--no-copy-bandwidth", action="store_true",
+                    help="skip the 1 GiB device copy timed for context (its dispatches "
+                         "also calibrate the HBM traffic counters)")
     return ap.parse_args()
 
 
 # ----------------------------------------------------------------- helpers
+
+def progress(msg):
+    """One progress line on stderr (the JSON result line is the only stdout)."""
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
 
 def kernel_times(pcg, names):
     out = {}
@@ -97,6 +111,21 @@ def time_plain(torch, fn, reps):
     return ev0.elapsed_time(ev1) / reps
 
 
+def measured_traffic(kernel, workload):
+    """Scaled HBM bytes (read + write) per dispatch from the committed counter
+    summary, or None when there is none for this kernel and workload or the
+    kernel's sources changed since the counters were taken."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))["kernels"][workload][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    from particle_cell_grid_amd.profsummary import source_digest
+
+    if rec.get("source_sha1") != source_digest(kernel):
+        return None
+    return int(rec["read_bytes"] + rec["write_bytes"])
+
+
 def roofline_entry(kt, name, bytes_per_launch=None, flops_per_launch=None):
     k = kt.get(name)
     if not k:
@@ -138,17 +167,19 @@ def cpu_baseline_deposit(wl, order, T, target_s):
 
 # ----------------------------------------------------------------- deposit family
 
-def bench_deposit(args, torch, pcg, k):
+def bench_deposit(args, torch, pcg, name):
     import numpy as np
 
     import synthetic
 
-    info = synthetic.CONFIG_INFO[k]
+    info = synthetic.WORKLOADS[name]
     order = info["order"]
     T = args.tile or (info.get("T") or 8)
     D = info["D"]
-    wl = synthetic.config(k)
+    progress(f"generating {name}")
+    wl = synthetic.workload(name)
     n, dim, cnt = wl.n, wl.dim, wl.count
+    progress(f"{cnt} particles generated; set-up sort")
     dev = torch.device("cuda:0")
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     # previous step's state: sorted on x, pushed to x_next (library sort, untimed)
@@ -170,6 +201,8 @@ def bench_deposit(args, torch, pcg, k):
     off1 = torch.empty(nt + 1, dtype=torch.int32, device=dev)
     nxt = [torch.empty_like(a) for a in cur]
     sws = torch.empty(pcg.pcg_sort_workspace_bytes(dim, n, cnt, T), dtype=torch.uint8, device=dev)
+    rws = torch.empty(pcg.pcg_deposit_regroup_workspace_bytes(dim, n, lay, cnt), dtype=torch.uint8,
+                      device=dev)
     xs, vs, q, w = cur[:dim], cur[dim:dim + 3], cur[dim + 3], cur[dim + 4]
 
     def deposit():
@@ -181,11 +214,15 @@ def bench_deposit(args, torch, pcg, k):
                           want_keys=False, tile_offsets=off1, workspace=sws, prev=lay)
 
     def step():
+        # deposit with the layout the particles are grouped by, and regroup them
+        # by their pushed positions (the next step's layout), in one pass
         J.zero_()
-        deposit()
-        resort()
+        pcg.deposit_currents_regroup(dim, n, order, xs, vs, q, w, J, lay, cur, outs=nxt,
+                                     tile_offsets=off1, workspace=rws)
 
+    progress("timing steps")
     ms, wall, kt = time_steps(torch, pcg, step, args.steps, args.warmup)
+    progress(f"{ms:.4f} ms per step")
     # escape count of one deposit of this input
     esc.zero_()
     deposit()
@@ -196,9 +233,16 @@ def bench_deposit(args, torch, pcg, k):
     jbytes = 3 * n[0] * n[1] * n[2] * 4
     pbytes = (dim + 5) * 4
     alg = {
+        # particle fields read once + J read-modify-write
         "deposit_tiled": cnt * pbytes + 2 * jbytes,
+        # the same, plus every field written once to its new slot
+        "deposit_regroup": cnt * 2 * pbytes + 2 * jbytes,
+        # positions read, 4-byte move code written
+        "sort_inc_rank": cnt * (dim * 4 + 4),
+        # move code read, every field read once and written once
+        "sort_inc_move": cnt * (4 + 2 * pbytes),
         "sort_keys": cnt * (dim * 4 + 4),
-        "sort_permute": cnt * (4 + 2 * (dim + 5) * 4),
+        "sort_permute": cnt * (4 + 2 * pbytes),
         "sort_offsets": cnt * 4 + (nt + 1) * 4,
     }
     kernels = {}
@@ -209,12 +253,17 @@ def bench_deposit(args, torch, pcg, k):
             e["GBps"] = round(alg[nm] / (kk["avg_us"] * 1e-6) / 1e9, 1)
         kernels[nm] = e
     dominant = max(kt, key=lambda nm: kt[nm]["total_ms"])
-    roof = roofline_entry(kt, "deposit_tiled", bytes_per_launch=alg["deposit_tiled"])
     roof_dom = (roofline_entry(kt, dominant, bytes_per_launch=alg[dominant])
                 if dominant in alg else None)
 
     extra = {}
-    dep_ms = time_plain(torch, lambda: (J.zero_(), deposit()), args.steps)
+    # the deposit alone (deposit_currents on the same input), with its own tap
+    progress("timing the deposit alone")
+    dep_ms, _, kt_dep = time_steps(torch, pcg, lambda: (J.zero_(), deposit()), args.steps, 1)
+    roof = roofline_entry(kt_dep, "deposit_tiled", bytes_per_launch=alg["deposit_tiled"])
+    for r in (roof, roof_dom):
+        if r:
+            r["traffic"] = measured_traffic(r["kernel"], name)
     extra["deposit_only_particles_per_s"] = round(cnt / (dep_ms * 1e-3), 1)
     extra["deposit_only_ms"] = round(dep_ms, 4)
     if not args.no_flat:
@@ -225,6 +274,8 @@ def bench_deposit(args, torch, pcg, k):
         extra["flat_deposit_particles_per_s"] = round(cnt / (fl_ms * 1e-3), 1)
         extra["tiled_speedup_vs_flat"] = round(fl_ms / dep_ms, 2)
     sort_ms = time_plain(torch, resort, args.steps)
+    unfused_ms = time_plain(torch, lambda: (J.zero_(), deposit(), resort()), args.steps)
+    extra["unfused_step_ms"] = round(unfused_ms, 4)
     cold_ms = time_plain(torch, lambda: pcg.pcg_tile_sort(
         dim, n, order, T, xs, cur, outs=nxt, perm=perm, sorted_keys=keys, tile_offsets=off1,
         workspace=sws), max(3, args.steps // 4))
@@ -233,12 +284,18 @@ def bench_deposit(args, torch, pcg, k):
     extra["escaped_particles"] = n_esc
     extra["deposit_roofline"] = roof
     extra["dominant_kernel"] = dominant
-    wk = {2: "2-D CIC current deposit + tile sort, 512^2 periodic, 16 ppc",
-          3: "3-D CIC current deposit + tile sort, 128^3 periodic, 32 ppc, 2% pushed 2-4 cells",
-          4: "3-D TSC current deposit + tile sort, 128^3 periodic, clustered (Gaussian blob)"}[k]
+    wk = {"cic2d_512_ppc16": "2-D CIC current deposit + tile sort, 512^2 periodic, 16 ppc",
+          "cic3d_128_ppc32": "3-D CIC current deposit + tile sort, 128^3 periodic, 32 ppc, "
+                             "2% pushed 2-4 cells",
+          "tsc3d_128_blob": "3-D TSC current deposit + tile sort, 128^3 periodic, clustered "
+                            "(Gaussian blob)"}[name]
     config = dict(workload=wk, particles=cnt, grid=n[:dim], order=order, tile=T, drift=D,
-                  block=args.block or 256, step="zero J + tiled deposit + tile sort/permute")
-    cpu = None if args.no_cpu_baseline else cpu_baseline_deposit(wl, order, T, args.cpu_seconds)
+                  block=args.block or 512,
+                  step="zero J + fused tiled deposit and regroup (incremental tile sort)")
+    cpu = None
+    if not args.no_cpu_baseline:
+        progress("timing the oracle on the host")
+        cpu = cpu_baseline_deposit(wl, order, T, args.cpu_seconds)
     return dict(value=cnt / (ms * 1e-3), ms=ms, wall=wall, dtype="f32", config=config,
                 roofline=roof_dom if roof_dom else roof, kernels=kernels, extra=extra,
                 cpu=cpu, unit="particles/s")
@@ -251,7 +308,8 @@ def bench_mass(args, torch, pcg):
 
     import synthetic
 
-    wl = synthetic.config(5)
+    progress("generating mass_64_ppc64")
+    wl = synthetic.workload("mass_64_ppc64")
     n, cnt = wl.n, wl.count
     dev = torch.device("cuda:0")
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -273,9 +331,13 @@ def bench_mass(args, torch, pcg):
         pcg.assemble_mass_matrix(n, outs[0:3], outs[3:6], outs[6], outs[7], outs[8], M, cells,
                                  pcg.PCG_MASS_MFMA)
 
+    progress("timing steps")
     ms, wall, kt = time_steps(torch, pcg, step, args.steps, args.warmup)
+    progress(f"{ms:.4f} ms per step")
     flops = cnt * 1152.0     # dense 8x8 node pairs x 9 components x 2 flops
     roof = roofline_entry(kt, "mass_mfma", flops_per_launch=flops)
+    if roof:
+        roof["traffic"] = measured_traffic("mass_mfma", "mass_64_ppc64")
     mbytes = M.numel() * 4
     kernels = {nm: dict(avg_us=round(kk["avg_us"], 2),
                         launches_per_step=kk["launches"] / args.steps) for nm, kk in kt.items()}
@@ -294,6 +356,7 @@ def bench_mass(args, torch, pcg):
     if not args.no_cpu_baseline:
         import oracle
 
+        progress("timing the oracle on the host")
         m = 1 << 20
         t0 = time.perf_counter()
         oracle.mass_matrix(n, [a[:m] for a in wl.x], [b[:m] for b in wl.B], wl.q[:m], wl.w[:m],
@@ -320,7 +383,7 @@ def bench_sweep(args, torch, pcg):
 
     import synthetic
 
-    s = synthetic.config(1)
+    s = synthetic.workload("sweep1d_2000")
     dev = torch.device("cuda:0")
     x0 = torch.from_numpy(s.x0).to(dev)
     v = torch.from_numpy(s.v).to(dev)
@@ -359,21 +422,21 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
-    if args.copy_calibration:
-        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(2):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-    if args.config in (2, 3, 4):
-        r = bench_deposit(args, torch, pcg, args.config)
-    elif args.config == 5:
+    copy_gbs = None
+    if not args.no_copy_bandwidth:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
+        b = torch.empty_like(a)
+        copy_ms = time_plain(torch, lambda: b.copy_(a), 10)
+        copy_gbs = round(2 * a.numel() * 4 / (copy_ms * 1e-3) / 1e9, 1)
+        del a, b
+    if args.workload in ("cic2d_512_ppc16", "cic3d_128_ppc32", "tsc3d_128_blob"):
+        r = bench_deposit(args, torch, pcg, args.workload)
+    elif args.workload == "mass_64_ppc64":
         r = bench_mass(args, torch, pcg)
     else:
         r = bench_sweep(args, torch, pcg)
     line = {
-        "metric": METRIC if args.config == 3 else f"config {args.config}: {r['unit']}",
+        "metric": METRIC if args.workload == HEADLINE else f"{args.workload}: {r['unit']}",
         "value": round(r["value"], 1),
         "unit": r["unit"],
         "n_gpus": 1,
@@ -389,7 +452,7 @@ def main():
         "roofline": r["roofline"],
         "cpu_baseline": r["cpu"],
         "kernels": r["kernels"],
-        "extra": r["extra"],
+        "extra": dict(r["extra"], device_copy_GBps=copy_gbs),
         "wall_s_timed": round(r["wall"], 3),
     }
     print(json.dumps(line), flush=True)

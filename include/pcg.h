@@ -77,8 +77,8 @@ typedef struct pcg_particles {
  *   order      shape order the layout was keyed with (1 CIC, 2 TSC).
  *   drift      halo budget D >= 0 in cells ([TD] "Halo sizing"): the scratch
  *              tile spans TE = T + order + 2*D nodes per used axis.
- *   block      work-group size; 0 = automatic (256), otherwise clamped to
- *              [64, 256] and rounded down to a multiple of 64 ([TD] team size
+ *   block      work-group size; 0 = automatic (512), otherwise clamped to
+ *              [64, 1024] and rounded down to a multiple of 64 ([TD] team size
  *              knob).
  *   tile_offsets  device uint32 [ntiles + 1], ntiles = prod_k (n_k / T). */
 typedef struct pcg_tile {
@@ -163,6 +163,37 @@ size_t pcg_deposit_workspace_bytes(const pcg_grid *grid, const pcg_tile *tile);
 pcg_status deposit_currents(const pcg_grid *grid, const pcg_particles *particles, int32_t order,
                             const pcg_tile *tile, float *J, unsigned long long *n_escaped,
                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace deposit_currents_regroup needs (0 if invalid). */
+size_t pcg_deposit_regroup_workspace_bytes(const pcg_grid *grid, const pcg_tile *tile,
+                                           int64_t count);
+
+/* One pass of a step over the particle data ([TD] "How a tile deposit runs"
+ * followed by "The tile-based spatial sort", the sort at the end of a step):
+ * the same results as
+ *     deposit_currents(grid, particles, order, tile, J, n_escaped, ...);
+ *     pcg_tile_sort(grid, order, tile->T, particles->count, particles->x,
+ *                   n_arrays, in_arrays, out_arrays, NULL, NULL,
+ *                   tile_offsets, tile, ...);
+ * (J and n_escaped accumulated as there; out_arrays and tile_offsets equal to
+ * the sort's, bit for bit), but when `tile` covers every particle
+ * (n_partitioned == count) the sort's move is made by the deposit kernel from
+ * the values it has loaded, so the particle arrays are read once instead of
+ * twice.  `tile` is the layout the particles are grouped by (required); the
+ * sort uses it as `prev`, so particles that moved further than one tile, or a
+ * layout that is not a partition, send the regrouping to the general sort
+ * path (decided on the device; the deposit is unaffected).  With a tail the
+ * two calls run one after the other.  in_arrays / out_arrays as in
+ * pcg_tile_sort (usually x[0..dim), v[0..3), q, w and any other per-particle
+ * fields; out of place).  tile_offsets: device uint32 [ntiles + 1], the new
+ * layout, distinct from tile->tile_offsets.  workspace: at least
+ * pcg_deposit_regroup_workspace_bytes(), 256-byte aligned. */
+pcg_status deposit_currents_regroup(const pcg_grid *grid, const pcg_particles *particles,
+                                    int32_t order, const pcg_tile *tile, float *J,
+                                    unsigned long long *n_escaped, int32_t n_arrays,
+                                    const float *const in_arrays[], float *const out_arrays[],
+                                    uint32_t *tile_offsets, void *workspace,
+                                    size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* ECSIM mass matrix  ([MM] §2.1 Eq.(4)-(6), §2.2 Eq.(9)-(11), §3)           */

@@ -56,6 +56,13 @@ _lib.pcg_deposit_workspace_bytes.restype = C.c_size_t
 _lib.deposit_currents.argtypes = [_P(Grid), _P(Particles), C.c_int32, _P(Tile), C.c_void_p,
                                   C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
 _lib.deposit_currents.restype = C.c_int32
+_lib.pcg_deposit_regroup_workspace_bytes.argtypes = [_P(Grid), _P(Tile), C.c_int64]
+_lib.pcg_deposit_regroup_workspace_bytes.restype = C.c_size_t
+_lib.deposit_currents_regroup.argtypes = [_P(Grid), _P(Particles), C.c_int32, _P(Tile),
+                                          C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
+                                          C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
+                                          C.c_void_p]
+_lib.deposit_currents_regroup.restype = C.c_int32
 _lib.assemble_mass_matrix.argtypes = [_P(Grid), _P(Particles), C.c_void_p, C.c_void_p, _P(Tile),
                                       C.c_int32, C.c_void_p, C.c_void_p]
 _lib.assemble_mass_matrix.restype = C.c_int32
@@ -211,6 +218,45 @@ def deposit_currents(dim: int, n: Sequence[int], order: int, x: List[torch.Tenso
                                int(workspace.numel()) if need else 0, _stream())
     _check(st, "deposit_currents")
     return J
+
+
+def pcg_deposit_regroup_workspace_bytes(dim: int, n: Sequence[int], layout: Layout,
+                                        count: int) -> int:
+    g = make_grid(dim, n)
+    t = layout.to_c()
+    return int(_lib.pcg_deposit_regroup_workspace_bytes(C.byref(g), C.byref(t), int(count)))
+
+
+def deposit_currents_regroup(dim: int, n: Sequence[int], order: int, x: List[torch.Tensor],
+                             v: List[torch.Tensor], q: torch.Tensor, w: torch.Tensor,
+                             J: torch.Tensor, layout: Layout, arrays: Sequence[torch.Tensor],
+                             outs: Optional[List[torch.Tensor]] = None,
+                             tile_offsets: Optional[torch.Tensor] = None,
+                             n_escaped: Optional[torch.Tensor] = None,
+                             workspace: Optional[torch.Tensor] = None):
+    """J += the deposit of q w v with `layout`, and `arrays` regrouped by the
+    tiles of x into `outs` / `tile_offsets` (the next layout), in one pass.
+    Returns (tile_offsets, outs)."""
+    g = make_grid(dim, n)
+    count = int(q.numel())
+    P = _particles(count, x, v, q, w)
+    tile = layout.to_c()
+    dev = q.device
+    if tile_offsets is None:
+        tile_offsets = torch.empty(ntiles(dim, n, layout.T) + 1, dtype=torch.int32, device=dev)
+    if outs is None:
+        outs = [torch.empty_like(a) for a in arrays]
+    need = pcg_deposit_regroup_workspace_bytes(dim, n, layout, count)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    na = len(arrays)
+    ins = (C.c_void_p * max(na, 1))(*[a.data_ptr() for a in arrays])
+    ous = (C.c_void_p * max(na, 1))(*[o.data_ptr() for o in outs])
+    st = _lib.deposit_currents_regroup(C.byref(g), C.byref(P), int(order), C.byref(tile), _ptr(J),
+                                       _ptr(n_escaped), na, ins, ous, _ptr(tile_offsets),
+                                       _ptr(workspace), int(workspace.numel()), _stream())
+    _check(st, "deposit_currents_regroup")
+    return tile_offsets, outs
 
 
 def assemble_mass_matrix(n: Sequence[int], x: List[torch.Tensor], B: List[torch.Tensor],

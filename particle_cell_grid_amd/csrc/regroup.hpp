@@ -1,0 +1,123 @@
+// regroup.hpp -- what the tile sort's incremental path shares with the kernel
+// that deposits and regroups in one pass over the particle data: the tile
+// geometry, the per-chunk direction/rank bookkeeping, and the host entry of the
+// sort with a hook for the move stage.
+#pragma once
+
+#include "common.hpp"
+
+namespace pcg {
+
+constexpr int MAX_ARRAYS = 16;        // SoA arrays a sort carries along
+constexpr int NDIR = 27;              // neighbour directions of the incremental path
+constexpr uint32_t INC_CHUNK = 2048;  // particles per chunk of the incremental path
+
+// A kernel runs only if `flag` is NULL or *flag == run.
+struct Gate {
+    const uint32_t *flag;
+    uint32_t run;
+};
+__device__ inline bool gated_off(const Gate &g) { return g.flag && *g.flag != g.run; }
+
+struct KeyGeom {
+    int n[3];
+    float nf[3];
+    int nt[3];
+    int T;
+    int T_shift;  // log2(T) if T is a power of two, else -1
+};
+
+// Tile coordinate of a particle along one axis: the tile holding its first
+// support node (wrapped).
+template <int ORDER>
+__device__ inline int tile_coord(float xraw, const KeyGeom &g, int k)
+{
+    const float xf = clamp_coord(xraw, g.nf[k]);
+    const float fl = floorf(xf);
+    int b = (int)fl;
+    if (ORDER == 2 && (xf - fl) < 0.5f)
+        b -= 1;
+    b = wrap_index(b, g.n[k]);
+    return g.T_shift >= 0 ? (b >> g.T_shift) : (b / g.T);
+}
+
+struct PermArgs {
+    const float *in[MAX_ARRAYS];
+    float *out[MAX_ARRAYS];
+    int n;
+};
+
+// State of the incremental path between its planning and its move.
+struct IncGeom {
+    KeyGeom g;
+    uint32_t ntiles;
+    const uint32_t *prev_off;
+    int64_t count;
+    const uint32_t *cum;  // [ntiles + 1] chunk numbering of the source slices
+    uint32_t *cnt;        // [nchunks][NDIR] particles per direction; then prefix over chunks
+    uint32_t *tcnt;       // [ntiles][NDIR] per source tile
+    uint32_t *tpre;       // [ntiles][NDIR] prefix over a new tile's sources
+    uint32_t *code;       // [count] direction << 27 | rank among the chunk's same-direction ones
+    uint32_t *flag;       // non-zero: the general path takes over
+};
+
+constexpr uint32_t RANK_MASK = (1u << 27) - 1;
+
+__device__ inline void tile_coords(uint32_t t, const KeyGeom &g, int *c)
+{
+    c[0] = (int)(t % (uint32_t)g.nt[0]);
+    c[1] = (int)((t / (uint32_t)g.nt[0]) % (uint32_t)g.nt[1]);
+    c[2] = (int)(t / ((uint32_t)g.nt[0] * (uint32_t)g.nt[1]));
+}
+
+__device__ inline uint32_t tile_index(const int *c, const KeyGeom &g)
+{
+    return (uint32_t)c[0] + (uint32_t)g.nt[0] * ((uint32_t)c[1] + (uint32_t)g.nt[1] * (uint32_t)c[2]);
+}
+
+// New tile reached from source coordinates sc by direction dir.
+__device__ inline uint32_t dest_tile(const int *sc, int dir, const KeyGeom &g)
+{
+    int c[3];
+    c[0] = wrap_index(sc[0] + dir % 3 - 1, g.nt[0]);
+    c[1] = wrap_index(sc[1] + (dir / 3) % 3 - 1, g.nt[1]);
+    c[2] = wrap_index(sc[2] + dir / 9 - 1, g.nt[2]);
+    return tile_index(c, g);
+}
+
+// Output slot base of every direction of incremental chunk `chunk` (global
+// chunk number) of source tile `tile`: off[new tile] + the tile's prefix among
+// the new tile's sources + the chunk's prefix among the tile's chunks.
+__device__ inline uint32_t move_base(const IncGeom &a, const uint32_t *off, uint32_t tile,
+                                     uint32_t chunk, int dir)
+{
+    int sc[3];
+    tile_coords(tile, a.g, sc);
+    const uint32_t t = dest_tile(sc, dir, a.g);
+    return off[t] + a.tpre[(size_t)tile * NDIR + dir] + a.cnt[(size_t)chunk * NDIR + dir];
+}
+
+// The move stage of the incremental path, replaceable by a caller of
+// tile_sort_impl: launched after the new tile offsets exist, in place of the
+// plain move kernel.  `off` holds the new offsets; `nwork` is the launch size
+// of the incremental kernels (chunks, some without work).
+struct MoveHook {
+    pcg_status (*launch)(void *ctx, const IncGeom &a, const uint32_t *off, uint32_t nwork,
+                         const PermArgs &arr, hipStream_t st);
+    void *ctx;
+};
+
+// pcg_tile_sort with an optional hook for the incremental path's move stage.
+// `incremental_taken` (may be NULL) reports whether the incremental path was
+// enqueued (its device flag may still hand the work to the general path).
+pcg_status tile_sort_impl(const pcg_grid *grid, int32_t order, int32_t T, int64_t count,
+                          const float *const key_x[3], int32_t n_arrays,
+                          const float *const in_arrays[], float *const out_arrays[],
+                          uint32_t *perm, uint32_t *sorted_keys, uint32_t *tile_offsets,
+                          const pcg_tile *prev, void *workspace, size_t workspace_bytes,
+                          hipStream_t st, const MoveHook *hook, bool *incremental_taken);
+
+// Bytes of sort workspace (the same as pcg_sort_workspace_bytes; 0 if invalid).
+size_t sort_workspace_bytes(const pcg_grid *grid, int64_t count, int32_t T);
+
+}  // namespace pcg

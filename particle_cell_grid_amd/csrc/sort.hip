@@ -30,6 +30,7 @@
 
 #include "common.hpp"
 #include "layout.hpp"
+#include "regroup.hpp"
 
 namespace pcg {
 namespace {
@@ -41,38 +42,6 @@ constexpr int SORT_SLOTS = SORT_IPT * (SORT_BLOCK / WAVE);  // wave-slots per bl
 constexpr int SCAN_BLOCK = 256;
 constexpr int SCAN_IPT = 16;
 constexpr int SCAN_TILE = SCAN_BLOCK * SCAN_IPT;
-constexpr int MAX_ARRAYS = 16;
-constexpr int NDIR = 27;            // neighbour directions of the incremental path
-constexpr uint32_t INC_CHUNK = 2048;  // particles per chunk of the incremental path
-
-// A kernel runs only if `flag` is NULL or *flag == run.
-struct Gate {
-    const uint32_t *flag;
-    uint32_t run;
-};
-__device__ inline bool gated_off(const Gate &g) { return g.flag && *g.flag != g.run; }
-
-struct KeyGeom {
-    int n[3];
-    float nf[3];
-    int nt[3];
-    int T;
-    int T_shift;  // log2(T) if T is a power of two, else -1
-};
-
-// Tile coordinate of a particle along one axis: the tile holding its first
-// support node (wrapped).
-template <int ORDER>
-__device__ inline int tile_coord(float xraw, const KeyGeom &g, int k)
-{
-    const float xf = clamp_coord(xraw, g.nf[k]);
-    const float fl = floorf(xf);
-    int b = (int)fl;
-    if (ORDER == 2 && (xf - fl) < 0.5f)
-        b -= 1;
-    b = wrap_index(b, g.n[k]);
-    return g.T_shift >= 0 ? (b >> g.T_shift) : (b / g.T);
-}
 
 // ----------------------------------------------------------------- keys
 
@@ -339,12 +308,6 @@ __global__ __launch_bounds__(256) void k_tile_offsets(const uint32_t *__restrict
     }
 }
 
-struct PermArgs {
-    const float *in[MAX_ARRAYS];
-    float *out[MAX_ARRAYS];
-    int n;
-};
-
 constexpr int PERM_EPT = 4;  // elements per thread: all index loads, then all gathers
 
 __global__ __launch_bounds__(256) void k_permute(PermArgs a, const uint32_t *__restrict__ perm,
@@ -404,19 +367,6 @@ __global__ __launch_bounds__(256) void k_inc_validate(const uint32_t *__restrict
         atomicOr(flag, 1u);
 }
 
-struct IncGeom {
-    KeyGeom g;
-    uint32_t ntiles;
-    const uint32_t *prev_off;
-    int64_t count;
-    const uint32_t *cum;
-    uint32_t *cnt;    // [nchunks][NDIR] particles per direction; then prefix over chunks
-    uint32_t *tcnt;   // [ntiles][NDIR] per source tile
-    uint32_t *tpre;   // [ntiles][NDIR] prefix over a new tile's sources
-    uint32_t *code;   // [count] direction << 27 | rank among the chunk's same-direction ones
-    uint32_t *flag;
-};
-
 // Direction index of the new tile coordinate t relative to source s on one
 // axis of nt tiles: 0, 1, 2 for -1, 0, +1; -1 if further.  On an axis of two
 // tiles only 0 and +1 are distinct, on an axis of one tile only 0.
@@ -451,28 +401,6 @@ __device__ inline int particle_dir(float x0, float x1, float x2, const KeyGeom &
         mul *= 3;
     }
     return far ? -1 : dir;
-}
-
-__device__ inline void tile_coords(uint32_t t, const KeyGeom &g, int *c)
-{
-    c[0] = (int)(t % (uint32_t)g.nt[0]);
-    c[1] = (int)((t / (uint32_t)g.nt[0]) % (uint32_t)g.nt[1]);
-    c[2] = (int)(t / ((uint32_t)g.nt[0] * (uint32_t)g.nt[1]));
-}
-
-__device__ inline uint32_t tile_index(const int *c, const KeyGeom &g)
-{
-    return (uint32_t)c[0] + (uint32_t)g.nt[0] * ((uint32_t)c[1] + (uint32_t)g.nt[1] * (uint32_t)c[2]);
-}
-
-// New tile reached from source coordinates sc by direction dir.
-__device__ inline uint32_t dest_tile(const int *sc, int dir, const KeyGeom &g)
-{
-    int c[3];
-    c[0] = wrap_index(sc[0] + dir % 3 - 1, g.nt[0]);
-    c[1] = wrap_index(sc[1] + (dir / 3) % 3 - 1, g.nt[1]);
-    c[2] = wrap_index(sc[2] + dir / 9 - 1, g.nt[2]);
-    return tile_index(c, g);
 }
 
 // One wave per chunk, walking it in order 64 particles at a time: every
@@ -678,7 +606,7 @@ __global__ __launch_bounds__(256) void k_inc_move(IncGeom a, const uint32_t *__r
             ok[e] = p[e] < s_hi;
             const uint32_t c = ok[e] ? a.code[p[e]] : 0u;
             const uint32_t d = c >> 27;
-            pos[e] = s_base[d < NDIR ? d : 0] + (c & ((1u << 27) - 1));
+            pos[e] = s_base[d < NDIR ? d : 0] + (c & RANK_MASK);
             ok[e] = ok[e] && d < NDIR && pos[e] < (uint64_t)a.count;
             if (ok[e] && keys)
                 keys[pos[e]] = s_dest[d];
@@ -861,7 +789,8 @@ pcg_status general_path(const pcg_grid *grid, int order, const SortPlan &p, cons
 template <int DIM, int ORDER>
 pcg_status incremental_launch(const IncGeom &a, const float *const key_x[3], uint32_t nwork,
                               const PermArgs &arr, uint32_t *perm, uint32_t *keys,
-                              uint32_t *tile_offsets, const SortBuffers &b, hipStream_t st)
+                              uint32_t *tile_offsets, const SortBuffers &b, const MoveHook *hook,
+                              hipStream_t st)
 {
     const float *x1 = DIM > 1 ? key_x[1] : nullptr, *x2 = DIM > 2 ? key_x[2] : nullptr;
     PCG_TRY(launch("sort_inc_rank", k_inc_rank<DIM, ORDER>, dim3(nwork), dim3(64), 0, st, a,
@@ -871,19 +800,16 @@ pcg_status incremental_launch(const IncGeom &a, const float *const key_x[3], uin
     PCG_TRY(launch("sort_inc_tiles", k_inc_tiles, dim3((a.ntiles + 1 + 255) / 256), dim3(256), 0,
                    st, a, tile_offsets));
     PCG_TRY(exclusive_scan(tile_offsets, (size_t)a.ntiles + 1, b.partial, Gate{b.flag, 0u}, st));
+    if (hook)
+        return hook->launch(hook->ctx, a, tile_offsets, nwork, arr, st);
     PCG_TRY(launch("sort_inc_move", k_inc_move<DIM>, dim3(nwork), dim3(256), 0, st, a,
                    (const uint32_t *)tile_offsets, arr, perm, keys));
     return PCG_OK;
 }
 
 }  // namespace
-}  // namespace pcg
 
-using namespace pcg;
-
-extern "C" {
-
-size_t pcg_sort_workspace_bytes(const pcg_grid *grid, int64_t count, int32_t T)
+size_t sort_workspace_bytes(const pcg_grid *grid, int64_t count, int32_t T)
 {
     if (check_sort_args(grid, count, T, "pcg_sort_workspace_bytes") != PCG_OK)
         return 0;
@@ -892,15 +818,16 @@ size_t pcg_sort_workspace_bytes(const pcg_grid *grid, int64_t count, int32_t T)
     return std::max<size_t>(carve(p, nullptr, &b), 256);
 }
 
-pcg_status pcg_tile_sort(const pcg_grid *grid, int32_t order, int32_t T, int64_t count,
-                         const float *const key_x[3], int32_t n_arrays,
-                         const float *const in_arrays[], float *const out_arrays[],
-                         uint32_t *perm, uint32_t *sorted_keys, uint32_t *tile_offsets,
-                         const pcg_tile *prev, void *workspace, size_t workspace_bytes,
-                         void *stream)
+pcg_status tile_sort_impl(const pcg_grid *grid, int32_t order, int32_t T, int64_t count,
+                          const float *const key_x[3], int32_t n_arrays,
+                          const float *const in_arrays[], float *const out_arrays[],
+                          uint32_t *perm, uint32_t *sorted_keys, uint32_t *tile_offsets,
+                          const pcg_tile *prev, void *workspace, size_t workspace_bytes,
+                          hipStream_t st, const MoveHook *hook, bool *incremental_taken)
 {
     const char *who = "pcg_tile_sort";
-    clear_error();
+    if (incremental_taken)
+        *incremental_taken = false;
     PCG_TRY(check_sort_args(grid, count, T, who));
     if (order != 1 && order != 2)
         return fail(PCG_EUNSUPPORTED, "%s: order %d not in {1,2}", who, order);
@@ -939,7 +866,6 @@ pcg_status pcg_tile_sort(const pcg_grid *grid, int32_t order, int32_t T, int64_t
     if (reinterpret_cast<uintptr_t>(workspace) % 256)
         return fail(PCG_EWORKSPACE, "%s: workspace must be 256-byte aligned", who);
     carve(p, workspace, &b);
-    hipStream_t st = static_cast<hipStream_t>(stream);
     const Gate always{nullptr, 0u};
 
     if (count == 0) {
@@ -967,6 +893,8 @@ pcg_status pcg_tile_sort(const pcg_grid *grid, int32_t order, int32_t T, int64_t
 
     // the incremental path needs a layout that covers every particle
     const bool incremental = prev && prev->n_partitioned == count;
+    if (incremental_taken)
+        *incremental_taken = incremental;
     Gate gate = always;
     if (incremental) {
         IncGeom a;
@@ -991,18 +919,42 @@ pcg_status pcg_tile_sort(const pcg_grid *grid, int32_t order, int32_t T, int64_t
         const int key = grid->dim * 10 + order;
         pcg_status s = PCG_OK;
         switch (key) {
-        case 11: s = incremental_launch<1, 1>(a, key_x, nwork, arr, perm, sorted_keys, tile_offsets, b, st); break;
-        case 12: s = incremental_launch<1, 2>(a, key_x, nwork, arr, perm, sorted_keys, tile_offsets, b, st); break;
-        case 21: s = incremental_launch<2, 1>(a, key_x, nwork, arr, perm, sorted_keys, tile_offsets, b, st); break;
-        case 22: s = incremental_launch<2, 2>(a, key_x, nwork, arr, perm, sorted_keys, tile_offsets, b, st); break;
-        case 31: s = incremental_launch<3, 1>(a, key_x, nwork, arr, perm, sorted_keys, tile_offsets, b, st); break;
-        case 32: s = incremental_launch<3, 2>(a, key_x, nwork, arr, perm, sorted_keys, tile_offsets, b, st); break;
+        case 11: s = incremental_launch<1, 1>(a, key_x, nwork, arr, perm, sorted_keys, tile_offsets, b, hook, st); break;
+        case 12: s = incremental_launch<1, 2>(a, key_x, nwork, arr, perm, sorted_keys, tile_offsets, b, hook, st); break;
+        case 21: s = incremental_launch<2, 1>(a, key_x, nwork, arr, perm, sorted_keys, tile_offsets, b, hook, st); break;
+        case 22: s = incremental_launch<2, 2>(a, key_x, nwork, arr, perm, sorted_keys, tile_offsets, b, hook, st); break;
+        case 31: s = incremental_launch<3, 1>(a, key_x, nwork, arr, perm, sorted_keys, tile_offsets, b, hook, st); break;
+        case 32: s = incremental_launch<3, 2>(a, key_x, nwork, arr, perm, sorted_keys, tile_offsets, b, hook, st); break;
         }
         PCG_TRY(s);
         gate = Gate{b.flag, 1u};  // the general path runs only if the flag was raised
     }
     return general_path(grid, order, p, g, key_x, arr, perm, sorted_keys, tile_offsets, b, gate,
                         st);
+}
+
+}  // namespace pcg
+
+using namespace pcg;
+
+extern "C" {
+
+size_t pcg_sort_workspace_bytes(const pcg_grid *grid, int64_t count, int32_t T)
+{
+    return sort_workspace_bytes(grid, count, T);
+}
+
+pcg_status pcg_tile_sort(const pcg_grid *grid, int32_t order, int32_t T, int64_t count,
+                         const float *const key_x[3], int32_t n_arrays,
+                         const float *const in_arrays[], float *const out_arrays[],
+                         uint32_t *perm, uint32_t *sorted_keys, uint32_t *tile_offsets,
+                         const pcg_tile *prev, void *workspace, size_t workspace_bytes,
+                         void *stream)
+{
+    clear_error();
+    return tile_sort_impl(grid, order, T, count, key_x, n_arrays, in_arrays, out_arrays, perm,
+                          sorted_keys, tile_offsets, prev, workspace, workspace_bytes,
+                          static_cast<hipStream_t>(stream), nullptr, nullptr);
 }
 
 }  // extern "C"

@@ -1,0 +1,164 @@
+"""Short text summaries of rocprofv3 output, for the committed profile records.
+
+    python -m particle_cell_grid_amd.profsummary trace   <dir> <out.md> <title> <command>
+    python -m particle_cell_grid_amd.profsummary traffic <fetch dir> <write dir> <out.md>
+        <workload> <fetch command> <write command> <traffic.json>
+    python -m particle_cell_grid_amd.profsummary counters <dir> <out.md> <title> <command>
+
+`trace` tabulates a `--kernel-trace --stats` run.  `traffic` turns one
+FETCH_SIZE and one WRITE_SIZE pass into HBM bytes per dispatch, scaled by what
+the same counters read for the 1 GiB device copy the benchmark times (a kernel
+whose bytes are known), and records them with a digest of the kernel's sources
+so that a later change of the kernel voids them.  `counters` tabulates any other
+`--pmc` pass (median per dispatch).
+"""
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+KERNEL_SOURCES = {"deposit": "deposit.hip", "sort": "sort.hip", "mass": "mass.hip",
+                  "sweep": "sweep.hip"}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 1 << 30          # the benchmark's context copy: 2^28 fp32 read and written
+
+
+def source_digest(kernel):
+    """sha1 over the file that holds `kernel` (named <file>_<what>) and the
+    headers every kernel file includes."""
+    h = hashlib.sha1()
+    for f in (KERNEL_SOURCES[kernel.split("_")[0]], "common.hpp", "layout.hpp"):
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()
+
+
+def short(name):
+    """Kernel symbol -> readable name, e.g. pcg::(anonymous namespace)::k_inc_move<3>."""
+    name = name.replace("pcg::(anonymous namespace)::", "").replace("void ", "")
+    depth, out = 0, []
+    for ch in name:                 # drop the parameter list, keep template arguments
+        if ch == "(" and depth == 0:
+            break
+        depth += ch == "<"
+        depth -= ch == ">"
+        out.append(ch)
+    return "".join(out).strip()
+
+
+def tap_name(kernel):
+    """The library's launch names for its kernels (as the benchmark reports them)."""
+    table = {"k_deposit_tiled": "deposit_tiled", "k_deposit_flat": "deposit_flat",
+             "k_inc_move": "sort_inc_move", "k_inc_rank": "sort_inc_rank",
+             "k_inc_tiles": "sort_inc_tiles", "k_inc_chunk_prefix": "sort_inc_chunk_prefix",
+             "k_mass_mfma": "mass_mfma", "k_mass_valu": "mass_valu", "k_mass_flat": "mass_flat",
+             "k_permute": "sort_permute", "k_tile_keys": "sort_keys",
+             "k_sweep1d": "sweep1d"}
+    return table.get(kernel.split("<")[0])
+
+
+def one(pattern):
+    f = glob.glob(pattern, recursive=True)
+    if not f:
+        sys.exit(f"profsummary: nothing matches {pattern}")
+    return f[0]
+
+
+def trace(d, out, title, command):
+    rows = list(csv.DictReader(open(one(os.path.join(d, "**", "*kernel_stats.csv")))))
+    lines = [f"# {title}", "", "Command (from the repository root, one MI355X):", "", "```",
+             command, "```", "",
+             "rocprofv3 `--stats` over every dispatch of the run (set-up sort, warm-up, timed "
+             "steps and the extra timings the benchmark makes).", "",
+             "| kernel | calls | average us | min us | max us | % of GPU time |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        lines.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.1f} |")
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
+def per_dispatch(d, counter):
+    out = collections.defaultdict(list)
+    for r in csv.DictReader(open(one(os.path.join(d, "**", "*counter_collection.csv")))):
+        if r["Counter_Name"] == counter:
+            out[short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return out
+
+
+def median(v):
+    v = sorted(v)
+    return v[len(v) // 2]
+
+
+def traffic(fetch_dir, write_dir, out, workload, cmd_fetch, cmd_write, json_path):
+    fe = per_dispatch(fetch_dir, "FETCH_SIZE")
+    wr = per_dispatch(write_dir, "WRITE_SIZE")
+    if COPY_KERNEL not in fe or COPY_KERNEL not in wr:
+        sys.exit("profsummary: the copy kernel is missing from a pass; no calibration")
+    kib = COPY_BYTES / 1024
+    ffac = kib / median(fe[COPY_KERNEL])
+    wfac = kib / median(wr[COPY_KERNEL])
+    lines = [f"# HBM traffic per dispatch: {workload}", "", "Commands (from the repository root, "
+             "one MI355X; one counter per pass):", "", "```", cmd_fetch, cmd_write, "```", "",
+             f"Calibration: the 1 GiB device copy (`{COPY_KERNEL}`, {kib:,.0f} KiB read and "
+             f"{kib:,.0f} KiB written) reads FETCH_SIZE = {median(fe[COPY_KERNEL]):,.0f} KiB and "
+             f"WRITE_SIZE = {median(wr[COPY_KERNEL]):,.0f} KiB per dispatch, so the counters "
+             f"are scaled by {ffac:.3f} (fetch) and {wfac:.3f} (write).", "",
+             "Median over the dispatches of each kernel:", "",
+             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | "
+             "write MB (scaled) |", "|---|---:|---:|---:|---:|---:|"]
+    try:
+        rec = json.load(open(json_path))
+    except (OSError, ValueError):
+        rec = {}
+    rec.setdefault("note", "HBM bytes per dispatch from rocprofv3 FETCH_SIZE/WRITE_SIZE, "
+                           "scaled by the 1 GiB copy calibration; source_sha1 digests the "
+                           "kernel's sources at the time the counters were taken")
+    kern = rec.setdefault("kernels", {}).setdefault(workload, {})
+    for n in sorted(fe):
+        if n == COPY_KERNEL:
+            continue
+        f, w = median(fe[n]), median(wr.get(n, [0.0]))
+        lines.append(f"| `{n}` | {len(fe[n])} | {f:,.0f} | {w:,.0f} | {f * ffac * 1024 / 1e6:,.1f} | "
+                     f"{w * wfac * 1024 / 1e6:,.1f} |")
+        tn = tap_name(n)
+        if tn:
+            kern[tn] = dict(read_bytes=round(f * ffac * 1024), write_bytes=round(w * wfac * 1024),
+                            fetch_kib=f, write_kib=w, source_sha1=source_digest(tn))
+    rec["calibration"] = dict(fetch_factor=round(ffac, 4), write_factor=round(wfac, 4))
+    open(out, "w").write("\n".join(lines) + "\n")
+    json.dump(rec, open(json_path, "w"), indent=1, sort_keys=True)
+    open(json_path, "a").write("\n")
+
+
+def counters(d, out, title, command):
+    by = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(one(os.path.join(d, "**", "*counter_collection.csv")))):
+        by[short(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    cols = sorted({c for k in by.values() for c in k})
+    lines = [f"# {title}", "", "Command (from the repository root, one MI355X):", "", "```",
+             command, "```", "", "Median per dispatch, summed over the chip.", "",
+             "| kernel | dispatches | " + " | ".join(cols) + " |", "|---|---:|" + "---:|" * len(cols)]
+    for n in sorted(by):
+        if n == COPY_KERNEL or "elementwise" in n or "reduce_kernel" in n:
+            continue
+        ncall = max(len(v) for v in by[n].values())
+        lines.append(f"| `{n}` | {ncall} | " +
+                     " | ".join(f"{median(by[n][c]):,.0f}" if c in by[n] else "" for c in cols) + " |")
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
+def main(argv):
+    if not argv:
+        sys.exit(__doc__)
+    cmd, rest = argv[0], argv[1:]
+    {"trace": trace, "traffic": traffic, "counters": counters}[cmd](*rest)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])

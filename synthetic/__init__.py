@@ -14,18 +14,21 @@ other per-particle quantity is drawn i.i.d. in that final order, so no array is
 ever gathered.  Draws are fp32 except the 1-D workload (fp64); a coordinate that
 rounds up to the grid edge n_k is mapped to 0 (positions live in [0, n_k)).
 
-Workloads (see ``config``):
-  1  1-D windowed sweep: 2000 particles, x0 ~ U[0,1), v ~ N(0, 0.05) (fp64),
-     1024 bins, 50 steps, dt = 0.02, half-width 0.005.
-  2  2-D 512x512, exactly 16 particles per cell, uniform in-cell; v ~ N(0,0.1)^3
-     rescaled below |v| = 1; w = 1; q = +1/-1 alternating; displaced by v.
-  3  3-D 128^3, exactly 32 per cell; as 2, plus 2% of the particles displaced
-     by a random direction times U[2,4] cells instead of v.
-  4  3-D 128^3, 33,554,432 particles: a Gaussian blob (sigma = 10 cells) at the
-     centre with 20x peak overdensity over a uniform background;
-     v ~ N(0,0.1)^3; w ~ U[0.5,1.5].
-  5  3-D 64^3, exactly 64 per cell; B ~ N(0,1)^3; q/m = +1/-1 alternating;
-     beta = (q/m) dt/2 with dt = 0.1; w = 1.
+Workloads (see ``workload``):
+  sweep1d_2000     1-D windowed sweep: 2000 particles, x0 ~ U[0,1),
+                   v ~ N(0, 0.05) (fp64), 1024 bins, 50 steps, dt = 0.02,
+                   half-width 0.005.
+  cic2d_512_ppc16  2-D 512x512, exactly 16 particles per cell, uniform in-cell;
+                   v ~ N(0,0.1)^3 rescaled below |v| = 1; w = 1; q = +1/-1
+                   alternating; displaced by v.
+  cic3d_128_ppc32  3-D 128^3, exactly 32 per cell; as the 2-D one, plus 2% of
+                   the particles displaced by a random direction times U[2,4]
+                   cells instead of v.
+  tsc3d_128_blob   3-D 128^3, 33,554,432 particles: a Gaussian blob (sigma = 10
+                   cells) at the centre with 20x peak overdensity over a uniform
+                   background; v ~ N(0,0.1)^3; w ~ U[0.5,1.5].
+  mass_64_ppc64    3-D 64^3, exactly 64 per cell; B ~ N(0,1)^3; q/m = +1/-1
+                   alternating; beta = (q/m) dt/2 with dt = 0.1; w = 1.
 """
 from __future__ import annotations
 
@@ -206,23 +209,31 @@ def sweep_workload(count=2000, sigma_v=0.05, nb=1024, T=50, dt=0.02, hw=0.005, s
 # the five configurations at full size, and scaled variants for tests
 # ----------------------------------------------------------------------------
 
-CONFIG_INFO = {
-    1: dict(kind="sweep1d", count=2000),
-    2: dict(kind="deposit", dim=2, n=[512, 512], ppc=16, order=1, T=8, D=1),
-    3: dict(kind="deposit", dim=3, n=[128, 128, 128], ppc=32, order=1, T=8, D=1,
-            far_fraction=0.02),
-    4: dict(kind="deposit", dim=3, n=[128, 128, 128], count=33554432, order=2, Ts=[4, 8, 16],
-            D=1, blob=dict(sigma=10.0, overdensity=20.0), w_uniform=True),
-    5: dict(kind="mass", n=[64, 64, 64], ppc=64),
+# The named workloads at full size; each draws from its own seed.
+WORKLOADS = {
+    # 1-D windowed sweep: 2000 particles, 50 steps, 1024 bins
+    "sweep1d_2000": dict(kind="sweep1d", count=2000, seed=SEED_BASE + 1),
+    # 2-D CIC current deposit, 512^2 periodic, 16 particles per cell
+    "cic2d_512_ppc16": dict(kind="deposit", dim=2, n=[512, 512], ppc=16, order=1, T=8, D=1,
+                            seed=SEED_BASE + 2),
+    # 3-D CIC current deposit, 128^3 periodic, 32 per cell, 2% pushed 2-4 cells
+    "cic3d_128_ppc32": dict(kind="deposit", dim=3, n=[128, 128, 128], ppc=32, order=1, T=8,
+                            D=1, far_fraction=0.02, seed=SEED_BASE + 3),
+    # 3-D TSC current deposit, 128^3 periodic, 16 per cell on average, Gaussian blob
+    "tsc3d_128_blob": dict(kind="deposit", dim=3, n=[128, 128, 128], count=33554432, order=2,
+                           Ts=[4, 8, 16], D=1, blob=dict(sigma=10.0, overdensity=20.0),
+                           w_uniform=True, seed=SEED_BASE + 4),
+    # ECSIM CIC mass matrix, 64^3 periodic, 64 particles per cell
+    "mass_64_ppc64": dict(kind="mass", n=[64, 64, 64], ppc=64, seed=SEED_BASE + 5),
 }
 
 
-def config(k: int, scale: Optional[dict] = None):
-    """Workload k at full size, or with fields of CONFIG_INFO[k] overridden by scale."""
-    info = dict(CONFIG_INFO[k])
+def workload(name: str, scale: Optional[dict] = None):
+    """The named workload at full size, or with fields of WORKLOADS[name] overridden by scale."""
+    info = dict(WORKLOADS[name])
     if scale:
         info.update(scale)
-    seed = SEED_BASE + k
+    seed = info["seed"]
     if info["kind"] == "sweep1d":
         return sweep_workload(count=info["count"], seed=seed)
     if info["kind"] == "mass":

@@ -45,11 +45,11 @@ def particle_arrays(wl, use_next=True):
 _FULL = {}
 
 
-def full_config(k):
-    """Full-size workload k, generated once per test session."""
+def full_workload(name):
+    """The named full-size workload, generated once per test session."""
     import synthetic
 
-    if k not in _FULL:
+    if name not in _FULL:
         _FULL.clear()   # keep at most one full-size workload in host memory
-        _FULL[k] = synthetic.config(k)
-    return _FULL[k]
+        _FULL[name] = synthetic.workload(name)
+    return _FULL[name]

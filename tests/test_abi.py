@@ -35,7 +35,8 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["pcg_tile_sort", "pcg_sort_workspace_bytes", "deposit_currents",
-              "pcg_deposit_workspace_bytes", "assemble_mass_matrix", "deposit_sweep1d",
+              "pcg_deposit_workspace_bytes", "deposit_currents_regroup",
+              "pcg_deposit_regroup_workspace_bytes", "assemble_mass_matrix", "deposit_sweep1d",
               "pcg_status_string", "pcg_last_error", "pcg_version", "pcg_timing_enable",
               "pcg_timing_reset", "pcg_timing_read", "pcg_timing_names"]:
         assert n in names
@@ -142,6 +143,32 @@ def test_deposit_workspace_size(lib):
     t = Tile(8, 1, 1, 0, 0, FAKE)
     assert lib.pcg_deposit_workspace_bytes(C.byref(g), C.byref(t)) >= 4097 * 4
     assert lib.pcg_deposit_workspace_bytes(C.byref(g), None) == 0
+
+
+def test_regroup_validation(lib):
+    lib.pcg_deposit_regroup_workspace_bytes.restype = C.c_size_t
+    fr = lib.deposit_currents_regroup
+    g = grid(3, [32, 32, 32])
+    P = particles(1000)
+    arr = (C.c_void_p * 1)(FAKE)
+    outs = (C.c_void_p * 1)(FAKE + 4096)
+    t = Tile(8, 1, 1, 0, 1000, FAKE)
+    need = lib.pcg_deposit_regroup_workspace_bytes(C.byref(g), C.byref(t), C.c_int64(1000))
+    assert need >= lib.pcg_sort_workspace_bytes(C.byref(g), C.c_int64(1000), 8)
+    assert lib.pcg_deposit_regroup_workspace_bytes(C.byref(g), None, C.c_int64(1000)) == 0
+
+    def call(tile=t, P=P, ws=FAKE, wsb=need, off=FAKE + 8192, J=FAKE, order=1):
+        return fr(C.byref(g), C.byref(P), order, C.byref(tile) if tile else None, C.c_void_p(J),
+                  None, 1, arr, outs, C.c_void_p(off), C.c_void_p(ws), C.c_size_t(wsb), None)
+
+    assert call(tile=None) == EINVAL                              # needs the current layout
+    assert call(wsb=need - 1) == EWORKSPACE
+    assert call(ws=FAKE + 8) == EWORKSPACE                        # misaligned
+    assert call(J=0) == EINVAL
+    assert call(order=3) == EUNSUPPORTED
+    assert call(tile=Tile(8, 2, 1, 0, 1000, FAKE)) == EINVAL      # keyed with TSC
+    assert call(off=0) == EINVAL                                  # no output offsets
+    assert call(off=FAKE) == EINVAL                               # output offsets alias the layout
 
 
 def test_tile_sort_validation(lib):

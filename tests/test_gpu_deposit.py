@@ -11,7 +11,7 @@ import torch
 
 import particle_cell_grid_amd as pcg
 import synthetic
-from gpu_util import DEV, dev, full_config, rel_max_err, say
+from gpu_util import DEV, dev, full_workload, rel_max_err, say
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-5
@@ -145,42 +145,42 @@ def test_single_particle_and_empty(orc):
 
 # ---------------------------------------------------------------- full sizes
 
-def _full(orc, k, order, T, D=1):
-    wl = full_config(k)
+def _full(orc, name, order, T, D=1):
+    wl = full_workload(name)
     s, off = _sorted_pushed(orc, wl, order, T)
     return wl, s, off
 
 
-def test_full_size_config2(orc):
-    wl, s, off = _full(orc, 2, 1, 8)
+def test_full_size_cic2d_512(orc):
+    wl, s, off = _full(orc, "cic2d_512_ppc16", 1, 8)
     J, esc = _run_tiled(s, 1, 8, 1, off)
     ref = orc.deposit(2, wl.n, 1, s.x_next, s.v, s.q, s.w)
     assert rel_max_err(J, ref) <= TOL and esc == 0
 
 
-def test_full_size_config3(orc):
+def test_full_size_cic3d_128(orc):
     """Headline workload: 128^3, 32 ppc, 67.1M particles, 2% displaced 2-4 cells."""
-    wl, s, off = _full(orc, 3, 1, 8)
+    wl, s, off = _full(orc, "cic3d_128_ppc32", 1, 8)
     J, esc = _run_tiled(s, 1, 8, 1, off)
     ref = orc.deposit(3, wl.n, 1, s.x_next, s.v, s.q, s.w)
     n_ref, _ = orc.escape(3, wl.n, 1, 8, 1, s.x_next, off)
     err = rel_max_err(J, ref)
-    say("config3 rel err", err, "escaped", esc, n_ref)
+    say("cic3d_128 rel err", err, "escaped", esc, n_ref)
     assert err <= TOL and esc == n_ref and n_ref > 0
 
 
-_C4 = {}
+_TSC_REF = {}
 
 
 @pytest.mark.parametrize("T", [4, 8, 16])
-def test_full_size_config4(orc, T):
+def test_full_size_tsc3d_blob(orc, T):
     """Clustered TSC workload (33.5M particles), tile edge swept over {4, 8, 16}."""
-    wl = full_config(4)
+    wl = full_workload("tsc3d_128_blob")
     s, off = _sorted_pushed(orc, wl, 2, T)
     J, esc = _run_tiled(s, 2, T, 1, off)
-    if "ref" not in _C4:
-        _C4["ref"] = orc.deposit(3, wl.n, 2, wl.x_next, wl.v, wl.q, wl.w)
-    assert rel_max_err(J, _C4["ref"]) <= TOL and esc == 0
+    if "ref" not in _TSC_REF:
+        _TSC_REF["ref"] = orc.deposit(3, wl.n, 2, wl.x_next, wl.v, wl.q, wl.w)
+    assert rel_max_err(J, _TSC_REF["ref"]) <= TOL and esc == 0
 
 
 # ---------------------------------------------------------------- magnitudes

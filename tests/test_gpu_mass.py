@@ -10,7 +10,7 @@ import torch
 
 import particle_cell_grid_amd as pcg
 import synthetic
-from gpu_util import DEV, dev, full_config, rel_frob_err, say
+from gpu_util import DEV, dev, full_workload, rel_frob_err, say
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-4
@@ -89,11 +89,11 @@ def test_mass_zero_field_reduces_to_scalar(orc):
     assert np.allclose(M[..., 0, 0], M[..., 2, 2], rtol=1e-6, atol=1e-6)
 
 
-def test_mass_full_size_config5(orc):
+def test_mass_full_size_64(orc):
     """64^3, 64 ppc (16.8M particles).  The oracle runs on the particles of a
     z-slab of cells; rows of nodes whose 8 adjacent cells all lie in the slab are
     compared, plus the global totals sum_{g,o} M = sum_p q w alpha_p."""
-    wl = full_config(5)
+    wl = full_workload("mass_64_ppc64")
     _, perm, off = orc.tile_sort(3, wl.n, 1, 1, wl.x)
     M = _run(wl, perm, off, pcg.PCG_MASS_MFMA)
     z0, z1 = 20, 30

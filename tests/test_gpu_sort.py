@@ -6,7 +6,7 @@ import torch
 
 import particle_cell_grid_amd as pcg
 import synthetic
-from gpu_util import DEV, dev, full_config, say, u32
+from gpu_util import DEV, dev, full_workload, say, u32
 
 pytestmark = pytest.mark.gpu
 
@@ -66,7 +66,7 @@ def test_sort_skewed_all_in_one_tile(orc):
 
 def test_sort_nearly_sorted_steady_state(orc):
     """Re-sorting pushed particles that were sorted one step earlier (the every-step case)."""
-    wl = synthetic.config(3, dict(n=[64, 64, 64], ppc=8))
+    wl = synthetic.workload("cic3d_128_ppc32", dict(n=[64, 64, 64], ppc=8))
     k, p, o = orc.tile_sort(3, wl.n, 1, 8, wl.x)
     s = wl.take(p.astype(np.int64))
     _check_sort(orc, 3, wl.n, 1, 8, s.x_next, s.x_next + s.v + [s.q, s.w])
@@ -80,15 +80,15 @@ def test_sort_deterministic_repeat(orc):
     assert all(torch.equal(res[0], r) for r in res[1:])
 
 
-def test_sort_full_size_config3(orc):
+def test_sort_full_size_cic3d_128(orc):
     """The headline workload's size: 67.1M particles, 4096 tiles (shuffled input)."""
-    wl = full_config(3)
+    wl = full_workload("cic3d_128_ppc32")
     _check_sort(orc, 3, wl.n, 1, 8, wl.x)
 
 
-def test_sort_full_size_config5_cells(orc):
+def test_sort_full_size_mass_cells(orc):
     """16.8M particles into 262,144 cells (the mass-matrix layout)."""
-    wl = full_config(5)
+    wl = full_workload("mass_64_ppc64")
     _check_sort(orc, 3, wl.n, 1, 1, wl.x, [wl.beta])
 
 
@@ -164,9 +164,9 @@ def test_resort_heavy_tiles(orc):
     _check_resort(orc, s, 2, 8, off, s.x_next, s.x_next + [s.q])
 
 
-def test_resort_full_size_config3(orc):
+def test_resort_full_size_cic3d_128(orc):
     """The bench step's sort: 67.1M pushed particles re-sorted from their layout."""
-    wl = full_config(3)
+    wl = full_workload("cic3d_128_ppc32")
     s, off = _sorted_state(orc, wl, 1, 8)
     _check_resort(orc, s, 1, 8, off, s.x_next, [s.x_next[0], s.q])
 

@@ -21,8 +21,8 @@ def _run(nb, x0, v, T, dt, hw):
     return H.cpu().numpy()
 
 
-def test_config1(orc):
-    s = synthetic.config(1)
+def test_sweep_workload(orc):
+    s = synthetic.workload("sweep1d_2000")
     H = _run(s.nb, s.x0, s.v, s.T, s.dt, s.hw)
     ref = orc.sweep1d(s.nb, s.x0, s.v, s.T, s.dt, s.hw)
     assert rel_max_err(H, ref) <= 1e-5

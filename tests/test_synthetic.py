@@ -71,7 +71,7 @@ def test_sweep_statistics_match_page_scale():
     """About 1% of particles in the window per step, a per-step maximum near the
     page's capacity of 30 at N = 2000, and about half ever selected (983/2000)."""
     g = json.load(open(os.path.join(GOLDEN, "pages_structural.json")))["sweep_statistics"]
-    wl = synthetic.config(1)
+    wl = synthetic.workload("sweep1d_2000")
     t = np.arange(1, wl.T + 1)[:, None]
     x = np.mod(wl.x0[None] + wl.v[None] * (t * wl.dt), 1.0)
     d = x - t / wl.T
@@ -81,3 +81,21 @@ def test_sweep_statistics_match_page_scale():
     assert abs(per_step.mean() / g["count"] - g["window_fraction_per_step"]) < 0.003
     assert 0.7 * g["capacity_printed"] <= per_step.max() <= 1.4 * g["capacity_printed"]
     assert 0.8 < sel.any(axis=0).sum() / g["ever_selected_printed"] < 1.2
+
+
+def test_every_named_workload_builds_small():
+    """Each named workload generates (shrunk) with its own seed and recipe."""
+    small = {"sweep1d_2000": dict(count=64),
+             "cic2d_512_ppc16": dict(n=[16, 16], ppc=2),
+             "cic3d_128_ppc32": dict(n=[16, 16, 16], ppc=2),
+             "tsc3d_128_blob": dict(n=[16, 16, 16], count=4096,
+                                    blob=dict(sigma=2.0, overdensity=20.0)),
+             "mass_64_ppc64": dict(n=[8, 8, 8], ppc=2)}
+    assert set(small) == set(synthetic.WORKLOADS)
+    for name, scale in small.items():
+        a = synthetic.workload(name, scale)
+        b = synthetic.workload(name, scale)
+        if name == "sweep1d_2000":
+            assert a.x0.size == 64 and np.array_equal(a.x0, b.x0)
+        else:
+            assert a.count > 0 and all(np.array_equal(p, r) for p, r in zip(a.x, b.x))

@@ -40,11 +40,15 @@ _lib = None
 
 
 def lib():
+    """The loaded oracle library.  PCG_ORACLE_LIB names another build of
+    oracle.c to load instead (the mutant tests load copies with a planted
+    mistake, to show that the pins catch it)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        path = os.environ.get("PCG_ORACLE_LIB") or _LIB
+        if path == _LIB and not os.path.exists(_LIB):
             build(force=True)
-        L = C.CDLL(_LIB)
+        L = C.CDLL(path)
         i32p = C.POINTER(C.c_int32)
         fpp = C.POINTER(C.c_void_p)
         L.oracle_shape_1d.argtypes = [C.c_int, C.c_double, C.POINTER(C.c_int64), C.c_void_p]

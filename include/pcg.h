@@ -204,6 +204,10 @@ pcg_status deposit_currents_regroup(const pcg_grid *grid, const pcg_particles *p
 #define PCG_MASS_VALU 2   /* the same per-cell contraction with vector FMAs         */
 #define PCG_MASS_FLAT 3   /* one thread per particle, 576 global atomics each      */
 
+/* Bytes of device workspace assemble_mass_matrix needs with a cell layout
+ * (MFMA and VALU variants). */
+size_t pcg_mass_workspace_bytes(const pcg_grid *grid);
+
 /* M^{ij}_{g, g+o} += q_p w_p alpha_p^{ij} W_{pg} W_{p,g+o} over every ordered
  * pair of the 8 CIC support nodes of every particle, with
  * alpha_p = (I - C(omega) + omega omega^T) / (1 + |omega|^2), C(omega)u = omega x u,
@@ -213,13 +217,21 @@ pcg_status deposit_currents_regroup(const pcg_grid *grid, const pcg_particles *p
  *   o = (dx+1) + 3(dy+1) + 9(dz+1) for the node g + (dx,dy,dz) (wrapped).
  * B[3], beta: device fp32 per-particle magnetic field and beta = q dt / (2m).
  * cells: a T = 1, order = 1 layout from pcg_tile_sort (cell c owns its slice;
- *   [MM] §3.1 assumes particles sorted by cell), or NULL (flat path).  A
- *   particle found in the slice of a cell it is not in is deposited by the
- *   flat path; the tail [n_partitioned, count) likewise.
- * variant: PCG_MASS_*; VALU and MFMA need `cells`. */
+ *   [MM] §3.1 assumes particles sorted by cell), or NULL (flat path).  With a
+ *   layout, the per-cell contractions ([MM] §3.2, Eq.(14)-(20)) are summed
+ *   into each row of M by the work-group that owns the row, and every row is
+ *   read and written once (no atomics).  A particle found in the slice of a
+ *   cell it is not in is deposited by the flat path after that; the tail
+ *   [n_partitioned, count) likewise.  Calls that write the same M on
+ *   different streams race.
+ * variant: PCG_MASS_*; VALU and MFMA need `cells`.
+ * workspace: device memory of at least pcg_mass_workspace_bytes() bytes,
+ *   256-byte aligned, needed when `cells` is given (may be NULL otherwise);
+ *   contents undefined on entry and exit. */
 pcg_status assemble_mass_matrix(const pcg_grid *grid, const pcg_particles *particles,
                                 const float *const B[3], const float *beta,
-                                const pcg_tile *cells, int32_t variant, float *M, void *stream);
+                                const pcg_tile *cells, int32_t variant, float *M,
+                                void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* 1-D windowed sweep  ([CS] "The problem", "Code")                          */

@@ -63,8 +63,10 @@ _lib.deposit_currents_regroup.argtypes = [_P(Grid), _P(Particles), C.c_int32, _P
                                           C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
                                           C.c_void_p]
 _lib.deposit_currents_regroup.restype = C.c_int32
+_lib.pcg_mass_workspace_bytes.argtypes = [_P(Grid)]
+_lib.pcg_mass_workspace_bytes.restype = C.c_size_t
 _lib.assemble_mass_matrix.argtypes = [_P(Grid), _P(Particles), C.c_void_p, C.c_void_p, _P(Tile),
-                                      C.c_int32, C.c_void_p, C.c_void_p]
+                                      C.c_int32, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
 _lib.assemble_mass_matrix.restype = C.c_int32
 _lib.deposit_sweep1d.argtypes = [C.c_int32, C.c_int64, C.c_void_p, C.c_void_p, C.c_int32,
                                  C.c_double, C.c_double, C.c_void_p, C.c_void_p]
@@ -259,17 +261,28 @@ def deposit_currents_regroup(dim: int, n: Sequence[int], order: int, x: List[tor
     return tile_offsets, outs
 
 
+def pcg_mass_workspace_bytes(n: Sequence[int]) -> int:
+    g = make_grid(3, n)
+    return int(_lib.pcg_mass_workspace_bytes(C.byref(g)))
+
+
 def assemble_mass_matrix(n: Sequence[int], x: List[torch.Tensor], B: List[torch.Tensor],
                          beta: torch.Tensor, q: torch.Tensor, w: torch.Tensor, M: torch.Tensor,
-                         cells: Optional[Layout] = None, variant: int = PCG_MASS_AUTO):
-    """M[nz, ny, nx, 27, 3, 3] (fp32) += the ECSIM CIC mass matrix."""
+                         cells: Optional[Layout] = None, variant: int = PCG_MASS_AUTO,
+                         workspace: Optional[torch.Tensor] = None):
+    """M[nz, ny, nx, 27, 3, 3] (fp32) += the ECSIM CIC mass matrix.  With a cell
+    layout a workspace of pcg_mass_workspace_bytes() is needed; one is taken
+    from torch's allocator when none is given."""
     g = make_grid(3, n)
     P = _particles(q.numel(), x, None, q, w)
     bp = (C.c_void_p * 3)(*[b.data_ptr() for b in B])
     tile = cells.to_c() if cells is not None else None
+    if cells is not None and workspace is None:
+        workspace = torch.empty(pcg_mass_workspace_bytes(n), dtype=torch.uint8, device=M.device)
+    wsb = int(workspace.numel()) if workspace is not None else 0
     st = _lib.assemble_mass_matrix(C.byref(g), C.byref(P), bp, _ptr(beta),
                                    C.byref(tile) if tile is not None else None, int(variant),
-                                   _ptr(M), _stream())
+                                   _ptr(M), _ptr(workspace), wsb, _stream())
     _check(st, "assemble_mass_matrix")
     return M
 

@@ -2,7 +2,8 @@
 
 Run as a script (``python particle_cell_grid_amd/csrc/build.py``) or call
 ``build()``; it does not import the package, so it works before anything is
-built.  Every .hip source in this directory is compiled in one hipcc call.
+built.  Every .hip source in this directory is compiled to an object (in parallel,
+under _build/) and the objects are linked into the shared library.
 
 Flags: -O3, C++17, gfx950 only, and packed-FP32 instruction selection turned
 off (``-target-feature -packed-fp32-ops``) so hipcc never emits v_pk_*_f32.
@@ -31,8 +32,27 @@ def sources():
 
 
 def build(verbose: bool = False) -> str:
+    """Compile every .hip source to an object (in parallel), then link libpcg.so."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    obj_dir = os.path.join(HERE, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", HERE]
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+
+    def compile_one(src):
+        obj = os.path.join(obj_dir, os.path.basename(src)[:-4] + ".o")
+        cmd = [HIPCC, *compile_flags, *inc, "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.check_call(cmd)
+        return obj
+
+    srcs = sources()
+    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(compile_one, srcs))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", HERE, *sources(), "-o", tmp]
+    cmd = [HIPCC, *FLAGS, *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)

@@ -18,13 +18,17 @@
 // Tiles (0,0), (0,1), (1,1) of the 2x2 tile grid hold all ten moments; tile
 // (1,0) is skipped (symmetry, as in the paper's Table 1 for TSC).
 //
-// Flush ([MM] §3.4): lane (a,b) forms the nine M^{ij}_{ab} and adds them to the
-// 27-offset store at row g_a, offset o(b - a) with global atomics.
+// Assembly of M: instead of [MM] §3.4's per-cell flush with global atomics, a
+// work-group owns a column of nodes, computes every cell that touches it (the
+// cells on its low faces are computed by both neighbouring columns), adds each
+// cell's block into LDS copies of two node planes and adds each finished plane
+// to M once with plain loads and stores (see k_mass_column).  M is then
+// written once per assembly, not once per cell-node pair.
 //
-// Variants: MFMA (one wave per cell), VALU (same staging, each lane
-// accumulating its (a,b) moments with FMAs) and FLAT (one thread per particle,
-// alpha computed directly, 576 global atomics -- also used for the tail and for
-// particles found in a cell slice they do not belong to).
+// Variants: MFMA and VALU (the same column kernel; the moments of a cell come
+// from the matrix cores or from per-lane FMAs) and FLAT (one thread per
+// particle, alpha computed directly, 576 global atomics -- also used for the
+// unsorted tail and for particles found in a cell slice they do not lie in).
 #include <algorithm>
 
 #include "common.hpp"
@@ -55,13 +59,38 @@ struct Particle {
     int base[3];    // cell (= first support node) per axis
 };
 
-__device__ inline Particle load_particle(const MassArgs &m, int64_t p)
+// The nine per-particle input values, as loaded.
+struct RawParticle {
+    float x[3], B[3], q, w, beta;
+};
+
+__device__ inline RawParticle load_raw(const MassArgs &m, int64_t p)
+{
+    // particle counts are below 2^31, so a 32-bit byte offset from each array's
+    // base addresses every element (one scalar base + one vector offset)
+    const uint32_t off = (uint32_t)p * 4u;
+    auto at = [off](const float *base) {
+        return *reinterpret_cast<const float *>(reinterpret_cast<const char *>(base) + off);
+    };
+    RawParticle r;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        r.x[k] = at(m.x[k]);
+        r.B[k] = at(m.B[k]);
+    }
+    r.q = at(m.q);
+    r.w = at(m.w);
+    r.beta = at(m.beta);
+    return r;
+}
+
+__device__ inline Particle make_particle(const MassArgs &m, const RawParticle &r)
 {
     Particle P;
     float wx[3][2];
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
-        const float x = clamp_coord(m.x[k][p], m.nf[k]);
+        const float x = clamp_coord(r.x[k], m.nf[k]);
         const float fl = floorf(x);
         const float xi = x - fl;
         P.base[k] = wrap_index((int)fl, m.n[k]);
@@ -71,14 +100,19 @@ __device__ inline Particle load_particle(const MassArgs &m, int64_t p)
 #pragma unroll
     for (int a = 0; a < 8; ++a)
         P.W[a] = wx[0][a & 1] * wx[1][(a >> 1) & 1] * wx[2][a >> 2];
-    const float bt = m.beta[p];
-    const float o0 = bt * m.B[0][p], o1 = bt * m.B[1][p], o2 = bt * m.B[2][p];
+    const float bt = r.beta;
+    const float o0 = bt * r.B[0], o1 = bt * r.B[1], o2 = bt * r.B[2];
     P.u[0] = 1.0f;
     P.u[1] = o0;
     P.u[2] = o1;
     P.u[3] = o2;
-    P.c = m.q[p] * m.w[p] / (1.0f + (o0 * o0 + o1 * o1 + o2 * o2));
+    P.c = r.q * r.w / (1.0f + (o0 * o0 + o1 * o1 + o2 * o2));
     return P;
+}
+
+__device__ inline Particle load_particle(const MassArgs &m, int64_t p)
+{
+    return make_particle(m, load_raw(m, p));
 }
 
 __device__ inline int64_t node_index(const MassArgs &m, const int *base, int a)
@@ -142,23 +176,76 @@ __global__ __launch_bounds__(256) void k_mass_flat(MassArgs m, int64_t begin, in
         deposit_particle_global(m, load_particle(m, p));
 }
 
-// LDS staging of one 64-particle batch of a cell (one wave per work-group).
+__device__ inline void cell_coords(const MassArgs &m, uint32_t cell, int *cc)
+{
+    cc[0] = (int)(cell % (uint32_t)m.n[0]);
+    cc[1] = (int)((cell / (uint32_t)m.n[0]) % (uint32_t)m.n[1]);
+    cc[2] = (int)(cell / ((uint32_t)m.n[0] * (uint32_t)m.n[1]));
+}
+
+// ---------------------------------------------------------------- column kernel
+//
+// Owner-computes assembly ([MM] §3.4 flushes per-cell blocks with atomics; here
+// every row of M is written exactly once, by plain loads and stores):
+// a work-group owns a column of COL_X x COL_Y x COL_Z nodes and walks the cell
+// layers below and through it (z from the column's first node - 1 upwards).
+// Node g receives from the eight cells g - {0,1}^3, so the work-group processes
+// the (COL_X+1) x (COL_Y+1) x (COL_Z+1) cells that touch its nodes -- the cells
+// on the low faces are also processed by the neighbouring column, each keeping
+// only the entries of its own nodes.  Two node planes of the column live in
+// LDS (27 x 9 fp32 per node): cell layer iz adds to node planes iz-1 and iz
+// (local numbering), so node plane iz-1 is complete after layer iz and is added
+// to M and its buffer cleared for plane iz+1.
+// Within a layer, the cells are taken in four colour classes by (x, y) parity:
+// two cells of one class share no node, so the waves that process them add to
+// the planes without atomics; a barrier separates the classes.
+#ifndef PCG_COL_X
+#define PCG_COL_X 8
+#define PCG_COL_Y 4
+#define PCG_COL_Z 16
+#endif
+constexpr int COL_X = PCG_COL_X, COL_Y = PCG_COL_Y, COL_Z = PCG_COL_Z;
+constexpr int COL_WAVES = 4;
+constexpr int COL_NODES = COL_X * COL_Y;
+constexpr int ROW = 27 * 9;  // floats per node row of M
+
+// LDS staging of one 64-particle batch of a cell, per wave; reused for the
+// 32 x 32 moment tile once the batches are done.
 struct Stage {
     float W[64][8];
     float u[64][4];  // stored as (u0, u2, u1, u3) so (u_k, u_{k+2}) are adjacent
     float c[64];
 };
+union WaveScratch {
+    Stage s;
+    float Tm[32][33];
+};
 
-// Loads particle slot `p` (if it belongs to `cell`) into lane's staging row;
-// particles that are not in `cell` are deposited directly and staged as zero.
-__device__ inline void stage_particle(const MassArgs &m, Stage &s, int lane, int64_t p,
-                                      int64_t end, const int *cell)
+constexpr size_t column_lds_bytes()
+{
+    return sizeof(float) * 2 * COL_NODES * ROW + sizeof(WaveScratch) * COL_WAVES;
+}
+
+// Orders this wave's earlier LDS accesses before its later ones (lanes exchange
+// data through LDS within one wave only).
+__device__ inline void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Stages one particle (raw values, valid = the slot is inside the cell's slice)
+// into the lane's row.  A particle that lies in another cell (a stale layout)
+// is staged as zero and reported through *stray: the follow-up pass deposits it.
+__device__ inline void stage_raw(const MassArgs &m, Stage &s, int lane, const RawParticle &r,
+                                 bool valid, const int *cell, bool *stray)
 {
     float W[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     float u[4] = {0, 0, 0, 0};
     float c = 0.0f;
-    if (p < end) {
-        Particle P = load_particle(m, p);
+    if (valid) {
+        const Particle P = make_particle(m, r);
         if (P.base[0] == cell[0] && P.base[1] == cell[1] && P.base[2] == cell[2]) {
 #pragma unroll
             for (int a = 0; a < 8; ++a)
@@ -168,141 +255,431 @@ __device__ inline void stage_particle(const MassArgs &m, Stage &s, int lane, int
                 u[k] = P.u[k];
             c = P.c;
         } else {
-            deposit_particle_global(m, P);
+            *stray = true;
         }
     }
-#pragma unroll
-    for (int a = 0; a < 8; ++a)
-        s.W[lane][a] = W[a];
-    s.u[lane][0] = u[0];
-    s.u[lane][1] = u[2];
-    s.u[lane][2] = u[1];
-    s.u[lane][3] = u[3];
+    float4 *w4 = reinterpret_cast<float4 *>(s.W[lane]);
+    w4[0] = make_float4(W[0], W[1], W[2], W[3]);
+    w4[1] = make_float4(W[4], W[5], W[6], W[7]);
+    *reinterpret_cast<float4 *>(s.u[lane]) = make_float4(u[0], u[2], u[1], u[3]);
     s.c[lane] = c;
 }
 
-__device__ inline void cell_coords(const MassArgs &m, uint32_t cell, int *cc)
+// One wave: the ten moments of cell `cell` (wrapped coordinates), whose slice
+// is [lo, hi), for this lane's node pair (a, b) = (lane / 8, lane % 8):
+// t[k][l] for k <= l.  `first` holds the lane's particle of the first batch
+// (slot lo + lane), loaded ahead by the caller; later batches (cells of more
+// than 64 particles) are loaded here.
+template <bool MFMA>
+__device__ inline void cell_moments(const MassArgs &m, WaveScratch &ws, int lane, const int *cell,
+                                    int64_t lo, int64_t hi, const RawParticle &first, bool *stray,
+                                    float t[4][4])
 {
-    cc[0] = (int)(cell % (uint32_t)m.n[0]);
-    cc[1] = (int)((cell / (uint32_t)m.n[0]) % (uint32_t)m.n[1]);
-    cc[2] = (int)(cell / ((uint32_t)m.n[0] * (uint32_t)m.n[1]));
-}
-
-// Adds lane (a,b)'s nine values, from moments t, to the global store.
-__device__ inline void flush_pair(const MassArgs &m, const int *cc, int a, int b,
-                                  const float t[4][4])
-{
-    float blk[9];
-    moments_to_block(t, blk);
-    const int64_t g = node_index(m, cc, a);
-    float *row = m.M + ((size_t)g * 27 + offset_index(a, b)) * 9;
 #pragma unroll
-    for (int ij = 0; ij < 9; ++ij)
-        atomic_add_f32(&row[ij], blk[ij]);
-}
-
-__global__ __launch_bounds__(64) void k_mass_mfma(MassArgs m)
-{
-    __shared__ Stage s;
-    __shared__ float Tm[32][33];
-    const uint32_t cell = blockIdx.x;
-    const int64_t lo = std::min<int64_t>(m.cell_offsets[cell], m.n_part);
-    const int64_t hi = std::min<int64_t>(m.cell_offsets[cell + 1], m.n_part);
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int l = 0; l < 4; ++l)
+            t[k][l] = 0.0f;
     if (hi <= lo)
         return;
-    const int lane = threadIdx.x;
-    int cc[3];
-    cell_coords(m, cell, cc);
-
-    // operand coordinates of this lane: row/col index r = l % 16 of a 16-row
-    // block, particle k = l / 16 of the 4-particle batch
+    const int pa = lane >> 3, pb = lane & 7;
+    // operand coordinates (MFMA): row/col index r = lane % 16 of a 16-row
+    // block, particle kk = lane / 16 of the 4-particle batch
     const int r = lane & 15, kk = lane >> 4;
     const int a = r & 7, khalf = r >> 3;  // node a, moment index k = khalf (+2)
     floatx4 acc00 = {0, 0, 0, 0}, acc01 = {0, 0, 0, 0}, acc11 = {0, 0, 0, 0};
-
-    for (int64_t base = lo; base < hi; base += 64) {
-        stage_particle(m, s, lane, base + lane, hi, cc);
-        __syncthreads();
+    auto batch = [&](const RawParticle &rp, int64_t base) {
+        wave_sync();
+        stage_raw(m, ws.s, lane, rp, base + lane < hi, cell, stray);
+        wave_sync();
         const int nb = (int)std::min<int64_t>(64, hi - base);
-        const int batches = (nb + 3) >> 2;
-        for (int bt = 0; bt < batches; ++bt) {
-            const int p = 4 * bt + kk;
-            const float wa = s.W[p][a];
-            const float2 uu = *reinterpret_cast<const float2 *>(&s.u[p][2 * khalf]);
-            const float cp = s.c[p];
-            const float a0 = uu.x * wa;  // u_k W_a      (k = khalf)
-            const float a1 = uu.y * wa;  // u_{k+2} W_a
-            const float b0 = cp * a0;
-            const float b1 = cp * a1;
-            acc00 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc00, 0, 0, 0);
-            acc01 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc01, 0, 0, 0);
-            acc11 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc11, 0, 0, 0);
-        }
-        __syncthreads();
-    }
-    // accumulator layout: lane holds D[4*(lane/16) + i][lane % 16], i = 0..3
+        if (MFMA) {
+            // one 4-particle batch: operands from the staged rows, three MFMAs
+            auto mfma_batch = [&](float wa, float2 uu, float cp) {
+                const float a0 = uu.x * wa;  // u_k W_a      (k = khalf)
+                const float a1 = uu.y * wa;  // u_{k+2} W_a
+                const float b0 = cp * a0;
+                const float b1 = cp * a1;
+                acc00 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc00, 0, 0, 0);
+                acc01 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc01, 0, 0, 0);
+                acc11 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc11, 0, 0, 0);
+            };
+            if (nb == 64) {
+                // a full batch: the operands of all sixteen 4-particle steps are
+                // read first (one LDS round trip), then the 48 products issue
+                // back to back
+                float wa[16], cp[16];
+                float2 uu[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 4 * kk + i, col = r;
-        Tm[row][col] = acc00[i];
-        Tm[row][16 + col] = acc01[i];
-        Tm[16 + row][16 + col] = acc11[i];
+                for (int i = 0; i < 16; ++i) {
+                    const int q = 4 * i + kk;
+                    wa[i] = ws.s.W[q][a];
+                    uu[i] = *reinterpret_cast<const float2 *>(&ws.s.u[q][2 * khalf]);
+                    cp[i] = ws.s.c[q];
+                }
+                // keep the reads ahead of the products (the scheduler would
+                // otherwise interleave them and wait once per step)
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    mfma_batch(wa[i], uu[i], cp[i]);
+            } else {
+                const int batches = (nb + 3) >> 2;
+                for (int bt = 0; bt < batches; ++bt) {
+                    const int q = 4 * bt + kk;
+                    mfma_batch(ws.s.W[q][a], *reinterpret_cast<const float2 *>(&ws.s.u[q][2 * khalf]),
+                               ws.s.c[q]);
+                }
+            }
+        } else {
+            for (int q = 0; q < nb; ++q) {
+                const float wab = ws.s.c[q] * ws.s.W[q][pa] * ws.s.W[q][pb];
+                const float u[4] = {ws.s.u[q][0], ws.s.u[q][2], ws.s.u[q][1], ws.s.u[q][3]};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float wk = wab * u[k];
+#pragma unroll
+                    for (int l = k; l < 4; ++l)
+                        t[k][l] += wk * u[l];
+                }
+            }
+        }
+    };
+    batch(first, lo);
+    // cells of more than 64 particles: the later batches load here
+    for (int64_t base = lo + 64; base < hi; base += 64) {
+        RawParticle rp{};
+        if (base + lane < hi)
+            rp = load_raw(m, base + lane);
+        batch(rp, base);
     }
-    __syncthreads();
-    {
-        const int pa = lane >> 3, pb = lane & 7;
-        float t[4][4];
+    wave_sync();
+    if (MFMA) {
+        // accumulator layout: lane holds D[4*(lane/16) + i][lane % 16], i = 0..3
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 4 * kk + i, col = r;
+            ws.Tm[row][col] = acc00[i];
+            ws.Tm[row][16 + col] = acc01[i];
+            ws.Tm[16 + row][16 + col] = acc11[i];
+        }
+        wave_sync();
 #pragma unroll
         for (int k = 0; k < 4; ++k)
 #pragma unroll
             for (int l = k; l < 4; ++l)
-                t[k][l] = Tm[8 * k + pa][8 * l + pb];
-        flush_pair(m, cc, pa, pb, t);
+                t[k][l] = ws.Tm[8 * k + pa][8 * l + pb];
+        wave_sync();
     }
 }
 
-__global__ __launch_bounds__(64) void k_mass_valu(MassArgs m)
+// Values of one y row of a column plane (COL_X nodes, contiguous in M) each
+// thread adds to M after a layer.
+constexpr int COL_ROW_PER_THREAD = (COL_X * ROW + COL_WAVES * WAVE - 1) / (COL_WAVES * WAVE);
+
+struct ColumnGeom {
+    int ncol[3];  // columns per axis
+    uint32_t nwork;
+    uint32_t *stray_flag;
+};
+
+// The column one work-group owns: first node and node count per axis; the
+// cells touching it have local index i <-> cell first - 1 + i, i < count + 1.
+struct ColumnShape {
+    int first[3], count[3];
+};
+
+// Cells of one colour class (x, y parity) in a layer; nx of them per row.
+__device__ inline int colour_cells(const ColumnShape &c, int colour, int &nx)
 {
-    __shared__ Stage s;
-    const uint32_t cell = blockIdx.x;
-    const int64_t lo = std::min<int64_t>(m.cell_offsets[cell], m.n_part);
-    const int64_t hi = std::min<int64_t>(m.cell_offsets[cell + 1], m.n_part);
-    if (hi <= lo)
+    const int px = colour & 1, py = colour >> 1;
+    nx = (c.count[0] + 1 - px + 1) / 2;
+    return nx * ((c.count[1] + 1 - py + 1) / 2);
+}
+
+// Cells per wave and phase: the largest colour class of a full column,
+// ceil((COL_X+2)/2) * ceil((COL_Y+2)/2), shared by the work-group's waves.
+constexpr int COL_SLOTS =
+    ((COL_X + 2) / 2 * ((COL_Y + 2) / 2) + COL_WAVES - 1) / COL_WAVES;
+
+// A wave's k-th cell of phase ph (layer ph / 4, colour ph % 4): local and
+// wrapped coordinates; false if the wave has no such cell.
+__device__ inline bool phase_cell(const MassArgs &m, const ColumnShape &c, int ph, int wave, int k,
+                                  int *li, int *cell)
+{
+    const int iz = ph >> 2, colour = ph & 3;
+    if (iz > c.count[2])
+        return false;
+    int nx;
+    const int cnt = colour_cells(c, colour, nx);
+    const int j = wave + COL_WAVES * k;
+    if (j >= cnt)
+        return false;
+    li[0] = (colour & 1) + 2 * (j % nx);
+    li[1] = (colour >> 1) + 2 * (j / nx);
+    li[2] = iz;
+#pragma unroll
+    for (int a = 0; a < 3; ++a)
+        cell[a] = wrap_index(c.first[a] - 1 + li[a], m.n[a]);
+    return true;
+}
+
+__device__ inline uint32_t cell_id(const MassArgs &m, const int *cell)
+{
+    return (uint32_t)cell[0] + (uint32_t)m.n[0] * ((uint32_t)cell[1] + (uint32_t)m.n[1] * cell[2]);
+}
+
+// Slice bounds of this wave's cells of phase ph, one vector read: lane 2k
+// gets the low bound of cell k, lane 2k+1 the high one (0 for no cell).
+__device__ inline uint32_t phase_offsets(const MassArgs &m, const ColumnShape &c, int ph, int wave)
+{
+    const int lane = lane_id();
+    uint32_t v = 0;
+    if (lane < 2 * COL_SLOTS) {
+        int li[3], cell[3];
+        if (phase_cell(m, c, ph, wave, lane >> 1, li, cell))
+            v = m.cell_offsets[cell_id(m, cell) + (lane & 1)];
+    }
+    return v;
+}
+
+// Bounds of cell k from a phase_offsets() vector, clipped to the partitioned
+// prefix.
+__device__ inline void slot_bounds(const MassArgs &m, uint32_t offv, int k, int64_t &lo,
+                                   int64_t &hi)
+{
+    lo = std::min<int64_t>(__builtin_amdgcn_readlane(offv, 2 * k), m.n_part);
+    hi = std::min<int64_t>(__builtin_amdgcn_readlane(offv, 2 * k + 1), m.n_part);
+}
+
+// The first batch of every cell of one phase, one particle per lane and cell
+// (COL_SLOTS = 4 named slots, so that they stay in registers).
+static_assert(COL_SLOTS >= 1 && COL_SLOTS <= 4, "PhaseRaw holds at most four slots");
+struct PhaseRaw {
+    RawParticle r0, r1, r2, r3;
+};
+
+__device__ inline RawParticle load_slot(const MassArgs &m, uint32_t offv, int k)
+{
+    int64_t lo, hi;
+    slot_bounds(m, offv, k, lo, hi);
+    RawParticle r{};
+    if (lo + lane_id() < hi)
+        r = load_raw(m, lo + lane_id());
+    return r;
+}
+
+__device__ inline void load_phase(const MassArgs &m, uint32_t offv, PhaseRaw &pr)
+{
+    pr.r0 = load_slot(m, offv, 0);
+    pr.r1 = COL_SLOTS > 1 ? load_slot(m, offv, 1) : RawParticle{};
+    pr.r2 = COL_SLOTS > 2 ? load_slot(m, offv, 2) : RawParticle{};
+    pr.r3 = COL_SLOTS > 3 ? load_slot(m, offv, 3) : RawParticle{};
+}
+
+// Slot k (uniform) of a phase, selected field by field.
+__device__ inline float pick1(int k, float a, float b, float c, float d)
+{
+    return k == 0 ? a : (k == 1 ? b : (k == 2 ? c : d));
+}
+
+__device__ inline RawParticle pick(const PhaseRaw &p, int k)
+{
+    RawParticle r;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        r.x[i] = pick1(k, p.r0.x[i], p.r1.x[i], p.r2.x[i], p.r3.x[i]);
+        r.B[i] = pick1(k, p.r0.B[i], p.r1.B[i], p.r2.B[i], p.r3.B[i]);
+    }
+    r.q = pick1(k, p.r0.q, p.r1.q, p.r2.q, p.r3.q);
+    r.w = pick1(k, p.r0.w, p.r1.w, p.r2.w, p.r3.w);
+    r.beta = pick1(k, p.r0.beta, p.r1.beta, p.r2.beta, p.r3.beta);
+    return r;
+}
+
+template <bool MFMA>
+__global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, ColumnGeom cg)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    float *planes = reinterpret_cast<float *>(smem);  // [2][COL_NODES][ROW]
+    WaveScratch *scratch = reinterpret_cast<WaveScratch *>(smem + sizeof(float) * 2 * COL_NODES * ROW);
+    // the wave index is uniform across the wave: keep the walk over the cells
+    // (and everything derived from it) in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), lane = lane_id();
+    WaveScratch &ws = scratch[wave];
+
+    // spread spatially adjacent columns over consecutive blocks of one XCD
+    // (blocks are dealt to the 8 XCDs round-robin), so the cells two columns
+    // share are read through the same L2
+    const uint32_t nw = cg.nwork;
+    const uint32_t per = (nw + 7) / 8;
+    const uint32_t b = blockIdx.x;
+    const uint32_t work = (b % 8) * per + b / 8;
+    if (work >= nw)
         return;
-    const int lane = threadIdx.x;
-    int cc[3];
-    cell_coords(m, cell, cc);
+    ColumnShape cs;
+    {
+        const int idx[3] = {(int)(work % (uint32_t)cg.ncol[0]),
+                            (int)((work / (uint32_t)cg.ncol[0]) % (uint32_t)cg.ncol[1]),
+                            (int)(work / ((uint32_t)cg.ncol[0] * (uint32_t)cg.ncol[1]))};
+        const int edge[3] = {COL_X, COL_Y, COL_Z};
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            cs.first[k] = idx[k] * edge[k];
+            cs.count[k] = min(edge[k], m.n[k] - cs.first[k]);
+        }
+    }
+    const int BX = cs.count[0], BY = cs.count[1], BZ = cs.count[2];
+    const int nphase = 4 * (BZ + 1);
+
+    for (int i = threadIdx.x; i < 2 * COL_NODES * ROW; i += blockDim.x)
+        planes[i] = 0.0f;
+
+    // Reads run one phase ahead of their use: during phase ph the first
+    // batches of the wave's cells of phase ph + 1 and the slice bounds of
+    // phase ph + 2 are in flight.
+    uint32_t off_next = phase_offsets(m, cs, 1, wave);
+    PhaseRaw cur, nxt;
+    {
+        const uint32_t off0 = phase_offsets(m, cs, 0, wave);
+        load_phase(m, off0, cur);
+    }
+    __syncthreads();
+
+    bool stray = false;
     const int pa = lane >> 3, pb = lane & 7;
-    float t[4][4] = {};
-    for (int64_t base = lo; base < hi; base += 64) {
-        stage_particle(m, s, lane, base + lane, hi, cc);
-        __syncthreads();
-        const int nb = (int)std::min<int64_t>(64, hi - base);
-        for (int p = 0; p < nb; ++p) {
-            const float wab = s.c[p] * s.W[p][pa] * s.W[p][pb];
-            const float u[4] = {s.u[p][0], s.u[p][2], s.u[p][1], s.u[p][3]};
+    const int ax = pa & 1, ay = (pa >> 1) & 1, az = pa >> 2;
+    const int o = offset_index(pa, pb);
+    uint32_t off_cur = phase_offsets(m, cs, 0, wave);
+    for (int ph = 0; ph < nphase; ++ph) {
+        const int iz = ph >> 2;
+        load_phase(m, off_next, nxt);
+        const uint32_t off_after = phase_offsets(m, cs, ph + 2, wave);
+        // the compiler must not sink these reads to their use
+        asm volatile("" ::: "memory");
+
+        const int lz = iz - 1 + az;  // local node plane of this lane's row
+#pragma unroll 1
+        for (int k = 0; k < COL_SLOTS; ++k) {
+            int li[3], cell[3];
+            if (!phase_cell(m, cs, ph, wave, k, li, cell))
+                break;
+            int64_t lo, hi;
+            slot_bounds(m, off_cur, k, lo, hi);
+            bool st = false;
+            float t[4][4];
+            cell_moments<MFMA>(m, ws, lane, cell, lo, hi, pick(cur, k), &st, t);
+            // a cell's stray particles are reported by the column holding its
+            // first node (each cell has exactly one such column)
+            if (li[0] >= 1 && li[1] >= 1 && li[2] >= 1)
+                stray |= st;
+            const int lx = li[0] - 1 + ax, ly = li[1] - 1 + ay;
+            if (lx >= 0 && lx < BX && ly >= 0 && ly < BY && lz >= 0 && lz < BZ) {
+                float blk[9];
+                moments_to_block(t, blk);
+                float *row =
+                    planes + ((size_t)(lz & 1) * COL_NODES + ly * COL_X + lx) * ROW + o * 9;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float wk = wab * u[k];
-#pragma unroll
-                for (int l = k; l < 4; ++l)
-                    t[k][l] += wk * u[l];
+                for (int ij = 0; ij < 9; ++ij)
+                    row[ij] += blk[ij];
             }
         }
         __syncthreads();
+
+        // after the layer's last colour node plane iz - 1 is complete: add it
+        // to M (rows of the column are contiguous in M along x) and clear it
+        const int done = iz - 1;
+        if ((ph & 3) == 3 && done >= 0) {
+            const int gz = cs.first[2] + done;
+            float *pl = planes + (size_t)(done & 1) * COL_NODES * ROW;
+            for (int ly = 0; ly < BY; ++ly) {
+                float *dst = m.M + (cs.first[0] + (int64_t)m.n[0] *
+                                    ((cs.first[1] + ly) + (int64_t)m.n[1] * gz)) * ROW;
+                float *src = pl + ly * COL_X * ROW;
+                float v[COL_ROW_PER_THREAD];
+#pragma unroll
+                for (int q = 0; q < COL_ROW_PER_THREAD; ++q) {
+                    const int r = threadIdx.x + q * COL_WAVES * WAVE;
+                    v[q] = r < BX * ROW ? dst[r] : 0.0f;
+                }
+#pragma unroll
+                for (int q = 0; q < COL_ROW_PER_THREAD; ++q) {
+                    const int r = threadIdx.x + q * COL_WAVES * WAVE;
+                    if (r < BX * ROW) {
+                        dst[r] = v[q] + src[r];
+                        src[r] = 0.0f;  // only this thread read this value
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        cur = nxt;
+        off_cur = off_next;
+        off_next = off_after;
     }
-    flush_pair(m, cc, pa, pb, t);
+    if (stray && cg.stray_flag)
+        atomicOr(cg.stray_flag, 1u);
 }
+
+// Follow-up of the column kernel, run only when it found stray particles: each
+// thread walks one cell's slice and deposits the particles that lie elsewhere
+// with global atomics.
+__global__ __launch_bounds__(256) void k_mass_strays(MassArgs m, const uint32_t *flag)
+{
+    if (*flag == 0u)
+        return;
+    for (uint32_t cid = blockIdx.x * blockDim.x + threadIdx.x; cid < m.ncells;
+         cid += gridDim.x * blockDim.x) {
+        int cc[3];
+        cell_coords(m, cid, cc);
+        const int64_t lo = std::min<int64_t>(m.cell_offsets[cid], m.n_part);
+        const int64_t hi = std::min<int64_t>(m.cell_offsets[cid + 1], m.n_part);
+        for (int64_t p = lo; p < hi; ++p) {
+            const Particle P = load_particle(m, p);
+            if (P.base[0] != cc[0] || P.base[1] != cc[1] || P.base[2] != cc[2])
+                deposit_particle_global(m, P);
+        }
+    }
+}
+
+__global__ void k_mass_clear_flag(uint32_t *flag) { *flag = 0u; }
 
 }  // namespace
 }  // namespace pcg
 
 using namespace pcg;
 
+namespace {
+
+// Workspace: one device flag (the column kernel raises it when it meets stray
+// particles), padded to 256 bytes.
+constexpr size_t MASS_WORKSPACE = 256;
+
+template <bool MFMA>
+pcg_status launch_column(const MassArgs &m, const ColumnGeom &cg, hipStream_t st)
+{
+    auto kern = k_mass_column<MFMA>;
+    const size_t lds = column_lds_bytes();
+    if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds) != hipSuccess)
+        return fail(PCG_EHIP, "assemble_mass_matrix: cannot raise dynamic LDS to %zu bytes", lds);
+    const uint32_t blocks = (cg.nwork + 7) / 8 * 8;
+    return launch(MFMA ? "mass_mfma" : "mass_valu", kern, dim3(blocks), dim3(COL_WAVES * WAVE),
+                  lds, st, m, cg);
+}
+
+}  // namespace
+
+extern "C" size_t pcg_mass_workspace_bytes(const pcg_grid *grid)
+{
+    (void)grid;
+    return MASS_WORKSPACE;
+}
+
 extern "C" pcg_status assemble_mass_matrix(const pcg_grid *grid, const pcg_particles *particles,
                                            const float *const B[3], const float *beta,
                                            const pcg_tile *cells, int32_t variant, float *M,
-                                           void *stream)
+                                           void *workspace, size_t workspace_bytes, void *stream)
 {
     const char *who = "assemble_mass_matrix";
     clear_error();
@@ -362,11 +739,30 @@ extern "C" pcg_status assemble_mass_matrix(const pcg_grid *grid, const pcg_parti
         return fail(PCG_EINVAL, "%s: cell offsets are NULL", who);
     if (cells->n_partitioned < 0 || cells->n_partitioned > count)
         return fail(PCG_EINVAL, "%s: n_partitioned outside [0, count]", who);
+    if (!workspace || workspace_bytes < MASS_WORKSPACE)
+        return fail(PCG_EWORKSPACE, "%s: workspace of %zu bytes given, %zu needed", who,
+                    workspace_bytes, MASS_WORKSPACE);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+        return fail(PCG_EWORKSPACE, "%s: workspace is not 256-byte aligned", who);
     m.cell_offsets = cells->tile_offsets;
     m.n_part = cells->n_partitioned;
-    if (variant == PCG_MASS_VALU)
-        PCG_TRY(launch("mass_valu", k_mass_valu, dim3(m.ncells), dim3(64), 0, st, m));
-    else
-        PCG_TRY(launch("mass_mfma", k_mass_mfma, dim3(m.ncells), dim3(64), 0, st, m));
+    ColumnGeom cg{};
+    cg.ncol[0] = (grid->n[0] + COL_X - 1) / COL_X;
+    cg.ncol[1] = (grid->n[1] + COL_Y - 1) / COL_Y;
+    cg.ncol[2] = (grid->n[2] + COL_Z - 1) / COL_Z;
+    cg.nwork = (uint32_t)cg.ncol[0] * cg.ncol[1] * cg.ncol[2];
+    cg.stray_flag = static_cast<uint32_t *>(workspace);
+    if (m.n_part > 0) {
+        PCG_TRY(launch("mass_clear_flag", k_mass_clear_flag, dim3(1), dim3(1), 0, st,
+                       cg.stray_flag));
+        if (variant == PCG_MASS_VALU)
+            PCG_TRY(launch_column<false>(m, cg, st));
+        else
+            PCG_TRY(launch_column<true>(m, cg, st));
+        const int64_t sblocks =
+            std::min<int64_t>((m.ncells + 255) / 256, (int64_t)device_cus() * 8);
+        PCG_TRY(launch("mass_strays", k_mass_strays, dim3((unsigned)sblocks), dim3(256), 0, st, m,
+                       (const uint32_t *)cg.stray_flag));
+    }
     return flat(cells->n_partitioned, count);
 }

@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["pcg_tile_sort", "pcg_sort_workspace_bytes", "deposit_currents",
               "pcg_deposit_workspace_bytes", "deposit_currents_regroup",
-              "pcg_deposit_regroup_workspace_bytes", "assemble_mass_matrix", "deposit_sweep1d",
+              "pcg_deposit_regroup_workspace_bytes", "pcg_mass_workspace_bytes", "assemble_mass_matrix", "deposit_sweep1d",
               "pcg_status_string", "pcg_last_error", "pcg_version", "pcg_timing_enable",
               "pcg_timing_reset", "pcg_timing_read", "pcg_timing_names"]:
         assert n in names
@@ -202,19 +202,27 @@ def test_tile_sort_validation(lib):
 
 def test_mass_and_sweep_validation(lib):
     am = lib.assemble_mass_matrix
+    am.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
+                   C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
     P = particles(100)
     B = (C.c_void_p * 3)(FAKE, FAKE, FAKE)
-    assert am(C.byref(grid(2, [8, 8])), C.byref(P), B, C.c_void_p(FAKE), None, 0,
-              C.c_void_p(FAKE), None) == EUNSUPPORTED
-    assert am(C.byref(grid(3, [2, 8, 8])), C.byref(P), B, C.c_void_p(FAKE), None, 0,
-              C.c_void_p(FAKE), None) == EINVAL
-    assert am(C.byref(grid(3, [8, 8, 8])), C.byref(P), B, C.c_void_p(FAKE), None, 9,
-              C.c_void_p(FAKE), None) == EINVAL
-    assert am(C.byref(grid(3, [8, 8, 8])), C.byref(P), B, C.c_void_p(FAKE), None, 1,
-              C.c_void_p(FAKE), None) == EINVAL                   # MFMA needs cells
+    g8 = C.byref(grid(3, [8, 8, 8]))
+
+    def call(g=g8, variant=0, cells=None, ws=FAKE, wsb=256):
+        return am(g, C.byref(P), B, FAKE, cells, variant, FAKE, ws, wsb, None)
+
+    assert call(g=C.byref(grid(2, [8, 8]))) == EUNSUPPORTED
+    assert call(g=C.byref(grid(3, [2, 8, 8]))) == EINVAL
+    assert call(variant=9) == EINVAL
+    assert call(variant=1) == EINVAL                              # MFMA needs cells
     t = Tile(2, 1, 0, 0, 100, FAKE)
-    assert am(C.byref(grid(3, [8, 8, 8])), C.byref(P), B, C.c_void_p(FAKE), C.byref(t), 1,
-              C.c_void_p(FAKE), None) == EINVAL                   # not a cell layout
+    assert call(variant=1, cells=C.byref(t)) == EINVAL            # not a cell layout
+    c1 = Tile(1, 1, 0, 0, 100, FAKE)
+    assert call(variant=1, cells=C.byref(c1), ws=None) == EWORKSPACE
+    assert call(variant=1, cells=C.byref(c1), wsb=8) == EWORKSPACE
+    assert call(variant=1, cells=C.byref(c1), ws=FAKE + 8) == EWORKSPACE   # misaligned
+    lib.pcg_mass_workspace_bytes.restype = C.c_size_t
+    assert lib.pcg_mass_workspace_bytes(g8) >= 4
     sw = lib.deposit_sweep1d
     sw.argtypes = [C.c_int32, C.c_int64, C.c_void_p, C.c_void_p, C.c_int32, C.c_double,
                    C.c_double, C.c_void_p, C.c_void_p]

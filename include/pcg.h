@@ -58,7 +58,9 @@ typedef struct pcg_grid {
     int32_t n[3];
 } pcg_grid;
 
-/* Particles, SoA fp32 device arrays of `count` entries (count < 2^31).
+/* Particles, SoA fp32 device arrays of `count` entries: count < 2^31 for
+ * pcg_tile_sort, count < 2^30 for deposit_currents, deposit_currents_regroup and
+ * assemble_mass_matrix (they address the arrays with 32-bit byte offsets).
  * x[k] is used for k < dim (others may be NULL); v[0..2] are always the three
  * velocity components (unused by assemble_mass_matrix, may be NULL there). */
 typedef struct pcg_particles {
@@ -78,7 +80,7 @@ typedef struct pcg_particles {
  *   drift      halo budget D >= 0 in cells ([TD] "Halo sizing"): the scratch
  *              tile spans TE = T + order + 2*D nodes per used axis.
  *   block      work-group size; 0 = automatic (512), otherwise clamped to
- *              [64, 1024] and rounded down to a multiple of 64 ([TD] team size
+ *              [64, 512] and rounded down to a multiple of 64 ([TD] team size
  *              knob).
  *   tile_offsets  device uint32 [ntiles + 1], ntiles = prod_k (n_k / T). */
 typedef struct pcg_tile {

@@ -14,6 +14,7 @@
 // (order+1)^dim x 3 global atomics -- used with no layout and for the tail.
 #include <algorithm>
 #include <climits>
+#include <type_traits>
 
 #include "common.hpp"
 #include "layout.hpp"
@@ -44,9 +45,12 @@ struct DepArgs {
     int64_t ng;
     const uint32_t *tile_offsets;
     int64_t n_part;
-    const uint32_t *chunk_cum;
+    const uint32_t *chunk_cum;   // [ntiles + 1] work items before each tile
+    const uint32_t *chunk_map;   // [nwork] tile of each work item
+    uint32_t *chunk_part;        // scratch of the chunk prefix
     uint32_t chunk;
     unsigned long long *n_escaped;
+    int fb64;  // tiled: the packed scratch falls back to 64-bit sums (else fp32)
 };
 
 // The regrouping half of the fused pass: every particle the deposit loads is
@@ -74,6 +78,41 @@ __device__ inline uint32_t chunk_start(uint32_t c, uint32_t L, uint32_t nch)
     return (uint32_t)(((uint64_t)L * c) / nch);
 }
 
+// One axis of the shape: first support node b, unwrapped (in [-1, n] for a
+// coordinate clamped into [0, n]), and order+1 weights.
+template <int ORDER>
+__device__ inline int shape_axis_raw(float xraw, float nf, float *W)
+{
+    const float x = clamp_coord(xraw, nf);
+    const float fl = floorf(x);
+    const float xi = x - fl;
+    int b = (int)fl;
+    if (ORDER == 1) {
+        W[0] = 1.0f - xi;
+        W[1] = xi;
+    } else {
+        float d;
+        if (xi < 0.5f) {
+            b -= 1;
+            d = xi;
+        } else {
+            d = xi - 1.0f;
+        }
+        const float lo = 0.5f - d, hi = 0.5f + d;
+        W[0] = 0.5f * lo * lo;
+        W[1] = 0.75f - d * d;
+        W[2] = 0.5f * hi * hi;
+    }
+    return b;
+}
+
+// v mod n for v in (-n, 2n).
+__device__ inline int wrap_once(int v, int n)
+{
+    v += v < 0 ? n : 0;
+    return v - (v >= n ? n : 0);
+}
+
 // One axis of the shape: first support node b (wrapped) and order+1 weights.
 template <int ORDER>
 __device__ inline int shape_axis(float xraw, float nf, int n, float *W)
@@ -98,26 +137,29 @@ __device__ inline int shape_axis(float xraw, float nf, int n, float *W)
         W[1] = 0.75f - d * d;
         W[2] = 0.5f * hi * hi;
     }
-    return wrap_index(b, n);
+    return wrap_once(b, n);  // b in [-1, n]
 }
 
-// All (order+1)^dim global atomics of one particle.
+// All (order+1)^dim global atomics of one particle; b[k] is wrapped into
+// [0, n_k) and order < n_k, so each node index wraps with one subtraction.
 template <int DIM, int ORDER>
-__device__ inline void deposit_global(const DepArgs &a, const int *b, float W[3][ORDER + 1],
-                                      const float *amp)
+__device__ __attribute__((always_inline)) inline void deposit_global(const DepArgs &a, const int *b,
+                                                                     float W[3][ORDER + 1],
+                                                                     const float *amp)
 {
+    auto wrap_up = [](int v, int n) { return v - (v >= n ? n : 0); };
     constexpr int M = ORDER + 1;
     constexpr int MY = DIM > 1 ? M : 1, MZ = DIM > 2 ? M : 1;
 #pragma unroll
     for (int az = 0; az < MZ; ++az) {
-        const int gz = DIM > 2 ? wrap_index(b[2] + az, a.n[2]) : 0;
+        const int gz = DIM > 2 ? wrap_up(b[2] + az, a.n[2]) : 0;
 #pragma unroll
         for (int ay = 0; ay < MY; ++ay) {
-            const int gy = DIM > 1 ? wrap_index(b[1] + ay, a.n[1]) : 0;
+            const int gy = DIM > 1 ? wrap_up(b[1] + ay, a.n[1]) : 0;
             const float wyz = (DIM > 1 ? W[1][ay] : 1.0f) * (DIM > 2 ? W[2][az] : 1.0f);
 #pragma unroll
             for (int ax = 0; ax < M; ++ax) {
-                const int gx = wrap_index(b[0] + ax, a.n[0]);
+                const int gx = wrap_up(b[0] + ax, a.n[0]);
                 const int64_t g = gx + (int64_t)a.n[0] * (gy + (int64_t)a.n[1] * gz);
                 const float wt = W[0][ax] * wyz;
 #pragma unroll
@@ -144,38 +186,242 @@ __global__ __launch_bounds__(1024) void k_deposit_flat(DepArgs a, int64_t begin,
     }
 }
 
-// LDS float atomics (ds_add_f32) are ~30x slower than integer LDS atomics on
-// gfx950, so the scratch tile normally holds int64 fixed-point sums: a
-// work-group picks a power-of-two scale 2^S from the largest |q w v_c| of its
-// first 256 particles (S puts that value near 2^23), every product
-// q w v_c W * 2^S is rounded once to an integer and added with ds_add_u64.
-// The sums are then exact and independent of the order of the adds.  A
-// particle whose largest |q w v_c| * 2^S is outside [2^8, 2^30) would overflow
-// or lose precision there, so it takes the escape valve like a particle that
-// left the window (only the latter are counted as escapes).  When the int64
-// scratch does not fit the LDS, FIXED = false keeps fp32 LDS atomics.
-template <int DIM, int ORDER, bool FIXED, int TEC, bool MOVE>
-__global__ __launch_bounds__(1024) void k_deposit_tiled(DepArgs a, MoveArgs m)
+// Accumulator of the LDS scratch tile.  LDS float atomics (ds_add_f32) are
+// about 30x slower than integer LDS atomics on gfx950, so the scratch holds
+// integer fixed-point sums: a work-group picks a power-of-two scale 2^S, every
+// product q w v_c W 2^S is rounded once to the nearest integer and added with
+// integer atomics.  The in-tile sums are then exact
+// and independent of the order of the adds.
+//   ACC_PACKED  two 32-bit sums per 64-bit word: x in the low half, y in the
+//               high half (added as y 2^32 + x, so a negative x borrows from y
+//               and the flush undoes it), z in a 32-bit word.  16 atomics per
+//               CIC particle instead of 24 64-bit ones.  A per-cell particle
+//               count proves afterwards that no 32-bit sum can have
+//               overflowed; a work-group that cannot prove it runs its chunk
+//               again at a scale the counts allow (or, if that scale would be
+//               too coarse, into ACC_FIXED, or ACC_FLOAT if that does not fit).
+//   ACC_FIXED   three 64-bit sums.
+//   ACC_FLOAT   fp32 LDS atomics (order-dependent rounding).
+enum AccMode { ACC_PACKED = 0, ACC_FIXED = 1, ACC_FLOAT = 2 };
+
+// a*b (formed in fp32) rounded to the nearest integer, ties to even; valid
+// for |a*b| < 2^31.
+__device__ inline int round_prod(float a, float b)
+{
+    return __float2int_rn(a * b);
+}
+
+// a*b rounded to the nearest integer, ties to even, with one FMA: a*b + 1.5 2^23
+// is formed exactly and rounded once to a float whose unit is 1; valid for
+// |a*b| < 2^22.
+__device__ inline int round_prod_fma(float a, float b)
+{
+    return __float_as_int(__builtin_fmaf(a, b, 12582912.0f)) - 0x4B400000;
+}
+
+// The packed sums of CIC scratch keep every product below 2^22 and round with
+// round_prod_fma; TSC (smaller weights, more rounding per node) allows up to
+// 2^24 and rounds with round_prod.
+template <int ORDER>
+__device__ inline int round_packed(float a, float b)
+{
+    return ORDER == 1 ? round_prod_fma(a, b) : round_prod(a, b);
+}
+
+// Per work-group constants of a chunk.
+struct TileCtx {
+    int origin[3];
+    int TE, vol, cedge;     // scratch edge and volume, cells per axis in the window
+    float scale, inv_scale; // 2^S and 2^-S
+    float lo_ok, hi_ok;     // admitted range of the largest scaled |q w v_c|
+};
+
+// LDS views of the scratch tile (all start at the dynamic LDS base).
+struct Scratch {
+    unsigned long long *xy;  // PACKED [vol]
+    uint32_t *z;             // PACKED [vol]
+    uint32_t *cnt;           // PACKED [cedge^dim] particles per base cell
+    unsigned long long *acc64;  // FIXED [3][vol]
+    float *acc32;               // FLOAT [3][vol]
+};
+
+// One particle: its support, then either the LDS scratch (mode MODE) or, if
+// its stencil leaves the window or its amplitude is outside the admitted
+// range, global atomics.  `again` marks the fallback pass: particles that
+// went to global memory in the first pass are skipped.  Returns 1 for an
+// escape (stencil outside the window) on the first pass.
+template <int DIM, int ORDER, int MODE, int TEC>
+__device__ __attribute__((always_inline)) inline uint32_t deposit_one(const DepArgs &a, const TileCtx &c, const Scratch &sc,
+                                       const float *xs, const float *vv, float cq, float cw,
+                                       bool again)
+{
+    constexpr int M = ORDER + 1;
+    constexpr int MY = DIM > 1 ? M : 1, MZ = DIM > 2 ? M : 1;
+    const int TE = TEC > 0 ? TEC : c.TE;
+    const int vol = TEC > 0 ? (DIM == 3 ? TEC * TEC * TEC : (DIM == 2 ? TEC * TEC : TEC)) : c.vol;
+    const int last = a.T - 1 + 2 * a.D;  // largest scratch start that keeps the stencil inside
+    const float qw = cq * cw;
+
+    float W[3][M];
+    int b[3] = {0, 0, 0};
+    int s[3] = {0, 0, 0};
+    bool esc = false;
+#pragma unroll
+    for (int k = 0; k < DIM; ++k) {
+        b[k] = shape_axis_raw<ORDER>(xs[k], a.nf[k], W[k]);
+        // scratch start: periodic offset of the base node from the window's low
+        // edge (b in [-1, n], origin in [0, n - T], so one wrap suffices)
+        s[k] = wrap_once(b[k] - c.origin[k] + a.D, a.n[k]);
+        esc |= s[k] > last;
+    }
+    const float qws = qw * c.scale;
+    float amp[3] = {qws * vv[0], qws * vv[1], qws * vv[2]};
+    const float amax = fmaxf(fabsf(amp[0]), fmaxf(fabsf(amp[1]), fabsf(amp[2])));
+    if (amax == 0.0f)  // deposits nothing, but an escape is still an escape
+        return (esc && !again) ? 1u : 0u;
+    const bool in_lds = !esc && amax >= c.lo_ok && amax < c.hi_ok;
+    if (!in_lds) {
+        if (again)
+            return 0u;
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            amp[k] *= c.inv_scale;  // exact: power-of-two scale
+#pragma unroll
+        for (int k = 0; k < DIM; ++k)
+            b[k] = wrap_once(b[k], a.n[k]);
+        deposit_global<DIM, ORDER>(a, b, W, amp);
+        return esc ? 1u : 0u;
+    }
+    // amp_c * W_x first, then one product per (node, component)
+    float ampx[3][M];
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+#pragma unroll
+        for (int ax = 0; ax < M; ++ax)
+            ampx[k][ax] = amp[k] * W[0][ax];
+    const int sbase = DIM == 3 ? (s[2] * TE + s[1]) * TE + s[0] : (DIM == 2 ? s[1] * TE + s[0] : s[0]);
+    if (MODE == ACC_PACKED) {
+        const int cell = DIM == 3 ? (s[2] * c.cedge + s[1]) * c.cedge + s[0]
+                                  : (DIM == 2 ? s[1] * c.cedge + s[0] : s[0]);
+        __hip_atomic_fetch_add(&sc.cnt[cell], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+#pragma unroll
+    for (int az = 0; az < MZ; ++az) {
+#pragma unroll
+        for (int ay = 0; ay < MY; ++ay) {
+            const int row = sbase + (DIM == 3 ? (az * TE + ay) * TE : ay * TE);
+            const float wyz = (DIM > 1 ? W[1][ay] : 1.0f) * (DIM > 2 ? W[2][az] : 1.0f);
+#pragma unroll
+            for (int ax = 0; ax < M; ++ax) {
+                const int idx = row + ax;
+                if (MODE == ACC_PACKED) {
+                    const int ix = round_packed<ORDER>(ampx[0][ax], wyz);
+                    const int iy = round_packed<ORDER>(ampx[1][ax], wyz);
+                    const int iz = round_packed<ORDER>(ampx[2][ax], wyz);
+                    const uint32_t hi = (uint32_t)(iy + (ix >> 31));
+                    const unsigned long long v = ((unsigned long long)hi << 32) | (uint32_t)ix;
+                    __hip_atomic_fetch_add(&sc.xy[idx], v, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+                    __hip_atomic_fetch_add(&sc.z[idx], (uint32_t)iz, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 3; ++k) {
+                        if (MODE == ACC_FIXED) {
+                            const long long f = (long long)round_prod(ampx[k][ax], wyz);
+                            __hip_atomic_fetch_add(&sc.acc64[k * vol + idx], (unsigned long long)f,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                        } else {
+                            __hip_atomic_fetch_add(&sc.acc32[k * vol + idx],
+                                                   ampx[k][ax] * wyz * c.inv_scale,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                        }
+                    }
+                }
+            }
+        }
+    }
+    return 0u;
+}
+
+// Global node index of scratch node i of the window (periodic wrap).
+template <int DIM>
+__device__ inline int64_t window_node(const DepArgs &a, const TileCtx &c, int i)
+{
+    int sx = i, sy = 0, sz = 0;
+    if (DIM > 1) {
+        sx = i % c.TE;
+        const int r = i / c.TE;
+        sy = DIM > 2 ? r % c.TE : r;
+        sz = DIM > 2 ? r / c.TE : 0;
+    }
+    // origin - D + s lies in [-D, n + order + D) and D + order < n
+    const int gx = wrap_once(c.origin[0] - a.D + sx, a.n[0]);
+    const int gy = DIM > 1 ? wrap_once(c.origin[1] - a.D + sy, a.n[1]) : 0;
+    const int gz = DIM > 2 ? wrap_once(c.origin[2] - a.D + sz, a.n[2]) : 0;
+    return gx + (int64_t)a.n[0] * (gy + (int64_t)a.n[1] * gz);
+}
+
+// Flush: one global atomic per non-zero scratch value.
+template <int DIM, int MODE>
+__device__ __attribute__((always_inline)) inline void flush_scratch(const DepArgs &a, const TileCtx &c, const Scratch &sc)
+{
+    for (int i = threadIdx.x; i < c.vol; i += blockDim.x) {
+        float val[3];
+        if (MODE == ACC_PACKED) {
+            const unsigned long long p = sc.xy[i];
+            const int ix = (int)(uint32_t)p;
+            const int iy = (int)(uint32_t)((p - (unsigned long long)(long long)ix) >> 32);
+            const int iz = (int)sc.z[i];
+            val[0] = (float)ix * c.inv_scale;
+            val[1] = (float)iy * c.inv_scale;
+            val[2] = (float)iz * c.inv_scale;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                if (MODE == ACC_FIXED)
+                    val[k] = (float)((double)(long long)sc.acc64[k * c.vol + i] * (double)c.inv_scale);
+                else
+                    val[k] = sc.acc32[k * c.vol + i];
+            }
+        }
+        if (val[0] == 0.0f && val[1] == 0.0f && val[2] == 0.0f)
+            continue;
+        const int64_t g = window_node<DIM>(a, c, i);
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            if (val[k] != 0.0f)
+                atomic_add_f32(&a.J[k * a.ng + g], val[k]);
+    }
+}
+
+// Bytes of LDS the packed scratch and its fallback need.
+__host__ __device__ constexpr size_t packed_bytes(size_t vol, size_t ncell)
+{
+    return vol * 12 + ncell * 4;
+}
+
+// Tiled deposit of one chunk per work-group.  ACC is ACC_PACKED (falling back
+// per work-group to ACC_FIXED when a.fb64, else ACC_FLOAT) or ACC_FLOAT.
+template <int DIM, int ORDER, int ACC, int TEC, bool MOVE>
+__global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    unsigned long long *acc64 = reinterpret_cast<unsigned long long *>(smem);  // [3][vol]
-    float *acc32 = reinterpret_cast<float *>(smem);                          // [3][vol]
-    __shared__ uint32_t s_tile, s_lo, s_hi, s_esc, s_maxbits, s_move;
+    __shared__ uint32_t s_tile, s_lo, s_hi, s_esc, s_maxbits, s_move, s_maxcnt;
     // MOVE: output slot base per (incremental chunk overlapped, direction), and
     // the end slot of each of those chunks
     __shared__ uint32_t s_base[MOVE ? MOVE_MAX_CHUNKS * NDIR : 1];
     __shared__ uint32_t s_cend[MOVE ? MOVE_MAX_CHUNKS : 1];
-    constexpr int M = ORDER + 1;
-    constexpr int MY = DIM > 1 ? M : 1, MZ = DIM > 2 ? M : 1;
 
     if (threadIdx.x == 0) {
-        const ChunkRange r = find_chunk(blockIdx.x, a.chunk_cum, a.ntiles, a.tile_offsets,
+        const ChunkRange r = find_chunk(blockIdx.x, a.chunk_cum, a.chunk_map, a.ntiles, a.tile_offsets,
                                         a.n_part);
         s_tile = r.tile;
         s_lo = r.lo;
         s_hi = r.hi;
         s_esc = 0;
         s_maxbits = 0;
+        s_maxcnt = 0;
         s_move = MOVE && *m.inc.flag == 0u;
     }
     __syncthreads();
@@ -183,20 +429,31 @@ __global__ __launch_bounds__(1024) void k_deposit_tiled(DepArgs a, MoveArgs m)
     if (tile == UINT_MAX)
         return;
     const uint32_t lo = s_lo, hi = s_hi;
-    int origin[3] = {0, 0, 0};
+    TileCtx c;
     {
         uint32_t t = tile;
 #pragma unroll
+        for (int k = 0; k < 3; ++k)
+            c.origin[k] = 0;
+#pragma unroll
         for (int k = 0; k < DIM; ++k) {
-            origin[k] = (int)(t % (uint32_t)a.nt[k]) * a.T;
+            c.origin[k] = (int)(t % (uint32_t)a.nt[k]) * a.T;
             t /= (uint32_t)a.nt[k];
         }
     }
-    // TEC > 0: the scratch edge is a compile-time constant, so every node offset
-    // folds into the LDS instruction's immediate offset
-    const int TE = TEC > 0 ? TEC : a.TE;
-    const int vol = TEC > 0 ? (DIM == 3 ? TEC * TEC * TEC : (DIM == 2 ? TEC * TEC : TEC)) : a.vol;
-    const int D = a.D;
+    c.TE = TEC > 0 ? TEC : a.TE;
+    c.vol = TEC > 0 ? (DIM == 3 ? TEC * TEC * TEC : (DIM == 2 ? TEC * TEC : TEC)) : a.vol;
+    c.cedge = a.T + 2 * a.D;
+    int ncell = 1;
+#pragma unroll
+    for (int k = 0; k < DIM; ++k)
+        ncell *= c.cedge;
+    Scratch sc;
+    sc.xy = reinterpret_cast<unsigned long long *>(smem);
+    sc.z = reinterpret_cast<uint32_t *>(smem + (size_t)c.vol * 8);
+    sc.cnt = reinterpret_cast<uint32_t *>(smem + (size_t)c.vol * 12);
+    sc.acc64 = reinterpret_cast<unsigned long long *>(smem);
+    sc.acc32 = reinterpret_cast<float *>(smem);
 
     // MOVE: the incremental chunks of this tile's slice that [lo, hi) overlaps
     const bool move = MOVE && s_move != 0u;
@@ -216,10 +473,17 @@ __global__ __launch_bounds__(1024) void k_deposit_tiled(DepArgs a, MoveArgs m)
             s_cend[i] = p0 + chunk_start(c_first + i + 1, L, nch);
     }
 
-    if (FIXED) {
-        for (int i = threadIdx.x; i < 3 * vol; i += blockDim.x)
-            acc64[i] = 0ull;
-        // scale from the first batch: largest |q w v_c|
+    // zero the scratch; scale from the first batch: largest |q w v_c|
+    if (ACC == ACC_PACKED) {
+        const int words = c.vol * 3 + ncell;  // xy (2 words each), z, cnt
+        uint32_t *w32 = reinterpret_cast<uint32_t *>(smem);
+        for (int i = threadIdx.x; i < words; i += blockDim.x)
+            w32[i] = 0u;
+    } else {
+        for (int i = threadIdx.x; i < 3 * c.vol; i += blockDim.x)
+            sc.acc32[i] = 0.0f;
+    }
+    {
         float mx = 0.0f;
         const uint32_t p = lo + threadIdx.x;
         if (p < hi) {
@@ -231,212 +495,223 @@ __global__ __launch_bounds__(1024) void k_deposit_tiled(DepArgs a, MoveArgs m)
             mx = fmaxf(mx, __shfl_xor(mx, o, WAVE));
         if (lane_id() == 0 && mx > 0.0f && mx <= 3.0e38f)
             atomicMax(&s_maxbits, __float_as_uint(mx));  // non-negative: int order = float order
-    } else {
-        for (int i = threadIdx.x; i < 3 * vol; i += blockDim.x)
-            acc32[i] = 0.0f;
     }
     __syncthreads();
-    float scale = 1.0f, inv_scale = 1.0f;
-    if (FIXED) {
+    // Scale.  Packed sums: the largest scaled product stays below 2^h, the
+    // first batch's largest in [2^(h-1), 2^h); h leaves room for the particles
+    // of (order+1)^dim cells at twice the chunk's mean density in a 32-bit sum
+    // (the count check below turns this into a guarantee), at most 22 (CIC,
+    // see round_packed) or 24 (TSC).  When
+    // that leaves fewer than PACKED_MIN_BITS bits for the rounding (dense
+    // chunks; the TSC weights are small, so it needs more), the chunk takes
+    // 64-bit sums from the start if they fit: first batch's largest in
+    // [2^23, 2^24), products below 2^30.
+    constexpr int PACKED_MIN_BITS = ORDER == 1 ? 21 : 23;
+    bool fixed_first = false;
+    {
+        int h = 24;
+        if (ACC == ACC_PACKED) {
+            int tcells = 1;
+            for (int k = 0; k < DIM; ++k)
+                tcells *= a.T;
+            constexpr int NS = DIM == 3 ? (ORDER + 1) * (ORDER + 1) * (ORDER + 1)
+                                        : (DIM == 2 ? (ORDER + 1) * (ORDER + 1) : ORDER + 1);
+            const uint64_t nb = (uint64_t)NS * ((2ull * (hi - lo)) / tcells + 1) + 1;
+            const int lg = 64 - __clzll((long long)(nb - 1));  // ceil(log2(nb))
+            h = max(10, min(ORDER == 1 ? 22 : 24, 31 - lg));
+            fixed_first = h < PACKED_MIN_BITS && a.fb64;
+        }
         const float mx = __uint_as_float(s_maxbits);
         int S = 0;
         if (mx > 0.0f)
-            S = 23 - ilogbf(mx);
+            S = (fixed_first ? 24 : h) - 1 - ilogbf(mx);
         S = max(-100, min(100, S));
-        scale = ldexpf(1.0f, S);
-        inv_scale = ldexpf(1.0f, -S);
+        c.scale = ldexpf(1.0f, S);
+        c.inv_scale = ldexpf(1.0f, -S);
+        c.hi_ok = ldexpf(1.0f, fixed_first ? 30 : h);
+        c.lo_ok = ldexpf(1.0f, fixed_first ? 8 : h - 16);
     }
-    const float lo_ok = 256.0f, hi_ok = 1073741824.0f;  // 2^8 and 2^30 (scaled)
+    if (fixed_first) {
+        for (int i = threadIdx.x; i < 3 * c.vol; i += blockDim.x)
+            sc.acc64[i] = 0ull;
+        __syncthreads();
+    }
 
-    const int last = a.T - 1 + 2 * D;  // largest scratch start that keeps the stencil inside
     // Each thread keeps U particles (stride blockDim.x apart) in flight: the
     // next group's values (and move codes) load while this group is weighed,
     // moved and accumulated.
     constexpr int U = DEPOSIT_UNROLL;
     const uint32_t stride = blockDim.x;
-    float nx[U][3], nv[U][3], nq[U], nw[U];
-    uint32_t ncode[U];
-    auto load_group = [&](uint32_t base) {
+    auto pass = [&](auto mode_tag, const TileCtx &cx, bool again) __attribute__((always_inline)) {
+        constexpr int MODE = decltype(mode_tag)::value;
+        float nx[U][3], nv[U][3], nq[U], nw[U];
+        uint32_t ncode[U];
+        const bool mv = move && !again;
+        auto load_group = [&](uint32_t base) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t p = base + u * stride;
-            nx[u][0] = nx[u][1] = nx[u][2] = 0.f;
-            nv[u][0] = nv[u][1] = nv[u][2] = 0.f;
-            nq[u] = nw[u] = 0.f;
-            ncode[u] = 0;
-            if (p < hi) {
+            for (int u = 0; u < U; ++u) {
+                const uint32_t p = base + u * stride;
+                nx[u][0] = nx[u][1] = nx[u][2] = 0.f;
+                nv[u][0] = nv[u][1] = nv[u][2] = 0.f;
+                nq[u] = nw[u] = 0.f;
+                ncode[u] = 0;
+                if (p < hi) {
+                    // counts are below 2^30: a 32-bit byte offset from each
+                    // array's base reaches every element
+                    const uint32_t off = p * 4u;
+                    auto at = [off](const float *base) {
+                        return *reinterpret_cast<const float *>(
+                            reinterpret_cast<const char *>(base) + off);
+                    };
 #pragma unroll
-                for (int k = 0; k < DIM; ++k)
-                    nx[u][k] = a.x[k][p];
+                    for (int k = 0; k < DIM; ++k)
+                        nx[u][k] = at(a.x[k]);
 #pragma unroll
-                for (int c = 0; c < 3; ++c)
-                    nv[u][c] = a.v[c][p];
-                nq[u] = a.q[p];
-                nw[u] = a.w[p];
-                if (move)
-                    ncode[u] = m.inc.code[p];
-            }
-        }
-    };
-    uint32_t ci = 0, c_end = 0;  // MOVE: this thread's chunk (relative to c_first) and its end
-    if (move) {
-        const uint32_t p = min(lo + threadIdx.x, hi - 1);
-        ci = min(chunk_of(p - p0, L, nch) - c_first, (uint32_t)MOVE_MAX_CHUNKS - 1);
-        c_end = s_cend[ci];
-    }
-    load_group(lo + threadIdx.x);
-
-    for (uint32_t base = lo + threadIdx.x; base < hi; base += U * stride) {
-        float gx[U][3], gv[U][3], gq[U], gw[U];
-        uint32_t gcode[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int k = 0; k < 3; ++k) {
-                gx[u][k] = nx[u][k];
-                gv[u][k] = nv[u][k];
-            }
-            gq[u] = nq[u];
-            gw[u] = nw[u];
-            gcode[u] = ncode[u];
-        }
-        load_group(base + U * stride);
-
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t p = base + u * stride;
-            if (p >= hi)
-                break;
-            const float *xs = gx[u], *vv = gv[u];
-            const float cq = gq[u], cw = gw[u];
-            if (move) {
-                // slot in the new layout: the (chunk, direction) base plus the rank
-                while (p >= c_end && ci + 1 < (uint32_t)MOVE_MAX_CHUNKS) {
-                    ++ci;
-                    c_end = s_cend[ci];
+                    for (int k = 0; k < 3; ++k)
+                        nv[u][k] = at(a.v[k]);
+                    nq[u] = at(a.q);
+                    nw[u] = at(a.w);
+                    if (mv)
+                        ncode[u] = m.inc.code[p];
                 }
-                const uint32_t code = gcode[u];
-                const uint32_t d = min(code >> 27, (uint32_t)NDIR - 1);
-                const uint32_t pos = s_base[ci * NDIR + d] + (code & RANK_MASK);
-                if (pos < (uint64_t)m.inc.count) {
-                    if (m.canon) {
+            }
+        };
+        uint32_t ci = 0, c_end = 0;  // MOVE: this thread's chunk (relative to c_first) and its end
+        if (mv) {
+            const uint32_t p = min(lo + threadIdx.x, hi - 1);
+            ci = min(chunk_of(p - p0, L, nch) - c_first, (uint32_t)MOVE_MAX_CHUNKS - 1);
+            c_end = s_cend[ci];
+        }
+        uint32_t esc_count = 0;
+        load_group(lo + threadIdx.x);
+        for (uint32_t base = lo + threadIdx.x; base < hi; base += U * stride) {
+            float gx[U][3], gv[U][3], gq[U], gw[U];
+            uint32_t gcode[U];
 #pragma unroll
-                        for (int k = 0; k < DIM; ++k)
-                            m.arr.out[k][pos] = xs[k];
+            for (int u = 0; u < U; ++u) {
 #pragma unroll
-                        for (int c = 0; c < 3; ++c)
-                            m.arr.out[DIM + c][pos] = vv[c];
-                        m.arr.out[DIM + 3][pos] = cq;
-                        m.arr.out[DIM + 4][pos] = cw;
-                    } else {
-                        for (int i = 0; i < m.arr.n; ++i)
-                            m.arr.out[i][pos] = m.arr.in[i][p];
+                for (int k = 0; k < 3; ++k) {
+                    gx[u][k] = nx[u][k];
+                    gv[u][k] = nv[u][k];
+                }
+                gq[u] = nq[u];
+                gw[u] = nw[u];
+                gcode[u] = ncode[u];
+            }
+            load_group(base + U * stride);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t p = base + u * stride;
+                if (p >= hi)
+                    break;
+                if (mv) {
+                    // slot in the new layout: the (chunk, direction) base plus the rank
+                    while (p >= c_end && ci + 1 < (uint32_t)MOVE_MAX_CHUNKS) {
+                        ++ci;
+                        c_end = s_cend[ci];
                     }
-                }
-            }
-            const float qw = cq * cw;
-
-            float W[3][M];
-            int b[3] = {0, 0, 0};
-            int s[3] = {0, 0, 0};
-            bool esc = false;
+                    const uint32_t code = gcode[u];
+                    const uint32_t d = min(code >> 27, (uint32_t)NDIR - 1);
+                    const uint32_t pos = s_base[ci * NDIR + d] + (code & RANK_MASK);
+                    if (pos < (uint64_t)m.inc.count) {
+                        if (m.canon) {
 #pragma unroll
-            for (int k = 0; k < DIM; ++k) {
-                b[k] = shape_axis<ORDER>(xs[k], a.nf[k], a.n[k], W[k]);
-                // scratch start: periodic offset of the base node from the window's low edge
-                s[k] = wrap_index(b[k] - origin[k] + D, a.n[k]);
-                esc |= s[k] > last;
-            }
-            float amp[3] = {qw * vv[0], qw * vv[1], qw * vv[2]};
-            bool in_lds = !esc;
-            if (FIXED) {
-                const float amax =
-                    fmaxf(fabsf(amp[0]), fmaxf(fabsf(amp[1]), fabsf(amp[2]))) * scale;
-                if (amax == 0.0f) {  // deposits nothing, but an escape is still an escape
-                    if (esc)
-                        atomicAdd(&s_esc, 1u);
-                    continue;
-                }
-                in_lds = in_lds && amax >= lo_ok && amax < hi_ok;
+                            for (int k = 0; k < DIM; ++k)
+                                m.arr.out[k][pos] = gx[u][k];
 #pragma unroll
-                for (int c = 0; c < 3; ++c)
-                    amp[c] *= scale;
-            }
-            if (in_lds) {
-                // amp_c * W_x first, then one multiply per (node, component)
-                float ampx[3][M];
+                            for (int k = 0; k < 3; ++k)
+                                m.arr.out[DIM + k][pos] = gv[u][k];
+                            m.arr.out[DIM + 3][pos] = gq[u];
+                            m.arr.out[DIM + 4][pos] = gw[u];
+                        } else {
+                            // constant indices: the pointer table stays in the
+                            // kernel arguments
 #pragma unroll
-                for (int c = 0; c < 3; ++c)
-#pragma unroll
-                    for (int ax = 0; ax < M; ++ax)
-                        ampx[c][ax] = amp[c] * W[0][ax];
-                const int sbase = DIM == 3 ? (s[2] * TE + s[1]) * TE + s[0]
-                                           : (DIM == 2 ? s[1] * TE + s[0] : s[0]);
-#pragma unroll
-                for (int az = 0; az < MZ; ++az) {
-#pragma unroll
-                    for (int ay = 0; ay < MY; ++ay) {
-                        const int row = sbase + (DIM == 3 ? (az * TE + ay) * TE : ay * TE);
-                        const float wyz =
-                            (DIM > 1 ? W[1][ay] : 1.0f) * (DIM > 2 ? W[2][az] : 1.0f);
-#pragma unroll
-                        for (int ax = 0; ax < M; ++ax) {
-                            const int idx = row + ax;
-#pragma unroll
-                            for (int c = 0; c < 3; ++c) {
-                                const float val = ampx[c][ax] * wyz;
-                                if (FIXED) {
-                                    const long long f = (long long)__float2int_rn(val);
-                                    __hip_atomic_fetch_add(&acc64[c * vol + idx],
-                                                           (unsigned long long)f,
-                                                           __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_WORKGROUP);
-                                } else {
-                                    __hip_atomic_fetch_add(&acc32[c * vol + idx], val,
-                                                           __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_WORKGROUP);
-                                }
-                            }
+                            for (int i = 0; i < MAX_ARRAYS; ++i)
+                                if (i < m.arr.n)
+                                    m.arr.out[i][pos] = m.arr.in[i][p];
                         }
                     }
                 }
-            } else {
-                if (FIXED) {
-#pragma unroll
-                    for (int c = 0; c < 3; ++c)
-                        amp[c] *= inv_scale;  // exact: power-of-two scale
-                }
-                deposit_global<DIM, ORDER>(a, b, W, amp);
-                if (esc)
-                    atomicAdd(&s_esc, 1u);
+                esc_count += deposit_one<DIM, ORDER, MODE, TEC>(a, cx, sc, gx[u], gv[u], gq[u],
+                                                                gw[u], again);
             }
         }
+        if (esc_count)
+            atomicAdd(&s_esc, esc_count);
+    };
+    if (ACC == ACC_PACKED && fixed_first) {
+        pass(std::integral_constant<int, ACC_FIXED>{}, c, false);
+        __syncthreads();
+        flush_scratch<DIM, ACC_FIXED>(a, c, sc);
+        if (threadIdx.x == 0 && s_esc && a.n_escaped)
+            atomicAdd(a.n_escaped, (unsigned long long)s_esc);
+        return;
     }
+    pass(std::integral_constant<int, ACC>{}, c, false);
     __syncthreads();
 
-    // flush: one global atomic per non-zero scratch value, node indices wrapped
-    for (int i = threadIdx.x; i < vol; i += blockDim.x) {
-        int sx = i, sy = 0, sz = 0;
-        if (DIM > 1) {
-            sx = i % TE;
-            const int r = i / TE;
-            sy = DIM > 2 ? r % TE : r;
-            sz = DIM > 2 ? r / TE : 0;
-        }
-        const int gx = wrap_index(origin[0] - D + sx, a.n[0]);
-        const int gy = DIM > 1 ? wrap_index(origin[1] - D + sy, a.n[1]) : 0;
-        const int gz = DIM > 2 ? wrap_index(origin[2] - D + sz, a.n[2]) : 0;
-        const int64_t g = gx + (int64_t)a.n[0] * (gy + (int64_t)a.n[1] * gz);
+    bool redo = false;
+    uint32_t maxcnt = 0;
+    constexpr int NS = DIM == 3 ? (ORDER + 1) * (ORDER + 1) * (ORDER + 1)
+                                : (DIM == 2 ? (ORDER + 1) * (ORDER + 1) : ORDER + 1);
+    if (ACC == ACC_PACKED) {
+        // no 32-bit sum can have overflowed if every node's contributing cells
+        // hold few enough particles: a node sums at most NS * maxcnt products,
+        // each at most 2^h in magnitude after rounding
+        uint32_t mc = 0;
+        for (int i = threadIdx.x; i < ncell; i += blockDim.x)
+            mc = max(mc, sc.cnt[i]);
 #pragma unroll
-        for (int c = 0; c < 3; ++c) {
-            float val;
-            if (FIXED)
-                val = (float)((double)(long long)acc64[c * vol + i] * (double)inv_scale);
-            else
-                val = acc32[c * vol + i];
-            if (val != 0.0f)
-                atomic_add_f32(&a.J[c * a.ng + g], val);
+        for (int o = 32; o > 0; o >>= 1)
+            mc = max(mc, (uint32_t)__shfl_xor((int)mc, o, WAVE));
+        if (lane_id() == 0 && mc)
+            atomicMax(&s_maxcnt, mc);
+        __syncthreads();
+        maxcnt = s_maxcnt;
+        redo = (double)NS * (double)maxcnt * (double)c.hi_ok > 2147483647.0;
+    }
+    if (ACC == ACC_PACKED && redo) {
+        // the chunk again, with the scale lowered so that the counts just
+        // measured fit (the same particles are admitted: the range moves with
+        // the scale); if that would cost too much precision, into 64-bit sums
+        // at the first scale (or, where those do not fit the LDS, fp32 sums
+        // once even the coarser packed pass would lose too much)
+        const int h2 = min(ORDER == 1 ? 22 : 24,
+                           (int)floor(log2(2147483647.0 / ((double)NS * (double)maxcnt))));
+        const int h = ilogbf(c.hi_ok);
+        // without room for 64-bit sums, a coarser packed pass still beats fp32
+        // LDS atomics by far
+        if (h2 >= PACKED_MIN_BITS || (!a.fb64 && h2 >= PACKED_MIN_BITS - 3)) {
+            TileCtx c2 = c;
+            c2.scale = ldexpf(c.scale, h2 - h);
+            c2.inv_scale = ldexpf(c.inv_scale, h - h2);
+            c2.hi_ok = ldexpf(1.0f, h2);
+            c2.lo_ok = ldexpf(c.lo_ok, h2 - h);
+            uint32_t *w32 = reinterpret_cast<uint32_t *>(smem);
+            for (int i = threadIdx.x; i < c.vol * 3 + ncell; i += blockDim.x)
+                w32[i] = 0u;
+            __syncthreads();
+            pass(std::integral_constant<int, ACC_PACKED>{}, c2, true);
+            __syncthreads();
+            flush_scratch<DIM, ACC_PACKED>(a, c2, sc);
+        } else if (a.fb64) {
+            for (int i = threadIdx.x; i < 3 * c.vol; i += blockDim.x)
+                sc.acc64[i] = 0ull;
+            __syncthreads();
+            pass(std::integral_constant<int, ACC_FIXED>{}, c, true);
+            __syncthreads();
+            flush_scratch<DIM, ACC_FIXED>(a, c, sc);
+        } else {
+            for (int i = threadIdx.x; i < 3 * c.vol; i += blockDim.x)
+                sc.acc32[i] = 0.0f;
+            __syncthreads();
+            pass(std::integral_constant<int, ACC_FLOAT>{}, c, true);
+            __syncthreads();
+            flush_scratch<DIM, ACC_FLOAT>(a, c, sc);
         }
+    } else {
+        flush_scratch<DIM, ACC == ACC_PACKED ? ACC_PACKED : ACC_FLOAT>(a, c, sc);
     }
     if (threadIdx.x == 0 && s_esc && a.n_escaped)
         atomicAdd(a.n_escaped, (unsigned long long)s_esc);
@@ -452,11 +727,11 @@ pcg_status launch_flat(const DepArgs &a, int64_t begin, int64_t end, hipStream_t
                   st, a, begin, end);
 }
 
-template <int DIM, int ORDER, bool FIXED, int TEC, bool MOVE>
+template <int DIM, int ORDER, int ACC, int TEC, bool MOVE>
 pcg_status launch_tiled_impl(const DepArgs &a, const MoveArgs &m, uint32_t nwork, int block,
                              size_t lds, hipStream_t st)
 {
-    auto kern = k_deposit_tiled<DIM, ORDER, FIXED, TEC, MOVE>;
+    auto kern = k_deposit_tiled<DIM, ORDER, ACC, TEC, MOVE>;
     if (lds > 65536) {
         if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)lds) != hipSuccess)
@@ -466,39 +741,43 @@ pcg_status launch_tiled_impl(const DepArgs &a, const MoveArgs &m, uint32_t nwork
                   st, a, m);
 }
 
-constexpr size_t scratch_bytes(int dim, int te, int elem)
-{
-    return (size_t)3 * elem * (dim == 3 ? te * te * te : (dim == 2 ? te * te : te));
-}
-
-// A compile-time scratch edge: int64 fixed-point scratch when it fits the LDS.
+// The scratch mode and LDS size of a layout: packed 32-bit sums (64-bit
+// fallback when three 64-bit sums per node fit) when the packed scratch fits,
+// else fp32 scratch.
 template <int DIM, int ORDER, int TEC, bool MOVE>
-pcg_status launch_tiled_te(const DepArgs &a, const MoveArgs &m, uint32_t nwork, int block,
-                           hipStream_t st)
+pcg_status launch_tiled_mode(DepArgs a, const MoveArgs &m, uint32_t nwork, int block,
+                             hipStream_t st)
 {
-    constexpr bool fixed = scratch_bytes(DIM, TEC, 8) <= LDS_LIMIT;
-    return launch_tiled_impl<DIM, ORDER, fixed, TEC, MOVE>(
-        a, m, nwork, block, scratch_bytes(DIM, TEC, fixed ? 8 : 4), st);
+    const size_t vol = (size_t)a.vol;
+    size_t ncell = 1;
+    for (int k = 0; k < DIM; ++k)
+        ncell *= (size_t)(a.T + 2 * a.D);
+    const size_t packed = packed_bytes(vol, ncell), fixed = vol * 24, flt = vol * 12;
+    if (packed <= LDS_LIMIT) {
+        a.fb64 = fixed <= LDS_LIMIT ? 1 : 0;
+        const size_t lds = std::max(packed, a.fb64 ? fixed : flt);
+        return launch_tiled_impl<DIM, ORDER, ACC_PACKED, TEC, MOVE>(a, m, nwork, block, lds, st);
+    }
+    a.fb64 = 0;
+    return launch_tiled_impl<DIM, ORDER, ACC_FLOAT, TEC, MOVE>(a, m, nwork, block, flt, st);
 }
 
 template <int DIM, int ORDER, bool MOVE>
 pcg_status launch_tiled(const DepArgs &a, const MoveArgs &m, uint32_t nwork, int block,
                         size_t lds, hipStream_t st)
 {
+    (void)lds;
     // the window shapes of tiles 4, 8, 16 with drift 1 are compiled with a
     // constant edge; any other shape uses the runtime-edge kernel
     if (DIM >= 2 && a.D == 1) {
         switch (a.TE) {
-        case ORDER == 1 ? 7 : 8: return launch_tiled_te<DIM, ORDER, ORDER == 1 ? 7 : 8, MOVE>(a, m, nwork, block, st);
-        case ORDER == 1 ? 11 : 12: return launch_tiled_te<DIM, ORDER, ORDER == 1 ? 11 : 12, MOVE>(a, m, nwork, block, st);
-        case ORDER == 1 ? 19 : 20: return launch_tiled_te<DIM, ORDER, ORDER == 1 ? 19 : 20, MOVE>(a, m, nwork, block, st);
+        case ORDER == 1 ? 7 : 8: return launch_tiled_mode<DIM, ORDER, ORDER == 1 ? 7 : 8, MOVE>(a, m, nwork, block, st);
+        case ORDER == 1 ? 11 : 12: return launch_tiled_mode<DIM, ORDER, ORDER == 1 ? 11 : 12, MOVE>(a, m, nwork, block, st);
+        case ORDER == 1 ? 19 : 20: return launch_tiled_mode<DIM, ORDER, ORDER == 1 ? 19 : 20, MOVE>(a, m, nwork, block, st);
         default: break;
         }
     }
-    // int64 fixed-point scratch when it fits, else fp32 scratch (lds is the fp32 size)
-    if (2 * lds <= LDS_LIMIT)
-        return launch_tiled_impl<DIM, ORDER, true, 0, MOVE>(a, m, nwork, block, 2 * lds, st);
-    return launch_tiled_impl<DIM, ORDER, false, 0, MOVE>(a, m, nwork, block, lds, st);
+    return launch_tiled_mode<DIM, ORDER, 0, MOVE>(a, m, nwork, block, st);
 }
 
 template <bool MOVE>
@@ -543,6 +822,31 @@ uint32_t tile_count(const pcg_grid *grid, int T)
     return (uint32_t)nt;
 }
 
+// Smallest chunk a tiled deposit splits a tile into.
+constexpr int64_t MIN_DEPOSIT_CHUNK = 2048;
+
+// Work items of a tiled deposit over `ntiles` tiles and n_part particles:
+// at most one per tile plus one per MIN_DEPOSIT_CHUNK particles.
+uint64_t max_deposit_work(uint32_t ntiles, int64_t n_part)
+{
+    return (uint64_t)ntiles + (uint64_t)(std::max<int64_t>(n_part, 0) / MIN_DEPOSIT_CHUNK) + 1;
+}
+
+// Workspace: chunk prefix, its block totals and the work-item map.
+size_t carve_deposit(uint32_t ntiles, int64_t n_part, void *ws, DepArgs *a)
+{
+    Carver c(ws);
+    uint32_t *cum = c.take<uint32_t>((size_t)ntiles + 1);
+    uint32_t *part = c.take<uint32_t>(chunk_part_len(ntiles));
+    uint32_t *map = c.take<uint32_t>(max_deposit_work(ntiles, n_part));
+    if (a) {
+        a->chunk_cum = cum;
+        a->chunk_part = part;
+        a->chunk_map = map;
+    }
+    return c.used;
+}
+
 size_t deposit_workspace_bytes(const pcg_grid *grid, const pcg_tile *tile)
 {
     if (!tile || !grid || check_grid(grid, "pcg_deposit_workspace_bytes") != PCG_OK || tile->T < 1)
@@ -550,7 +854,7 @@ size_t deposit_workspace_bytes(const pcg_grid *grid, const pcg_tile *tile)
     for (int k = 0; k < grid->dim; ++k)
         if (grid->n[k] % tile->T)
             return 0;
-    return align_up(((size_t)tile_count(grid, tile->T) + 1) * sizeof(uint32_t), 256);
+    return carve_deposit(tile_count(grid, tile->T), tile->n_partitioned, nullptr, nullptr);
 }
 
 // A validated tiled deposit, ready to launch.
@@ -576,8 +880,8 @@ pcg_status prepare_deposit(const char *who, const pcg_grid *grid, const pcg_part
     if (order != 1 && order != 2)
         return fail(PCG_EUNSUPPORTED, "%s: order %d not in {1,2}", who, order);
     const int64_t count = particles->count;
-    if (count < 0 || count >= (int64_t(1) << 31))
-        return fail(PCG_EINVAL, "%s: count %lld outside [0, 2^31)", who, (long long)count);
+    if (count < 0 || count >= (int64_t(1) << 30))
+        return fail(PCG_EINVAL, "%s: count %lld outside [0, 2^30)", who, (long long)count);
     if (!J)
         return fail(PCG_EINVAL, "%s: J is NULL", who);
     if (count > 0) {
@@ -643,7 +947,7 @@ pcg_status prepare_deposit(const char *who, const pcg_grid *grid, const pcg_part
     int block = tile->block;
     if (block <= 0)
         block = 512;  // one scratch tile (up to ~36 KB) shared by 8 waves
-    block = std::max(64, std::min(1024, block)) / 64 * 64;
+    block = std::max(64, std::min(512, block)) / 64 * 64;
 
     a.T = T;
     a.D = D;
@@ -654,15 +958,34 @@ pcg_status prepare_deposit(const char *who, const pcg_grid *grid, const pcg_part
     a.ntiles = tile_count(grid, T);
     a.tile_offsets = tile->tile_offsets;
     a.n_part = tile->n_partitioned;
-    a.chunk_cum = static_cast<const uint32_t *>(workspace);
+    carve_deposit(a.ntiles, a.n_part, workspace, &a);
     // a tile holding more than `chunk` particles is split over several
     // work-groups (each with its own scratch and flush) to balance load
     const int64_t target = (count + (int64_t)device_cus() * 4 - 1) / ((int64_t)device_cus() * 4);
-    int64_t chunk = std::max<int64_t>(2048, target);
+    int64_t chunk = std::max<int64_t>(MIN_DEPOSIT_CHUNK, target);
     if (max_chunk)
         chunk = std::min<int64_t>(chunk, max_chunk);
+    {
+        // Where the 64-bit sums do not fit the LDS (no exact fallback for a
+        // dense chunk), chunks are kept small enough that the packed 32-bit
+        // sums get their full rounding precision (2^PACKED_MIN_BITS) at twice
+        // a chunk's mean density: (order+1)^dim (2 c + 1) + 1 <= 2^(31 - bits)
+        // particles per cell c.
+        int64_t tcells = 1, ns = 1;
+        for (int k = 0; k < grid->dim; ++k) {
+            tcells *= T;
+            ns *= order + 1;
+        }
+        if ((size_t)vol * 24 > LDS_LIMIT) {
+            const int bits = order == 1 ? 21 : 23;
+            const int64_t per_cell = std::max<int64_t>(1, (((int64_t)1 << (31 - bits)) - 1 - ns) / (2 * ns));
+            chunk = std::min<int64_t>(chunk, std::max<int64_t>(MIN_DEPOSIT_CHUNK, per_cell * tcells));
+        }
+    }
     a.chunk = (uint32_t)chunk;
     const uint64_t nwork = (uint64_t)a.ntiles + ((uint64_t)a.n_part + a.chunk - 1) / a.chunk;
+    if (nwork > max_deposit_work(a.ntiles, a.n_part))
+        return fail(PCG_EINVAL, "%s: internal: work items exceed the map", who);
     if (nwork >= (uint64_t(1) << 31))
         return fail(PCG_EINVAL, "%s: too many work-groups", who);
     plan->nwork = (uint32_t)nwork;
@@ -673,9 +996,10 @@ pcg_status prepare_deposit(const char *who, const pcg_grid *grid, const pcg_part
 
 pcg_status launch_chunks(const DepArgs &a, hipStream_t st)
 {
-    return launch("deposit_chunks", k_chunk_cum, dim3(1), dim3(1024), 0, st, a.tile_offsets,
-                  a.ntiles, a.n_part, a.chunk, const_cast<uint32_t *>(a.chunk_cum),
-                  (const uint32_t *)nullptr, 0u);
+    return launch_chunk_layout("deposit_chunks", a.tile_offsets, a.ntiles, a.n_part, a.chunk,
+                               const_cast<uint32_t *>(a.chunk_cum), a.chunk_part,
+                               const_cast<uint32_t *>(a.chunk_map),
+                               (uint32_t)max_deposit_work(a.ntiles, a.n_part), nullptr, 0u, st);
 }
 
 // The fused pass's move hook: it replaces the incremental sort's move kernel.

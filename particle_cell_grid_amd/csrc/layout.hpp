@@ -1,7 +1,9 @@
 // layout.hpp -- work decomposition over a tile layout, shared by the deposit
 // and the incremental sort: each tile slice [off[t], off[t+1]) (clipped to the
 // partitioned prefix) is split into ceil(len / chunk) balanced chunks; a
-// prefix over tiles numbers the chunks so that one work-group takes one chunk.
+// prefix over tiles numbers the chunks so that one work-group takes one chunk,
+// and a map from chunk number to tile lets a work-group find its chunk with
+// two dependent reads.
 #pragma once
 
 #include <algorithm>
@@ -12,29 +14,23 @@
 namespace pcg {
 namespace {
 
-// Work items per tile: ceil(len/chunk) (0 for an empty tile), exclusive prefix
-// over tiles into cum[0..ntiles]; one work-group of 1024 threads.
-__global__ __launch_bounds__(1024) void k_chunk_cum(const uint32_t *__restrict__ off,
-                                                    uint32_t ntiles, int64_t n_part,
-                                                    uint32_t chunk, uint32_t *__restrict__ cum,
-                                                    const uint32_t *gate, uint32_t gate_run)
+constexpr int CHUNK_SCAN_BLOCK = 1024;  // tiles per block of the chunk prefix
+
+// Work items of tile t: ceil(len / chunk), 0 for an empty tile.
+__device__ inline uint32_t tile_items(const uint32_t *__restrict__ off, uint32_t t, int64_t n_part,
+                                      uint32_t chunk)
 {
-    if (gate && *gate != gate_run)
-        return;
-    __shared__ uint32_t wsum[1024 / WAVE];
-    const uint32_t per = (ntiles + 1023) / 1024;
-    const uint32_t t0 = threadIdx.x * per;
-    const uint32_t t1 = min(t0 + per, ntiles);
-    auto items = [&](uint32_t t) -> uint32_t {
-        const uint64_t p0 = std::min<uint64_t>(off[t], (uint64_t)n_part);
-        const uint64_t p1 = std::min<uint64_t>(off[t + 1], (uint64_t)n_part);
-        return p1 > p0 ? (uint32_t)((p1 - p0 + chunk - 1) / chunk) : 0u;
-    };
-    uint32_t s = 0;
-    for (uint32_t t = t0; t < t1; ++t)
-        s += items(t);
+    const uint64_t p0 = std::min<uint64_t>(off[t], (uint64_t)n_part);
+    const uint64_t p1 = std::min<uint64_t>(off[t + 1], (uint64_t)n_part);
+    return p1 > p0 ? (uint32_t)((p1 - p0 + chunk - 1) / chunk) : 0u;
+}
+
+// Exclusive prefix of v over the block (1024 threads); *total gets the sum.
+__device__ inline uint32_t block_exclusive_1024(uint32_t v, uint32_t *total)
+{
+    __shared__ uint32_t wsum[CHUNK_SCAN_BLOCK / WAVE];
     const int wave = threadIdx.x / WAVE, lane = lane_id();
-    uint32_t inc = s;
+    uint32_t inc = v;
 #pragma unroll
     for (int o = 1; o < WAVE; o <<= 1) {
         const uint32_t u = __shfl_up(inc, o, WAVE);
@@ -45,17 +41,102 @@ __global__ __launch_bounds__(1024) void k_chunk_cum(const uint32_t *__restrict__
         wsum[wave] = inc;
     __syncthreads();
     uint32_t before = 0, all = 0;
-    for (int w = 0; w < 1024 / WAVE; ++w) {
+    for (int w = 0; w < CHUNK_SCAN_BLOCK / WAVE; ++w) {
         before += w < wave ? wsum[w] : 0u;
         all += wsum[w];
     }
-    uint32_t run = before + inc - s;
-    for (uint32_t t = t0; t < t1; ++t) {
-        cum[t] = run;
-        run += items(t);
+    *total = all;
+    return before + inc - v;
+}
+
+// Pass 1, one block per CHUNK_SCAN_BLOCK tiles: block-local exclusive prefix of
+// the work items into cum[], the block's total into part[block].
+__global__ __launch_bounds__(CHUNK_SCAN_BLOCK) void k_chunk_scan1(
+    const uint32_t *__restrict__ off, uint32_t ntiles, int64_t n_part, uint32_t chunk,
+    uint32_t *__restrict__ cum, uint32_t *__restrict__ part, const uint32_t *gate,
+    uint32_t gate_run)
+{
+    if (gate && *gate != gate_run)
+        return;
+    const uint32_t t = blockIdx.x * CHUNK_SCAN_BLOCK + threadIdx.x;
+    const uint32_t v = t < ntiles ? tile_items(off, t, n_part, chunk) : 0u;
+    uint32_t total;
+    const uint32_t ex = block_exclusive_1024(v, &total);
+    if (t < ntiles)
+        cum[t] = ex;
+    if (threadIdx.x == 0)
+        part[blockIdx.x] = total;
+}
+
+// Pass 2, one block: exclusive prefix of the nb block totals (in place); the
+// grand total goes to cum[ntiles].
+__global__ __launch_bounds__(CHUNK_SCAN_BLOCK) void k_chunk_scan2(uint32_t *__restrict__ part,
+                                                                 uint32_t nb,
+                                                                 uint32_t *__restrict__ cum,
+                                                                 uint32_t ntiles,
+                                                                 const uint32_t *gate,
+                                                                 uint32_t gate_run)
+{
+    if (gate && *gate != gate_run)
+        return;
+    uint32_t carry = 0;
+    for (uint32_t base = 0; base < nb; base += CHUNK_SCAN_BLOCK) {
+        const uint32_t i = base + threadIdx.x;
+        const uint32_t v = i < nb ? part[i] : 0u;
+        uint32_t total;
+        const uint32_t ex = block_exclusive_1024(v, &total);
+        if (i < nb)
+            part[i] = carry + ex;
+        carry += total;
+        __syncthreads();  // wsum is reused by the next round
     }
     if (threadIdx.x == 0)
-        cum[ntiles] = all;
+        cum[ntiles] = carry;
+}
+
+// Pass 3: global prefix (cum[t] += block offset) and the map from work item to
+// tile: map[cum[t] + j] = t for j < items(t).
+// Entries past map_len are not written (offsets that are not a partition
+// could ask for more); their work items are never launched.
+__global__ __launch_bounds__(CHUNK_SCAN_BLOCK) void k_chunk_scan3(
+    const uint32_t *__restrict__ off, uint32_t ntiles, int64_t n_part, uint32_t chunk,
+    uint32_t *__restrict__ cum, const uint32_t *__restrict__ part, uint32_t *__restrict__ map,
+    uint32_t map_len, const uint32_t *gate, uint32_t gate_run)
+{
+    if (gate && *gate != gate_run)
+        return;
+    const uint32_t t = blockIdx.x * CHUNK_SCAN_BLOCK + threadIdx.x;
+    if (t >= ntiles)
+        return;
+    const uint32_t c0 = cum[t] + part[blockIdx.x];
+    cum[t] = c0;
+    const uint32_t n = tile_items(off, t, n_part, chunk);
+    for (uint32_t j = 0; j < n && (uint64_t)c0 + j < map_len; ++j)
+        map[c0 + j] = t;
+}
+
+// Enqueues the three passes: cum[0..ntiles] and map[0..min(cum[ntiles],
+// map_len)).  part
+// needs ceil(ntiles / CHUNK_SCAN_BLOCK) entries.  With a gate, the kernels
+// return at once unless *gate == gate_run.
+inline pcg_status launch_chunk_layout(const char *name, const uint32_t *off, uint32_t ntiles,
+                                      int64_t n_part, uint32_t chunk, uint32_t *cum,
+                                      uint32_t *part, uint32_t *map, uint32_t map_len,
+                                      const uint32_t *gate, uint32_t gate_run, hipStream_t st)
+{
+    const uint32_t nb = (ntiles + CHUNK_SCAN_BLOCK - 1) / CHUNK_SCAN_BLOCK;
+    PCG_TRY(launch(name, k_chunk_scan1, dim3(nb), dim3(CHUNK_SCAN_BLOCK), 0, st, off, ntiles,
+                   n_part, chunk, cum, part, gate, gate_run));
+    PCG_TRY(launch(name, k_chunk_scan2, dim3(1), dim3(CHUNK_SCAN_BLOCK), 0, st, part, nb, cum,
+                   ntiles, gate, gate_run));
+    return launch(name, k_chunk_scan3, dim3(nb), dim3(CHUNK_SCAN_BLOCK), 0, st, off, ntiles,
+                  n_part, chunk, cum, (const uint32_t *)part, map, map_len, gate, gate_run);
+}
+
+// Entries of part[] launch_chunk_layout needs for ntiles tiles.
+inline size_t chunk_part_len(uint32_t ntiles)
+{
+    return (ntiles + CHUNK_SCAN_BLOCK - 1) / CHUNK_SCAN_BLOCK + 1;
 }
 
 struct ChunkRange {
@@ -64,29 +145,24 @@ struct ChunkRange {
     uint32_t lo, hi;
 };
 
-// Decode work item `item` (one thread calls this): the tile whose chunk range
-// holds it, and the item's share of that tile's slice.
-__device__ inline ChunkRange find_chunk(uint32_t item, const uint32_t *cum, uint32_t ntiles,
-                                        const uint32_t *off, int64_t n_part)
+// Decode work item `item` (one thread calls this; item < the map's length):
+// the tile that holds it, from the map, and the item's share of the tile's
+// slice.
+__device__ inline ChunkRange find_chunk(uint32_t item, const uint32_t *cum, const uint32_t *map,
+                                        uint32_t ntiles, const uint32_t *off, int64_t n_part)
 {
     ChunkRange r{UINT_MAX, item, 0, 0};
-    if (item >= cum[ntiles])
+    const uint32_t total = cum[ntiles];
+    const uint32_t t = map[item];  // stale past the total: checked first
+    if (item >= total || t >= ntiles)
         return r;
-    // largest t with cum[t] <= item (empty tiles own no items)
-    uint32_t lo = 0, hi = ntiles - 1;
-    while (lo < hi) {
-        const uint32_t mid = (lo + hi + 1) >> 1;
-        if (cum[mid] <= item)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    const uint32_t t = lo;
     const uint32_t nch = cum[t + 1] - cum[t];
     const uint32_t c = item - cum[t];
     const uint64_t p0 = std::min<uint64_t>(off[t], (uint64_t)n_part);
     const uint64_t p1 = std::min<uint64_t>(off[t + 1], (uint64_t)n_part);
     const uint64_t len = p1 > p0 ? p1 - p0 : 0;
+    if (c >= nch)
+        return r;
     r.tile = t;
     r.lo = (uint32_t)(p0 + len * c / nch);
     r.hi = (uint32_t)(p0 + len * (c + 1) / nch);

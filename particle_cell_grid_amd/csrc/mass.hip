@@ -66,7 +66,7 @@ struct RawParticle {
 
 __device__ inline RawParticle load_raw(const MassArgs &m, int64_t p)
 {
-    // particle counts are below 2^31, so a 32-bit byte offset from each array's
+    // particle counts are below 2^30, so a 32-bit byte offset from each array's
     // base addresses every element (one scalar base + one vector offset)
     const uint32_t off = (uint32_t)p * 4u;
     auto at = [off](const float *base) {
@@ -695,8 +695,8 @@ extern "C" pcg_status assemble_mass_matrix(const pcg_grid *grid, const pcg_parti
     if (variant < PCG_MASS_AUTO || variant > PCG_MASS_FLAT)
         return fail(PCG_EINVAL, "%s: unknown variant %d", who, variant);
     const int64_t count = particles->count;
-    if (count < 0 || count >= (int64_t(1) << 31))
-        return fail(PCG_EINVAL, "%s: count %lld outside [0, 2^31)", who, (long long)count);
+    if (count < 0 || count >= (int64_t(1) << 30))
+        return fail(PCG_EINVAL, "%s: count %lld outside [0, 2^30)", who, (long long)count);
     if (count > 0) {
         for (int k = 0; k < 3; ++k)
             if (!particles->x[k] || !B || !B[k])

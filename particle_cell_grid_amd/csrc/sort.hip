@@ -10,7 +10,8 @@
 // (fewer on a thin grid) neighbours of the tile whose slice holds it, so the
 // stable order is a counting sort over (source chunk, direction):
 //   k_inc_validate  prev is a partition of [0, count) (else fall back);
-//   k_chunk_cum     source slices split into balanced chunks;
+//   k_chunk_scan*   source slices split into balanced chunks (prefix and a
+//                   chunk-to-tile map);
 //   k_inc_count     per chunk, particles per direction (a particle that moved
 //                   further raises the fall-back flag);
 //   k_inc_totals    per new tile, the sum over its source (chunk, direction)s;
@@ -415,7 +416,7 @@ __global__ __launch_bounds__(64) void k_inc_rank(IncGeom a, const float *x0, con
     __shared__ uint32_t s_tile, s_lo, s_hi;
     __shared__ uint32_t s_run[32];
     if (threadIdx.x == 0) {
-        const ChunkRange r = find_chunk(blockIdx.x, a.cum, a.ntiles, a.prev_off, a.count);
+        const ChunkRange r = find_chunk(blockIdx.x, a.cum, a.map, a.ntiles, a.prev_off, a.count);
         s_tile = r.tile;
         s_lo = r.lo;
         s_hi = r.hi;
@@ -578,7 +579,7 @@ __global__ __launch_bounds__(256) void k_inc_move(IncGeom a, const uint32_t *__r
     __shared__ uint32_t s_tile, s_lo, s_hi;
     __shared__ uint32_t s_base[NDIR], s_dest[NDIR];
     if (threadIdx.x == 0) {
-        const ChunkRange r = find_chunk(blockIdx.x, a.cum, a.ntiles, a.prev_off, a.count);
+        const ChunkRange r = find_chunk(blockIdx.x, a.cum, a.map, a.ntiles, a.prev_off, a.count);
         s_tile = r.tile;
         s_lo = r.lo;
         s_hi = r.hi;
@@ -665,7 +666,7 @@ SortPlan make_plan(const pcg_grid *grid, int64_t count, int T)
 
 struct SortBuffers {
     uint32_t *k0, *ak, *av, *bv, *fk, *pm, *counts, *partial;
-    uint32_t *flag, *cum, *cnt, *tcnt, *tpre;
+    uint32_t *flag, *cum, *cnt, *tcnt, *tpre, *cpart, *cmap;
 };
 
 size_t carve(const SortPlan &p, void *ws, SortBuffers *b)
@@ -686,6 +687,8 @@ size_t carve(const SortPlan &p, void *ws, SortBuffers *b)
     b->cnt = c.take<uint32_t>((size_t)p.nchunks_max * NDIR);
     b->tcnt = c.take<uint32_t>((size_t)p.ntiles * NDIR);
     b->tpre = c.take<uint32_t>((size_t)p.ntiles * NDIR);
+    b->cpart = c.take<uint32_t>(chunk_part_len(p.ntiles));
+    b->cmap = c.take<uint32_t>(p.nchunks_max);
     return c.used;
 }
 
@@ -903,6 +906,7 @@ pcg_status tile_sort_impl(const pcg_grid *grid, int32_t order, int32_t T, int64_
         a.prev_off = prev->tile_offsets;
         a.count = count;
         a.cum = b.cum;
+        a.map = b.cmap;
         a.cnt = b.cnt;
         a.tcnt = b.tcnt;
         a.tpre = b.tpre;
@@ -913,9 +917,9 @@ pcg_status tile_sort_impl(const pcg_grid *grid, int32_t order, int32_t T, int64_
         PCG_TRY(launch("sort_inc_flag", k_set_flag, dim3(1), dim3(64), 0, st, b.flag, 0u));
         PCG_TRY(launch("sort_inc_validate", k_inc_validate, dim3((p.ntiles + 1 + 255) / 256),
                        dim3(256), 0, st, prev->tile_offsets, p.ntiles, count, b.flag));
-        PCG_TRY(launch("sort_inc_chunks", k_chunk_cum, dim3(1), dim3(1024), 0, st,
-                       prev->tile_offsets, p.ntiles, count, chunk, b.cum,
-                       (const uint32_t *)b.flag, 0u));
+        PCG_TRY(launch_chunk_layout("sort_inc_chunks", prev->tile_offsets, p.ntiles, count, chunk,
+                                    b.cum, b.cpart, b.cmap, p.nchunks_max,
+                                    (const uint32_t *)b.flag, 0u, st));
         const int key = grid->dim * 10 + order;
         pcg_status s = PCG_OK;
         switch (key) {

@@ -115,6 +115,7 @@ def test_deposit_validation(lib):
     P2.q = None
     assert call(grid(3, [8, 8, 8]), P=P2) == EINVAL
     assert call(grid(3, [8, 8, 8]), P=particles(-1)) == EINVAL
+    assert call(grid(3, [8, 8, 8]), P=particles(1 << 30)) == EINVAL   # 32-bit byte offsets
     g = grid(3, [64, 64, 64])
     t = Tile(8, 2, 1, 0, 1000, FAKE)
     assert call(g, order=1, tile=t) == EINVAL                     # layout keyed with TSC
@@ -214,6 +215,8 @@ def test_mass_and_sweep_validation(lib):
     assert call(g=C.byref(grid(2, [8, 8]))) == EUNSUPPORTED
     assert call(g=C.byref(grid(3, [2, 8, 8]))) == EINVAL
     assert call(variant=9) == EINVAL
+    big = particles(1 << 30)
+    assert am(g8, C.byref(big), B, FAKE, None, 0, FAKE, FAKE, 256, None) == EINVAL
     assert call(variant=1) == EINVAL                              # MFMA needs cells
     t = Tile(2, 1, 0, 0, 100, FAKE)
     assert call(variant=1, cells=C.byref(t)) == EINVAL            # not a cell layout

@@ -233,3 +233,44 @@ def test_tiled_is_deterministic(orc):
     a = J1.reshape(3, 4, 8, 4, 8, 4, 8)[:, :, 2:7, :, 2:7, :, 2:7]
     b = J2.reshape(3, 4, 8, 4, 8, 4, 8)[:, :, 2:7, :, 2:7, :, 2:7]
     assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------- 32-bit sums
+
+def _crowded_cell(n, order, count_bg, count_cell, cell, seed):
+    """A sparse uniform background plus one cell holding `count_cell` particles
+    that all carry the same current: the tile's mean density is low, so its
+    32-bit sums are sized for few particles per cell and the per-cell count
+    cannot rule out an overflow -- the work-group re-runs its chunk into wider
+    sums."""
+    r = np.random.default_rng(seed)
+    dim = len(n)
+    x = [r.uniform(0, n[k], count_bg).astype(np.float32) for k in range(dim)]
+    for k in range(dim):
+        x[k] = np.concatenate([x[k], (cell[k] + r.uniform(0.05, 0.95, count_cell))
+                               .astype(np.float32)])
+    cnt = count_bg + count_cell
+    v = [np.concatenate([r.normal(0, 0.1, count_bg), np.full(count_cell, 0.45)])
+         .astype(np.float32) for _ in range(3)]
+    q = np.ones(cnt, np.float32)
+    w = np.ones(cnt, np.float32)
+    return synthetic.Workload(dim, list(n), x, [a.copy() for a in x], v, q, w)
+
+
+@pytest.mark.parametrize("dim,n,order,T,crowd", [
+    (3, [16, 16, 16], 1, 8, 400),    # runs again at a lower scale
+    (3, [16, 16, 16], 1, 8, 3000),   # runs again into 64-bit sums
+    (2, [32, 32], 1, 8, 3000),
+    (3, [32, 32, 32], 2, 16, 3000),  # 64-bit sums do not fit the LDS: fp32 sums
+])
+def test_overflow_guard_reruns_the_chunk(orc, dim, n, order, T, crowd):
+    cell = [T // 2] * dim
+    wl = _crowded_cell(n, order, 400, crowd, cell, seed=49 + dim + order)
+    s, off = _sorted_pushed(orc, wl, order, T)
+    J, esc = _run_tiled(s, order, T, 1, off)
+    ref = orc.deposit(dim, wl.n, order, s.x_next, s.v, s.q, s.w)
+    n_ref, _ = orc.escape(dim, wl.n, order, T, 1, s.x_next, off)
+    assert rel_max_err(J, ref) <= TOL and esc == n_ref
+    # the crowded cell's nodes carry ~crowd x 0.45 / 2^dim each: far beyond
+    # the range the 32-bit sums were first sized for
+    assert np.abs(ref).max() > crowd * 0.45 / 2 ** dim / 2

@@ -50,14 +50,24 @@ def short(name):
 
 
 def tap_name(kernel):
-    """The library's launch names for its kernels (as the benchmark reports them)."""
-    table = {"k_deposit_tiled": "deposit_tiled", "k_deposit_flat": "deposit_flat",
+    """The library's launch names for its kernels (as the benchmark reports them).
+    Template arguments tell apart launches of one kernel template: the tiled
+    deposit with its regroup flag set is `deposit_regroup`, the column mass
+    kernel on matrix cores is `mass_mfma`."""
+    base = kernel.split("<")[0]
+    targs = kernel[len(base) + 1:-1].split(",") if "<" in kernel else []
+    last = targs[-1].strip() if targs else ""
+    if base == "k_deposit_tiled":
+        return "deposit_regroup" if last == "true" else "deposit_tiled"
+    if base == "k_mass_column":
+        return "mass_mfma" if last == "true" else "mass_valu"
+    table = {"k_deposit_flat": "deposit_flat",
              "k_inc_move": "sort_inc_move", "k_inc_rank": "sort_inc_rank",
-             "k_inc_tiles": "sort_inc_tiles", "k_inc_chunk_prefix": "sort_inc_chunk_prefix",
-             "k_mass_mfma": "mass_mfma", "k_mass_valu": "mass_valu", "k_mass_flat": "mass_flat",
+             "k_inc_tiles": "sort_inc_tiles", "k_mass_flat": "mass_flat",
+             "k_mass_strays": "mass_strays",
              "k_permute": "sort_permute", "k_tile_keys": "sort_keys",
              "k_sweep1d": "sweep1d"}
-    return table.get(kernel.split("<")[0])
+    return table.get(base)
 
 
 def one(pattern):

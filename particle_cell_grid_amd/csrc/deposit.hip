@@ -6,10 +6,12 @@
 // chunk of a heavy tile) zeroes an LDS scratch window of TE = T + order + 2D
 // nodes per used axis (D nodes of drift below the tile origin, D + order
 // above), adds every particle of its slice into it with LDS atomics (exact
-// int64 fixed-point sums, see k_deposit_tiled), then adds each non-zero scratch
-// value to J with one global atomic, wrapping node indices periodically.  A particle whose support does not fit the window is
-// deposited directly to J with global atomics (the escape valve, [TD]
-// "Correctness is independent of the halo").
+// integer fixed-point sums, see k_deposit_tiled), then adds each non-zero
+// scratch value to J with one global atomic, wrapping node indices
+// periodically.  A particle whose support does not fit the window is deposited
+// directly to J with global atomics (the escape valve, [TD] "Correctness is
+// independent of the halo"), from a queue the work-group drains after its
+// chunk.
 // Flat path ([TD] "The two paths", flat column): one thread per particle,
 // (order+1)^dim x 3 global atomics -- used with no layout and for the tail.
 #include <algorithm>
@@ -51,6 +53,8 @@ struct DepArgs {
     uint32_t chunk;
     unsigned long long *n_escaped;
     int fb64;  // tiled: the packed scratch falls back to 64-bit sums (else fp32)
+    uint32_t qoff, qcap;  // tiled: byte offset and capacity of the LDS queue of
+                          // particles deposited with global atomics
 };
 
 // The regrouping half of the fused pass: every particle the deposit loads is
@@ -236,14 +240,22 @@ struct TileCtx {
     float lo_ok, hi_ok;     // admitted range of the largest scaled |q w v_c|
 };
 
-// LDS views of the scratch tile (all start at the dynamic LDS base).
+// LDS views of the scratch tile (all start at the dynamic LDS base), and the
+// queue of particles that take global atomics (after the scratch).
 struct Scratch {
     unsigned long long *xy;  // PACKED [vol]
     uint32_t *z;             // PACKED [vol]
     uint32_t *cnt;           // PACKED [cedge^dim] particles per base cell
     unsigned long long *acc64;  // FIXED [3][vol]
     float *acc32;               // FLOAT [3][vol]
+    float *queue;               // [qcap][QUEUE_FLOATS]: raw x[3], q w v[3]
+    uint32_t *qn;               // entries claimed (may exceed qcap)
+    uint32_t qcap;
 };
+
+// A queued particle: its raw coordinates and its amplitude q w v_c.
+constexpr int QUEUE_FLOATS = 6;
+constexpr uint32_t QUEUE_MAX = 512;  // entries per work-group (12 KiB)
 
 // One particle: its support, then either the LDS scratch (mode MODE) or, if
 // its stencil leaves the window or its amplitude is outside the admitted
@@ -286,10 +298,23 @@ __device__ __attribute__((always_inline)) inline uint32_t deposit_one(const DepA
 #pragma unroll
         for (int k = 0; k < 3; ++k)
             amp[k] *= c.inv_scale;  // exact: power-of-two scale
+        // queue it for the work-group's global pass after the chunk (a wave
+        // would otherwise run this particle's global atomics with every other
+        // lane idle); straight to global memory when the queue is full
+        const uint32_t slot = sc.qcap ? atomicAdd(sc.qn, 1u) : 0u;
+        if (slot < sc.qcap) {
+            float *e = sc.queue + (size_t)slot * QUEUE_FLOATS;
 #pragma unroll
-        for (int k = 0; k < DIM; ++k)
-            b[k] = wrap_once(b[k], a.n[k]);
-        deposit_global<DIM, ORDER>(a, b, W, amp);
+            for (int k = 0; k < 3; ++k) {
+                e[k] = k < DIM ? xs[k] : 0.0f;
+                e[3 + k] = amp[k];
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < DIM; ++k)
+                b[k] = wrap_once(b[k], a.n[k]);
+            deposit_global<DIM, ORDER>(a, b, W, amp);
+        }
         return esc ? 1u : 0u;
     }
     // amp_c * W_x first, then one product per (node, component)
@@ -395,6 +420,42 @@ __device__ __attribute__((always_inline)) inline void flush_scratch(const DepArg
     }
 }
 
+// The queued particles' global atomics, one (particle, stencil node) pair per
+// thread: the same weights and products as deposit_global.  Call after a
+// barrier that follows the last queue write.
+template <int DIM, int ORDER>
+__device__ __attribute__((always_inline)) inline void drain_queue(const DepArgs &a,
+                                                                  const Scratch &sc)
+{
+    constexpr int M = ORDER + 1;
+    constexpr int NS = DIM == 3 ? M * M * M : (DIM == 2 ? M * M : M);
+    auto wrap_up = [](int v, int n) { return v - (v >= n ? n : 0); };
+    const uint32_t n = min(*sc.qn, sc.qcap);
+    for (uint32_t i = threadIdx.x; i < n * NS; i += blockDim.x) {
+        const float *e = sc.queue + (size_t)(i / NS) * QUEUE_FLOATS;
+        const int node = (int)(i % NS);
+        const int off[3] = {node % M, (node / M) % M, node / (M * M)};
+        int g[3] = {0, 0, 0};
+        float wk[3] = {1.0f, 1.0f, 1.0f};
+#pragma unroll
+        for (int k = 0; k < DIM; ++k) {
+            float W[M];
+            const int b = shape_axis<ORDER>(e[k], a.nf[k], a.n[k], W);
+            float w = W[0];
+#pragma unroll
+            for (int j = 1; j < M; ++j)
+                w = off[k] == j ? W[j] : w;
+            wk[k] = w;
+            g[k] = wrap_up(b + off[k], a.n[k]);
+        }
+        const int64_t gi = g[0] + (int64_t)a.n[0] * (g[1] + (int64_t)a.n[1] * g[2]);
+        const float wt = wk[0] * ((DIM > 1 ? wk[1] : 1.0f) * (DIM > 2 ? wk[2] : 1.0f));
+#pragma unroll
+        for (int c = 0; c < 3; ++c)
+            atomic_add_f32(&a.J[c * a.ng + gi], e[3 + c] * wt);
+    }
+}
+
 // Bytes of LDS the packed scratch and its fallback need.
 __host__ __device__ constexpr size_t packed_bytes(size_t vol, size_t ncell)
 {
@@ -407,7 +468,7 @@ template <int DIM, int ORDER, int ACC, int TEC, bool MOVE>
 __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    __shared__ uint32_t s_tile, s_lo, s_hi, s_esc, s_maxbits, s_move, s_maxcnt;
+    __shared__ uint32_t s_tile, s_lo, s_hi, s_esc, s_maxbits, s_move, s_maxcnt, s_qn;
     // MOVE: output slot base per (incremental chunk overlapped, direction), and
     // the end slot of each of those chunks
     __shared__ uint32_t s_base[MOVE ? MOVE_MAX_CHUNKS * NDIR : 1];
@@ -420,6 +481,7 @@ __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
         s_lo = r.lo;
         s_hi = r.hi;
         s_esc = 0;
+        s_qn = 0;
         s_maxbits = 0;
         s_maxcnt = 0;
         s_move = MOVE && *m.inc.flag == 0u;
@@ -454,6 +516,9 @@ __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
     sc.cnt = reinterpret_cast<uint32_t *>(smem + (size_t)c.vol * 12);
     sc.acc64 = reinterpret_cast<unsigned long long *>(smem);
     sc.acc32 = reinterpret_cast<float *>(smem);
+    sc.queue = reinterpret_cast<float *>(smem + a.qoff);
+    sc.qn = &s_qn;
+    sc.qcap = a.qcap;
 
     // MOVE: the incremental chunks of this tile's slice that [lo, hi) overlaps
     const bool move = MOVE && s_move != 0u;
@@ -550,30 +615,31 @@ __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
         auto load_group = [&](uint32_t base) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const uint32_t p = base + u * stride;
+                // no branch around the loads: a lane past the slice reloads the
+                // slice's last particle (never used), so the number of loads in
+                // flight is fixed and the wait for this group can leave the
+                // next group's loads outstanding.  Counts are below 2^30, so a
+                // 32-bit byte offset from each array's base reaches every
+                // element.
+                const uint32_t p = min(base + u * stride, hi - 1);
+                const uint32_t off = p * 4u;
+                auto at = [off](const float *base) {
+                    return *reinterpret_cast<const float *>(
+                        reinterpret_cast<const char *>(base) + off);
+                };
                 nx[u][0] = nx[u][1] = nx[u][2] = 0.f;
-                nv[u][0] = nv[u][1] = nv[u][2] = 0.f;
-                nq[u] = nw[u] = 0.f;
+#pragma unroll
+                for (int k = 0; k < DIM; ++k)
+                    nx[u][k] = at(a.x[k]);
+#pragma unroll
+                for (int k = 0; k < 3; ++k)
+                    nv[u][k] = at(a.v[k]);
+                nq[u] = at(a.q);
+                nw[u] = at(a.w);
                 ncode[u] = 0;
-                if (p < hi) {
-                    // counts are below 2^30: a 32-bit byte offset from each
-                    // array's base reaches every element
-                    const uint32_t off = p * 4u;
-                    auto at = [off](const float *base) {
-                        return *reinterpret_cast<const float *>(
-                            reinterpret_cast<const char *>(base) + off);
-                    };
-#pragma unroll
-                    for (int k = 0; k < DIM; ++k)
-                        nx[u][k] = at(a.x[k]);
-#pragma unroll
-                    for (int k = 0; k < 3; ++k)
-                        nv[u][k] = at(a.v[k]);
-                    nq[u] = at(a.q);
-                    nw[u] = at(a.w);
-                    if (mv)
-                        ncode[u] = m.inc.code[p];
-                }
+                if (MOVE)
+                    ncode[u] = *reinterpret_cast<const uint32_t *>(
+                        reinterpret_cast<const char *>(m.inc.code) + off);
             }
         };
         uint32_t ci = 0, c_end = 0;  // MOVE: this thread's chunk (relative to c_first) and its end
@@ -599,6 +665,18 @@ __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
                 gcode[u] = ncode[u];
             }
             load_group(base + U * stride);
+            // One unconditional wait for this group's values (loaded an
+            // iteration ago), before any branch: the per-particle branches
+            // below then need no waits of their own, and the counter-based
+            // waits the compiler would place there after the move stores
+            // would also drain the next group's loads.
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                asm volatile("" ::"v"(gx[u][0]), "v"(gx[u][1]), "v"(gx[u][2]), "v"(gv[u][0]),
+                             "v"(gv[u][1]), "v"(gv[u][2]), "v"(gq[u]), "v"(gw[u]));
+                if (MOVE)
+                    asm volatile("" ::"v"(gcode[u]));
+            }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const uint32_t p = base + u * stride;
@@ -644,6 +722,7 @@ __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
         pass(std::integral_constant<int, ACC_FIXED>{}, c, false);
         __syncthreads();
         flush_scratch<DIM, ACC_FIXED>(a, c, sc);
+        drain_queue<DIM, ORDER>(a, sc);
         if (threadIdx.x == 0 && s_esc && a.n_escaped)
             atomicAdd(a.n_escaped, (unsigned long long)s_esc);
         return;
@@ -713,6 +792,7 @@ __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
     } else {
         flush_scratch<DIM, ACC == ACC_PACKED ? ACC_PACKED : ACC_FLOAT>(a, c, sc);
     }
+    drain_queue<DIM, ORDER>(a, sc);
     if (threadIdx.x == 0 && s_esc && a.n_escaped)
         atomicAdd(a.n_escaped, (unsigned long long)s_esc);
 }
@@ -753,13 +833,23 @@ pcg_status launch_tiled_mode(DepArgs a, const MoveArgs &m, uint32_t nwork, int b
     for (int k = 0; k < DIM; ++k)
         ncell *= (size_t)(a.T + 2 * a.D);
     const size_t packed = packed_bytes(vol, ncell), fixed = vol * 24, flt = vol * 12;
+    // the queue of globally deposited particles follows the scratch, as large
+    // as the LDS left allows (up to QUEUE_MAX entries; none: no queue)
+    auto with_queue = [&](size_t scratch) {
+        const size_t qoff = (scratch + 15) / 16 * 16;
+        const size_t room = LDS_LIMIT > qoff ? (LDS_LIMIT - qoff) / (QUEUE_FLOATS * 4) : 0;
+        a.qoff = (uint32_t)qoff;
+        a.qcap = (uint32_t)std::min<size_t>(QUEUE_MAX, room);
+        return a.qcap ? qoff + (size_t)a.qcap * QUEUE_FLOATS * 4 : scratch;
+    };
     if (packed <= LDS_LIMIT) {
         a.fb64 = fixed <= LDS_LIMIT ? 1 : 0;
-        const size_t lds = std::max(packed, a.fb64 ? fixed : flt);
+        const size_t lds = with_queue(std::max(packed, a.fb64 ? fixed : flt));
         return launch_tiled_impl<DIM, ORDER, ACC_PACKED, TEC, MOVE>(a, m, nwork, block, lds, st);
     }
     a.fb64 = 0;
-    return launch_tiled_impl<DIM, ORDER, ACC_FLOAT, TEC, MOVE>(a, m, nwork, block, flt, st);
+    const size_t lds = with_queue(flt);
+    return launch_tiled_impl<DIM, ORDER, ACC_FLOAT, TEC, MOVE>(a, m, nwork, block, lds, st);
 }
 
 template <int DIM, int ORDER, bool MOVE>

@@ -55,6 +55,8 @@ struct DepArgs {
     int fb64;  // tiled: the packed scratch falls back to 64-bit sums (else fp32)
     uint32_t qoff, qcap;  // tiled: byte offset and capacity of the LDS queue of
                           // particles deposited with global atomics
+    uint32_t moff, mcap;  // fused pass: the same for the queue of particles
+                          // that change tile
 };
 
 // The regrouping half of the fused pass: every particle the deposit loads is
@@ -251,11 +253,19 @@ struct Scratch {
     float *queue;               // [qcap][QUEUE_FLOATS]: raw x[3], q w v[3]
     uint32_t *qn;               // entries claimed (may exceed qcap)
     uint32_t qcap;
+    float *mq;                  // [mcap][MQ_WORDS]: new slot, then the fields
+    uint32_t *mn;
+    uint32_t mcap;
 };
 
 // A queued particle: its raw coordinates and its amplitude q w v_c.
 constexpr int QUEUE_FLOATS = 6;
 constexpr uint32_t QUEUE_MAX = 512;  // entries per work-group (12 KiB)
+// A particle of the fused pass that changes tile: its slot in the new layout
+// and its x[dim], v[3], q, w.
+constexpr int MQ_WORDS = 9;
+constexpr uint32_t MOVE_QUEUE_MAX = 1024;  // entries per work-group (36 KiB)
+constexpr int DIR_STAY = NDIR / 2;         // direction (0, 0, 0): same tile
 
 // One particle: its support, then either the LDS scratch (mode MODE) or, if
 // its stencil leaves the window or its amplitude is outside the admitted
@@ -456,6 +466,22 @@ __device__ __attribute__((always_inline)) inline void drain_queue(const DepArgs 
     }
 }
 
+// The staged particles of the fused pass, one per thread, to their new slots.
+// Call after a barrier that follows the last staging write.
+template <int DIM>
+__device__ __attribute__((always_inline)) inline void drain_moves(const MoveArgs &m,
+                                                                  const Scratch &sc)
+{
+    const uint32_t n = min(*sc.mn, sc.mcap);
+    for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
+        const float *e = sc.mq + (size_t)i * MQ_WORDS;
+        const uint32_t pos = reinterpret_cast<const uint32_t *>(e)[0];
+#pragma unroll
+        for (int k = 0; k < DIM + 5; ++k)
+            m.arr.out[k][pos] = e[1 + k];
+    }
+}
+
 // Bytes of LDS the packed scratch and its fallback need.
 __host__ __device__ constexpr size_t packed_bytes(size_t vol, size_t ncell)
 {
@@ -468,7 +494,7 @@ template <int DIM, int ORDER, int ACC, int TEC, bool MOVE>
 __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    __shared__ uint32_t s_tile, s_lo, s_hi, s_esc, s_maxbits, s_move, s_maxcnt, s_qn;
+    __shared__ uint32_t s_tile, s_lo, s_hi, s_esc, s_maxbits, s_move, s_maxcnt, s_qn, s_mn;
     // MOVE: output slot base per (incremental chunk overlapped, direction), and
     // the end slot of each of those chunks
     __shared__ uint32_t s_base[MOVE ? MOVE_MAX_CHUNKS * NDIR : 1];
@@ -482,6 +508,7 @@ __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
         s_hi = r.hi;
         s_esc = 0;
         s_qn = 0;
+        s_mn = 0;
         s_maxbits = 0;
         s_maxcnt = 0;
         s_move = MOVE && *m.inc.flag == 0u;
@@ -519,6 +546,9 @@ __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
     sc.queue = reinterpret_cast<float *>(smem + a.qoff);
     sc.qn = &s_qn;
     sc.qcap = a.qcap;
+    sc.mq = reinterpret_cast<float *>(smem + a.moff);
+    sc.mn = &s_mn;
+    sc.mcap = MOVE ? a.mcap : 0u;
 
     // MOVE: the incremental chunks of this tile's slice that [lo, hi) overlaps
     const bool move = MOVE && s_move != 0u;
@@ -597,6 +627,9 @@ __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
         c.lo_ok = ldexpf(1.0f, fixed_first ? 8 : h - 16);
     }
     if (fixed_first) {
+        // the 64-bit scratch reaches into the queues' LDS: no queues here
+        sc.qcap = 0;
+        sc.mcap = 0;
         for (int i = threadIdx.x; i < 3 * c.vol; i += blockDim.x)
             sc.acc64[i] = 0ull;
         __syncthreads();
@@ -691,7 +724,28 @@ __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
                     const uint32_t code = gcode[u];
                     const uint32_t d = min(code >> 27, (uint32_t)NDIR - 1);
                     const uint32_t pos = s_base[ci * NDIR + d] + (code & RANK_MASK);
-                    if (pos < (uint64_t)m.inc.count) {
+                    // a particle that changes tile is staged in LDS and written
+                    // with the rest of its chunk's leavers after the pass:
+                    // stored here, its lines would be written back piecemeal
+                    bool staged = false;
+                    if (pos < (uint64_t)m.inc.count && m.canon && d != (uint32_t)DIR_STAY &&
+                        sc.mcap) {
+                        const uint32_t slot = atomicAdd(sc.mn, 1u);
+                        if (slot < sc.mcap) {
+                            float *e = sc.mq + (size_t)slot * MQ_WORDS;
+                            reinterpret_cast<uint32_t *>(e)[0] = pos;
+#pragma unroll
+                            for (int k = 0; k < DIM; ++k)
+                                e[1 + k] = gx[u][k];
+#pragma unroll
+                            for (int k = 0; k < 3; ++k)
+                                e[1 + DIM + k] = gv[u][k];
+                            e[DIM + 4] = gq[u];
+                            e[DIM + 5] = gw[u];
+                            staged = true;
+                        }
+                    }
+                    if (pos < (uint64_t)m.inc.count && !staged) {
                         if (m.canon) {
 #pragma unroll
                             for (int k = 0; k < DIM; ++k)
@@ -722,13 +776,18 @@ __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
         pass(std::integral_constant<int, ACC_FIXED>{}, c, false);
         __syncthreads();
         flush_scratch<DIM, ACC_FIXED>(a, c, sc);
-        drain_queue<DIM, ORDER>(a, sc);
         if (threadIdx.x == 0 && s_esc && a.n_escaped)
             atomicAdd(a.n_escaped, (unsigned long long)s_esc);
         return;
     }
     pass(std::integral_constant<int, ACC>{}, c, false);
     __syncthreads();
+    // the queues lie past the packed scratch, where a 64-bit rerun would
+    // write: drain them now (the barrier of the count check below separates
+    // the drains from any rerun)
+    if (MOVE)
+        drain_moves<DIM>(m, sc);
+    drain_queue<DIM, ORDER>(a, sc);
 
     bool redo = false;
     uint32_t maxcnt = 0;
@@ -792,7 +851,6 @@ __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
     } else {
         flush_scratch<DIM, ACC == ACC_PACKED ? ACC_PACKED : ACC_FLOAT>(a, c, sc);
     }
-    drain_queue<DIM, ORDER>(a, sc);
     if (threadIdx.x == 0 && s_esc && a.n_escaped)
         atomicAdd(a.n_escaped, (unsigned long long)s_esc);
 }
@@ -821,6 +879,21 @@ pcg_status launch_tiled_impl(const DepArgs &a, const MoveArgs &m, uint32_t nwork
                   st, a, m);
 }
 
+// Static LDS of a tiled kernel (its __shared__ variables), so that the dynamic
+// part plus this stays within the CU's LDS.
+template <int DIM, int ORDER, int ACC, int TEC, bool MOVE>
+size_t static_lds()
+{
+    static const size_t bytes = [] {
+        hipFuncAttributes fa{};
+        if (hipFuncGetAttributes(&fa, (const void *)k_deposit_tiled<DIM, ORDER, ACC, TEC, MOVE>) !=
+            hipSuccess)
+            return (size_t)8192;  // above what the kernels declare
+        return (size_t)fa.sharedSizeBytes;
+    }();
+    return bytes;
+}
+
 // The scratch mode and LDS size of a layout: packed 32-bit sums (64-bit
 // fallback when three 64-bit sums per node fit) when the packed scratch fits,
 // else fp32 scratch.
@@ -833,22 +906,32 @@ pcg_status launch_tiled_mode(DepArgs a, const MoveArgs &m, uint32_t nwork, int b
     for (int k = 0; k < DIM; ++k)
         ncell *= (size_t)(a.T + 2 * a.D);
     const size_t packed = packed_bytes(vol, ncell), fixed = vol * 24, flt = vol * 12;
-    // the queue of globally deposited particles follows the scratch, as large
-    // as the LDS left allows (up to QUEUE_MAX entries; none: no queue)
-    auto with_queue = [&](size_t scratch) {
-        const size_t qoff = (scratch + 15) / 16 * 16;
-        const size_t room = LDS_LIMIT > qoff ? (LDS_LIMIT - qoff) / (QUEUE_FLOATS * 4) : 0;
-        a.qoff = (uint32_t)qoff;
-        a.qcap = (uint32_t)std::min<size_t>(QUEUE_MAX, room);
-        return a.qcap ? qoff + (size_t)a.qcap * QUEUE_FLOATS * 4 : scratch;
+    // The queues (globally deposited particles; in the fused pass, particles
+    // that change tile) follow the first pass's scratch, as large as the LDS
+    // left allows (none: no queue).  They may reach into the 64-bit scratch,
+    // which is used only after they are drained, or instead of them.
+    auto with_queues = [&](size_t first, size_t rest, size_t limit) {
+        size_t at = (first + 15) / 16 * 16;
+        auto room = [&](size_t bytes) { return limit > at ? (limit - at) / bytes : 0; };
+        a.qoff = (uint32_t)at;
+        a.qcap = (uint32_t)std::min<size_t>(QUEUE_MAX, room(QUEUE_FLOATS * 4));
+        at += (size_t)a.qcap * QUEUE_FLOATS * 4;
+        a.moff = (uint32_t)at;
+        a.mcap = MOVE ? (uint32_t)std::min<size_t>(MOVE_QUEUE_MAX, room(MQ_WORDS * 4)) : 0u;
+        at += (size_t)a.mcap * MQ_WORDS * 4;
+        return std::max(at, rest);
     };
-    if (packed <= LDS_LIMIT) {
-        a.fb64 = fixed <= LDS_LIMIT ? 1 : 0;
-        const size_t lds = with_queue(std::max(packed, a.fb64 ? fixed : flt));
+    const size_t lim_p = LDS_LIMIT - static_lds<DIM, ORDER, ACC_PACKED, TEC, MOVE>();
+    if (packed <= lim_p) {
+        a.fb64 = fixed <= lim_p ? 1 : 0;
+        const size_t lds = with_queues(packed, a.fb64 ? fixed : flt, lim_p);
         return launch_tiled_impl<DIM, ORDER, ACC_PACKED, TEC, MOVE>(a, m, nwork, block, lds, st);
     }
     a.fb64 = 0;
-    const size_t lds = with_queue(flt);
+    const size_t lim_f = LDS_LIMIT - static_lds<DIM, ORDER, ACC_FLOAT, TEC, MOVE>();
+    if (flt > lim_f)
+        return fail(PCG_ELDS, "deposit_currents: scratch of %zu bytes exceeds the LDS", flt);
+    const size_t lds = with_queues(flt, flt, lim_f);
     return launch_tiled_impl<DIM, ORDER, ACC_FLOAT, TEC, MOVE>(a, m, nwork, block, lds, st);
 }
 

@@ -103,6 +103,21 @@ def test_far_moves_fall_back_to_the_general_sort(orc):
     _check(orc, s, 1, 2, 1, off, _run(s, 1, 2, 1, off))
 
 
+def test_queues_overflow(orc):
+    """Most particles pushed 2-4 cells with tiles of edge 4: a chunk holds more
+    tile-leavers than the work-group stages in LDS (1024) and more escapes than
+    its queue of global deposits (512); the rest are stored and deposited
+    directly."""
+    wl = synthetic.deposit_workload(3, [16, 16, 16], ppc=64, far_fraction=0.9, w_uniform=True,
+                                    seed=536)
+    s, off = _sorted_pushed(orc, wl, 1, 4)
+    n_esc = _check(orc, s, 1, 4, 1, off, _run(s, 1, 4, 1, off))
+    chunks = 64 * 2  # 64 tiles of 4096 particles, chunks of 2048
+    assert n_esc > chunks * 512
+    leavers = int(np.sum(orc.tile_keys(3, s.n, 1, 4, s.x) != orc.tile_keys(3, s.n, 1, 4, s.x_next)))
+    assert leavers > chunks * 1024
+
+
 def test_other_arrays_take_the_generic_store(orc):
     """Arrays other than exactly (x, v, q, w) in order: extra fields, another order."""
     wl = synthetic.deposit_workload(3, [32, 32, 32], ppc=3, far_fraction=0.02, seed=533)

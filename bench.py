@@ -237,10 +237,10 @@ def bench_deposit(args, torch, pcg, name):
         "deposit_tiled": cnt * pbytes + 2 * jbytes,
         # the same, plus every field written once to its new slot
         "deposit_regroup": cnt * 2 * pbytes + 2 * jbytes,
-        # positions read, 4-byte move code written
-        "sort_inc_rank": cnt * (dim * 4 + 4),
-        # move code read, every field read once and written once
-        "sort_inc_move": cnt * (4 + 2 * pbytes),
+        # positions read (per-chunk direction counts are negligible)
+        "sort_inc_count": cnt * dim * 4,
+        # every field read once and written once
+        "sort_inc_move": cnt * 2 * pbytes,
         "sort_keys": cnt * (dim * 4 + 4),
         "sort_permute": cnt * (4 + 2 * pbytes),
         "sort_offsets": cnt * 4 + (nt + 1) * 4,

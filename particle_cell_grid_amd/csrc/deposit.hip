@@ -62,23 +62,18 @@ struct DepArgs {
 // The regrouping half of the fused pass: every particle the deposit loads is
 // also written to its slot in the next tile layout, as the incremental tile
 // sort's move stage would (same slots, so the same result).
-constexpr int MOVE_MAX_CHUNKS = 40;          // incremental chunks one deposit chunk can overlap
 constexpr uint32_t MOVE_DEPOSIT_CHUNK = 32768;  // largest deposit chunk when moving
+constexpr int MAX_WAVES = 8;                    // waves of a tiled work-group (512 threads)
 
 struct MoveArgs {
     IncGeom inc;
     const uint32_t *off;  // the new tile offsets
-    PermArgs arr;
-    int canon;            // arr.in[] are exactly x[0..dim), v[0..3), q, w: store from registers
+    float *out[8];        // new arrays of x[0..dim), v[0..3), q, w
+    uint32_t group;       // incremental chunks per deposit work item
 };
 
-// Incremental chunk (0-based within the tile) holding slot r of a tile slice of
-// L particles split into nch balanced chunks (chunk c starts at floor(L c / nch)).
-__device__ inline uint32_t chunk_of(uint32_t r, uint32_t L, uint32_t nch)
-{
-    return (uint32_t)(((uint64_t)(r + 1) * nch + L - 1) / L) - 1u;
-}
-
+// Start of chunk c of a tile slice of L particles split into nch balanced
+// chunks (the split of the incremental sort).
 __device__ inline uint32_t chunk_start(uint32_t c, uint32_t L, uint32_t nch)
 {
     return (uint32_t)(((uint64_t)L * c) / nch);
@@ -478,8 +473,22 @@ __device__ __attribute__((always_inline)) inline void drain_moves(const MoveArgs
         const uint32_t pos = reinterpret_cast<const uint32_t *>(e)[0];
 #pragma unroll
         for (int k = 0; k < DIM + 5; ++k)
-            m.arr.out[k][pos] = e[1 + k];
+            m.out[k][pos] = e[1 + k];
     }
+}
+
+// One unconditional wait for a group of N particles' values (loaded an
+// iteration ago), placed before any branch: the per-particle branches then need
+// no waits of their own, and counter-based waits placed after stores there
+// would also drain the next group's loads.
+template <int N>
+__device__ __attribute__((always_inline)) inline void wait_values(float (*x)[3], float (*v)[3],
+                                                                  float *q, float *w)
+{
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+        asm volatile("" ::"v"(x[u][0]), "v"(x[u][1]), "v"(x[u][2]), "v"(v[u][0]), "v"(v[u][1]),
+                     "v"(v[u][2]), "v"(q[u]), "v"(w[u]));
 }
 
 // Bytes of LDS the packed scratch and its fallback need.
@@ -497,21 +506,44 @@ __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
     __shared__ uint32_t s_tile, s_lo, s_hi, s_esc, s_maxbits, s_move, s_maxcnt, s_qn, s_mn;
     // MOVE: output slot base per (incremental chunk overlapped, direction), and
     // the end slot of each of those chunks
-    __shared__ uint32_t s_base[MOVE ? MOVE_MAX_CHUNKS * NDIR : 1];
-    __shared__ uint32_t s_cend[MOVE ? MOVE_MAX_CHUNKS : 1];
+    // MOVE: each wave's next free slot per direction in the chunk it walks;
+    // the work item's first incremental chunk (within the tile) and count
+    __shared__ uint32_t s_run[MOVE ? MAX_WAVES : 1][32];
+    __shared__ uint32_t s_c0, s_nsub;
 
     if (threadIdx.x == 0) {
-        const ChunkRange r = find_chunk(blockIdx.x, a.chunk_cum, a.chunk_map, a.ntiles, a.tile_offsets,
-                                        a.n_part);
-        s_tile = r.tile;
-        s_lo = r.lo;
-        s_hi = r.hi;
+        ChunkRange r = find_chunk(blockIdx.x, a.chunk_cum, a.chunk_map, a.ntiles, a.tile_offsets,
+                                  a.n_part);
         s_esc = 0;
         s_qn = 0;
         s_mn = 0;
         s_maxbits = 0;
         s_maxcnt = 0;
         s_move = MOVE && *m.inc.flag == 0u;
+        s_c0 = 0;
+        s_nsub = 0;
+        if (MOVE && s_move && r.tile != UINT_MAX) {
+            // the work item is `group` whole chunks of the incremental sort's
+            // split of the tile (the same number of items per tile), so that
+            // each wave can walk whole chunks in order
+            const uint32_t t = r.tile;
+            const uint32_t item = r.chunk - a.chunk_cum[t];
+            const uint32_t nch = m.inc.cum[t + 1] - m.inc.cum[t];
+            const uint32_t c0 = item * m.group, c1 = min(c0 + m.group, nch);
+            const uint32_t p0 = (uint32_t)min((int64_t)m.inc.prev_off[t], m.inc.count);
+            const uint32_t L = (uint32_t)min((int64_t)m.inc.prev_off[t + 1], m.inc.count) - p0;
+            if (c0 < c1) {
+                r.lo = p0 + chunk_start(c0, L, nch);
+                r.hi = p0 + chunk_start(c1, L, nch);
+                s_c0 = c0;
+                s_nsub = c1 - c0;
+            } else {
+                r.tile = UINT_MAX;
+            }
+        }
+        s_tile = r.tile;
+        s_lo = r.lo;
+        s_hi = r.hi;
     }
     __syncthreads();
     const uint32_t tile = s_tile;
@@ -550,23 +582,7 @@ __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
     sc.mn = &s_mn;
     sc.mcap = MOVE ? a.mcap : 0u;
 
-    // MOVE: the incremental chunks of this tile's slice that [lo, hi) overlaps
     const bool move = MOVE && s_move != 0u;
-    uint32_t p0 = 0, L = 1, nch = 1, c_first = 0;
-    if (move) {
-        p0 = (uint32_t)min((int64_t)m.inc.prev_off[tile], m.inc.count);
-        const uint32_t p1 = (uint32_t)min((int64_t)m.inc.prev_off[tile + 1], m.inc.count);
-        L = p1 - p0;  // >= hi - lo > 0
-        const uint32_t g0 = m.inc.cum[tile];
-        nch = m.inc.cum[tile + 1] - g0;
-        c_first = chunk_of(lo - p0, L, nch);
-        const uint32_t c_last = chunk_of(hi - 1 - p0, L, nch);
-        const uint32_t nc = min(c_last - c_first + 1, (uint32_t)MOVE_MAX_CHUNKS);
-        for (uint32_t i = threadIdx.x; i < nc * NDIR; i += blockDim.x)
-            s_base[i] = move_base(m.inc, m.off, tile, g0 + c_first + i / NDIR, (int)(i % NDIR));
-        for (uint32_t i = threadIdx.x; i < nc; i += blockDim.x)
-            s_cend[i] = p0 + chunk_start(c_first + i + 1, L, nch);
-    }
 
     // zero the scratch; scale from the first batch: largest |q w v_c|
     if (ACC == ACC_PACKED) {
@@ -635,57 +651,46 @@ __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
         __syncthreads();
     }
 
-    // Each thread keeps U particles (stride blockDim.x apart) in flight: the
-    // next group's values (and move codes) load while this group is weighed,
-    // moved and accumulated.
+    // Each thread keeps U particles in flight: the next group's values load
+    // while this group is weighed (and moved) and accumulated.
     constexpr int U = DEPOSIT_UNROLL;
-    const uint32_t stride = blockDim.x;
+    // Loads of particle p (clamped into the slice by the caller): a 32-bit
+    // byte offset from each array's base (counts are below 2^30).
+    auto load_one = [&](uint32_t p, float *x, float *v, float &q, float &w)
+        __attribute__((always_inline)) {
+        const uint32_t off = p * 4u;
+        auto at = [off](const float *base) {
+            return *reinterpret_cast<const float *>(reinterpret_cast<const char *>(base) + off);
+        };
+        x[0] = x[1] = x[2] = 0.f;
+#pragma unroll
+        for (int k = 0; k < DIM; ++k)
+            x[k] = at(a.x[k]);
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            v[k] = at(a.v[k]);
+        q = at(a.q);
+        w = at(a.w);
+    };
+    // The chunk in an order of no consequence to the deposit: thread t takes
+    // particles lo + t, lo + t + blockDim.x, ... (no moves).
     auto pass = [&](auto mode_tag, const TileCtx &cx, bool again) __attribute__((always_inline)) {
         constexpr int MODE = decltype(mode_tag)::value;
+        const uint32_t stride = blockDim.x;
         float nx[U][3], nv[U][3], nq[U], nw[U];
-        uint32_t ncode[U];
-        const bool mv = move && !again;
+        // no branch around the loads: a lane past the slice reloads the
+        // slice's last particle (never used), so the number of loads in flight
+        // is fixed and the wait for one group leaves the next group's loads
+        // outstanding
         auto load_group = [&](uint32_t base) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                // no branch around the loads: a lane past the slice reloads the
-                // slice's last particle (never used), so the number of loads in
-                // flight is fixed and the wait for this group can leave the
-                // next group's loads outstanding.  Counts are below 2^30, so a
-                // 32-bit byte offset from each array's base reaches every
-                // element.
-                const uint32_t p = min(base + u * stride, hi - 1);
-                const uint32_t off = p * 4u;
-                auto at = [off](const float *base) {
-                    return *reinterpret_cast<const float *>(
-                        reinterpret_cast<const char *>(base) + off);
-                };
-                nx[u][0] = nx[u][1] = nx[u][2] = 0.f;
-#pragma unroll
-                for (int k = 0; k < DIM; ++k)
-                    nx[u][k] = at(a.x[k]);
-#pragma unroll
-                for (int k = 0; k < 3; ++k)
-                    nv[u][k] = at(a.v[k]);
-                nq[u] = at(a.q);
-                nw[u] = at(a.w);
-                ncode[u] = 0;
-                if (MOVE)
-                    ncode[u] = *reinterpret_cast<const uint32_t *>(
-                        reinterpret_cast<const char *>(m.inc.code) + off);
-            }
+            for (int u = 0; u < U; ++u)
+                load_one(min(base + u * stride, hi - 1), nx[u], nv[u], nq[u], nw[u]);
         };
-        uint32_t ci = 0, c_end = 0;  // MOVE: this thread's chunk (relative to c_first) and its end
-        if (mv) {
-            const uint32_t p = min(lo + threadIdx.x, hi - 1);
-            ci = min(chunk_of(p - p0, L, nch) - c_first, (uint32_t)MOVE_MAX_CHUNKS - 1);
-            c_end = s_cend[ci];
-        }
         uint32_t esc_count = 0;
         load_group(lo + threadIdx.x);
         for (uint32_t base = lo + threadIdx.x; base < hi; base += U * stride) {
             float gx[U][3], gv[U][3], gq[U], gw[U];
-            uint32_t gcode[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -695,76 +700,14 @@ __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
                 }
                 gq[u] = nq[u];
                 gw[u] = nw[u];
-                gcode[u] = ncode[u];
             }
             load_group(base + U * stride);
-            // One unconditional wait for this group's values (loaded an
-            // iteration ago), before any branch: the per-particle branches
-            // below then need no waits of their own, and the counter-based
-            // waits the compiler would place there after the move stores
-            // would also drain the next group's loads.
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                asm volatile("" ::"v"(gx[u][0]), "v"(gx[u][1]), "v"(gx[u][2]), "v"(gv[u][0]),
-                             "v"(gv[u][1]), "v"(gv[u][2]), "v"(gq[u]), "v"(gw[u]));
-                if (MOVE)
-                    asm volatile("" ::"v"(gcode[u]));
-            }
+            wait_values<U>(gx, gv, gq, gw);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const uint32_t p = base + u * stride;
                 if (p >= hi)
                     break;
-                if (mv) {
-                    // slot in the new layout: the (chunk, direction) base plus the rank
-                    while (p >= c_end && ci + 1 < (uint32_t)MOVE_MAX_CHUNKS) {
-                        ++ci;
-                        c_end = s_cend[ci];
-                    }
-                    const uint32_t code = gcode[u];
-                    const uint32_t d = min(code >> 27, (uint32_t)NDIR - 1);
-                    const uint32_t pos = s_base[ci * NDIR + d] + (code & RANK_MASK);
-                    // a particle that changes tile is staged in LDS and written
-                    // with the rest of its chunk's leavers after the pass:
-                    // stored here, its lines would be written back piecemeal
-                    bool staged = false;
-                    if (pos < (uint64_t)m.inc.count && m.canon && d != (uint32_t)DIR_STAY &&
-                        sc.mcap) {
-                        const uint32_t slot = atomicAdd(sc.mn, 1u);
-                        if (slot < sc.mcap) {
-                            float *e = sc.mq + (size_t)slot * MQ_WORDS;
-                            reinterpret_cast<uint32_t *>(e)[0] = pos;
-#pragma unroll
-                            for (int k = 0; k < DIM; ++k)
-                                e[1 + k] = gx[u][k];
-#pragma unroll
-                            for (int k = 0; k < 3; ++k)
-                                e[1 + DIM + k] = gv[u][k];
-                            e[DIM + 4] = gq[u];
-                            e[DIM + 5] = gw[u];
-                            staged = true;
-                        }
-                    }
-                    if (pos < (uint64_t)m.inc.count && !staged) {
-                        if (m.canon) {
-#pragma unroll
-                            for (int k = 0; k < DIM; ++k)
-                                m.arr.out[k][pos] = gx[u][k];
-#pragma unroll
-                            for (int k = 0; k < 3; ++k)
-                                m.arr.out[DIM + k][pos] = gv[u][k];
-                            m.arr.out[DIM + 3][pos] = gq[u];
-                            m.arr.out[DIM + 4][pos] = gw[u];
-                        } else {
-                            // constant indices: the pointer table stays in the
-                            // kernel arguments
-#pragma unroll
-                            for (int i = 0; i < MAX_ARRAYS; ++i)
-                                if (i < m.arr.n)
-                                    m.arr.out[i][pos] = m.arr.in[i][p];
-                        }
-                    }
-                }
                 esc_count += deposit_one<DIM, ORDER, MODE, TEC>(a, cx, sc, gx[u], gv[u], gq[u],
                                                                 gw[u], again);
             }
@@ -772,15 +715,137 @@ __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
         if (esc_count)
             atomicAdd(&s_esc, esc_count);
     };
+
+    // Particles per lane in flight in the walk (its slot bookkeeping needs
+    // registers the plain pass does not).
+    constexpr int UW = DIM == 3 && ORDER == 2 ? 2 : 3;
+    // MOVE, first pass: the work item's incremental chunks (or, without the
+    // incremental layout, balanced pieces of [lo, hi)) go to the waves in
+    // turn; a wave walks each of its chunks in order, 64 U particles at a
+    // time, so that it can give every particle its slot in the new layout
+    // from its direction and its running count (as the incremental sort's
+    // move does), deposits it, and stores it (or stages it, if it changes
+    // tile).
+    auto walk = [&](auto mode_tag, const TileCtx &cx) __attribute__((always_inline)) {
+        constexpr int MODE = decltype(mode_tag)::value;
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), lane = lane_id();
+        const int nwaves = blockDim.x / WAVE;
+        const uint32_t nsub = move ? s_nsub : (hi - lo + INC_CHUNK - 1) / INC_CHUNK;
+        uint32_t p0 = 0, L = 0, nch = 0, g0 = 0;
+        int tsc[3] = {0, 0, 0};
+        if (move) {
+            p0 = (uint32_t)min((int64_t)m.inc.prev_off[tile], m.inc.count);
+            L = (uint32_t)min((int64_t)m.inc.prev_off[tile + 1], m.inc.count) - p0;
+            g0 = m.inc.cum[tile];
+            nch = m.inc.cum[tile + 1] - g0;
+            tile_coords(tile, m.inc.g, tsc);
+        }
+        uint32_t *run = s_run[MOVE ? wave : 0];
+        uint32_t esc_count = 0;
+        for (uint32_t j = wave; j < nsub; j += nwaves) {
+            uint32_t clo, chi;
+            if (move) {
+                clo = p0 + chunk_start(s_c0 + j, L, nch);
+                chi = p0 + chunk_start(s_c0 + j + 1, L, nch);
+                if (lane < NDIR)
+                    run[lane] = move_base(m.inc, m.off, tile, g0 + s_c0 + j, lane);
+                __builtin_amdgcn_wave_barrier();
+            } else {
+                clo = lo + (uint32_t)((uint64_t)(hi - lo) * j / nsub);
+                chi = lo + (uint32_t)((uint64_t)(hi - lo) * (j + 1) / nsub);
+            }
+            float nx[UW][3], nv[UW][3], nq[UW], nw[UW];
+            auto load_group = [&](uint32_t base) {
+#pragma unroll
+                for (int u = 0; u < UW; ++u)
+                    load_one(min(base + u * WAVE + lane, chi - 1), nx[u], nv[u], nq[u], nw[u]);
+            };
+            load_group(clo);
+            for (uint32_t base = clo; base < chi; base += UW * WAVE) {
+                float gx[UW][3], gv[UW][3], gq[UW], gw[UW];
+#pragma unroll
+                for (int u = 0; u < UW; ++u) {
+#pragma unroll
+                    for (int k = 0; k < 3; ++k) {
+                        gx[u][k] = nx[u][k];
+                        gv[u][k] = nv[u][k];
+                    }
+                    gq[u] = nq[u];
+                    gw[u] = nw[u];
+                }
+                load_group(base + UW * WAVE);
+                wait_values<UW>(gx, gv, gq, gw);
+#pragma unroll
+                for (int u = 0; u < UW; ++u) {
+                    const uint32_t p = base + u * WAVE + lane;
+                    const bool valid = p < chi;
+                    if (move) {
+                        // wave-uniform: the slot comes from the whole wave's
+                        // directions
+                        const int d = particle_dir<DIM, ORDER>(gx[u][0], gx[u][1], gx[u][2],
+                                                               m.inc.g, tsc);
+                        const bool ok = valid && d >= 0;  // d < 0 cannot occur: flag clear
+                        const uint32_t pos = walk_slot(run, d, ok);
+                        if (ok && pos < (uint64_t)m.inc.count) {
+                            // a particle that changes tile is staged in LDS and
+                            // written with the rest of its chunk's leavers after
+                            // the pass: stored here, its lines would be written
+                            // back piecemeal
+                            bool staged = false;
+                            if (d != DIR_STAY && sc.mcap) {
+                                const uint32_t slot = atomicAdd(sc.mn, 1u);
+                                if (slot < sc.mcap) {
+                                    float *e = sc.mq + (size_t)slot * MQ_WORDS;
+                                    reinterpret_cast<uint32_t *>(e)[0] = pos;
+#pragma unroll
+                                    for (int k = 0; k < DIM; ++k)
+                                        e[1 + k] = gx[u][k];
+#pragma unroll
+                                    for (int k = 0; k < 3; ++k)
+                                        e[1 + DIM + k] = gv[u][k];
+                                    e[DIM + 4] = gq[u];
+                                    e[DIM + 5] = gw[u];
+                                    staged = true;
+                                }
+                            }
+                            if (!staged) {
+#pragma unroll
+                                for (int k = 0; k < DIM; ++k)
+                                    m.out[k][pos] = gx[u][k];
+#pragma unroll
+                                for (int k = 0; k < 3; ++k)
+                                    m.out[DIM + k][pos] = gv[u][k];
+                                m.out[DIM + 3][pos] = gq[u];
+                                m.out[DIM + 4][pos] = gw[u];
+                            }
+                        }
+                    }
+                    if (valid)
+                        esc_count += deposit_one<DIM, ORDER, MODE, TEC>(a, cx, sc, gx[u], gv[u],
+                                                                        gq[u], gw[u], false);
+                }
+            }
+        }
+        if (esc_count)
+            atomicAdd(&s_esc, esc_count);
+    };
+    // the first pass of a kernel
+    auto first = [&](auto mode_tag, const TileCtx &cx) __attribute__((always_inline)) {
+        if constexpr (MOVE)
+            walk(mode_tag, cx);
+        else
+            pass(mode_tag, cx, false);
+    };
+
     if (ACC == ACC_PACKED && fixed_first) {
-        pass(std::integral_constant<int, ACC_FIXED>{}, c, false);
+        first(std::integral_constant<int, ACC_FIXED>{}, c);
         __syncthreads();
         flush_scratch<DIM, ACC_FIXED>(a, c, sc);
         if (threadIdx.x == 0 && s_esc && a.n_escaped)
             atomicAdd(a.n_escaped, (unsigned long long)s_esc);
         return;
     }
-    pass(std::integral_constant<int, ACC>{}, c, false);
+    first(std::integral_constant<int, ACC>{}, c);
     __syncthreads();
     // the queues lie past the packed scratch, where a 64-bit rerun would
     // write: drain them now (the barrier of the count check below separates
@@ -1155,6 +1220,17 @@ pcg_status prepare_deposit(const char *who, const pcg_grid *grid, const pcg_part
             chunk = std::min<int64_t>(chunk, std::max<int64_t>(MIN_DEPOSIT_CHUNK, per_cell * tcells));
         }
     }
+    if (max_chunk) {
+        // the fused pass: whole chunks of the incremental sort per work item
+        chunk = std::max<int64_t>(INC_CHUNK, chunk / INC_CHUNK * INC_CHUNK);
+        if (tile->block <= 0) {
+            // one wave per incremental chunk of an average tile's work item
+            const int64_t per_tile = a.n_part / std::max<int64_t>(1, a.ntiles);
+            const int64_t chunks = std::min<int64_t>(chunk / INC_CHUNK,
+                                                     (per_tile + INC_CHUNK - 1) / INC_CHUNK);
+            block = 64 * (int)std::max<int64_t>(1, std::min<int64_t>(MAX_WAVES, chunks));
+        }
+    }
     a.chunk = (uint32_t)chunk;
     const uint64_t nwork = (uint64_t)a.ntiles + ((uint64_t)a.n_part + a.chunk - 1) / a.chunk;
     if (nwork > max_deposit_work(a.ntiles, a.n_part))
@@ -1179,7 +1255,6 @@ pcg_status launch_chunks(const DepArgs &a, hipStream_t st)
 struct RegroupCtx {
     const TiledPlan *plan;
     int dim, order;
-    int canon;
 };
 
 pcg_status regroup_hook(void *ctx, const IncGeom &inc, const uint32_t *off, uint32_t,
@@ -1189,8 +1264,9 @@ pcg_status regroup_hook(void *ctx, const IncGeom &inc, const uint32_t *off, uint
     MoveArgs m{};
     m.inc = inc;
     m.off = off;
-    m.arr = arr;
-    m.canon = c.canon;
+    for (int k = 0; k < arr.n && k < 8; ++k)
+        m.out[k] = arr.out[k];
+    m.group = c.plan->a.chunk / INC_CHUNK;
     PCG_TRY(launch_chunks(c.plan->a, st));
     return dispatch_tiled<true>(c.dim, c.order, c.plan->a, m, c.plan->nwork, c.plan->block,
                                 c.plan->lds, st);
@@ -1264,6 +1340,19 @@ pcg_status deposit_currents_regroup(const pcg_grid *grid, const pcg_particles *p
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int64_t count = particles->count;
     const int dim = grid->dim;
+    // the sort's own checks, before anything is enqueued
+    if (!tile_offsets)
+        return fail(PCG_EINVAL, "%s: tile_offsets is NULL", who);
+    if ((const void *)tile_offsets == (const void *)tile->tile_offsets)
+        return fail(PCG_EINVAL, "%s: tile_offsets must differ from the layout's offsets", who);
+    if (n_arrays < 0 || n_arrays > MAX_ARRAYS)
+        return fail(PCG_EINVAL, "%s: n_arrays = %d not in [0, %d]", who, n_arrays, MAX_ARRAYS);
+    for (int i = 0; i < n_arrays && count > 0; ++i) {
+        if (!in_arrays || !out_arrays || !in_arrays[i] || !out_arrays[i])
+            return fail(PCG_EINVAL, "%s: array %d is NULL", who, i);
+        if ((const void *)in_arrays[i] == (const void *)out_arrays[i])
+            return fail(PCG_EINVAL, "%s: array %d is moved in place (out == in)", who, i);
+    }
     if (tile->n_partitioned != count) {
         // a tail: the layout does not cover every particle, so there is no
         // incremental regroup to fuse with -- deposit, then sort
@@ -1273,16 +1362,22 @@ pcg_status deposit_currents_regroup(const pcg_grid *grid, const pcg_particles *p
                               out_arrays, nullptr, nullptr, tile_offsets, tile, sort_ws,
                               workspace_bytes - dbytes, st, nullptr, nullptr);
     }
-    RegroupCtx ctx{&plan, dim, order, 0};
-    if (in_arrays && n_arrays == dim + 5) {
-        bool canon = true;
-        for (int k = 0; k < dim; ++k)
-            canon = canon && in_arrays[k] == particles->x[k];
-        for (int c = 0; c < 3; ++c)
-            canon = canon && in_arrays[dim + c] == particles->v[c];
-        canon = canon && in_arrays[dim + 3] == particles->q && in_arrays[dim + 4] == particles->w;
-        ctx.canon = canon ? 1 : 0;
+    bool canon = in_arrays && n_arrays == dim + 5;
+    for (int k = 0; canon && k < dim; ++k)
+        canon = in_arrays[k] == particles->x[k];
+    for (int c = 0; canon && c < 3; ++c)
+        canon = in_arrays[dim + c] == particles->v[c];
+    canon = canon && in_arrays[dim + 3] == particles->q && in_arrays[dim + 4] == particles->w;
+    if (!canon) {
+        // other arrays than exactly (x, v, q, w): the deposit, then the
+        // incremental sort's own move of every array
+        PCG_TRY(deposit_currents(grid, particles, order, tile, J, n_escaped, workspace, dbytes,
+                                 stream));
+        return tile_sort_impl(grid, order, tile->T, count, particles->x, n_arrays, in_arrays,
+                              out_arrays, nullptr, nullptr, tile_offsets, tile, sort_ws,
+                              workspace_bytes - dbytes, st, nullptr, nullptr);
     }
+    RegroupCtx ctx{&plan, dim, order};
     const MoveHook hook{regroup_hook, &ctx};
     bool taken = false;
     PCG_TRY(tile_sort_impl(grid, order, tile->T, count, particles->x, n_arrays, in_arrays,

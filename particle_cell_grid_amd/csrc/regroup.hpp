@@ -58,11 +58,8 @@ struct IncGeom {
     uint32_t *cnt;        // [nchunks][NDIR] particles per direction; then prefix over chunks
     uint32_t *tcnt;       // [ntiles][NDIR] per source tile
     uint32_t *tpre;       // [ntiles][NDIR] prefix over a new tile's sources
-    uint32_t *code;       // [count] direction << 27 | rank among the chunk's same-direction ones
     uint32_t *flag;       // non-zero: the general path takes over
 };
-
-constexpr uint32_t RANK_MASK = (1u << 27) - 1;
 
 __device__ inline void tile_coords(uint32_t t, const KeyGeom &g, int *c)
 {
@@ -84,6 +81,74 @@ __device__ inline uint32_t dest_tile(const int *sc, int dir, const KeyGeom &g)
     c[1] = wrap_index(sc[1] + (dir / 3) % 3 - 1, g.nt[1]);
     c[2] = wrap_index(sc[2] + dir / 9 - 1, g.nt[2]);
     return tile_index(c, g);
+}
+
+// Lanes of this wave whose `bits`-bit digit equals mine (among valid lanes).
+template <int BITS>
+__device__ inline uint64_t peer_mask(uint32_t digit, bool valid)
+{
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < BITS; ++b) {
+        const bool bit = (digit >> b) & 1u;
+        const uint64_t m = __ballot(bit);
+        peers &= bit ? m : ~m;
+    }
+    return peers;
+}
+
+// Direction index of the new tile coordinate t relative to source s on one
+// axis of nt tiles: 0, 1, 2 for -1, 0, +1; -1 if further.  On an axis of two
+// tiles only 0 and +1 are distinct, on an axis of one tile only 0.
+__device__ inline int axis_dir(int t, int s, int nt)
+{
+    int d = t - s;
+    if (d < 0)
+        d += nt;
+    if (d == 0)
+        return 1;
+    if (d == 1)
+        return 2;
+    if (d == nt - 1)
+        return 0;
+    return -1;
+}
+
+template <int DIM, int ORDER>
+__device__ inline int particle_dir(float x0, float x1, float x2, const KeyGeom &g, const int *sc)
+{
+    const float xs[3] = {x0, x1, x2};
+    int dir = 0, mul = 1;
+    bool far = false;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        int d = 1;  // unused axes: direction 0
+        if (k < DIM) {
+            d = axis_dir(tile_coord<ORDER>(xs[k], g, k), sc[k], g.nt[k]);
+            far |= d < 0;
+        }
+        dir += mul * (d < 0 ? 0 : d);
+        mul *= 3;
+    }
+    return far ? -1 : dir;
+}
+
+// One 64-particle step of a wave's in-order walk through a chunk: the new
+// slot of each lane's particle (lanes with ok set; dir in [0, NDIR)), from the
+// wave's next free slot per direction run[] in LDS, advanced past this step.
+// Particles keep their order within each direction, so the slots are those of
+// a stable counting sort.  Wave-uniform control flow only.
+__device__ inline uint32_t walk_slot(uint32_t *run, int dir, bool ok)
+{
+    const uint32_t d = ok ? (uint32_t)dir : 0u;
+    const uint64_t peers = peer_mask<5>(d, ok);
+    const uint32_t rank = (uint32_t)__popcll(peers & lanemask_lt());
+    const uint32_t before = run[d];
+    __builtin_amdgcn_wave_barrier();
+    if (ok && rank == 0)
+        run[d] = before + (uint32_t)__popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+    return before + rank;
 }
 
 // Output slot base of every direction of incremental chunk `chunk` (global

@@ -69,20 +69,6 @@ __global__ __launch_bounds__(256) void k_tile_keys(int64_t count, const float *_
 
 // ----------------------------------------------------------------- radix
 
-// Lanes of this wave whose `bits`-bit digit equals mine (among valid lanes).
-template <int BITS>
-__device__ inline uint64_t peer_mask(uint32_t digit, bool valid)
-{
-    uint64_t peers = __ballot(valid);
-#pragma unroll
-    for (int b = 0; b < BITS; ++b) {
-        const bool bit = (digit >> b) & 1u;
-        const uint64_t m = __ballot(bit);
-        peers &= bit ? m : ~m;
-    }
-    return peers;
-}
-
 template <int BITS>
 __global__ __launch_bounds__(SORT_BLOCK) void k_radix_hist(const uint32_t *__restrict__ keys,
                                                            int64_t count, int shift,
@@ -368,53 +354,17 @@ __global__ __launch_bounds__(256) void k_inc_validate(const uint32_t *__restrict
         atomicOr(flag, 1u);
 }
 
-// Direction index of the new tile coordinate t relative to source s on one
-// axis of nt tiles: 0, 1, 2 for -1, 0, +1; -1 if further.  On an axis of two
-// tiles only 0 and +1 are distinct, on an axis of one tile only 0.
-__device__ inline int axis_dir(int t, int s, int nt)
-{
-    int d = t - s;
-    if (d < 0)
-        d += nt;
-    if (d == 0)
-        return 1;
-    if (d == 1)
-        return 2;
-    if (d == nt - 1)
-        return 0;
-    return -1;
-}
-
+// One wave per chunk: every particle's direction (the new tile relative to
+// the source tile), the chunk's per-direction counts, and the device flag if a
+// particle moved further than one tile.
 template <int DIM, int ORDER>
-__device__ inline int particle_dir(float x0, float x1, float x2, const KeyGeom &g, const int *sc)
-{
-    const float xs[3] = {x0, x1, x2};
-    int dir = 0, mul = 1;
-    bool far = false;
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-        int d = 1;  // unused axes: direction 0
-        if (k < DIM) {
-            d = axis_dir(tile_coord<ORDER>(xs[k], g, k), sc[k], g.nt[k]);
-            far |= d < 0;
-        }
-        dir += mul * (d < 0 ? 0 : d);
-        mul *= 3;
-    }
-    return far ? -1 : dir;
-}
-
-// One wave per chunk, walking it in order 64 particles at a time: every
-// particle gets its direction and its rank among the chunk's particles of that
-// direction (stable), and the chunk's per-direction totals are written.
-template <int DIM, int ORDER>
-__global__ __launch_bounds__(64) void k_inc_rank(IncGeom a, const float *x0, const float *x1,
-                                                 const float *x2)
+__global__ __launch_bounds__(64) void k_inc_count(IncGeom a, const float *x0, const float *x1,
+                                                  const float *x2)
 {
     if (*a.flag != 0u)
         return;
     __shared__ uint32_t s_tile, s_lo, s_hi;
-    __shared__ uint32_t s_run[32];
+    __shared__ uint32_t s_cnt[32];
     if (threadIdx.x == 0) {
         const ChunkRange r = find_chunk(blockIdx.x, a.cum, a.map, a.ntiles, a.prev_off, a.count);
         s_tile = r.tile;
@@ -422,7 +372,7 @@ __global__ __launch_bounds__(64) void k_inc_rank(IncGeom a, const float *x0, con
         s_hi = r.hi;
     }
     if (threadIdx.x < 32)
-        s_run[threadIdx.x] = 0;
+        s_cnt[threadIdx.x] = 0;
     __syncthreads();
     if (s_tile == UINT_MAX)
         return;
@@ -430,40 +380,30 @@ __global__ __launch_bounds__(64) void k_inc_rank(IncGeom a, const float *x0, con
     tile_coords(s_tile, a.g, sc);
     const uint32_t lo = s_lo, hi = s_hi;
     bool far = false;
-    // software pipeline: the next batch's coordinates load while this one ranks
-    uint32_t p = lo + threadIdx.x;
-    float c0 = 0.f, c1 = 0.f, c2 = 0.f;
-    if (p < hi) {
-        c0 = x0[p];
-        c1 = DIM > 1 ? x1[p] : 0.f;
-        c2 = DIM > 2 ? x2[p] : 0.f;
-    }
+    // software pipeline: the next batch's coordinates load while this one is
+    // classified (clamped loads: no branch around them)
+    auto load = [&](uint32_t p, float &c0, float &c1, float &c2) {
+        const uint32_t q = min(p, hi - 1);
+        c0 = x0[q];
+        c1 = DIM > 1 ? x1[q] : 0.f;
+        c2 = DIM > 2 ? x2[q] : 0.f;
+    };
+    float c0, c1, c2;
+    load(lo + threadIdx.x, c0, c1, c2);
     for (uint32_t b = lo; b < hi; b += 64) {
+        const uint32_t p = b + threadIdx.x;
         const bool valid = p < hi;
-        const uint32_t pn = p + 64;
-        float n0 = 0.f, n1 = 0.f, n2 = 0.f;
-        if (pn < hi) {
-            n0 = x0[pn];
-            n1 = DIM > 1 ? x1[pn] : 0.f;
-            n2 = DIM > 2 ? x2[pn] : 0.f;
-        }
-        int dir = valid ? particle_dir<DIM, ORDER>(c0, c1, c2, a.g, sc) : 0;
+        float n0, n1, n2;
+        load(p + 64, n0, n1, n2);
+        int dir = particle_dir<DIM, ORDER>(c0, c1, c2, a.g, sc);
         far |= valid && dir < 0;
         const bool ok = valid && dir >= 0;
         if (!ok)
             dir = 0;
         const uint64_t peers = peer_mask<5>((uint32_t)dir, ok);
-        const uint32_t rank = (uint32_t)__popcll(peers & lanemask_lt());
-        // all lanes read the running counts, then each group's first lane
-        // advances its direction's count (a single wave: LDS runs in order)
-        const uint32_t before = s_run[dir];
-        __builtin_amdgcn_wave_barrier();
-        if (ok && rank == 0)
-            s_run[dir] = before + (uint32_t)__popcll(peers);
-        __builtin_amdgcn_wave_barrier();
-        if (ok)
-            a.code[p] = ((uint32_t)dir << 27) | (before + rank);
-        p = pn;
+        // one lane per direction present adds the direction's count
+        if (ok && (peers & lanemask_lt()) == 0)
+            s_cnt[dir] += (uint32_t)__popcll(peers);
         c0 = n0;
         c1 = n1;
         c2 = n2;
@@ -473,7 +413,7 @@ __global__ __launch_bounds__(64) void k_inc_rank(IncGeom a, const float *x0, con
             atomicOr(a.flag, 1u);
     __syncthreads();
     if (threadIdx.x < NDIR)
-        a.cnt[(size_t)blockIdx.x * NDIR + threadIdx.x] = s_run[threadIdx.x];
+        a.cnt[(size_t)blockIdx.x * NDIR + threadIdx.x] = s_cnt[threadIdx.x];
 }
 
 // Thread per (source tile, direction): exclusive prefix of the counts over the
@@ -567,50 +507,58 @@ __global__ __launch_bounds__(256) void k_inc_tiles(IncGeom a, uint32_t *__restri
     totals[t] = run;
 }
 
-// One work-group per chunk, no ordering left: each particle's slot is
-// off[new tile] + tile prefix + chunk prefix + rank.
-template <int DIM>
-__global__ __launch_bounds__(256) void k_inc_move(IncGeom a, const uint32_t *__restrict__ off,
-                                                  PermArgs arr, uint32_t *__restrict__ perm,
-                                                  uint32_t *__restrict__ keys)
+// One wave per chunk (four per work-group), walking it in order 64 particles
+// at a time: each particle's direction again from its position, its slot from
+// the wave's running slot per direction (stable), then every array moved.
+constexpr int MOVE_WAVES = 4;
+
+template <int DIM, int ORDER>
+__global__ __launch_bounds__(MOVE_WAVES * WAVE) void k_inc_move(
+    IncGeom a, const uint32_t *off, const float *x0, const float *x1, const float *x2,
+    PermArgs arr, uint32_t *perm, uint32_t *keys, uint32_t nwork)
 {
     if (*a.flag != 0u)
         return;
-    __shared__ uint32_t s_tile, s_lo, s_hi;
-    __shared__ uint32_t s_base[NDIR], s_dest[NDIR];
-    if (threadIdx.x == 0) {
-        const ChunkRange r = find_chunk(blockIdx.x, a.cum, a.map, a.ntiles, a.prev_off, a.count);
-        s_tile = r.tile;
-        s_lo = r.lo;
-        s_hi = r.hi;
-    }
-    __syncthreads();
-    if (s_tile == UINT_MAX)
+    __shared__ uint32_t s_run[MOVE_WAVES][32];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), lane = lane_id();
+    const uint32_t item = blockIdx.x * MOVE_WAVES + wave;
+    if (item >= nwork)
         return;
-    if (threadIdx.x < NDIR) {
-        const int d = threadIdx.x;
-        int sc[3];
-        tile_coords(s_tile, a.g, sc);
-        const uint32_t t = dest_tile(sc, d, a.g);
-        const size_t j = (size_t)s_tile * NDIR + d;
-        s_dest[d] = t;
-        s_base[d] = off[t] + a.tpre[j] + a.cnt[(size_t)blockIdx.x * NDIR + d];
-    }
-    __syncthreads();
+    const ChunkRange r = find_chunk(item, a.cum, a.map, a.ntiles, a.prev_off, a.count);
+    if (r.tile == UINT_MAX)
+        return;
+    int sc[3];
+    tile_coords(r.tile, a.g, sc);
+    uint32_t *run = s_run[wave];
+    if (lane < NDIR)
+        run[lane] = move_base(a, off, r.tile, r.chunk, lane);
+    __builtin_amdgcn_wave_barrier();
     constexpr int EPT = 4;
-    for (uint32_t b = s_lo; b < s_hi; b += 256 * EPT) {
-        uint32_t pos[EPT], p[EPT];
+    for (uint32_t b = r.lo; b < r.hi; b += WAVE * EPT) {
+        uint32_t p[EPT], pc[EPT], pos[EPT];
+        int dir[EPT];
         bool ok[EPT];
+        float c[EPT][3];
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
-            p[e] = b + e * 256 + threadIdx.x;
-            ok[e] = p[e] < s_hi;
-            const uint32_t c = ok[e] ? a.code[p[e]] : 0u;
-            const uint32_t d = c >> 27;
-            pos[e] = s_base[d < NDIR ? d : 0] + (c & RANK_MASK);
-            ok[e] = ok[e] && d < NDIR && pos[e] < (uint64_t)a.count;
-            if (ok[e] && keys)
-                keys[pos[e]] = s_dest[d];
+            p[e] = b + e * WAVE + lane;
+            pc[e] = min(p[e], r.hi - 1);  // clamped: loads without a branch
+            c[e][0] = x0[pc[e]];
+            c[e][1] = DIM > 1 ? x1[pc[e]] : 0.f;
+            c[e][2] = DIM > 2 ? x2[pc[e]] : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            dir[e] = particle_dir<DIM, ORDER>(c[e][0], c[e][1], c[e][2], a.g, sc);
+            ok[e] = p[e] < r.hi && dir[e] >= 0;  // dir < 0 cannot occur: the flag is clear
+            pos[e] = walk_slot(run, dir[e], ok[e]);
+            ok[e] = ok[e] && pos[e] < (uint64_t)a.count;
+        }
+        if (keys) {
+#pragma unroll
+            for (int e = 0; e < EPT; ++e)
+                if (ok[e])
+                    keys[pos[e]] = dest_tile(sc, dir[e], a.g);
         }
         if (perm) {
 #pragma unroll
@@ -622,7 +570,7 @@ __global__ __launch_bounds__(256) void k_inc_move(IncGeom a, const uint32_t *__r
             float v[EPT];
 #pragma unroll
             for (int e = 0; e < EPT; ++e)
-                v[e] = ok[e] ? arr.in[k][p[e]] : 0.f;
+                v[e] = arr.in[k][pc[e]];
 #pragma unroll
             for (int e = 0; e < EPT; ++e)
                 if (ok[e])
@@ -796,7 +744,7 @@ pcg_status incremental_launch(const IncGeom &a, const float *const key_x[3], uin
                               hipStream_t st)
 {
     const float *x1 = DIM > 1 ? key_x[1] : nullptr, *x2 = DIM > 2 ? key_x[2] : nullptr;
-    PCG_TRY(launch("sort_inc_rank", k_inc_rank<DIM, ORDER>, dim3(nwork), dim3(64), 0, st, a,
+    PCG_TRY(launch("sort_inc_count", k_inc_count<DIM, ORDER>, dim3(nwork), dim3(64), 0, st, a,
                    key_x[0], x1, x2));
     PCG_TRY(launch("sort_inc_chunk_prefix", k_inc_chunk_prefix,
                    dim3((a.ntiles * NDIR + 255) / 256), dim3(256), 0, st, a));
@@ -805,8 +753,9 @@ pcg_status incremental_launch(const IncGeom &a, const float *const key_x[3], uin
     PCG_TRY(exclusive_scan(tile_offsets, (size_t)a.ntiles + 1, b.partial, Gate{b.flag, 0u}, st));
     if (hook)
         return hook->launch(hook->ctx, a, tile_offsets, nwork, arr, st);
-    PCG_TRY(launch("sort_inc_move", k_inc_move<DIM>, dim3(nwork), dim3(256), 0, st, a,
-                   (const uint32_t *)tile_offsets, arr, perm, keys));
+    PCG_TRY(launch("sort_inc_move", k_inc_move<DIM, ORDER>,
+                   dim3((nwork + MOVE_WAVES - 1) / MOVE_WAVES), dim3(MOVE_WAVES * WAVE), 0, st, a,
+                   (const uint32_t *)tile_offsets, key_x[0], x1, x2, arr, perm, keys, nwork));
     return PCG_OK;
 }
 
@@ -910,7 +859,6 @@ pcg_status tile_sort_impl(const pcg_grid *grid, int32_t order, int32_t T, int64_
         a.cnt = b.cnt;
         a.tcnt = b.tcnt;
         a.tpre = b.tpre;
-        a.code = b.k0;  // the general path reuses it only if this path gave up
         a.flag = b.flag;
         const uint32_t chunk = INC_CHUNK;
         const uint32_t nwork = p.nchunks_max;  // >= ntiles + ceil(count / chunk)

@@ -62,7 +62,7 @@ def tap_name(kernel):
     if base == "k_mass_column":
         return "mass_mfma" if last == "true" else "mass_valu"
     table = {"k_deposit_flat": "deposit_flat",
-             "k_inc_move": "sort_inc_move", "k_inc_rank": "sort_inc_rank",
+             "k_inc_move": "sort_inc_move", "k_inc_count": "sort_inc_count",
              "k_inc_tiles": "sort_inc_tiles", "k_mass_flat": "mass_flat",
              "k_mass_strays": "mass_strays",
              "k_permute": "sort_permute", "k_tile_keys": "sort_keys",

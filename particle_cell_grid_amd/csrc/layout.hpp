@@ -115,15 +115,81 @@ __global__ __launch_bounds__(CHUNK_SCAN_BLOCK) void k_chunk_scan3(
         map[c0 + j] = t;
 }
 
-// Enqueues the three passes: cum[0..ntiles] and map[0..min(cum[ntiles],
-// map_len)).  part
-// needs ceil(ntiles / CHUNK_SCAN_BLOCK) entries.  With a gate, the kernels
-// return at once unless *gate == gate_run.
+// Tiles up to which one work-group computes the whole layout in one launch.
+constexpr uint32_t CHUNK_ONE_BLOCK_MAX = 16384;
+constexpr int CHUNK_TPT = 4;  // tiles per thread per round of the one-launch layout
+
+// The whole layout in one work-group (ntiles <= CHUNK_ONE_BLOCK_MAX), and,
+// if `flag` is given, whether off is a partition of [0, n_part): *flag = 0 if
+// off[0] = 0, off is non-decreasing and off[ntiles] = n_part, else 1.
+__global__ __launch_bounds__(CHUNK_SCAN_BLOCK) void k_chunk_layout_one(
+    const uint32_t *__restrict__ off, uint32_t ntiles, int64_t n_part, uint32_t chunk,
+    uint32_t *__restrict__ cum, uint32_t *__restrict__ map, uint32_t map_len, const uint32_t *gate,
+    uint32_t gate_run, uint32_t *flag)
+{
+    if (gate && *gate != gate_run)
+        return;
+    __shared__ uint32_t s_carry, s_bad;
+    if (threadIdx.x == 0) {
+        s_carry = 0;
+        s_bad = 0;
+    }
+    __syncthreads();
+    for (uint32_t base = 0; base < ntiles; base += CHUNK_SCAN_BLOCK * CHUNK_TPT) {
+        const uint32_t t0 = base + threadIdx.x * CHUNK_TPT;
+        uint32_t items[CHUNK_TPT], sum = 0;
+        bool bad = false;
+#pragma unroll
+        for (int j = 0; j < CHUNK_TPT; ++j) {
+            const uint32_t t = t0 + j;
+            items[j] = t < ntiles ? tile_items(off, t, n_part, chunk) : 0u;
+            sum += items[j];
+            if (flag && t < ntiles)
+                bad = bad || (t == 0 ? off[0] != 0u : off[t] < off[t - 1]);
+        }
+        if (bad)
+            atomicOr(&s_bad, 1u);
+        uint32_t total;
+        const uint32_t ex = block_exclusive_1024(sum, &total);
+        uint32_t c = s_carry + ex;
+#pragma unroll
+        for (int j = 0; j < CHUNK_TPT; ++j) {
+            const uint32_t t = t0 + j;
+            if (t < ntiles) {
+                cum[t] = c;
+                for (uint32_t k = 0; k < items[j] && (uint64_t)c + k < map_len; ++k)
+                    map[c + k] = t;
+                c += items[j];
+            }
+        }
+        __syncthreads();  // s_carry read and wsum reused below
+        if (threadIdx.x == 0)
+            s_carry += total;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        cum[ntiles] = s_carry;
+        if (flag) {
+            bool bad = s_bad != 0u || (int64_t)off[ntiles] != n_part;
+            bad = bad || (ntiles == 0 ? off[0] != 0u : off[ntiles] < off[ntiles - 1]);
+            *flag = bad ? 1u : 0u;
+        }
+    }
+}
+
+// Enqueues the layout: cum[0..ntiles] and map[0..min(cum[ntiles], map_len)),
+// in one launch for up to CHUNK_ONE_BLOCK_MAX tiles, else in three passes
+// (part needs ceil(ntiles / CHUNK_SCAN_BLOCK) entries).  With a gate, the
+// kernels return at once unless *gate == gate_run.
 inline pcg_status launch_chunk_layout(const char *name, const uint32_t *off, uint32_t ntiles,
                                       int64_t n_part, uint32_t chunk, uint32_t *cum,
                                       uint32_t *part, uint32_t *map, uint32_t map_len,
                                       const uint32_t *gate, uint32_t gate_run, hipStream_t st)
 {
+    if (ntiles <= CHUNK_ONE_BLOCK_MAX)
+        return launch(name, k_chunk_layout_one, dim3(1), dim3(CHUNK_SCAN_BLOCK), 0, st, off,
+                      ntiles, n_part, chunk, cum, map, map_len, gate, gate_run,
+                      (uint32_t *)nullptr);
     const uint32_t nb = (ntiles + CHUNK_SCAN_BLOCK - 1) / CHUNK_SCAN_BLOCK;
     PCG_TRY(launch(name, k_chunk_scan1, dim3(nb), dim3(CHUNK_SCAN_BLOCK), 0, st, off, ntiles,
                    n_part, chunk, cum, part, gate, gate_run));

@@ -264,9 +264,48 @@ __global__ __launch_bounds__(SCAN_BLOCK) void k_scan_down(uint32_t *__restrict__
     }
 }
 
+// The whole scan in one work-group, for short arrays: rounds of SCAN_ONE_IPT
+// consecutive elements per thread, carried from round to round.
+constexpr int SCAN_ONE_IPT = 16;
+constexpr size_t SCAN_ONE_MAX = 65536;
+
+__global__ __launch_bounds__(1024) void k_scan_one(uint32_t *__restrict__ data, size_t len,
+                                                   Gate gate)
+{
+    if (gated_off(gate))
+        return;
+    __shared__ uint32_t s_carry;
+    if (threadIdx.x == 0)
+        s_carry = 0;
+    __syncthreads();
+    for (size_t base = 0; base < len; base += (size_t)1024 * SCAN_ONE_IPT) {
+        const size_t i0 = base + (size_t)threadIdx.x * SCAN_ONE_IPT;
+        uint32_t v[SCAN_ONE_IPT], s = 0;
+#pragma unroll
+        for (int j = 0; j < SCAN_ONE_IPT; ++j) {
+            v[j] = i0 + j < len ? data[i0 + j] : 0u;
+            s += v[j];
+        }
+        uint32_t total;
+        uint32_t run = s_carry + block_exclusive_scan<1024>(s, &total);
+#pragma unroll
+        for (int j = 0; j < SCAN_ONE_IPT; ++j) {
+            if (i0 + j < len)
+                data[i0 + j] = run;
+            run += v[j];
+        }
+        __syncthreads();  // every thread has read s_carry
+        if (threadIdx.x == 0)
+            s_carry += total;
+        __syncthreads();
+    }
+}
+
 pcg_status exclusive_scan(uint32_t *data, size_t len, uint32_t *partial, Gate gate,
                           hipStream_t st)
 {
+    if (len <= SCAN_ONE_MAX)
+        return launch("sort_scan", k_scan_one, dim3(1), dim3(1024), 0, st, data, len, gate);
     const uint32_t nparts = (uint32_t)((len + SCAN_TILE - 1) / SCAN_TILE);
     PCG_TRY(launch("sort_scan_reduce", k_scan_reduce, dim3(nparts), dim3(SCAN_BLOCK), 0, st,
                    (const uint32_t *)data, len, partial, gate));
@@ -862,12 +901,21 @@ pcg_status tile_sort_impl(const pcg_grid *grid, int32_t order, int32_t T, int64_
         a.flag = b.flag;
         const uint32_t chunk = INC_CHUNK;
         const uint32_t nwork = p.nchunks_max;  // >= ntiles + ceil(count / chunk)
-        PCG_TRY(launch("sort_inc_flag", k_set_flag, dim3(1), dim3(64), 0, st, b.flag, 0u));
-        PCG_TRY(launch("sort_inc_validate", k_inc_validate, dim3((p.ntiles + 1 + 255) / 256),
-                       dim3(256), 0, st, prev->tile_offsets, p.ntiles, count, b.flag));
-        PCG_TRY(launch_chunk_layout("sort_inc_chunks", prev->tile_offsets, p.ntiles, count, chunk,
-                                    b.cum, b.cpart, b.cmap, p.nchunks_max,
-                                    (const uint32_t *)b.flag, 0u, st));
+        if (p.ntiles <= CHUNK_ONE_BLOCK_MAX) {
+            // one launch: the chunk layout, and the flag set from the check
+            // that prev is a partition
+            PCG_TRY(launch("sort_inc_chunks", k_chunk_layout_one, dim3(1), dim3(CHUNK_SCAN_BLOCK),
+                           0, st, prev->tile_offsets, p.ntiles, count, chunk, b.cum, b.cmap,
+                           p.nchunks_max, (const uint32_t *)nullptr, 0u, b.flag));
+        } else {
+            PCG_TRY(launch("sort_inc_flag", k_set_flag, dim3(1), dim3(64), 0, st, b.flag, 0u));
+            PCG_TRY(launch("sort_inc_validate", k_inc_validate,
+                           dim3((p.ntiles + 1 + 255) / 256), dim3(256), 0, st,
+                           prev->tile_offsets, p.ntiles, count, b.flag));
+            PCG_TRY(launch_chunk_layout("sort_inc_chunks", prev->tile_offsets, p.ntiles, count,
+                                        chunk, b.cum, b.cpart, b.cmap, p.nchunks_max,
+                                        (const uint32_t *)b.flag, 0u, st));
+        }
         const int key = grid->dim * 10 + order;
         pcg_status s = PCG_OK;
         switch (key) {

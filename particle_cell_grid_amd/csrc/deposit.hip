@@ -260,7 +260,6 @@ constexpr uint32_t QUEUE_MAX = 512;  // entries per work-group (12 KiB)
 // and its x[dim], v[3], q, w.
 constexpr int MQ_WORDS = 9;
 constexpr uint32_t MOVE_QUEUE_MAX = 1024;  // entries per work-group (36 KiB)
-constexpr int DIR_STAY = NDIR / 2;         // direction (0, 0, 0): same tile
 
 // One particle: its support, then either the LDS scratch (mode MODE) or, if
 // its stencil leaves the window or its amplitude is outside the admitted

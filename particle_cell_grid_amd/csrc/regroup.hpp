@@ -11,6 +11,7 @@ namespace pcg {
 constexpr int MAX_ARRAYS = 16;        // SoA arrays a sort carries along
 constexpr int NDIR = 27;              // neighbour directions of the incremental path
 constexpr uint32_t INC_CHUNK = 2048;  // particles per chunk of the incremental path
+constexpr int DIR_STAY = NDIR / 2;    // direction (0, 0, 0): the same tile
 
 // A kernel runs only if `flag` is NULL or *flag == run.
 struct Gate {
@@ -37,7 +38,10 @@ __device__ inline int tile_coord(float xraw, const KeyGeom &g, int k)
     int b = (int)fl;
     if (ORDER == 2 && (xf - fl) < 0.5f)
         b -= 1;
-    b = wrap_index(b, g.n[k]);
+    // b is in [-1, n] (the coordinate is clamped into [0, n]): two selects wrap it
+    const int n = g.n[k];
+    b += b < 0 ? n : 0;
+    b -= b >= n ? n : 0;
     return g.T_shift >= 0 ? (b >> g.T_shift) : (b / g.T);
 }
 
@@ -102,16 +106,12 @@ __device__ inline uint64_t peer_mask(uint32_t digit, bool valid)
 // tiles only 0 and +1 are distinct, on an axis of one tile only 0.
 __device__ inline int axis_dir(int t, int s, int nt)
 {
-    int d = t - s;
-    if (d < 0)
-        d += nt;
-    if (d == 0)
-        return 1;
-    if (d == 1)
-        return 2;
-    if (d == nt - 1)
-        return 0;
-    return -1;
+    int d = t - s;  // in (-nt, nt)
+    d += d < 0 ? nt : 0;
+    // selects, not branches: 0 wins over 1 and 1 over nt - 1 (nt <= 2)
+    int r = d == nt - 1 ? 0 : -1;
+    r = d == 1 ? 2 : r;
+    return d == 0 ? 1 : r;
 }
 
 template <int DIM, int ORDER>

@@ -393,12 +393,17 @@ __global__ __launch_bounds__(256) void k_inc_validate(const uint32_t *__restrict
         atomicOr(flag, 1u);
 }
 
-// One wave per chunk: every particle's direction (the new tile relative to
-// the source tile), the chunk's per-direction counts, and the device flag if a
-// particle moved further than one tile.
-template <int DIM, int ORDER>
-__global__ __launch_bounds__(64) void k_inc_count(IncGeom a, const float *x0, const float *x1,
-                                                  const float *x2)
+// One work-group per chunk: every particle's direction (the new tile relative
+// to the source tile), the chunk's per-direction counts, and the device flag
+// if a particle moved further than one tile.  The work-group's lanes read
+// consecutive particles (COUNT_EPT per lane in flight, the next batch loading
+// while this one is classified); counts are per wave (ballots) and then per
+// work-group (LDS).  Launched with 256 threads and 4 particles per lane for
+// chunks of thousands of particles, with one wave and one particle per lane
+// for small ones.
+template <int DIM, int ORDER, int COUNT_EPT>
+__global__ __launch_bounds__(256) void k_inc_count(IncGeom a, const float *x0, const float *x1,
+                                                   const float *x2)
 {
     if (*a.flag != 0u)
         return;
@@ -417,38 +422,44 @@ __global__ __launch_bounds__(64) void k_inc_count(IncGeom a, const float *x0, co
         return;
     int sc[3];
     tile_coords(s_tile, a.g, sc);
-    const uint32_t lo = s_lo, hi = s_hi;
-    bool far = false;
-    // software pipeline: the next batch's coordinates load while this one is
-    // classified (clamped loads: no branch around them)
-    auto load = [&](uint32_t p, float &c0, float &c1, float &c2) {
-        const uint32_t q = min(p, hi - 1);
-        c0 = x0[q];
-        c1 = DIM > 1 ? x1[q] : 0.f;
-        c2 = DIM > 2 ? x2[q] : 0.f;
+    const uint32_t lo = s_lo, hi = s_hi, stride = blockDim.x;
+    // clamped loads: no branch around them, so the next batch stays in flight
+    float c[COUNT_EPT][3], nc[COUNT_EPT][3];
+    auto load = [&](uint32_t b, float (*dst)[3]) {
+#pragma unroll
+        for (int e = 0; e < COUNT_EPT; ++e) {
+            const uint32_t q = min(b + e * stride, hi - 1);
+            dst[e][0] = x0[q];
+            dst[e][1] = DIM > 1 ? x1[q] : 0.f;
+            dst[e][2] = DIM > 2 ? x2[q] : 0.f;
+        }
     };
-    float c0, c1, c2;
-    load(lo + threadIdx.x, c0, c1, c2);
-    for (uint32_t b = lo; b < hi; b += 64) {
-        const uint32_t p = b + threadIdx.x;
-        const bool valid = p < hi;
-        float n0, n1, n2;
-        load(p + 64, n0, n1, n2);
-        int dir = particle_dir<DIM, ORDER>(c0, c1, c2, a.g, sc);
-        far |= valid && dir < 0;
-        const bool ok = valid && dir >= 0;
-        if (!ok)
-            dir = 0;
-        const uint64_t peers = peer_mask<5>((uint32_t)dir, ok);
-        // one lane per direction present adds the direction's count
-        if (ok && (peers & lanemask_lt()) == 0)
-            s_cnt[dir] += (uint32_t)__popcll(peers);
-        c0 = n0;
-        c1 = n1;
-        c2 = n2;
+    bool far = false;
+    load(lo + threadIdx.x, nc);
+    for (uint32_t b = lo + threadIdx.x; b - threadIdx.x < hi; b += COUNT_EPT * stride) {
+#pragma unroll
+        for (int e = 0; e < COUNT_EPT; ++e)
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+                c[e][k] = nc[e][k];
+        load(b + COUNT_EPT * stride, nc);
+#pragma unroll
+        for (int e = 0; e < COUNT_EPT; ++e) {
+            const bool valid = b + e * stride < hi;
+            int dir = particle_dir<DIM, ORDER>(c[e][0], c[e][1], c[e][2], a.g, sc);
+            far |= valid && dir < 0;
+            const bool ok = valid && dir >= 0;
+            // most particles stay in their tile: one ballot counts those, and
+            // each leaver adds itself
+            const uint64_t stay = __ballot(ok && dir == DIR_STAY);
+            if (lane_id() == 0 && stay)
+                atomicAdd(&s_cnt[DIR_STAY], (uint32_t)__popcll(stay));
+            if (ok && dir != DIR_STAY)
+                atomicAdd(&s_cnt[dir], 1u);
+        }
     }
     if (__ballot(far))
-        if (threadIdx.x == 0)
+        if (lane_id() == 0)
             atomicOr(a.flag, 1u);
     __syncthreads();
     if (threadIdx.x < NDIR)
@@ -546,12 +557,13 @@ __global__ __launch_bounds__(256) void k_inc_tiles(IncGeom a, uint32_t *__restri
     totals[t] = run;
 }
 
-// One wave per chunk (four per work-group), walking it in order 64 particles
-// at a time: each particle's direction again from its position, its slot from
-// the wave's running slot per direction (stable), then every array moved.
+// One wave per chunk (four per work-group), walking it in order EPT * 64
+// particles at a time: each particle's direction again from its position, its
+// slot from the wave's running slot per direction (stable), then every array
+// moved.
 constexpr int MOVE_WAVES = 4;
 
-template <int DIM, int ORDER>
+template <int DIM, int ORDER, int EPT>
 __global__ __launch_bounds__(MOVE_WAVES * WAVE) void k_inc_move(
     IncGeom a, const uint32_t *off, const float *x0, const float *x1, const float *x2,
     PermArgs arr, uint32_t *perm, uint32_t *keys, uint32_t nwork)
@@ -572,7 +584,6 @@ __global__ __launch_bounds__(MOVE_WAVES * WAVE) void k_inc_move(
     if (lane < NDIR)
         run[lane] = move_base(a, off, r.tile, r.chunk, lane);
     __builtin_amdgcn_wave_barrier();
-    constexpr int EPT = 4;
     for (uint32_t b = r.lo; b < r.hi; b += WAVE * EPT) {
         uint32_t p[EPT], pc[EPT], pos[EPT];
         int dir[EPT];
@@ -783,8 +794,14 @@ pcg_status incremental_launch(const IncGeom &a, const float *const key_x[3], uin
                               hipStream_t st)
 {
     const float *x1 = DIM > 1 ? key_x[1] : nullptr, *x2 = DIM > 2 ? key_x[2] : nullptr;
-    PCG_TRY(launch("sort_inc_count", k_inc_count<DIM, ORDER>, dim3(nwork), dim3(64), 0, st, a,
-                   key_x[0], x1, x2));
+    // a work-group per chunk: 256 threads when a tile's slice averages a
+    // chunk or more, one wave when chunks are small
+    if (a.count / std::max<int64_t>(1, a.ntiles) >= (int64_t)INC_CHUNK)
+        PCG_TRY(launch("sort_inc_count", k_inc_count<DIM, ORDER, 4>, dim3(nwork), dim3(256), 0, st,
+                       a, key_x[0], x1, x2));
+    else
+        PCG_TRY(launch("sort_inc_count", k_inc_count<DIM, ORDER, 1>, dim3(nwork), dim3(64), 0, st,
+                       a, key_x[0], x1, x2));
     PCG_TRY(launch("sort_inc_chunk_prefix", k_inc_chunk_prefix,
                    dim3((a.ntiles * NDIR + 255) / 256), dim3(256), 0, st, a));
     PCG_TRY(launch("sort_inc_tiles", k_inc_tiles, dim3((a.ntiles + 1 + 255) / 256), dim3(256), 0,
@@ -792,9 +809,13 @@ pcg_status incremental_launch(const IncGeom &a, const float *const key_x[3], uin
     PCG_TRY(exclusive_scan(tile_offsets, (size_t)a.ntiles + 1, b.partial, Gate{b.flag, 0u}, st));
     if (hook)
         return hook->launch(hook->ctx, a, tile_offsets, nwork, arr, st);
-    PCG_TRY(launch("sort_inc_move", k_inc_move<DIM, ORDER>,
-                   dim3((nwork + MOVE_WAVES - 1) / MOVE_WAVES), dim3(MOVE_WAVES * WAVE), 0, st, a,
-                   (const uint32_t *)tile_offsets, key_x[0], x1, x2, arr, perm, keys, nwork));
+    // 4 x 64 particles per step of a wave's walk, or 64 where chunks are small
+    auto kmove = a.count / std::max<int64_t>(1, a.ntiles) >= (int64_t)INC_CHUNK
+                     ? k_inc_move<DIM, ORDER, 4>
+                     : k_inc_move<DIM, ORDER, 1>;
+    PCG_TRY(launch("sort_inc_move", kmove, dim3((nwork + MOVE_WAVES - 1) / MOVE_WAVES),
+                   dim3(MOVE_WAVES * WAVE), 0, st, a, (const uint32_t *)tile_offsets, key_x[0],
+                   x1, x2, arr, perm, keys, nwork));
     return PCG_OK;
 }
 

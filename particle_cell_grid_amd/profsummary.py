@@ -31,7 +31,7 @@ def source_digest(kernel):
     """sha1 over the file that holds `kernel` (named <file>_<what>) and the
     headers every kernel file includes."""
     h = hashlib.sha1()
-    for f in (KERNEL_SOURCES[kernel.split("_")[0]], "common.hpp", "layout.hpp"):
+    for f in (KERNEL_SOURCES[kernel.split("_")[0]], "common.hpp", "layout.hpp", "regroup.hpp"):
         h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()
 
@@ -129,7 +129,7 @@ def traffic(fetch_dir, write_dir, out, workload, cmd_fetch, cmd_write, json_path
     rec.setdefault("note", "HBM bytes per dispatch from rocprofv3 FETCH_SIZE/WRITE_SIZE, "
                            "scaled by the 1 GiB copy calibration; source_sha1 digests the "
                            "kernel's sources at the time the counters were taken")
-    kern = rec.setdefault("kernels", {}).setdefault(workload, {})
+    kern = rec.setdefault("kernels", {})[workload] = {}  # this pass replaces the workload's record
     for n in sorted(fe):
         if n == COPY_KERNEL:
             continue

@@ -477,6 +477,25 @@ __device__ inline void load_phase(const MassArgs &m, uint32_t offv, PhaseRaw &pr
     pr.r3 = COL_SLOTS > 3 ? load_slot(m, offv, 3) : RawParticle{};
 }
 
+// An empty use of every value of a phase's particles: the compiler waits for
+// their loads here.
+__device__ __attribute__((always_inline)) inline void consume(const RawParticle &r)
+{
+    asm volatile("" ::"v"(r.x[0]), "v"(r.x[1]), "v"(r.x[2]), "v"(r.B[0]), "v"(r.B[1]),
+                 "v"(r.B[2]), "v"(r.q), "v"(r.w), "v"(r.beta));
+}
+
+__device__ __attribute__((always_inline)) inline void consume(const PhaseRaw &p)
+{
+    consume(p.r0);
+    if (COL_SLOTS > 1)
+        consume(p.r1);
+    if (COL_SLOTS > 2)
+        consume(p.r2);
+    if (COL_SLOTS > 3)
+        consume(p.r3);
+}
+
 // Slot k (uniform) of a phase, selected field by field.
 __device__ inline float pick1(int k, float a, float b, float c, float d)
 {
@@ -553,6 +572,11 @@ __global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, Co
     uint32_t off_cur = phase_offsets(m, cs, 0, wave);
     for (int ph = 0; ph < nphase; ++ph) {
         const int iz = ph >> 2;
+        // this phase's operands (loaded during the last phase) are waited for
+        // here, before the next loads issue: later uses then need no waits,
+        // which would also drain the loads issued below
+        consume(cur);
+        asm volatile("" ::"v"(off_cur), "v"(off_next));
         load_phase(m, off_next, nxt);
         const uint32_t off_after = phase_offsets(m, cs, ph + 2, wave);
         // the compiler must not sink these reads to their use
@@ -592,21 +616,37 @@ __global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, Co
         if ((ph & 3) == 3 && done >= 0) {
             const int gz = cs.first[2] + done;
             float *pl = planes + (size_t)(done & 1) * COL_NODES * ROW;
-            for (int ly = 0; ly < BY; ++ly) {
-                float *dst = m.M + (cs.first[0] + (int64_t)m.n[0] *
-                                    ((cs.first[1] + ly) + (int64_t)m.n[1] * gz)) * ROW;
-                float *src = pl + ly * COL_X * ROW;
-                float v[COL_ROW_PER_THREAD];
+            // every row's M values are read first (one round trip), then each
+            // row is added and stored
+            float v[COL_Y][COL_ROW_PER_THREAD];
+#pragma unroll
+            for (int ly = 0; ly < COL_Y; ++ly) {
+                const float *dst = m.M + (cs.first[0] + (int64_t)m.n[0] *
+                                          ((cs.first[1] + ly) + (int64_t)m.n[1] * gz)) * ROW;
 #pragma unroll
                 for (int q = 0; q < COL_ROW_PER_THREAD; ++q) {
                     const int r = threadIdx.x + q * COL_WAVES * WAVE;
-                    v[q] = r < BX * ROW ? dst[r] : 0.0f;
+                    v[ly][q] = ly < BY && r < BX * ROW ? dst[r] : 0.0f;
                 }
+            }
+            // one wait for all of them, so that the stores below need none
+#pragma unroll
+            for (int ly = 0; ly < COL_Y; ++ly)
+#pragma unroll
+                for (int q = 0; q < COL_ROW_PER_THREAD; ++q)
+                    asm volatile("" ::"v"(v[ly][q]));
+#pragma unroll
+            for (int ly = 0; ly < COL_Y; ++ly) {
+                if (ly >= BY)
+                    break;
+                float *dst = m.M + (cs.first[0] + (int64_t)m.n[0] *
+                                    ((cs.first[1] + ly) + (int64_t)m.n[1] * gz)) * ROW;
+                float *src = pl + ly * COL_X * ROW;
 #pragma unroll
                 for (int q = 0; q < COL_ROW_PER_THREAD; ++q) {
                     const int r = threadIdx.x + q * COL_WAVES * WAVE;
                     if (r < BX * ROW) {
-                        dst[r] = v[q] + src[r];
+                        dst[r] = v[ly][q] + src[r];
                         src[r] = 0.0f;  // only this thread read this value
                     }
                 }

@@ -84,6 +84,14 @@ __device__ inline RawParticle load_raw(const MassArgs &m, int64_t p)
     return r;
 }
 
+// An empty use of every value of a particle: the compiler waits for its
+// loads here.
+__device__ __attribute__((always_inline)) inline void consume(const RawParticle &r)
+{
+    asm volatile("" ::"v"(r.x[0]), "v"(r.x[1]), "v"(r.x[2]), "v"(r.B[0]), "v"(r.B[1]),
+                 "v"(r.B[2]), "v"(r.q), "v"(r.w), "v"(r.beta));
+}
+
 __device__ inline Particle make_particle(const MassArgs &m, const RawParticle &r)
 {
     Particle P;
@@ -348,9 +356,9 @@ __device__ inline void cell_moments(const MassArgs &m, WaveScratch &ws, int lane
     batch(first, lo);
     // cells of more than 64 particles: the later batches load here
     for (int64_t base = lo + 64; base < hi; base += 64) {
-        RawParticle rp{};
-        if (base + lane < hi)
-            rp = load_raw(m, base + lane);
+        // clamped load, waited for at once: the wait stays on this rare path
+        const RawParticle rp = load_raw(m, std::min<int64_t>(base + lane, hi - 1));
+        consume(rp);
         batch(rp, base);
     }
     wave_sync();
@@ -477,14 +485,6 @@ __device__ inline void load_phase(const MassArgs &m, uint32_t offv, PhaseRaw &pr
     pr.r3 = COL_SLOTS > 3 ? load_slot(m, offv, 3) : RawParticle{};
 }
 
-// An empty use of every value of a phase's particles: the compiler waits for
-// their loads here.
-__device__ __attribute__((always_inline)) inline void consume(const RawParticle &r)
-{
-    asm volatile("" ::"v"(r.x[0]), "v"(r.x[1]), "v"(r.x[2]), "v"(r.B[0]), "v"(r.B[1]),
-                 "v"(r.B[2]), "v"(r.q), "v"(r.w), "v"(r.beta));
-}
-
 __device__ __attribute__((always_inline)) inline void consume(const PhaseRaw &p)
 {
     consume(p.r0);
@@ -559,24 +559,18 @@ __global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, Co
     // phase ph + 2 are in flight.
     uint32_t off_next = phase_offsets(m, cs, 1, wave);
     PhaseRaw cur, nxt;
-    {
-        const uint32_t off0 = phase_offsets(m, cs, 0, wave);
-        load_phase(m, off0, cur);
-    }
+    uint32_t off_cur = phase_offsets(m, cs, 0, wave);
+    load_phase(m, off_cur, cur);
     __syncthreads();
 
+    consume(cur);
+    asm volatile("" ::"v"(off_cur), "v"(off_next));
     bool stray = false;
     const int pa = lane >> 3, pb = lane & 7;
     const int ax = pa & 1, ay = (pa >> 1) & 1, az = pa >> 2;
     const int o = offset_index(pa, pb);
-    uint32_t off_cur = phase_offsets(m, cs, 0, wave);
     for (int ph = 0; ph < nphase; ++ph) {
         const int iz = ph >> 2;
-        // this phase's operands (loaded during the last phase) are waited for
-        // here, before the next loads issue: later uses then need no waits,
-        // which would also drain the loads issued below
-        consume(cur);
-        asm volatile("" ::"v"(off_cur), "v"(off_next));
         load_phase(m, off_next, nxt);
         const uint32_t off_after = phase_offsets(m, cs, ph + 2, wave);
         // the compiler must not sink these reads to their use
@@ -608,6 +602,14 @@ __global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, Co
                     row[ij] += blk[ij];
             }
         }
+        // the next phase's operands (loaded during this one) are taken over and
+        // waited for here, before the write-out's stores: later uses then need
+        // no waits, which would also drain those stores or the next loads
+        cur = nxt;
+        off_cur = off_next;
+        off_next = off_after;
+        consume(cur);
+        asm volatile("" ::"v"(off_cur), "v"(off_next));
         __syncthreads();
 
         // after the layer's last colour node plane iz - 1 is complete: add it
@@ -653,9 +655,6 @@ __global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, Co
             }
             __syncthreads();
         }
-        cur = nxt;
-        off_cur = off_next;
-        off_next = off_after;
     }
     if (stray && cg.stray_flag)
         atomicOr(cg.stray_flag, 1u);

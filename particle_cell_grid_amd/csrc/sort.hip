@@ -532,7 +532,12 @@ __global__ __launch_bounds__(256) void k_inc_tiles(IncGeom a, uint32_t *__restri
 {
     if (*a.flag != 0u)
         return;
-    const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+    // blocks are dealt to the 8 XCDs in turn: give each XCD a contiguous run
+    // of new tiles, so that the rows of their shared source tiles are read
+    // through one L2 (the grid is a multiple of 8 blocks)
+    const uint32_t per = gridDim.x / 8;
+    const uint32_t blk = (blockIdx.x % 8) * per + blockIdx.x / 8;
+    const uint32_t t = blk * blockDim.x + threadIdx.x;
     if (t > a.ntiles)
         return;
     if (t == a.ntiles) {
@@ -545,14 +550,35 @@ __global__ __launch_bounds__(256) void k_inc_tiles(IncGeom a, uint32_t *__restri
     const int nx = axis_sources(tc[0], a.g.nt[0], cx, dx);
     const int ny = axis_sources(tc[1], a.g.nt[1], cy, dy);
     const int nz = axis_sources(tc[2], a.g.nt[2], cz, dz);
+    // all (up to 27) source counts are read first, then prefixed in source
+    // order; the loops have fixed bounds so that the reads issue together
+    size_t jj[27];
+    uint32_t v[27];
+#pragma unroll
+    for (int iz = 0; iz < 3; ++iz)
+#pragma unroll
+        for (int iy = 0; iy < 3; ++iy)
+#pragma unroll
+            for (int ix = 0; ix < 3; ++ix) {
+                const int q = ix + 3 * iy + 9 * iz;
+                const bool ok = ix < nx && iy < ny && iz < nz;
+                const int c[3] = {cx[ok ? ix : 0], cy[ok ? iy : 0], cz[ok ? iz : 0]};
+                jj[q] = (size_t)tile_index(c, a.g) * NDIR + dx[ok ? ix : 0] + 3 * dy[ok ? iy : 0] +
+                        9 * dz[ok ? iz : 0];
+                v[q] = ok ? a.tcnt[jj[q]] : 0u;
+            }
     uint32_t run = 0;
-    for (int iz = 0; iz < nz; ++iz)
-        for (int iy = 0; iy < ny; ++iy)
-            for (int ix = 0; ix < nx; ++ix) {
-                const int c[3] = {cx[ix], cy[iy], cz[iz]};
-                const size_t j = (size_t)tile_index(c, a.g) * NDIR + dx[ix] + 3 * dy[iy] + 9 * dz[iz];
-                a.tpre[j] = run;
-                run += a.tcnt[j];
+#pragma unroll
+    for (int iz = 0; iz < 3; ++iz)
+#pragma unroll
+        for (int iy = 0; iy < 3; ++iy)
+#pragma unroll
+            for (int ix = 0; ix < 3; ++ix) {
+                const int q = ix + 3 * iy + 9 * iz;
+                if (ix < nx && iy < ny && iz < nz) {
+                    a.tpre[jj[q]] = run;
+                    run += v[q];
+                }
             }
     totals[t] = run;
 }
@@ -804,8 +830,8 @@ pcg_status incremental_launch(const IncGeom &a, const float *const key_x[3], uin
                        a, key_x[0], x1, x2));
     PCG_TRY(launch("sort_inc_chunk_prefix", k_inc_chunk_prefix,
                    dim3((a.ntiles * NDIR + 255) / 256), dim3(256), 0, st, a));
-    PCG_TRY(launch("sort_inc_tiles", k_inc_tiles, dim3((a.ntiles + 1 + 255) / 256), dim3(256), 0,
-                   st, a, tile_offsets));
+    PCG_TRY(launch("sort_inc_tiles", k_inc_tiles, dim3((a.ntiles + 1 + 2047) / 2048 * 8),
+                   dim3(256), 0, st, a, tile_offsets));
     PCG_TRY(exclusive_scan(tile_offsets, (size_t)a.ntiles + 1, b.partial, Gate{b.flag, 0u}, st));
     if (hook)
         return hook->launch(hook->ctx, a, tile_offsets, nwork, arr, st);

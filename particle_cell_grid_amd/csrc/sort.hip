@@ -655,6 +655,111 @@ __global__ __launch_bounds__(MOVE_WAVES * WAVE) void k_inc_move(
     }
 }
 
+// The move for small chunks (a few dozen particles, e.g. cells): each wave
+// takes MOVE_SMALL_K consecutive chunks and issues every stage's reads for all
+// of them at once -- the chunk lookups, the 27 slot bases of each, then one
+// 64-particle step of each chunk's positions and arrays -- instead of paying
+// the round trips once per chunk.  Ranks, slots and stores are those of
+// k_inc_move.
+constexpr int MOVE_SMALL_K = 4;
+
+template <int DIM, int ORDER>
+__global__ __launch_bounds__(MOVE_WAVES * WAVE) void k_inc_move_small(
+    IncGeom a, const uint32_t *off, const float *x0, const float *x1, const float *x2,
+    PermArgs arr, uint32_t *perm, uint32_t *keys, uint32_t nwork)
+{
+    constexpr int K = MOVE_SMALL_K;
+    static_assert(K * NDIR <= 2 * WAVE, "two slot bases per lane");
+    if (*a.flag != 0u)
+        return;
+    __shared__ uint32_t s_run[MOVE_WAVES][K][32];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), lane = lane_id();
+    const uint32_t item0 = (blockIdx.x * MOVE_WAVES + wave) * K;
+    if (item0 >= nwork)
+        return;
+    // the K chunks, one per lane
+    uint32_t ct = UINT_MAX, cc = 0, clo = 0, chi = 0;
+    if (lane < K && item0 + lane < nwork) {
+        const ChunkRange r = find_chunk(item0 + lane, a.cum, a.map, a.ntiles, a.prev_off, a.count);
+        ct = r.tile;
+        cc = r.chunk;
+        clo = r.lo;
+        chi = r.hi;
+    }
+    // their slot bases, (chunk j, direction d) at lane j * NDIR + d (two rounds of lanes)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int idx = lane + WAVE * h;
+        const int j = min(idx / NDIR, K - 1), d = idx % NDIR;
+        const uint32_t tj = __shfl(ct, j), cj = __shfl(cc, j);
+        if (idx < K * NDIR && tj != UINT_MAX)
+            s_run[wave][j][d] = move_base(a, off, tj, cj, d);
+    }
+    __builtin_amdgcn_wave_barrier();
+    uint32_t tile[K], lo[K], hi[K], len = 0;
+    int sc[K][3];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        tile[j] = __builtin_amdgcn_readlane(ct, j);
+        lo[j] = __builtin_amdgcn_readlane(clo, j);
+        hi[j] = __builtin_amdgcn_readlane(chi, j);
+        if (tile[j] == UINT_MAX)
+            hi[j] = lo[j];
+        tile_coords(tile[j] == UINT_MAX ? 0u : tile[j], a.g, sc[j]);
+        len = max(len, hi[j] - lo[j]);
+    }
+    for (uint32_t st = 0; st < len; st += WAVE) {
+        uint32_t p[K], pc[K], pos[K];
+        int dir[K];
+        bool ok[K];
+        float c[K][3];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            p[j] = lo[j] + st + lane;
+            // clamped into the chunk (or to particle 0 for an empty one): no branch
+            pc[j] = hi[j] > lo[j] ? min(p[j], hi[j] - 1) : 0u;
+            c[j][0] = x0[pc[j]];
+            c[j][1] = DIM > 1 ? x1[pc[j]] : 0.f;
+            c[j][2] = DIM > 2 ? x2[pc[j]] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            dir[j] = particle_dir<DIM, ORDER>(c[j][0], c[j][1], c[j][2], a.g, sc[j]);
+            ok[j] = p[j] < hi[j] && dir[j] >= 0;  // dir < 0 cannot occur: the flag is clear
+            pos[j] = walk_slot(s_run[wave][j], dir[j], ok[j]);
+            ok[j] = ok[j] && pos[j] < (uint64_t)a.count;
+        }
+        if (keys) {
+#pragma unroll
+            for (int j = 0; j < K; ++j)
+                if (ok[j])
+                    keys[pos[j]] = dest_tile(sc[j], dir[j], a.g);
+        }
+        if (perm) {
+#pragma unroll
+            for (int j = 0; j < K; ++j)
+                if (ok[j])
+                    perm[pos[j]] = p[j];
+        }
+        // every array's values first (one round trip), then the stores
+        float v[MAX_ARRAYS][K];
+#pragma unroll
+        for (int k = 0; k < MAX_ARRAYS; ++k)
+#pragma unroll
+            for (int j = 0; j < K; ++j)
+                v[k][j] = k < arr.n ? arr.in[k][pc[j]] : 0.f;
+#pragma unroll
+        for (int k = 0; k < MAX_ARRAYS; ++k) {
+            if (k < arr.n) {
+#pragma unroll
+                for (int j = 0; j < K; ++j)
+                    if (ok[j])
+                        arr.out[k][pos[j]] = v[k][j];
+            }
+        }
+    }
+}
+
 // ----------------------------------------------------------------- host
 
 struct SortPlan {
@@ -835,13 +940,18 @@ pcg_status incremental_launch(const IncGeom &a, const float *const key_x[3], uin
     PCG_TRY(exclusive_scan(tile_offsets, (size_t)a.ntiles + 1, b.partial, Gate{b.flag, 0u}, st));
     if (hook)
         return hook->launch(hook->ctx, a, tile_offsets, nwork, arr, st);
-    // 4 x 64 particles per step of a wave's walk, or 64 where chunks are small
-    auto kmove = a.count / std::max<int64_t>(1, a.ntiles) >= (int64_t)INC_CHUNK
-                     ? k_inc_move<DIM, ORDER, 4>
-                     : k_inc_move<DIM, ORDER, 1>;
-    PCG_TRY(launch("sort_inc_move", kmove, dim3((nwork + MOVE_WAVES - 1) / MOVE_WAVES),
-                   dim3(MOVE_WAVES * WAVE), 0, st, a, (const uint32_t *)tile_offsets, key_x[0],
-                   x1, x2, arr, perm, keys, nwork));
+    // 4 x 64 particles per step of a wave's walk through its chunk; where
+    // chunks are small, several chunks per wave
+    if (a.count / std::max<int64_t>(1, a.ntiles) >= (int64_t)INC_CHUNK)
+        PCG_TRY(launch("sort_inc_move", k_inc_move<DIM, ORDER, 4>,
+                       dim3((nwork + MOVE_WAVES - 1) / MOVE_WAVES), dim3(MOVE_WAVES * WAVE), 0, st,
+                       a, (const uint32_t *)tile_offsets, key_x[0], x1, x2, arr, perm, keys,
+                       nwork));
+    else
+        PCG_TRY(launch("sort_inc_move", k_inc_move_small<DIM, ORDER>,
+                       dim3((nwork + MOVE_WAVES * MOVE_SMALL_K - 1) / (MOVE_WAVES * MOVE_SMALL_K)),
+                       dim3(MOVE_WAVES * WAVE), 0, st, a, (const uint32_t *)tile_offsets, key_x[0],
+                       x1, x2, arr, perm, keys, nwork));
     return PCG_OK;
 }
 

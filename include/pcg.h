@@ -179,15 +179,16 @@ size_t pcg_deposit_regroup_workspace_bytes(const pcg_grid *grid, const pcg_tile 
  *                   tile_offsets, tile, ...);
  * (J and n_escaped accumulated as there; out_arrays and tile_offsets equal to
  * the sort's, bit for bit), but when `tile` covers every particle
- * (n_partitioned == count) the sort's move is made by the deposit kernel from
- * the values it has loaded, so the particle arrays are read once instead of
- * twice.  `tile` is the layout the particles are grouped by (required); the
- * sort uses it as `prev`, so particles that moved further than one tile, or a
- * layout that is not a partition, send the regrouping to the general sort
- * path (decided on the device; the deposit is unaffected).  With a tail the
- * two calls run one after the other.  in_arrays / out_arrays as in
- * pcg_tile_sort (usually x[0..dim), v[0..3), q, w and any other per-particle
- * fields; out of place).  tile_offsets: device uint32 [ntiles + 1], the new
+ * (n_partitioned == count) and in_arrays are exactly x[0..dim), v[0..3), q, w
+ * of `particles`, in that order, the sort's move is made by the deposit
+ * kernel from the values it has loaded, so the particle arrays are read once
+ * instead of twice.  `tile` is the layout the particles are grouped by
+ * (required); the sort uses it as `prev`, so particles that moved further
+ * than one tile, or a layout that is not a partition, send the regrouping to
+ * the general sort path (decided on the device; the deposit is unaffected).
+ * With a tail, or with any other list of arrays, the two calls run one after
+ * the other.  in_arrays / out_arrays as in pcg_tile_sort (out of place).  The
+ * sort's argument checks run before anything is enqueued.  tile_offsets: device uint32 [ntiles + 1], the new
  * layout, distinct from tile->tile_offsets.  workspace: at least
  * pcg_deposit_regroup_workspace_bytes(), 256-byte aligned. */
 pcg_status deposit_currents_regroup(const pcg_grid *grid, const pcg_particles *particles,

@@ -104,4 +104,10 @@ __device__ inline void atomic_add_f32(float *p, float v)
     __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// One entry of a chunk map (a work item of a tile layout): the chunk's tile
+// and particle range [lo, hi).
+struct alignas(16) ChunkEntry {
+    uint32_t tile, lo, hi, pad;
+};
+
 }  // namespace pcg

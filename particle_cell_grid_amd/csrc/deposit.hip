@@ -48,7 +48,7 @@ struct DepArgs {
     const uint32_t *tile_offsets;
     int64_t n_part;
     const uint32_t *chunk_cum;   // [ntiles + 1] work items before each tile
-    const uint32_t *chunk_map;   // [nwork] tile of each work item
+    const ChunkEntry *chunk_map;  // [nwork] tile and range of each work item
     uint32_t *chunk_part;        // scratch of the chunk prefix
     uint32_t chunk;
     unsigned long long *n_escaped;
@@ -1075,7 +1075,7 @@ size_t carve_deposit(uint32_t ntiles, int64_t n_part, void *ws, DepArgs *a)
     Carver c(ws);
     uint32_t *cum = c.take<uint32_t>((size_t)ntiles + 1);
     uint32_t *part = c.take<uint32_t>(chunk_part_len(ntiles));
-    uint32_t *map = c.take<uint32_t>(max_deposit_work(ntiles, n_part));
+    ChunkEntry *map = c.take<ChunkEntry>(max_deposit_work(ntiles, n_part));
     if (a) {
         a->chunk_cum = cum;
         a->chunk_part = part;
@@ -1246,7 +1246,7 @@ pcg_status launch_chunks(const DepArgs &a, hipStream_t st)
 {
     return launch_chunk_layout("deposit_chunks", a.tile_offsets, a.ntiles, a.n_part, a.chunk,
                                const_cast<uint32_t *>(a.chunk_cum), a.chunk_part,
-                               const_cast<uint32_t *>(a.chunk_map),
+                               const_cast<ChunkEntry *>(a.chunk_map),
                                (uint32_t)max_deposit_work(a.ntiles, a.n_part), nullptr, 0u, st);
 }
 

@@ -2,8 +2,8 @@
 // and the incremental sort: each tile slice [off[t], off[t+1]) (clipped to the
 // partitioned prefix) is split into ceil(len / chunk) balanced chunks; a
 // prefix over tiles numbers the chunks so that one work-group takes one chunk,
-// and a map from chunk number to tile lets a work-group find its chunk with
-// two dependent reads.
+// and a map from chunk number to (tile, first, end) lets a work-group find its
+// chunk with one read.
 #pragma once
 
 #include <algorithm>
@@ -15,6 +15,20 @@ namespace pcg {
 namespace {
 
 constexpr int CHUNK_SCAN_BLOCK = 1024;  // tiles per block of the chunk prefix
+
+// Writes the n map entries of tile t (chunks c0 .. c0 + n - 1, the balanced
+// split of its clipped slice), those below map_len.
+__device__ inline void write_tile_chunks(ChunkEntry *map, uint32_t map_len, uint32_t c0,
+                                         uint32_t n, uint32_t t, const uint32_t *off,
+                                         int64_t n_part)
+{
+    const uint64_t p0 = std::min<uint64_t>(off[t], (uint64_t)n_part);
+    const uint64_t p1 = std::min<uint64_t>(off[t + 1], (uint64_t)n_part);
+    const uint64_t len = p1 > p0 ? p1 - p0 : 0;
+    for (uint32_t j = 0; j < n && (uint64_t)c0 + j < map_len; ++j)
+        map[c0 + j] = ChunkEntry{t, (uint32_t)(p0 + len * j / n), (uint32_t)(p0 + len * (j + 1) / n),
+                                 0u};
+}
 
 // Work items of tile t: ceil(len / chunk), 0 for an empty tile.
 __device__ inline uint32_t tile_items(const uint32_t *__restrict__ off, uint32_t t, int64_t n_part,
@@ -94,13 +108,13 @@ __global__ __launch_bounds__(CHUNK_SCAN_BLOCK) void k_chunk_scan2(uint32_t *__re
         cum[ntiles] = carry;
 }
 
-// Pass 3: global prefix (cum[t] += block offset) and the map from work item to
-// tile: map[cum[t] + j] = t for j < items(t).
+// Pass 3: global prefix (cum[t] += block offset) and the map entries of the
+// tile's items cum[t] .. cum[t] + items(t) - 1.
 // Entries past map_len are not written (offsets that are not a partition
 // could ask for more); their work items are never launched.
 __global__ __launch_bounds__(CHUNK_SCAN_BLOCK) void k_chunk_scan3(
     const uint32_t *__restrict__ off, uint32_t ntiles, int64_t n_part, uint32_t chunk,
-    uint32_t *__restrict__ cum, const uint32_t *__restrict__ part, uint32_t *__restrict__ map,
+    uint32_t *__restrict__ cum, const uint32_t *__restrict__ part, ChunkEntry *__restrict__ map,
     uint32_t map_len, const uint32_t *gate, uint32_t gate_run)
 {
     if (gate && *gate != gate_run)
@@ -110,9 +124,7 @@ __global__ __launch_bounds__(CHUNK_SCAN_BLOCK) void k_chunk_scan3(
         return;
     const uint32_t c0 = cum[t] + part[blockIdx.x];
     cum[t] = c0;
-    const uint32_t n = tile_items(off, t, n_part, chunk);
-    for (uint32_t j = 0; j < n && (uint64_t)c0 + j < map_len; ++j)
-        map[c0 + j] = t;
+    write_tile_chunks(map, map_len, c0, tile_items(off, t, n_part, chunk), t, off, n_part);
 }
 
 // Tiles up to which one work-group computes the whole layout in one launch.
@@ -124,8 +136,8 @@ constexpr int CHUNK_TPT = 4;  // tiles per thread per round of the one-launch la
 // off[0] = 0, off is non-decreasing and off[ntiles] = n_part, else 1.
 __global__ __launch_bounds__(CHUNK_SCAN_BLOCK) void k_chunk_layout_one(
     const uint32_t *__restrict__ off, uint32_t ntiles, int64_t n_part, uint32_t chunk,
-    uint32_t *__restrict__ cum, uint32_t *__restrict__ map, uint32_t map_len, const uint32_t *gate,
-    uint32_t gate_run, uint32_t *flag)
+    uint32_t *__restrict__ cum, ChunkEntry *__restrict__ map, uint32_t map_len,
+    const uint32_t *gate, uint32_t gate_run, uint32_t *flag)
 {
     if (gate && *gate != gate_run)
         return;
@@ -157,8 +169,7 @@ __global__ __launch_bounds__(CHUNK_SCAN_BLOCK) void k_chunk_layout_one(
             const uint32_t t = t0 + j;
             if (t < ntiles) {
                 cum[t] = c;
-                for (uint32_t k = 0; k < items[j] && (uint64_t)c + k < map_len; ++k)
-                    map[c + k] = t;
+                write_tile_chunks(map, map_len, c, items[j], t, off, n_part);
                 c += items[j];
             }
         }
@@ -183,7 +194,7 @@ __global__ __launch_bounds__(CHUNK_SCAN_BLOCK) void k_chunk_layout_one(
 // kernels return at once unless *gate == gate_run.
 inline pcg_status launch_chunk_layout(const char *name, const uint32_t *off, uint32_t ntiles,
                                       int64_t n_part, uint32_t chunk, uint32_t *cum,
-                                      uint32_t *part, uint32_t *map, uint32_t map_len,
+                                      uint32_t *part, ChunkEntry *map, uint32_t map_len,
                                       const uint32_t *gate, uint32_t gate_run, hipStream_t st)
 {
     if (ntiles <= CHUNK_ONE_BLOCK_MAX)
@@ -211,27 +222,21 @@ struct ChunkRange {
     uint32_t lo, hi;
 };
 
-// Decode work item `item` (one thread calls this; item < the map's length):
-// the tile that holds it, from the map, and the item's share of the tile's
-// slice.
-__device__ inline ChunkRange find_chunk(uint32_t item, const uint32_t *cum, const uint32_t *map,
+// Decode work item `item` (item < the map's length): its tile and particle
+// range, from one map entry (entries past the total are stale: checked first).
+__device__ inline ChunkRange find_chunk(uint32_t item, const uint32_t *cum, const ChunkEntry *map,
                                         uint32_t ntiles, const uint32_t *off, int64_t n_part)
 {
+    (void)off;
+    (void)n_part;
     ChunkRange r{UINT_MAX, item, 0, 0};
     const uint32_t total = cum[ntiles];
-    const uint32_t t = map[item];  // stale past the total: checked first
-    if (item >= total || t >= ntiles)
+    const ChunkEntry e = map[item];
+    if (item >= total || e.tile >= ntiles || e.hi <= e.lo)
         return r;
-    const uint32_t nch = cum[t + 1] - cum[t];
-    const uint32_t c = item - cum[t];
-    const uint64_t p0 = std::min<uint64_t>(off[t], (uint64_t)n_part);
-    const uint64_t p1 = std::min<uint64_t>(off[t + 1], (uint64_t)n_part);
-    const uint64_t len = p1 > p0 ? p1 - p0 : 0;
-    if (c >= nch)
-        return r;
-    r.tile = t;
-    r.lo = (uint32_t)(p0 + len * c / nch);
-    r.hi = (uint32_t)(p0 + len * (c + 1) / nch);
+    r.tile = e.tile;
+    r.lo = e.lo;
+    r.hi = e.hi;
     return r;
 }
 

@@ -58,7 +58,7 @@ struct IncGeom {
     const uint32_t *prev_off;
     int64_t count;
     const uint32_t *cum;  // [ntiles + 1] chunk numbering of the source slices
-    const uint32_t *map;  // [nchunks] source tile of each chunk
+    const ChunkEntry *map;  // [nchunks] source tile and range of each chunk
     uint32_t *cnt;        // [nchunks][NDIR] particles per direction; then prefix over chunks
     uint32_t *tcnt;       // [ntiles][NDIR] per source tile
     uint32_t *tpre;       // [ntiles][NDIR] prefix over a new tile's sources

@@ -795,7 +795,8 @@ SortPlan make_plan(const pcg_grid *grid, int64_t count, int T)
 
 struct SortBuffers {
     uint32_t *k0, *ak, *av, *bv, *fk, *pm, *counts, *partial;
-    uint32_t *flag, *cum, *cnt, *tcnt, *tpre, *cpart, *cmap;
+    uint32_t *flag, *cum, *cnt, *tcnt, *tpre, *cpart;
+    ChunkEntry *cmap;
 };
 
 size_t carve(const SortPlan &p, void *ws, SortBuffers *b)
@@ -817,7 +818,7 @@ size_t carve(const SortPlan &p, void *ws, SortBuffers *b)
     b->tcnt = c.take<uint32_t>((size_t)p.ntiles * NDIR);
     b->tpre = c.take<uint32_t>((size_t)p.ntiles * NDIR);
     b->cpart = c.take<uint32_t>(chunk_part_len(p.ntiles));
-    b->cmap = c.take<uint32_t>(p.nchunks_max);
+    b->cmap = c.take<ChunkEntry>(p.nchunks_max);
     return c.used;
 }
 

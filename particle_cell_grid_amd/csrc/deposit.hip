@@ -511,8 +511,7 @@ __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
     __shared__ uint32_t s_c0, s_nsub;
 
     if (threadIdx.x == 0) {
-        ChunkRange r = find_chunk(blockIdx.x, a.chunk_cum, a.chunk_map, a.ntiles, a.tile_offsets,
-                                  a.n_part);
+        ChunkRange r = find_chunk(blockIdx.x, a.chunk_cum, a.chunk_map, a.ntiles);
         s_esc = 0;
         s_qn = 0;
         s_mn = 0;

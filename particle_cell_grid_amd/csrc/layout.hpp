@@ -225,10 +225,8 @@ struct ChunkRange {
 // Decode work item `item` (item < the map's length): its tile and particle
 // range, from one map entry (entries past the total are stale: checked first).
 __device__ inline ChunkRange find_chunk(uint32_t item, const uint32_t *cum, const ChunkEntry *map,
-                                        uint32_t ntiles, const uint32_t *off, int64_t n_part)
+                                        uint32_t ntiles)
 {
-    (void)off;
-    (void)n_part;
     ChunkRange r{UINT_MAX, item, 0, 0};
     const uint32_t total = cum[ntiles];
     const ChunkEntry e = map[item];

@@ -410,7 +410,7 @@ __global__ __launch_bounds__(256) void k_inc_count(IncGeom a, const float *x0, c
     __shared__ uint32_t s_tile, s_lo, s_hi;
     __shared__ uint32_t s_cnt[32];
     if (threadIdx.x == 0) {
-        const ChunkRange r = find_chunk(blockIdx.x, a.cum, a.map, a.ntiles, a.prev_off, a.count);
+        const ChunkRange r = find_chunk(blockIdx.x, a.cum, a.map, a.ntiles);
         s_tile = r.tile;
         s_lo = r.lo;
         s_hi = r.hi;
@@ -601,7 +601,7 @@ __global__ __launch_bounds__(MOVE_WAVES * WAVE) void k_inc_move(
     const uint32_t item = blockIdx.x * MOVE_WAVES + wave;
     if (item >= nwork)
         return;
-    const ChunkRange r = find_chunk(item, a.cum, a.map, a.ntiles, a.prev_off, a.count);
+    const ChunkRange r = find_chunk(item, a.cum, a.map, a.ntiles);
     if (r.tile == UINT_MAX)
         return;
     int sc[3];
@@ -680,7 +680,7 @@ __global__ __launch_bounds__(MOVE_WAVES * WAVE) void k_inc_move_small(
     // the K chunks, one per lane
     uint32_t ct = UINT_MAX, cc = 0, clo = 0, chi = 0;
     if (lane < K && item0 + lane < nwork) {
-        const ChunkRange r = find_chunk(item0 + lane, a.cum, a.map, a.ntiles, a.prev_off, a.count);
+        const ChunkRange r = find_chunk(item0 + lane, a.cum, a.map, a.ntiles);
         ct = r.tile;
         cc = r.chunk;
         clo = r.lo;

@@ -68,6 +68,9 @@ def lib():
         L.oracle_mass_matrix.argtypes = [i32p, C.c_int64, fpp, fpp, C.c_void_p, C.c_void_p,
                                          C.c_void_p, C.c_void_p]
         L.oracle_mass_matrix.restype = C.c_int
+        L.oracle_mass_matrix_scalar.argtypes = [i32p, C.c_int64, fpp, C.c_void_p, C.c_void_p,
+                                                C.c_void_p]
+        L.oracle_mass_matrix_scalar.restype = C.c_int
         L.oracle_sweep1d.argtypes = [C.c_int, C.c_int64, C.c_void_p, C.c_void_p, C.c_int,
                                      C.c_double, C.c_double, C.c_void_p]
         L.oracle_sweep1d.restype = C.c_int
@@ -213,6 +216,21 @@ def mass_matrix(n, x, B, q, w, beta, M=None):
     rc = lib().oracle_mass_matrix(_grid(n3), int(q.size), xs, bs, _ptr(q), _ptr(w), _ptr(beta),
                                   _ptr(M))
     _check(rc, "mass_matrix")
+    return M
+
+
+def mass_matrix_scalar(n, x, q, w, M=None):
+    """Scalar mass matrix (one component per node pair), 27-offset store
+    [nz, ny, nx, 27] fp64 (accumulated)."""
+    n3 = list(n)
+    keep = []
+    xs = _ptrs(list(x), keep)
+    q, w = _f32(q), _f32(w)
+    if M is None:
+        M = np.zeros((n3[2], n3[1], n3[0], 27), dtype=np.float64)
+    assert M.dtype == np.float64 and M.flags.c_contiguous
+    rc = lib().oracle_mass_matrix_scalar(_grid(n3), int(q.size), xs, _ptr(q), _ptr(w), _ptr(M))
+    _check(rc, "mass_matrix_scalar")
     return M
 
 

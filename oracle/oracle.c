@@ -328,6 +328,43 @@ int oracle_mass_matrix(const int32_t n[3], int64_t np, const float *const x[3],
     return 0;
 }
 
+/* [MM] §2.1, the scalar case of Eq.(6): the per-particle coefficient is
+ * q_p w_p times the identity, so a node pair carries one component
+ * (the mass matrix of MPM), with sigma = 1:
+ *   M_{g g'} += q_p w_p W_{pg} W_{pg'}
+ * over every ordered pair (g, g') of the particle's 8 CIC support nodes, in
+ * the same 27-offset store as oracle_mass_matrix: M is fp64
+ * [n_z][n_y][n_x][27] and is accumulated.  3D, CIC only; n_k >= 3. */
+int oracle_mass_matrix_scalar(const int32_t n[3], int64_t np, const float *const x[3],
+                              const float *q, const float *w, double *M)
+{
+    if (n[0] < 3 || n[1] < 3 || n[2] < 3 || np < 0)
+        return -1;
+    for (int64_t p = 0; p < np; ++p) {
+        const double s = (double)q[p] * (double)w[p];
+        int64_t base[3];
+        double W[3][2];
+        for (int k = 0; k < 3; ++k)
+            oracle_shape_1d(1, (double)x[k][p], &base[k], W[k]);
+        for (int az = 0; az < 2; ++az)
+            for (int ay = 0; ay < 2; ++ay)
+                for (int ax = 0; ax < 2; ++ax) {
+                    const int64_t g = wrap(base[0] + ax, n[0]) +
+                                      (int64_t)n[0] * (wrap(base[1] + ay, n[1]) +
+                                                       (int64_t)n[1] * wrap(base[2] + az, n[2]));
+                    const double wg = W[0][ax] * W[1][ay] * W[2][az];
+                    for (int bz = 0; bz < 2; ++bz)
+                        for (int by = 0; by < 2; ++by)
+                            for (int bx = 0; bx < 2; ++bx) {
+                                const double wh = W[0][bx] * W[1][by] * W[2][bz];
+                                const int o = (bx - ax + 1) + 3 * (by - ay + 1) + 9 * (bz - az + 1);
+                                M[g * 27 + o] += s * wg * wh;
+                            }
+                }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* 1-D windowed sweep deposit                                                */
 /* ------------------------------------------------------------------------ */

@@ -497,6 +497,76 @@ def test_mass_matrix_row_nonzeros_bounded(orc):
     assert per_row.max() == g["row_nonzeros_max"]["cic_3d"] == 27
 
 
+def test_scalar_mass_matrix_equals_dense_contraction(orc):
+    """[MM] Eq.(10) in the scalar case of Eq.(6): M = W diag(q w) W^T on a 4^3
+    grid, against the 27-offset store."""
+    r = np.random.default_rng(41)
+    n = [4, 4, 4]
+    x, _, q, w, _ = _mm_inputs(r, n, 150)
+    M = orc.mass_matrix_scalar(n, x, q, w)
+    W = _weights_matrix(orc, n, x)
+    dense = W @ np.diag(q.astype(np.float64) * w.astype(np.float64)) @ W.T
+    store = np.zeros((64, 64))
+    for gz in range(4):
+        for gy in range(4):
+            for gx in range(4):
+                g = gx + 4 * (gy + 4 * gz)
+                for o, (dx, dy, dz) in enumerate(OFFS):
+                    g2 = (gx + dx) % 4 + 4 * (((gy + dy) % 4) + 4 * ((gz + dz) % 4))
+                    store[g, g2] += M[gz, gy, gx, o]
+    assert np.abs(store - dense).max() < 1e-12 * max(1.0, np.abs(dense).max())
+
+
+def test_scalar_mass_matrix_symmetry_row_sums_and_charge(orc):
+    """[MM] Eq.(11) symmetry; row sums equal the CIC deposit of q w (partition of
+    unity of the second factor), and the grand total is sum q w."""
+    r = np.random.default_rng(42)
+    n = [6, 5, 4]
+    x, _, q, w, _ = _mm_inputs(r, n, 500)
+    M = orc.mass_matrix_scalar(n, x, q, w)
+    for o, (dx, dy, dz) in enumerate(OFFS):
+        mo = OFFS.index((-dx, -dy, -dz))
+        rolled = np.roll(M[:, :, :, mo], shift=(-dz, -dy, -dx), axis=(0, 1, 2))
+        assert np.abs(M[:, :, :, o] - rolled).max() < 1e-13
+    ones = np.ones_like(q)
+    zeros = np.zeros_like(q)
+    J = orc.deposit(3, n, 1, x, [ones, zeros, zeros], q, w)  # J_x = sum_p q w W_pg
+    assert np.abs(M.sum(axis=3) - J[0]).max() < 1e-12
+    assert abs(M.sum() - float(np.sum(q.astype(np.float64) * w.astype(np.float64)))) < 1e-10
+
+
+def test_scalar_mass_matrix_single_particle(orc):
+    # x = (1.25, 2.5, 3.75) on 8^3, q w = -3: M_{g,g+o} = -3 W_g W_{g+o}, by hand
+    x = _one([1.25, 2.5, 3.75])
+    M = orc.mass_matrix_scalar([8, 8, 8], x, np.float32([-1.0]), np.float32([3.0]))
+    wx = {1: .75, 2: .25}
+    wy = {2: .5, 3: .5}
+    wz = {3: .25, 4: .75}
+    nz = 0
+    for gz in wz:
+        for gy in wy:
+            for gx in wx:
+                for o, (dx, dy, dz) in enumerate(OFFS):
+                    hx, hy, hz = gx + dx, gy + dy, gz + dz
+                    if hx in wx and hy in wy and hz in wz:
+                        val = -3.0 * (wx[gx] * wy[gy] * wz[gz]) * (wx[hx] * wy[hy] * wz[hz])
+                        assert M[gz, gy, gx, o] == val
+                        nz += 1
+    assert nz == 64 and np.count_nonzero(M) == 64
+
+
+def test_scalar_mass_matrix_is_the_zero_field_tensor_diagonal(orc):
+    """B = 0 gives alpha = I, so each diagonal component of the ECSIM matrix is
+    the scalar matrix ([MM] Eq.(6) with s = q delta_ij)."""
+    r = np.random.default_rng(43)
+    n = [5, 4, 6]
+    x, B, q, w, beta = _mm_inputs(r, n, 300, zero_B=True)
+    Ms = orc.mass_matrix_scalar(n, x, q, w)
+    Mt = orc.mass_matrix(n, x, B, q, w, beta)
+    for i in range(3):
+        assert np.abs(Mt[..., i, i] - Ms).max() < 1e-13
+
+
 # ---------------------------------------------------------------------------
 # 1-D windowed sweep  ([CS] "The problem", "Code")
 # ---------------------------------------------------------------------------

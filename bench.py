@@ -14,7 +14,8 @@ timed steps.
 
 Other workloads (--workload): cic2d_512_ppc16 (2-D CIC 512^2), tsc3d_128_blob
 (3-D TSC clustered, T from --tile), mass_64_ppc64 (ECSIM mass matrix 64^3: cell
-sort + MFMA assembly), sweep1d_2000 (1-D windowed sweep).
+sort + MFMA assembly), mass_scalar_64_ppc64 (the scalar mass matrix, coefficient
+q w, on the same particles), sweep1d_2000 (1-D windowed sweep).
 
 Prints ONE JSON line (rank 0).  Only one GPU is used: --gpus above 1 exits.
 """
@@ -46,7 +47,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=HEADLINE,
                     choices=["sweep1d_2000", "cic2d_512_ppc16", "cic3d_128_ppc32",
-                             "tsc3d_128_blob", "mass_64_ppc64"])
+                             "tsc3d_128_blob", "mass_64_ppc64", "mass_scalar_64_ppc64"])
     ap.add_argument("--tile", type=int, default=0, help="tile edge T (0 = the workload's)")
     ap.add_argument("--block", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -310,7 +311,9 @@ def bench_deposit(args, torch, pcg, name):
 
 # ----------------------------------------------------------------- mass matrix
 
-def bench_mass(args, torch, pcg):
+def bench_mass(args, torch, pcg, scalar=False):
+    """The ECSIM mass matrix, or with scalar=True the scalar one (coefficient q w:
+    x, q, w are read and sorted, 27 floats per node row)."""
     import numpy as np
 
     import synthetic
@@ -321,8 +324,12 @@ def bench_mass(args, torch, pcg):
     dev = torch.device("cuda:0")
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     x = [t(a) for a in wl.x]
-    shuffled = x + [t(b) for b in wl.B] + [t(wl.beta), t(wl.q), t(wl.w)]
-    M = torch.zeros(n[2], n[1], n[0], 27, 3, 3, dtype=torch.float32, device=dev)
+    if scalar:
+        shuffled = x + [t(wl.q), t(wl.w)]
+        M = torch.zeros(n[2], n[1], n[0], 27, dtype=torch.float32, device=dev)
+    else:
+        shuffled = x + [t(b) for b in wl.B] + [t(wl.beta), t(wl.q), t(wl.w)]
+        M = torch.zeros(n[2], n[1], n[0], 27, 3, 3, dtype=torch.float32, device=dev)
     nc = n[0] * n[1] * n[2]
     perm = torch.empty(cnt, dtype=torch.int32, device=dev)
     keys = torch.empty(cnt, dtype=torch.int32, device=dev)
@@ -341,8 +348,12 @@ def bench_mass(args, torch, pcg):
     cells = pcg.Layout(T=1, order=1, tile_offsets=off1, n_partitioned=cnt, drift=0)
 
     def assemble(variant):
-        pcg.assemble_mass_matrix(n, nxt[0:3], nxt[3:6], nxt[6], nxt[7], nxt[8], M, cells,
-                                 variant, workspace=mws)
+        if scalar:
+            pcg.assemble_mass_matrix_scalar(n, nxt[0:3], nxt[3], nxt[4], M, cells, variant,
+                                            workspace=mws)
+        else:
+            pcg.assemble_mass_matrix(n, nxt[0:3], nxt[3:6], nxt[6], nxt[7], nxt[8], M, cells,
+                                     variant, workspace=mws)
 
     def step():
         # re-sort by cell from the previous layout, then assemble
@@ -354,11 +365,20 @@ def bench_mass(args, torch, pcg):
     progress("timing steps")
     ms, wall, kt = time_steps(torch, pcg, step, args.steps, args.warmup)
     progress(f"{ms:.4f} ms per step")
-    flops = cnt * 1152.0     # dense 8x8 node pairs x 9 components x 2 flops
-    roof = roofline_entry(kt, "mass_mfma", flops_per_launch=flops)
-    if roof:
-        roof["traffic"] = measured_traffic("mass_mfma", "mass_64_ppc64")
     mbytes = M.numel() * 4
+    kname = "mass_scalar_mfma" if scalar else "mass_mfma"
+    wname = "mass_scalar_64_ppc64" if scalar else "mass_64_ppc64"
+    # per particle: 8x8 node pairs x 2 flops (scalar) or x 9 components x 2 flops
+    flops = cnt * (128.0 if scalar else 1152.0)
+    # algorithmic HBM bytes: the particle values once (x, q, w; tensor: + B,
+    # beta) and every row of M read and written once
+    pbytes = 20 if scalar else 36
+    if scalar:
+        roof = roofline_entry(kt, kname, bytes_per_launch=cnt * pbytes + 2 * mbytes)
+    else:
+        roof = roofline_entry(kt, kname, flops_per_launch=flops)
+    if roof:
+        roof["traffic"] = measured_traffic(kname, wname)
     kernels = {nm: dict(avg_us=round(kk["avg_us"], 2),
                         launches_per_step=kk["launches"] / args.steps) for nm, kk in kt.items()}
     extra = {}
@@ -369,32 +389,51 @@ def bench_mass(args, torch, pcg):
     extra["cold_cell_sort_ms"] = round(time_plain(torch, lambda: pcg.pcg_tile_sort(
         3, n, 1, 1, x, shuffled, outs=cur, perm=perm, sorted_keys=keys, tile_offsets=off0,
         workspace=sws), 3), 4)
-    if "mass_mfma" in kt:
-        sec = kt["mass_mfma"]["avg_us"] * 1e-6
-        hbm = (cnt * 36 + 2 * mbytes) / sec / 1e9
+    if kname in kt and not scalar:
+        sec = kt[kname]["avg_us"] * 1e-6
+        hbm = (cnt * pbytes + 2 * mbytes) / sec / 1e9
         extra["mass_hbm_roofline"] = dict(bound="hbm", achieved=round(hbm, 1), peak=HBM_PEAK_GBS,
                                           unit="GB/s", frac=round(hbm / HBM_PEAK_GBS, 4))
+    if kname in kt and scalar:
+        tf = flops / (kt[kname]["avg_us"] * 1e-6) / 1e12
+        extra["mass_mfma_roofline"] = dict(bound="mfma", achieved=round(tf, 2),
+                                           peak=MFMA_FP32_PEAK_TFLOPS, unit="TFLOP/s",
+                                           frac=round(tf / MFMA_FP32_PEAK_TFLOPS, 4))
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
 
         progress("timing the oracle on the host")
+
+        def run_oracle(m):
+            if scalar:
+                oracle.mass_matrix_scalar(n, [a[:m] for a in wl.x], wl.q[:m], wl.w[:m])
+            else:
+                oracle.mass_matrix(n, [a[:m] for a in wl.x], [b[:m] for b in wl.B], wl.q[:m],
+                                   wl.w[:m], wl.beta[:m])
+
         m = 1 << 20
         t0 = time.perf_counter()
-        oracle.mass_matrix(n, [a[:m] for a in wl.x], [b[:m] for b in wl.B], wl.q[:m], wl.w[:m],
-                           wl.beta[:m])
+        run_oracle(m)
         per = (time.perf_counter() - t0) / m
         m2 = int(min(cnt, max(m, args.cpu_seconds / per)))
         t0 = time.perf_counter()
-        oracle.mass_matrix(n, [a[:m2] for a in wl.x], [b[:m2] for b in wl.B], wl.q[:m2],
-                           wl.w[:m2], wl.beta[:m2])
+        run_oracle(m2)
         sec = time.perf_counter() - t0
         cpu = dict(value=round(m2 / sec, 1), unit="particles/s", cores=1, kind="oracle",
                    sample=f"first {m2} of {cnt} particles: fp64 per-particle outer products, "
                           f"{sec:.1f} s, 1 thread")
-    config = dict(workload="ECSIM 3-D CIC mass matrix 64^3, 64 ppc (cell sort + MFMA assembly)",
-                  particles=cnt, grid=n,
-                  step="zero M + cell re-sort from the previous layout + MFMA assembly")
+    if scalar:
+        config = dict(workload="scalar 3-D CIC mass matrix (coefficient q w) 64^3, 64 ppc "
+                               "(cell sort + MFMA assembly)",
+                      particles=cnt, grid=n,
+                      step="zero M + cell re-sort of x, q, w from the previous layout + "
+                           "scalar MFMA assembly")
+    else:
+        config = dict(workload="ECSIM 3-D CIC mass matrix 64^3, 64 ppc (cell sort + MFMA "
+                               "assembly)",
+                      particles=cnt, grid=n,
+                      step="zero M + cell re-sort from the previous layout + MFMA assembly")
     return dict(value=cnt / (ms * 1e-3), ms=ms, wall=wall, dtype="f32", config=config,
                 roofline=roof, kernels=kernels, extra=extra, cpu=cpu, unit="particles/s")
 
@@ -456,6 +495,8 @@ def main():
         r = bench_deposit(args, torch, pcg, args.workload)
     elif args.workload == "mass_64_ppc64":
         r = bench_mass(args, torch, pcg)
+    elif args.workload == "mass_scalar_64_ppc64":
+        r = bench_mass(args, torch, pcg, scalar=True)
     else:
         r = bench_sweep(args, torch, pcg)
     line = {

@@ -236,6 +236,23 @@ pcg_status assemble_mass_matrix(const pcg_grid *grid, const pcg_particles *parti
                                 const pcg_tile *cells, int32_t variant, float *M,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
+/* Scalar mass matrix ([MM] §2.1: Eq.(6) with the scalar coefficient
+ * s_p = q_p w_p in place of the tensor q_p w_p alpha_p, one value per node pair,
+ * the form a mass matrix takes in MPM):
+ *   M_{g, g+o} += q_p w_p W_{pg} W_{p,g+o}
+ * over every ordered pair of the 8 CIC support nodes of every particle.
+ * 3-D, CIC, every n_k >= 3; no field is read.
+ * M: device fp32 [n_z][n_y][n_x][27], accumulated; offsets numbered as for
+ *   assemble_mass_matrix.
+ * cells, variant, workspace, stream: as for assemble_mass_matrix, with the same
+ *   column assembly (each row of M read and written once), stray and tail
+ *   handling, and the same workspace size (pcg_mass_workspace_bytes()).
+ *   PCG_MASS_MFMA takes eight particles per 16x16x4 fp32 product.
+ * Errors: as for assemble_mass_matrix (B and beta are not taken). */
+pcg_status assemble_mass_matrix_scalar(const pcg_grid *grid, const pcg_particles *particles,
+                                       const pcg_tile *cells, int32_t variant, float *M,
+                                       void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* 1-D windowed sweep  ([CS] "The problem", "Code")                          */
 /* ------------------------------------------------------------------------ */

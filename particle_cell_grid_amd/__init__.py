@@ -68,6 +68,9 @@ _lib.pcg_mass_workspace_bytes.restype = C.c_size_t
 _lib.assemble_mass_matrix.argtypes = [_P(Grid), _P(Particles), C.c_void_p, C.c_void_p, _P(Tile),
                                       C.c_int32, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
 _lib.assemble_mass_matrix.restype = C.c_int32
+_lib.assemble_mass_matrix_scalar.argtypes = [_P(Grid), _P(Particles), _P(Tile), C.c_int32,
+                                             C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+_lib.assemble_mass_matrix_scalar.restype = C.c_int32
 _lib.deposit_sweep1d.argtypes = [C.c_int32, C.c_int64, C.c_void_p, C.c_void_p, C.c_int32,
                                  C.c_double, C.c_double, C.c_void_p, C.c_void_p]
 _lib.deposit_sweep1d.restype = C.c_int32
@@ -284,6 +287,25 @@ def assemble_mass_matrix(n: Sequence[int], x: List[torch.Tensor], B: List[torch.
                                    C.byref(tile) if tile is not None else None, int(variant),
                                    _ptr(M), _ptr(workspace), wsb, _stream())
     _check(st, "assemble_mass_matrix")
+    return M
+
+
+def assemble_mass_matrix_scalar(n: Sequence[int], x: List[torch.Tensor], q: torch.Tensor,
+                                w: torch.Tensor, M: torch.Tensor, cells: Optional[Layout] = None,
+                                variant: int = PCG_MASS_AUTO,
+                                workspace: Optional[torch.Tensor] = None):
+    """M[nz, ny, nx, 27] (fp32) += the scalar CIC mass matrix (coefficient q w).
+    Layout, variants and workspace as for assemble_mass_matrix."""
+    g = make_grid(3, n)
+    P = _particles(q.numel(), x, None, q, w)
+    tile = cells.to_c() if cells is not None else None
+    if cells is not None and workspace is None:
+        workspace = torch.empty(pcg_mass_workspace_bytes(n), dtype=torch.uint8, device=M.device)
+    wsb = int(workspace.numel()) if workspace is not None else 0
+    st = _lib.assemble_mass_matrix_scalar(C.byref(g), C.byref(P),
+                                          C.byref(tile) if tile is not None else None,
+                                          int(variant), _ptr(M), _ptr(workspace), wsb, _stream())
+    _check(st, "assemble_mass_matrix_scalar")
     return M
 
 

@@ -29,6 +29,15 @@
 // from the matrix cores or from per-lane FMAs) and FLAT (one thread per
 // particle, alpha computed directly, 576 global atomics -- also used for the
 // unsorted tail and for particles found in a cell slice they do not lie in).
+//
+// Scalar mass matrix ([MM] §2.1, the scalar case of Eq.(6): s_p = q_p w_p, one
+// value per node pair, as for a mass matrix in MPM): the same kernels with
+// SC = true.  B and beta are not read, u = (1, 0, 0, 0), only T_00 is formed
+// and a node row of M holds 27 floats.  On the matrix cores one 16x16x4 product
+// then takes eight particles: rows 0-7 of both operands carry the nodes of
+// particles 8i + k and rows 8-15 those of particles 8i + 4 + k (k = 0..3), so
+// the two diagonal 8x8 blocks of the result are T_00 of the two groups (the
+// off-diagonal blocks mix particles and are dropped).
 #include <algorithm>
 
 #include "common.hpp"
@@ -64,6 +73,16 @@ struct RawParticle {
     float x[3], B[3], q, w, beta;
 };
 
+// Floats per node row of M: 27 offsets x 9 tensor components, or 27 (scalar).
+template <bool SC>
+constexpr int row_floats()
+{
+    return SC ? 27 : 27 * 9;
+}
+
+// The scalar matrix reads no field: B and beta are zero constants, so omega,
+// u = (1, 0, 0, 0) and c = q w fold at compile time.
+template <bool SC>
 __device__ inline RawParticle load_raw(const MassArgs &m, int64_t p)
 {
     // particle counts are below 2^30, so a 32-bit byte offset from each array's
@@ -76,21 +95,33 @@ __device__ inline RawParticle load_raw(const MassArgs &m, int64_t p)
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
         r.x[k] = at(m.x[k]);
-        r.B[k] = at(m.B[k]);
+        r.B[k] = SC ? 0.0f : at(m.B[k]);
     }
     r.q = at(m.q);
     r.w = at(m.w);
-    r.beta = at(m.beta);
+    r.beta = SC ? 0.0f : at(m.beta);
     return r;
 }
 
 // An empty use of every value of a particle: the compiler waits for its
 // loads here.
+template <bool SC>
 __device__ __attribute__((always_inline)) inline void consume(const RawParticle &r)
 {
-    asm volatile("" ::"v"(r.x[0]), "v"(r.x[1]), "v"(r.x[2]), "v"(r.B[0]), "v"(r.B[1]),
-                 "v"(r.B[2]), "v"(r.q), "v"(r.w), "v"(r.beta));
+    if constexpr (SC)
+        asm volatile("" ::"v"(r.x[0]), "v"(r.x[1]), "v"(r.x[2]), "v"(r.q), "v"(r.w));
+    else
+        asm volatile("" ::"v"(r.x[0]), "v"(r.x[1]), "v"(r.x[2]), "v"(r.B[0]), "v"(r.B[1]),
+                     "v"(r.B[2]), "v"(r.q), "v"(r.w), "v"(r.beta));
 }
+
+// i in [0, 2n) taken into [0, n): the node indices here are at most n (a
+// coordinate clamped to [0, n], or the cell's upper neighbour), so one select
+// replaces the general periodic wrap.
+__device__ inline int wrap_once(int i, int n) { return i >= n ? i - n : i; }
+
+// i in [-1, n] (a cell next to a column, whose nodes lie in [0, n)) wrapped.
+__device__ inline int wrap_near(int i, int n) { return i < 0 ? i + n : wrap_once(i, n); }
 
 __device__ inline Particle make_particle(const MassArgs &m, const RawParticle &r)
 {
@@ -101,7 +132,7 @@ __device__ inline Particle make_particle(const MassArgs &m, const RawParticle &r
         const float x = clamp_coord(r.x[k], m.nf[k]);
         const float fl = floorf(x);
         const float xi = x - fl;
-        P.base[k] = wrap_index((int)fl, m.n[k]);
+        P.base[k] = wrap_once((int)fl, m.n[k]);
         wx[k][0] = 1.0f - xi;
         wx[k][1] = xi;
     }
@@ -118,16 +149,17 @@ __device__ inline Particle make_particle(const MassArgs &m, const RawParticle &r
     return P;
 }
 
+template <bool SC>
 __device__ inline Particle load_particle(const MassArgs &m, int64_t p)
 {
-    return make_particle(m, load_raw(m, p));
+    return make_particle(m, load_raw<SC>(m, p));
 }
 
 __device__ inline int64_t node_index(const MassArgs &m, const int *base, int a)
 {
-    const int gx = wrap_index(base[0] + (a & 1), m.n[0]);
-    const int gy = wrap_index(base[1] + ((a >> 1) & 1), m.n[1]);
-    const int gz = wrap_index(base[2] + (a >> 2), m.n[2]);
+    const int gx = wrap_once(base[0] + (a & 1), m.n[0]);
+    const int gy = wrap_once(base[1] + ((a >> 1) & 1), m.n[1]);
+    const int gz = wrap_once(base[2] + (a >> 2), m.n[2]);
     return gx + (int64_t)m.n[0] * (gy + (int64_t)m.n[1] * gz);
 }
 
@@ -151,7 +183,8 @@ __device__ inline void moments_to_block(const float t[4][4], float *out)
     out[8] = t[0][0] + t[3][3];   // zz
 }
 
-// The particle's whole 8x8x9 contribution with global atomics.
+// The particle's whole 8x8x9 (scalar: 8x8) contribution with global atomics.
+template <bool SC>
 __device__ inline void deposit_particle_global(const MassArgs &m, const Particle &P)
 {
     float t[4][4];
@@ -159,6 +192,16 @@ __device__ inline void deposit_particle_global(const MassArgs &m, const Particle
 #pragma unroll
     for (int a = 0; a < 8; ++a)
         g[a] = node_index(m, P.base, a);
+    if constexpr (SC) {
+        for (int a = 0; a < 8; ++a) {
+            const float ca = P.c * P.W[a];
+            float *row = m.M + (size_t)g[a] * 27;
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+                atomic_add_f32(&row[offset_index(a, b)], ca * P.W[b]);
+        }
+        return;
+    }
     for (int a = 0; a < 8; ++a) {
         for (int b = 0; b < 8; ++b) {
             const float wab = P.c * P.W[a] * P.W[b];
@@ -177,11 +220,12 @@ __device__ inline void deposit_particle_global(const MassArgs &m, const Particle
     }
 }
 
+template <bool SC>
 __global__ __launch_bounds__(256) void k_mass_flat(MassArgs m, int64_t begin, int64_t end)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t p = begin + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < end; p += stride)
-        deposit_particle_global(m, load_particle(m, p));
+        deposit_particle_global<SC>(m, load_particle<SC>(m, p));
 }
 
 __device__ inline void cell_coords(const MassArgs &m, uint32_t cell, int *cc)
@@ -212,10 +256,21 @@ __device__ inline void cell_coords(const MassArgs &m, uint32_t cell, int *cc)
 #define PCG_COL_Y 4
 #define PCG_COL_Z 16
 #endif
+#ifndef PCG_COL_Z_SCALAR
+#define PCG_COL_Z_SCALAR 8
+#endif
 constexpr int COL_X = PCG_COL_X, COL_Y = PCG_COL_Y, COL_Z = PCG_COL_Z;
 constexpr int COL_WAVES = 4;
 constexpr int COL_NODES = COL_X * COL_Y;
-constexpr int ROW = 27 * 9;  // floats per node row of M
+
+// Column height: the scalar matrix does little work per cell, so its
+// work-groups wait on loads at every phase; a lower column takes fewer
+// phases per work-group and spreads the grid over more of them.
+template <bool SC>
+constexpr int col_z()
+{
+    return SC ? PCG_COL_Z_SCALAR : COL_Z;
+}
 
 // LDS staging of one 64-particle batch of a cell, per wave; reused for the
 // 32 x 32 moment tile once the batches are done.
@@ -229,9 +284,10 @@ union WaveScratch {
     float Tm[32][33];
 };
 
+template <bool SC>
 constexpr size_t column_lds_bytes()
 {
-    return sizeof(float) * 2 * COL_NODES * ROW + sizeof(WaveScratch) * COL_WAVES;
+    return sizeof(float) * 2 * COL_NODES * row_floats<SC>() + sizeof(WaveScratch) * COL_WAVES;
 }
 
 // Orders this wave's earlier LDS accesses before its later ones (lanes exchange
@@ -246,39 +302,38 @@ __device__ inline void wave_sync()
 // Stages one particle (raw values, valid = the slot is inside the cell's slice)
 // into the lane's row.  A particle that lies in another cell (a stale layout)
 // is staged as zero and reported through *stray: the follow-up pass deposits it.
+template <bool SC>
 __device__ inline void stage_raw(const MassArgs &m, Stage &s, int lane, const RawParticle &r,
                                  bool valid, const int *cell, bool *stray)
 {
-    float W[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    float u[4] = {0, 0, 0, 0};
-    float c = 0.0f;
-    if (valid) {
-        const Particle P = make_particle(m, r);
-        if (P.base[0] == cell[0] && P.base[1] == cell[1] && P.base[2] == cell[2]) {
+    // computed for every lane (an empty slot holds zeros), then selected:
+    // no divergent branches
+    const Particle P = make_particle(m, r);
+    const bool home = P.base[0] == cell[0] && P.base[1] == cell[1] && P.base[2] == cell[2];
+    const bool take = valid && home;
+    *stray = *stray || (valid && !home);
+    float W[8], u[4];
 #pragma unroll
-            for (int a = 0; a < 8; ++a)
-                W[a] = P.W[a];
+    for (int a = 0; a < 8; ++a)
+        W[a] = take ? P.W[a] : 0.0f;
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                u[k] = P.u[k];
-            c = P.c;
-        } else {
-            *stray = true;
-        }
-    }
+    for (int k = 0; k < 4; ++k)
+        u[k] = take ? P.u[k] : 0.0f;
+    const float c = take ? P.c : 0.0f;
     float4 *w4 = reinterpret_cast<float4 *>(s.W[lane]);
     w4[0] = make_float4(W[0], W[1], W[2], W[3]);
     w4[1] = make_float4(W[4], W[5], W[6], W[7]);
-    *reinterpret_cast<float4 *>(s.u[lane]) = make_float4(u[0], u[2], u[1], u[3]);
+    if constexpr (!SC)
+        *reinterpret_cast<float4 *>(s.u[lane]) = make_float4(u[0], u[2], u[1], u[3]);
     s.c[lane] = c;
 }
 
 // One wave: the ten moments of cell `cell` (wrapped coordinates), whose slice
 // is [lo, hi), for this lane's node pair (a, b) = (lane / 8, lane % 8):
-// t[k][l] for k <= l.  `first` holds the lane's particle of the first batch
-// (slot lo + lane), loaded ahead by the caller; later batches (cells of more
-// than 64 particles) are loaded here.
-template <bool MFMA>
+// t[k][l] for k <= l (scalar: t[0][0] only).  `first` holds the lane's
+// particle of the first batch (slot lo + lane), loaded ahead by the caller;
+// later batches (cells of more than 64 particles) are loaded here.
+template <bool MFMA, bool SC>
 __device__ inline void cell_moments(const MassArgs &m, WaveScratch &ws, int lane, const int *cell,
                                     int64_t lo, int64_t hi, const RawParticle &first, bool *stray,
                                     float t[4][4])
@@ -298,10 +353,37 @@ __device__ inline void cell_moments(const MassArgs &m, WaveScratch &ws, int lane
     floatx4 acc00 = {0, 0, 0, 0}, acc01 = {0, 0, 0, 0}, acc11 = {0, 0, 0, 0};
     auto batch = [&](const RawParticle &rp, int64_t base) {
         wave_sync();
-        stage_raw(m, ws.s, lane, rp, base + lane < hi, cell, stray);
+        stage_raw<SC>(m, ws.s, lane, rp, base + lane < hi, cell, stray);
         wave_sync();
         const int nb = (int)std::min<int64_t>(64, hi - base);
-        if (MFMA) {
+        if constexpr (MFMA && SC) {
+            // eight particles per product: row half khalf takes particle
+            // 8 i + 4 khalf + kk (staged rows past the slice are zero)
+            auto slot = [&](int i) { return 8 * i + 4 * khalf + kk; };
+            if (nb == 64) {
+                float wa[8], cp[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    wa[i] = ws.s.W[slot(i)][a];
+                    cp[i] = ws.s.c[slot(i)];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    acc00 = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[i], cp[i] * wa[i], acc00, 0, 0,
+                                                                 0);
+            } else {
+                const int batches = (nb + 7) >> 3;
+                for (int bt = 0; bt < batches; ++bt) {
+                    const float wa = ws.s.W[slot(bt)][a];
+                    acc00 = __builtin_amdgcn_mfma_f32_16x16x4f32(wa, ws.s.c[slot(bt)] * wa, acc00,
+                                                                 0, 0, 0);
+                }
+            }
+        } else if constexpr (SC) {
+            for (int q = 0; q < nb; ++q)
+                t[0][0] += ws.s.c[q] * ws.s.W[q][pa] * ws.s.W[q][pb];
+        } else if constexpr (MFMA) {
             // one 4-particle batch: operands from the staged rows, three MFMAs
             auto mfma_batch = [&](float wa, float2 uu, float cp) {
                 const float a0 = uu.x * wa;  // u_k W_a      (k = khalf)
@@ -357,12 +439,20 @@ __device__ inline void cell_moments(const MassArgs &m, WaveScratch &ws, int lane
     // cells of more than 64 particles: the later batches load here
     for (int64_t base = lo + 64; base < hi; base += 64) {
         // clamped load, waited for at once: the wait stays on this rare path
-        const RawParticle rp = load_raw(m, std::min<int64_t>(base + lane, hi - 1));
-        consume(rp);
+        const RawParticle rp = load_raw<SC>(m, std::min<int64_t>(base + lane, hi - 1));
+        consume<SC>(rp);
         batch(rp, base);
     }
     wave_sync();
-    if (MFMA) {
+    if constexpr (MFMA && SC) {
+        // the two diagonal 8x8 blocks of the accumulator, summed
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            ws.Tm[4 * kk + i][r] = acc00[i];
+        wave_sync();
+        t[0][0] = ws.Tm[pa][pb] + ws.Tm[8 + pa][8 + pb];
+        wave_sync();
+    } else if constexpr (MFMA) {
         // accumulator layout: lane holds D[4*(lane/16) + i][lane % 16], i = 0..3
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -383,7 +473,11 @@ __device__ inline void cell_moments(const MassArgs &m, WaveScratch &ws, int lane
 
 // Values of one y row of a column plane (COL_X nodes, contiguous in M) each
 // thread adds to M after a layer.
-constexpr int COL_ROW_PER_THREAD = (COL_X * ROW + COL_WAVES * WAVE - 1) / (COL_WAVES * WAVE);
+template <bool SC>
+constexpr int col_row_per_thread()
+{
+    return (COL_X * row_floats<SC>() + COL_WAVES * WAVE - 1) / (COL_WAVES * WAVE);
+}
 
 struct ColumnGeom {
     int ncol[3];  // columns per axis
@@ -428,7 +522,7 @@ __device__ inline bool phase_cell(const MassArgs &m, const ColumnShape &c, int p
     li[2] = iz;
 #pragma unroll
     for (int a = 0; a < 3; ++a)
-        cell[a] = wrap_index(c.first[a] - 1 + li[a], m.n[a]);
+        cell[a] = wrap_near(c.first[a] - 1 + li[a], m.n[a]);
     return true;
 }
 
@@ -467,33 +561,36 @@ struct PhaseRaw {
     RawParticle r0, r1, r2, r3;
 };
 
+template <bool SC>
 __device__ inline RawParticle load_slot(const MassArgs &m, uint32_t offv, int k)
 {
     int64_t lo, hi;
     slot_bounds(m, offv, k, lo, hi);
     RawParticle r{};
     if (lo + lane_id() < hi)
-        r = load_raw(m, lo + lane_id());
+        r = load_raw<SC>(m, lo + lane_id());
     return r;
 }
 
+template <bool SC>
 __device__ inline void load_phase(const MassArgs &m, uint32_t offv, PhaseRaw &pr)
 {
-    pr.r0 = load_slot(m, offv, 0);
-    pr.r1 = COL_SLOTS > 1 ? load_slot(m, offv, 1) : RawParticle{};
-    pr.r2 = COL_SLOTS > 2 ? load_slot(m, offv, 2) : RawParticle{};
-    pr.r3 = COL_SLOTS > 3 ? load_slot(m, offv, 3) : RawParticle{};
+    pr.r0 = load_slot<SC>(m, offv, 0);
+    pr.r1 = COL_SLOTS > 1 ? load_slot<SC>(m, offv, 1) : RawParticle{};
+    pr.r2 = COL_SLOTS > 2 ? load_slot<SC>(m, offv, 2) : RawParticle{};
+    pr.r3 = COL_SLOTS > 3 ? load_slot<SC>(m, offv, 3) : RawParticle{};
 }
 
+template <bool SC>
 __device__ __attribute__((always_inline)) inline void consume(const PhaseRaw &p)
 {
-    consume(p.r0);
+    consume<SC>(p.r0);
     if (COL_SLOTS > 1)
-        consume(p.r1);
+        consume<SC>(p.r1);
     if (COL_SLOTS > 2)
-        consume(p.r2);
+        consume<SC>(p.r2);
     if (COL_SLOTS > 3)
-        consume(p.r3);
+        consume<SC>(p.r3);
 }
 
 // Slot k (uniform) of a phase, selected field by field.
@@ -516,9 +613,11 @@ __device__ inline RawParticle pick(const PhaseRaw &p, int k)
     return r;
 }
 
-template <bool MFMA>
+template <bool MFMA, bool SC>
 __global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, ColumnGeom cg)
 {
+    constexpr int ROW = row_floats<SC>();
+    constexpr int COL_ROW_PER_THREAD = col_row_per_thread<SC>();
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     float *planes = reinterpret_cast<float *>(smem);  // [2][COL_NODES][ROW]
     WaveScratch *scratch = reinterpret_cast<WaveScratch *>(smem + sizeof(float) * 2 * COL_NODES * ROW);
@@ -541,7 +640,7 @@ __global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, Co
         const int idx[3] = {(int)(work % (uint32_t)cg.ncol[0]),
                             (int)((work / (uint32_t)cg.ncol[0]) % (uint32_t)cg.ncol[1]),
                             (int)(work / ((uint32_t)cg.ncol[0] * (uint32_t)cg.ncol[1]))};
-        const int edge[3] = {COL_X, COL_Y, COL_Z};
+        const int edge[3] = {COL_X, COL_Y, col_z<SC>()};
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
             cs.first[k] = idx[k] * edge[k];
@@ -560,10 +659,10 @@ __global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, Co
     uint32_t off_next = phase_offsets(m, cs, 1, wave);
     PhaseRaw cur, nxt;
     uint32_t off_cur = phase_offsets(m, cs, 0, wave);
-    load_phase(m, off_cur, cur);
+    load_phase<SC>(m, off_cur, cur);
     __syncthreads();
 
-    consume(cur);
+    consume<SC>(cur);
     asm volatile("" ::"v"(off_cur), "v"(off_next));
     bool stray = false;
     const int pa = lane >> 3, pb = lane & 7;
@@ -571,7 +670,7 @@ __global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, Co
     const int o = offset_index(pa, pb);
     for (int ph = 0; ph < nphase; ++ph) {
         const int iz = ph >> 2;
-        load_phase(m, off_next, nxt);
+        load_phase<SC>(m, off_next, nxt);
         const uint32_t off_after = phase_offsets(m, cs, ph + 2, wave);
         // the compiler must not sink these reads to their use
         asm volatile("" ::: "memory");
@@ -586,20 +685,29 @@ __global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, Co
             slot_bounds(m, off_cur, k, lo, hi);
             bool st = false;
             float t[4][4];
-            cell_moments<MFMA>(m, ws, lane, cell, lo, hi, pick(cur, k), &st, t);
+            cell_moments<MFMA, SC>(m, ws, lane, cell, lo, hi, pick(cur, k), &st, t);
             // a cell's stray particles are reported by the column holding its
             // first node (each cell has exactly one such column)
             if (li[0] >= 1 && li[1] >= 1 && li[2] >= 1)
                 stray |= st;
             const int lx = li[0] - 1 + ax, ly = li[1] - 1 + ay;
             if (lx >= 0 && lx < BX && ly >= 0 && ly < BY && lz >= 0 && lz < BZ) {
-                float blk[9];
-                moments_to_block(t, blk);
-                float *row =
-                    planes + ((size_t)(lz & 1) * COL_NODES + ly * COL_X + lx) * ROW + o * 9;
+                // the product is kept out of the address add: fused, it becomes
+                // a 64-bit multiply-add whose unused high addend can share a
+                // register with an in-flight load, and then waits for every
+                // outstanding load
+                uint32_t e = ((lz & 1) * COL_NODES + ly * COL_X + lx) * ROW;
+                asm("" : "+v"(e));
+                float *node = planes + e;
+                if constexpr (SC) {
+                    node[o] += t[0][0];
+                } else {
+                    float blk[9];
+                    moments_to_block(t, blk);
 #pragma unroll
-                for (int ij = 0; ij < 9; ++ij)
-                    row[ij] += blk[ij];
+                    for (int ij = 0; ij < 9; ++ij)
+                        node[o * 9 + ij] += blk[ij];
+                }
             }
         }
         // the next phase's operands (loaded during this one) are taken over and
@@ -608,7 +716,7 @@ __global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, Co
         cur = nxt;
         off_cur = off_next;
         off_next = off_after;
-        consume(cur);
+        consume<SC>(cur);
         asm volatile("" ::"v"(off_cur), "v"(off_next));
         __syncthreads();
 
@@ -663,6 +771,7 @@ __global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, Co
 // Follow-up of the column kernel, run only when it found stray particles: each
 // thread walks one cell's slice and deposits the particles that lie elsewhere
 // with global atomics.
+template <bool SC>
 __global__ __launch_bounds__(256) void k_mass_strays(MassArgs m, const uint32_t *flag)
 {
     if (*flag == 0u)
@@ -674,9 +783,9 @@ __global__ __launch_bounds__(256) void k_mass_strays(MassArgs m, const uint32_t 
         const int64_t lo = std::min<int64_t>(m.cell_offsets[cid], m.n_part);
         const int64_t hi = std::min<int64_t>(m.cell_offsets[cid + 1], m.n_part);
         for (int64_t p = lo; p < hi; ++p) {
-            const Particle P = load_particle(m, p);
+            const Particle P = load_particle<SC>(m, p);
             if (P.base[0] != cc[0] || P.base[1] != cc[1] || P.base[2] != cc[2])
-                deposit_particle_global(m, P);
+                deposit_particle_global<SC>(m, P);
         }
     }
 }
@@ -694,33 +803,27 @@ namespace {
 // particles), padded to 256 bytes.
 constexpr size_t MASS_WORKSPACE = 256;
 
-template <bool MFMA>
+template <bool MFMA, bool SC>
 pcg_status launch_column(const MassArgs &m, const ColumnGeom &cg, hipStream_t st)
 {
-    auto kern = k_mass_column<MFMA>;
-    const size_t lds = column_lds_bytes();
+    auto kern = k_mass_column<MFMA, SC>;
+    const size_t lds = column_lds_bytes<SC>();
     if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)lds) != hipSuccess)
-        return fail(PCG_EHIP, "assemble_mass_matrix: cannot raise dynamic LDS to %zu bytes", lds);
+        return fail(PCG_EHIP, "mass matrix: cannot raise dynamic LDS to %zu bytes", lds);
     const uint32_t blocks = (cg.nwork + 7) / 8 * 8;
-    return launch(MFMA ? "mass_mfma" : "mass_valu", kern, dim3(blocks), dim3(COL_WAVES * WAVE),
-                  lds, st, m, cg);
+    const char *name = SC ? (MFMA ? "mass_scalar_mfma" : "mass_scalar_valu")
+                          : (MFMA ? "mass_mfma" : "mass_valu");
+    return launch(name, kern, dim3(blocks), dim3(COL_WAVES * WAVE), lds, st, m, cg);
 }
 
-}  // namespace
-
-extern "C" size_t pcg_mass_workspace_bytes(const pcg_grid *grid)
+// Both entry points: the tensor matrix (B and beta given) or the scalar one.
+template <bool SC>
+pcg_status assemble(const char *who, const pcg_grid *grid, const pcg_particles *particles,
+                    const float *const B[3], const float *beta, const pcg_tile *cells,
+                    int32_t variant, float *M, void *workspace, size_t workspace_bytes,
+                    void *stream)
 {
-    (void)grid;
-    return MASS_WORKSPACE;
-}
-
-extern "C" pcg_status assemble_mass_matrix(const pcg_grid *grid, const pcg_particles *particles,
-                                           const float *const B[3], const float *beta,
-                                           const pcg_tile *cells, int32_t variant, float *M,
-                                           void *workspace, size_t workspace_bytes, void *stream)
-{
-    const char *who = "assemble_mass_matrix";
     clear_error();
     PCG_TRY(check_grid(grid, who));
     if (grid->dim != 3)
@@ -738,21 +841,22 @@ extern "C" pcg_status assemble_mass_matrix(const pcg_grid *grid, const pcg_parti
         return fail(PCG_EINVAL, "%s: count %lld outside [0, 2^30)", who, (long long)count);
     if (count > 0) {
         for (int k = 0; k < 3; ++k)
-            if (!particles->x[k] || !B || !B[k])
-                return fail(PCG_EINVAL, "%s: x[%d] or B[%d] is NULL", who, k, k);
-        if (!particles->q || !particles->w || !beta)
-            return fail(PCG_EINVAL, "%s: q, w or beta is NULL", who);
+            if (!particles->x[k] || (!SC && (!B || !B[k])))
+                return fail(PCG_EINVAL, SC ? "%s: x[%d] is NULL" : "%s: x[%d] or B[%d] is NULL",
+                            who, k, k);
+        if (!particles->q || !particles->w || (!SC && !beta))
+            return fail(PCG_EINVAL, SC ? "%s: q or w is NULL" : "%s: q, w or beta is NULL", who);
     }
     MassArgs m{};
     for (int k = 0; k < 3; ++k) {
         m.n[k] = grid->n[k];
         m.nf[k] = (float)grid->n[k];
         m.x[k] = particles->x[k];
-        m.B[k] = B ? B[k] : nullptr;
+        m.B[k] = !SC && B ? B[k] : nullptr;
     }
     m.q = particles->q;
     m.w = particles->w;
-    m.beta = beta;
+    m.beta = SC ? nullptr : beta;
     m.M = M;
     m.ncells = (uint32_t)((int64_t)grid->n[0] * grid->n[1] * grid->n[2]);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -763,8 +867,8 @@ extern "C" pcg_status assemble_mass_matrix(const pcg_grid *grid, const pcg_parti
             return PCG_OK;
         const int64_t blocks =
             std::min<int64_t>((end - begin + 255) / 256, (int64_t)device_cus() * 32);
-        return launch("mass_flat", k_mass_flat, dim3((unsigned)blocks), dim3(256), 0, st, m, begin,
-                      end);
+        return launch(SC ? "mass_scalar_flat" : "mass_flat", k_mass_flat<SC>,
+                      dim3((unsigned)blocks), dim3(256), 0, st, m, begin, end);
     };
     if (variant == PCG_MASS_FLAT || (!cells && variant == PCG_MASS_AUTO))
         return flat(0, count);
@@ -788,20 +892,48 @@ extern "C" pcg_status assemble_mass_matrix(const pcg_grid *grid, const pcg_parti
     ColumnGeom cg{};
     cg.ncol[0] = (grid->n[0] + COL_X - 1) / COL_X;
     cg.ncol[1] = (grid->n[1] + COL_Y - 1) / COL_Y;
-    cg.ncol[2] = (grid->n[2] + COL_Z - 1) / COL_Z;
+    cg.ncol[2] = (grid->n[2] + col_z<SC>() - 1) / col_z<SC>();
     cg.nwork = (uint32_t)cg.ncol[0] * cg.ncol[1] * cg.ncol[2];
     cg.stray_flag = static_cast<uint32_t *>(workspace);
     if (m.n_part > 0) {
         PCG_TRY(launch("mass_clear_flag", k_mass_clear_flag, dim3(1), dim3(1), 0, st,
                        cg.stray_flag));
         if (variant == PCG_MASS_VALU)
-            PCG_TRY(launch_column<false>(m, cg, st));
+            PCG_TRY((launch_column<false, SC>(m, cg, st)));
         else
-            PCG_TRY(launch_column<true>(m, cg, st));
+            PCG_TRY((launch_column<true, SC>(m, cg, st)));
         const int64_t sblocks =
             std::min<int64_t>((m.ncells + 255) / 256, (int64_t)device_cus() * 8);
-        PCG_TRY(launch("mass_strays", k_mass_strays, dim3((unsigned)sblocks), dim3(256), 0, st, m,
+        PCG_TRY(launch(SC ? "mass_scalar_strays" : "mass_strays", k_mass_strays<SC>,
+                       dim3((unsigned)sblocks), dim3(256), 0, st, m,
                        (const uint32_t *)cg.stray_flag));
     }
     return flat(cells->n_partitioned, count);
+}
+
+}  // namespace
+
+extern "C" size_t pcg_mass_workspace_bytes(const pcg_grid *grid)
+{
+    (void)grid;
+    return MASS_WORKSPACE;
+}
+
+extern "C" pcg_status assemble_mass_matrix(const pcg_grid *grid, const pcg_particles *particles,
+                                           const float *const B[3], const float *beta,
+                                           const pcg_tile *cells, int32_t variant, float *M,
+                                           void *workspace, size_t workspace_bytes, void *stream)
+{
+    return assemble<false>("assemble_mass_matrix", grid, particles, B, beta, cells, variant, M,
+                           workspace, workspace_bytes, stream);
+}
+
+extern "C" pcg_status assemble_mass_matrix_scalar(const pcg_grid *grid,
+                                                  const pcg_particles *particles,
+                                                  const pcg_tile *cells, int32_t variant, float *M,
+                                                  void *workspace, size_t workspace_bytes,
+                                                  void *stream)
+{
+    return assemble<true>("assemble_mass_matrix_scalar", grid, particles, nullptr, nullptr, cells,
+                          variant, M, workspace, workspace_bytes, stream);
 }

@@ -53,18 +53,22 @@ def tap_name(kernel):
     """The library's launch names for its kernels (as the benchmark reports them).
     Template arguments tell apart launches of one kernel template: the tiled
     deposit with its regroup flag set is `deposit_regroup`, the column mass
-    kernel on matrix cores is `mass_mfma`."""
+    kernel on matrix cores is `mass_mfma` (`mass_scalar_mfma` for the scalar
+    matrix)."""
     base = kernel.split("<")[0]
     targs = kernel[len(base) + 1:-1].split(",") if "<" in kernel else []
     last = targs[-1].strip() if targs else ""
     if base == "k_deposit_tiled":
         return "deposit_regroup" if last == "true" else "deposit_tiled"
-    if base == "k_mass_column":
-        return "mass_mfma" if last == "true" else "mass_valu"
+    scalar = "mass_scalar_" if base.startswith("k_mass_") and last == "true" else "mass_"
+    if base == "k_mass_column":     # <MFMA, scalar>
+        mfma = targs[0].strip() == "true"
+        return scalar + ("mfma" if mfma else "valu")
+    if base in ("k_mass_flat", "k_mass_strays"):
+        return scalar + base[len("k_mass_"):]
     table = {"k_deposit_flat": "deposit_flat",
              "k_inc_move": "sort_inc_move", "k_inc_count": "sort_inc_count",
-             "k_inc_tiles": "sort_inc_tiles", "k_mass_flat": "mass_flat",
-             "k_mass_strays": "mass_strays",
+             "k_inc_tiles": "sort_inc_tiles",
              "k_permute": "sort_permute", "k_tile_keys": "sort_keys",
              "k_sweep1d": "sweep1d"}
     return table.get(base)

@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["pcg_tile_sort", "pcg_sort_workspace_bytes", "deposit_currents",
               "pcg_deposit_workspace_bytes", "deposit_currents_regroup",
-              "pcg_deposit_regroup_workspace_bytes", "pcg_mass_workspace_bytes", "assemble_mass_matrix", "deposit_sweep1d",
+              "pcg_deposit_regroup_workspace_bytes", "pcg_mass_workspace_bytes", "assemble_mass_matrix",
+              "assemble_mass_matrix_scalar", "deposit_sweep1d",
               "pcg_status_string", "pcg_last_error", "pcg_version", "pcg_timing_enable",
               "pcg_timing_reset", "pcg_timing_read", "pcg_timing_names"]:
         assert n in names
@@ -226,6 +227,28 @@ def test_mass_and_sweep_validation(lib):
     assert call(variant=1, cells=C.byref(c1), ws=FAKE + 8) == EWORKSPACE   # misaligned
     lib.pcg_mass_workspace_bytes.restype = C.c_size_t
     assert lib.pcg_mass_workspace_bytes(g8) >= 4
+    # the scalar matrix: the same checks, without B and beta
+    sm = lib.assemble_mass_matrix_scalar
+    sm.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
+                   C.c_size_t, C.c_void_p]
+
+    def scall(g=g8, variant=0, cells=None, ws=FAKE, wsb=256, p=P, M=FAKE):
+        return sm(g, C.byref(p) if p is not None else None, cells, variant, M, ws, wsb, None)
+
+    assert scall(g=C.byref(grid(2, [8, 8]))) == EUNSUPPORTED
+    assert scall(g=C.byref(grid(3, [8, 2, 8]))) == EINVAL
+    assert scall(variant=-1) == EINVAL
+    assert scall(p=None) == EINVAL
+    assert scall(M=None) == EINVAL
+    assert scall(p=big) == EINVAL
+    nox = particles(100)
+    nox.q = None
+    assert scall(p=nox) == EINVAL
+    assert scall(variant=2) == EINVAL                             # VALU needs cells
+    assert scall(variant=1, cells=C.byref(t)) == EINVAL
+    assert scall(variant=1, cells=C.byref(c1), ws=None) == EWORKSPACE
+    assert scall(variant=1, cells=C.byref(c1), ws=FAKE + 8) == EWORKSPACE
+    assert scall(variant=1, cells=C.byref(Tile(1, 1, 0, 0, 101, FAKE))) == EINVAL  # > count
     sw = lib.deposit_sweep1d
     sw.argtypes = [C.c_int32, C.c_int64, C.c_void_p, C.c_void_p, C.c_int32, C.c_double,
                    C.c_double, C.c_void_p, C.c_void_p]

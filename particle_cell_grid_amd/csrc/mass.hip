@@ -504,26 +504,50 @@ __device__ inline int colour_cells(const ColumnShape &c, int colour, int &nx)
 constexpr int COL_SLOTS =
     ((COL_X + 2) / 2 * ((COL_Y + 2) / 2) + COL_WAVES - 1) / COL_WAVES;
 
-// A wave's k-th cell of phase ph (layer ph / 4, colour ph % 4): local and
-// wrapped coordinates; false if the wave has no such cell.
-__device__ inline bool phase_cell(const MassArgs &m, const ColumnShape &c, int ph, int wave, int k,
+// The wave's cells of every colour class, tabled once per work-group (the
+// class sizes are the same in every layer): lane colour * COL_SLOTS + k holds
+// the local (x, y) index of the wave's k-th cell of that class as
+// x | y << 8 with bit 31 set, or 0 if the wave has no such cell.
+__device__ inline uint32_t colour_table(const ColumnShape &c, int wave)
+{
+    const int lane = lane_id();
+    uint32_t e = 0;
+    if (lane < 4 * COL_SLOTS) {
+        const int colour = lane / COL_SLOTS, k = lane % COL_SLOTS;
+        int nx;
+        const int cnt = colour_cells(c, colour, nx);
+        const int j = wave + COL_WAVES * k;
+        if (j < cnt)
+            e = 0x80000000u | (uint32_t)((colour & 1) + 2 * (j % nx)) |
+                ((uint32_t)((colour >> 1) + 2 * (j / nx)) << 8);
+    }
+    return e;
+}
+
+// Local and wrapped coordinates of table entry e in layer iz; false if the
+// entry is empty or the layer is past the column.
+__device__ inline bool entry_cell(const MassArgs &m, const ColumnShape &c, uint32_t e, int iz,
                                   int *li, int *cell)
 {
-    const int iz = ph >> 2, colour = ph & 3;
-    if (iz > c.count[2])
+    if (!(e >> 31) || iz > c.count[2])
         return false;
-    int nx;
-    const int cnt = colour_cells(c, colour, nx);
-    const int j = wave + COL_WAVES * k;
-    if (j >= cnt)
-        return false;
-    li[0] = (colour & 1) + 2 * (j % nx);
-    li[1] = (colour >> 1) + 2 * (j / nx);
+    li[0] = (int)(e & 0xffu);
+    li[1] = (int)((e >> 8) & 0xffu);
     li[2] = iz;
 #pragma unroll
     for (int a = 0; a < 3; ++a)
         cell[a] = wrap_near(c.first[a] - 1 + li[a], m.n[a]);
     return true;
+}
+
+// A wave's k-th cell of phase ph (layer ph / 4, colour ph % 4): local and
+// wrapped coordinates; false if the wave has no such cell.  ph and k are
+// uniform: one lane read of the table.
+__device__ inline bool phase_cell(const MassArgs &m, const ColumnShape &c, uint32_t table, int ph,
+                                  int k, int *li, int *cell)
+{
+    const uint32_t e = __builtin_amdgcn_readlane(table, (ph & 3) * COL_SLOTS + k);
+    return entry_cell(m, c, e, ph >> 2, li, cell);
 }
 
 __device__ inline uint32_t cell_id(const MassArgs &m, const int *cell)
@@ -533,15 +557,16 @@ __device__ inline uint32_t cell_id(const MassArgs &m, const int *cell)
 
 // Slice bounds of this wave's cells of phase ph, one vector read: lane 2k
 // gets the low bound of cell k, lane 2k+1 the high one (0 for no cell).
-__device__ inline uint32_t phase_offsets(const MassArgs &m, const ColumnShape &c, int ph, int wave)
+__device__ inline uint32_t phase_offsets(const MassArgs &m, const ColumnShape &c, uint32_t table,
+                                        int ph)
 {
     const int lane = lane_id();
+    // every lane takes part in the shuffle; lanes past 2 COL_SLOTS drop it
+    const uint32_t e = (uint32_t)__shfl((int)table, (ph & 3) * COL_SLOTS + ((lane >> 1) & 3), WAVE);
     uint32_t v = 0;
-    if (lane < 2 * COL_SLOTS) {
-        int li[3], cell[3];
-        if (phase_cell(m, c, ph, wave, lane >> 1, li, cell))
-            v = m.cell_offsets[cell_id(m, cell) + (lane & 1)];
-    }
+    int li[3], cell[3];
+    if (lane < 2 * COL_SLOTS && entry_cell(m, c, e, ph >> 2, li, cell))
+        v = m.cell_offsets[cell_id(m, cell) + (lane & 1)];
     return v;
 }
 
@@ -656,9 +681,10 @@ __global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, Co
     // Reads run one phase ahead of their use: during phase ph the first
     // batches of the wave's cells of phase ph + 1 and the slice bounds of
     // phase ph + 2 are in flight.
-    uint32_t off_next = phase_offsets(m, cs, 1, wave);
+    const uint32_t table = colour_table(cs, wave);
+    uint32_t off_next = phase_offsets(m, cs, table, 1);
     PhaseRaw cur, nxt;
-    uint32_t off_cur = phase_offsets(m, cs, 0, wave);
+    uint32_t off_cur = phase_offsets(m, cs, table, 0);
     load_phase<SC>(m, off_cur, cur);
     __syncthreads();
 
@@ -671,7 +697,7 @@ __global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, Co
     for (int ph = 0; ph < nphase; ++ph) {
         const int iz = ph >> 2;
         load_phase<SC>(m, off_next, nxt);
-        const uint32_t off_after = phase_offsets(m, cs, ph + 2, wave);
+        const uint32_t off_after = phase_offsets(m, cs, table, ph + 2);
         // the compiler must not sink these reads to their use
         asm volatile("" ::: "memory");
 
@@ -679,7 +705,7 @@ __global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, Co
 #pragma unroll 1
         for (int k = 0; k < COL_SLOTS; ++k) {
             int li[3], cell[3];
-            if (!phase_cell(m, cs, ph, wave, k, li, cell))
+            if (!phase_cell(m, cs, table, ph, k, li, cell))
                 break;
             int64_t lo, hi;
             slot_bounds(m, off_cur, k, lo, hi);

@@ -14,8 +14,9 @@ timed steps.
 
 Other workloads (--workload): cic2d_512_ppc16 (2-D CIC 512^2), tsc3d_128_blob
 (3-D TSC clustered, T from --tile), mass_64_ppc64 (ECSIM mass matrix 64^3: cell
-sort + MFMA assembly), mass_scalar_64_ppc64 (the scalar mass matrix, coefficient
-q w, on the same particles), sweep1d_2000 (1-D windowed sweep).
+sort + MFMA assembly), mass_f64_64_ppc64 (the same in fp64), mass_scalar_64_ppc64
+(the scalar mass matrix, coefficient q w, on the same particles), sweep1d_2000
+(1-D windowed sweep).
 
 Prints ONE JSON line (rank 0).  Only one GPU is used: --gpus above 1 exits.
 """
@@ -30,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
+MFMA_FP64_PEAK_TFLOPS = 78.6   # MI355X dense fp64 matrix
 
 # HBM bytes per dispatch measured by rocprofv3 FETCH_SIZE / WRITE_SIZE passes
 # (scaled by the copy calibration), with the digest of the kernel's sources at
@@ -47,7 +49,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=HEADLINE,
                     choices=["sweep1d_2000", "cic2d_512_ppc16", "cic3d_128_ppc32",
-                             "tsc3d_128_blob", "mass_64_ppc64", "mass_scalar_64_ppc64"])
+                             "tsc3d_128_blob", "mass_64_ppc64", "mass_f64_64_ppc64",
+                             "mass_scalar_64_ppc64"])
     ap.add_argument("--tile", type=int, default=0, help="tile edge T (0 = the workload's)")
     ap.add_argument("--block", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -134,15 +137,16 @@ def measured_traffic(kernel, workload):
     return int(rec["read_bytes"] + rec["write_bytes"])
 
 
-def roofline_entry(kt, name, bytes_per_launch=None, flops_per_launch=None):
+def roofline_entry(kt, name, bytes_per_launch=None, flops_per_launch=None,
+                   mfma_peak=MFMA_FP32_PEAK_TFLOPS):
     k = kt.get(name)
     if not k:
         return None
     sec = k["avg_us"] * 1e-6
     if flops_per_launch is not None:
         achieved = flops_per_launch / sec / 1e12
-        return dict(bound="mfma", achieved=round(achieved, 3), peak=MFMA_FP32_PEAK_TFLOPS,
-                    unit="TFLOP/s", frac=round(achieved / MFMA_FP32_PEAK_TFLOPS, 4),
+        return dict(bound="mfma", achieved=round(achieved, 3), peak=mfma_peak,
+                    unit="TFLOP/s", frac=round(achieved / mfma_peak, 4),
                     traffic=None, kernel=name, avg_us=round(k["avg_us"], 2))
     achieved = bytes_per_launch / sec / 1e9
     return dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
@@ -311,9 +315,10 @@ def bench_deposit(args, torch, pcg, name):
 
 # ----------------------------------------------------------------- mass matrix
 
-def bench_mass(args, torch, pcg, scalar=False):
+def bench_mass(args, torch, pcg, scalar=False, f64=False):
     """The ECSIM mass matrix, or with scalar=True the scalar one (coefficient q w:
-    x, q, w are read and sorted, 27 floats per node row)."""
+    x, q, w are read and sorted, 27 values per node row); f64: M and all
+    arithmetic in fp64 (the fp64 entry points)."""
     import numpy as np
 
     import synthetic
@@ -324,12 +329,13 @@ def bench_mass(args, torch, pcg, scalar=False):
     dev = torch.device("cuda:0")
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     x = [t(a) for a in wl.x]
+    mdt = torch.float64 if f64 else torch.float32
     if scalar:
         shuffled = x + [t(wl.q), t(wl.w)]
-        M = torch.zeros(n[2], n[1], n[0], 27, dtype=torch.float32, device=dev)
+        M = torch.zeros(n[2], n[1], n[0], 27, dtype=mdt, device=dev)
     else:
         shuffled = x + [t(b) for b in wl.B] + [t(wl.beta), t(wl.q), t(wl.w)]
-        M = torch.zeros(n[2], n[1], n[0], 27, 3, 3, dtype=torch.float32, device=dev)
+        M = torch.zeros(n[2], n[1], n[0], 27, 3, 3, dtype=mdt, device=dev)
     nc = n[0] * n[1] * n[2]
     perm = torch.empty(cnt, dtype=torch.int32, device=dev)
     keys = torch.empty(cnt, dtype=torch.int32, device=dev)
@@ -365,9 +371,11 @@ def bench_mass(args, torch, pcg, scalar=False):
     progress("timing steps")
     ms, wall, kt = time_steps(torch, pcg, step, args.steps, args.warmup)
     progress(f"{ms:.4f} ms per step")
-    mbytes = M.numel() * 4
-    kname = "mass_scalar_mfma" if scalar else "mass_mfma"
-    wname = "mass_scalar_64_ppc64" if scalar else "mass_64_ppc64"
+    mbytes = M.numel() * M.element_size()
+    sfx = "_f64" if f64 else ""
+    kname = ("mass_scalar_mfma" if scalar else "mass_mfma") + sfx
+    wname = "mass_scalar_64_ppc64" if scalar else ("mass_f64_64_ppc64" if f64 else "mass_64_ppc64")
+    mfma_peak = MFMA_FP64_PEAK_TFLOPS if f64 else MFMA_FP32_PEAK_TFLOPS
     # per particle: 8x8 node pairs x 2 flops (scalar) or x 9 components x 2 flops
     flops = cnt * (128.0 if scalar else 1152.0)
     # algorithmic HBM bytes: the particle values once (x, q, w; tensor: + B,
@@ -376,7 +384,7 @@ def bench_mass(args, torch, pcg, scalar=False):
     if scalar:
         roof = roofline_entry(kt, kname, bytes_per_launch=cnt * pbytes + 2 * mbytes)
     else:
-        roof = roofline_entry(kt, kname, flops_per_launch=flops)
+        roof = roofline_entry(kt, kname, flops_per_launch=flops, mfma_peak=mfma_peak)
     if roof:
         roof["traffic"] = measured_traffic(kname, wname)
     kernels = {nm: dict(avg_us=round(kk["avg_us"], 2),
@@ -430,11 +438,14 @@ def bench_mass(args, torch, pcg, scalar=False):
                       step="zero M + cell re-sort of x, q, w from the previous layout + "
                            "scalar MFMA assembly")
     else:
-        config = dict(workload="ECSIM 3-D CIC mass matrix 64^3, 64 ppc (cell sort + MFMA "
-                               "assembly)",
+        prec = "fp64 " if f64 else ""
+        config = dict(workload=f"ECSIM 3-D CIC mass matrix {prec}64^3, 64 ppc (cell sort + "
+                               "MFMA assembly)",
                       particles=cnt, grid=n,
-                      step="zero M + cell re-sort from the previous layout + MFMA assembly")
-    return dict(value=cnt / (ms * 1e-3), ms=ms, wall=wall, dtype="f32", config=config,
+                      step=f"zero M + cell re-sort from the previous layout + {prec}MFMA "
+                           "assembly")
+    return dict(value=cnt / (ms * 1e-3), ms=ms, wall=wall, dtype="f64" if f64 else "f32",
+                config=config,
                 roofline=roof, kernels=kernels, extra=extra, cpu=cpu, unit="particles/s")
 
 
@@ -495,6 +506,8 @@ def main():
         r = bench_deposit(args, torch, pcg, args.workload)
     elif args.workload == "mass_64_ppc64":
         r = bench_mass(args, torch, pcg)
+    elif args.workload == "mass_f64_64_ppc64":
+        r = bench_mass(args, torch, pcg, f64=True)
     elif args.workload == "mass_scalar_64_ppc64":
         r = bench_mass(args, torch, pcg, scalar=True)
     else:

@@ -253,6 +253,23 @@ pcg_status assemble_mass_matrix_scalar(const pcg_grid *grid, const pcg_particles
                                        const pcg_tile *cells, int32_t variant, float *M,
                                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* fp64 variants of the two matrices ([MM] §4 and §4.1, Figs. 6-7: the CIC
+ * scalar and tensor assemblies are measured with every operand in FP64; §5
+ * "Tile-support matching and portability" names AMD's FP64 16x16x4 product):
+ * the same operation and arguments as
+ * assemble_mass_matrix and assemble_mass_matrix_scalar, with M in fp64 and
+ * every product and sum formed in fp64 (the inputs stay fp32).
+ * PCG_MASS_MFMA contracts on v_mfma_f64_16x16x4f64.
+ * M: device fp64, layout as for the fp32 entry points, accumulated.
+ * Errors: as for the fp32 entry points. */
+pcg_status assemble_mass_matrix_f64(const pcg_grid *grid, const pcg_particles *particles,
+                                    const float *const B[3], const float *beta,
+                                    const pcg_tile *cells, int32_t variant, double *M,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+pcg_status assemble_mass_matrix_scalar_f64(const pcg_grid *grid, const pcg_particles *particles,
+                                           const pcg_tile *cells, int32_t variant, double *M,
+                                           void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* 1-D windowed sweep  ([CS] "The problem", "Code")                          */
 /* ------------------------------------------------------------------------ */

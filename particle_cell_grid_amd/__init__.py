@@ -71,6 +71,10 @@ _lib.assemble_mass_matrix.restype = C.c_int32
 _lib.assemble_mass_matrix_scalar.argtypes = [_P(Grid), _P(Particles), _P(Tile), C.c_int32,
                                              C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
 _lib.assemble_mass_matrix_scalar.restype = C.c_int32
+_lib.assemble_mass_matrix_f64.argtypes = _lib.assemble_mass_matrix.argtypes
+_lib.assemble_mass_matrix_f64.restype = C.c_int32
+_lib.assemble_mass_matrix_scalar_f64.argtypes = _lib.assemble_mass_matrix_scalar.argtypes
+_lib.assemble_mass_matrix_scalar_f64.restype = C.c_int32
 _lib.deposit_sweep1d.argtypes = [C.c_int32, C.c_int64, C.c_void_p, C.c_void_p, C.c_int32,
                                  C.c_double, C.c_double, C.c_void_p, C.c_void_p]
 _lib.deposit_sweep1d.restype = C.c_int32
@@ -269,13 +273,23 @@ def pcg_mass_workspace_bytes(n: Sequence[int]) -> int:
     return int(_lib.pcg_mass_workspace_bytes(C.byref(g)))
 
 
+def _mass_suffix(M: torch.Tensor) -> str:
+    """The entry point for M's dtype: fp32 -> "", fp64 -> "_f64"."""
+    if M.dtype == torch.float32:
+        return ""
+    if M.dtype == torch.float64:
+        return "_f64"
+    raise TypeError(f"mass matrix: M must be float32 or float64, not {M.dtype}")
+
+
 def assemble_mass_matrix(n: Sequence[int], x: List[torch.Tensor], B: List[torch.Tensor],
                          beta: torch.Tensor, q: torch.Tensor, w: torch.Tensor, M: torch.Tensor,
                          cells: Optional[Layout] = None, variant: int = PCG_MASS_AUTO,
                          workspace: Optional[torch.Tensor] = None):
-    """M[nz, ny, nx, 27, 3, 3] (fp32) += the ECSIM CIC mass matrix.  With a cell
-    layout a workspace of pcg_mass_workspace_bytes() is needed; one is taken
-    from torch's allocator when none is given."""
+    """M[nz, ny, nx, 27, 3, 3] += the ECSIM CIC mass matrix, in M's dtype (fp32, or
+    fp64: the fp64 entry point).  With a cell layout a workspace of
+    pcg_mass_workspace_bytes() is needed; one is taken from torch's allocator
+    when none is given."""
     g = make_grid(3, n)
     P = _particles(q.numel(), x, None, q, w)
     bp = (C.c_void_p * 3)(*[b.data_ptr() for b in B])
@@ -283,10 +297,11 @@ def assemble_mass_matrix(n: Sequence[int], x: List[torch.Tensor], B: List[torch.
     if cells is not None and workspace is None:
         workspace = torch.empty(pcg_mass_workspace_bytes(n), dtype=torch.uint8, device=M.device)
     wsb = int(workspace.numel()) if workspace is not None else 0
-    st = _lib.assemble_mass_matrix(C.byref(g), C.byref(P), bp, _ptr(beta),
-                                   C.byref(tile) if tile is not None else None, int(variant),
-                                   _ptr(M), _ptr(workspace), wsb, _stream())
-    _check(st, "assemble_mass_matrix")
+    fn = "assemble_mass_matrix" + _mass_suffix(M)
+    st = getattr(_lib, fn)(C.byref(g), C.byref(P), bp, _ptr(beta),
+                           C.byref(tile) if tile is not None else None, int(variant),
+                           _ptr(M), _ptr(workspace), wsb, _stream())
+    _check(st, fn)
     return M
 
 
@@ -294,18 +309,19 @@ def assemble_mass_matrix_scalar(n: Sequence[int], x: List[torch.Tensor], q: torc
                                 w: torch.Tensor, M: torch.Tensor, cells: Optional[Layout] = None,
                                 variant: int = PCG_MASS_AUTO,
                                 workspace: Optional[torch.Tensor] = None):
-    """M[nz, ny, nx, 27] (fp32) += the scalar CIC mass matrix (coefficient q w).
-    Layout, variants and workspace as for assemble_mass_matrix."""
+    """M[nz, ny, nx, 27] += the scalar CIC mass matrix (coefficient q w), in M's
+    dtype (fp32 or fp64).  Layout, variants and workspace as for
+    assemble_mass_matrix."""
     g = make_grid(3, n)
     P = _particles(q.numel(), x, None, q, w)
     tile = cells.to_c() if cells is not None else None
     if cells is not None and workspace is None:
         workspace = torch.empty(pcg_mass_workspace_bytes(n), dtype=torch.uint8, device=M.device)
     wsb = int(workspace.numel()) if workspace is not None else 0
-    st = _lib.assemble_mass_matrix_scalar(C.byref(g), C.byref(P),
-                                          C.byref(tile) if tile is not None else None,
-                                          int(variant), _ptr(M), _ptr(workspace), wsb, _stream())
-    _check(st, "assemble_mass_matrix_scalar")
+    fn = "assemble_mass_matrix_scalar" + _mass_suffix(M)
+    st = getattr(_lib, fn)(C.byref(g), C.byref(P), C.byref(tile) if tile is not None else None,
+                           int(variant), _ptr(M), _ptr(workspace), wsb, _stream())
+    _check(st, fn)
     return M
 
 

@@ -46,6 +46,46 @@ namespace pcg {
 namespace {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef double doublex4 __attribute__((ext_vector_type(4)));
+
+// R, the arithmetic type of a variant: float, or double (M in fp64, every
+// product and sum in fp64, the contractions on v_mfma_f64_16x16x4f64).  Both
+// 16x16x4 products take A[i][k] and B[k][j] from lane i + 16 k (resp.
+// j + 16 k); accumulator register r of lane l holds D[row][l % 16] with
+// row = 4 (l / 16) + r in fp32 and row = l / 16 + 4 r in fp64 (measured).
+template <typename R>
+struct Real;
+template <>
+struct Real<float> {
+    typedef floatx4 acc;
+    typedef float2 pair;
+};
+template <>
+struct Real<double> {
+    typedef doublex4 acc;
+    typedef double2 pair;
+};
+
+__device__ inline floatx4 mfma16x4(float a, float b, floatx4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ inline doublex4 mfma16x4(double a, double b, doublex4 c)
+{
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+template <typename R>
+__device__ inline int acc_row(int kk, int r)
+{
+    return sizeof(R) == 4 ? 4 * kk + r : kk + 4 * r;
+}
+
+__device__ inline void atomic_add_r(float *p, float v) { atomic_add_f32(p, v); }
+__device__ inline void atomic_add_r(double *p, double v)
+{
+    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 struct MassArgs {
     int n[3];
@@ -55,17 +95,24 @@ struct MassArgs {
     const float *q;
     const float *w;
     const float *beta;
-    float *M;
+    void *M;  // R [n_z][n_y][n_x][27] (scalar) or [..][27][3][3]
     const uint32_t *cell_offsets;
     int64_t n_part;
     uint32_t ncells;
 };
 
+template <typename R>
+__device__ inline R *mat(const MassArgs &m)
+{
+    return static_cast<R *>(m.M);
+}
+
+template <typename R>
 struct Particle {
-    float W[8];     // CIC node weights, a = ax + 2 ay + 4 az
-    float u[4];     // (1, omega)
-    float c;        // q w / (1 + |omega|^2)
-    int base[3];    // cell (= first support node) per axis
+    R W[8];       // CIC node weights, a = ax + 2 ay + 4 az
+    R u[4];       // (1, omega)
+    R c;          // q w / (1 + |omega|^2)
+    int base[3];  // cell (= first support node) per axis
 };
 
 // The nine per-particle input values, as loaded.
@@ -123,36 +170,37 @@ __device__ inline int wrap_once(int i, int n) { return i >= n ? i - n : i; }
 // i in [-1, n] (a cell next to a column, whose nodes lie in [0, n)) wrapped.
 __device__ inline int wrap_near(int i, int n) { return i < 0 ? i + n : wrap_once(i, n); }
 
-__device__ inline Particle make_particle(const MassArgs &m, const RawParticle &r)
+template <typename R>
+__device__ inline Particle<R> make_particle(const MassArgs &m, const RawParticle &r)
 {
-    Particle P;
-    float wx[3][2];
+    Particle<R> P;
+    R wx[3][2];
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
         const float x = clamp_coord(r.x[k], m.nf[k]);
         const float fl = floorf(x);
-        const float xi = x - fl;
+        const R xi = (R)(x - fl);  // exact in fp32
         P.base[k] = wrap_once((int)fl, m.n[k]);
-        wx[k][0] = 1.0f - xi;
+        wx[k][0] = (R)1 - xi;
         wx[k][1] = xi;
     }
 #pragma unroll
     for (int a = 0; a < 8; ++a)
         P.W[a] = wx[0][a & 1] * wx[1][(a >> 1) & 1] * wx[2][a >> 2];
-    const float bt = r.beta;
-    const float o0 = bt * r.B[0], o1 = bt * r.B[1], o2 = bt * r.B[2];
-    P.u[0] = 1.0f;
+    const R bt = r.beta;
+    const R o0 = bt * (R)r.B[0], o1 = bt * (R)r.B[1], o2 = bt * (R)r.B[2];
+    P.u[0] = (R)1;
     P.u[1] = o0;
     P.u[2] = o1;
     P.u[3] = o2;
-    P.c = r.q * r.w / (1.0f + (o0 * o0 + o1 * o1 + o2 * o2));
+    P.c = (R)r.q * (R)r.w / ((R)1 + (o0 * o0 + o1 * o1 + o2 * o2));
     return P;
 }
 
-template <bool SC>
-__device__ inline Particle load_particle(const MassArgs &m, int64_t p)
+template <bool SC, typename R>
+__device__ inline Particle<R> load_particle(const MassArgs &m, int64_t p)
 {
-    return make_particle(m, load_raw<SC>(m, p));
+    return make_particle<R>(m, load_raw<SC>(m, p));
 }
 
 __device__ inline int64_t node_index(const MassArgs &m, const int *base, int a)
@@ -170,7 +218,8 @@ __device__ inline int offset_index(int a, int b)
 }
 
 // Nine components of M^{ij}_{ab} from the ten moments t[k][l] (k <= l).
-__device__ inline void moments_to_block(const float t[4][4], float *out)
+template <typename R>
+__device__ inline void moments_to_block(const R t[4][4], R *out)
 {
     out[0] = t[0][0] + t[1][1];   // xx
     out[1] = t[0][3] + t[1][2];   // xy: +eps_xyz omega_z + omega_x omega_y
@@ -184,48 +233,48 @@ __device__ inline void moments_to_block(const float t[4][4], float *out)
 }
 
 // The particle's whole 8x8x9 (scalar: 8x8) contribution with global atomics.
-template <bool SC>
-__device__ inline void deposit_particle_global(const MassArgs &m, const Particle &P)
+template <bool SC, typename R>
+__device__ inline void deposit_particle_global(const MassArgs &m, const Particle<R> &P)
 {
-    float t[4][4];
+    R t[4][4];
     int64_t g[8];
 #pragma unroll
     for (int a = 0; a < 8; ++a)
         g[a] = node_index(m, P.base, a);
     if constexpr (SC) {
         for (int a = 0; a < 8; ++a) {
-            const float ca = P.c * P.W[a];
-            float *row = m.M + (size_t)g[a] * 27;
+            const R ca = P.c * P.W[a];
+            R *row = mat<R>(m) + (size_t)g[a] * 27;
 #pragma unroll
             for (int b = 0; b < 8; ++b)
-                atomic_add_f32(&row[offset_index(a, b)], ca * P.W[b]);
+                atomic_add_r(&row[offset_index(a, b)], ca * P.W[b]);
         }
         return;
     }
     for (int a = 0; a < 8; ++a) {
         for (int b = 0; b < 8; ++b) {
-            const float wab = P.c * P.W[a] * P.W[b];
+            const R wab = P.c * P.W[a] * P.W[b];
 #pragma unroll
             for (int k = 0; k < 4; ++k)
 #pragma unroll
                 for (int l = k; l < 4; ++l)
                     t[k][l] = wab * P.u[k] * P.u[l];
-            float blk[9];
+            R blk[9];
             moments_to_block(t, blk);
-            float *row = m.M + ((size_t)g[a] * 27 + offset_index(a, b)) * 9;
+            R *row = mat<R>(m) + ((size_t)g[a] * 27 + offset_index(a, b)) * 9;
 #pragma unroll
             for (int ij = 0; ij < 9; ++ij)
-                atomic_add_f32(&row[ij], blk[ij]);
+                atomic_add_r(&row[ij], blk[ij]);
         }
     }
 }
 
-template <bool SC>
+template <bool SC, typename R>
 __global__ __launch_bounds__(256) void k_mass_flat(MassArgs m, int64_t begin, int64_t end)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t p = begin + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < end; p += stride)
-        deposit_particle_global<SC>(m, load_particle<SC>(m, p));
+        deposit_particle_global<SC, R>(m, load_particle<SC, R>(m, p));
 }
 
 __device__ inline void cell_coords(const MassArgs &m, uint32_t cell, int *cc)
@@ -274,21 +323,26 @@ constexpr int col_z()
 
 // LDS staging of one 64-particle batch of a cell, per wave; reused for the
 // 32 x 32 moment tile once the batches are done.
+template <typename R>
 struct Stage {
-    float W[64][8];
-    float u[64][4];  // stored as (u0, u2, u1, u3) so (u_k, u_{k+2}) are adjacent
-    float c[64];
+    R W[64][8];
+    R u[64][4];  // stored as (u0, u2, u1, u3) so (u_k, u_{k+2}) are adjacent
+    R c[64];
 };
+template <typename R>
 union WaveScratch {
-    Stage s;
-    float Tm[32][33];
+    Stage<R> s;
+    R Tm[32][33];
 };
 
-template <bool SC>
+// The work-group's LDS: two node planes and one scratch per wave (fp64
+// tensor: 158,208 bytes, within the 160 KiB of a CU).
+template <bool SC, typename R>
 constexpr size_t column_lds_bytes()
 {
-    return sizeof(float) * 2 * COL_NODES * row_floats<SC>() + sizeof(WaveScratch) * COL_WAVES;
+    return sizeof(R) * 2 * COL_NODES * row_floats<SC>() + sizeof(WaveScratch<R>) * COL_WAVES;
 }
+static_assert(column_lds_bytes<false, double>() <= 160 * 1024, "fp64 planes exceed the LDS");
 
 // Orders this wave's earlier LDS accesses before its later ones (lanes exchange
 // data through LDS within one wave only).
@@ -302,29 +356,41 @@ __device__ inline void wave_sync()
 // Stages one particle (raw values, valid = the slot is inside the cell's slice)
 // into the lane's row.  A particle that lies in another cell (a stale layout)
 // is staged as zero and reported through *stray: the follow-up pass deposits it.
-template <bool SC>
-__device__ inline void stage_raw(const MassArgs &m, Stage &s, int lane, const RawParticle &r,
+template <bool SC, typename R>
+__device__ inline void stage_raw(const MassArgs &m, Stage<R> &s, int lane, const RawParticle &r,
                                  bool valid, const int *cell, bool *stray)
 {
     // computed for every lane (an empty slot holds zeros), then selected:
     // no divergent branches
-    const Particle P = make_particle(m, r);
+    const Particle<R> P = make_particle<R>(m, r);
     const bool home = P.base[0] == cell[0] && P.base[1] == cell[1] && P.base[2] == cell[2];
     const bool take = valid && home;
     *stray = *stray || (valid && !home);
-    float W[8], u[4];
+    R W[8], u[4];
 #pragma unroll
     for (int a = 0; a < 8; ++a)
-        W[a] = take ? P.W[a] : 0.0f;
+        W[a] = take ? P.W[a] : (R)0;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-        u[k] = take ? P.u[k] : 0.0f;
-    const float c = take ? P.c : 0.0f;
-    float4 *w4 = reinterpret_cast<float4 *>(s.W[lane]);
-    w4[0] = make_float4(W[0], W[1], W[2], W[3]);
-    w4[1] = make_float4(W[4], W[5], W[6], W[7]);
-    if constexpr (!SC)
-        *reinterpret_cast<float4 *>(s.u[lane]) = make_float4(u[0], u[2], u[1], u[3]);
+        u[k] = take ? P.u[k] : (R)0;
+    const R c = take ? P.c : (R)0;
+    if constexpr (sizeof(R) == 4) {
+        float4 *w4 = reinterpret_cast<float4 *>(s.W[lane]);
+        w4[0] = make_float4(W[0], W[1], W[2], W[3]);
+        w4[1] = make_float4(W[4], W[5], W[6], W[7]);
+        if constexpr (!SC)
+            *reinterpret_cast<float4 *>(s.u[lane]) = make_float4(u[0], u[2], u[1], u[3]);
+    } else {
+        double2 *w2 = reinterpret_cast<double2 *>(s.W[lane]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w2[i] = make_double2(W[2 * i], W[2 * i + 1]);
+        if constexpr (!SC) {
+            double2 *u2 = reinterpret_cast<double2 *>(s.u[lane]);
+            u2[0] = make_double2(u[0], u[2]);
+            u2[1] = make_double2(u[1], u[3]);
+        }
+    }
     s.c[lane] = c;
 }
 
@@ -333,16 +399,18 @@ __device__ inline void stage_raw(const MassArgs &m, Stage &s, int lane, const Ra
 // t[k][l] for k <= l (scalar: t[0][0] only).  `first` holds the lane's
 // particle of the first batch (slot lo + lane), loaded ahead by the caller;
 // later batches (cells of more than 64 particles) are loaded here.
-template <bool MFMA, bool SC>
-__device__ inline void cell_moments(const MassArgs &m, WaveScratch &ws, int lane, const int *cell,
-                                    int64_t lo, int64_t hi, const RawParticle &first, bool *stray,
-                                    float t[4][4])
+template <bool MFMA, bool SC, typename R>
+__device__ inline void cell_moments(const MassArgs &m, WaveScratch<R> &ws, int lane,
+                                    const int *cell, int64_t lo, int64_t hi,
+                                    const RawParticle &first, bool *stray, R t[4][4])
 {
+    typedef typename Real<R>::acc Acc;
+    typedef typename Real<R>::pair Pair;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
         for (int l = 0; l < 4; ++l)
-            t[k][l] = 0.0f;
+            t[k][l] = (R)0;
     if (hi <= lo)
         return;
     const int pa = lane >> 3, pb = lane & 7;
@@ -350,10 +418,10 @@ __device__ inline void cell_moments(const MassArgs &m, WaveScratch &ws, int lane
     // block, particle kk = lane / 16 of the 4-particle batch
     const int r = lane & 15, kk = lane >> 4;
     const int a = r & 7, khalf = r >> 3;  // node a, moment index k = khalf (+2)
-    floatx4 acc00 = {0, 0, 0, 0}, acc01 = {0, 0, 0, 0}, acc11 = {0, 0, 0, 0};
+    Acc acc00 = {0, 0, 0, 0}, acc01 = {0, 0, 0, 0}, acc11 = {0, 0, 0, 0};
     auto batch = [&](const RawParticle &rp, int64_t base) {
         wave_sync();
-        stage_raw<SC>(m, ws.s, lane, rp, base + lane < hi, cell, stray);
+        stage_raw<SC, R>(m, ws.s, lane, rp, base + lane < hi, cell, stray);
         wave_sync();
         const int nb = (int)std::min<int64_t>(64, hi - base);
         if constexpr (MFMA && SC) {
@@ -361,7 +429,7 @@ __device__ inline void cell_moments(const MassArgs &m, WaveScratch &ws, int lane
             // 8 i + 4 khalf + kk (staged rows past the slice are zero)
             auto slot = [&](int i) { return 8 * i + 4 * khalf + kk; };
             if (nb == 64) {
-                float wa[8], cp[8];
+                R wa[8], cp[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     wa[i] = ws.s.W[slot(i)][a];
@@ -370,14 +438,12 @@ __device__ inline void cell_moments(const MassArgs &m, WaveScratch &ws, int lane
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
-                    acc00 = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[i], cp[i] * wa[i], acc00, 0, 0,
-                                                                 0);
+                    acc00 = mfma16x4(wa[i], cp[i] * wa[i], acc00);
             } else {
                 const int batches = (nb + 7) >> 3;
                 for (int bt = 0; bt < batches; ++bt) {
-                    const float wa = ws.s.W[slot(bt)][a];
-                    acc00 = __builtin_amdgcn_mfma_f32_16x16x4f32(wa, ws.s.c[slot(bt)] * wa, acc00,
-                                                                 0, 0, 0);
+                    const R wa = ws.s.W[slot(bt)][a];
+                    acc00 = mfma16x4(wa, ws.s.c[slot(bt)] * wa, acc00);
                 }
             }
         } else if constexpr (SC) {
@@ -385,49 +451,53 @@ __device__ inline void cell_moments(const MassArgs &m, WaveScratch &ws, int lane
                 t[0][0] += ws.s.c[q] * ws.s.W[q][pa] * ws.s.W[q][pb];
         } else if constexpr (MFMA) {
             // one 4-particle batch: operands from the staged rows, three MFMAs
-            auto mfma_batch = [&](float wa, float2 uu, float cp) {
-                const float a0 = uu.x * wa;  // u_k W_a      (k = khalf)
-                const float a1 = uu.y * wa;  // u_{k+2} W_a
-                const float b0 = cp * a0;
-                const float b1 = cp * a1;
-                acc00 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc00, 0, 0, 0);
-                acc01 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc01, 0, 0, 0);
-                acc11 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc11, 0, 0, 0);
+            auto mfma_batch = [&](R wa, Pair uu, R cp) {
+                const R a0 = uu.x * wa;  // u_k W_a      (k = khalf)
+                const R a1 = uu.y * wa;  // u_{k+2} W_a
+                const R b0 = cp * a0;
+                const R b1 = cp * a1;
+                acc00 = mfma16x4(a0, b0, acc00);
+                acc01 = mfma16x4(a0, b1, acc01);
+                acc11 = mfma16x4(a1, b1, acc11);
             };
             if (nb == 64) {
-                // a full batch: the operands of all sixteen 4-particle steps are
-                // read first (one LDS round trip), then the 48 products issue
-                // back to back
-                float wa[16], cp[16];
-                float2 uu[16];
+                // a full batch: the operands of G 4-particle steps are read
+                // first (one LDS round trip), then their 3 G products issue
+                // back to back (G = 16 in fp32, 8 in fp64 for registers)
+                constexpr int G = sizeof(R) == 4 ? 16 : 8;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int q = 4 * i + kk;
-                    wa[i] = ws.s.W[q][a];
-                    uu[i] = *reinterpret_cast<const float2 *>(&ws.s.u[q][2 * khalf]);
-                    cp[i] = ws.s.c[q];
+                for (int g0 = 0; g0 < 16; g0 += G) {
+                    R wa[G], cp[G];
+                    Pair uu[G];
+#pragma unroll
+                    for (int i = 0; i < G; ++i) {
+                        const int q = 4 * (g0 + i) + kk;
+                        wa[i] = ws.s.W[q][a];
+                        uu[i] = *reinterpret_cast<const Pair *>(&ws.s.u[q][2 * khalf]);
+                        cp[i] = ws.s.c[q];
+                    }
+                    // keep the reads ahead of the products (the scheduler would
+                    // otherwise interleave them and wait once per step)
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int i = 0; i < G; ++i)
+                        mfma_batch(wa[i], uu[i], cp[i]);
                 }
-                // keep the reads ahead of the products (the scheduler would
-                // otherwise interleave them and wait once per step)
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    mfma_batch(wa[i], uu[i], cp[i]);
             } else {
                 const int batches = (nb + 3) >> 2;
                 for (int bt = 0; bt < batches; ++bt) {
                     const int q = 4 * bt + kk;
-                    mfma_batch(ws.s.W[q][a], *reinterpret_cast<const float2 *>(&ws.s.u[q][2 * khalf]),
+                    mfma_batch(ws.s.W[q][a], *reinterpret_cast<const Pair *>(&ws.s.u[q][2 * khalf]),
                                ws.s.c[q]);
                 }
             }
         } else {
             for (int q = 0; q < nb; ++q) {
-                const float wab = ws.s.c[q] * ws.s.W[q][pa] * ws.s.W[q][pb];
-                const float u[4] = {ws.s.u[q][0], ws.s.u[q][2], ws.s.u[q][1], ws.s.u[q][3]};
+                const R wab = ws.s.c[q] * ws.s.W[q][pa] * ws.s.W[q][pb];
+                const R u[4] = {ws.s.u[q][0], ws.s.u[q][2], ws.s.u[q][1], ws.s.u[q][3]};
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const float wk = wab * u[k];
+                    const R wk = wab * u[k];
 #pragma unroll
                     for (int l = k; l < 4; ++l)
                         t[k][l] += wk * u[l];
@@ -448,15 +518,15 @@ __device__ inline void cell_moments(const MassArgs &m, WaveScratch &ws, int lane
         // the two diagonal 8x8 blocks of the accumulator, summed
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            ws.Tm[4 * kk + i][r] = acc00[i];
+            ws.Tm[acc_row<R>(kk, i)][r] = acc00[i];
         wave_sync();
         t[0][0] = ws.Tm[pa][pb] + ws.Tm[8 + pa][8 + pb];
         wave_sync();
     } else if constexpr (MFMA) {
-        // accumulator layout: lane holds D[4*(lane/16) + i][lane % 16], i = 0..3
+        // accumulator register i of this lane holds D[acc_row(kk, i)][lane % 16]
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = 4 * kk + i, col = r;
+            const int row = acc_row<R>(kk, i), col = r;
             ws.Tm[row][col] = acc00[i];
             ws.Tm[row][16 + col] = acc01[i];
             ws.Tm[16 + row][16 + col] = acc11[i];
@@ -638,18 +708,19 @@ __device__ inline RawParticle pick(const PhaseRaw &p, int k)
     return r;
 }
 
-template <bool MFMA, bool SC>
+template <bool MFMA, bool SC, typename R>
 __global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, ColumnGeom cg)
 {
     constexpr int ROW = row_floats<SC>();
     constexpr int COL_ROW_PER_THREAD = col_row_per_thread<SC>();
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    float *planes = reinterpret_cast<float *>(smem);  // [2][COL_NODES][ROW]
-    WaveScratch *scratch = reinterpret_cast<WaveScratch *>(smem + sizeof(float) * 2 * COL_NODES * ROW);
+    R *planes = reinterpret_cast<R *>(smem);  // [2][COL_NODES][ROW]
+    WaveScratch<R> *scratch =
+        reinterpret_cast<WaveScratch<R> *>(smem + sizeof(R) * 2 * COL_NODES * ROW);
     // the wave index is uniform across the wave: keep the walk over the cells
     // (and everything derived from it) in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), lane = lane_id();
-    WaveScratch &ws = scratch[wave];
+    WaveScratch<R> &ws = scratch[wave];
 
     // spread spatially adjacent columns over consecutive blocks of one XCD
     // (blocks are dealt to the 8 XCDs round-robin), so the cells two columns
@@ -676,7 +747,7 @@ __global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, Co
     const int nphase = 4 * (BZ + 1);
 
     for (int i = threadIdx.x; i < 2 * COL_NODES * ROW; i += blockDim.x)
-        planes[i] = 0.0f;
+        planes[i] = (R)0;
 
     // Reads run one phase ahead of their use: during phase ph the first
     // batches of the wave's cells of phase ph + 1 and the slice bounds of
@@ -710,8 +781,8 @@ __global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, Co
             int64_t lo, hi;
             slot_bounds(m, off_cur, k, lo, hi);
             bool st = false;
-            float t[4][4];
-            cell_moments<MFMA, SC>(m, ws, lane, cell, lo, hi, pick(cur, k), &st, t);
+            R t[4][4];
+            cell_moments<MFMA, SC, R>(m, ws, lane, cell, lo, hi, pick(cur, k), &st, t);
             // a cell's stray particles are reported by the column holding its
             // first node (each cell has exactly one such column)
             if (li[0] >= 1 && li[1] >= 1 && li[2] >= 1)
@@ -724,11 +795,11 @@ __global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, Co
                 // outstanding load
                 uint32_t e = ((lz & 1) * COL_NODES + ly * COL_X + lx) * ROW;
                 asm("" : "+v"(e));
-                float *node = planes + e;
+                R *node = planes + e;
                 if constexpr (SC) {
                     node[o] += t[0][0];
                 } else {
-                    float blk[9];
+                    R blk[9];
                     moments_to_block(t, blk);
 #pragma unroll
                     for (int ij = 0; ij < 9; ++ij)
@@ -751,18 +822,18 @@ __global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, Co
         const int done = iz - 1;
         if ((ph & 3) == 3 && done >= 0) {
             const int gz = cs.first[2] + done;
-            float *pl = planes + (size_t)(done & 1) * COL_NODES * ROW;
+            R *pl = planes + (size_t)(done & 1) * COL_NODES * ROW;
             // every row's M values are read first (one round trip), then each
             // row is added and stored
-            float v[COL_Y][COL_ROW_PER_THREAD];
+            R v[COL_Y][COL_ROW_PER_THREAD];
 #pragma unroll
             for (int ly = 0; ly < COL_Y; ++ly) {
-                const float *dst = m.M + (cs.first[0] + (int64_t)m.n[0] *
-                                          ((cs.first[1] + ly) + (int64_t)m.n[1] * gz)) * ROW;
+                const R *dst = mat<R>(m) + (cs.first[0] + (int64_t)m.n[0] *
+                                            ((cs.first[1] + ly) + (int64_t)m.n[1] * gz)) * ROW;
 #pragma unroll
                 for (int q = 0; q < COL_ROW_PER_THREAD; ++q) {
                     const int r = threadIdx.x + q * COL_WAVES * WAVE;
-                    v[ly][q] = ly < BY && r < BX * ROW ? dst[r] : 0.0f;
+                    v[ly][q] = ly < BY && r < BX * ROW ? dst[r] : (R)0;
                 }
             }
             // one wait for all of them, so that the stores below need none
@@ -775,15 +846,15 @@ __global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, Co
             for (int ly = 0; ly < COL_Y; ++ly) {
                 if (ly >= BY)
                     break;
-                float *dst = m.M + (cs.first[0] + (int64_t)m.n[0] *
-                                    ((cs.first[1] + ly) + (int64_t)m.n[1] * gz)) * ROW;
-                float *src = pl + ly * COL_X * ROW;
+                R *dst = mat<R>(m) + (cs.first[0] + (int64_t)m.n[0] *
+                                      ((cs.first[1] + ly) + (int64_t)m.n[1] * gz)) * ROW;
+                R *src = pl + ly * COL_X * ROW;
 #pragma unroll
                 for (int q = 0; q < COL_ROW_PER_THREAD; ++q) {
                     const int r = threadIdx.x + q * COL_WAVES * WAVE;
                     if (r < BX * ROW) {
                         dst[r] = v[ly][q] + src[r];
-                        src[r] = 0.0f;  // only this thread read this value
+                        src[r] = (R)0;  // only this thread read this value
                     }
                 }
             }
@@ -797,7 +868,7 @@ __global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, Co
 // Follow-up of the column kernel, run only when it found stray particles: each
 // thread walks one cell's slice and deposits the particles that lie elsewhere
 // with global atomics.
-template <bool SC>
+template <bool SC, typename R>
 __global__ __launch_bounds__(256) void k_mass_strays(MassArgs m, const uint32_t *flag)
 {
     if (*flag == 0u)
@@ -809,9 +880,9 @@ __global__ __launch_bounds__(256) void k_mass_strays(MassArgs m, const uint32_t 
         const int64_t lo = std::min<int64_t>(m.cell_offsets[cid], m.n_part);
         const int64_t hi = std::min<int64_t>(m.cell_offsets[cid + 1], m.n_part);
         for (int64_t p = lo; p < hi; ++p) {
-            const Particle P = load_particle<SC>(m, p);
+            const Particle<R> P = load_particle<SC, R>(m, p);
             if (P.base[0] != cc[0] || P.base[1] != cc[1] || P.base[2] != cc[2])
-                deposit_particle_global<SC>(m, P);
+                deposit_particle_global<SC, R>(m, P);
         }
     }
 }
@@ -829,25 +900,38 @@ namespace {
 // particles), padded to 256 bytes.
 constexpr size_t MASS_WORKSPACE = 256;
 
-template <bool MFMA, bool SC>
+// Launch names: mass_[scalar_]{mfma,valu,flat,strays}[_f64].
+template <bool SC, typename R>
+const char *kernel_name(int which)
+{
+    static const char *const names[2][2][4] = {
+        {{"mass_mfma", "mass_valu", "mass_flat", "mass_strays"},
+         {"mass_mfma_f64", "mass_valu_f64", "mass_flat_f64", "mass_strays_f64"}},
+        {{"mass_scalar_mfma", "mass_scalar_valu", "mass_scalar_flat", "mass_scalar_strays"},
+         {"mass_scalar_mfma_f64", "mass_scalar_valu_f64", "mass_scalar_flat_f64",
+          "mass_scalar_strays_f64"}}};
+    return names[SC ? 1 : 0][sizeof(R) == 8 ? 1 : 0][which];
+}
+
+template <bool MFMA, bool SC, typename R>
 pcg_status launch_column(const MassArgs &m, const ColumnGeom &cg, hipStream_t st)
 {
-    auto kern = k_mass_column<MFMA, SC>;
-    const size_t lds = column_lds_bytes<SC>();
+    auto kern = k_mass_column<MFMA, SC, R>;
+    const size_t lds = column_lds_bytes<SC, R>();
     if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)lds) != hipSuccess)
         return fail(PCG_EHIP, "mass matrix: cannot raise dynamic LDS to %zu bytes", lds);
     const uint32_t blocks = (cg.nwork + 7) / 8 * 8;
-    const char *name = SC ? (MFMA ? "mass_scalar_mfma" : "mass_scalar_valu")
-                          : (MFMA ? "mass_mfma" : "mass_valu");
-    return launch(name, kern, dim3(blocks), dim3(COL_WAVES * WAVE), lds, st, m, cg);
+    return launch(kernel_name<SC, R>(MFMA ? 0 : 1), kern, dim3(blocks), dim3(COL_WAVES * WAVE),
+                  lds, st, m, cg);
 }
 
-// Both entry points: the tensor matrix (B and beta given) or the scalar one.
-template <bool SC>
+// Every entry point: the tensor matrix (B and beta given) or the scalar one,
+// with M in R.
+template <bool SC, typename R>
 pcg_status assemble(const char *who, const pcg_grid *grid, const pcg_particles *particles,
                     const float *const B[3], const float *beta, const pcg_tile *cells,
-                    int32_t variant, float *M, void *workspace, size_t workspace_bytes,
+                    int32_t variant, R *M, void *workspace, size_t workspace_bytes,
                     void *stream)
 {
     clear_error();
@@ -893,8 +977,8 @@ pcg_status assemble(const char *who, const pcg_grid *grid, const pcg_particles *
             return PCG_OK;
         const int64_t blocks =
             std::min<int64_t>((end - begin + 255) / 256, (int64_t)device_cus() * 32);
-        return launch(SC ? "mass_scalar_flat" : "mass_flat", k_mass_flat<SC>,
-                      dim3((unsigned)blocks), dim3(256), 0, st, m, begin, end);
+        return launch(kernel_name<SC, R>(2), k_mass_flat<SC, R>, dim3((unsigned)blocks),
+                      dim3(256), 0, st, m, begin, end);
     };
     if (variant == PCG_MASS_FLAT || (!cells && variant == PCG_MASS_AUTO))
         return flat(0, count);
@@ -925,14 +1009,13 @@ pcg_status assemble(const char *who, const pcg_grid *grid, const pcg_particles *
         PCG_TRY(launch("mass_clear_flag", k_mass_clear_flag, dim3(1), dim3(1), 0, st,
                        cg.stray_flag));
         if (variant == PCG_MASS_VALU)
-            PCG_TRY((launch_column<false, SC>(m, cg, st)));
+            PCG_TRY((launch_column<false, SC, R>(m, cg, st)));
         else
-            PCG_TRY((launch_column<true, SC>(m, cg, st)));
+            PCG_TRY((launch_column<true, SC, R>(m, cg, st)));
         const int64_t sblocks =
             std::min<int64_t>((m.ncells + 255) / 256, (int64_t)device_cus() * 8);
-        PCG_TRY(launch(SC ? "mass_scalar_strays" : "mass_strays", k_mass_strays<SC>,
-                       dim3((unsigned)sblocks), dim3(256), 0, st, m,
-                       (const uint32_t *)cg.stray_flag));
+        PCG_TRY(launch(kernel_name<SC, R>(3), k_mass_strays<SC, R>, dim3((unsigned)sblocks),
+                       dim3(256), 0, st, m, (const uint32_t *)cg.stray_flag));
     }
     return flat(cells->n_partitioned, count);
 }
@@ -950,8 +1033,8 @@ extern "C" pcg_status assemble_mass_matrix(const pcg_grid *grid, const pcg_parti
                                            const pcg_tile *cells, int32_t variant, float *M,
                                            void *workspace, size_t workspace_bytes, void *stream)
 {
-    return assemble<false>("assemble_mass_matrix", grid, particles, B, beta, cells, variant, M,
-                           workspace, workspace_bytes, stream);
+    return assemble<false, float>("assemble_mass_matrix", grid, particles, B, beta, cells,
+                                  variant, M, workspace, workspace_bytes, stream);
 }
 
 extern "C" pcg_status assemble_mass_matrix_scalar(const pcg_grid *grid,
@@ -960,6 +1043,27 @@ extern "C" pcg_status assemble_mass_matrix_scalar(const pcg_grid *grid,
                                                   void *workspace, size_t workspace_bytes,
                                                   void *stream)
 {
-    return assemble<true>("assemble_mass_matrix_scalar", grid, particles, nullptr, nullptr, cells,
-                          variant, M, workspace, workspace_bytes, stream);
+    return assemble<true, float>("assemble_mass_matrix_scalar", grid, particles, nullptr, nullptr,
+                                 cells, variant, M, workspace, workspace_bytes, stream);
+}
+
+extern "C" pcg_status assemble_mass_matrix_f64(const pcg_grid *grid,
+                                               const pcg_particles *particles,
+                                               const float *const B[3], const float *beta,
+                                               const pcg_tile *cells, int32_t variant, double *M,
+                                               void *workspace, size_t workspace_bytes,
+                                               void *stream)
+{
+    return assemble<false, double>("assemble_mass_matrix_f64", grid, particles, B, beta, cells,
+                                   variant, M, workspace, workspace_bytes, stream);
+}
+
+extern "C" pcg_status assemble_mass_matrix_scalar_f64(const pcg_grid *grid,
+                                                      const pcg_particles *particles,
+                                                      const pcg_tile *cells, int32_t variant,
+                                                      double *M, void *workspace,
+                                                      size_t workspace_bytes, void *stream)
+{
+    return assemble<true, double>("assemble_mass_matrix_scalar_f64", grid, particles, nullptr,
+                                  nullptr, cells, variant, M, workspace, workspace_bytes, stream);
 }

@@ -60,12 +60,14 @@ def tap_name(kernel):
     last = targs[-1].strip() if targs else ""
     if base == "k_deposit_tiled":
         return "deposit_regroup" if last == "true" else "deposit_tiled"
-    scalar = "mass_scalar_" if base.startswith("k_mass_") and last == "true" else "mass_"
-    if base == "k_mass_column":     # <MFMA, scalar>
-        mfma = targs[0].strip() == "true"
-        return scalar + ("mfma" if mfma else "valu")
-    if base in ("k_mass_flat", "k_mass_strays"):
-        return scalar + base[len("k_mass_"):]
+    if base.startswith("k_mass_") and targs:
+        # <MFMA, scalar, real> for the column kernel, <scalar, real> otherwise
+        scalar = "mass_scalar_" if targs[-2].strip() == "true" else "mass_"
+        f64 = "_f64" if last == "double" else ""
+        if base == "k_mass_column":
+            return scalar + ("mfma" if targs[0].strip() == "true" else "valu") + f64
+        if base in ("k_mass_flat", "k_mass_strays"):
+            return scalar + base[len("k_mass_"):] + f64
     table = {"k_deposit_flat": "deposit_flat",
              "k_inc_move": "sort_inc_move", "k_inc_count": "sort_inc_count",
              "k_inc_tiles": "sort_inc_tiles",

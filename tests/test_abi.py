@@ -37,7 +37,8 @@ def test_header_declares_the_entry_points():
     for n in ["pcg_tile_sort", "pcg_sort_workspace_bytes", "deposit_currents",
               "pcg_deposit_workspace_bytes", "deposit_currents_regroup",
               "pcg_deposit_regroup_workspace_bytes", "pcg_mass_workspace_bytes", "assemble_mass_matrix",
-              "assemble_mass_matrix_scalar", "deposit_sweep1d",
+              "assemble_mass_matrix_scalar", "assemble_mass_matrix_f64",
+              "assemble_mass_matrix_scalar_f64", "deposit_sweep1d",
               "pcg_status_string", "pcg_last_error", "pcg_version", "pcg_timing_enable",
               "pcg_timing_reset", "pcg_timing_read", "pcg_timing_names"]:
         assert n in names
@@ -249,6 +250,17 @@ def test_mass_and_sweep_validation(lib):
     assert scall(variant=1, cells=C.byref(c1), ws=None) == EWORKSPACE
     assert scall(variant=1, cells=C.byref(c1), ws=FAKE + 8) == EWORKSPACE
     assert scall(variant=1, cells=C.byref(Tile(1, 1, 0, 0, 101, FAKE))) == EINVAL  # > count
+    # the fp64 entry points validate alike
+    af = lib.assemble_mass_matrix_f64
+    af.argtypes = am.argtypes
+    assert af(g8, C.byref(P), B, FAKE, None, 9, FAKE, FAKE, 256, None) == EINVAL
+    assert af(g8, C.byref(P), None, FAKE, None, 0, FAKE, FAKE, 256, None) == EINVAL  # no B
+    assert af(g8, C.byref(P), B, FAKE, C.byref(c1), 1, FAKE, None, 0, None) == EWORKSPACE
+    sf = lib.assemble_mass_matrix_scalar_f64
+    sf.argtypes = sm.argtypes
+    assert sf(C.byref(grid(2, [8, 8])), C.byref(P), None, 0, FAKE, FAKE, 256, None) == EUNSUPPORTED
+    assert sf(g8, C.byref(P), C.byref(t), 1, FAKE, FAKE, 256, None) == EINVAL
+    assert sf(g8, C.byref(P), None, 0, None, FAKE, 256, None) == EINVAL            # no M
     sw = lib.deposit_sweep1d
     sw.argtypes = [C.c_int32, C.c_int64, C.c_void_p, C.c_void_p, C.c_int32, C.c_double,
                    C.c_double, C.c_void_p, C.c_void_p]

@@ -1,0 +1,94 @@
+"""GPU fp64 mass matrices (ECSIM tensor and scalar; MFMA on v_mfma_f64_16x16x4f64,
+VALU and flat variants) vs the fp64 oracle.
+
+Tolerance: every product and sum is fp64 on both sides and the inputs are the
+same fp32 values, so the two differ only in summation order: ||M_gpu -
+M_oracle||_F <= 1e-12 ||M_oracle||_F and max |M_gpu - M_oracle| <= 1e-12 max
+|M_oracle| (the mass-matrix paper, §5 "Exactness and precision": no rounding
+error seen with its FP64 tile).
+"""
+import numpy as np
+import pytest
+import torch
+
+import particle_cell_grid_amd as pcg
+import synthetic
+from gpu_util import DEV, dev, full_workload, rel_frob_err, say
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-12
+VARIANTS = [pcg.PCG_MASS_MFMA, pcg.PCG_MASS_VALU, pcg.PCG_MASS_FLAT]
+
+
+def _run(wl, perm, off, variant, scalar, n_part=None):
+    s = wl.take(perm.astype(np.int64)) if perm is not None else wl
+    shape = (wl.n[2], wl.n[1], wl.n[0], 27) + (() if scalar else (3, 3))
+    M = torch.zeros(shape, dtype=torch.float64, device=DEV)
+    cells = pcg.Layout(T=1, order=1, tile_offsets=dev(off.view(np.int32)),
+                       n_partitioned=wl.count if n_part is None else n_part, drift=0)
+    say("mass f64", "scalar" if scalar else "tensor", wl.n, wl.count, variant, n_part)
+    if scalar:
+        pcg.assemble_mass_matrix_scalar(wl.n, [dev(a) for a in s.x], dev(s.q), dev(s.w), M, cells,
+                                        variant)
+    else:
+        pcg.assemble_mass_matrix(wl.n, [dev(a) for a in s.x], [dev(b) for b in s.B],
+                                 dev(s.beta), dev(s.q), dev(s.w), M, cells, variant)
+    torch.cuda.synchronize()
+    return M.cpu().numpy()
+
+
+def _ref(orc, n, s, scalar):
+    if scalar:
+        return orc.mass_matrix_scalar(n, s.x, s.q, s.w)
+    return orc.mass_matrix(n, s.x, s.B, s.q, s.w, s.beta)
+
+
+def _check(M, ref):
+    assert M.dtype == np.float64
+    assert rel_frob_err(M, ref) <= TOL
+    assert np.abs(M - ref).max() <= TOL * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("scalar", [False, True])
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("n,ppc", [([8, 8, 8], 16), ([6, 5, 7], 64), ([4, 4, 4], 100)])
+def test_f64_mass_matches_oracle(orc, scalar, variant, n, ppc):
+    """Uniform loading; ppc = 100 takes a second, partial 64-particle batch."""
+    wl = synthetic.mass_workload(n, ppc, w_uniform=True, seed=700 + ppc)
+    _, perm, off = orc.tile_sort(3, n, 1, 1, wl.x)
+    _check(_run(wl, perm, off, variant, scalar), _ref(orc, n, wl, scalar))
+
+
+@pytest.mark.parametrize("scalar", [False, True])
+def test_f64_mass_ragged_stale_and_tail(orc, scalar):
+    """Random positions (empty, sparse and crowded cells), a stale layout (every
+    7th particle moved after the sort) and an unsorted tail of 500."""
+    r = np.random.default_rng(71)
+    n = [10, 9, 8]
+    cnt = 6000
+    x = [r.uniform(0, n[k], cnt).astype(np.float32) for k in range(3)]
+    x[0][:1500] = r.uniform(2, 3, 1500).astype(np.float32)
+    x[1][:1500] = r.uniform(4, 5, 1500).astype(np.float32)
+    B = [r.normal(0, 1, cnt).astype(np.float32) for _ in range(3)]
+    q = np.where(r.random(cnt) < 0.5, 1.0, -1.0).astype(np.float32)
+    w = r.uniform(0.5, 1.5, cnt).astype(np.float32)
+    beta = (q * 0.05).astype(np.float32)
+    wl = synthetic.Workload(3, n, x, x, [np.zeros(cnt, np.float32)] * 3, q, w, B, beta)
+    _, perm, off = orc.tile_sort(3, n, 1, 1, x)
+    s = wl.take(perm.astype(np.int64))
+    s.x[0] = synthetic.periodic_shift(s.x[0], np.where(np.arange(cnt) % 7 == 0, 0.6, 0.0), n[0])
+    M = _run(s, None, off, pcg.PCG_MASS_MFMA, scalar, n_part=cnt - 500)
+    _check(M, _ref(orc, n, s, scalar))
+
+
+def test_f64_mass_full_size_64(orc):
+    """64^3, 64 ppc, the tensor matrix in fp64 on the matrix cores: rows of a
+    z-slab against the oracle on the slab's particles."""
+    wl = full_workload("mass_64_ppc64")
+    _, perm, off = orc.tile_sort(3, wl.n, 1, 1, wl.x)
+    M = _run(wl, perm, off, pcg.PCG_MASS_MFMA, scalar=False)
+    z0, z1 = 20, 30
+    cz = np.floor(wl.x[2]).astype(np.int64)
+    sub = wl.take(np.nonzero((cz >= z0) & (cz < z1))[0])
+    ref = orc.mass_matrix(wl.n, sub.x, sub.B, sub.q, sub.w, sub.beta)
+    _check(M[z0 + 1:z1], ref[z0 + 1:z1])

@@ -74,6 +74,9 @@ def lib():
         L.oracle_sweep1d.argtypes = [C.c_int, C.c_int64, C.c_void_p, C.c_void_p, C.c_int,
                                      C.c_double, C.c_double, C.c_void_p]
         L.oracle_sweep1d.restype = C.c_int
+        L.oracle_sweep1d_grad.argtypes = [C.c_int, C.c_int64, C.c_void_p, C.c_void_p, C.c_int,
+                                          C.c_double, C.c_double, C.c_void_p, C.c_void_p]
+        L.oracle_sweep1d_grad.restype = C.c_int
         _lib = L
     return _lib
 
@@ -243,3 +246,16 @@ def sweep1d(nb, x0, v, T, dt, hw):
                               float(hw), _ptr(H))
     _check(rc, "sweep1d")
     return H
+
+
+def sweep1d_grad(nb, x0, v, T, dt, hw, dH):
+    """The reverse of sweep1d: dL/dx0 fp64 [count] for a given dL/dH (fp64 [nb])."""
+    x0 = np.ascontiguousarray(x0, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    dH = np.ascontiguousarray(dH, dtype=np.float64)
+    assert dH.size == int(nb)
+    dx0 = np.zeros(x0.size, dtype=np.float64)
+    rc = lib().oracle_sweep1d_grad(int(nb), int(x0.size), _ptr(x0), _ptr(v), int(T), float(dt),
+                                   float(hw), _ptr(dH), _ptr(dx0))
+    _check(rc, "sweep1d_grad")
+    return dx0

@@ -407,3 +407,44 @@ int oracle_sweep1d(int nb, int64_t np, const double *x0, const double *v,
     }
     return 0;
 }
+
+/* [CS] "Code": the reverse of the sweep above, as the page's autodiff call
+ * computes it: x0 active, v and the set-up constant.  dH holds dL/dH (the page
+ * seeds it with 2 (H - target)); dx0[p] is overwritten with dL/dx0[p].  For a
+ * selected particle at step t (same x, d, u, w, g, j, f as the forward pass):
+ *   dx/dx0 = 1 and dd/dx = 1 (the wrap and the minimum image are locally
+ *   shifts); dw/dx = -2 u sign(d) / hw; df/dx = nb;
+ *   the deposits w (1 - f) into j and w f into j + 1 give
+ *   dx0 += dw/dx ((1 - f) dH[j] + f dH[j+1]) + w nb (dH[j+1] - dH[j]).
+ * sign(0) is taken as 0 (the derivative of |d| at 0). */
+int oracle_sweep1d_grad(int nb, int64_t np, const double *x0, const double *v,
+                        int T, double dt, double hw, const double *dH, double *dx0)
+{
+    if (nb < 1 || np < 0 || T < 0 || !(hw > 0.0))
+        return -1;
+    for (int64_t p = 0; p < np; ++p)
+        dx0[p] = 0.0;
+    for (int t = 1; t <= T; ++t) {
+        double c = (double)t / (double)T;
+        double shift = (double)t * dt;
+        for (int64_t p = 0; p < np; ++p) {
+            double x = x0[p] + v[p] * shift;
+            x = x - floor(x);
+            double r = x - c;
+            double d = r - rint(r);
+            if (fabs(d) < hw) {
+                double u = 1.0 - fabs(d) / hw;
+                double weight = u * u;
+                double sgn = d > 0.0 ? 1.0 : (d < 0.0 ? -1.0 : 0.0);
+                double dw = -2.0 * u * sgn / hw;
+                double g = x * (double)nb - 0.5;
+                double jf = floor(g);
+                double f = g - jf;
+                int64_t j = (int64_t)jf;
+                double h0 = dH[wrap(j, nb)], h1 = dH[wrap(j + 1, nb)];
+                dx0[p] += dw * ((1.0 - f) * h0 + f * h1) + weight * (double)nb * (h1 - h0);
+            }
+        }
+    }
+    return 0;
+}

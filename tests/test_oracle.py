@@ -625,3 +625,56 @@ def test_sweep_is_linear_in_particles(orc):
     Hsum = sum(orc.sweep1d(wl.nb, wl.x0[i:i + 1], wl.v[i:i + 1], wl.T, wl.dt, wl.hw)
                for i in range(300))
     assert np.allclose(Hall, Hsum, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# 1-D sweep, reverse  ([CS] "Code": the gradient of sum (H - target)^2 in x0)
+
+def test_sweep_grad_hand_values(orc):
+    """One step (T = 1: the window centre is c = 1 = 0 mod 1), v = 0, nb = 8,
+    hw = 1/4, dyadic positions, by hand from the forward formulas."""
+    def g(x0, dH):
+        return orc.sweep1d_grad(8, [x0], [0.0], 1, 0.5, 0.25, dH)[0]
+    # x0 = 1/16: d = 1/16, u = 3/4, w = 9/16, dw/dx = -6; g = 0 -> j = 0, f = 0:
+    # -6 (1 dH0 + 0 dH1) + (9/16) 8 (dH1 - dH0) = -10.5 dH0 + 4.5 dH1
+    assert g(1 / 16, [1, 2, 0, 0, 0, 0, 0, 0]) == -1.5
+    # x0 = 29/32: d = -3/32, u = 5/8, w = 25/64, dw/dx = +5; g = 6.75 -> j = 6,
+    # f = 3/4: 5 (dH6/4 + 3 dH7/4) + (25/8)(dH7 - dH6)
+    assert g(29 / 32, [0, 0, 0, 0, 0, 0, 3, -1]) == -12.5
+    # x0 = 1/64: d = 1/64, u = 15/16, w = 225/256, dw/dx = -7.5; g = -3/8 -> j = -1
+    # (bin 7), f = 5/8: -7.5 (3/8 dH7 + 5/8 dH0) + (225/32)(dH0 - dH7)
+    assert g(1 / 64, [2, 0, 0, 0, 0, 0, 0, 1]) == -5.15625
+    # outside the window (|d| = 1/4 is not < hw): no contribution
+    assert g(0.25, [1, 1, 1, 1, 1, 1, 1, 1]) == 0.0
+
+
+def test_sweep_grad_matches_finite_differences(orc):
+    """Central differences of L(x0) = sum (H(x0) - target)^2 over the oracle's own
+    forward sweep, particle by particle: L is piecewise smooth, and a random
+    particle is not within eps of a kink (|d| = 0, a bin centre)."""
+    r = np.random.default_rng(81)
+    nb, T, dt, hw, n = 64, 20, 0.02, 0.06, 40
+    x0 = r.random(n)
+    v = r.normal(0.0, 0.3, n)
+    target = r.random(nb)
+    H = orc.sweep1d(nb, x0, v, T, dt, hw)
+    grad = orc.sweep1d_grad(nb, x0, v, T, dt, hw, 2.0 * (H - target))
+    assert np.count_nonzero(grad) > n // 2
+    eps = 1e-6
+    for i in range(n):
+        xp = x0.copy()
+        xp[i] += eps
+        xm = x0.copy()
+        xm[i] -= eps
+        lp = np.sum((orc.sweep1d(nb, xp, v, T, dt, hw) - target) ** 2)
+        lm = np.sum((orc.sweep1d(nb, xm, v, T, dt, hw) - target) ** 2)
+        fd = (lp - lm) / (2 * eps)
+        assert abs(fd - grad[i]) <= 1e-5 * max(1.0, abs(grad[i])), (i, fd, grad[i])
+
+
+def test_sweep_grad_zero_when_never_selected(orc):
+    # T = 10 window centres at 0.1, ..., 1.0 with hw = 0.01: a particle resting
+    # at 0.05 is never inside, so neither H nor dL/dx0 sees it
+    dH = np.linspace(-1, 1, 32)
+    g = orc.sweep1d_grad(32, [0.05, 0.3], [0.0, 0.0], 10, 0.02, 0.01, dH)
+    assert g[0] == 0.0 and g[1] != 0.0

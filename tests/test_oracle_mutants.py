@@ -57,6 +57,17 @@ MUTANTS = [
      "double u = 1.0 - fabs(d) / hw;", "double u = 1.0 - fabs(d) / (2.0 * hw);"),
     ("sweep bins without the half-bin shift",
      "double g = x * (double)nb - 0.5;", "double g = x * (double)nb;"),
+    ("sweep gradient drops the bin-position term",
+     " + weight * (double)nb * (h1 - h0);", ";"),
+    ("sweep gradient with the taper slope's sign flipped",
+     "double dw = -2.0 * u * sgn / hw;", "double dw = 2.0 * u * sgn / hw;"),
+    ("sweep gradient reads the two bins swapped",
+     "double h0 = dH[wrap(j, nb)], h1 = dH[wrap(j + 1, nb)];",
+     "double h0 = dH[wrap(j + 1, nb)], h1 = dH[wrap(j, nb)];"),
+    ("scalar mass matrix without the weight",
+     "const double s = (double)q[p] * (double)w[p];", "const double s = (double)q[p];"),
+    ("scalar mass matrix weighted by the first node twice",
+     "M[g * 27 + o] += s * wg * wh;", "M[g * 27 + o] += s * wg * wg;"),
 ]
 
 

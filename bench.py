@@ -16,7 +16,8 @@ Other workloads (--workload): cic2d_512_ppc16 (2-D CIC 512^2), tsc3d_128_blob
 (3-D TSC clustered, T from --tile), mass_64_ppc64 (ECSIM mass matrix 64^3: cell
 sort + MFMA assembly), mass_f64_64_ppc64 (the same in fp64), mass_scalar_64_ppc64
 (the scalar mass matrix, coefficient q w, on the same particles), sweep1d_2000
-(1-D windowed sweep).
+(1-D windowed sweep), sweep1d_grad_1e7 (the sweep's loss gradient, 10^7 particles:
+forward sweep, seed and reverse gather in one library call).
 
 Prints ONE JSON line (rank 0).  Only one GPU is used: --gpus above 1 exits.
 """
@@ -50,7 +51,7 @@ def parse():
     ap.add_argument("--workload", default=HEADLINE,
                     choices=["sweep1d_2000", "cic2d_512_ppc16", "cic3d_128_ppc32",
                              "tsc3d_128_blob", "mass_64_ppc64", "mass_f64_64_ppc64",
-                             "mass_scalar_64_ppc64"])
+                             "mass_scalar_64_ppc64", "sweep1d_grad_1e7"])
     ap.add_argument("--tile", type=int, default=0, help="tile edge T (0 = the workload's)")
     ap.add_argument("--block", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -481,6 +482,74 @@ def bench_sweep(args, torch, pcg):
                 roofline=None, kernels=kernels, extra={}, cpu=cpu, unit="particle-steps/s")
 
 
+# ------------------------------------------------------------- 1-D sweep, reverse
+
+FP64_VECTOR_OPS = 39.3e12   # MI355X fp64 vector instructions x lanes per s (78.6 TFLOP/s / 2)
+SELECT_OPS = 9              # fp64 ops of one particle-step's selection test (see DESIGN)
+
+
+def bench_sweep_grad(args, torch, pcg):
+    """The page's gradient at its timing-table size: deposit_sweep1d_loss_grad
+    (forward sweep into H, seed 2 (H - target), reverse gather into dx0)."""
+    import numpy as np
+
+    import synthetic
+
+    progress("generating sweep1d_grad_1e7")
+    s = synthetic.workload("sweep1d_grad_1e7")
+    dev = torch.device("cuda:0")
+    x0 = torch.from_numpy(s.x0).to(dev)
+    v = torch.from_numpy(s.v).to(dev)
+    target = torch.from_numpy(np.random.default_rng(7).random(s.nb)).to(dev)
+    H = torch.empty(s.nb, dtype=torch.float32, device=dev)
+    dx0 = torch.empty_like(x0)
+    n, T = s.x0.size, s.T
+    step = lambda: pcg.deposit_sweep1d_loss_grad(s.nb, x0, v, T, s.dt, s.hw, target, H, dx0)
+    ms, wall, kt = time_steps(torch, pcg, step, args.steps, args.warmup)
+    progress(f"{ms:.4f} ms per gradient")
+    kernels = {nm: dict(avg_us=round(kk["avg_us"], 2)) for nm, kk in kt.items()}
+    roof = None
+    if "sweep1d_grad" in kt:
+        sec = kt["sweep1d_grad"]["avg_us"] * 1e-6
+        ops = SELECT_OPS * n * T / sec
+        roof = dict(bound="alu", achieved=round(ops / 1e12, 3), peak=FP64_VECTOR_OPS / 1e12,
+                    unit="T fp64 ops/s", frac=round(ops / FP64_VECTOR_OPS, 4), traffic=None,
+                    kernel="sweep1d_grad", avg_us=round(kt["sweep1d_grad"]["avg_us"], 2))
+    extra = dict(page_gpu_gradient_ms={"jax_compacted": 52.6, "enzyme_atomics": 146.9},
+                 page_gpu="unnamed 16 GB NVIDIA GPU (context, not this machine)",
+                 selected_particle_steps=int(np.count_nonzero(dx0.cpu().numpy())))
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        progress("timing the oracle on the host")
+        m = 200_000
+        t0 = time.perf_counter()
+        Ho = oracle.sweep1d(s.nb, s.x0[:m], s.v[:m], T, s.dt, s.hw)
+        oracle.sweep1d_grad(s.nb, s.x0[:m], s.v[:m], T, s.dt, s.hw,
+                            2.0 * (Ho - target.cpu().numpy()))
+        per = (time.perf_counter() - t0) / m
+        m2 = int(min(n, max(m, args.cpu_seconds / per)))
+        t0 = time.perf_counter()
+        Ho = oracle.sweep1d(s.nb, s.x0[:m2], s.v[:m2], T, s.dt, s.hw)
+        oracle.sweep1d_grad(s.nb, s.x0[:m2], s.v[:m2], T, s.dt, s.hw,
+                            2.0 * (Ho - target.cpu().numpy()))
+        sec = time.perf_counter() - t0
+        cpu = dict(value=round(m2 * T / sec, 1), unit="particle-steps/s", cores=1,
+                   kind="oracle", sample=f"first {m2} of {n} particles, forward + reverse, "
+                                         f"{sec:.1f} s, 1 thread")
+    config = dict(workload="1-D windowed sweep loss gradient: 10^7 particles, 50 steps, 1024 "
+                           "bins (forward, seed, reverse gather)",
+                  particles=n, steps=T, bins=s.nb)
+    # the page's fastest GPU gradient at this size, as the same rate (another
+    # machine: context)
+    page_rate = n * T / 52.6e-3
+    extra["vs_baseline_is"] = "value / the page's 52.6 ms JAX gradient as particle-steps/s"
+    return dict(value=n * T / (ms * 1e-3), ms=ms, wall=wall, dtype="f64", config=config,
+                roofline=roof, kernels=kernels, extra=extra, cpu=cpu,
+                unit="particle-steps/s", vs_baseline=round(n * T / (ms * 1e-3) / page_rate, 2))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -508,6 +577,8 @@ def main():
         r = bench_mass(args, torch, pcg)
     elif args.workload == "mass_f64_64_ppc64":
         r = bench_mass(args, torch, pcg, f64=True)
+    elif args.workload == "sweep1d_grad_1e7":
+        r = bench_sweep_grad(args, torch, pcg)
     elif args.workload == "mass_scalar_64_ppc64":
         r = bench_mass(args, torch, pcg, scalar=True)
     else:
@@ -522,7 +593,7 @@ def main():
         "ms_per_step": round(r["ms"], 4),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": None,
+        "vs_baseline": r.get("vs_baseline"),
         "dtype": r["dtype"],
         "data": "synthetic",
         "config": r["config"],

@@ -18,7 +18,8 @@
  *   0 <= x_k < n_k.  Grid arrays are x-fastest (linear node
  *   g = gx + n_x*(gy + n_y*gz)).  Unused axes of a 1-D or 2-D grid have n_k = 1.
  * Accumulation.  deposit_currents and assemble_mass_matrix ADD into their
- *   output (the caller zeroes it); deposit_sweep1d OVERWRITES its output.
+ *   output (the caller zeroes it); the 1-D sweep entry points OVERWRITE their
+ *   outputs.
  * Errors.  Every entry point returns a pcg_status.  Arguments are validated on
  *   the host before anything is enqueued; on failure nothing is launched and
  *   pcg_last_error() gives a message (per host thread).  A launch failure
@@ -284,6 +285,31 @@ pcg_status assemble_mass_matrix_scalar_f64(const pcg_grid *grid, const pcg_parti
  * x0, v: device fp64 [count]. */
 pcg_status deposit_sweep1d(int32_t nb, int64_t count, const double *x0, const double *v,
                            int32_t steps, double dt, double half_width, float *H, void *stream);
+
+/* The reverse of deposit_sweep1d ([CS] "Code": the gradient the page takes of
+ * its loss sum (H - target)^2 with respect to x0, with v and the set-up held
+ * constant).  Given dH = dL/dH (fp64 [nb]; the page's loss gives
+ * 2 (H - target)), dx0[p] is OVERWRITTEN with dL/dx0[p]: for every step at
+ * which the particle is selected (the same fp64 decisions as the forward call),
+ *   dx0 += dw/dx ((1 - f) dH[j] + f dH[j+1]) + w nb (dH[j+1] - dH[j])
+ * with w = (1 - |d|/half_width)^2, dw/dx = -2 (1 - |d|/half_width) sign(d) /
+ * half_width (sign(0) = 0), f and j the forward split and bin (mod nb).
+ * x0, v, dx0: device fp64 [count]; dH: device fp64 [nb].
+ * Errors: PCG_EINVAL as for deposit_sweep1d, or a NULL array with count > 0. */
+pcg_status deposit_sweep1d_grad(int32_t nb, int64_t count, const double *x0, const double *v,
+                                int32_t steps, double dt, double half_width, const double *dH,
+                                double *dx0, void *stream);
+
+/* The page's whole gradient call ([CS] "Code", deposit_gradient): the forward
+ * sweep into H, the seed dL/dH = 2 (H - target) of its loss sum (H - target)^2,
+ * and the reverse above, enqueued as one call.  H: device fp32 [nb], OVERWRITTEN
+ * with the forward histogram (the seed is formed from these fp32 values);
+ * target: device fp64 [nb]; dx0: device fp64 [count], OVERWRITTEN.
+ * Errors: as for deposit_sweep1d_grad; H and target may not be NULL. */
+pcg_status deposit_sweep1d_loss_grad(int32_t nb, int64_t count, const double *x0,
+                                     const double *v, int32_t steps, double dt,
+                                     double half_width, const double *target, float *H,
+                                     double *dx0, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* Diagnostics and measurement                                               */

@@ -78,6 +78,14 @@ _lib.assemble_mass_matrix_scalar_f64.restype = C.c_int32
 _lib.deposit_sweep1d.argtypes = [C.c_int32, C.c_int64, C.c_void_p, C.c_void_p, C.c_int32,
                                  C.c_double, C.c_double, C.c_void_p, C.c_void_p]
 _lib.deposit_sweep1d.restype = C.c_int32
+_lib.deposit_sweep1d_grad.argtypes = [C.c_int32, C.c_int64, C.c_void_p, C.c_void_p, C.c_int32,
+                                      C.c_double, C.c_double, C.c_void_p, C.c_void_p,
+                                      C.c_void_p]
+_lib.deposit_sweep1d_grad.restype = C.c_int32
+_lib.deposit_sweep1d_loss_grad.argtypes = [C.c_int32, C.c_int64, C.c_void_p, C.c_void_p,
+                                           C.c_int32, C.c_double, C.c_double, C.c_void_p,
+                                           C.c_void_p, C.c_void_p, C.c_void_p]
+_lib.deposit_sweep1d_loss_grad.restype = C.c_int32
 _lib.pcg_status_string.argtypes = [C.c_int32]
 _lib.pcg_status_string.restype = C.c_char_p
 _lib.pcg_last_error.argtypes = []
@@ -332,6 +340,30 @@ def deposit_sweep1d(nb: int, x0: torch.Tensor, v: torch.Tensor, steps: int, dt: 
                               float(half_width), _ptr(H), _stream())
     _check(st, "deposit_sweep1d")
     return H
+
+
+def deposit_sweep1d_grad(nb: int, x0: torch.Tensor, v: torch.Tensor, steps: int, dt: float,
+                         half_width: float, dH: torch.Tensor,
+                         dx0: Optional[torch.Tensor] = None):
+    """dx0[count] (fp64) = dL/dx0 of the sweep for dL/dH = dH (fp64 [nb]), overwritten."""
+    if dx0 is None:
+        dx0 = torch.empty_like(x0)
+    st = _lib.deposit_sweep1d_grad(int(nb), int(x0.numel()), _ptr(x0), _ptr(v), int(steps),
+                                   float(dt), float(half_width), _ptr(dH), _ptr(dx0), _stream())
+    _check(st, "deposit_sweep1d_grad")
+    return dx0
+
+
+def deposit_sweep1d_loss_grad(nb: int, x0: torch.Tensor, v: torch.Tensor, steps: int, dt: float,
+                              half_width: float, target: torch.Tensor, H: torch.Tensor,
+                              dx0: torch.Tensor):
+    """Forward sweep into H (fp32 [nb]), then dx0 = dL/dx0 of L = sum (H - target)^2
+    (target fp64 [nb], dx0 fp64 [count]); both outputs overwritten."""
+    st = _lib.deposit_sweep1d_loss_grad(int(nb), int(x0.numel()), _ptr(x0), _ptr(v), int(steps),
+                                        float(dt), float(half_width), _ptr(target), _ptr(H),
+                                        _ptr(dx0), _stream())
+    _check(st, "deposit_sweep1d_loss_grad")
+    return H, dx0
 
 
 def pcg_timing_enable(enable: bool = True):

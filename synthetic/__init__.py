@@ -213,6 +213,9 @@ def sweep_workload(count=2000, sigma_v=0.05, nb=1024, T=50, dt=0.02, hw=0.005, s
 WORKLOADS = {
     # 1-D windowed sweep: 2000 particles, 50 steps, 1024 bins
     "sweep1d_2000": dict(kind="sweep1d", count=2000, seed=SEED_BASE + 1),
+    # the same sweep at the size of the compaction page's timing table: 10^7
+    # particles, 50 steps, 1024 bins (its gradient is timed there)
+    "sweep1d_grad_1e7": dict(kind="sweep1d", count=10_000_000, seed=SEED_BASE + 6),
     # 2-D CIC current deposit, 512^2 periodic, 16 particles per cell
     "cic2d_512_ppc16": dict(kind="deposit", dim=2, n=[512, 512], ppc=16, order=1, T=8, D=1,
                             seed=SEED_BASE + 2),

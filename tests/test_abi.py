@@ -38,7 +38,8 @@ def test_header_declares_the_entry_points():
               "pcg_deposit_workspace_bytes", "deposit_currents_regroup",
               "pcg_deposit_regroup_workspace_bytes", "pcg_mass_workspace_bytes", "assemble_mass_matrix",
               "assemble_mass_matrix_scalar", "assemble_mass_matrix_f64",
-              "assemble_mass_matrix_scalar_f64", "deposit_sweep1d",
+              "assemble_mass_matrix_scalar_f64", "deposit_sweep1d", "deposit_sweep1d_grad",
+              "deposit_sweep1d_loss_grad",
               "pcg_status_string", "pcg_last_error", "pcg_version", "pcg_timing_enable",
               "pcg_timing_reset", "pcg_timing_read", "pcg_timing_names"]:
         assert n in names
@@ -268,3 +269,21 @@ def test_mass_and_sweep_validation(lib):
     assert sw(1 << 15, 10, FAKE, FAKE, 50, 0.02, 0.005, FAKE, None) == EINVAL
     assert sw(1024, 10, FAKE, FAKE, 50, 0.02, 0.0, FAKE, None) == EINVAL
     assert sw(1024, 10, None, FAKE, 50, 0.02, 0.005, FAKE, None) == EINVAL
+    gr = lib.deposit_sweep1d_grad
+    gr.argtypes = [C.c_int32, C.c_int64, C.c_void_p, C.c_void_p, C.c_int32, C.c_double,
+                   C.c_double, C.c_void_p, C.c_void_p, C.c_void_p]
+    assert gr(0, 10, FAKE, FAKE, 50, 0.02, 0.005, FAKE, FAKE, None) == EINVAL
+    assert gr(16385, 10, FAKE, FAKE, 50, 0.02, 0.005, FAKE, FAKE, None) == EINVAL
+    assert gr(1024, -1, FAKE, FAKE, 50, 0.02, 0.005, FAKE, FAKE, None) == EINVAL
+    assert gr(1024, 10, FAKE, FAKE, -1, 0.02, 0.005, FAKE, FAKE, None) == EINVAL
+    assert gr(1024, 10, FAKE, FAKE, 50, 0.02, 0.0, FAKE, FAKE, None) == EINVAL
+    assert gr(1024, 10, FAKE, FAKE, 50, 0.02, 0.005, None, FAKE, None) == EINVAL   # no dH
+    assert gr(1024, 10, FAKE, FAKE, 50, 0.02, 0.005, FAKE, None, None) == EINVAL   # no dx0
+    assert gr(1024, 0, None, None, 50, 0.02, 0.005, None, None, None) == 0        # empty
+    lg = lib.deposit_sweep1d_loss_grad
+    lg.argtypes = [C.c_int32, C.c_int64, C.c_void_p, C.c_void_p, C.c_int32, C.c_double,
+                   C.c_double, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
+    assert lg(0, 10, FAKE, FAKE, 50, 0.02, 0.005, FAKE, FAKE, FAKE, None) == EINVAL
+    assert lg(1024, 10, FAKE, FAKE, 50, 0.02, 0.005, None, FAKE, FAKE, None) == EINVAL  # target
+    assert lg(1024, 10, FAKE, FAKE, 50, 0.02, 0.005, FAKE, None, FAKE, None) == EINVAL  # H
+    assert lg(1024, 10, FAKE, FAKE, 50, 0.02, 0.005, FAKE, FAKE, None, None) == EINVAL  # dx0

@@ -36,7 +36,8 @@ def test_large_count(orc):
     assert rel_max_err(H, ref) <= 1e-5
 
 
-@pytest.mark.parametrize("nb,T,hw", [(7, 13, 0.2), (16384, 50, 0.001), (1, 5, 0.5)])
+@pytest.mark.parametrize("nb,T,hw", [(7, 13, 0.2), (16384, 50, 0.001), (1, 5, 0.5),
+                                     (64, 5000, 0.02), (16384, 4000, 0.001)])
 def test_odd_shapes(orc, nb, T, hw):
     s = synthetic.sweep_workload(count=5000, nb=nb, T=T, hw=hw, seed=62)
     H = _run(nb, s.x0, s.v, T, s.dt, hw)

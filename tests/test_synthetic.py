@@ -86,6 +86,7 @@ def test_sweep_statistics_match_page_scale():
 def test_every_named_workload_builds_small():
     """Each named workload generates (shrunk) with its own seed and recipe."""
     small = {"sweep1d_2000": dict(count=64),
+             "sweep1d_grad_1e7": dict(count=64),
              "cic2d_512_ppc16": dict(n=[16, 16], ppc=2),
              "cic3d_128_ppc32": dict(n=[16, 16, 16], ppc=2),
              "tsc3d_128_blob": dict(n=[16, 16, 16], count=4096,
@@ -95,7 +96,7 @@ def test_every_named_workload_builds_small():
     for name, scale in small.items():
         a = synthetic.workload(name, scale)
         b = synthetic.workload(name, scale)
-        if name == "sweep1d_2000":
+        if name.startswith("sweep1d"):
             assert a.x0.size == 64 and np.array_equal(a.x0, b.x0)
         else:
             assert a.count > 0 and all(np.array_equal(p, r) for p, r in zip(a.x, b.x))

@@ -8,14 +8,21 @@
 // window test and the bin index are decided in fp64 with contraction off so
 // they round exactly as written.
 //
+// Compaction inside the wave (what the page lists as not done on its GPU
+// side): about 1% of particle-steps fall in the window, yet with one lane per
+// particle about half of all wave-steps hold at least one such lane, and the
+// whole wave would run the deposit for it.  Instead each step only tests; the
+// lanes in the window append (x, d, lane) to the wave's LDS queue (ballot and
+// rank), and the queue is deposited 64 items at a time, one per lane.
+//
 // The reverse (the gradient the page takes with its autodiff call, x0 active,
-// v and the set-up constant) is a gather: each thread walks its particle's
-// steps as the forward kernel does, with the same fp64 decisions, and at each
-// selected step reads dL/dH at the two bins the step deposited into:
+// v and the set-up constant) walks the same steps with the same fp64
+// decisions and queue, and for each queued item reads dL/dH at the two bins
+// the step deposited into:
 //   dx0 += dw/dx ((1 - f) dH[j] + f dH[j+1]) + w nb (dH[j+1] - dH[j]),
 //   dw/dx = -2 u sign(d) / hw   (the wrap and minimum image are local shifts).
-// dH is copied to LDS once per work-group; there are no atomics and dx0 is
-// written once per particle.
+// dH is copied to LDS once per work-group.  An item's term is added (LDS fp64
+// add) to its particle's slot, and each particle's dx0 is written once.
 #include <algorithm>
 
 #include "common.hpp"
@@ -25,11 +32,12 @@ namespace {
 
 // Per-step window centre c = t / steps and shift t dt, the same for every
 // particle: tabled once per work-group in LDS after the histogram (when the
-// host finds room: up to STEP_TABLE_MAX steps within the CU's LDS), by the
-// same fp64 operations as inline, so the same bits.  The inline division cost
-// as much as the rest of a step's test.
+// host finds room: up to STEP_TABLE_MAX steps within the CU's LDS beside the
+// static queues), by the same fp64 operations as inline, so the same bits.  The
+// inline division cost as much as the rest of a step's test.
 constexpr int STEP_TABLE_MAX = 4096;
-constexpr size_t SWEEP_LDS_MAX = 160 * 1024;
+constexpr size_t SWEEP_LDS_MAX = 152 * 1024;
+constexpr int SWEEP_WAVES = 256 / WAVE;
 
 __device__ inline size_t align16(size_t b) { return (b + 15) & ~size_t(15); }
 
@@ -46,6 +54,71 @@ __device__ inline double2 step_consts(const double2 *tab, bool tabled, int t, in
     return tabled ? tab[t - 1] : make_double2((double)t / (double)steps, (double)t * dt);
 }
 
+// One wave's queue of selected (particle, step) items, and (reverse) the
+// per-lane sums of the current particles.
+struct SweepQueue {
+    double x[WAVE];   // wrapped position
+    double d[WAVE];   // minimum-image distance to the window centre
+    int owner[WAVE];  // lane whose particle it is
+    double acc[WAVE];
+};
+
+// Orders this wave's earlier LDS accesses before its later ones.
+__device__ inline void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The step's window test for one particle (fp64, no contraction): wrapped x
+// and minimum-image d; true if |d| < hw.
+__device__ inline bool window_test(double xp, double vp, double2 cs, double hw, double &x,
+                                   double &d)
+{
+#pragma clang fp contract(off)
+    x = xp + vp * cs.y;
+    x = x - floor(x);
+    const double r = x - cs.x;
+    d = r - rint(r);
+    return fabs(d) < hw;
+}
+
+// Bins of an item: j = floor(x nb - 1/2) in [-1, nb - 1] (x in [0, 1]) and the
+// next one, wrapped; f the share of the second.
+__device__ inline void item_bins(double x, int nb, int &j0, int &j1, double &f)
+{
+#pragma clang fp contract(off)
+    const double g = x * (double)nb - 0.5;
+    const double jf = floor(g);
+    f = g - jf;
+    const int j = (int)jf;
+    j0 = j < 0 ? j + nb : j;
+    j1 = j + 1 >= nb ? j + 1 - nb : j + 1;
+}
+
+// Appends the wave's selected lanes (mask) to the queue at qn (uniform), after
+// handling what is queued if the new items would not fit.
+template <typename Handle>
+__device__ inline void enqueue(SweepQueue &q, int &qn, uint64_t mask, bool sel, double x,
+                               double d, int lane, Handle &&handle)
+{
+    const int n = __popcll(mask);
+    if (qn + n > WAVE) {
+        handle(qn);
+        qn = 0;
+    }
+    if (sel) {
+        const int k = qn + (int)__builtin_amdgcn_mbcnt_hi(
+                               (uint32_t)(mask >> 32),
+                               __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+        q.x[k] = x;
+        q.d[k] = d;
+        q.owner[k] = lane;
+    }
+    qn += n;
+}
+
 __global__ __launch_bounds__(256) void k_fill(float *__restrict__ H, int nb, float value)
 {
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nb; i += gridDim.x * blockDim.x)
@@ -60,38 +133,54 @@ __global__ __launch_bounds__(256) void k_sweep1d(int nb, int64_t count,
 {
 #pragma clang fp contract(off)
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    __shared__ SweepQueue queues[SWEEP_WAVES];
     float *hist = reinterpret_cast<float *>(smem);
     double2 *tab = reinterpret_cast<double2 *>(smem + align16((size_t)nb * sizeof(float)));
+    const int lane = lane_id(), wave = (int)(threadIdx.x / WAVE);
+    SweepQueue &q = queues[wave];
     for (int i = threadIdx.x; i < nb; i += blockDim.x)
         hist[i] = 0.0f;
     if (tabled)
         fill_steps(tab, steps, dt);
     __syncthreads();
+    // deposits the first n queued items, one per lane
+    auto handle = [&](int n) {
+        wave_lds_sync();
+        if (lane < n) {
+            const double x = q.x[lane], d = q.d[lane];
+            const double u = 1.0 - fabs(d) / hw;
+            const double weight = u * u;
+            int j0, j1;
+            double f;
+            item_bins(x, nb, j0, j1, f);
+            __hip_atomic_fetch_add(&hist[j0], (float)(weight * (1.0 - f)), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_fetch_add(&hist[j1], (float)(weight * f), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        wave_lds_sync();
+    };
+    int qn = 0;
+    // the wave walks its particles together (the queue needs every lane):
+    // lanes past the end test a clamped particle and never select it
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < count; p += stride) {
-        const double xp = x0[p], vp = v[p];
+    for (int64_t base = (int64_t)blockIdx.x * blockDim.x + wave * WAVE; base < count;
+         base += stride) {
+        const int64_t p = base + lane;
+        const bool live = p < count;
+        const int64_t pc = live ? p : count - 1;
+        const double xp = x0[pc], vp = v[pc];
         for (int t = 1; t <= steps; ++t) {
-            const double2 cs = step_consts(tab, tabled, t, steps, dt);
-            const double c = cs.x, shift = cs.y;
-            double x = xp + vp * shift;
-            x = x - floor(x);
-            const double r = x - c;
-            const double d = r - rint(r);
-            if (fabs(d) < hw) {
-                const double u = 1.0 - fabs(d) / hw;
-                const double weight = u * u;
-                const double g = x * (double)nb - 0.5;
-                const double jf = floor(g);
-                const double f = g - jf;
-                const int j = (int)jf;  // in [-1, nb-1]: x is in [0, 1]
-                const int j0 = wrap_index(j, nb), j1 = wrap_index(j + 1, nb);
-                __hip_atomic_fetch_add(&hist[j0], (float)(weight * (1.0 - f)), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_WORKGROUP);
-                __hip_atomic_fetch_add(&hist[j1], (float)(weight * f), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_WORKGROUP);
-            }
+            double x, d;
+            const bool sel = window_test(xp, vp, step_consts(tab, tabled, t, steps, dt), hw, x,
+                                         d) && live;
+            const uint64_t mask = __ballot(sel);
+            if (mask)
+                enqueue(q, qn, mask, sel, x, d, lane, handle);
         }
     }
+    if (qn)
+        handle(qn);
     __syncthreads();
     for (int i = threadIdx.x; i < nb; i += blockDim.x) {
         const float h = hist[i];
@@ -114,38 +203,60 @@ __global__ __launch_bounds__(256) void k_sweep1d_grad(int nb, int64_t count,
 {
 #pragma clang fp contract(off)
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    __shared__ SweepQueue queues[SWEEP_WAVES];
     double *dh = reinterpret_cast<double *>(smem);
     double2 *tab = reinterpret_cast<double2 *>(smem + align16((size_t)nb * sizeof(double)));
+    const int lane = lane_id(), wave = (int)(threadIdx.x / WAVE);
+    SweepQueue &q = queues[wave];
     for (int i = threadIdx.x; i < nb; i += blockDim.x)
         dh[i] = SEED ? 2.0 * ((double)H[i] - target[i]) : dH[i];
     if (tabled)
         fill_steps(tab, steps, dt);
     __syncthreads();
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < count; p += stride) {
-        const double xp = x0[p], vp = v[p];
-        double acc = 0.0;
-        for (int t = 1; t <= steps; ++t) {
-            const double2 cs = step_consts(tab, tabled, t, steps, dt);
-            const double c = cs.x, shift = cs.y;
-            double x = xp + vp * shift;
-            x = x - floor(x);
-            const double r = x - c;
-            const double d = r - rint(r);
-            if (fabs(d) < hw) {
-                const double u = 1.0 - fabs(d) / hw;
-                const double weight = u * u;
-                const double sgn = d > 0.0 ? 1.0 : (d < 0.0 ? -1.0 : 0.0);
-                const double dw = -2.0 * u * sgn / hw;
-                const double g = x * (double)nb - 0.5;
-                const double jf = floor(g);
-                const double f = g - jf;
-                const int j = (int)jf;  // in [-1, nb-1]
-                const double h0 = dh[wrap_index(j, nb)], h1 = dh[wrap_index(j + 1, nb)];
-                acc += dw * ((1.0 - f) * h0 + f * h1) + weight * (double)nb * (h1 - h0);
-            }
+    // adds the terms of the first n queued items to their particles' sums
+    auto handle = [&](int n) {
+        wave_lds_sync();
+        if (lane < n) {
+            const double x = q.x[lane], d = q.d[lane];
+            const double u = 1.0 - fabs(d) / hw;
+            const double weight = u * u;
+            const double sgn = d > 0.0 ? 1.0 : (d < 0.0 ? -1.0 : 0.0);
+            const double dw = -2.0 * u * sgn / hw;
+            int j0, j1;
+            double f;
+            item_bins(x, nb, j0, j1, f);
+            const double h0 = dh[j0], h1 = dh[j1];
+            __hip_atomic_fetch_add(&q.acc[q.owner[lane]],
+                                   dw * ((1.0 - f) * h0 + f * h1) + weight * (double)nb * (h1 - h0),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
-        dx0[p] = acc;
+        wave_lds_sync();
+    };
+    int qn = 0;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t base = (int64_t)blockIdx.x * blockDim.x + wave * WAVE; base < count;
+         base += stride) {
+        const int64_t p = base + lane;
+        const bool live = p < count;
+        const int64_t pc = live ? p : count - 1;
+        const double xp = x0[pc], vp = v[pc];
+        q.acc[lane] = 0.0;
+        for (int t = 1; t <= steps; ++t) {
+            double x, d;
+            const bool sel = window_test(xp, vp, step_consts(tab, tabled, t, steps, dt), hw, x,
+                                         d) && live;
+            const uint64_t mask = __ballot(sel);
+            if (mask)
+                enqueue(q, qn, mask, sel, x, d, lane, handle);
+        }
+        // the queue refers to these particles: drain it before moving on
+        if (qn) {
+            handle(qn);
+            qn = 0;
+        }
+        wave_lds_sync();
+        if (live)
+            dx0[p] = q.acc[lane];
     }
 }
 

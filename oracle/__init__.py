@@ -71,6 +71,9 @@ def lib():
         L.oracle_mass_matrix_scalar.argtypes = [i32p, C.c_int64, fpp, C.c_void_p, C.c_void_p,
                                                 C.c_void_p]
         L.oracle_mass_matrix_scalar.restype = C.c_int
+        L.oracle_mass_matrix_scalar_tsc.argtypes = [i32p, C.c_int64, fpp, C.c_void_p, C.c_void_p,
+                                                C.c_void_p]
+        L.oracle_mass_matrix_scalar_tsc.restype = C.c_int
         L.oracle_sweep1d.argtypes = [C.c_int, C.c_int64, C.c_void_p, C.c_void_p, C.c_int,
                                      C.c_double, C.c_double, C.c_void_p]
         L.oracle_sweep1d.restype = C.c_int
@@ -234,6 +237,22 @@ def mass_matrix_scalar(n, x, q, w, M=None):
     assert M.dtype == np.float64 and M.flags.c_contiguous
     rc = lib().oracle_mass_matrix_scalar(_grid(n3), int(q.size), xs, _ptr(q), _ptr(w), _ptr(M))
     _check(rc, "mass_matrix_scalar")
+    return M
+
+
+def mass_matrix_scalar_tsc(n, x, q, w, M=None):
+    """Scalar mass matrix with TSC weights (27 support nodes), 125-offset store
+    [nz, ny, nx, 125] fp64 (accumulated)."""
+    n3 = list(n)
+    keep = []
+    xs = _ptrs(list(x), keep)
+    q, w = _f32(q), _f32(w)
+    if M is None:
+        M = np.zeros((n3[2], n3[1], n3[0], 125), dtype=np.float64)
+    assert M.dtype == np.float64 and M.flags.c_contiguous
+    rc = lib().oracle_mass_matrix_scalar_tsc(_grid(n3), int(q.size), xs, _ptr(q), _ptr(w),
+                                             _ptr(M))
+    _check(rc, "mass_matrix_scalar_tsc")
     return M
 
 

@@ -365,6 +365,43 @@ int oracle_mass_matrix_scalar(const int32_t n[3], int64_t np, const float *const
     return 0;
 }
 
+/* [MM] §2.1 Eq.(6), scalar case, with TSC shape functions ([MM] §2.3 Eq.(12),
+ * order 2; the paper's TSC experiments, §4.1 Fig. 8): every ordered pair of
+ * the 27 support nodes of every particle,
+ *   M_{g, g+o} += q_p w_p W_{pg} W_{p,g+o},
+ * into a 125-offset store: M is fp64 [n_z][n_y][n_x][125] with
+ * o = (dx+2) + 5 (dy+2) + 25 (dz+2) for the node g + (dx,dy,dz), and is
+ * accumulated.  3D; n_k >= 5 (the 125 offsets are then distinct nodes). */
+int oracle_mass_matrix_scalar_tsc(const int32_t n[3], int64_t np, const float *const x[3],
+                                  const float *q, const float *w, double *M)
+{
+    if (n[0] < 5 || n[1] < 5 || n[2] < 5 || np < 0)
+        return -1;
+    for (int64_t p = 0; p < np; ++p) {
+        const double s = (double)q[p] * (double)w[p];
+        int64_t base[3];
+        double W[3][3];
+        for (int k = 0; k < 3; ++k)
+            oracle_shape_1d(2, (double)x[k][p], &base[k], W[k]);
+        for (int az = 0; az < 3; ++az)
+            for (int ay = 0; ay < 3; ++ay)
+                for (int ax = 0; ax < 3; ++ax) {
+                    const int64_t g = wrap(base[0] + ax, n[0]) +
+                                      (int64_t)n[0] * (wrap(base[1] + ay, n[1]) +
+                                                       (int64_t)n[1] * wrap(base[2] + az, n[2]));
+                    const double wg = W[0][ax] * W[1][ay] * W[2][az];
+                    for (int bz = 0; bz < 3; ++bz)
+                        for (int by = 0; by < 3; ++by)
+                            for (int bx = 0; bx < 3; ++bx) {
+                                const double wh = W[0][bx] * W[1][by] * W[2][bz];
+                                const int o = (bx - ax + 2) + 5 * (by - ay + 2) + 25 * (bz - az + 2);
+                                M[g * 125 + o] += s * wg * wh;
+                            }
+                }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* 1-D windowed sweep deposit                                                */
 /* ------------------------------------------------------------------------ */

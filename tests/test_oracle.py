@@ -678,3 +678,80 @@ def test_sweep_grad_zero_when_never_selected(orc):
     dH = np.linspace(-1, 1, 32)
     g = orc.sweep1d_grad(32, [0.05, 0.3], [0.0, 0.0], 10, 0.02, 0.01, dH)
     assert g[0] == 0.0 and g[1] != 0.0
+
+
+# ---------------------------------------------------------------------------
+# Scalar mass matrix with TSC weights  ([MM] Eq.(6) scalar case, §2.3 order 2)
+
+OFFS5 = [(dx, dy, dz) for dz in (-2, -1, 0, 1, 2) for dy in (-2, -1, 0, 1, 2)
+         for dx in (-2, -1, 0, 1, 2)]
+
+
+def _weights_matrix_tsc(orc, n, x):
+    """Dense TSC W (Ng x Np) from the oracle's own order-2 deposit."""
+    npart = x[0].size
+    W = np.zeros((int(np.prod(n)), npart))
+    for p in range(npart):
+        J = orc.deposit(3, n, 2, [a[p:p + 1] for a in x],
+                        [np.float32([1]), np.float32([0]), np.float32([0])],
+                        np.float32([1]), np.float32([1]))
+        W[:, p] = J[0].ravel()
+    return W
+
+
+def test_tsc_scalar_mass_matrix_equals_dense_contraction(orc):
+    """[MM] Eq.(10): W diag(q w) W^T on a 5^3 grid (the 125 offsets are then every
+    node once), against the 125-offset store."""
+    r = np.random.default_rng(45)
+    n = [5, 5, 5]
+    x, _, q, w, _ = _mm_inputs(r, n, 120)
+    M = orc.mass_matrix_scalar_tsc(n, x, q, w)
+    W = _weights_matrix_tsc(orc, n, x)
+    dense = W @ np.diag(q.astype(np.float64) * w.astype(np.float64)) @ W.T
+    store = np.zeros((125, 125))
+    for gz in range(5):
+        for gy in range(5):
+            for gx in range(5):
+                g = gx + 5 * (gy + 5 * gz)
+                for o, (dx, dy, dz) in enumerate(OFFS5):
+                    g2 = (gx + dx) % 5 + 5 * (((gy + dy) % 5) + 5 * ((gz + dz) % 5))
+                    store[g, g2] += M[gz, gy, gx, o]
+    assert np.abs(store - dense).max() < 1e-12 * max(1.0, np.abs(dense).max())
+
+
+def test_tsc_scalar_mass_matrix_symmetry_and_charge(orc):
+    """Eq.(11) symmetry; row sums equal the TSC deposit of q w; total sum q w."""
+    r = np.random.default_rng(46)
+    n = [7, 6, 8]
+    x, _, q, w, _ = _mm_inputs(r, n, 400)
+    M = orc.mass_matrix_scalar_tsc(n, x, q, w)
+    for o, (dx, dy, dz) in enumerate(OFFS5):
+        mo = OFFS5.index((-dx, -dy, -dz))
+        rolled = np.roll(M[..., mo], shift=(-dz, -dy, -dx), axis=(0, 1, 2))
+        assert np.abs(M[..., o] - rolled).max() < 1e-13
+    ones, zeros = np.ones_like(q), np.zeros_like(q)
+    J = orc.deposit(3, n, 2, x, [ones, zeros, zeros], q, w)
+    assert np.abs(M.sum(axis=3) - J[0]).max() < 1e-12
+    assert abs(M.sum() - float(np.sum(q.astype(np.float64) * w.astype(np.float64)))) < 1e-10
+
+
+def test_tsc_scalar_mass_matrix_single_particle(orc):
+    # x = (3.0, 2.25, 3.75) on 8^3, q w = 2.  TSC weights by hand ([MM] §2.3):
+    # x: frac 0 -> base 2, (1/8, 3/4, 1/8); y: frac 1/4 < 1/2 -> base 1,
+    # (1/32, 11/16, 9/32); z: frac 3/4 -> base 3, (9/32, 11/16, 1/32)
+    x = _one([3.0, 2.25, 3.75])
+    M = orc.mass_matrix_scalar_tsc([8, 8, 8], x, np.float32([2.0]), np.float32([1.0]))
+    wx = {2: 0.125, 3: 0.75, 4: 0.125}
+    wy = {1: 0.03125, 2: 0.6875, 3: 0.28125}
+    wz = {3: 0.28125, 4: 0.6875, 5: 0.03125}
+    nz = 0
+    for gz in wz:
+        for gy in wy:
+            for gx in wx:
+                for o, (dx, dy, dz) in enumerate(OFFS5):
+                    hx, hy, hz = gx + dx, gy + dy, gz + dz
+                    if hx in wx and hy in wy and hz in wz:
+                        assert M[gz, gy, gx, o] == 2.0 * (wx[gx] * wy[gy] * wz[gz]) * (
+                            wx[hx] * wy[hy] * wz[hz])
+                        nz += 1
+    assert nz == 729 and np.count_nonzero(M) == 729

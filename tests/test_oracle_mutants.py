@@ -68,6 +68,10 @@ MUTANTS = [
      "const double s = (double)q[p] * (double)w[p];", "const double s = (double)q[p];"),
     ("scalar mass matrix weighted by the first node twice",
      "M[g * 27 + o] += s * wg * wh;", "M[g * 27 + o] += s * wg * wg;"),
+    ("TSC scalar mass matrix with the z offset reversed",
+     "25 * (bz - az + 2)", "25 * (az - bz + 2)"),
+    ("TSC scalar mass matrix without the second node's weight",
+     "M[g * 125 + o] += s * wg * wh;", "M[g * 125 + o] += s * wg;"),
 ]
 
 

@@ -16,7 +16,8 @@ Other workloads (--workload): cic2d_512_ppc16 (2-D CIC 512^2), tsc3d_128_blob
 (3-D TSC clustered, T from --tile), mass_64_ppc64 (ECSIM mass matrix 64^3: cell
 sort + MFMA assembly), mass_f64_64_ppc64 (the same in fp64), mass_scalar_64_ppc64
 (the scalar mass matrix, coefficient q w, on the same particles), sweep1d_2000
-(1-D windowed sweep), sweep1d_grad_1e7 (the sweep's loss gradient, 10^7 particles:
+(1-D windowed sweep), mass_tsc_scalar_64_ppc64 (the scalar matrix with TSC
+weights, support-group sort + MFMA assembly), sweep1d_grad_1e7 (the sweep's loss gradient, 10^7 particles:
 forward sweep, seed and reverse gather in one library call).
 
 Prints ONE JSON line (rank 0).  Only one GPU is used: --gpus above 1 exits.
@@ -51,7 +52,8 @@ def parse():
     ap.add_argument("--workload", default=HEADLINE,
                     choices=["sweep1d_2000", "cic2d_512_ppc16", "cic3d_128_ppc32",
                              "tsc3d_128_blob", "mass_64_ppc64", "mass_f64_64_ppc64",
-                             "mass_scalar_64_ppc64", "sweep1d_grad_1e7"])
+                             "mass_scalar_64_ppc64", "mass_tsc_scalar_64_ppc64",
+                             "sweep1d_grad_1e7"])
     ap.add_argument("--tile", type=int, default=0, help="tile edge T (0 = the workload's)")
     ap.add_argument("--block", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -482,6 +484,86 @@ def bench_sweep(args, torch, pcg):
                 roofline=None, kernels=kernels, extra={}, cpu=cpu, unit="particle-steps/s")
 
 
+# -------------------------------------------------- scalar mass matrix, TSC weights
+
+def bench_mass_tsc(args, torch, pcg):
+    """Scalar mass matrix with TSC weights on the mass_64_ppc64 particles: re-sort
+    by support base (T = 1, order = 2) from the previous layout, then assemble."""
+    import numpy as np
+
+    import synthetic
+
+    progress("generating mass_64_ppc64")
+    wl = synthetic.workload("mass_64_ppc64")
+    n, cnt = wl.n, wl.count
+    dev = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    x = [t(a) for a in wl.x]
+    shuffled = x + [t(wl.q), t(wl.w)]
+    M = torch.zeros(n[2], n[1], n[0], 125, dtype=torch.float32, device=dev)
+    nc = n[0] * n[1] * n[2]
+    perm = torch.empty(cnt, dtype=torch.int32, device=dev)
+    keys = torch.empty(cnt, dtype=torch.int32, device=dev)
+    sws = torch.empty(pcg.pcg_sort_workspace_bytes(3, n, cnt, 1), dtype=torch.uint8, device=dev)
+    off0 = torch.empty(nc + 1, dtype=torch.int32, device=dev)
+    cur = [torch.empty_like(a) for a in shuffled]
+    pcg.pcg_tile_sort(3, n, 2, 1, x, shuffled, outs=cur, perm=perm, sorted_keys=keys,
+                      tile_offsets=off0, workspace=sws)
+    torch.cuda.synchronize()
+    prev = pcg.Layout(T=1, order=2, tile_offsets=off0, n_partitioned=cnt, drift=0)
+    off1 = torch.empty(nc + 1, dtype=torch.int32, device=dev)
+    nxt = [torch.empty_like(a) for a in cur]
+    groups = pcg.Layout(T=1, order=2, tile_offsets=off1, n_partitioned=cnt, drift=0)
+
+    def assemble(variant):
+        pcg.assemble_mass_matrix_scalar_tsc(n, nxt[0:3], nxt[3], nxt[4], M, groups, variant)
+
+    def step():
+        M.zero_()
+        pcg.pcg_tile_sort(3, n, 2, 1, cur[0:3], cur, outs=nxt, want_perm=False, want_keys=False,
+                          tile_offsets=off1, workspace=sws, prev=prev)
+        assemble(pcg.PCG_MASS_MFMA)
+
+    progress("timing steps")
+    ms, wall, kt = time_steps(torch, pcg, step, args.steps, args.warmup)
+    progress(f"{ms:.4f} ms per step")
+    kname = "mass_tsc_mfma"
+    flops = cnt * 27.0 * 27.0 * 2.0    # dense 27 x 27 node pairs x 2 flops
+    roof = roofline_entry(kt, kname, flops_per_launch=flops)
+    if roof:
+        roof["traffic"] = measured_traffic(kname, "mass_tsc_scalar_64_ppc64")
+    kernels = {nm: dict(avg_us=round(kk["avg_us"], 2),
+                        launches_per_step=kk["launches"] / args.steps) for nm, kk in kt.items()}
+    extra = {}
+    for nm, var in (("valu", pcg.PCG_MASS_VALU), ("mfma", pcg.PCG_MASS_MFMA)):
+        extra[f"mass_{nm}_ms"] = round(time_plain(torch, lambda: (M.zero_(), assemble(var)), 5), 4)
+    extra["mfma_speedup_vs_valu"] = round(extra["mass_valu_ms"] / extra["mass_mfma_ms"], 2)
+    extra["flush_atomics_per_launch"] = 729 * nc
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        progress("timing the oracle on the host")
+        m = 1 << 18
+        t0 = time.perf_counter()
+        oracle.mass_matrix_scalar_tsc(n, [a[:m] for a in wl.x], wl.q[:m], wl.w[:m])
+        per = (time.perf_counter() - t0) / m
+        m2 = int(min(cnt, max(m, args.cpu_seconds / per)))
+        t0 = time.perf_counter()
+        oracle.mass_matrix_scalar_tsc(n, [a[:m2] for a in wl.x], wl.q[:m2], wl.w[:m2])
+        sec = time.perf_counter() - t0
+        cpu = dict(value=round(m2 / sec, 1), unit="particles/s", cores=1, kind="oracle",
+                   sample=f"first {m2} of {cnt} particles: fp64 per-particle 27 x 27 outer "
+                          f"products, {sec:.1f} s, 1 thread")
+    config = dict(workload="scalar 3-D TSC mass matrix (coefficient q w) 64^3, 64 ppc "
+                           "(support-group sort + MFMA assembly)",
+                  particles=cnt, grid=n,
+                  step="zero M + support-group re-sort of x, q, w from the previous layout + "
+                       "MFMA assembly with an atomic flush")
+    return dict(value=cnt / (ms * 1e-3), ms=ms, wall=wall, dtype="f32", config=config,
+                roofline=roof, kernels=kernels, extra=extra, cpu=cpu, unit="particles/s")
+
+
 # ------------------------------------------------------------- 1-D sweep, reverse
 
 FP64_VECTOR_OPS = 39.3e12   # MI355X fp64 vector instructions x lanes per s (78.6 TFLOP/s / 2)
@@ -577,6 +659,8 @@ def main():
         r = bench_mass(args, torch, pcg)
     elif args.workload == "mass_f64_64_ppc64":
         r = bench_mass(args, torch, pcg, f64=True)
+    elif args.workload == "mass_tsc_scalar_64_ppc64":
+        r = bench_mass_tsc(args, torch, pcg)
     elif args.workload == "sweep1d_grad_1e7":
         r = bench_sweep_grad(args, torch, pcg)
     elif args.workload == "mass_scalar_64_ppc64":

@@ -254,6 +254,27 @@ pcg_status assemble_mass_matrix_scalar(const pcg_grid *grid, const pcg_particles
                                        const pcg_tile *cells, int32_t variant, float *M,
                                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* Scalar mass matrix with TSC weights ([MM] §2.1 Eq.(6) scalar case, §2.3
+ * Eq.(12) at order 2; the paper's TSC runs, §4.1 Fig. 8):
+ *   M_{g, g+o} += q_p w_p W_{pg} W_{p,g+o}
+ * over every ordered pair of the 27 TSC support nodes of every particle.
+ * 3-D, every n_k >= 5.
+ * M: device fp32 [n_z][n_y][n_x][125], accumulated; o = (dx+2) + 5(dy+2) +
+ *   25(dz+2) for the node g + (dx,dy,dz) (wrapped).
+ * groups: a T = 1, order = 2 layout from pcg_tile_sort (group = the particles
+ *   sharing one TSC support base, [MM] §3.3), or NULL (flat path).  With it,
+ *   each group's 27 x 27 block is one product over its particles on the matrix
+ *   cores (PCG_MASS_MFMA) or vector FMAs (PCG_MASS_VALU), added to M with
+ *   device atomics ([MM] §3.4).  A particle in a slice whose group it is not in,
+ *   and the tail [n_partitioned, count), take the flat path (729 atomics each).
+ * No workspace.  Calls that write the same M on different streams race.
+ * Errors: PCG_EINVAL for n_k < 5, a NULL array, a count outside [0, 2^30), a
+ *   layout that is not T = 1, order = 2, or MFMA/VALU without a layout;
+ *   PCG_EUNSUPPORTED for dim != 3. */
+pcg_status assemble_mass_matrix_scalar_tsc(const pcg_grid *grid, const pcg_particles *particles,
+                                           const pcg_tile *groups, int32_t variant, float *M,
+                                           void *stream);
+
 /* fp64 variants of the two matrices ([MM] §4 and §4.1, Figs. 6-7: the CIC
  * scalar and tensor assemblies are measured with every operand in FP64; §5
  * "Tile-support matching and portability" names AMD's FP64 16x16x4 product):

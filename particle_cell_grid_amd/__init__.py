@@ -71,6 +71,9 @@ _lib.assemble_mass_matrix.restype = C.c_int32
 _lib.assemble_mass_matrix_scalar.argtypes = [_P(Grid), _P(Particles), _P(Tile), C.c_int32,
                                              C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
 _lib.assemble_mass_matrix_scalar.restype = C.c_int32
+_lib.assemble_mass_matrix_scalar_tsc.argtypes = [_P(Grid), _P(Particles), _P(Tile), C.c_int32,
+                                                 C.c_void_p, C.c_void_p]
+_lib.assemble_mass_matrix_scalar_tsc.restype = C.c_int32
 _lib.assemble_mass_matrix_f64.argtypes = _lib.assemble_mass_matrix.argtypes
 _lib.assemble_mass_matrix_f64.restype = C.c_int32
 _lib.assemble_mass_matrix_scalar_f64.argtypes = _lib.assemble_mass_matrix_scalar.argtypes
@@ -330,6 +333,22 @@ def assemble_mass_matrix_scalar(n: Sequence[int], x: List[torch.Tensor], q: torc
     st = getattr(_lib, fn)(C.byref(g), C.byref(P), C.byref(tile) if tile is not None else None,
                            int(variant), _ptr(M), _ptr(workspace), wsb, _stream())
     _check(st, fn)
+    return M
+
+
+def assemble_mass_matrix_scalar_tsc(n: Sequence[int], x: List[torch.Tensor], q: torch.Tensor,
+                                    w: torch.Tensor, M: torch.Tensor,
+                                    groups: Optional[Layout] = None,
+                                    variant: int = PCG_MASS_AUTO):
+    """M[nz, ny, nx, 125] (fp32) += the scalar mass matrix with TSC weights.  groups:
+    a T = 1, order = 2 layout (particles grouped by support base), or None (flat)."""
+    g = make_grid(3, n)
+    P = _particles(q.numel(), x, None, q, w)
+    tile = groups.to_c() if groups is not None else None
+    st = _lib.assemble_mass_matrix_scalar_tsc(C.byref(g), C.byref(P),
+                                              C.byref(tile) if tile is not None else None,
+                                              int(variant), _ptr(M), _stream())
+    _check(st, "assemble_mass_matrix_scalar_tsc")
     return M
 
 

@@ -1,0 +1,326 @@
+// mass_tsc.hip -- scalar mass matrix with TSC weights ([MM] Pennati & Markidis,
+// "Mass Matrix Assembly on Tensor Cores for Implicit PIC": §2.1 Eq.(6) in the
+// scalar case, §2.3 Eq.(12) at order 2, §3.2-§3.4; the paper's TSC runs, §4.1
+// Fig. 8).
+//
+// Each particle has 27 support nodes; its node pairs span offsets -2..2 per
+// axis, so a node row of M holds 125 values, o = (dx+2) + 5 (dy+2) + 25 (dz+2).
+// Particles sorted by their TSC support base (pcg_tile_sort with T = 1,
+// order = 2) form groups that share all 27 nodes ([MM] §3.3 "support groups";
+// the key already is the group, so one pass suffices).  Per group the 27 x 27
+// block T[a][b] = sum_p c_p W_a(p) W_b(p) (c = q w) is one product over the
+// group's particles: rows padded to 32 and computed as the three tiles (0,0),
+// (0,1), (1,1) of v_mfma_f32_16x16x4_f32 per 4 particles (T is symmetric, so
+// tile (1,0) is tile (0,1) transposed).  The block is added to M with device
+// atomics, 729 per group ([MM] §3.4).
+//
+// Variants: MFMA, VALU (each lane sums its node pairs over the staged
+// particles) and FLAT (one thread per particle, 729 atomics; also the unsorted
+// tail).  A particle found in a slice whose group it does not belong to (a
+// stale layout) is deposited by its own lane with the flat path.
+#include <algorithm>
+
+#include "common.hpp"
+
+namespace pcg {
+namespace {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int TSC_NODES = 27;
+constexpr int TSC_OFFS = 125;
+constexpr int TSC_WAVES = 4;
+
+struct TscArgs {
+    int n[3];
+    float nf[3];
+    const float *x[3];
+    const float *q;
+    const float *w;
+    float *M;  // [n_z][n_y][n_x][125]
+    const uint32_t *offsets;
+    int64_t n_part;
+    uint32_t ngroups;
+};
+
+// One particle's TSC support: wrapped base node per axis and the 27 weights,
+// node a = ax + 3 ay + 9 az.  The base is the node below the nearest one
+// (fraction < 1/2: floor - 1, else floor), decided exactly in fp32; with
+// t = x - (base + 1) in [-1/2, 1/2) the three weights are (1/2 - t)^2 / 2,
+// 3/4 - t^2 and (1/2 + t)^2 / 2 ([MM] §2.3 Eq.(12) at order 2).
+struct TscParticle {
+    int base[3];
+    float W[TSC_NODES];
+    float c;
+};
+
+__device__ inline TscParticle tsc_particle(const TscArgs &m, float x0, float x1, float x2,
+                                           float q, float w)
+{
+    TscParticle P;
+    const float xs[3] = {x0, x1, x2};
+    float wk[3][3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const float x = clamp_coord(xs[k], m.nf[k]);
+        const float fl = floorf(x);
+        const bool low = x - fl < 0.5f;
+        const float b = low ? fl - 1.0f : fl;
+        const float t = x - (b + 1.0f);
+        const int bi = (int)b;  // in [-1, n]
+        P.base[k] = bi < 0 ? bi + m.n[k] : (bi >= m.n[k] ? bi - m.n[k] : bi);
+        wk[k][0] = 0.5f * (0.5f - t) * (0.5f - t);
+        wk[k][1] = 0.75f - t * t;
+        wk[k][2] = 0.5f * (0.5f + t) * (0.5f + t);
+    }
+#pragma unroll
+    for (int a = 0; a < TSC_NODES; ++a)
+        P.W[a] = wk[0][a % 3] * wk[1][(a / 3) % 3] * wk[2][a / 9];
+    P.c = q * w;
+    return P;
+}
+
+__device__ inline int wrap_add(int b, int d, int n)
+{
+    const int i = b + d;
+    return i >= n ? i - n : i;
+}
+
+// Node a of a support whose base is `base` (wrapped), as a linear index.
+__device__ inline int64_t tsc_node(const TscArgs &m, const int *base, int a)
+{
+    const int gx = wrap_add(base[0], a % 3, m.n[0]);
+    const int gy = wrap_add(base[1], (a / 3) % 3, m.n[1]);
+    const int gz = wrap_add(base[2], a / 9, m.n[2]);
+    return gx + (int64_t)m.n[0] * (gy + (int64_t)m.n[1] * gz);
+}
+
+// Offset of node b seen from node a of one support.
+__device__ inline int tsc_offset(int a, int b)
+{
+    return (b % 3 - a % 3 + 2) + 5 * ((b / 3) % 3 - (a / 3) % 3 + 2) + 25 * (b / 9 - a / 9 + 2);
+}
+
+// The particle's whole 27 x 27 contribution with global atomics.
+__device__ inline void tsc_deposit_global(const TscArgs &m, const TscParticle &P)
+{
+    for (int a = 0; a < TSC_NODES; ++a) {
+        float *row = m.M + (size_t)tsc_node(m, P.base, a) * TSC_OFFS;
+        const float ca = P.c * P.W[a];
+        for (int b = 0; b < TSC_NODES; ++b)
+            atomic_add_f32(&row[tsc_offset(a, b)], ca * P.W[b]);
+    }
+}
+
+__device__ inline float ld(const float *base, int64_t p) { return base[p]; }
+
+__global__ __launch_bounds__(256) void k_mass_tsc_flat(TscArgs m, int64_t begin, int64_t end)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t p = begin + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < end; p += stride)
+        tsc_deposit_global(m, tsc_particle(m, ld(m.x[0], p), ld(m.x[1], p), ld(m.x[2], p),
+                                           ld(m.q, p), ld(m.w, p)));
+}
+
+// Per-wave LDS: one staged 64-particle batch (rows padded to 32 nodes, the pads
+// zero), reused for the 32 x 32 block once the batches are done.
+struct TscStage {
+    float W[64][32];
+    float c[64];
+};
+union TscScratch {
+    TscStage s;
+    float Tm[32][33];
+};
+
+__device__ inline void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One wave per group: group = the wave's global index (groups are the support
+// base nodes, linear index gx + n_x (gy + n_y gz)).
+template <bool MFMA>
+__global__ __launch_bounds__(TSC_WAVES * WAVE) void k_mass_tsc_group(TscArgs m)
+{
+    __shared__ TscScratch scratch[TSC_WAVES];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), lane = lane_id();
+    TscScratch &ws = scratch[wave];
+    // neighbouring groups (which share M rows) on one XCD: blocks are dealt to
+    // the 8 XCDs round-robin
+    const uint32_t nblocks = (m.ngroups + TSC_WAVES - 1) / TSC_WAVES;
+    const uint32_t per = (nblocks + 7) / 8;
+    const uint32_t blk = (blockIdx.x % 8) * per + blockIdx.x / 8;
+    const uint32_t g = blk * TSC_WAVES + wave;
+    if (blk >= nblocks || g >= m.ngroups)
+        return;
+    const int64_t lo = std::min<int64_t>(m.offsets[g], m.n_part);
+    const int64_t hi = std::min<int64_t>(m.offsets[g + 1], m.n_part);
+    if (hi <= lo)
+        return;
+    int gb[3];
+    gb[0] = (int)(g % (uint32_t)m.n[0]);
+    gb[1] = (int)((g / (uint32_t)m.n[0]) % (uint32_t)m.n[1]);
+    gb[2] = (int)(g / ((uint32_t)m.n[0] * (uint32_t)m.n[1]));
+
+    const int r = lane & 15, kk = lane >> 4;
+    floatx4 acc00 = {0, 0, 0, 0}, acc01 = {0, 0, 0, 0}, acc11 = {0, 0, 0, 0};
+    // VALU: lane owns node pairs lane + 64 k (k < 12; 729 pairs)
+    constexpr int PAIRS = (TSC_NODES * TSC_NODES + WAVE - 1) / WAVE;
+    float tv[PAIRS];
+#pragma unroll
+    for (int k = 0; k < PAIRS; ++k)
+        tv[k] = 0.0f;
+
+    for (int64_t base = lo; base < hi; base += 64) {
+        const int64_t p = std::min<int64_t>(base + lane, hi - 1);  // clamped
+        const bool valid = base + lane < hi;
+        const TscParticle P =
+            tsc_particle(m, ld(m.x[0], p), ld(m.x[1], p), ld(m.x[2], p), ld(m.q, p), ld(m.w, p));
+        const bool home = P.base[0] == gb[0] && P.base[1] == gb[1] && P.base[2] == gb[2];
+        const bool take = valid && home;
+        if (valid && !home)
+            tsc_deposit_global(m, P);  // stale layout: this lane deposits it alone
+        wave_sync();
+#pragma unroll
+        for (int a = 0; a < 32; a += 4) {
+            float4 v4;
+            v4.x = take && a + 0 < TSC_NODES ? P.W[a + 0] : 0.0f;
+            v4.y = take && a + 1 < TSC_NODES ? P.W[a + 1] : 0.0f;
+            v4.z = take && a + 2 < TSC_NODES ? P.W[a + 2] : 0.0f;
+            v4.w = take && a + 3 < TSC_NODES ? P.W[a + 3] : 0.0f;
+            *reinterpret_cast<float4 *>(&ws.s.W[lane][a]) = v4;
+        }
+        ws.s.c[lane] = take ? P.c : 0.0f;
+        wave_sync();
+        const int nb = (int)std::min<int64_t>(64, hi - base);
+        if (MFMA) {
+            const int steps = (nb + 3) >> 2;
+            for (int i = 0; i < steps; ++i) {
+                const int q = 4 * i + kk;
+                const float a0 = ws.s.W[q][r], a1 = ws.s.W[q][16 + r];
+                const float cq = ws.s.c[q];
+                const float b0 = cq * a0, b1 = cq * a1;
+                acc00 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc00, 0, 0, 0);
+                acc01 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc01, 0, 0, 0);
+                acc11 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc11, 0, 0, 0);
+            }
+        } else {
+            for (int q = 0; q < nb; ++q) {
+                const float cq = ws.s.c[q];
+#pragma unroll
+                for (int k = 0; k < PAIRS; ++k) {
+                    const int pr = lane + WAVE * k;
+                    if (pr < TSC_NODES * TSC_NODES)
+                        tv[k] += cq * ws.s.W[q][pr / TSC_NODES] * ws.s.W[q][pr % TSC_NODES];
+                }
+            }
+        }
+    }
+    wave_sync();
+    if (MFMA) {
+        // register i of this lane holds D[4 (lane / 16) + i][lane % 16]; tile
+        // (1,0) is filled as tile (0,1) transposed
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 4 * kk + i, col = r;
+            ws.Tm[row][col] = acc00[i];
+            ws.Tm[row][16 + col] = acc01[i];
+            ws.Tm[16 + col][row] = acc01[i];
+            ws.Tm[16 + row][16 + col] = acc11[i];
+        }
+        wave_sync();
+    }
+#pragma unroll
+    for (int k = 0; k < PAIRS; ++k) {
+        const int pr = lane + WAVE * k;
+        if (pr < TSC_NODES * TSC_NODES) {
+            const int a = pr / TSC_NODES, b = pr % TSC_NODES;
+            const float v = MFMA ? ws.Tm[a][b] : tv[k];
+            atomic_add_f32(&m.M[(size_t)tsc_node(m, gb, a) * TSC_OFFS + tsc_offset(a, b)], v);
+        }
+    }
+}
+
+}  // namespace
+}  // namespace pcg
+
+using namespace pcg;
+
+extern "C" pcg_status assemble_mass_matrix_scalar_tsc(const pcg_grid *grid,
+                                                      const pcg_particles *particles,
+                                                      const pcg_tile *groups, int32_t variant,
+                                                      float *M, void *stream)
+{
+    const char *who = "assemble_mass_matrix_scalar_tsc";
+    clear_error();
+    PCG_TRY(check_grid(grid, who));
+    if (grid->dim != 3)
+        return fail(PCG_EUNSUPPORTED, "%s: only 3-D grids (dim = %d)", who, grid->dim);
+    for (int k = 0; k < 3; ++k)
+        if (grid->n[k] < 5)
+            return fail(PCG_EINVAL, "%s: n[%d] = %d < 5 (the 125 offsets must be distinct nodes)",
+                        who, k, grid->n[k]);
+    if (!particles || !M)
+        return fail(PCG_EINVAL, "%s: particles or M is NULL", who);
+    if (variant < PCG_MASS_AUTO || variant > PCG_MASS_FLAT)
+        return fail(PCG_EINVAL, "%s: unknown variant %d", who, variant);
+    const int64_t count = particles->count;
+    if (count < 0 || count >= (int64_t(1) << 30))
+        return fail(PCG_EINVAL, "%s: count %lld outside [0, 2^30)", who, (long long)count);
+    if (count > 0 && (!particles->x[0] || !particles->x[1] || !particles->x[2] ||
+                      !particles->q || !particles->w))
+        return fail(PCG_EINVAL, "%s: x, q or w is NULL", who);
+    const bool grouped = variant != PCG_MASS_FLAT && groups;
+    if (!groups && (variant == PCG_MASS_MFMA || variant == PCG_MASS_VALU))
+        return fail(PCG_EINVAL, "%s: the %s variant needs a support-group layout", who,
+                    variant == PCG_MASS_VALU ? "VALU" : "MFMA");
+    if (grouped) {
+        if (groups->T != 1 || groups->order != 2)
+            return fail(PCG_EINVAL,
+                        "%s: groups must be a T = 1, order = 2 layout (T = %d, order = %d)", who,
+                        groups->T, groups->order);
+        if (!groups->tile_offsets)
+            return fail(PCG_EINVAL, "%s: group offsets are NULL", who);
+        if (groups->n_partitioned < 0 || groups->n_partitioned > count)
+            return fail(PCG_EINVAL, "%s: n_partitioned outside [0, count]", who);
+    }
+    TscArgs m{};
+    for (int k = 0; k < 3; ++k) {
+        m.n[k] = grid->n[k];
+        m.nf[k] = (float)grid->n[k];
+        m.x[k] = particles->x[k];
+    }
+    m.q = particles->q;
+    m.w = particles->w;
+    m.M = M;
+    m.ngroups = (uint32_t)((int64_t)grid->n[0] * grid->n[1] * grid->n[2]);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (count == 0)
+        return PCG_OK;
+    auto flat = [&](int64_t begin, int64_t end) -> pcg_status {
+        if (end <= begin)
+            return PCG_OK;
+        const int64_t blocks =
+            std::min<int64_t>((end - begin + 255) / 256, (int64_t)device_cus() * 32);
+        return launch("mass_tsc_flat", k_mass_tsc_flat, dim3((unsigned)blocks), dim3(256), 0, st,
+                      m, begin, end);
+    };
+    if (!grouped)
+        return flat(0, count);
+    m.offsets = groups->tile_offsets;
+    m.n_part = groups->n_partitioned;
+    if (m.n_part > 0) {
+        const uint32_t nblocks = (m.ngroups + TSC_WAVES - 1) / TSC_WAVES;
+        const uint32_t blocks = (nblocks + 7) / 8 * 8;
+        if (variant == PCG_MASS_VALU)
+            PCG_TRY(launch("mass_tsc_valu", k_mass_tsc_group<false>, dim3(blocks),
+                           dim3(TSC_WAVES * WAVE), 0, st, m));
+        else
+            PCG_TRY(launch("mass_tsc_mfma", k_mass_tsc_group<true>, dim3(blocks),
+                           dim3(TSC_WAVES * WAVE), 0, st, m));
+    }
+    return flat(groups->n_partitioned, count);
+}

@@ -22,7 +22,7 @@ import sys
 
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 KERNEL_SOURCES = {"deposit": "deposit.hip", "sort": "sort.hip", "mass": "mass.hip",
-                  "sweep": "sweep.hip"}
+                  "mass_tsc": "mass_tsc.hip", "sweep": "sweep.hip"}
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30          # the benchmark's context copy: 2^28 fp32 read and written
 
@@ -31,7 +31,8 @@ def source_digest(kernel):
     """sha1 over the file that holds `kernel` (named <file>_<what>) and the
     headers every kernel file includes."""
     h = hashlib.sha1()
-    for f in (KERNEL_SOURCES[kernel.split("_")[0]], "common.hpp", "layout.hpp", "regroup.hpp"):
+    key = "mass_tsc" if kernel.startswith("mass_tsc_") else kernel.split("_")[0]
+    for f in (KERNEL_SOURCES[key], "common.hpp", "layout.hpp", "regroup.hpp"):
         h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()
 
@@ -60,6 +61,10 @@ def tap_name(kernel):
     last = targs[-1].strip() if targs else ""
     if base == "k_deposit_tiled":
         return "deposit_regroup" if last == "true" else "deposit_tiled"
+    if base == "k_mass_tsc_group":
+        return "mass_tsc_mfma" if last == "true" else "mass_tsc_valu"
+    if base == "k_mass_tsc_flat":
+        return "mass_tsc_flat"
     if base.startswith("k_mass_") and targs:
         # <MFMA, scalar, real> for the column kernel, <scalar, real> otherwise
         scalar = "mass_scalar_" if targs[-2].strip() == "true" else "mass_"

@@ -37,7 +37,8 @@ def test_header_declares_the_entry_points():
     for n in ["pcg_tile_sort", "pcg_sort_workspace_bytes", "deposit_currents",
               "pcg_deposit_workspace_bytes", "deposit_currents_regroup",
               "pcg_deposit_regroup_workspace_bytes", "pcg_mass_workspace_bytes", "assemble_mass_matrix",
-              "assemble_mass_matrix_scalar", "assemble_mass_matrix_f64",
+              "assemble_mass_matrix_scalar", "assemble_mass_matrix_scalar_tsc",
+              "assemble_mass_matrix_f64",
               "assemble_mass_matrix_scalar_f64", "deposit_sweep1d", "deposit_sweep1d_grad",
               "deposit_sweep1d_loss_grad",
               "pcg_status_string", "pcg_last_error", "pcg_version", "pcg_timing_enable",
@@ -251,6 +252,20 @@ def test_mass_and_sweep_validation(lib):
     assert scall(variant=1, cells=C.byref(c1), ws=None) == EWORKSPACE
     assert scall(variant=1, cells=C.byref(c1), ws=FAKE + 8) == EWORKSPACE
     assert scall(variant=1, cells=C.byref(Tile(1, 1, 0, 0, 101, FAKE))) == EINVAL  # > count
+    # the scalar TSC matrix: n_k >= 5, an order-2 cell layout
+    tm = lib.assemble_mass_matrix_scalar_tsc
+    tm.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p]
+    assert tm(C.byref(grid(3, [8, 4, 8])), C.byref(P), None, 0, FAKE, None) == EINVAL
+    assert tm(C.byref(grid(2, [8, 8])), C.byref(P), None, 0, FAKE, None) == EUNSUPPORTED
+    assert tm(g8, C.byref(P), None, 1, FAKE, None) == EINVAL               # MFMA needs groups
+    assert tm(g8, C.byref(P), None, 2, FAKE, None) == EINVAL               # VALU too
+    assert tm(g8, C.byref(P), C.byref(c1), 1, FAKE, None) == EINVAL        # order 1 layout
+    o2 = Tile(1, 2, 0, 0, 100, FAKE)
+    assert tm(g8, C.byref(P), C.byref(Tile(1, 2, 0, 0, 101, FAKE)), 1, FAKE, None) == EINVAL
+    assert tm(g8, C.byref(P), C.byref(Tile(1, 2, 0, 0, 100, None)), 1, FAKE, None) == EINVAL
+    assert tm(g8, C.byref(P), C.byref(o2), 9, FAKE, None) == EINVAL
+    assert tm(g8, C.byref(P), C.byref(o2), 1, None, None) == EINVAL       # no M
+    assert tm(g8, C.byref(big), C.byref(o2), 1, FAKE, None) == EINVAL
     # the fp64 entry points validate alike
     af = lib.assemble_mass_matrix_f64
     af.argtypes = am.argtypes

@@ -1,0 +1,95 @@
+"""GPU scalar mass matrix with TSC weights (MFMA, VALU and flat variants) vs the
+fp64 oracle.
+
+Tolerance as for the fp32 CIC matrices: ||M_gpu - M_oracle||_F <= 1e-4
+||M_oracle||_F over the 125-offset store and max |M_gpu - M_oracle| <= 1e-4
+max |M_oracle| (fp32 products and sums, fp32 atomics into M; the mass-matrix
+paper, §5 "Exactness and precision")."""
+import numpy as np
+import pytest
+import torch
+
+import particle_cell_grid_amd as pcg
+import synthetic
+from gpu_util import DEV, dev, full_workload, rel_frob_err, say
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+VARIANTS = [pcg.PCG_MASS_MFMA, pcg.PCG_MASS_VALU, pcg.PCG_MASS_FLAT]
+
+
+def _run(n, s, off, variant, n_part=None, use_layout=True):
+    M = torch.zeros(n[2], n[1], n[0], 125, dtype=torch.float32, device=DEV)
+    groups = None
+    if use_layout:
+        groups = pcg.Layout(T=1, order=2, tile_offsets=dev(off.view(np.int32)),
+                            n_partitioned=s.count if n_part is None else n_part, drift=0)
+    say("mass tsc", n, s.count, variant, n_part, use_layout)
+    pcg.assemble_mass_matrix_scalar_tsc(n, [dev(a) for a in s.x], dev(s.q), dev(s.w), M, groups,
+                                        variant)
+    torch.cuda.synchronize()
+    return M.cpu().numpy()
+
+
+def _check(M, ref):
+    assert rel_frob_err(M, ref) <= TOL
+    assert np.abs(M - ref).max() <= TOL * np.abs(ref).max()
+
+
+def _grouped(orc, wl):
+    _, perm, off = orc.tile_sort(3, wl.n, 2, 1, wl.x)   # order 2, T = 1
+    return wl.take(perm.astype(np.int64)), off
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("n,ppc", [([5, 5, 5], 16), ([7, 6, 8], 64), ([6, 6, 6], 100)])
+def test_tsc_mass_matches_oracle(orc, variant, n, ppc):
+    """Uniform loading: support groups of varied size (several above 64 at ppc 64
+    and 100 take a second, partial batch)."""
+    wl = synthetic.mass_workload(n, ppc, w_uniform=True, seed=800 + ppc)
+    s, off = _grouped(orc, wl)
+    _check(_run(n, s, off, variant), orc.mass_matrix_scalar_tsc(n, wl.x, wl.q, wl.w))
+
+
+@pytest.mark.parametrize("variant", [pcg.PCG_MASS_MFMA, pcg.PCG_MASS_VALU])
+def test_tsc_mass_ragged_stale_and_tail(orc, variant):
+    """Random positions with a crowded column, every 7th particle moved after the
+    sort (found in another group's slice), and an unsorted tail of 400."""
+    r = np.random.default_rng(81)
+    n = [9, 8, 10]
+    cnt = 5000
+    x = [r.uniform(0, n[k], cnt).astype(np.float32) for k in range(3)]
+    x[0][:1200] = r.uniform(2, 3, 1200).astype(np.float32)
+    x[1][:1200] = r.uniform(4, 5, 1200).astype(np.float32)
+    q = np.where(r.random(cnt) < 0.5, 1.0, -1.0).astype(np.float32)
+    w = r.uniform(0.5, 1.5, cnt).astype(np.float32)
+    z = np.zeros(cnt, np.float32)
+    wl = synthetic.Workload(3, n, x, x, [z] * 3, q, w, [z] * 3, z)
+    s, off = _grouped(orc, wl)
+    s.x[0] = synthetic.periodic_shift(s.x[0], np.where(np.arange(cnt) % 7 == 0, 0.6, 0.0), n[0])
+    M = _run(n, s, off, variant, n_part=cnt - 400)
+    _check(M, orc.mass_matrix_scalar_tsc(n, s.x, s.q, s.w))
+
+
+def test_tsc_mass_no_layout_is_flat(orc):
+    wl = synthetic.mass_workload([5, 6, 7], 9, seed=82)
+    _check(_run(wl.n, wl, None, pcg.PCG_MASS_AUTO, use_layout=False),
+           orc.mass_matrix_scalar_tsc(wl.n, wl.x, wl.q, wl.w))
+
+
+def test_tsc_mass_full_size_64(orc):
+    """64^3, 64 ppc on the matrix cores: rows of a z-slab against the oracle on the
+    particles whose support base lies in the slab (node plane z receives from
+    bases z-2 .. z), and the grand total sum q w."""
+    wl = full_workload("mass_64_ppc64")
+    s, off = _grouped(orc, wl)
+    M = _run(wl.n, s, off, pcg.PCG_MASS_MFMA)
+    z = wl.x[2].astype(np.float64)
+    fl = np.floor(z)
+    bz = np.where(z - fl < 0.5, fl - 1, fl)
+    z0, z1 = 20, 30
+    sub = wl.take(np.nonzero((bz >= z0) & (bz < z1))[0])
+    ref = orc.mass_matrix_scalar_tsc(wl.n, sub.x, sub.q, sub.w)
+    _check(M[z0 + 2:z1], ref[z0 + 2:z1])
+    qw = wl.q.astype(np.float64) * wl.w
+    assert abs(M.astype(np.float64).sum() - qw.sum()) <= 1e-4 * np.abs(qw).sum()

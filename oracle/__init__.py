@@ -68,6 +68,9 @@ def lib():
         L.oracle_mass_matrix.argtypes = [i32p, C.c_int64, fpp, fpp, C.c_void_p, C.c_void_p,
                                          C.c_void_p, C.c_void_p]
         L.oracle_mass_matrix.restype = C.c_int
+        L.oracle_mass_matrix_tsc.argtypes = [i32p, C.c_int64, fpp, fpp, C.c_void_p, C.c_void_p,
+                                         C.c_void_p, C.c_void_p]
+        L.oracle_mass_matrix_tsc.restype = C.c_int
         L.oracle_mass_matrix_scalar.argtypes = [i32p, C.c_int64, fpp, C.c_void_p, C.c_void_p,
                                                 C.c_void_p]
         L.oracle_mass_matrix_scalar.restype = C.c_int
@@ -222,6 +225,23 @@ def mass_matrix(n, x, B, q, w, beta, M=None):
     rc = lib().oracle_mass_matrix(_grid(n3), int(q.size), xs, bs, _ptr(q), _ptr(w), _ptr(beta),
                                   _ptr(M))
     _check(rc, "mass_matrix")
+    return M
+
+
+def mass_matrix_tsc(n, x, B, q, w, beta, M=None):
+    """ECSIM mass matrix with TSC weights, 125-offset store [nz, ny, nx, 125, 3, 3]
+    fp64 (accumulated)."""
+    n3 = list(n)
+    keep = []
+    xs = _ptrs(list(x), keep)
+    bs = _ptrs(list(B), keep)
+    q, w, beta = _f32(q), _f32(w), _f32(beta)
+    if M is None:
+        M = np.zeros((n3[2], n3[1], n3[0], 125, 3, 3), dtype=np.float64)
+    assert M.dtype == np.float64 and M.flags.c_contiguous
+    rc = lib().oracle_mass_matrix_tsc(_grid(n3), int(q.size), xs, bs, _ptr(q), _ptr(w),
+                                      _ptr(beta), _ptr(M))
+    _check(rc, "mass_matrix_tsc")
     return M
 
 

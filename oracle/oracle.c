@@ -402,6 +402,50 @@ int oracle_mass_matrix_scalar_tsc(const int32_t n[3], int64_t np, const float *c
     return 0;
 }
 
+/* [MM] §2.1 Eq.(4)-(6) with TSC shape functions (§2.3 Eq.(12) at order 2; the
+ * paper's tensorial TSC runs, §4.1 Fig. 9): every ordered pair of the 27
+ * support nodes of every particle,
+ *   M^{ij}_{g, g+o} += q_p w_p alpha_p^{ij} W_{pg} W_{p,g+o},
+ * alpha_p from oracle_alpha.  M is fp64 [n_z][n_y][n_x][125][3][3] with the
+ * 125 offsets numbered as in oracle_mass_matrix_scalar_tsc, and is
+ * accumulated.  3D; n_k >= 5. */
+int oracle_mass_matrix_tsc(const int32_t n[3], int64_t np, const float *const x[3],
+                           const float *const B[3], const float *q, const float *w,
+                           const float *beta, double *M)
+{
+    if (n[0] < 5 || n[1] < 5 || n[2] < 5 || np < 0)
+        return -1;
+    for (int64_t p = 0; p < np; ++p) {
+        double omega[3], alpha[9], s[9];
+        for (int k = 0; k < 3; ++k)
+            omega[k] = (double)beta[p] * (double)B[k][p];
+        oracle_alpha(omega, alpha);
+        double qw = (double)q[p] * (double)w[p];
+        for (int ij = 0; ij < 9; ++ij)
+            s[ij] = qw * alpha[ij];
+        int64_t base[3];
+        double W[3][3];
+        for (int k = 0; k < 3; ++k)
+            oracle_shape_1d(2, (double)x[k][p], &base[k], W[k]);
+        for (int a = 0; a < 27; ++a) {
+            int ax = a % 3, ay = (a / 3) % 3, az = a / 9;
+            int64_t ga = wrap(base[0] + ax, n[0]) +
+                         (int64_t)n[0] * (wrap(base[1] + ay, n[1]) +
+                                          (int64_t)n[1] * wrap(base[2] + az, n[2]));
+            double wa = W[0][ax] * W[1][ay] * W[2][az];
+            for (int b = 0; b < 27; ++b) {
+                int bx = b % 3, by = (b / 3) % 3, bz = b / 9;
+                double wb = W[0][bx] * W[1][by] * W[2][bz];
+                int o = (bx - ax + 2) + 5 * (by - ay + 2) + 25 * (bz - az + 2);
+                double *row = M + (ga * 125 + o) * 9;
+                for (int ij = 0; ij < 9; ++ij)
+                    row[ij] += s[ij] * (wa * wb);
+            }
+        }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* 1-D windowed sweep deposit                                                */
 /* ------------------------------------------------------------------------ */

@@ -755,3 +755,52 @@ def test_tsc_scalar_mass_matrix_single_particle(orc):
                             wx[hx] * wy[hy] * wz[hz])
                         nz += 1
     assert nz == 729 and np.count_nonzero(M) == 729
+
+
+# ---------------------------------------------------------------------------
+# ECSIM mass matrix with TSC weights  ([MM] Eq.(4)-(6), §2.3 order 2)
+
+def test_tsc_mass_matrix_equals_dense_contraction(orc):
+    """[MM] Eq.(10) per component: M^ij = W diag(q w alpha^ij) W^T on 5^3 with the
+    order-2 W, against the 125-offset store."""
+    r = np.random.default_rng(47)
+    n = [5, 5, 5]
+    x, B, q, w, beta = _mm_inputs(r, n, 80)
+    M = orc.mass_matrix_tsc(n, x, B, q, w, beta)
+    W = _weights_matrix_tsc(orc, n, x)
+    s = _coeffs(orc, B, q, w, beta)
+    for ij in range(9):
+        dense = W @ np.diag(s[:, ij]) @ W.T
+        store = np.zeros((125, 125))
+        for gz in range(5):
+            for gy in range(5):
+                for gx in range(5):
+                    g = gx + 5 * (gy + 5 * gz)
+                    for o, (dx, dy, dz) in enumerate(OFFS5):
+                        g2 = (gx + dx) % 5 + 5 * (((gy + dy) % 5) + 5 * ((gz + dz) % 5))
+                        store[g, g2] += M[gz, gy, gx, o].ravel()[ij]
+        assert np.abs(store - dense).max() < 1e-12 * max(1.0, np.abs(dense).max())
+
+
+def test_tsc_mass_matrix_symmetry_row_sums_and_zero_field(orc):
+    """Eq.(11) component-wise symmetry; block row sums W s; with B = 0 each diagonal
+    component is the scalar TSC matrix and the off-diagonal ones vanish."""
+    r = np.random.default_rng(48)
+    n = [6, 5, 7]
+    x, B, q, w, beta = _mm_inputs(r, n, 300)
+    M = orc.mass_matrix_tsc(n, x, B, q, w, beta)
+    for o, (dx, dy, dz) in enumerate(OFFS5):
+        mo = OFFS5.index((-dx, -dy, -dz))
+        rolled = np.roll(M[:, :, :, mo], shift=(-dz, -dy, -dx), axis=(0, 1, 2))
+        assert np.abs(M[:, :, :, o] - rolled).max() < 1e-13
+    s = _coeffs(orc, B, q, w, beta)
+    rows = M.sum(axis=3).reshape(-1, 9)
+    W = _weights_matrix_tsc(orc, n, x)
+    for ij in range(9):
+        assert np.abs(rows[:, ij] - W @ s[:, ij]).max() < 1e-12
+    x, B, q, w, beta = _mm_inputs(r, n, 200, zero_B=True)
+    M0 = orc.mass_matrix_tsc(n, x, B, q, w, beta)
+    Ms = orc.mass_matrix_scalar_tsc(n, x, q, w)
+    for i in range(3):
+        assert np.abs(M0[..., i, i] - Ms).max() < 1e-13
+    assert np.abs(M0[..., 0, 1]).max() == 0 and np.abs(M0[..., 2, 1]).max() == 0

@@ -72,9 +72,9 @@ MUTANTS = [
      "25 * (bz - az + 2)", "25 * (az - bz + 2)"),
     ("TSC scalar mass matrix without the second node's weight",
      "M[g * 125 + o] += s * wg * wh;", "M[g * 125 + o] += s * wg;"),
-    ("TSC tensor mass matrix with the second node's y and z swapped",
-     "int bx = b % 3, by = (b / 3) % 3, bz = b / 9;",
-     "int bx = b % 3, by = b / 9, bz = (b / 3) % 3;"),
+    ("TSC tensor mass matrix with the first node's z taken from its y digit",
+     "int ax = a % 3, ay = (a / 3) % 3, az = a / 9;",
+     "int ax = a % 3, ay = (a / 3) % 3, az = (a / 3) % 3;"),
     ("TSC tensor mass matrix without the node weights' product",
      "row[ij] += s[ij] * (wa * wb);", "row[ij] += s[ij] * wa;"),
 ]

@@ -17,7 +17,8 @@ Other workloads (--workload): cic2d_512_ppc16 (2-D CIC 512^2), tsc3d_128_blob
 sort + MFMA assembly), mass_f64_64_ppc64 (the same in fp64), mass_scalar_64_ppc64
 (the scalar mass matrix, coefficient q w, on the same particles), sweep1d_2000
 (1-D windowed sweep), mass_tsc_scalar_64_ppc64 (the scalar matrix with TSC
-weights, support-group sort + MFMA assembly), sweep1d_grad_1e7 (the sweep's loss gradient, 10^7 particles:
+weights, support-group sort + MFMA assembly), mass_tsc_64_ppc64 (the ECSIM
+matrix with TSC weights), sweep1d_grad_1e7 (the sweep's loss gradient, 10^7 particles:
 forward sweep, seed and reverse gather in one library call).
 
 Prints ONE JSON line (rank 0).  Only one GPU is used: --gpus above 1 exits.
@@ -53,6 +54,7 @@ def parse():
                     choices=["sweep1d_2000", "cic2d_512_ppc16", "cic3d_128_ppc32",
                              "tsc3d_128_blob", "mass_64_ppc64", "mass_f64_64_ppc64",
                              "mass_scalar_64_ppc64", "mass_tsc_scalar_64_ppc64",
+                             "mass_tsc_64_ppc64",
                              "sweep1d_grad_1e7"])
     ap.add_argument("--tile", type=int, default=0, help="tile edge T (0 = the workload's)")
     ap.add_argument("--block", type=int, default=0)
@@ -486,9 +488,10 @@ def bench_sweep(args, torch, pcg):
 
 # -------------------------------------------------- scalar mass matrix, TSC weights
 
-def bench_mass_tsc(args, torch, pcg):
-    """Scalar mass matrix with TSC weights on the mass_64_ppc64 particles: re-sort
-    by support base (T = 1, order = 2) from the previous layout, then assemble."""
+def bench_mass_tsc(args, torch, pcg, tensor=False):
+    """Mass matrix with TSC weights on the mass_64_ppc64 particles, scalar or (tensor)
+    ECSIM: re-sort by support base (T = 1, order = 2) from the previous layout,
+    then assemble."""
     import numpy as np
 
     import synthetic
@@ -499,8 +502,12 @@ def bench_mass_tsc(args, torch, pcg):
     dev = torch.device("cuda:0")
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     x = [t(a) for a in wl.x]
-    shuffled = x + [t(wl.q), t(wl.w)]
-    M = torch.zeros(n[2], n[1], n[0], 125, dtype=torch.float32, device=dev)
+    if tensor:
+        shuffled = x + [t(wl.q), t(wl.w)] + [t(b) for b in wl.B] + [t(wl.beta)]
+        M = torch.zeros(n[2], n[1], n[0], 125, 3, 3, dtype=torch.float32, device=dev)
+    else:
+        shuffled = x + [t(wl.q), t(wl.w)]
+        M = torch.zeros(n[2], n[1], n[0], 125, dtype=torch.float32, device=dev)
     nc = n[0] * n[1] * n[2]
     perm = torch.empty(cnt, dtype=torch.int32, device=dev)
     keys = torch.empty(cnt, dtype=torch.int32, device=dev)
@@ -516,7 +523,11 @@ def bench_mass_tsc(args, torch, pcg):
     groups = pcg.Layout(T=1, order=2, tile_offsets=off1, n_partitioned=cnt, drift=0)
 
     def assemble(variant):
-        pcg.assemble_mass_matrix_scalar_tsc(n, nxt[0:3], nxt[3], nxt[4], M, groups, variant)
+        if tensor:
+            pcg.assemble_mass_matrix_tsc(n, nxt[0:3], nxt[5:8], nxt[8], nxt[3], nxt[4], M, groups,
+                                         variant)
+        else:
+            pcg.assemble_mass_matrix_scalar_tsc(n, nxt[0:3], nxt[3], nxt[4], M, groups, variant)
 
     def step():
         M.zero_()
@@ -527,38 +538,48 @@ def bench_mass_tsc(args, torch, pcg):
     progress("timing steps")
     ms, wall, kt = time_steps(torch, pcg, step, args.steps, args.warmup)
     progress(f"{ms:.4f} ms per step")
-    kname = "mass_tsc_mfma"
-    flops = cnt * 27.0 * 27.0 * 2.0    # dense 27 x 27 node pairs x 2 flops
+    kname = "mass_tsc_tensor_mfma" if tensor else "mass_tsc_mfma"
+    wname = "mass_tsc_64_ppc64" if tensor else "mass_tsc_scalar_64_ppc64"
+    # dense 27 x 27 node pairs x 2 flops (x 9 components for the tensor)
+    flops = cnt * 27.0 * 27.0 * 2.0 * (9.0 if tensor else 1.0)
     roof = roofline_entry(kt, kname, flops_per_launch=flops)
     if roof:
-        roof["traffic"] = measured_traffic(kname, "mass_tsc_scalar_64_ppc64")
+        roof["traffic"] = measured_traffic(kname, wname)
     kernels = {nm: dict(avg_us=round(kk["avg_us"], 2),
                         launches_per_step=kk["launches"] / args.steps) for nm, kk in kt.items()}
     extra = {}
     for nm, var in (("valu", pcg.PCG_MASS_VALU), ("mfma", pcg.PCG_MASS_MFMA)):
         extra[f"mass_{nm}_ms"] = round(time_plain(torch, lambda: (M.zero_(), assemble(var)), 5), 4)
     extra["mfma_speedup_vs_valu"] = round(extra["mass_valu_ms"] / extra["mass_mfma_ms"], 2)
-    extra["flush_atomics_per_launch"] = 729 * nc
+    extra["flush_atomics_per_launch"] = 729 * nc * (9 if tensor else 1)
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
 
         progress("timing the oracle on the host")
-        m = 1 << 18
+        def run_oracle(k):
+            if tensor:
+                oracle.mass_matrix_tsc(n, [a[:k] for a in wl.x], [b[:k] for b in wl.B], wl.q[:k],
+                                       wl.w[:k], wl.beta[:k])
+            else:
+                oracle.mass_matrix_scalar_tsc(n, [a[:k] for a in wl.x], wl.q[:k], wl.w[:k])
+
+        m = 1 << 16
         t0 = time.perf_counter()
-        oracle.mass_matrix_scalar_tsc(n, [a[:m] for a in wl.x], wl.q[:m], wl.w[:m])
+        run_oracle(m)
         per = (time.perf_counter() - t0) / m
         m2 = int(min(cnt, max(m, args.cpu_seconds / per)))
         t0 = time.perf_counter()
-        oracle.mass_matrix_scalar_tsc(n, [a[:m2] for a in wl.x], wl.q[:m2], wl.w[:m2])
+        run_oracle(m2)
         sec = time.perf_counter() - t0
         cpu = dict(value=round(m2 / sec, 1), unit="particles/s", cores=1, kind="oracle",
                    sample=f"first {m2} of {cnt} particles: fp64 per-particle 27 x 27 outer "
                           f"products, {sec:.1f} s, 1 thread")
-    config = dict(workload="scalar 3-D TSC mass matrix (coefficient q w) 64^3, 64 ppc "
-                           "(support-group sort + MFMA assembly)",
+    kind = "ECSIM 3-D TSC mass matrix" if tensor else "scalar 3-D TSC mass matrix (coefficient q w)"
+    config = dict(workload=f"{kind} 64^3, 64 ppc (support-group sort + MFMA assembly)",
                   particles=cnt, grid=n,
-                  step="zero M + support-group re-sort of x, q, w from the previous layout + "
+                  step="zero M + support-group re-sort of x, q, w" + (", B, beta" if tensor else "")
+                       + " from the previous layout + "
                        "MFMA assembly with an atomic flush")
     return dict(value=cnt / (ms * 1e-3), ms=ms, wall=wall, dtype="f32", config=config,
                 roofline=roof, kernels=kernels, extra=extra, cpu=cpu, unit="particles/s")
@@ -661,6 +682,8 @@ def main():
         r = bench_mass(args, torch, pcg, f64=True)
     elif args.workload == "mass_tsc_scalar_64_ppc64":
         r = bench_mass_tsc(args, torch, pcg)
+    elif args.workload == "mass_tsc_64_ppc64":
+        r = bench_mass_tsc(args, torch, pcg, tensor=True)
     elif args.workload == "sweep1d_grad_1e7":
         r = bench_sweep_grad(args, torch, pcg)
     elif args.workload == "mass_scalar_64_ppc64":

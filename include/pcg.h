@@ -275,6 +275,22 @@ pcg_status assemble_mass_matrix_scalar_tsc(const pcg_grid *grid, const pcg_parti
                                            const pcg_tile *groups, int32_t variant, float *M,
                                            void *stream);
 
+/* The ECSIM (tensor) mass matrix with TSC weights ([MM] Eq.(4)-(6) with §2.3
+ * Eq.(12) at order 2; the paper's tensorial TSC runs, §4.1 Fig. 9):
+ *   M^{ij}_{g, g+o} += q_p w_p alpha_p^{ij} W_{pg} W_{p,g+o},
+ * alpha_p as for assemble_mass_matrix, over every ordered pair of the 27 TSC
+ * support nodes.  3-D, every n_k >= 5.
+ * M: device fp32 [n_z][n_y][n_x][125][3][3], accumulated; offsets as for
+ *   assemble_mass_matrix_scalar_tsc.
+ * B[3], beta: as for assemble_mass_matrix.  groups, variant, strays, tail and
+ *   errors: as for assemble_mass_matrix_scalar_tsc; per group the ten moment
+ *   matrices of the CIC kernels (27 x 27 each) are formed and the 9-component
+ *   block is added with 6561 device atomics ([MM] §3.4).  No workspace. */
+pcg_status assemble_mass_matrix_tsc(const pcg_grid *grid, const pcg_particles *particles,
+                                    const float *const B[3], const float *beta,
+                                    const pcg_tile *groups, int32_t variant, float *M,
+                                    void *stream);
+
 /* fp64 variants of the two matrices ([MM] §4 and §4.1, Figs. 6-7: the CIC
  * scalar and tensor assemblies are measured with every operand in FP64; §5
  * "Tile-support matching and portability" names AMD's FP64 16x16x4 product):

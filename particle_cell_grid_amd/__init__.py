@@ -74,6 +74,9 @@ _lib.assemble_mass_matrix_scalar.restype = C.c_int32
 _lib.assemble_mass_matrix_scalar_tsc.argtypes = [_P(Grid), _P(Particles), _P(Tile), C.c_int32,
                                                  C.c_void_p, C.c_void_p]
 _lib.assemble_mass_matrix_scalar_tsc.restype = C.c_int32
+_lib.assemble_mass_matrix_tsc.argtypes = [_P(Grid), _P(Particles), C.c_void_p, C.c_void_p,
+                                          _P(Tile), C.c_int32, C.c_void_p, C.c_void_p]
+_lib.assemble_mass_matrix_tsc.restype = C.c_int32
 _lib.assemble_mass_matrix_f64.argtypes = _lib.assemble_mass_matrix.argtypes
 _lib.assemble_mass_matrix_f64.restype = C.c_int32
 _lib.assemble_mass_matrix_scalar_f64.argtypes = _lib.assemble_mass_matrix_scalar.argtypes
@@ -349,6 +352,23 @@ def assemble_mass_matrix_scalar_tsc(n: Sequence[int], x: List[torch.Tensor], q: 
                                               C.byref(tile) if tile is not None else None,
                                               int(variant), _ptr(M), _stream())
     _check(st, "assemble_mass_matrix_scalar_tsc")
+    return M
+
+
+def assemble_mass_matrix_tsc(n: Sequence[int], x: List[torch.Tensor], B: List[torch.Tensor],
+                             beta: torch.Tensor, q: torch.Tensor, w: torch.Tensor,
+                             M: torch.Tensor, groups: Optional[Layout] = None,
+                             variant: int = PCG_MASS_AUTO):
+    """M[nz, ny, nx, 125, 3, 3] (fp32) += the ECSIM mass matrix with TSC weights.
+    groups: a T = 1, order = 2 layout, or None (flat)."""
+    g = make_grid(3, n)
+    P = _particles(q.numel(), x, None, q, w)
+    bp = (C.c_void_p * 3)(*[b.data_ptr() for b in B])
+    tile = groups.to_c() if groups is not None else None
+    st = _lib.assemble_mass_matrix_tsc(C.byref(g), C.byref(P), bp, _ptr(beta),
+                                       C.byref(tile) if tile is not None else None,
+                                       int(variant), _ptr(M), _stream())
+    _check(st, "assemble_mass_matrix_tsc")
     return M
 
 

@@ -18,6 +18,14 @@
 // particles) and FLAT (one thread per particle, 729 atomics; also the unsorted
 // tail).  A particle found in a slice whose group it does not belong to (a
 // stale layout) is deposited by its own lane with the flat path.
+//
+// The tensor (ECSIM) matrix with TSC weights ([MM] Eq.(4)-(5); §4.1 Fig. 9)
+// uses the moments of the CIC kernels: with u = (1, omega) and
+// c = q w / (1 + |omega|^2), T_kl[a][b] = sum_p c u_k u_l W_a W_b (k <= l) and
+//   M^ij = delta_ij T_00 + eps_ijk T_0(k+1) + T_(i+1)(j+1).
+// Each T_kl is a symmetric 27 x 27 matrix: tiles (0,0), (0,1), (1,1), i.e.
+// 30 products of 16x16x4 per 4 particles, accumulators in place (120 AGPRs).
+// The block (729 node pairs x 9 components) is added to M with 6561 atomics.
 #include <algorithm>
 
 #include "common.hpp"
@@ -37,7 +45,9 @@ struct TscArgs {
     const float *x[3];
     const float *q;
     const float *w;
-    float *M;  // [n_z][n_y][n_x][125]
+    const float *B[3];  // tensor matrix only
+    const float *beta;
+    float *M;  // [n_z][n_y][n_x][125] (scalar) or [..][125][3][3] (tensor)
     const uint32_t *offsets;
     int64_t n_part;
     uint32_t ngroups;
@@ -244,17 +254,280 @@ __global__ __launch_bounds__(TSC_WAVES * WAVE) void k_mass_tsc_group(TscArgs m)
     }
 }
 
+// ---------------------------------------------------------------- tensor matrix
+
+// omega = beta B, u = (1, omega), c = q w / (1 + |omega|^2).
+__device__ inline void tsc_alpha(const TscArgs &m, int64_t p, float q, float w, float *u,
+                                 float &c)
+{
+    const float bt = ld(m.beta, p);
+    const float o0 = bt * ld(m.B[0], p), o1 = bt * ld(m.B[1], p), o2 = bt * ld(m.B[2], p);
+    u[0] = 1.0f;
+    u[1] = o0;
+    u[2] = o1;
+    u[3] = o2;
+    c = q * w / (1.0f + (o0 * o0 + o1 * o1 + o2 * o2));
+}
+
+// Adds moment t of pair (k, l) into the nine components of a block ([MM]
+// Eq.(5) written out: +eps_ijk omega_k for the rotation, omega_i omega_j).
+__device__ inline void add_moment(int k, int l, float t, float *blk)
+{
+    if (k == 0 && l == 0) {
+        blk[0] += t;
+        blk[4] += t;
+        blk[8] += t;
+    } else if (k == 0) {  // T_0(l): omega_{l-1} in the rotation
+        if (l == 1) {
+            blk[5] += t;  // yz
+            blk[7] -= t;  // zy
+        } else if (l == 2) {
+            blk[2] -= t;  // xz
+            blk[6] += t;  // zx
+        } else {
+            blk[1] += t;  // xy
+            blk[3] -= t;  // yx
+        }
+    } else {  // T_(i+1)(j+1) = omega_i omega_j, into (i, j) and (j, i)
+        const int i = k - 1, j = l - 1;
+        blk[3 * i + j] += t;
+        if (i != j)
+            blk[3 * j + i] += t;
+    }
+}
+
+// The particle's whole 27 x 27 x 9 contribution with global atomics.
+__device__ inline void tsc_tensor_global(const TscArgs &m, const TscParticle &P, const float *u,
+                                         float c)
+{
+    for (int a = 0; a < TSC_NODES; ++a) {
+        float *row = m.M + (size_t)tsc_node(m, P.base, a) * TSC_OFFS * 9;
+        for (int b = 0; b < TSC_NODES; ++b) {
+            const float wab = c * P.W[a] * P.W[b];
+            float blk[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+            for (int k = 0; k < 4; ++k)
+                for (int l = k; l < 4; ++l)
+                    add_moment(k, l, wab * u[k] * u[l], blk);
+            float *dst = row + tsc_offset(a, b) * 9;
+            for (int ij = 0; ij < 9; ++ij)
+                atomic_add_f32(&dst[ij], blk[ij]);
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_mass_tsc_tensor_flat(TscArgs m, int64_t begin,
+                                                              int64_t end)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t p = begin + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < end;
+         p += stride) {
+        const float q = ld(m.q, p), w = ld(m.w, p);
+        const TscParticle P = tsc_particle(m, ld(m.x[0], p), ld(m.x[1], p), ld(m.x[2], p), q, w);
+        float u[4], c;
+        tsc_alpha(m, p, q, w, u, c);
+        tsc_tensor_global(m, P, u, c);
+    }
+}
+
+struct TscTensorStage {
+    float W[64][32];
+    float u[64][4];
+    float c[64];
+};
+union TscTensorScratch {
+    TscTensorStage s;
+    float Tm[32][33];
+};
+
+// the ten moments (k <= l) in a fixed order
+__device__ constexpr int MOM_K[10] = {0, 0, 0, 0, 1, 1, 1, 2, 2, 3};
+__device__ constexpr int MOM_L[10] = {0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
+
+template <bool MFMA>
+__global__ __launch_bounds__(TSC_WAVES * WAVE) void k_mass_tsc_tensor_group(TscArgs m)
+{
+    __shared__ TscTensorScratch scratch[TSC_WAVES];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), lane = lane_id();
+    TscTensorScratch &ws = scratch[wave];
+    const uint32_t nblocks = (m.ngroups + TSC_WAVES - 1) / TSC_WAVES;
+    const uint32_t per = (nblocks + 7) / 8;
+    const uint32_t blk_id = (blockIdx.x % 8) * per + blockIdx.x / 8;
+    const uint32_t g = blk_id * TSC_WAVES + wave;
+    if (blk_id >= nblocks || g >= m.ngroups)
+        return;
+    const int64_t lo = std::min<int64_t>(m.offsets[g], m.n_part);
+    const int64_t hi = std::min<int64_t>(m.offsets[g + 1], m.n_part);
+    if (hi <= lo)
+        return;
+    int gb[3];
+    gb[0] = (int)(g % (uint32_t)m.n[0]);
+    gb[1] = (int)((g / (uint32_t)m.n[0]) % (uint32_t)m.n[1]);
+    gb[2] = (int)(g / ((uint32_t)m.n[0] * (uint32_t)m.n[1]));
+
+    const int r = lane & 15, kk = lane >> 4;
+    // MFMA: acc[3 mom + t], tiles t = (0,0), (0,1), (1,1) of moment mom
+    floatx4 acc[30];
+#pragma unroll
+    for (int i = 0; i < 30; ++i)
+        acc[i] = floatx4{0, 0, 0, 0};
+    // VALU: lane owns node pairs lane + 64 k (k < 12) and their 9 components
+    constexpr int PAIRS = (TSC_NODES * TSC_NODES + WAVE - 1) / WAVE;
+    constexpr int VPAIRS = MFMA ? 1 : PAIRS;
+    float tv[VPAIRS][9];
+#pragma unroll
+    for (int k = 0; k < VPAIRS; ++k)
+#pragma unroll
+        for (int ij = 0; ij < 9; ++ij)
+            tv[k][ij] = 0.0f;
+
+    for (int64_t base = lo; base < hi; base += 64) {
+        const int64_t p = std::min<int64_t>(base + lane, hi - 1);  // clamped
+        const bool valid = base + lane < hi;
+        const float q = ld(m.q, p), w = ld(m.w, p);
+        const TscParticle P = tsc_particle(m, ld(m.x[0], p), ld(m.x[1], p), ld(m.x[2], p), q, w);
+        float u[4], c;
+        tsc_alpha(m, p, q, w, u, c);
+        const bool home = P.base[0] == gb[0] && P.base[1] == gb[1] && P.base[2] == gb[2];
+        const bool take = valid && home;
+        if (valid && !home)
+            tsc_tensor_global(m, P, u, c);  // stale layout: this lane deposits it alone
+        wave_sync();
+#pragma unroll
+        for (int a = 0; a < 32; a += 4) {
+            float4 v4;
+            v4.x = take && a + 0 < TSC_NODES ? P.W[a + 0] : 0.0f;
+            v4.y = take && a + 1 < TSC_NODES ? P.W[a + 1] : 0.0f;
+            v4.z = take && a + 2 < TSC_NODES ? P.W[a + 2] : 0.0f;
+            v4.w = take && a + 3 < TSC_NODES ? P.W[a + 3] : 0.0f;
+            *reinterpret_cast<float4 *>(&ws.s.W[lane][a]) = v4;
+        }
+        *reinterpret_cast<float4 *>(ws.s.u[lane]) =
+            take ? make_float4(u[0], u[1], u[2], u[3]) : make_float4(0, 0, 0, 0);
+        ws.s.c[lane] = take ? c : 0.0f;
+        wave_sync();
+        const int nb = (int)std::min<int64_t>(64, hi - base);
+        if (MFMA) {
+            const int steps = (nb + 3) >> 2;
+            for (int i = 0; i < steps; ++i) {
+                const int qq = 4 * i + kk;
+                const float w0 = ws.s.W[qq][r], w1 = ws.s.W[qq][16 + r];
+                const float4 uq = *reinterpret_cast<const float4 *>(ws.s.u[qq]);
+                const float cq = ws.s.c[qq];
+                const float uk[4] = {uq.x, uq.y, uq.z, uq.w};
+                float a0[4], a1[4], b0[4], b1[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    a0[k] = uk[k] * w0;
+                    a1[k] = uk[k] * w1;
+                    b0[k] = cq * a0[k];
+                    b1[k] = cq * a1[k];
+                }
+#pragma unroll
+                for (int mo = 0; mo < 10; ++mo) {
+                    const int k = MOM_K[mo], l = MOM_L[mo];
+                    acc[3 * mo + 0] =
+                        __builtin_amdgcn_mfma_f32_16x16x4f32(a0[k], b0[l], acc[3 * mo + 0], 0, 0, 0);
+                    acc[3 * mo + 1] =
+                        __builtin_amdgcn_mfma_f32_16x16x4f32(a0[k], b1[l], acc[3 * mo + 1], 0, 0, 0);
+                    acc[3 * mo + 2] =
+                        __builtin_amdgcn_mfma_f32_16x16x4f32(a1[k], b1[l], acc[3 * mo + 2], 0, 0, 0);
+                }
+            }
+        } else {
+            for (int qq = 0; qq < nb; ++qq) {
+                const float cq = ws.s.c[qq];
+                const float4 uq = *reinterpret_cast<const float4 *>(ws.s.u[qq]);
+                const float uk[4] = {uq.x, uq.y, uq.z, uq.w};
+#pragma unroll
+                for (int k2 = 0; k2 < VPAIRS; ++k2) {
+                    const int pr = lane + WAVE * k2;
+                    if (pr < TSC_NODES * TSC_NODES) {
+                        const float wab =
+                            cq * ws.s.W[qq][pr / TSC_NODES] * ws.s.W[qq][pr % TSC_NODES];
+#pragma unroll
+                        for (int mo = 0; mo < 10; ++mo)
+                            add_moment(MOM_K[mo], MOM_L[mo], wab * uk[MOM_K[mo]] * uk[MOM_L[mo]],
+                                       tv[k2]);
+                    }
+                }
+            }
+        }
+    }
+    wave_sync();
+    if (MFMA) {
+        // per half of the lane's pairs, each moment once through LDS: register
+        // i of this lane holds D[4 (lane / 16) + i][lane % 16]; tile (1,0) is
+        // tile (0,1) transposed
+        constexpr int HALF = (PAIRS + 1) / 2;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float blk[HALF][9];
+#pragma unroll
+            for (int k2 = 0; k2 < HALF; ++k2)
+#pragma unroll
+                for (int ij = 0; ij < 9; ++ij)
+                    blk[k2][ij] = 0.0f;
+#pragma unroll
+            for (int mo = 0; mo < 10; ++mo) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 4 * kk + i, col = r;
+                    ws.Tm[row][col] = acc[3 * mo + 0][i];
+                    ws.Tm[row][16 + col] = acc[3 * mo + 1][i];
+                    ws.Tm[16 + col][row] = acc[3 * mo + 1][i];
+                    ws.Tm[16 + row][16 + col] = acc[3 * mo + 2][i];
+                }
+                wave_sync();
+#pragma unroll
+                for (int k2 = 0; k2 < HALF; ++k2) {
+                    const int pr = lane + WAVE * (h * HALF + k2);
+                    if (h * HALF + k2 < PAIRS && pr < TSC_NODES * TSC_NODES)
+                        add_moment(MOM_K[mo], MOM_L[mo], ws.Tm[pr / TSC_NODES][pr % TSC_NODES],
+                                   blk[k2]);
+                }
+                wave_sync();
+            }
+#pragma unroll
+            for (int k2 = 0; k2 < HALF; ++k2) {
+                const int pr = lane + WAVE * (h * HALF + k2);
+                if (h * HALF + k2 < PAIRS && pr < TSC_NODES * TSC_NODES) {
+                    const int a = pr / TSC_NODES, b = pr % TSC_NODES;
+                    float *dst = m.M + ((size_t)tsc_node(m, gb, a) * TSC_OFFS + tsc_offset(a, b)) * 9;
+#pragma unroll
+                    for (int ij = 0; ij < 9; ++ij)
+                        atomic_add_f32(&dst[ij], blk[k2][ij]);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int k2 = 0; k2 < VPAIRS; ++k2) {
+            const int pr = lane + WAVE * k2;
+            if (pr < TSC_NODES * TSC_NODES) {
+                const int a = pr / TSC_NODES, b = pr % TSC_NODES;
+                float *dst = m.M + ((size_t)tsc_node(m, gb, a) * TSC_OFFS + tsc_offset(a, b)) * 9;
+#pragma unroll
+                for (int ij = 0; ij < 9; ++ij)
+                    atomic_add_f32(&dst[ij], tv[k2][ij]);
+            }
+        }
+    }
+}
+
 }  // namespace
 }  // namespace pcg
 
 using namespace pcg;
 
-extern "C" pcg_status assemble_mass_matrix_scalar_tsc(const pcg_grid *grid,
-                                                      const pcg_particles *particles,
-                                                      const pcg_tile *groups, int32_t variant,
-                                                      float *M, void *stream)
+namespace {
+
+// Both entry points: the scalar matrix or (TENSOR, B and beta given) the ECSIM
+// one, with TSC weights.
+template <bool TENSOR>
+pcg_status assemble_tsc(const char *who, const pcg_grid *grid, const pcg_particles *particles,
+                        const float *const B[3], const float *beta, const pcg_tile *groups,
+                        int32_t variant, float *M, void *stream)
 {
-    const char *who = "assemble_mass_matrix_scalar_tsc";
     clear_error();
     PCG_TRY(check_grid(grid, who));
     if (grid->dim != 3)
@@ -273,6 +546,8 @@ extern "C" pcg_status assemble_mass_matrix_scalar_tsc(const pcg_grid *grid,
     if (count > 0 && (!particles->x[0] || !particles->x[1] || !particles->x[2] ||
                       !particles->q || !particles->w))
         return fail(PCG_EINVAL, "%s: x, q or w is NULL", who);
+    if (TENSOR && count > 0 && (!B || !B[0] || !B[1] || !B[2] || !beta))
+        return fail(PCG_EINVAL, "%s: B or beta is NULL", who);
     const bool grouped = variant != PCG_MASS_FLAT && groups;
     if (!groups && (variant == PCG_MASS_MFMA || variant == PCG_MASS_VALU))
         return fail(PCG_EINVAL, "%s: the %s variant needs a support-group layout", who,
@@ -292,9 +567,11 @@ extern "C" pcg_status assemble_mass_matrix_scalar_tsc(const pcg_grid *grid,
         m.n[k] = grid->n[k];
         m.nf[k] = (float)grid->n[k];
         m.x[k] = particles->x[k];
+        m.B[k] = TENSOR && B ? B[k] : nullptr;
     }
     m.q = particles->q;
     m.w = particles->w;
+    m.beta = TENSOR ? beta : nullptr;
     m.M = M;
     m.ngroups = (uint32_t)((int64_t)grid->n[0] * grid->n[1] * grid->n[2]);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -305,6 +582,9 @@ extern "C" pcg_status assemble_mass_matrix_scalar_tsc(const pcg_grid *grid,
             return PCG_OK;
         const int64_t blocks =
             std::min<int64_t>((end - begin + 255) / 256, (int64_t)device_cus() * 32);
+        if (TENSOR)
+            return launch("mass_tsc_tensor_flat", k_mass_tsc_tensor_flat, dim3((unsigned)blocks),
+                          dim3(256), 0, st, m, begin, end);
         return launch("mass_tsc_flat", k_mass_tsc_flat, dim3((unsigned)blocks), dim3(256), 0, st,
                       m, begin, end);
     };
@@ -315,12 +595,36 @@ extern "C" pcg_status assemble_mass_matrix_scalar_tsc(const pcg_grid *grid,
     if (m.n_part > 0) {
         const uint32_t nblocks = (m.ngroups + TSC_WAVES - 1) / TSC_WAVES;
         const uint32_t blocks = (nblocks + 7) / 8 * 8;
-        if (variant == PCG_MASS_VALU)
-            PCG_TRY(launch("mass_tsc_valu", k_mass_tsc_group<false>, dim3(blocks),
-                           dim3(TSC_WAVES * WAVE), 0, st, m));
+        const bool valu = variant == PCG_MASS_VALU;
+        if (TENSOR)
+            PCG_TRY(launch(valu ? "mass_tsc_tensor_valu" : "mass_tsc_tensor_mfma",
+                           valu ? k_mass_tsc_tensor_group<false> : k_mass_tsc_tensor_group<true>,
+                           dim3(blocks), dim3(TSC_WAVES * WAVE), 0, st, m));
         else
-            PCG_TRY(launch("mass_tsc_mfma", k_mass_tsc_group<true>, dim3(blocks),
+            PCG_TRY(launch(valu ? "mass_tsc_valu" : "mass_tsc_mfma",
+                           valu ? k_mass_tsc_group<false> : k_mass_tsc_group<true>, dim3(blocks),
                            dim3(TSC_WAVES * WAVE), 0, st, m));
     }
     return flat(groups->n_partitioned, count);
+}
+
+}  // namespace
+
+extern "C" pcg_status assemble_mass_matrix_scalar_tsc(const pcg_grid *grid,
+                                                      const pcg_particles *particles,
+                                                      const pcg_tile *groups, int32_t variant,
+                                                      float *M, void *stream)
+{
+    return assemble_tsc<false>("assemble_mass_matrix_scalar_tsc", grid, particles, nullptr,
+                               nullptr, groups, variant, M, stream);
+}
+
+extern "C" pcg_status assemble_mass_matrix_tsc(const pcg_grid *grid,
+                                               const pcg_particles *particles,
+                                               const float *const B[3], const float *beta,
+                                               const pcg_tile *groups, int32_t variant, float *M,
+                                               void *stream)
+{
+    return assemble_tsc<true>("assemble_mass_matrix_tsc", grid, particles, B, beta, groups,
+                              variant, M, stream);
 }

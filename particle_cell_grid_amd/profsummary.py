@@ -63,8 +63,10 @@ def tap_name(kernel):
         return "deposit_regroup" if last == "true" else "deposit_tiled"
     if base == "k_mass_tsc_group":
         return "mass_tsc_mfma" if last == "true" else "mass_tsc_valu"
-    if base == "k_mass_tsc_flat":
-        return "mass_tsc_flat"
+    if base == "k_mass_tsc_tensor_group":
+        return "mass_tsc_tensor_mfma" if last == "true" else "mass_tsc_tensor_valu"
+    if base in ("k_mass_tsc_flat", "k_mass_tsc_tensor_flat"):
+        return base[2:]
     if base.startswith("k_mass_") and targs:
         # <MFMA, scalar, real> for the column kernel, <scalar, real> otherwise
         scalar = "mass_scalar_" if targs[-2].strip() == "true" else "mass_"

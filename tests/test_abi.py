@@ -38,6 +38,7 @@ def test_header_declares_the_entry_points():
               "pcg_deposit_workspace_bytes", "deposit_currents_regroup",
               "pcg_deposit_regroup_workspace_bytes", "pcg_mass_workspace_bytes", "assemble_mass_matrix",
               "assemble_mass_matrix_scalar", "assemble_mass_matrix_scalar_tsc",
+              "assemble_mass_matrix_tsc",
               "assemble_mass_matrix_f64",
               "assemble_mass_matrix_scalar_f64", "deposit_sweep1d", "deposit_sweep1d_grad",
               "deposit_sweep1d_loss_grad",
@@ -266,6 +267,14 @@ def test_mass_and_sweep_validation(lib):
     assert tm(g8, C.byref(P), C.byref(o2), 9, FAKE, None) == EINVAL
     assert tm(g8, C.byref(P), C.byref(o2), 1, None, None) == EINVAL       # no M
     assert tm(g8, C.byref(big), C.byref(o2), 1, FAKE, None) == EINVAL
+    tt = lib.assemble_mass_matrix_tsc
+    tt.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
+                   C.c_void_p, C.c_void_p]
+    assert tt(g8, C.byref(P), None, FAKE, C.byref(o2), 1, FAKE, None) == EINVAL    # no B
+    assert tt(g8, C.byref(P), B, None, C.byref(o2), 1, FAKE, None) == EINVAL       # no beta
+    assert tt(C.byref(grid(3, [4, 8, 8])), C.byref(P), B, FAKE, None, 0, FAKE, None) == EINVAL
+    assert tt(g8, C.byref(P), B, FAKE, C.byref(c1), 1, FAKE, None) == EINVAL       # order 1
+    assert tt(g8, C.byref(P), B, FAKE, None, 1, FAKE, None) == EINVAL              # no groups
     # the fp64 entry points validate alike
     af = lib.assemble_mass_matrix_f64
     af.argtypes = am.argtypes

@@ -1,5 +1,5 @@
-"""GPU scalar mass matrix with TSC weights (MFMA, VALU and flat variants) vs the
-fp64 oracle.
+"""GPU mass matrices with TSC weights, scalar and ECSIM tensor (MFMA, VALU and
+flat variants), vs the fp64 oracle.
 
 Tolerance as for the fp32 CIC matrices: ||M_gpu - M_oracle||_F <= 1e-4
 ||M_oracle||_F over the 125-offset store and max |M_gpu - M_oracle| <= 1e-4
@@ -93,3 +93,57 @@ def test_tsc_mass_full_size_64(orc):
     _check(M[z0 + 2:z1], ref[z0 + 2:z1])
     qw = wl.q.astype(np.float64) * wl.w
     assert abs(M.astype(np.float64).sum() - qw.sum()) <= 1e-4 * np.abs(qw).sum()
+
+
+def _run_tensor(n, s, off, variant, n_part=None, use_layout=True):
+    M = torch.zeros(n[2], n[1], n[0], 125, 3, 3, dtype=torch.float32, device=DEV)
+    groups = None
+    if use_layout:
+        groups = pcg.Layout(T=1, order=2, tile_offsets=dev(off.view(np.int32)),
+                            n_partitioned=s.count if n_part is None else n_part, drift=0)
+    say("mass tsc tensor", n, s.count, variant, n_part, use_layout)
+    pcg.assemble_mass_matrix_tsc(n, [dev(a) for a in s.x], [dev(b) for b in s.B], dev(s.beta),
+                                 dev(s.q), dev(s.w), M, groups, variant)
+    torch.cuda.synchronize()
+    return M.cpu().numpy()
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("n,ppc", [([5, 5, 5], 16), ([7, 6, 8], 64), ([6, 6, 6], 100)])
+def test_tsc_tensor_mass_matches_oracle(orc, variant, n, ppc):
+    wl = synthetic.mass_workload(n, ppc, w_uniform=True, seed=900 + ppc)
+    s, off = _grouped(orc, wl)
+    _check(_run_tensor(n, s, off, variant), orc.mass_matrix_tsc(n, wl.x, wl.B, wl.q, wl.w,
+                                                                wl.beta))
+
+
+def test_tsc_tensor_mass_stale_layout_and_tail(orc):
+    wl = synthetic.mass_workload([8, 7, 9], 20, seed=91)
+    s, off = _grouped(orc, wl)
+    s.x[0] = synthetic.periodic_shift(s.x[0], np.where(np.arange(s.count) % 7 == 0, 0.6, 0.0),
+                                      wl.n[0])
+    M = _run_tensor(wl.n, s, off, pcg.PCG_MASS_MFMA, n_part=s.count - 300)
+    _check(M, orc.mass_matrix_tsc(wl.n, s.x, s.B, s.q, s.w, s.beta))
+
+
+def test_tsc_tensor_zero_field_is_scalar(orc):
+    """B = 0: each diagonal component equals the scalar TSC matrix's kernel output
+    to fp32 rounding, and the off-diagonal components vanish."""
+    wl = synthetic.mass_workload([6, 6, 6], 16, seed=92)
+    wl.B = [np.zeros_like(b) for b in wl.B]
+    s, off = _grouped(orc, wl)
+    Mt = _run_tensor(wl.n, s, off, pcg.PCG_MASS_MFMA)
+    Ms = _run(wl.n, s, off, pcg.PCG_MASS_MFMA)
+    assert np.abs(Mt[..., 0, 1]).max() <= 1e-6 * np.abs(Ms).max()
+    for i in range(3):
+        assert np.abs(Mt[..., i, i] - Ms).max() <= 1e-5 * np.abs(Ms).max()
+
+
+def test_tsc_tensor_mass_large(orc):
+    """24^3, 64 ppc (885K particles) on the matrix cores, every row against the
+    oracle: thousands of groups and both batch paths, small enough for the
+    single-threaded fp64 oracle."""
+    wl = synthetic.mass_workload([24, 24, 24], 64, seed=93)
+    s, off = _grouped(orc, wl)
+    M = _run_tensor(wl.n, s, off, pcg.PCG_MASS_MFMA)
+    _check(M, orc.mass_matrix_tsc(wl.n, wl.x, wl.B, wl.q, wl.w, wl.beta))

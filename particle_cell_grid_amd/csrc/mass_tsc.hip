@@ -25,7 +25,9 @@
 //   M^ij = delta_ij T_00 + eps_ijk T_0(k+1) + T_(i+1)(j+1).
 // Each T_kl is a symmetric 27 x 27 matrix: tiles (0,0), (0,1), (1,1), i.e.
 // 30 products of 16x16x4 per 4 particles, accumulators in place (120 AGPRs).
-// The block (729 node pairs x 9 components) is added to M with 6561 atomics.
+// The block (729 node pairs x 9 components) is added to M with 6561 atomics,
+// staged in LDS so that consecutive lanes add consecutive floats of M (a lane
+// per pair would put 36 bytes between neighbouring lanes' addresses).
 #include <algorithm>
 
 #include "common.hpp"
@@ -334,9 +336,13 @@ struct TscTensorStage {
     float u[64][4];
     float c[64];
 };
+// pairs per lane (729 over 64 lanes), flushed in two halves
+constexpr int TSC_PAIRS = (TSC_NODES * TSC_NODES + WAVE - 1) / WAVE;
+constexpr int TSC_HALF = (TSC_PAIRS + 1) / 2;
 union TscTensorScratch {
     TscTensorStage s;
     float Tm[32][33];
+    float F[WAVE * TSC_HALF * 9];  // one half's blocks, pair-major
 };
 
 // the ten moments (k <= l) in a fixed order
@@ -371,7 +377,7 @@ __global__ __launch_bounds__(TSC_WAVES * WAVE) void k_mass_tsc_tensor_group(TscA
     for (int i = 0; i < 30; ++i)
         acc[i] = floatx4{0, 0, 0, 0};
     // VALU: lane owns node pairs lane + 64 k (k < 12) and their 9 components
-    constexpr int PAIRS = (TSC_NODES * TSC_NODES + WAVE - 1) / WAVE;
+    constexpr int PAIRS = TSC_PAIRS;
     constexpr int VPAIRS = MFMA ? 1 : PAIRS;
     float tv[VPAIRS][9];
 #pragma unroll
@@ -454,19 +460,21 @@ __global__ __launch_bounds__(TSC_WAVES * WAVE) void k_mass_tsc_tensor_group(TscA
         }
     }
     wave_sync();
-    if (MFMA) {
-        // per half of the lane's pairs, each moment once through LDS: register
-        // i of this lane holds D[4 (lane / 16) + i][lane % 16]; tile (1,0) is
-        // tile (0,1) transposed
-        constexpr int HALF = (PAIRS + 1) / 2;
+    // per half of the lane's pairs (lane + 64 (h TSC_HALF + k2)): the blocks,
+    // from the moments through LDS (MFMA) or from the lane's sums (VALU), then
+    // the half's 64 TSC_HALF x 9 floats flushed with consecutive lanes on
+    // consecutive values v: pair 64 h TSC_HALF + v / 9, component v % 9
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            float blk[HALF][9];
+    for (int h = 0; h < 2; ++h) {
+        float blk[TSC_HALF][9];
 #pragma unroll
-            for (int k2 = 0; k2 < HALF; ++k2)
+        for (int k2 = 0; k2 < TSC_HALF; ++k2)
 #pragma unroll
-                for (int ij = 0; ij < 9; ++ij)
-                    blk[k2][ij] = 0.0f;
+            for (int ij = 0; ij < 9; ++ij)
+                blk[k2][ij] = MFMA ? 0.0f : tv[(h * TSC_HALF + k2) % VPAIRS][ij];
+        if (MFMA) {
+            // register i of this lane holds D[4 (lane / 16) + i][lane % 16];
+            // tile (1,0) is tile (0,1) transposed
 #pragma unroll
             for (int mo = 0; mo < 10; ++mo) {
 #pragma unroll
@@ -479,38 +487,32 @@ __global__ __launch_bounds__(TSC_WAVES * WAVE) void k_mass_tsc_tensor_group(TscA
                 }
                 wave_sync();
 #pragma unroll
-                for (int k2 = 0; k2 < HALF; ++k2) {
-                    const int pr = lane + WAVE * (h * HALF + k2);
-                    if (h * HALF + k2 < PAIRS && pr < TSC_NODES * TSC_NODES)
+                for (int k2 = 0; k2 < TSC_HALF; ++k2) {
+                    const int pr = lane + WAVE * (h * TSC_HALF + k2);
+                    if (h * TSC_HALF + k2 < PAIRS && pr < TSC_NODES * TSC_NODES)
                         add_moment(MOM_K[mo], MOM_L[mo], ws.Tm[pr / TSC_NODES][pr % TSC_NODES],
                                    blk[k2]);
                 }
                 wave_sync();
             }
-#pragma unroll
-            for (int k2 = 0; k2 < HALF; ++k2) {
-                const int pr = lane + WAVE * (h * HALF + k2);
-                if (h * HALF + k2 < PAIRS && pr < TSC_NODES * TSC_NODES) {
-                    const int a = pr / TSC_NODES, b = pr % TSC_NODES;
-                    float *dst = m.M + ((size_t)tsc_node(m, gb, a) * TSC_OFFS + tsc_offset(a, b)) * 9;
-#pragma unroll
-                    for (int ij = 0; ij < 9; ++ij)
-                        atomic_add_f32(&dst[ij], blk[k2][ij]);
-                }
-            }
         }
-    } else {
 #pragma unroll
-        for (int k2 = 0; k2 < VPAIRS; ++k2) {
-            const int pr = lane + WAVE * k2;
+        for (int k2 = 0; k2 < TSC_HALF; ++k2)
+#pragma unroll
+            for (int ij = 0; ij < 9; ++ij)
+                ws.F[(k2 * WAVE + lane) * 9 + ij] = blk[k2][ij];
+        wave_sync();
+        for (int v = lane; v < WAVE * TSC_HALF * 9; v += WAVE) {
+            const int pl = v / 9, ij = v - 9 * pl;
+            const int pr = WAVE * TSC_HALF * h + pl;
             if (pr < TSC_NODES * TSC_NODES) {
                 const int a = pr / TSC_NODES, b = pr % TSC_NODES;
-                float *dst = m.M + ((size_t)tsc_node(m, gb, a) * TSC_OFFS + tsc_offset(a, b)) * 9;
-#pragma unroll
-                for (int ij = 0; ij < 9; ++ij)
-                    atomic_add_f32(&dst[ij], tv[k2][ij]);
+                atomic_add_f32(
+                    &m.M[((size_t)tsc_node(m, gb, a) * TSC_OFFS + tsc_offset(a, b)) * 9 + ij],
+                    ws.F[v]);
             }
         }
+        wave_sync();
     }
 }
 

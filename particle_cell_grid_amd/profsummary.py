@@ -31,7 +31,8 @@ def source_digest(kernel):
     """sha1 over the file that holds `kernel` (named <file>_<what>) and the
     headers every kernel file includes."""
     h = hashlib.sha1()
-    key = "mass_tsc" if kernel.startswith("mass_tsc_") else kernel.split("_")[0]
+    # the longest source key the name starts with (mass_tsc_* before mass_*)
+    key = max((k for k in KERNEL_SOURCES if kernel.startswith(k)), key=len)
     for f in (KERNEL_SOURCES[key], "common.hpp", "layout.hpp", "regroup.hpp"):
         h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()

@@ -616,7 +616,8 @@ def bench_sweep_grad(args, torch, pcg):
         sec = kt["sweep1d_grad"]["avg_us"] * 1e-6
         ops = SELECT_OPS * n * T / sec
         roof = dict(bound="alu", achieved=round(ops / 1e12, 3), peak=FP64_VECTOR_OPS / 1e12,
-                    unit="T fp64 ops/s", frac=round(ops / FP64_VECTOR_OPS, 4), traffic=None,
+                    unit="T fp64 ops/s", frac=round(ops / FP64_VECTOR_OPS, 4),
+                    traffic=measured_traffic("sweep1d_grad", "sweep1d_grad_1e7"),
                     kernel="sweep1d_grad", avg_us=round(kt["sweep1d_grad"]["avg_us"], 2))
     extra = dict(page_gpu_gradient_ms={"jax_compacted": 52.6, "enzyme_atomics": 146.9},
                  page_gpu="unnamed 16 GB NVIDIA GPU (context, not this machine)",

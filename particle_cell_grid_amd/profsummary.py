@@ -80,7 +80,7 @@ def tap_name(kernel):
              "k_inc_move": "sort_inc_move", "k_inc_count": "sort_inc_count",
              "k_inc_tiles": "sort_inc_tiles",
              "k_permute": "sort_permute", "k_tile_keys": "sort_keys",
-             "k_sweep1d": "sweep1d"}
+             "k_sweep1d": "sweep1d", "k_sweep1d_grad": "sweep1d_grad"}
     return table.get(base)
 
 

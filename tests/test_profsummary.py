@@ -26,6 +26,8 @@ from particle_cell_grid_amd import profsummary as ps
     ("k_mass_tsc_tensor_group<true>", "mass_tsc_tensor_mfma"),
     ("k_mass_tsc_flat", "mass_tsc_flat"),
     ("k_mass_tsc_tensor_flat", "mass_tsc_tensor_flat"),
+    ("k_sweep1d", "sweep1d"),
+    ("k_sweep1d_grad<true>", "sweep1d_grad"),
 ])
 def test_tap_names(symbol, name):
     assert ps.tap_name(symbol) == name

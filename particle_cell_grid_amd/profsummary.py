@@ -119,19 +119,28 @@ def median(v):
     return v[len(v) // 2]
 
 
+def calibration_reading(values):
+    """The counter's reading for the 1 GiB copy: the median over the copy
+    dispatches of at least half the largest one (a workload may also run small
+    copies of its own through the same copy kernel)."""
+    top = max(values)
+    return median([v for v in values if v >= 0.5 * top])
+
+
 def traffic(fetch_dir, write_dir, out, workload, cmd_fetch, cmd_write, json_path):
     fe = per_dispatch(fetch_dir, "FETCH_SIZE")
     wr = per_dispatch(write_dir, "WRITE_SIZE")
     if COPY_KERNEL not in fe or COPY_KERNEL not in wr:
         sys.exit("profsummary: the copy kernel is missing from a pass; no calibration")
     kib = COPY_BYTES / 1024
-    ffac = kib / median(fe[COPY_KERNEL])
-    wfac = kib / median(wr[COPY_KERNEL])
+    ffac = kib / calibration_reading(fe[COPY_KERNEL])
+    wfac = kib / calibration_reading(wr[COPY_KERNEL])
     lines = [f"# HBM traffic per dispatch: {workload}", "", "Commands (from the repository root, "
              "one MI355X; one counter per pass):", "", "```", cmd_fetch, cmd_write, "```", "",
              f"Calibration: the 1 GiB device copy (`{COPY_KERNEL}`, {kib:,.0f} KiB read and "
-             f"{kib:,.0f} KiB written) reads FETCH_SIZE = {median(fe[COPY_KERNEL]):,.0f} KiB and "
-             f"WRITE_SIZE = {median(wr[COPY_KERNEL]):,.0f} KiB per dispatch, so the counters "
+             f"{kib:,.0f} KiB written) reads FETCH_SIZE = {calibration_reading(fe[COPY_KERNEL]):,.0f} "
+             f"KiB and WRITE_SIZE = {calibration_reading(wr[COPY_KERNEL]):,.0f} KiB per dispatch, "
+             f"so the counters "
              f"are scaled by {ffac:.3f} (fetch) and {wfac:.3f} (write).", "",
              "Median over the dispatches of each kernel:", "",
              "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | "

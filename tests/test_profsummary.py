@@ -57,3 +57,12 @@ def test_digest_covers_the_kernel_source(name, src, tmp_path, monkeypatch):
     with open(os.path.join(csrc, src), "a") as f:
         f.write("\n// touched\n")
     assert ps.source_digest(name) != before
+
+
+def test_calibration_uses_the_large_copy():
+    """Small copies of the workload's own (bins, read-backs) go through the same
+    copy kernel; the calibration reading is the 1 GiB copy's."""
+    big = [524300.0, 524315.0, 524290.0]
+    small = [7.0, 162.0, 524.0, 524.0, 524.0, 524.0, 524.0]
+    assert ps.calibration_reading(big + small) in big
+    assert ps.calibration_reading(big) == 524300.0

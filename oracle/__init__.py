@@ -71,6 +71,9 @@ def lib():
         L.oracle_mass_matrix_tsc.argtypes = [i32p, C.c_int64, fpp, fpp, C.c_void_p, C.c_void_p,
                                          C.c_void_p, C.c_void_p]
         L.oracle_mass_matrix_tsc.restype = C.c_int
+        L.oracle_deposit_zigzag.argtypes = [i32p, C.c_int64, fpp, fpp, C.c_void_p, C.c_void_p,
+                                            C.c_void_p]
+        L.oracle_deposit_zigzag.restype = C.c_int
         L.oracle_mass_matrix_scalar.argtypes = [i32p, C.c_int64, fpp, C.c_void_p, C.c_void_p,
                                                 C.c_void_p]
         L.oracle_mass_matrix_scalar.restype = C.c_int
@@ -243,6 +246,23 @@ def mass_matrix_tsc(n, x, B, q, w, beta, M=None):
                                       _ptr(beta), _ptr(M))
     _check(rc, "mass_matrix_tsc")
     return M
+
+
+def deposit_zigzag(n, x, xp, q, w, J=None):
+    """Charge-conserving zigzag current deposit, J fp64 [3, nz, ny, nx] (accumulated;
+    J_c staggered by half a cell along c).  x: new positions, xp: previous ones
+    (unwrapped, less than one cell away per axis)."""
+    n3 = list(n)
+    keep = []
+    xs = _ptrs(list(x), keep)
+    ps = _ptrs(list(xp), keep)
+    q, w = _f32(q), _f32(w)
+    if J is None:
+        J = np.zeros((3, n3[2], n3[1], n3[0]), dtype=np.float64)
+    assert J.dtype == np.float64 and J.flags.c_contiguous
+    rc = lib().oracle_deposit_zigzag(_grid(n3), int(q.size), xs, ps, _ptr(q), _ptr(w), _ptr(J))
+    _check(rc, "deposit_zigzag")
+    return J
 
 
 def mass_matrix_scalar(n, x, q, w, M=None):

@@ -446,6 +446,69 @@ int oracle_mass_matrix_tsc(const int32_t n[3], int64_t np, const float *const x[
     return 0;
 }
 
+/* [TD] "Halo sizing": the charge-conserving zigzag deposit (shape order 0 in
+ * Entity's numbering), which writes up to two cells above min(i, i_prev).  The
+ * page names the scheme without its formulas; the reading taken: a move from
+ * xp to x (less than one cell per axis) is split at the relay point
+ *   xr_k = min(min(i1_k, i2_k) + 1, max(max(i1_k, i2_k), (xp_k + x_k) / 2))
+ * (i1 = floor(xp), i2 = floor(x)) into two segments that each stay in one
+ * cell, and each segment deposits the exact current of a straight path inside
+ * its cell: with F = q w (end - start) and W = midpoint - cell per axis,
+ *   J_c(cell + d1 e_k1 + d2 e_k2) += F_c [w(d1, W_k1) w(d2, W_k2) +/- F'_k1 F'_k2 / 12]
+ * (k1, k2 the other two axes, w(0, W) = 1 - W, w(1, W) = W, + when d1 = d2,
+ * F' = end - start).  J_c[g] sits at g + e_c / 2 (staggered), so that
+ *   rho(x) - rho(xp) + sum_c (J_c[g] - J_c[g - e_c]) = 0
+ * with rho the CIC charge density at the nodes.  J is fp64 [3][n_z][n_y][n_x]
+ * and is accumulated; xp is the unwrapped previous position. */
+int oracle_deposit_zigzag(const int32_t n[3], int64_t np, const float *const x[3],
+                          const float *const xp[3], const float *q, const float *w, double *J)
+{
+    if (n[0] < 1 || n[1] < 1 || n[2] < 1 || np < 0)
+        return -1;
+    const int64_t ng = (int64_t)n[0] * n[1] * n[2];
+    for (int64_t p = 0; p < np; ++p) {
+        const double qw = (double)q[p] * (double)w[p];
+        double a[3], b[3], xr[3];
+        int64_t i1[3], i2[3];
+        for (int k = 0; k < 3; ++k) {
+            a[k] = (double)xp[k][p];
+            b[k] = (double)x[k][p];
+            i1[k] = (int64_t)floor(a[k]);
+            i2[k] = (int64_t)floor(b[k]);
+            double lo = (double)(i1[k] < i2[k] ? i1[k] : i2[k]) + 1.0;
+            double hi = (double)(i1[k] > i2[k] ? i1[k] : i2[k]);
+            xr[k] = fmin(lo, fmax(hi, 0.5 * (a[k] + b[k])));
+        }
+        for (int s = 0; s < 2; ++s) {
+            const double *st = s == 0 ? a : xr, *en = s == 0 ? xr : b;
+            const int64_t *cell = s == 0 ? i1 : i2;
+            double F[3], W[3];
+            for (int k = 0; k < 3; ++k) {
+                F[k] = en[k] - st[k];
+                W[k] = 0.5 * (st[k] + en[k]) - (double)cell[k];
+            }
+            for (int c = 0; c < 3; ++c) {
+                const int k1 = c == 0 ? 1 : 0, k2 = c == 2 ? 1 : 2;
+                for (int d2 = 0; d2 < 2; ++d2)
+                    for (int d1 = 0; d1 < 2; ++d1) {
+                        const double w1 = d1 ? W[k1] : 1.0 - W[k1];
+                        const double w2 = d2 ? W[k2] : 1.0 - W[k2];
+                        const double cross = F[k1] * F[k2] / 12.0;
+                        const double wt = w1 * w2 + (d1 == d2 ? cross : -cross);
+                        int64_t g[3] = {cell[0], cell[1], cell[2]};
+                        g[k1] += d1;
+                        g[k2] += d2;
+                        const int64_t idx = wrap(g[0], n[0]) +
+                                            (int64_t)n[0] * (wrap(g[1], n[1]) +
+                                                             (int64_t)n[1] * wrap(g[2], n[2]));
+                        J[c * ng + idx] += qw * F[c] * wt;
+                    }
+            }
+        }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* 1-D windowed sweep deposit                                                */
 /* ------------------------------------------------------------------------ */

@@ -804,3 +804,54 @@ def test_tsc_mass_matrix_symmetry_row_sums_and_zero_field(orc):
     for i in range(3):
         assert np.abs(M0[..., i, i] - Ms).max() < 1e-13
     assert np.abs(M0[..., 0, 1]).max() == 0 and np.abs(M0[..., 2, 1]).max() == 0
+
+
+# ---------------------------------------------------------------------------
+# Charge-conserving zigzag deposit  ([TD] "Halo sizing", reading in the header)
+
+def _zz_inputs(r, n, npart):
+    x = [r.uniform(0, n[k], npart).astype(np.float32) for k in range(3)]
+    xp = [(x[k] - r.uniform(-0.95, 0.95, npart)).astype(np.float32) for k in range(3)]
+    q = np.where(r.random(npart) < 0.5, 1.0, -1.0).astype(np.float32)
+    w = r.uniform(0.5, 1.5, npart).astype(np.float32)
+    return x, xp, q, w
+
+
+def test_zigzag_conserves_charge(orc):
+    """rho(x) - rho(xp) + div J = 0 at every node, with rho the oracle's own CIC
+    charge deposit and J_c staggered by half a cell along c (moves that cross
+    cells and the periodic boundary included)."""
+    r = np.random.default_rng(51)
+    n = [6, 5, 7]
+    x, xp, q, w = _zz_inputs(r, n, 400)
+    J = orc.deposit_zigzag(n, x, xp, q, w)
+    ones, zeros = np.ones_like(q), np.zeros_like(q)
+    rho1 = orc.deposit(3, n, 1, x, [ones, zeros, zeros], q, w)[0]
+    rho0 = orc.deposit(3, n, 1, xp, [ones, zeros, zeros], q, w)[0]
+    div = sum(J[c] - np.roll(J[c], 1, axis=2 - c) for c in range(3))
+    assert np.abs(rho1 - rho0 + div).max() < 1e-12
+
+
+def test_zigzag_total_current(orc):
+    """sum_g J_c = sum_p q w (x_c - xp_c) per component."""
+    r = np.random.default_rng(52)
+    n = [5, 6, 5]
+    x, xp, q, w = _zz_inputs(r, n, 300)
+    J = orc.deposit_zigzag(n, x, xp, q, w)
+    qw = q.astype(np.float64) * w
+    for c in range(3):
+        tot = np.sum(qw * (x[c].astype(np.float64) - xp[c].astype(np.float64)))
+        assert abs(J[c].sum() - tot) < 1e-11
+
+
+def test_zigzag_single_particle(orc):
+    # xp = (2.25, 3.5, 1.5) -> x = (2.75, 3.5, 1.5), q w = 1, inside cell (2, 3, 1):
+    # relay at x = 2.5; each half carries F_x = 1/4 at transverse weights 1/2,
+    # so J_x = 2 * 1/4 * 1/4 = 1/8 at the four nodes (2, 3..4, 1..2); no J_y, J_z
+    J = orc.deposit_zigzag([8, 8, 8], _one([2.75, 3.5, 1.5]), _one([2.25, 3.5, 1.5]),
+                           np.float32([1.0]), np.float32([1.0]))
+    exp = np.zeros_like(J)
+    for gz in (1, 2):
+        for gy in (3, 4):
+            exp[0, gz, gy, 2] = 0.125
+    assert np.array_equal(J, exp)

@@ -75,6 +75,11 @@ MUTANTS = [
     ("TSC tensor mass matrix with the first node's z taken from its y digit",
      "int ax = a % 3, ay = (a / 3) % 3, az = a / 9;",
      "int ax = a % 3, ay = (a / 3) % 3, az = (a / 3) % 3;"),
+    ("zigzag deposit without the straight-segment cross term",
+     "const double wt = w1 * w2 + (d1 == d2 ? cross : -cross);", "const double wt = w1 * w2;"),
+    ("zigzag relay point from the lower bound twice",
+     "xr[k] = fmin(lo, fmax(hi, 0.5 * (a[k] + b[k])));",
+     "xr[k] = fmin(lo, fmax(lo - 1.0, 0.5 * (a[k] + b[k])));"),
     ("TSC tensor mass matrix without the node weights' product",
      "row[ij] += s[ij] * (wa * wb);", "row[ij] += s[ij] * wa;"),
 ]

@@ -19,7 +19,9 @@ sort + MFMA assembly), mass_f64_64_ppc64 (the same in fp64), mass_scalar_64_ppc6
 (1-D windowed sweep), mass_tsc_scalar_64_ppc64 (the scalar matrix with TSC
 weights, support-group sort + MFMA assembly), mass_tsc_64_ppc64 (the ECSIM
 matrix with TSC weights), sweep1d_grad_1e7 (the sweep's loss gradient, 10^7 particles:
-forward sweep, seed and reverse gather in one library call).
+forward sweep, seed and reverse gather in one library call), zigzag3d_128_ppc32
+(the charge-conserving zigzag deposit of the cic3d particles moved by their
+velocities, with the incremental tile sort).
 
 Prints ONE JSON line (rank 0).  Only one GPU is used: --gpus above 1 exits.
 """
@@ -55,7 +57,7 @@ def parse():
                              "tsc3d_128_blob", "mass_64_ppc64", "mass_f64_64_ppc64",
                              "mass_scalar_64_ppc64", "mass_tsc_scalar_64_ppc64",
                              "mass_tsc_64_ppc64",
-                             "sweep1d_grad_1e7"])
+                             "sweep1d_grad_1e7", "zigzag3d_128_ppc32"])
     ap.add_argument("--tile", type=int, default=0, help="tile edge T (0 = the workload's)")
     ap.add_argument("--block", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -316,6 +318,111 @@ def bench_deposit(args, torch, pcg, name):
     return dict(value=cnt / (ms * 1e-3), ms=ms, wall=wall, dtype="f32", config=config,
                 roofline=roof_dom if roof_dom else roof, kernels=kernels, extra=extra,
                 cpu=cpu, unit="particles/s")
+
+
+def bench_zigzag(args, torch, pcg):
+    """Charge-conserving zigzag deposit on the cic3d_128_ppc32 particles, each
+    moved by its velocity (x_prev = x - v, unwrapped).  The particles are
+    grouped by a layout keyed on their previous positions, as the last step's
+    sort left them; one step deposits their currents with that layout and
+    regroups them by the new positions (incremental tile sort from it)."""
+    import numpy as np
+
+    import synthetic
+
+    T = args.tile or 8
+    D = 1
+    progress("generating cic3d_128_ppc32 (zigzag moves)")
+    wl = synthetic.workload("cic3d_128_ppc32")
+    n, cnt = wl.n, wl.count
+    xp = synthetic.previous_positions(wl.x, scale_v=1.0, v=wl.v)
+    key0 = [np.mod(a, np.float32(n[k])).astype(np.float32) for k, a in enumerate(xp)]
+    key0 = [np.where(a >= n[k], np.float32(0), a) for k, a in enumerate(key0)]
+    dev = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    arrays = [t(a) for a in wl.x] + [t(a) for a in xp] + [t(wl.q), t(wl.w)]
+    _, _, off0, cur = pcg.pcg_tile_sort(3, n, 1, T, [t(a) for a in key0], arrays)
+    del arrays
+    torch.cuda.synchronize()
+    nt = pcg.ntiles(3, n, T)
+    J = torch.zeros(3, n[2], n[1], n[0], dtype=torch.float32, device=dev)
+    esc = torch.zeros(1, dtype=torch.int64, device=dev)
+    lay = pcg.Layout(T=T, order=1, tile_offsets=off0, n_partitioned=cnt, drift=D)
+    off1 = torch.empty(nt + 1, dtype=torch.int32, device=dev)
+    nxt = [torch.empty_like(a) for a in cur]
+    sws = torch.empty(pcg.pcg_sort_workspace_bytes(3, n, cnt, T), dtype=torch.uint8, device=dev)
+    x, xpd, q, w = cur[0:3], cur[3:6], cur[6], cur[7]
+
+    def deposit():
+        pcg.deposit_currents_zigzag(n, x, xpd, q, w, J, lay, esc)
+
+    def step():
+        J.zero_()
+        deposit()
+        pcg.pcg_tile_sort(3, n, 1, T, x, cur, outs=nxt, want_perm=False, want_keys=False,
+                          tile_offsets=off1, workspace=sws, prev=lay)
+
+    progress("timing steps")
+    ms, wall, kt = time_steps(torch, pcg, step, args.steps, args.warmup)
+    progress(f"{ms:.4f} ms per step")
+    esc.zero_()
+    deposit()
+    torch.cuda.synchronize()
+    n_esc = int(esc.item())
+    jbytes = 3 * n[0] * n[1] * n[2] * 4
+    alg = {
+        # x, x_prev, q, w read once + J read-modify-write
+        "zigzag_tiled": cnt * 8 * 4 + 2 * jbytes,
+        "sort_inc_count": cnt * 3 * 4,
+        "sort_inc_move": cnt * 2 * 8 * 4,
+    }
+    kernels = {}
+    for nm, kk in kt.items():
+        e = dict(avg_us=round(kk["avg_us"], 2), launches_per_step=kk["launches"] / args.steps)
+        if nm in alg:
+            e["alg_bytes"] = alg[nm]
+            e["GBps"] = round(alg[nm] / (kk["avg_us"] * 1e-6) / 1e9, 1)
+        kernels[nm] = e
+    roof = roofline_entry(kt, "zigzag_tiled", bytes_per_launch=alg["zigzag_tiled"])
+    if roof:
+        roof["traffic"] = measured_traffic("zigzag_tiled", "zigzag3d_128_ppc32")
+    extra = dict(escaped_particles=n_esc)
+    dep_ms = time_plain(torch, lambda: (J.zero_(), deposit()), args.steps)
+    extra["deposit_only_ms"] = round(dep_ms, 4)
+    if not args.no_flat:
+        def flat():
+            J.zero_()
+            pcg.deposit_currents_zigzag(n, x, xpd, q, w, J, None)
+        fl_ms = time_plain(torch, flat, max(3, args.steps // 4))
+        extra["flat_deposit_ms"] = round(fl_ms, 4)
+        extra["tiled_speedup_vs_flat"] = round(fl_ms / dep_ms, 2)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        progress("timing the oracle on the host")
+
+        def run(m):
+            t0 = time.perf_counter()
+            oracle.tile_sort(3, n, 1, T, [a[:m] for a in wl.x])
+            oracle.deposit_zigzag(n, [a[:m] for a in wl.x], [a[:m] for a in xp], wl.q[:m],
+                                  wl.w[:m])
+            return time.perf_counter() - t0
+
+        cal = 1 << 20
+        per = run(cal) / cal
+        m = int(min(cnt, max(cal, args.cpu_seconds / per)))
+        sec = run(m)
+        cpu = dict(value=round(m / sec, 1), unit="particles/s", cores=1, kind="oracle",
+                   sample=f"first {m} of {cnt} particles: oracle tile sort + fp64 zigzag "
+                          f"deposit, {sec:.1f} s, 1 thread")
+    config = dict(workload="3-D charge-conserving zigzag current deposit + tile sort, 128^3 "
+                           "periodic, 32 ppc, each particle moved by its velocity",
+                  particles=cnt, grid=n, tile=T, drift=D,
+                  step="zero J + tiled zigzag deposit with the layout of the previous "
+                       "positions + incremental tile sort on the new positions")
+    return dict(value=cnt / (ms * 1e-3), ms=ms, wall=wall, dtype="f32", config=config,
+                roofline=roof, kernels=kernels, extra=extra, cpu=cpu, unit="particles/s")
 
 
 # ----------------------------------------------------------------- mass matrix
@@ -689,6 +796,8 @@ def main():
         r = bench_sweep_grad(args, torch, pcg)
     elif args.workload == "mass_scalar_64_ppc64":
         r = bench_mass(args, torch, pcg, scalar=True)
+    elif args.workload == "zigzag3d_128_ppc32":
+        r = bench_zigzag(args, torch, pcg)
     else:
         r = bench_sweep(args, torch, pcg)
     line = {

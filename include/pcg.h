@@ -17,7 +17,7 @@
  *   cell g spans [g, g+1), so positions are in cell units with
  *   0 <= x_k < n_k.  Grid arrays are x-fastest (linear node
  *   g = gx + n_x*(gy + n_y*gz)).  Unused axes of a 1-D or 2-D grid have n_k = 1.
- * Accumulation.  deposit_currents and assemble_mass_matrix ADD into their
+ * Accumulation.  deposit_currents(_zigzag) and assemble_mass_matrix ADD into their
  *   output (the caller zeroes it); the 1-D sweep entry points OVERWRITE their
  *   outputs.
  * Errors.  Every entry point returns a pcg_status.  Arguments are validated on
@@ -198,6 +198,41 @@ pcg_status deposit_currents_regroup(const pcg_grid *grid, const pcg_particles *p
                                     const float *const in_arrays[], float *const out_arrays[],
                                     uint32_t *tile_offsets, void *workspace,
                                     size_t workspace_bytes, void *stream);
+
+/* The charge-conserving zigzag current deposit ([TD] "Halo sizing", which
+ * names it as writing up to two cells above min(i, i_prev)).  Each particle p
+ * moves from x_prev to x, less than one cell per axis (x_prev unwrapped:
+ * x_prev_k - x_k in (-1, 1); x in [0, n_k)).  The move is split at the relay
+ * point xr_k = min(min(i1_k, i2_k) + 1, max(max(i1_k, i2_k), (x_prev_k + x_k)/2))
+ * (i1 = floor(x_prev), i2 = floor(x)) into two segments that each stay in one
+ * cell; each segment deposits the exact current of a straight path inside its
+ * cell: with F = q w (end - start), F' = end - start and W = midpoint - cell,
+ *   J_c(cell + d1 e_k1 + d2 e_k2) += F_c [w(d1, W_k1) w(d2, W_k2) +/- F'_k1 F'_k2 / 12]
+ * (k1 < k2 the other axes, w(0, W) = 1 - W, w(1, W) = W, + when d1 = d2),
+ * 24 contributions per particle.  J_c[g] is the current through the face at
+ * g + e_c/2, so that rho(x) - rho(x_prev) + sum_c (J_c[g] - J_c[g - e_c]) = 0
+ * at every node, rho the CIC charge density.  3-D grids only.
+ * J: device fp32 [3][n_z][n_y][n_x], accumulated.  x_prev: host array of 3
+ *   device fp32 pointers [count].
+ * tile: a layout from pcg_tile_sort with order 1 keyed on x (the new
+ *   positions) or on the previous ones, or NULL.  With a layout, one
+ *   work-group per tile accumulates into an LDS window of TE = T + 2*drift + 3
+ *   nodes per axis starting drift + 1 nodes below the tile origin ([TD] "How a
+ *   tile deposit runs") and adds it to J with one atomic per non-zero node.
+ *   The window holds exact int64 fixed-point sums, scaled per tile from its
+ *   particle count and largest |q w| so that no sum can overflow, or fp32
+ *   sums when 3*TE^3*8 bytes exceed the LDS.  A particle whose stencil does
+ *   not fit (its layout is more than `drift` cells stale, or it crossed more
+ *   than one cell boundary on an axis) takes the escape valve to global
+ *   atomics and is counted.  The tail [n_partitioned, count) and tile == NULL
+ *   use the flat one-thread-per-particle kernel.  Requires n_k % T == 0 and
+ *   3*TE^3*4 bytes <= 160 KiB (else PCG_ELDS).
+ * n_escaped: optional device uint64 counter, ADDED to.
+ * Errors: PCG_EUNSUPPORTED for dim != 3; PCG_EINVAL for a NULL array with
+ *   count > 0, a count outside [0, 2^31) or a bad layout. */
+pcg_status deposit_currents_zigzag(const pcg_grid *grid, const pcg_particles *particles,
+                                   const float *const x_prev[3], const pcg_tile *tile, float *J,
+                                   unsigned long long *n_escaped, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* ECSIM mass matrix  ([MM] §2.1 Eq.(4)-(6), §2.2 Eq.(9)-(11), §3)           */

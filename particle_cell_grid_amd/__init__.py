@@ -63,6 +63,9 @@ _lib.deposit_currents_regroup.argtypes = [_P(Grid), _P(Particles), C.c_int32, _P
                                           C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
                                           C.c_void_p]
 _lib.deposit_currents_regroup.restype = C.c_int32
+_lib.deposit_currents_zigzag.argtypes = [_P(Grid), _P(Particles), C.c_void_p, _P(Tile),
+                                         C.c_void_p, C.c_void_p, C.c_void_p]
+_lib.deposit_currents_zigzag.restype = C.c_int32
 _lib.pcg_mass_workspace_bytes.argtypes = [_P(Grid)]
 _lib.pcg_mass_workspace_bytes.restype = C.c_size_t
 _lib.assemble_mass_matrix.argtypes = [_P(Grid), _P(Particles), C.c_void_p, C.c_void_p, _P(Tile),
@@ -280,6 +283,24 @@ def deposit_currents_regroup(dim: int, n: Sequence[int], order: int, x: List[tor
                                        _ptr(workspace), int(workspace.numel()), _stream())
     _check(st, "deposit_currents_regroup")
     return tile_offsets, outs
+
+
+def deposit_currents_zigzag(n: Sequence[int], x: List[torch.Tensor], x_prev: List[torch.Tensor],
+                            q: torch.Tensor, w: torch.Tensor, J: torch.Tensor,
+                            layout: Optional[Layout] = None,
+                            n_escaped: Optional[torch.Tensor] = None):
+    """J[3, nz, ny, nx] (fp32) += the charge-conserving zigzag current of each
+    particle's move from x_prev to x (3-D).  `layout`: an order-1 tile layout
+    keyed on x, or None for the flat kernel."""
+    g = make_grid(3, n)
+    P = _particles(q.numel(), x, None, q, w)
+    xp = (C.c_void_p * 3)(*[x_prev[k].data_ptr() for k in range(3)])
+    tile = layout.to_c() if layout is not None else None
+    st = _lib.deposit_currents_zigzag(C.byref(g), C.byref(P), xp,
+                                      C.byref(tile) if tile is not None else None, _ptr(J),
+                                      _ptr(n_escaped), _stream())
+    _check(st, "deposit_currents_zigzag")
+    return J
 
 
 def pcg_mass_workspace_bytes(n: Sequence[int]) -> int:

@@ -1,0 +1,341 @@
+// zigzag.hip -- charge-conserving zigzag current deposit ([TD] Entity wiki,
+// "Tiled current deposit": "Halo sizing" names the zigzag deposit, which writes
+// up to two cells above min(i, i_prev); "How a tile deposit runs" for the
+// tiled form).
+//
+// A move from xp to x (less than one cell per axis) is split at the relay
+// point xr_k = min(min(i1_k, i2_k) + 1, max(max(i1_k, i2_k), (xp_k + x_k) / 2)),
+// i1 = floor(xp), i2 = floor(x), into two segments that each stay in one cell.
+// Each segment deposits the exact current of a straight path inside its cell:
+// with F = q w (end - start) and W = midpoint - cell per axis, component c gets
+//   F_c [w(d1, W_k1) w(d2, W_k2) +/- F'_k1 F'_k2 / 12]
+// at cell + d1 e_k1 + d2 e_k2 (k1, k2 the other axes, + when d1 = d2).  J_c[g]
+// sits at g + e_c / 2, so that the CIC charge density obeys the discrete
+// continuity equation to round-off.  24 contributions per particle.
+//
+// Tiled: one work-group per tile of a layout keyed on the new position (the
+// order-1 tile sort); its LDS window per axis starts D + 1 nodes below the
+// tile origin and spans TE = T + 2 D + 3 nodes, which holds every stencil of a
+// particle that moved at most D cells since the layout was made.  Others take
+// the escape valve (global atomics, counted).  The window is added to J with
+// one atomic per non-zero node.
+#include <algorithm>
+#include <type_traits>
+
+#include "common.hpp"
+
+namespace pcg {
+namespace {
+
+// Dynamic LDS available to the tiled kernel (its static part is a few words).
+constexpr size_t ZZ_LDS_MAX = 160 * 1024 - 256;
+
+struct ZzArgs {
+    int n[3];
+    const float *x[3];
+    const float *xp[3];
+    const float *q;
+    const float *w;
+    float *J;  // [3][n_z][n_y][n_x]
+    const uint32_t *offsets;
+    int64_t n_part;
+    int T, D, TE;
+    int nt[3];  // tiles per axis
+    unsigned long long *n_escaped;
+};
+
+__device__ inline int wrapn(int64_t i, int n)
+{
+    const int64_t r = i % n;
+    return (int)(r < 0 ? r + n : r);
+}
+
+// The particle's move: relay point, cells and midpoints of both segments.
+struct Move {
+    int cell[2][3];
+    float F[2][3];  // end - start of each segment
+    float W[2][3];  // midpoint - cell
+    float qw;
+    int lo[3];       // min(i1, i2): the first node of the stencil per axis
+    int64_t ext[3];  // max(i1, i2) + 1 - lo: its last node (2 for a move under a cell)
+};
+
+// Positions are taken relative to lo = min(i1, i2) first: a - lo and b - lo
+// lie in [-1, 2) and are exact (or within an ulp of 1 for |a| < 1), so the
+// segment lengths and midpoints keep fp32's relative precision wherever the
+// particle sits on the grid.
+__device__ inline Move make_move(const ZzArgs &m, int64_t p)
+{
+    Move mv;
+    mv.qw = m.q[p] * m.w[p];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const float a = m.xp[k][p], b = m.x[k][p];
+        const float fa = floorf(a), fb = floorf(b);
+        const float flo = fminf(fa, fb);
+        const float A = a - flo, B = b - flo;   // in cell units above lo
+        const float ca = fa - flo, cb = fb - flo;  // 0 or 1 (or more for a long move)
+        const float xr = fminf(1.0f, fmaxf(fmaxf(ca, cb), 0.5f * (A + B)));
+        mv.cell[0][k] = (int)fa;
+        mv.cell[1][k] = (int)fb;
+        mv.F[0][k] = xr - A;
+        mv.F[1][k] = B - xr;
+        mv.W[0][k] = 0.5f * (A + xr) - ca;
+        mv.W[1][k] = 0.5f * (xr + B) - cb;
+        mv.lo[k] = (int)flo;
+        mv.ext[k] = (int64_t)(int)fmaxf(fa, fb) + 1 - mv.lo[k];
+    }
+    return mv;
+}
+
+// Calls f(c, g[3] (unwrapped node), value) for the 24 contributions.
+template <typename Fn>
+__device__ inline void for_each_contribution(const Move &mv, Fn &&f)
+{
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+            const int k1 = c == 0 ? 1 : 0, k2 = c == 2 ? 1 : 2;
+            const float cross = mv.F[s][k1] * mv.F[s][k2] * (1.0f / 12.0f);
+            const float fc = mv.qw * mv.F[s][c];
+#pragma unroll
+            for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+                for (int d1 = 0; d1 < 2; ++d1) {
+                    const float w1 = d1 ? mv.W[s][k1] : 1.0f - mv.W[s][k1];
+                    const float w2 = d2 ? mv.W[s][k2] : 1.0f - mv.W[s][k2];
+                    int g[3] = {mv.cell[s][0], mv.cell[s][1], mv.cell[s][2]};
+                    g[k1] += d1;
+                    g[k2] += d2;
+                    f(c, g, fc * (w1 * w2 + (d1 == d2 ? cross : -cross)));
+                }
+        }
+    }
+}
+
+__device__ inline void deposit_global(const ZzArgs &m, const Move &mv)
+{
+    const int64_t ng = (int64_t)m.n[0] * m.n[1] * m.n[2];
+    for_each_contribution(mv, [&](int c, const int *g, float v) {
+        const int64_t idx = wrapn(g[0], m.n[0]) +
+                            (int64_t)m.n[0] * (wrapn(g[1], m.n[1]) +
+                                               (int64_t)m.n[1] * wrapn(g[2], m.n[2]));
+        atomic_add_f32(&m.J[c * ng + idx], v);
+    });
+}
+
+__global__ __launch_bounds__(256) void k_zigzag_flat(ZzArgs m, int64_t begin, int64_t end)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t p = begin + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < end; p += stride)
+        deposit_global(m, make_move(m, p));
+}
+
+// Per-axis window coordinate of a stencil's first node: lo - ws, brought into
+// [0, n) by at most one period each way (enough for positions within a period
+// of the grid; anything else fails the fit test and takes the valve).
+__device__ inline int64_t window_coord(int lo, int ws, int n)
+{
+    int64_t d = (int64_t)lo - ws;
+    d += d < 0 ? n : 0;
+    d -= d >= n ? n : 0;
+    return d;
+}
+
+// The largest |q w| of the tile's particles (the fixed-point scale's bound).
+__device__ inline float tile_max_qw(const ZzArgs &m, int64_t lo, int64_t hi, float *red)
+{
+    float mx = 0.0f;
+    for (int64_t p = lo + threadIdx.x; p < hi; p += blockDim.x)
+        mx = fmaxf(mx, fabsf(m.q[p] * m.w[p]));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        mx = fmaxf(mx, __shfl_xor(mx, off));
+    if ((threadIdx.x & 63) == 0)
+        red[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    mx = red[0];
+    for (int i = 1; i < (int)(blockDim.x >> 6); ++i)
+        mx = fmaxf(mx, red[i]);
+    return mx;
+}
+
+// One work-group per tile.  FIXED: the window holds int64 sums of the
+// contributions scaled by 2^k (exact and independent of the order of the adds;
+// LDS integer atomics run over twenty times the rate of float ones on this
+// chip).  A particle whose move stays within neighbouring cells on every axis
+// has |F'| <= 1 and 0 <= w <= 1 per segment, so it adds at most 2 (13/12) |q w|
+// to any node (two segments); with N particles in the tile every node sum stays
+// below N * 2.17 * max|q w|, and k is chosen so that this bound is below 2^62.
+// Longer moves take the valve.  Not FIXED: fp32 sums (the window in int64 does
+// not fit the LDS).
+template <bool FIXED>
+__global__ __launch_bounds__(256) void k_zigzag_tiled(ZzArgs m)
+{
+    using Acc = typename std::conditional<FIXED, unsigned long long, float>::type;
+    extern __shared__ __align__(8) unsigned char lds_raw[];
+    Acc *win = reinterpret_cast<Acc *>(lds_raw);  // [3][TE][TE][TE]
+    __shared__ float red[4];
+    const int TE = m.TE;
+    const int vol = TE * TE * TE;
+    const uint32_t t = blockIdx.x;
+    const int tc[3] = {(int)(t % (uint32_t)m.nt[0]), (int)((t / (uint32_t)m.nt[0]) % (uint32_t)m.nt[1]),
+                       (int)(t / ((uint32_t)m.nt[0] * (uint32_t)m.nt[1]))};
+    int ws[3];  // window start (unwrapped node index)
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+        ws[k] = tc[k] * m.T - m.D - 1;
+    for (int i = threadIdx.x; i < 3 * vol; i += blockDim.x)
+        win[i] = 0;
+    const int64_t lo = std::min<int64_t>(m.offsets[t], m.n_part);
+    const int64_t hi = std::max<int64_t>(lo, std::min<int64_t>(m.offsets[t + 1], m.n_part));
+    int k_scale = 0;
+    if (FIXED) {
+        const float bound = (float)(hi - lo) * 2.17f * tile_max_qw(m, lo, hi, red);
+        int e = 0;
+        frexpf(bound, &e);  // bound < 2^e
+        k_scale = bound > 0.0f ? 62 - e : 0;
+    }
+    __syncthreads();
+    uint32_t escaped = 0;
+    for (int64_t p = lo + threadIdx.x; p < hi; p += blockDim.x) {
+        const Move mv = make_move(m, p);
+        // the stencil fits if its last node lies in the window (a move over
+        // more than a neighbouring cell is sent to global memory)
+        int l0[3];
+        bool fits = true;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const int64_t d = window_coord(mv.lo[k], ws[k], m.n[k]);
+            l0[k] = (int)d;
+            fits = fits && d >= 0 && mv.ext[k] >= 1 && mv.ext[k] <= 2 && d + mv.ext[k] < TE;
+        }
+        if (!fits) {
+            deposit_global(m, mv);
+            ++escaped;
+            continue;
+        }
+        for_each_contribution(mv, [&](int c, const int *g, float v) {
+            const int lx = l0[0] + (g[0] - mv.lo[0]), ly = l0[1] + (g[1] - mv.lo[1]),
+                      lz = l0[2] + (g[2] - mv.lo[2]);
+            Acc *a = &win[c * vol + (lz * TE + ly) * TE + lx];
+            if constexpr (FIXED)
+                atomicAdd(a, (unsigned long long)(long long)ldexpf(v, k_scale));
+            else
+                atomicAdd(a, v);
+        });
+    }
+    __syncthreads();
+    const int64_t ng = (int64_t)m.n[0] * m.n[1] * m.n[2];
+    for (int i = threadIdx.x; i < 3 * vol; i += blockDim.x) {
+        const Acc a = win[i];
+        if (a == 0)
+            continue;
+        float v;
+        if constexpr (FIXED)
+            v = (float)ldexp((double)(long long)a, -k_scale);
+        else
+            v = a;
+        const int c = i / vol, r = i - c * vol;
+        const int lx = r % TE, ly = (r / TE) % TE, lz = r / (TE * TE);
+        const int64_t idx = wrapn(ws[0] + lx, m.n[0]) +
+                            (int64_t)m.n[0] * (wrapn(ws[1] + ly, m.n[1]) +
+                                               (int64_t)m.n[1] * wrapn(ws[2] + lz, m.n[2]));
+        atomic_add_f32(&m.J[c * ng + idx], v);
+    }
+    if (m.n_escaped && escaped)
+        atomicAdd(m.n_escaped, (unsigned long long)escaped);
+}
+
+}  // namespace
+}  // namespace pcg
+
+using namespace pcg;
+
+extern "C" pcg_status deposit_currents_zigzag(const pcg_grid *grid, const pcg_particles *particles,
+                                              const float *const x_prev[3], const pcg_tile *tile,
+                                              float *J, unsigned long long *n_escaped,
+                                              void *stream)
+{
+    const char *who = "deposit_currents_zigzag";
+    clear_error();
+    PCG_TRY(check_grid(grid, who));
+    if (grid->dim != 3)
+        return fail(PCG_EUNSUPPORTED, "%s: only 3-D grids (dim = %d)", who, grid->dim);
+    if (!particles || !J)
+        return fail(PCG_EINVAL, "%s: particles or J is NULL", who);
+    const int64_t count = particles->count;
+    if (count < 0 || count >= (int64_t(1) << 31))
+        return fail(PCG_EINVAL, "%s: count %lld outside [0, 2^31)", who, (long long)count);
+    if (count > 0) {
+        for (int k = 0; k < 3; ++k)
+            if (!particles->x[k] || !x_prev || !x_prev[k])
+                return fail(PCG_EINVAL, "%s: x[%d] or x_prev[%d] is NULL", who, k, k);
+        if (!particles->q || !particles->w)
+            return fail(PCG_EINVAL, "%s: q or w is NULL", who);
+    }
+    ZzArgs m{};
+    for (int k = 0; k < 3; ++k) {
+        m.n[k] = grid->n[k];
+        m.x[k] = particles->x[k];
+        m.xp[k] = x_prev ? x_prev[k] : nullptr;
+    }
+    m.q = particles->q;
+    m.w = particles->w;
+    m.J = J;
+    m.n_escaped = n_escaped;
+    size_t lds = 0;
+    bool fixed = true;
+    if (tile) {
+        if (tile->order != 1)
+            return fail(PCG_EINVAL, "%s: the layout must be keyed on CIC cells (order 1, not %d)",
+                        who, tile->order);
+        if (tile->T < 1 || tile->drift < 0 || !tile->tile_offsets)
+            return fail(PCG_EINVAL, "%s: bad layout (T = %d, drift = %d, offsets %p)", who,
+                        tile->T, tile->drift, (const void *)tile->tile_offsets);
+        for (int k = 0; k < 3; ++k)
+            if (grid->n[k] % tile->T)
+                return fail(PCG_EINVAL, "%s: n[%d] = %d is not a multiple of T = %d", who, k,
+                            grid->n[k], tile->T);
+        if (tile->n_partitioned < 0 || tile->n_partitioned > count)
+            return fail(PCG_EINVAL, "%s: n_partitioned outside [0, count]", who);
+        m.T = tile->T;
+        m.D = tile->drift;
+        m.TE = tile->T + 2 * tile->drift + 3;
+        lds = (size_t)3 * m.TE * m.TE * m.TE * sizeof(unsigned long long);
+        fixed = lds <= ZZ_LDS_MAX;
+        if (!fixed)
+            lds /= 2;  // fp32 sums
+        if (lds > ZZ_LDS_MAX)
+            return fail(PCG_ELDS, "%s: window of %zu bytes exceeds the LDS (T = %d, D = %d)",
+                        who, lds, tile->T, tile->drift);
+        for (int k = 0; k < 3; ++k)
+            m.nt[k] = grid->n[k] / tile->T;
+        m.offsets = tile->tile_offsets;
+        m.n_part = tile->n_partitioned;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (count == 0)
+        return PCG_OK;
+    auto flat = [&](int64_t begin, int64_t end) -> pcg_status {
+        if (end <= begin)
+            return PCG_OK;
+        const int64_t blocks =
+            std::min<int64_t>((end - begin + 255) / 256, (int64_t)device_cus() * 32);
+        return launch("zigzag_flat", k_zigzag_flat, dim3((unsigned)blocks), dim3(256), 0, st, m,
+                      begin, end);
+    };
+    if (!tile)
+        return flat(0, count);
+    if (m.n_part > 0) {
+        auto kern = fixed ? k_zigzag_tiled<true> : k_zigzag_tiled<false>;
+        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds) != hipSuccess)
+            return fail(PCG_EHIP, "%s: cannot raise dynamic LDS to %zu bytes", who, lds);
+        const int64_t ntiles = (int64_t)m.nt[0] * m.nt[1] * m.nt[2];
+        PCG_TRY(launch(fixed ? "zigzag_tiled" : "zigzag_tiled_f32", kern, dim3((unsigned)ntiles),
+                       dim3(256), lds, st, m));
+    }
+    return flat(tile->n_partitioned, count);
+}

@@ -22,7 +22,7 @@ import sys
 
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 KERNEL_SOURCES = {"deposit": "deposit.hip", "sort": "sort.hip", "mass": "mass.hip",
-                  "mass_tsc": "mass_tsc.hip", "sweep": "sweep.hip"}
+                  "mass_tsc": "mass_tsc.hip", "sweep": "sweep.hip", "zigzag": "zigzag.hip"}
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30          # the benchmark's context copy: 2^28 fp32 read and written
 
@@ -80,7 +80,8 @@ def tap_name(kernel):
              "k_inc_move": "sort_inc_move", "k_inc_count": "sort_inc_count",
              "k_inc_tiles": "sort_inc_tiles",
              "k_permute": "sort_permute", "k_tile_keys": "sort_keys",
-             "k_sweep1d": "sweep1d", "k_sweep1d_grad": "sweep1d_grad"}
+             "k_sweep1d": "sweep1d", "k_sweep1d_grad": "sweep1d_grad",
+             "k_zigzag_tiled": "zigzag_tiled", "k_zigzag_flat": "zigzag_flat"}
     return table.get(base)
 
 

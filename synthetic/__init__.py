@@ -171,6 +171,31 @@ def deposit_workload(dim, n, ppc=None, count=None, sigma_v=0.1, w_uniform=False,
                               n_far=n_far, seed=seed))
 
 
+def previous_positions(x, max_step=0.95, scale_v=None, v=None, seed=0):
+    """Unwrapped previous positions for a move deposit (fp32): x_k - d_k with
+    d_k ~ U(-max_step, max_step), or, with ``v`` given, d = scale_v * v.  The
+    result may lie outside [0, n_k) by less than a cell (the particle crossed
+    the periodic boundary)."""
+    if v is not None:
+        return [(np.asarray(x[k], F32) - F32(scale_v) * np.asarray(v[k], F32)).astype(F32)
+                for k in range(len(x))]
+    r = rng(seed)
+    return [(np.asarray(x[k], F32) - r.uniform(-max_step, max_step, x[k].size).astype(F32))
+            .astype(F32) for k in range(len(x))]
+
+
+def stale_keys(x, n, fraction, span, seed=0):
+    """Positions to key a stale tile layout on: x, except a ``fraction`` subset
+    shifted by U(-span, span) cells per axis (wrapped into [0, n_k))."""
+    r = rng(seed)
+    out = []
+    for k in range(len(x)):
+        d = r.uniform(-span, span, x[k].size).astype(F32)
+        d[r.random(x[k].size) >= fraction] = 0
+        out.append(periodic_shift(x[k], d, int(n[k])))
+    return out
+
+
 def mass_workload(n, ppc, dt=0.1, w_uniform=False, seed=0):
     """Particles for the ECSIM mass matrix: exactly ppc per cell, B ~ N(0,1)^3,
     q/m = +1/-1 alternating (m = 1), beta = (q/m) dt / 2."""

@@ -41,7 +41,7 @@ def test_header_declares_the_entry_points():
               "assemble_mass_matrix_tsc",
               "assemble_mass_matrix_f64",
               "assemble_mass_matrix_scalar_f64", "deposit_sweep1d", "deposit_sweep1d_grad",
-              "deposit_sweep1d_loss_grad",
+              "deposit_sweep1d_loss_grad", "deposit_currents_zigzag",
               "pcg_status_string", "pcg_last_error", "pcg_version", "pcg_timing_enable",
               "pcg_timing_reset", "pcg_timing_read", "pcg_timing_names"]:
         assert n in names
@@ -141,6 +141,38 @@ def test_deposit_validation(lib):
     small = grid(3, [4, 4, 4])
     t = Tile(4, 1, 3, 0, 1000, FAKE)                              # drift + order >= n
     assert call(small, tile=t) == EINVAL
+
+
+def test_zigzag_validation(lib):
+    lib.pcg_last_error.restype = C.c_char_p
+    zz = lib.deposit_currents_zigzag
+    P = particles(1000)
+    xp = (C.c_void_p * 3)(FAKE, FAKE, FAKE)
+
+    def call(g, tile=None, J=C.c_void_p(FAKE), P=P, xp=xp):
+        return zz(C.byref(g), C.byref(P), xp, C.byref(tile) if tile else None, J, None, None)
+
+    assert call(grid(0, [1, 1, 1])) == EINVAL
+    assert call(grid(2, [8, 8])) == EUNSUPPORTED                  # 3-D only
+    assert call(grid(3, [8, 8, 8]), J=None) == EINVAL
+    assert call(grid(3, [8, 8, 8]), xp=None) == EINVAL
+    bad = (C.c_void_p * 3)(FAKE, None, FAKE)
+    assert call(grid(3, [8, 8, 8]), xp=bad) == EINVAL
+    P2 = particles(1000)
+    P2.w = None
+    assert call(grid(3, [8, 8, 8]), P=P2) == EINVAL
+    assert call(grid(3, [8, 8, 8]), P=particles(-1)) == EINVAL
+    assert call(grid(3, [8, 8, 8]), P=particles(1 << 31)) == EINVAL
+    g = grid(3, [64, 64, 64])
+    assert call(g, tile=Tile(8, 2, 1, 0, 1000, FAKE)) == EINVAL  # layout keyed with TSC
+    assert b"order" in lib.pcg_last_error()
+    assert call(g, tile=Tile(6, 1, 1, 0, 1000, FAKE)) == EINVAL  # 64 % 6
+    assert call(g, tile=Tile(8, 1, -1, 0, 1000, FAKE)) == EINVAL  # negative drift
+    assert call(g, tile=Tile(8, 1, 1, 0, 1001, FAKE)) == EINVAL  # n_partitioned > count
+    assert call(g, tile=Tile(8, 1, 1, 0, 1000, None)) == EINVAL  # no offsets
+    assert call(g, tile=Tile(16, 1, 8, 0, 1000, FAKE)) == ELDS   # TE = 35: 35^3*12 B > 160 KiB
+    # no particles: nothing to check beyond the grid, nothing launched
+    assert call(g, P=particles(0), xp=None) == 0
 
 
 def test_deposit_workspace_size(lib):

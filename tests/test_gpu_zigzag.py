@@ -1,0 +1,169 @@
+"""GPU charge-conserving zigzag deposit (tiled and flat) vs the fp64 oracle.
+
+Tolerance: max |J_gpu - J_oracle| <= 1e-5 max |J_oracle| over the whole array
+(fp32 products and atomics against fp64).  Escape counts are compared exactly
+with a classifier written here from the window's definition.  ([TD] "Halo
+sizing" for the scheme and its stencil, "How a tile deposit runs" for the tiled
+form, "Correctness is independent of the halo" for the escape valve.)
+"""
+import numpy as np
+import pytest
+import torch
+
+import particle_cell_grid_amd as pcg
+import synthetic
+from gpu_util import DEV, dev, full_workload, rel_max_err, say
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+def _J(n):
+    return torch.zeros(3, n[2], n[1], n[0], dtype=torch.float32, device=DEV)
+
+
+def _inputs(n, ppc, seed, max_step=0.95):
+    wl = synthetic.deposit_workload(3, n, ppc=ppc, w_uniform=True, seed=seed)
+    x = wl.x
+    xp = synthetic.previous_positions(x, max_step=max_step, seed=seed + 1)
+    return x, xp, wl.q, wl.w
+
+
+def _sorted(orc, n, T, key, arrays):
+    """Oracle tile sort (order 1) keyed on `key`; returns the permuted arrays
+    and the tile offsets."""
+    _, p, off = orc.tile_sort(3, n, 1, T, key)
+    p = p.astype(np.int64)
+    return [a[p] for a in arrays], off
+
+
+def _expected_escapes(n, T, D, key, x, xp):
+    """Particles whose stencil min(i1, i2) .. max(i1, i2) + 1 per axis does not
+    fit the window of TE = T + 2D + 3 nodes starting D + 1 below the origin of
+    the tile holding `key`."""
+    TE = T + 2 * D + 3
+    esc = np.zeros(x[0].size, dtype=bool)
+    for k in range(3):
+        i1 = np.floor(xp[k].astype(np.float64)).astype(np.int64)
+        i2 = np.floor(x[k].astype(np.float64)).astype(np.int64)
+        lo = np.minimum(i1, i2)
+        ext = np.maximum(i1, i2) + 1 - lo
+        ws = (np.floor(key[k].astype(np.float64)).astype(np.int64) // T) * T - D - 1
+        l0 = np.mod(lo - ws, n[k])
+        esc |= (l0 + ext >= TE) | (ext > 2)
+    return int(esc.sum())
+
+
+def _run(n, x, xp, q, w, layout=None):
+    J = _J(n)
+    esc = torch.zeros(1, dtype=torch.int64, device=DEV)
+    pcg.deposit_currents_zigzag(n, [dev(a) for a in x], [dev(a) for a in xp], dev(q), dev(w), J,
+                                layout, esc)
+    torch.cuda.synchronize()
+    return J.cpu().numpy(), int(esc.item())
+
+
+def _layout(T, D, off, n_part):
+    return pcg.Layout(T=T, order=1, tile_offsets=dev(off.view(np.int32)), n_partitioned=n_part,
+                      drift=D)
+
+
+@pytest.mark.parametrize("n,T,D", [
+    ([32, 32, 32], 8, 1),
+    ([32, 32, 32], 4, 0),
+    ([24, 16, 32], 8, 2),
+    ([16, 16, 16], 16, 1),   # the int64 window exceeds the LDS: fp32 sums
+])
+def test_tiled_matches_oracle(orc, n, T, D):
+    x, xp, q, w = _inputs(n, 3, seed=700 + T + D)
+    (x0, x1, x2, p0, p1, p2, q, w), off = _sorted(orc, n, T, x, [*x, *xp, q, w])
+    x, xp = [x0, x1, x2], [p0, p1, p2]
+    say("zigzag tiled", n, T, D, x0.size)
+    J, esc = _run(n, x, xp, q, w, _layout(T, D, off, x0.size))
+    ref = orc.deposit_zigzag(n, x, xp, q, w)
+    assert rel_max_err(J, ref) <= TOL
+    assert esc == 0  # keyed on the new positions: every move under a cell fits
+
+
+@pytest.mark.parametrize("D", [0, 1, 2])
+def test_stale_layout_escapes(orc, D):
+    """A layout keyed on positions up to 2.5 cells off for 10% of the particles:
+    those whose stencil leaves the window take the valve and are counted."""
+    n, T = [32, 32, 32], 8
+    x, xp, q, w = _inputs(n, 2, seed=720 + D)
+    key = synthetic.stale_keys(x, n, fraction=0.1, span=2.5, seed=730 + D)
+    (x0, x1, x2, p0, p1, p2, k0, k1, k2, q, w), off = _sorted(orc, n, T, key,
+                                                             [*x, *xp, *key, q, w])
+    x, xp, key = [x0, x1, x2], [p0, p1, p2], [k0, k1, k2]
+    say("zigzag stale", n, T, D, x0.size)
+    J, esc = _run(n, x, xp, q, w, _layout(T, D, off, x0.size))
+    ref = orc.deposit_zigzag(n, x, xp, q, w)
+    assert rel_max_err(J, ref) <= TOL
+    expect = _expected_escapes(n, T, D, key, x, xp)
+    assert esc == expect
+    assert expect > 0  # the valve was exercised
+
+
+def test_flat_and_tail(orc):
+    """No layout (flat kernel), and a layout over a prefix with the ragged rest
+    sent to the flat kernel."""
+    n, T = [24, 20, 16], 4
+    x, xp, q, w = _inputs(n, 2, seed=740)
+    say("zigzag flat", n, x[0].size)
+    J, esc = _run(n, x, xp, q, w)
+    ref = orc.deposit_zigzag(n, x, xp, q, w)
+    assert rel_max_err(J, ref) <= TOL and esc == 0
+    m = x[0].size - 1237
+    head, off = _sorted(orc, n, T, [a[:m] for a in x], [a[:m] for a in [*x, *xp, q, w]])
+    rest = [a[m:] for a in [*x, *xp, q, w]]
+    x0, x1, x2, p0, p1, p2, qq, ww = [np.concatenate([h, r]) for h, r in zip(head, rest)]
+    say("zigzag tail", n, T, m, x0.size)
+    J, esc = _run(n, [x0, x1, x2], [p0, p1, p2], qq, ww, _layout(T, 1, off, m))
+    assert rel_max_err(J, ref) <= TOL and esc == 0
+
+
+def test_edge_cases(orc):
+    """No particles; one particle on a 1x1x1-tile grid whose move crosses the
+    periodic boundary on every axis; particles at rest (no current)."""
+    n = [8, 8, 8]
+    e = np.zeros(0, np.float32)
+    say("zigzag empty")
+    J, esc = _run(n, [e] * 3, [e] * 3, e, e)
+    assert not J.any() and esc == 0
+    x = [np.array([0.2], np.float32)] * 3
+    xp = [np.array([-0.4], np.float32)] * 3
+    q = np.array([-1.0], np.float32)
+    w = np.array([1.25], np.float32)
+    off = np.array([0] + [1] * 8, np.uint32)   # 2x2x2 tiles of T = 4; the particle in tile 0
+    say("zigzag boundary crossing")
+    J, esc = _run(n, x, xp, q, w, _layout(4, 0, off, 1))
+    ref = orc.deposit_zigzag(n, x, xp, q, w)
+    assert rel_max_err(J, ref) <= TOL and esc == 0
+    xs, _, q2, w2 = _inputs(n, 1, seed=750)
+    say("zigzag at rest")
+    J, _ = _run(n, xs, xs, q2, w2)
+    assert not J.any()
+
+
+def test_full_size_parity(orc):
+    """3-D 128^3 with 32 per cell (the headline loading), each particle moved by
+    its velocity: the tiled launch (T = 8, drift 1) against the oracle over the
+    whole array, and the total current sum_g J_c = sum_p q w (x - x_prev)_c."""
+    wl = full_workload("cic3d_128_ppc32")
+    n, T = wl.n, 8
+    x = wl.x
+    xp = synthetic.previous_positions(x, scale_v=1.0, v=wl.v)
+    _, p, off = orc.tile_sort(3, n, 1, T, x)
+    p = p.astype(np.int64)
+    x, xp = [a[p] for a in x], [a[p] for a in xp]
+    q, w = wl.q[p], wl.w[p]
+    say("zigzag full", n, T, x[0].size)
+    J, esc = _run(n, x, xp, q, w, _layout(T, 1, off, x[0].size))
+    assert esc == 0
+    ref = orc.deposit_zigzag(n, x, xp, q, w)
+    assert rel_max_err(J, ref) <= TOL
+    qw = q.astype(np.float64) * w
+    for c in range(3):
+        tot = float((qw * (x[c].astype(np.float64) - xp[c])).sum())
+        scale = float(np.abs(qw * (x[c].astype(np.float64) - xp[c])).sum())
+        assert abs(float(J[c].astype(np.float64).sum()) - tot) <= 1e-6 * scale

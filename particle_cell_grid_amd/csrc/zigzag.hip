@@ -64,13 +64,31 @@ struct Move {
 // lie in [-1, 2) and are exact (or within an ulp of 1 for |a| < 1), so the
 // segment lengths and midpoints keep fp32's relative precision wherever the
 // particle sits on the grid.
-__device__ inline Move make_move(const ZzArgs &m, int64_t p)
+// A particle's inputs: previous and new position, charge, weight.
+struct Raw {
+    float a[3], b[3], q, w;
+};
+
+__device__ inline Raw load_raw(const ZzArgs &m, int64_t p)
 {
-    Move mv;
-    mv.qw = m.q[p] * m.w[p];
+    Raw r;
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
-        const float a = m.xp[k][p], b = m.x[k][p];
+        r.a[k] = m.xp[k][p];
+        r.b[k] = m.x[k][p];
+    }
+    r.q = m.q[p];
+    r.w = m.w[p];
+    return r;
+}
+
+__device__ inline Move make_move(const Raw &r)
+{
+    Move mv;
+    mv.qw = r.q * r.w;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const float a = r.a[k], b = r.b[k];
         const float fa = floorf(a), fb = floorf(b);
         const float flo = fminf(fa, fb);
         const float A = a - flo, B = b - flo;   // in cell units above lo
@@ -88,30 +106,42 @@ __device__ inline Move make_move(const ZzArgs &m, int64_t p)
     return mv;
 }
 
-// Calls f(c, g[3] (unwrapped node), value) for the 24 contributions.
+__device__ inline Move make_move(const ZzArgs &m, int64_t p)
+{
+    return make_move(load_raw(m, p));
+}
+
+// Calls f(c, j, g[3] (unwrapped node), value) for the 12 contributions of
+// segment s (j = d1 + 2 d2 numbers the node of component c).
+template <typename Fn>
+__device__ inline void for_each_in_segment(const Move &mv, int s, Fn &&f)
+{
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+        const int k1 = c == 0 ? 1 : 0, k2 = c == 2 ? 1 : 2;
+        const float cross = mv.F[s][k1] * mv.F[s][k2] * (1.0f / 12.0f);
+        const float fc = mv.qw * mv.F[s][c];
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+            for (int d1 = 0; d1 < 2; ++d1) {
+                const float w1 = d1 ? mv.W[s][k1] : 1.0f - mv.W[s][k1];
+                const float w2 = d2 ? mv.W[s][k2] : 1.0f - mv.W[s][k2];
+                int g[3] = {mv.cell[s][0], mv.cell[s][1], mv.cell[s][2]};
+                g[k1] += d1;
+                g[k2] += d2;
+                f(c, d1 + 2 * d2, g, fc * (w1 * w2 + (d1 == d2 ? cross : -cross)));
+            }
+    }
+}
+
+// The 24 contributions of both segments.
 template <typename Fn>
 __device__ inline void for_each_contribution(const Move &mv, Fn &&f)
 {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-        for (int c = 0; c < 3; ++c) {
-            const int k1 = c == 0 ? 1 : 0, k2 = c == 2 ? 1 : 2;
-            const float cross = mv.F[s][k1] * mv.F[s][k2] * (1.0f / 12.0f);
-            const float fc = mv.qw * mv.F[s][c];
-#pragma unroll
-            for (int d2 = 0; d2 < 2; ++d2)
-#pragma unroll
-                for (int d1 = 0; d1 < 2; ++d1) {
-                    const float w1 = d1 ? mv.W[s][k1] : 1.0f - mv.W[s][k1];
-                    const float w2 = d2 ? mv.W[s][k2] : 1.0f - mv.W[s][k2];
-                    int g[3] = {mv.cell[s][0], mv.cell[s][1], mv.cell[s][2]};
-                    g[k1] += d1;
-                    g[k2] += d2;
-                    f(c, g, fc * (w1 * w2 + (d1 == d2 ? cross : -cross)));
-                }
-        }
-    }
+    for (int s = 0; s < 2; ++s)
+        for_each_in_segment(mv, s, [&](int c, int, const int *g, float v) { f(c, g, v); });
 }
 
 __device__ inline void deposit_global(const ZzArgs &m, const Move &mv)
@@ -161,6 +191,18 @@ __device__ inline float tile_max_qw(const ZzArgs &m, int64_t lo, int64_t hi, flo
     return mx;
 }
 
+// x (|x| < 2^62, already scaled) as a two's-complement int64, rounded toward
+// -inf: x = h 2^32 + l with h = floor(x 2^-32) and 0 <= l < 2^32, where l is
+// exact in fp32 (for |x| >= 2^32 it has at most 24 significant bits; below
+// that it is x or x + 2^32, off by at most half an ulp of 2^32 there, i.e.
+// 2^-54 of the scale bound).
+__device__ inline unsigned long long to_fixed(float x)
+{
+    const float h = floorf(x * 0x1p-32f);
+    const float l = fminf(fmaf(h, -0x1p32f, x), 4294967040.0f);
+    return ((unsigned long long)(uint32_t)(int32_t)h << 32) | (uint32_t)l;
+}
+
 // One work-group per tile.  FIXED: the window holds int64 sums of the
 // contributions scaled by 2^k (exact and independent of the order of the adds;
 // LDS integer atomics run over twenty times the rate of float ones on this
@@ -169,16 +211,18 @@ __device__ inline float tile_max_qw(const ZzArgs &m, int64_t lo, int64_t hi, flo
 // to any node (two segments); with N particles in the tile every node sum stays
 // below N * 2.17 * max|q w|, and k is chosen so that this bound is below 2^62.
 // Longer moves take the valve.  Not FIXED: fp32 sums (the window in int64 does
-// not fit the LDS).
-template <bool FIXED>
+// not fit the LDS).  TEC: the window edge when fixed at compile time (0: m.TE),
+// so that every slot a segment adds to is its base plus a constant.
+template <bool FIXED, int TEC>
 __global__ __launch_bounds__(256) void k_zigzag_tiled(ZzArgs m)
 {
     using Acc = typename std::conditional<FIXED, unsigned long long, float>::type;
     extern __shared__ __align__(8) unsigned char lds_raw[];
     Acc *win = reinterpret_cast<Acc *>(lds_raw);  // [3][TE][TE][TE]
     __shared__ float red[4];
-    const int TE = m.TE;
+    const int TE = TEC ? TEC : m.TE;
     const int vol = TE * TE * TE;
+    const int stride[3] = {1, TE, TE * TE};
     const uint32_t t = blockIdx.x;
     const int tc[3] = {(int)(t % (uint32_t)m.nt[0]), (int)((t / (uint32_t)m.nt[0]) % (uint32_t)m.nt[1]),
                        (int)(t / ((uint32_t)m.nt[0] * (uint32_t)m.nt[1]))};
@@ -199,8 +243,15 @@ __global__ __launch_bounds__(256) void k_zigzag_tiled(ZzArgs m)
     }
     __syncthreads();
     uint32_t escaped = 0;
+    // the next particle's inputs are loaded while this one is deposited
+    Raw next = {};
+    if (lo + (int64_t)threadIdx.x < hi)
+        next = load_raw(m, lo + threadIdx.x);
     for (int64_t p = lo + threadIdx.x; p < hi; p += blockDim.x) {
-        const Move mv = make_move(m, p);
+        const Raw cur = next;
+        if (p + blockDim.x < hi)
+            next = load_raw(m, p + blockDim.x);
+        Move mv = make_move(cur);
         // the stencil fits if its last node lies in the window (a move over
         // more than a neighbouring cell is sent to global memory)
         int l0[3];
@@ -216,15 +267,38 @@ __global__ __launch_bounds__(256) void k_zigzag_tiled(ZzArgs m)
             ++escaped;
             continue;
         }
-        for_each_contribution(mv, [&](int c, const int *g, float v) {
-            const int lx = l0[0] + (g[0] - mv.lo[0]), ly = l0[1] + (g[1] - mv.lo[1]),
-                      lz = l0[2] + (g[2] - mv.lo[2]);
-            Acc *a = &win[c * vol + (lz * TE + ly) * TE + lx];
+        if (FIXED)
+            mv.qw = ldexpf(mv.qw, k_scale);  // every contribution comes out scaled
+        // window slot of each segment's cell corner
+        int base[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            base[s] = (l0[0] + mv.cell[s][0] - mv.lo[0]) +
+                      TE * ((l0[1] + mv.cell[s][1] - mv.lo[1]) +
+                            TE * (l0[2] + mv.cell[s][2] - mv.lo[2]));
+        auto add = [&](int s, int c, int j, float v) {
+            const int k1 = c == 0 ? 1 : 0, k2 = c == 2 ? 1 : 2;
+            Acc *a = &win[base[s] + c * vol + (j & 1) * stride[k1] + (j >> 1) * stride[k2]];
             if constexpr (FIXED)
-                atomicAdd(a, (unsigned long long)(long long)ldexpf(v, k_scale));
+                atomicAdd(a, to_fixed(v));
             else
                 atomicAdd(a, v);
+        };
+        // a move that crosses no cell boundary has both segments in one cell:
+        // their contributions to each node are summed before the add
+        const bool same = mv.cell[0][0] == mv.cell[1][0] && mv.cell[0][1] == mv.cell[1][1] &&
+                          mv.cell[0][2] == mv.cell[1][2];
+        float v1[3][4];
+        for_each_in_segment(mv, 1, [&](int c, int j, const int *, float v) { v1[c][j] = v; });
+        for_each_in_segment(mv, 0, [&](int c, int j, const int *, float v) {
+            add(0, c, j, same ? v + v1[c][j] : v);
         });
+        if (!same)
+#pragma unroll
+            for (int c = 0; c < 3; ++c)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    add(1, c, j, v1[c][j]);
     }
     __syncthreads();
     const int64_t ng = (int64_t)m.n[0] * m.n[1] * m.n[2];
@@ -329,7 +403,13 @@ extern "C" pcg_status deposit_currents_zigzag(const pcg_grid *grid, const pcg_pa
     if (!tile)
         return flat(0, count);
     if (m.n_part > 0) {
-        auto kern = fixed ? k_zigzag_tiled<true> : k_zigzag_tiled<false>;
+        // window edges of tiles 4 and 8 with drift 0 and 1 are compiled in
+        auto kern = !fixed         ? k_zigzag_tiled<false, 0>
+                    : m.TE == 7  ? k_zigzag_tiled<true, 7>
+                    : m.TE == 9  ? k_zigzag_tiled<true, 9>
+                    : m.TE == 11 ? k_zigzag_tiled<true, 11>
+                    : m.TE == 13 ? k_zigzag_tiled<true, 13>
+                                 : k_zigzag_tiled<true, 0>;
         if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)lds) != hipSuccess)
             return fail(PCG_EHIP, "%s: cannot raise dynamic LDS to %zu bytes", who, lds);

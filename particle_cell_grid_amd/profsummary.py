@@ -66,6 +66,9 @@ def tap_name(kernel):
         return "mass_tsc_mfma" if last == "true" else "mass_tsc_valu"
     if base == "k_mass_tsc_tensor_group":
         return "mass_tsc_tensor_mfma" if last == "true" else "mass_tsc_tensor_valu"
+    if base == "k_zigzag_tiled":
+        # <fixed point, window edge>
+        return "zigzag_tiled" if targs and targs[0].strip() == "true" else "zigzag_tiled_f32"
     if base in ("k_mass_tsc_flat", "k_mass_tsc_tensor_flat"):
         return base[2:]
     if base.startswith("k_mass_") and targs:

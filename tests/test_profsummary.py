@@ -28,6 +28,9 @@ from particle_cell_grid_amd import profsummary as ps
     ("k_mass_tsc_tensor_flat", "mass_tsc_tensor_flat"),
     ("k_sweep1d", "sweep1d"),
     ("k_sweep1d_grad<true>", "sweep1d_grad"),
+    ("k_zigzag_tiled<true, 13>", "zigzag_tiled"),
+    ("k_zigzag_tiled<false, 0>", "zigzag_tiled_f32"),
+    ("k_zigzag_flat", "zigzag_flat"),
 ])
 def test_tap_names(symbol, name):
     assert ps.tap_name(symbol) == name

@@ -173,22 +173,31 @@ __device__ inline int64_t window_coord(int lo, int ws, int n)
     return d;
 }
 
-// The largest |q w| of the tile's particles (the fixed-point scale's bound).
-__device__ inline float tile_max_qw(const ZzArgs &m, int64_t lo, int64_t hi, float *red)
+// The largest of the work-group's values v (one per thread).  Ends with a
+// barrier, so red may be written again afterwards.
+__device__ inline float block_max(float v, float *red)
 {
-    float mx = 0.0f;
-    for (int64_t p = lo + threadIdx.x; p < hi; p += blockDim.x)
-        mx = fmaxf(mx, fabsf(m.q[p] * m.w[p]));
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1)
-        mx = fmaxf(mx, __shfl_xor(mx, off));
+        v = fmaxf(v, __shfl_xor(v, off));
     if ((threadIdx.x & 63) == 0)
-        red[threadIdx.x >> 6] = mx;
+        red[threadIdx.x >> 6] = v;
     __syncthreads();
-    mx = red[0];
+    v = red[0];
     for (int i = 1; i < (int)(blockDim.x >> 6); ++i)
-        mx = fmaxf(mx, red[i]);
-    return mx;
+        v = fmaxf(v, red[i]);
+    __syncthreads();
+    return v;
+}
+
+// The int64 scale exponent k for a tile of n particles whose |q w| is at most
+// qmax: 2^k n 2.17 qmax < 2^62.
+__device__ inline int fixed_scale(int64_t n, float qmax)
+{
+    const float bound = (float)n * 2.17f * qmax;
+    int e = 0;
+    frexpf(bound, &e);  // bound < 2^e
+    return bound > 0.0f ? 62 - e : 0;
 }
 
 // x (|x| < 2^62, already scaled) as a two's-complement int64, rounded toward
@@ -210,9 +219,13 @@ __device__ inline unsigned long long to_fixed(float x)
 // has |F'| <= 1 and 0 <= w <= 1 per segment, so it adds at most 2 (13/12) |q w|
 // to any node (two segments); with N particles in the tile every node sum stays
 // below N * 2.17 * max|q w|, and k is chosen so that this bound is below 2^62.
-// Longer moves take the valve.  Not FIXED: fp32 sums (the window in int64 does
-// not fit the LDS).  TEC: the window edge when fixed at compile time (0: m.TE),
-// so that every slot a segment adds to is its base plus a constant.
+// max|q w| is taken as twice the largest of the first particle of every
+// thread, and checked after the pass against every particle seen; a tile that
+// breaks it is cleared and deposited again with its true maximum (escapes,
+// already deposited, are skipped then).  Longer moves take the valve.  Not
+// FIXED: fp32 sums (the window in int64 does not fit the LDS).  TEC: the
+// window edge when fixed at compile time (0: m.TE), so that every slot a
+// segment adds to is its base plus a constant.
 template <bool FIXED, int TEC>
 __global__ __launch_bounds__(256) void k_zigzag_tiled(ZzArgs m)
 {
@@ -230,77 +243,102 @@ __global__ __launch_bounds__(256) void k_zigzag_tiled(ZzArgs m)
 #pragma unroll
     for (int k = 0; k < 3; ++k)
         ws[k] = tc[k] * m.T - m.D - 1;
-    for (int i = threadIdx.x; i < 3 * vol; i += blockDim.x)
-        win[i] = 0;
     const int64_t lo = std::min<int64_t>(m.offsets[t], m.n_part);
     const int64_t hi = std::max<int64_t>(lo, std::min<int64_t>(m.offsets[t + 1], m.n_part));
-    int k_scale = 0;
-    if (FIXED) {
-        const float bound = (float)(hi - lo) * 2.17f * tile_max_qw(m, lo, hi, red);
-        int e = 0;
-        frexpf(bound, &e);  // bound < 2^e
-        k_scale = bound > 0.0f ? 62 - e : 0;
-    }
-    __syncthreads();
     uint32_t escaped = 0;
-    // the next particle's inputs are loaded while this one is deposited
-    Raw next = {};
-    if (lo + (int64_t)threadIdx.x < hi)
-        next = load_raw(m, lo + threadIdx.x);
-    for (int64_t p = lo + threadIdx.x; p < hi; p += blockDim.x) {
-        const Raw cur = next;
-        if (p + blockDim.x < hi)
-            next = load_raw(m, p + blockDim.x);
-        Move mv = make_move(cur);
-        // the stencil fits if its last node lies in the window (a move over
-        // more than a neighbouring cell is sent to global memory)
-        int l0[3];
-        bool fits = true;
+
+    // one pass over the tile's particles at scale 2^k_scale; returns the
+    // largest |q w| this thread saw
+    auto deposit_pass = [&](int k_scale, bool first) -> float {
+        for (int i = threadIdx.x; i < 3 * vol; i += blockDim.x)
+            win[i] = 0;
+        __syncthreads();
+        float seen = 0.0f;
+        // the next particle's inputs are loaded while this one is deposited
+        Raw next = {};
+        if (lo + (int64_t)threadIdx.x < hi)
+            next = load_raw(m, lo + threadIdx.x);
+        for (int64_t p = lo + threadIdx.x; p < hi; p += blockDim.x) {
+            const Raw cur = next;
+            if (p + blockDim.x < hi)
+                next = load_raw(m, p + blockDim.x);
+            Move mv = make_move(cur);
+            seen = fmaxf(seen, fabsf(mv.qw));
+            // the stencil fits if its last node lies in the window (a move over
+            // more than a neighbouring cell is sent to global memory)
+            int l0[3];
+            bool fits = true;
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            const int64_t d = window_coord(mv.lo[k], ws[k], m.n[k]);
-            l0[k] = (int)d;
-            fits = fits && d >= 0 && mv.ext[k] >= 1 && mv.ext[k] <= 2 && d + mv.ext[k] < TE;
+            for (int k = 0; k < 3; ++k) {
+                const int64_t d = window_coord(mv.lo[k], ws[k], m.n[k]);
+                l0[k] = (int)d;
+                fits = fits && d >= 0 && mv.ext[k] >= 1 && mv.ext[k] <= 2 && d + mv.ext[k] < TE;
+            }
+            if (!fits) {
+                if (first) {
+                    deposit_global(m, mv);
+                    ++escaped;
+                }
+                continue;
+            }
+            if (FIXED)
+                mv.qw = ldexpf(mv.qw, k_scale);  // every contribution comes out scaled
+            // window slot of each segment's cell corner
+            int base[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                base[s] = (l0[0] + mv.cell[s][0] - mv.lo[0]) +
+                          TE * ((l0[1] + mv.cell[s][1] - mv.lo[1]) +
+                                TE * (l0[2] + mv.cell[s][2] - mv.lo[2]));
+            auto add = [&](int s, int c, int j, float v) {
+                const int k1 = c == 0 ? 1 : 0, k2 = c == 2 ? 1 : 2;
+                Acc *a = &win[base[s] + c * vol + (j & 1) * stride[k1] + (j >> 1) * stride[k2]];
+                if constexpr (FIXED)
+                    atomicAdd(a, to_fixed(v));
+                else
+                    atomicAdd(a, v);
+            };
+            // a move that crosses no cell boundary has both segments in one
+            // cell: their contributions to each node are summed before the add
+            const bool same = mv.cell[0][0] == mv.cell[1][0] && mv.cell[0][1] == mv.cell[1][1] &&
+                              mv.cell[0][2] == mv.cell[1][2];
+            float v1[3][4];
+            for_each_in_segment(mv, 1, [&](int c, int j, const int *, float v) { v1[c][j] = v; });
+            for_each_in_segment(mv, 0, [&](int c, int j, const int *, float v) {
+                add(0, c, j, same ? v + v1[c][j] : v);
+            });
+            if (!same)
+#pragma unroll
+                for (int c = 0; c < 3; ++c)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        add(1, c, j, v1[c][j]);
         }
-        if (!fits) {
-            deposit_global(m, mv);
-            ++escaped;
-            continue;
-        }
-        if (FIXED)
-            mv.qw = ldexpf(mv.qw, k_scale);  // every contribution comes out scaled
-        // window slot of each segment's cell corner
-        int base[2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-            base[s] = (l0[0] + mv.cell[s][0] - mv.lo[0]) +
-                      TE * ((l0[1] + mv.cell[s][1] - mv.lo[1]) +
-                            TE * (l0[2] + mv.cell[s][2] - mv.lo[2]));
-        auto add = [&](int s, int c, int j, float v) {
-            const int k1 = c == 0 ? 1 : 0, k2 = c == 2 ? 1 : 2;
-            Acc *a = &win[base[s] + c * vol + (j & 1) * stride[k1] + (j >> 1) * stride[k2]];
-            if constexpr (FIXED)
-                atomicAdd(a, to_fixed(v));
-            else
-                atomicAdd(a, v);
-        };
-        // a move that crosses no cell boundary has both segments in one cell:
-        // their contributions to each node are summed before the add
-        const bool same = mv.cell[0][0] == mv.cell[1][0] && mv.cell[0][1] == mv.cell[1][1] &&
-                          mv.cell[0][2] == mv.cell[1][2];
-        float v1[3][4];
-        for_each_in_segment(mv, 1, [&](int c, int j, const int *, float v) { v1[c][j] = v; });
-        for_each_in_segment(mv, 0, [&](int c, int j, const int *, float v) {
-            add(0, c, j, same ? v + v1[c][j] : v);
-        });
-        if (!same)
-#pragma unroll
-            for (int c = 0; c < 3; ++c)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    add(1, c, j, v1[c][j]);
+        __syncthreads();
+        return seen;
+    };
+
+    int k_scale = 0;
+    float assumed = 0.0f;
+    if (FIXED) {
+        float first_qw = 0.0f;
+        if (lo + (int64_t)threadIdx.x < hi)
+            first_qw = fabsf(m.q[lo + threadIdx.x] * m.w[lo + threadIdx.x]);
+        assumed = 2.0f * block_max(first_qw, red);
+        k_scale = fixed_scale(hi - lo, assumed);
     }
-    __syncthreads();
+    // at most two passes: the second runs with the true maximum, which holds
+    for (bool first = true;; first = false) {
+        const float seen_here = deposit_pass(k_scale, first);
+        if (!FIXED)
+            break;
+        const float seen = block_max(seen_here, red);
+        if (!first || seen <= assumed)
+            break;
+        assumed = seen;  // the bound may not have held: deposit again
+        k_scale = fixed_scale(hi - lo, seen);
+    }
+
     const int64_t ng = (int64_t)m.n[0] * m.n[1] * m.n[2];
     for (int i = threadIdx.x; i < 3 * vol; i += blockDim.x) {
         const Acc a = win[i];

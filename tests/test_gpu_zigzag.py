@@ -104,6 +104,33 @@ def test_stale_layout_escapes(orc, D):
     assert expect > 0  # the valve was exercised
 
 
+@pytest.mark.parametrize("heavy_w", [40.0, 1e5])
+def test_scale_redo_with_escapes(orc, heavy_w):
+    """The fixed-point scale comes from the first particle of each thread; a
+    tile holding a later particle with |q w| above twice that is deposited
+    again at its true maximum.  One heavy particle per tile past its first 256,
+    on a stale layout so that the same tiles also send particles to the valve
+    (which the second pass must not deposit or count again).  At w = 40 a
+    window not cleared or an escape deposited twice shows at 1e-3 or more; at
+    w = 1e5 the first scale would overflow int64 had the tile not been redone."""
+    n, T, D = [16, 16, 16], 8, 1
+    x, xp, q, w = _inputs(n, 4, seed=760)
+    key = synthetic.stale_keys(x, n, fraction=0.1, span=2.5, seed=761)
+    (x0, x1, x2, p0, p1, p2, k0, k1, k2, q, w), off = _sorted(orc, n, T, key,
+                                                             [*x, *xp, *key, q, w])
+    x, xp, key = [x0, x1, x2], [p0, p1, p2], [k0, k1, k2]
+    w = np.full_like(w, 0.5)
+    heavy = [int(off[t]) + 300 for t in range(off.size - 1) if off[t + 1] - off[t] > 300]
+    assert len(heavy) == off.size - 1
+    w[heavy] = heavy_w
+    say("zigzag scale redo", n, T, D, x0.size)
+    J, esc = _run(n, x, xp, q, w, _layout(T, D, off, x0.size))
+    ref = orc.deposit_zigzag(n, x, xp, q, w)
+    assert rel_max_err(J, ref) <= TOL
+    expect = _expected_escapes(n, T, D, key, x, xp)
+    assert esc == expect and expect > 0
+
+
 def test_flat_and_tail(orc):
     """No layout (flat kernel), and a layout over a prefix with the ragged rest
     sent to the flat kernel."""

@@ -190,26 +190,21 @@ __device__ inline float block_max(float v, float *red)
     return v;
 }
 
-// The int64 scale exponent k for a tile of n particles whose |q w| is at most
-// qmax: 2^k n 2.17 qmax < 2^62.
-__device__ inline int fixed_scale(int64_t n, float qmax)
+// The fixed-point scale exponent k for particles whose |q w| is at most qmax:
+// 2^k 2.17 qmax < 2^31, so every scaled contribution fits an int32.
+__device__ inline int fixed_scale(float qmax)
 {
-    const float bound = (float)n * 2.17f * qmax;
+    const float bound = 2.17f * qmax;
     int e = 0;
     frexpf(bound, &e);  // bound < 2^e
-    return bound > 0.0f ? 62 - e : 0;
+    return bound > 0.0f ? 31 - e : 0;
 }
 
-// x (|x| < 2^62, already scaled) as a two's-complement int64, rounded toward
-// -inf: x = h 2^32 + l with h = floor(x 2^-32) and 0 <= l < 2^32, where l is
-// exact in fp32 (for |x| >= 2^32 it has at most 24 significant bits; below
-// that it is x or x + 2^32, off by at most half an ulp of 2^32 there, i.e.
-// 2^-54 of the scale bound).
+// x (|x| < 2^31, already scaled) as a two's-complement int64, rounded toward
+// zero (an error below one unit of 2^-k, some 5e-10 of max|q w|).
 __device__ inline unsigned long long to_fixed(float x)
 {
-    const float h = floorf(x * 0x1p-32f);
-    const float l = fminf(fmaf(h, -0x1p32f, x), 4294967040.0f);
-    return ((unsigned long long)(uint32_t)(int32_t)h << 32) | (uint32_t)l;
+    return (unsigned long long)(long long)(int32_t)x;
 }
 
 // One work-group per tile.  FIXED: the window holds int64 sums of the
@@ -217,9 +212,9 @@ __device__ inline unsigned long long to_fixed(float x)
 // LDS integer atomics run over twenty times the rate of float ones on this
 // chip).  A particle whose move stays within neighbouring cells on every axis
 // has |F'| <= 1 and 0 <= w <= 1 per segment, so it adds at most 2 (13/12) |q w|
-// to any node (two segments); with N particles in the tile every node sum stays
-// below N * 2.17 * max|q w|, and k is chosen so that this bound is below 2^62.
-// max|q w| is taken as twice the largest of the first particle of every
+// to any node (both segments, summed before the add); k is chosen so that this
+// bound, scaled, is below 2^31.  Each add then converts one int32, and a node
+// sum of fewer than 2^31 particles' adds stays below 2^62.  max|q w| is taken as twice the largest of the first particle of every
 // thread, and checked after the pass against every particle seen; a tile that
 // breaks it is cleared and deposited again with its true maximum (escapes,
 // already deposited, are skipped then).  Longer moves take the valve.  Not
@@ -227,12 +222,12 @@ __device__ inline unsigned long long to_fixed(float x)
 // window edge when fixed at compile time (0: m.TE), so that every slot a
 // segment adds to is its base plus a constant.
 template <bool FIXED, int TEC>
-__global__ __launch_bounds__(256) void k_zigzag_tiled(ZzArgs m)
+__global__ __launch_bounds__(512) void k_zigzag_tiled(ZzArgs m)
 {
     using Acc = typename std::conditional<FIXED, unsigned long long, float>::type;
     extern __shared__ __align__(8) unsigned char lds_raw[];
     Acc *win = reinterpret_cast<Acc *>(lds_raw);  // [3][TE][TE][TE]
-    __shared__ float red[4];
+    __shared__ float red[8];  // one per wave
     const int TE = TEC ? TEC : m.TE;
     const int vol = TE * TE * TE;
     const int stride[3] = {1, TE, TE * TE};
@@ -325,7 +320,7 @@ __global__ __launch_bounds__(256) void k_zigzag_tiled(ZzArgs m)
         if (lo + (int64_t)threadIdx.x < hi)
             first_qw = fabsf(m.q[lo + threadIdx.x] * m.w[lo + threadIdx.x]);
         assumed = 2.0f * block_max(first_qw, red);
-        k_scale = fixed_scale(hi - lo, assumed);
+        k_scale = fixed_scale(assumed);
     }
     // at most two passes: the second runs with the true maximum, which holds
     for (bool first = true;; first = false) {
@@ -336,7 +331,7 @@ __global__ __launch_bounds__(256) void k_zigzag_tiled(ZzArgs m)
         if (!first || seen <= assumed)
             break;
         assumed = seen;  // the bound may not have held: deposit again
-        k_scale = fixed_scale(hi - lo, seen);
+        k_scale = fixed_scale(seen);
     }
 
     const int64_t ng = (int64_t)m.n[0] * m.n[1] * m.n[2];
@@ -424,6 +419,9 @@ extern "C" pcg_status deposit_currents_zigzag(const pcg_grid *grid, const pcg_pa
                         who, lds, tile->T, tile->drift);
         for (int k = 0; k < 3; ++k)
             m.nt[k] = grid->n[k] / tile->T;
+        if ((int64_t)m.nt[0] * m.nt[1] * m.nt[2] >= (int64_t(1) << 31))
+            return fail(PCG_EINVAL, "%s: %lld tiles exceed one launch", who,
+                        (long long)m.nt[0] * m.nt[1] * m.nt[2]);
         m.offsets = tile->tile_offsets;
         m.n_part = tile->n_partitioned;
     }
@@ -452,8 +450,10 @@ extern "C" pcg_status deposit_currents_zigzag(const pcg_grid *grid, const pcg_pa
                                 (int)lds) != hipSuccess)
             return fail(PCG_EHIP, "%s: cannot raise dynamic LDS to %zu bytes", who, lds);
         const int64_t ntiles = (int64_t)m.nt[0] * m.nt[1] * m.nt[2];
+        // a window that leaves room for few work-groups per CU gets wider ones
+        const unsigned block = lds > 32 * 1024 ? 512 : 256;
         PCG_TRY(launch(fixed ? "zigzag_tiled" : "zigzag_tiled_f32", kern, dim3((unsigned)ntiles),
-                       dim3(256), lds, st, m));
+                       dim3(block), lds, st, m));
     }
     return flat(tile->n_partitioned, count);
 }

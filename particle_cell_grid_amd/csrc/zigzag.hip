@@ -116,21 +116,26 @@ __device__ inline Move make_move(const ZzArgs &m, int64_t p)
 template <typename Fn>
 __device__ inline void for_each_in_segment(const Move &mv, int s, Fn &&f)
 {
+    // value = (F_c w1) w2 +/- F_c cross: one FMA per contribution
+    float wm[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+        wm[k] = 1.0f - mv.W[s][k];
 #pragma unroll
     for (int c = 0; c < 3; ++c) {
         const int k1 = c == 0 ? 1 : 0, k2 = c == 2 ? 1 : 2;
-        const float cross = mv.F[s][k1] * mv.F[s][k2] * (1.0f / 12.0f);
         const float fc = mv.qw * mv.F[s][c];
+        const float fx = fc * (mv.F[s][k1] * mv.F[s][k2] * (1.0f / 12.0f));
+        const float a[2] = {fc * wm[k1], fc * mv.W[s][k1]};
 #pragma unroll
         for (int d2 = 0; d2 < 2; ++d2)
 #pragma unroll
             for (int d1 = 0; d1 < 2; ++d1) {
-                const float w1 = d1 ? mv.W[s][k1] : 1.0f - mv.W[s][k1];
-                const float w2 = d2 ? mv.W[s][k2] : 1.0f - mv.W[s][k2];
                 int g[3] = {mv.cell[s][0], mv.cell[s][1], mv.cell[s][2]};
                 g[k1] += d1;
                 g[k2] += d2;
-                f(c, d1 + 2 * d2, g, fc * (w1 * w2 + (d1 == d2 ? cross : -cross)));
+                f(c, d1 + 2 * d2, g,
+                  fmaf(a[d1], d2 ? mv.W[s][k2] : wm[k2], d1 == d2 ? fx : -fx));
             }
     }
 }

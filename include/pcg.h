@@ -220,8 +220,9 @@ pcg_status deposit_currents_regroup(const pcg_grid *grid, const pcg_particles *p
  *   nodes per axis starting drift + 1 nodes below the tile origin ([TD] "How a
  *   tile deposit runs") and adds it to J with one atomic per non-zero node.
  *   The window holds exact int64 fixed-point sums, scaled per tile from its
- *   particle count and largest |q w| so that no sum can overflow, or fp32
- *   sums when 3*TE^3*8 bytes exceed the LDS.  A particle whose stencil does
+ *   largest |q w| so that every add fits an int32 and no sum can overflow (a
+ *   tile is deposited a second time if its first estimate proves low), or
+ *   fp32 sums when 3*TE^3*8 bytes exceed the LDS.  A particle whose stencil does
  *   not fit (its layout is more than `drift` cells stale, or it crossed more
  *   than one cell boundary on an axis) takes the escape valve to global
  *   atomics and is counted.  The tail [n_partitioned, count) and tile == NULL

@@ -588,6 +588,7 @@ __global__ __launch_bounds__(256) void k_inc_tiles(IncGeom a, uint32_t *__restri
 // slot from the wave's running slot per direction (stable), then every array
 // moved.
 constexpr int MOVE_WAVES = 4;
+constexpr int MOVE_GROUP = 8;  // arrays whose loads the move issues together
 
 template <int DIM, int ORDER, int EPT>
 __global__ __launch_bounds__(MOVE_WAVES * WAVE) void k_inc_move(
@@ -642,15 +643,24 @@ __global__ __launch_bounds__(MOVE_WAVES * WAVE) void k_inc_move(
                 if (ok[e])
                     perm[pos[e]] = p[e];
         }
-        for (int k = 0; k < arr.n; ++k) {
-            float v[EPT];
+        // up to MOVE_GROUP arrays are loaded before any is stored, so that
+        // their loads are in flight together (a store may alias a later load,
+        // which would otherwise keep each array's round trip apart)
+        for (int k0 = 0; k0 < arr.n; k0 += MOVE_GROUP) {
+            float v[MOVE_GROUP][EPT];
 #pragma unroll
-            for (int e = 0; e < EPT; ++e)
-                v[e] = arr.in[k][pc[e]];
+            for (int j = 0; j < MOVE_GROUP; ++j)
+                if (k0 + j < arr.n)
 #pragma unroll
-            for (int e = 0; e < EPT; ++e)
-                if (ok[e])
-                    arr.out[k][pos[e]] = v[e];
+                    for (int e = 0; e < EPT; ++e)
+                        v[j][e] = arr.in[k0 + j][pc[e]];
+#pragma unroll
+            for (int j = 0; j < MOVE_GROUP; ++j)
+                if (k0 + j < arr.n)
+#pragma unroll
+                    for (int e = 0; e < EPT; ++e)
+                        if (ok[e])
+                            arr.out[k0 + j][pos[e]] = v[j][e];
         }
     }
 }

@@ -60,6 +60,8 @@ def parse():
                              "sweep1d_grad_1e7", "zigzag3d_128_ppc32"])
     ap.add_argument("--tile", type=int, default=0, help="tile edge T (0 = the workload's)")
     ap.add_argument("--block", type=int, default=0)
+    ap.add_argument("--drift", type=int, default=-1,
+                    help="zigzag workload: the layout's drift D (-1 = the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -330,8 +332,10 @@ def bench_zigzag(args, torch, pcg):
 
     import synthetic
 
+    # every move is under a cell and the layout is keyed on one end of it, so
+    # the window needs no drift
     T = args.tile or 8
-    D = 1
+    D = args.drift if args.drift >= 0 else 0
     progress("generating cic3d_128_ppc32 (zigzag moves)")
     wl = synthetic.workload("cic3d_128_ppc32")
     n, cnt = wl.n, wl.count

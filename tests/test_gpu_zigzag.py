@@ -172,20 +172,26 @@ def test_edge_cases(orc):
     assert not J.any()
 
 
-def test_full_size_parity(orc):
+@pytest.mark.parametrize("D", [0, 1])
+def test_full_size_parity(orc, D):
     """3-D 128^3 with 32 per cell (the headline loading), each particle moved by
-    its velocity: the tiled launch (T = 8, drift 1) against the oracle over the
-    whole array, and the total current sum_g J_c = sum_p q w (x - x_prev)_c."""
+    its velocity: the tiled launch (T = 8; drift 0 as benchmarked, and 1)
+    against the oracle over the whole array, and the total current
+    sum_g J_c = sum_p q w (x - x_prev)_c."""
     wl = full_workload("cic3d_128_ppc32")
     n, T = wl.n, 8
     x = wl.x
     xp = synthetic.previous_positions(x, scale_v=1.0, v=wl.v)
-    _, p, off = orc.tile_sort(3, n, 1, T, x)
+    # grouped by the previous positions (wrapped into the grid), as a step
+    # finds them after the last sort
+    key = [np.mod(a, np.float32(n[k])).astype(np.float32) for k, a in enumerate(xp)]
+    key = [np.where(a >= n[k], np.float32(0), a) for k, a in enumerate(key)]
+    _, p, off = orc.tile_sort(3, n, 1, T, key)
     p = p.astype(np.int64)
     x, xp = [a[p] for a in x], [a[p] for a in xp]
     q, w = wl.q[p], wl.w[p]
-    say("zigzag full", n, T, x[0].size)
-    J, esc = _run(n, x, xp, q, w, _layout(T, 1, off, x[0].size))
+    say("zigzag full", n, T, D, x[0].size)
+    J, esc = _run(n, x, xp, q, w, _layout(T, D, off, x[0].size))
     assert esc == 0
     ref = orc.deposit_zigzag(n, x, xp, q, w)
     assert rel_max_err(J, ref) <= TOL

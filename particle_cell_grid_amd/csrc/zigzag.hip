@@ -13,12 +13,13 @@
 // sits at g + e_c / 2, so that the CIC charge density obeys the discrete
 // continuity equation to round-off.  24 contributions per particle.
 //
-// Tiled: one work-group per tile of a layout keyed on the new position (the
-// order-1 tile sort); its LDS window per axis starts D + 1 nodes below the
-// tile origin and spans TE = T + 2 D + 3 nodes, which holds every stencil of a
-// particle that moved at most D cells since the layout was made.  Others take
-// the escape valve (global atomics, counted).  The window is added to J with
-// one atomic per non-zero node.
+// Tiled: one work-group per tile of a layout keyed on either end of the move
+// (the order-1 tile sort); its LDS window per axis starts D + 1 nodes below
+// the tile origin and spans TE = T + 2 D + 3 nodes, which holds the stencil
+// min(i1, i2) .. max(i1, i2) + 1 of every particle whose layout is at most D
+// cells stale and whose move stays within neighbouring cells.  Others take the
+// escape valve (global atomics, counted).  The window is added to J with one
+// atomic per non-zero slot.
 #include <algorithm>
 #include <type_traits>
 
@@ -60,10 +61,6 @@ struct Move {
     int64_t ext[3];  // max(i1, i2) + 1 - lo: its last node (2 for a move under a cell)
 };
 
-// Positions are taken relative to lo = min(i1, i2) first: a - lo and b - lo
-// lie in [-1, 2) and are exact (or within an ulp of 1 for |a| < 1), so the
-// segment lengths and midpoints keep fp32's relative precision wherever the
-// particle sits on the grid.
 // A particle's inputs: previous and new position, charge, weight.
 struct Raw {
     float a[3], b[3], q, w;
@@ -82,6 +79,10 @@ __device__ inline Raw load_raw(const ZzArgs &m, int64_t p)
     return r;
 }
 
+// Positions are taken relative to lo = min(i1, i2) first: a - lo and b - lo
+// lie in [0, 2) for a move within neighbouring cells and are exact (or within
+// an ulp of 1 for |a| < 1), so the segment lengths and midpoints keep fp32's
+// relative precision wherever the particle sits on the grid.
 __device__ inline Move make_move(const Raw &r)
 {
     Move mv;
@@ -219,10 +220,11 @@ __device__ inline unsigned long long to_fixed(float x)
 // has |F'| <= 1 and 0 <= w <= 1 per segment, so it adds at most 2 (13/12) |q w|
 // to any node (both segments, summed before the add); k is chosen so that this
 // bound, scaled, is below 2^31.  Each add then converts one int32, and a node
-// sum of fewer than 2^31 particles' adds stays below 2^62.  max|q w| is taken as twice the largest of the first particle of every
-// thread, and checked after the pass against every particle seen; a tile that
-// breaks it is cleared and deposited again with its true maximum (escapes,
-// already deposited, are skipped then).  Longer moves take the valve.  Not
+// sum of fewer than 2^31 particles' adds stays below 2^62.  max|q w| is taken
+// as twice the largest of the first particle of every thread, and checked
+// after the pass against every particle seen; a tile that breaks it is cleared
+// and deposited again with its true maximum (escapes, already deposited, are
+// skipped then).  Longer moves take the valve.  Not
 // FIXED: fp32 sums (the window in int64 does not fit the LDS).  TEC: the
 // window edge when fixed at compile time (0: m.TE), so that every slot a
 // segment adds to is its base plus a constant.
@@ -412,9 +414,13 @@ extern "C" pcg_status deposit_currents_zigzag(const pcg_grid *grid, const pcg_pa
                             grid->n[k], tile->T);
         if (tile->n_partitioned < 0 || tile->n_partitioned > count)
             return fail(PCG_EINVAL, "%s: n_partitioned outside [0, count]", who);
+        const int64_t te = (int64_t)tile->T + 2 * (int64_t)tile->drift + 3;
+        if (te > 64)  // 3 * 64^3 fp32 sums already exceed the LDS
+            return fail(PCG_ELDS, "%s: window edge %lld exceeds the LDS (T = %d, D = %d)", who,
+                        (long long)te, tile->T, tile->drift);
         m.T = tile->T;
         m.D = tile->drift;
-        m.TE = tile->T + 2 * tile->drift + 3;
+        m.TE = (int)te;
         lds = (size_t)3 * m.TE * m.TE * m.TE * sizeof(unsigned long long);
         fixed = lds <= ZZ_LDS_MAX;
         if (!fixed)

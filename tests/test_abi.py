@@ -171,6 +171,7 @@ def test_zigzag_validation(lib):
     assert call(g, tile=Tile(8, 1, 1, 0, 1001, FAKE)) == EINVAL  # n_partitioned > count
     assert call(g, tile=Tile(8, 1, 1, 0, 1000, None)) == EINVAL  # no offsets
     assert call(g, tile=Tile(16, 1, 8, 0, 1000, FAKE)) == ELDS   # TE = 35: 35^3*12 B > 160 KiB
+    assert call(g, tile=Tile(8, 1, 1 << 30, 0, 1000, FAKE)) == ELDS  # T + 2D + 3 overflows int
     big = grid(3, [2048, 2048, 2048])
     assert call(big, tile=Tile(1, 1, 1, 0, 1000, FAKE)) == EINVAL  # 2^33 tiles: one launch
     # no particles: nothing to check beyond the grid, nothing launched

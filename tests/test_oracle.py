@@ -855,3 +855,23 @@ def test_zigzag_single_particle(orc):
         for gy in (3, 4):
             exp[0, gz, gy, 2] = 0.125
     assert np.array_equal(J, exp)
+
+
+def test_zigzag_single_particle_bound(orc):
+    """A move of less than a cell puts at most 2 * 13/12 |q w| on any one J value
+    (two segments, each |F'| <= 1 with weights in [0, 1] and the cross term at
+    most 1/12): the bound the tiled kernel's fixed-point scale rests on.  Moves
+    that reach the edge of the bound's assumptions (near a whole cell, across
+    the periodic boundary) are included."""
+    r = np.random.default_rng(53)
+    n = [6, 6, 6]
+    worst = 0.0
+    for _ in range(300):
+        x = [np.float32([r.uniform(0, n[k])]) for k in range(3)]
+        d = r.choice([-0.999, 0.999], 3) * r.uniform(0.5, 1.0, 3)
+        xp = [(x[k] - np.float32(d[k])).astype(np.float32) for k in range(3)]
+        qw = r.uniform(0.5, 1.5)
+        J = orc.deposit_zigzag(n, x, xp, np.float32([1.0]), np.float32([qw]))
+        worst = max(worst, float(np.abs(J).max()) / float(np.float32(qw)))
+    assert worst <= 2.0 * 13.0 / 12.0
+    assert worst > 0.5  # long moves do come near it

@@ -951,10 +951,11 @@ pcg_status incremental_launch(const IncGeom &a, const float *const key_x[3], uin
     PCG_TRY(exclusive_scan(tile_offsets, (size_t)a.ntiles + 1, b.partial, Gate{b.flag, 0u}, st));
     if (hook)
         return hook->launch(hook->ctx, a, tile_offsets, nwork, arr, st);
-    // 4 x 64 particles per step of a wave's walk through its chunk; where
+    // 8 x 64 particles per step of a wave's walk through its chunk (eight
+    // arrays of them in flight at once; four per step ran 10% slower); where
     // chunks are small, several chunks per wave
     if (a.count / std::max<int64_t>(1, a.ntiles) >= (int64_t)INC_CHUNK)
-        PCG_TRY(launch("sort_inc_move", k_inc_move<DIM, ORDER, 4>,
+        PCG_TRY(launch("sort_inc_move", k_inc_move<DIM, ORDER, 8>,
                        dim3((nwork + MOVE_WAVES - 1) / MOVE_WAVES), dim3(MOVE_WAVES * WAVE), 0, st,
                        a, (const uint32_t *)tile_offsets, key_x[0], x1, x2, arr, perm, keys,
                        nwork));

@@ -83,10 +83,20 @@ __device__ inline Raw load_raw(const ZzArgs &m, int64_t p)
 // lie in [0, 2) for a move within neighbouring cells and are exact (or within
 // an ulp of 1 for |a| < 1), so the segment lengths and midpoints keep fp32's
 // relative precision wherever the particle sits on the grid.
+// WHOLE: a move that crosses no cell boundary is one segment (the relay point
+// at its end, the second segment empty).  The exact current of a straight
+// path is additive along it, so this is the sum of the two halves the split
+// at the midpoint would give, in one set of adds.
+template <bool WHOLE = false>
 __device__ inline Move make_move(const Raw &r)
 {
     Move mv;
     mv.qw = r.q * r.w;
+    bool same = true;
+    if (WHOLE)
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            same = same && floorf(r.a[k]) == floorf(r.b[k]);
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
         const float a = r.a[k], b = r.b[k];
@@ -94,7 +104,8 @@ __device__ inline Move make_move(const Raw &r)
         const float flo = fminf(fa, fb);
         const float A = a - flo, B = b - flo;   // in cell units above lo
         const float ca = fa - flo, cb = fb - flo;  // 0 or 1 (or more for a long move)
-        const float xr = fminf(1.0f, fmaxf(fmaxf(ca, cb), 0.5f * (A + B)));
+        const float relay = fminf(1.0f, fmaxf(fmaxf(ca, cb), 0.5f * (A + B)));
+        const float xr = WHOLE && same ? B : relay;
         mv.cell[0][k] = (int)fa;
         mv.cell[1][k] = (int)fb;
         mv.F[0][k] = xr - A;
@@ -264,7 +275,7 @@ __global__ __launch_bounds__(512) void k_zigzag_tiled(ZzArgs m)
             const Raw cur = next;
             if (p + blockDim.x < hi)
                 next = load_raw(m, p + blockDim.x);
-            Move mv = make_move(cur);
+            Move mv = make_move<FIXED>(cur);
             seen = fmaxf(seen, fabsf(mv.qw));
             // the stencil fits if its last node lies in the window (a move over
             // more than a neighbouring cell is sent to global memory)
@@ -300,21 +311,15 @@ __global__ __launch_bounds__(512) void k_zigzag_tiled(ZzArgs m)
                 else
                     atomicAdd(a, v);
             };
-            // a move that crosses no cell boundary has both segments in one
-            // cell: their contributions to each node are summed before the add
+            // a move that crosses no cell boundary is one segment when FIXED
+            // (above); its second, empty one is not added
             const bool same = mv.cell[0][0] == mv.cell[1][0] && mv.cell[0][1] == mv.cell[1][1] &&
                               mv.cell[0][2] == mv.cell[1][2];
-            float v1[3][4];
-            for_each_in_segment(mv, 1, [&](int c, int j, const int *, float v) { v1[c][j] = v; });
-            for_each_in_segment(mv, 0, [&](int c, int j, const int *, float v) {
-                add(0, c, j, same ? v + v1[c][j] : v);
-            });
-            if (!same)
-#pragma unroll
-                for (int c = 0; c < 3; ++c)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        add(1, c, j, v1[c][j]);
+            for_each_in_segment(mv, 0, [&](int c, int j, const int *, float v) { add(0, c, j, v); });
+            if (!(FIXED && same))
+                for_each_in_segment(mv, 1, [&](int c, int j, const int *, float v) {
+                    add(1, c, j, v);
+                });
         }
         __syncthreads();
         return seen;

@@ -649,11 +649,30 @@ __global__ __launch_bounds__(MOVE_WAVES * WAVE) void k_inc_move(
         for (int k0 = 0; k0 < arr.n; k0 += MOVE_GROUP) {
             float v[MOVE_GROUP][EPT];
 #pragma unroll
-            for (int j = 0; j < MOVE_GROUP; ++j)
-                if (k0 + j < arr.n)
+            for (int j = 0; j < MOVE_GROUP; ++j) {
+                if (k0 + j >= arr.n)
+                    continue;
+                // an array that is one of the keyed positions is already in
+                // registers (a wave-uniform pointer test): not fetched twice
+                const float *src = arr.in[k0 + j];
+                if (src == x0) {
 #pragma unroll
                     for (int e = 0; e < EPT; ++e)
-                        v[j][e] = arr.in[k0 + j][pc[e]];
+                        v[j][e] = c[e][0];
+                } else if (DIM > 1 && src == x1) {
+#pragma unroll
+                    for (int e = 0; e < EPT; ++e)
+                        v[j][e] = c[e][1];
+                } else if (DIM > 2 && src == x2) {
+#pragma unroll
+                    for (int e = 0; e < EPT; ++e)
+                        v[j][e] = c[e][2];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < EPT; ++e)
+                        v[j][e] = src[pc[e]];
+                }
+            }
 #pragma unroll
             for (int j = 0; j < MOVE_GROUP; ++j)
                 if (k0 + j < arr.n)

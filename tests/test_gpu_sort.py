@@ -131,6 +131,31 @@ def test_resort_steady_state(orc, dim, n, order, T, ppc):
     _check_resort(orc, s, order, T, off, s.x_next, s.x_next + s.v + [s.q, s.w])
 
 
+@pytest.mark.parametrize("dim,n,order,T,ppc", [
+    (3, [32, 32, 32], 1, 8, 4),
+    (2, [64, 64], 1, 8, 6),
+    (3, [24, 24, 24], 1, 1, 2),    # cell layout (the small-chunk move)
+])
+def test_resort_positions_among_arrays(orc, dim, n, order, T, ppc):
+    """The keyed positions passed again as moved arrays (the same device
+    tensors, as a step re-sorting its own state does): the move takes them
+    from registers and must still give the oracle's stable order."""
+    wl = synthetic.deposit_workload(dim, n, ppc=ppc, far_fraction=0.02, seed=640 + T + dim)
+    s, off = _sorted_state(orc, wl, order, T)
+    say("resort aliased", dim, n, order, T, s.count)
+    fields = s.x_next + s.v + [s.q, s.w]
+    cur = [dev(a) for a in fields]
+    prev = pcg.Layout(T=T, order=order, tile_offsets=dev(off.view(np.int32)),
+                      n_partitioned=s.count)
+    perm, keys, noff, outs = pcg.pcg_tile_sort(dim, n, order, T, cur[:dim], cur, prev=prev)
+    torch.cuda.synchronize()
+    k_ref, p_ref, o_ref = orc.tile_sort(dim, n, order, T, s.x_next)
+    assert np.array_equal(u32(perm), p_ref)
+    assert np.array_equal(u32(noff), o_ref)
+    for a, o in zip(fields, outs):
+        assert np.array_equal(o.cpu().numpy(), a[p_ref])
+
+
 def test_resort_far_moves_fall_back(orc):
     """Particles that moved more than one tile raise the device flag; the radix
     path then produces the same stable result."""

@@ -771,12 +771,33 @@ __global__ __launch_bounds__(MOVE_WAVES * WAVE) void k_inc_move_small(
                     perm[pos[j]] = p[j];
         }
         // every array's values first (one round trip), then the stores
+        // (a keyed position array is taken from registers, as in k_inc_move)
         float v[MAX_ARRAYS][K];
 #pragma unroll
-        for (int k = 0; k < MAX_ARRAYS; ++k)
+        for (int k = 0; k < MAX_ARRAYS; ++k) {
+            const float *src = k < arr.n ? arr.in[k] : nullptr;
+            if (src == nullptr) {
 #pragma unroll
-            for (int j = 0; j < K; ++j)
-                v[k][j] = k < arr.n ? arr.in[k][pc[j]] : 0.f;
+                for (int j = 0; j < K; ++j)
+                    v[k][j] = 0.f;
+            } else if (src == x0) {
+#pragma unroll
+                for (int j = 0; j < K; ++j)
+                    v[k][j] = c[j][0];
+            } else if (DIM > 1 && src == x1) {
+#pragma unroll
+                for (int j = 0; j < K; ++j)
+                    v[k][j] = c[j][1];
+            } else if (DIM > 2 && src == x2) {
+#pragma unroll
+                for (int j = 0; j < K; ++j)
+                    v[k][j] = c[j][2];
+            } else {
+#pragma unroll
+                for (int j = 0; j < K; ++j)
+                    v[k][j] = src[pc[j]];
+            }
+        }
 #pragma unroll
         for (int k = 0; k < MAX_ARRAYS; ++k) {
             if (k < arr.n) {

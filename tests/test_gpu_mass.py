@@ -10,7 +10,7 @@ import torch
 
 import particle_cell_grid_amd as pcg
 import synthetic
-from gpu_util import DEV, dev, full_workload, rel_frob_err, say
+from gpu_util import DEV, dev, full_size_checks, full_workload, rel_frob_err, say
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-4
@@ -89,29 +89,21 @@ def test_mass_zero_field_reduces_to_scalar(orc):
     assert np.allclose(M[..., 0, 0], M[..., 2, 2], rtol=1e-6, atol=1e-6)
 
 
+@pytest.mark.parametrize("variant", [pcg.PCG_MASS_MFMA, pcg.PCG_MASS_VALU])
+@pytest.mark.parametrize("n,ppc", [([8, 8, 40], 16), ([10, 9, 36], 24)])
+def test_mass_z_seams(orc, variant, n, ppc):
+    """Grids taller than one work-group column of nodes in z: every row, the
+    rows on both sides of each column boundary and of the periodic wrap
+    included, against the oracle.  Weights w ~ U[0.5, 1.5]."""
+    wl = synthetic.mass_workload(n, ppc, w_uniform=True, seed=510 + ppc)
+    _, perm, off = orc.tile_sort(3, n, 1, 1, wl.x)
+    M = _run(wl, perm, off, variant)
+    _check(M, orc.mass_matrix(n, wl.x, wl.B, wl.q, wl.w, wl.beta))
+
+
 def test_mass_full_size_64(orc):
-    """64^3, 64 ppc (16.8M particles).  The oracle runs on the particles of a
-    z-slab of cells; rows of nodes whose 8 adjacent cells all lie in the slab are
-    compared, plus the global totals sum_{g,o} M = sum_p q w alpha_p."""
+    """64^3, 64 ppc (16.8M particles), the launch the benchmark times."""
     wl = full_workload("mass_64_ppc64")
     _, perm, off = orc.tile_sort(3, wl.n, 1, 1, wl.x)
     M = _run(wl, perm, off, pcg.PCG_MASS_MFMA)
-    z0, z1 = 20, 30
-    cz = np.floor(wl.x[2]).astype(np.int64)
-    sel = (cz >= z0) & (cz < z1)
-    sub = wl.take(np.nonzero(sel)[0])
-    ref = orc.mass_matrix(wl.n, sub.x, sub.B, sub.q, sub.w, sub.beta)
-    # node z = g touches cells z in {g-1, g}: rows g in [z0+1, z1-1] are complete
-    _check(M[z0 + 1:z1], ref[z0 + 1:z1])
-    # totals over the whole grid: 9 components, fp64 sums of the per-particle alphas
-    om = np.stack([wl.beta.astype(np.float64) * b for b in wl.B])
-    den = 1.0 + (om * om).sum(axis=0)
-    qw = wl.q.astype(np.float64) * wl.w
-    eps = np.zeros((3, 3, 3))
-    eps[0, 1, 2] = eps[1, 2, 0] = eps[2, 0, 1] = 1
-    eps[0, 2, 1] = eps[2, 1, 0] = eps[1, 0, 2] = -1
-    for i in range(3):
-        for j in range(3):
-            a_ij = ((i == j) + np.einsum("k,kp->p", eps[i, j], om) + om[i] * om[j]) / den
-            tot = (qw * a_ij).sum()
-            assert abs(M[..., i, j].astype(np.float64).sum() - tot) <= 1e-4 * np.abs(qw).sum()
+    full_size_checks(orc, wl.take(perm.astype(np.int64)), M, TOL)

@@ -13,7 +13,8 @@ import torch
 
 import particle_cell_grid_amd as pcg
 import synthetic
-from gpu_util import DEV, dev, full_workload, rel_frob_err, say
+from gpu_util import (DEV, block_row_sums, check_row_sums, dev, full_size_checks,
+                      full_workload, node_row_sums, rel_frob_err, say, seam_cells)
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-12
@@ -81,14 +82,40 @@ def test_f64_mass_ragged_stale_and_tail(orc, scalar):
     _check(M, _ref(orc, n, s, scalar))
 
 
+@pytest.mark.parametrize("scalar", [False, True])
+@pytest.mark.parametrize("variant", [pcg.PCG_MASS_MFMA, pcg.PCG_MASS_VALU])
+@pytest.mark.parametrize("n,ppc", [([8, 8, 40], 16), ([10, 9, 36], 24)])
+def test_f64_mass_z_seams(orc, scalar, variant, n, ppc):
+    """Grids taller than one work-group column of nodes in z (both matrices):
+    every row, those on both sides of each column boundary and of the wrap
+    included, against the oracle."""
+    wl = synthetic.mass_workload(n, ppc, w_uniform=True, seed=710 + ppc)
+    _, perm, off = orc.tile_sort(3, n, 1, 1, wl.x)
+    _check(_run(wl, perm, off, variant, scalar), _ref(orc, n, wl, scalar))
+
+
 def test_f64_mass_full_size_64(orc):
-    """64^3, 64 ppc, the tensor matrix in fp64 on the matrix cores: rows of a
-    z-slab against the oracle on the slab's particles."""
+    """64^3, 64 ppc, the tensor matrix in fp64 on the matrix cores: the rows on
+    both sides of every z plane 8k entry by entry, and every row's block sums."""
     wl = full_workload("mass_64_ppc64")
     _, perm, off = orc.tile_sort(3, wl.n, 1, 1, wl.x)
     M = _run(wl, perm, off, pcg.PCG_MASS_MFMA, scalar=False)
-    z0, z1 = 20, 30
-    cz = np.floor(wl.x[2]).astype(np.int64)
-    sub = wl.take(np.nonzero((cz >= z0) & (cz < z1))[0])
-    ref = orc.mass_matrix(wl.n, sub.x, sub.B, sub.q, sub.w, sub.beta)
-    _check(M[z0 + 1:z1], ref[z0 + 1:z1])
+    full_size_checks(orc, wl.take(perm.astype(np.int64)), M, TOL)
+
+
+def test_f64_scalar_mass_full_size_64(orc):
+    """64^3, 64 ppc, the scalar matrix in fp64 on the matrix cores: the rows on
+    both sides of every z plane 4k (its work-group columns are 8 nodes tall)
+    entry by entry, and every row's sum against sum_p q w W_pg."""
+    wl = full_workload("mass_64_ppc64")
+    _, perm, off = orc.tile_sort(3, wl.n, 1, 1, wl.x)
+    M = _run(wl, perm, off, pcg.PCG_MASS_MFMA, scalar=True)
+    s = wl.take(perm.astype(np.int64))
+    cells, rows = seam_cells(wl.n[2], 4)
+    sub = s.take(np.nonzero(cells[np.floor(s.x[2]).astype(np.int64)])[0])
+    ref = orc.mass_matrix_scalar(wl.n, sub.x, sub.q, sub.w)
+    _check(M[rows], ref[rows])
+    qw = s.q.astype(np.float64) * s.w
+    want = node_row_sums(wl.n, s.x, 1, [qw])
+    scale = node_row_sums(wl.n, s.x, 1, [np.abs(qw)])
+    say("row sums: worst error / bound", check_row_sums(block_row_sums(M), want, scale, TOL))

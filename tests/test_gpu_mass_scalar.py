@@ -12,7 +12,8 @@ import torch
 
 import particle_cell_grid_amd as pcg
 import synthetic
-from gpu_util import DEV, dev, full_workload, rel_frob_err, say
+from gpu_util import (DEV, block_row_sums, check_row_sums, dev, full_workload, node_row_sums,
+                      rel_frob_err, say, seam_cells)
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-4
@@ -86,21 +87,33 @@ def test_scalar_mass_no_layout_is_flat(orc):
     _check(M, orc.mass_matrix_scalar(wl.n, wl.x, wl.q, wl.w))
 
 
+@pytest.mark.parametrize("variant", [pcg.PCG_MASS_MFMA, pcg.PCG_MASS_VALU])
+def test_scalar_mass_z_seams(orc, variant):
+    """A grid of several 8-node work-group columns in z and two in y: every row
+    against the oracle."""
+    wl = synthetic.mass_workload([8, 10, 36], 24, w_uniform=True, seed=611)
+    _, perm, off = orc.tile_sort(3, wl.n, 1, 1, wl.x)
+    _check(_run(wl, perm, off, variant), orc.mass_matrix_scalar(wl.n, wl.x, wl.q, wl.w))
+
+
 def test_scalar_mass_full_size_64(orc):
-    """64^3, 64 ppc (16.8M particles), the launch the benchmark times.  The oracle
-    runs on the particles of a z-slab of cells and the rows whose 8 adjacent cells
-    lie in the slab are compared; the grand total is sum_p q w; entries (g, o)
-    and (g + o, -o) agree (symmetry) to fp32 rounding."""
+    """64^3, 64 ppc (16.8M particles), the launch the benchmark times.  The
+    oracle runs on the particles of the cell planes on both sides of every z
+    plane 4k (the wrap included) and the node rows only they reach are
+    compared entry by entry; every row's sum equals sum_p q w W_pg (Eq.(11),
+    numpy); entries (g, o) and (g + o, -o) agree (symmetry) to fp32 rounding."""
     wl = full_workload("mass_64_ppc64")
     _, perm, off = orc.tile_sort(3, wl.n, 1, 1, wl.x)
     M = _run(wl, perm, off, pcg.PCG_MASS_MFMA)
-    z0, z1 = 20, 30
-    cz = np.floor(wl.x[2]).astype(np.int64)
-    sub = wl.take(np.nonzero((cz >= z0) & (cz < z1))[0])
+    s = wl.take(perm.astype(np.int64))
+    cells, rows = seam_cells(wl.n[2], 4)
+    sub = s.take(np.nonzero(cells[np.floor(s.x[2]).astype(np.int64)])[0])
     ref = orc.mass_matrix_scalar(wl.n, sub.x, sub.q, sub.w)
-    _check(M[z0 + 1:z1], ref[z0 + 1:z1])
-    qw = wl.q.astype(np.float64) * wl.w
-    assert abs(M.astype(np.float64).sum() - qw.sum()) <= 1e-4 * np.abs(qw).sum()
+    _check(M[rows], ref[rows])
+    qw = s.q.astype(np.float64) * s.w
+    want = node_row_sums(wl.n, s.x, 1, [qw])
+    scale = node_row_sums(wl.n, s.x, 1, [np.abs(qw)])
+    say("row sums: worst error / bound", check_row_sums(block_row_sums(M), want, scale, TOL))
     offs = [(dx, dy, dz) for dz in (-1, 0, 1) for dy in (-1, 0, 1) for dx in (-1, 0, 1)]
     scale = np.abs(M).max()
     for o, (dx, dy, dz) in enumerate(offs):

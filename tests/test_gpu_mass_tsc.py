@@ -11,7 +11,8 @@ import torch
 
 import particle_cell_grid_amd as pcg
 import synthetic
-from gpu_util import DEV, dev, full_workload, rel_frob_err, say
+from gpu_util import (DEV, alpha_coefs, axis_weights, block_row_sums, check_row_sums, dev,
+                      full_workload, node_row_sums, rel_frob_err, say)
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-4
@@ -80,7 +81,8 @@ def test_tsc_mass_no_layout_is_flat(orc):
 def test_tsc_mass_full_size_64(orc):
     """64^3, 64 ppc on the matrix cores: rows of a z-slab against the oracle on the
     particles whose support base lies in the slab (node plane z receives from
-    bases z-2 .. z), and the grand total sum q w."""
+    bases z-2 .. z), and every row's sum against sum_p q w W_pg (Eq.(11),
+    numpy)."""
     wl = full_workload("mass_64_ppc64")
     s, off = _grouped(orc, wl)
     M = _run(wl.n, s, off, pcg.PCG_MASS_MFMA)
@@ -91,8 +93,10 @@ def test_tsc_mass_full_size_64(orc):
     sub = wl.take(np.nonzero((bz >= z0) & (bz < z1))[0])
     ref = orc.mass_matrix_scalar_tsc(wl.n, sub.x, sub.q, sub.w)
     _check(M[z0 + 2:z1], ref[z0 + 2:z1])
-    qw = wl.q.astype(np.float64) * wl.w
-    assert abs(M.astype(np.float64).sum() - qw.sum()) <= 1e-4 * np.abs(qw).sum()
+    qw = s.q.astype(np.float64) * s.w
+    want = node_row_sums(wl.n, s.x, 2, [qw])
+    scale = node_row_sums(wl.n, s.x, 2, [np.abs(qw)])
+    say("row sums: worst error / bound", check_row_sums(block_row_sums(M), want, scale, TOL))
 
 
 def _run_tensor(n, s, off, variant, n_part=None, use_layout=True):
@@ -147,3 +151,36 @@ def test_tsc_tensor_mass_large(orc):
     s, off = _grouped(orc, wl)
     M = _run_tensor(wl.n, s, off, pcg.PCG_MASS_MFMA)
     _check(M, orc.mass_matrix_tsc(wl.n, wl.x, wl.B, wl.q, wl.w, wl.beta))
+
+
+def test_tsc_tensor_mass_full_size_64(orc):
+    """64^3, 64 ppc (16.8M particles), the launch the benchmark times.
+    (1) Element-wise: the oracle runs on the particles whose support base lies
+    in a 10^3 box of nodes straddling the periodic wrap on every axis (bases
+    59..63, 0..4); the 8^3 node rows that only those bases reach (node g
+    receives from bases g-2 .. g) are compared entry by entry.
+    (2) Every row: block row sums of the trace, of the skew pair (0,1)-(1,0) and
+    of the symmetric pair (0,2)+(2,0) against sum_p c_p W_pg (Eq.(11), numpy)."""
+    wl = full_workload("mass_64_ppc64")
+    s, off = _grouped(orc, wl)
+    M = _run_tensor(wl.n, s, off, pcg.PCG_MASS_MFMA)
+    box = (np.arange(64) >= 59) | (np.arange(64) < 5)
+    inside = np.ones(s.count, bool)
+    for k in range(3):
+        base, _ = axis_weights(s.x[k], 64, 2)
+        inside &= box[base]
+    sub = s.take(np.nonzero(inside)[0])
+    ref = orc.mass_matrix_tsc(wl.n, sub.x, sub.B, sub.q, sub.w, sub.beta)
+    rows = np.r_[61:64, 0:5]
+    ix = np.ix_(rows, rows, rows)
+    _check(M[ix], ref[ix])
+    del ref
+    c = alpha_coefs(s)
+    combos = [c[0] + c[4] + c[8], c[1] - c[3], c[2] + c[6]]
+    want = node_row_sums(wl.n, s.x, 2, combos)
+    scale = node_row_sums(wl.n, s.x, 2, [np.abs(c[0]) + np.abs(c[4]) + np.abs(c[8]),
+                                         np.abs(c[1]) + np.abs(c[3]),
+                                         np.abs(c[2]) + np.abs(c[6])])
+    rs = block_row_sums(M)
+    got = np.stack([rs[0] + rs[4] + rs[8], rs[1] - rs[3], rs[2] + rs[6]])
+    say("row sums: worst error / bound", check_row_sums(got, want, scale, TOL))

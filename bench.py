@@ -88,12 +88,15 @@ def kernel_times(pcg, names):
     return out
 
 
+EVICT_BYTES = 1 << 30  # written before each rep of the cold-cache protocol
+
+
 def time_steps(torch, pcg, step, steps, warmup):
-    """K timed steps, twice.  The first, uninstrumented, gives ms per step and
-    the wall time; the second repeats the same K steps with the library's
-    per-launch HIP events (recorded on the launch stream) for each kernel's
-    duration.  The events add gaps between launches, so they stay out of the
-    step time."""
+    """K timed steps, back to back, twice.  The first, uninstrumented, gives ms
+    per step and the wall time; the second repeats the same K steps with the
+    library's per-launch HIP events (recorded on the launch stream) for each
+    kernel's duration.  The events add gaps between launches, so they stay out
+    of the step time."""
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -115,6 +118,29 @@ def time_steps(torch, pcg, step, steps, warmup):
     pcg.pcg_timing_enable(False)
     kt = kernel_times(pcg, pcg.pcg_timing_names())
     return ms, wall, kt
+
+
+def time_cold(torch, fn, reps, evict):
+    """The cold-cache protocol: before every rep, outside its timed region, a
+    write of `evict` (1 GiB) flushes the L2s and the Infinity Cache of
+    everything the previous rep left; each rep is timed alone with events on
+    the current stream.  Returns dict(median, min, p90, reps) in ms."""
+    import numpy as np
+
+    times = []
+    for i in range(reps):
+        evict.fill_(i & 255)
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        times.append(ev0.elapsed_time(ev1))
+    t = np.asarray(times)
+    return dict(median=round(float(np.median(t)), 4), min=round(float(t.min()), 4),
+                p90=round(float(np.percentile(t, 90)), 4), reps=reps,
+                evict_bytes=int(evict.numel()))
 
 
 def time_plain(torch, fn, reps):
@@ -163,12 +189,54 @@ def roofline_entry(kt, name, bytes_per_launch=None, flops_per_launch=None,
                 avg_us=round(k["avg_us"], 2))
 
 
-def cpu_baseline_deposit(wl, order, T, target_s):
-    """The fp64 oracle as it stands (single thread) on a bounded prefix sample of
-    the same particles: its tile sort (keys + stable counting sort) and deposit."""
-    import numpy as np
+# Launches of the general sort path.  When a step re-sorts from the previous
+# layout, the library enqueues them behind the incremental path and they
+# return at once unless a device flag hands them the work (a particle moved
+# further than a tile, or the layout was not a partition).
+GENERAL_SORT = ("sort_keys", "sort_hist", "sort_scatter", "sort_scan_reduce",
+                "sort_scan_partials", "sort_scan_down", "sort_offsets", "sort_permute",
+                "radix_hist", "radix_scatter", "radix_scan", "radix_offsets", "radix_permute")
 
+
+def kernel_table(kt, steps, alg, gated=False):
+    """Per-kernel entries of the timed steps: average duration and launches per
+    step, and for a kernel that does the step's work its algorithmic bytes and
+    their rate.  With gated=True the general sort's launches are marked as
+    such and carry no bytes (they moved none)."""
+    out = {}
+    for nm, kk in kt.items():
+        e = dict(avg_us=round(kk["avg_us"], 2), launches_per_step=kk["launches"] / steps)
+        if gated and nm in GENERAL_SORT:
+            e["gated"] = ("general-sort fallback enqueued behind the incremental sort; returns "
+                          "at once unless the device flag is raised")
+        elif nm in alg:
+            e["alg_bytes"] = alg[nm]
+            e["GBps"] = round(alg[nm] / (kk["avg_us"] * 1e-6) / 1e9, 1)
+        out[nm] = e
+    return out
+
+
+def cpu_baseline(single, parallel_fn, nthreads, unit):
+    """The cpu_baseline object: the oracle on every host core it may use (the
+    reported figure), with the single-thread figure beside it.  single and the
+    result of parallel_fn are (items, seconds, sample)."""
+    from oracle import parallel
+
+    items, sec, sample = parallel_fn()
+    s_items, s_sec, s_sample = single
+    return dict(value=round(items / sec, 1), unit=unit, cores=nthreads, kind="oracle",
+                sample=sample, cpu_model=parallel.cpu_model(),
+                affinity_cores=parallel.host_cores(),
+                single_thread=dict(value=round(s_items / s_sec, 1), cores=1, sample=s_sample))
+
+
+def cpu_baseline_deposit(wl, order, T, target_s):
+    """The fp64 oracle as it stands on a bounded prefix sample of the same
+    particles, its tile sort (keys + stable counting sort) and deposit: on one
+    thread, and on every host core (per-thread ranges, private J added in
+    thread order)."""
     import oracle
+    from oracle import parallel
 
     def run(m):
         x = [a[:m] for a in wl.x_next]
@@ -181,9 +249,19 @@ def cpu_baseline_deposit(wl, order, T, target_s):
     per = run(cal) / cal
     m = int(min(wl.count, max(cal, target_s / per)))
     sec = run(m)
-    return dict(value=round(m / sec, 1), unit="particles/s", cores=1, kind="oracle",
-                sample=f"first {m} of {wl.count} particles of the step input: oracle tile sort "
-                       f"(keys + stable counting sort) + fp64 deposit, {sec:.1f} s, 1 thread")
+    single = (m, sec, f"first {m} of {wl.count} particles of the step input: oracle tile sort "
+                      f"(keys + stable counting sort) + fp64 deposit, {sec:.1f} s, 1 thread")
+    nth = parallel.thread_count(3 * 8 * wl.n[0] * wl.n[1] * wl.n[2])
+
+    def run_par():
+        t0 = time.perf_counter()
+        parallel.deposit_step(wl.dim, wl.n, order, T, wl.x_next, wl.v, wl.q, wl.w, nth)
+        sec = time.perf_counter() - t0
+        return wl.count, sec, (f"all {wl.count} particles of the step input: oracle tile sort + "
+                               f"fp64 deposit on {nth} threads (per-thread ranges, private fp64 "
+                               f"J added in thread order), {sec:.1f} s")
+
+    return cpu_baseline(single, run_par, nth, "particles/s")
 
 
 # ----------------------------------------------------------------- deposit family
@@ -266,18 +344,19 @@ def bench_deposit(args, torch, pcg, name):
         "sort_permute": cnt * (4 + 2 * pbytes),
         "sort_offsets": cnt * 4 + (nt + 1) * 4,
     }
-    kernels = {}
-    for nm, kk in kt.items():
-        e = dict(avg_us=round(kk["avg_us"], 2), launches_per_step=kk["launches"] / args.steps)
-        if nm in alg:
-            e["alg_bytes"] = alg[nm]
-            e["GBps"] = round(alg[nm] / (kk["avg_us"] * 1e-6) / 1e9, 1)
-        kernels[nm] = e
+    # the step re-sorts from the previous layout: the general sort's launches
+    # are the gated fallback
+    kernels = kernel_table(kt, args.steps, alg, gated=True)
     dominant = max(kt, key=lambda nm: kt[nm]["total_ms"])
     roof_dom = (roofline_entry(kt, dominant, bytes_per_launch=alg[dominant])
                 if dominant in alg else None)
 
     extra = {}
+    progress("timing the step with cold caches")
+    evict = torch.empty(EVICT_BYTES, dtype=torch.uint8, device=dev)
+    extra["cold_step_ms"] = time_cold(torch, step, args.steps, evict)
+    extra["cold_deposit_ms"] = time_cold(torch, lambda: (J.zero_(), deposit()), args.steps, evict)
+    del evict
     # the deposit alone (deposit_currents on the same input), with its own tap
     progress("timing the deposit alone")
     dep_ms, _, kt_dep = time_steps(torch, pcg, lambda: (J.zero_(), deposit()), args.steps, 1)
@@ -380,17 +459,15 @@ def bench_zigzag(args, torch, pcg):
         "sort_inc_count": cnt * 3 * 4,
         "sort_inc_move": cnt * 2 * 8 * 4,
     }
-    kernels = {}
-    for nm, kk in kt.items():
-        e = dict(avg_us=round(kk["avg_us"], 2), launches_per_step=kk["launches"] / args.steps)
-        if nm in alg:
-            e["alg_bytes"] = alg[nm]
-            e["GBps"] = round(alg[nm] / (kk["avg_us"] * 1e-6) / 1e9, 1)
-        kernels[nm] = e
+    kernels = kernel_table(kt, args.steps, alg, gated=True)
     roof = roofline_entry(kt, "zigzag_tiled", bytes_per_launch=alg["zigzag_tiled"])
     if roof:
         roof["traffic"] = measured_traffic("zigzag_tiled", "zigzag3d_128_ppc32")
     extra = dict(escaped_particles=n_esc)
+    progress("timing the step with cold caches")
+    evict = torch.empty(EVICT_BYTES, dtype=torch.uint8, device=dev)
+    extra["cold_step_ms"] = time_cold(torch, step, args.steps, evict)
+    del evict
     dep_ms = time_plain(torch, lambda: (J.zero_(), deposit()), args.steps)
     extra["deposit_only_ms"] = round(dep_ms, 4)
     if not args.no_flat:
@@ -417,9 +494,21 @@ def bench_zigzag(args, torch, pcg):
         per = run(cal) / cal
         m = int(min(cnt, max(cal, args.cpu_seconds / per)))
         sec = run(m)
-        cpu = dict(value=round(m / sec, 1), unit="particles/s", cores=1, kind="oracle",
-                   sample=f"first {m} of {cnt} particles: oracle tile sort + fp64 zigzag "
+        single = (m, sec, f"first {m} of {cnt} particles: oracle tile sort + fp64 zigzag "
                           f"deposit, {sec:.1f} s, 1 thread")
+        from oracle import parallel
+
+        nth = parallel.thread_count(3 * 8 * n[0] * n[1] * n[2])
+
+        def run_par():
+            t0 = time.perf_counter()
+            parallel.zigzag_step(n, T, wl.x, xp, wl.q, wl.w, nth)
+            sec = time.perf_counter() - t0
+            return cnt, sec, (f"all {cnt} particles: oracle tile sort + fp64 zigzag deposit on "
+                              f"{nth} threads (per-thread ranges, private fp64 J added in thread "
+                              f"order), {sec:.1f} s")
+
+        cpu = cpu_baseline(single, run_par, nth, "particles/s")
     config = dict(workload="3-D charge-conserving zigzag current deposit + tile sort, 128^3 "
                            "periodic, 32 ppc, each particle moved by its velocity",
                   particles=cnt, grid=n, tile=T, drift=D,
@@ -503,9 +592,14 @@ def bench_mass(args, torch, pcg, scalar=False, f64=False):
         roof = roofline_entry(kt, kname, flops_per_launch=flops, mfma_peak=mfma_peak)
     if roof:
         roof["traffic"] = measured_traffic(kname, wname)
-    kernels = {nm: dict(avg_us=round(kk["avg_us"], 2),
-                        launches_per_step=kk["launches"] / args.steps) for nm, kk in kt.items()}
+    kernels = kernel_table(kt, args.steps, {}, gated=True)
     extra = {}
+    progress("timing with cold caches")
+    evict = torch.empty(EVICT_BYTES, dtype=torch.uint8, device=dev)
+    extra["cold_step_ms"] = time_cold(torch, step, args.steps, evict)
+    extra["cold_assembly_ms"] = time_cold(
+        torch, lambda: (M.zero_(), assemble(pcg.PCG_MASS_MFMA)), args.steps, evict)
+    del evict
     for nm, var in (("valu", pcg.PCG_MASS_VALU), ("mfma", pcg.PCG_MASS_MFMA)):
         mm = time_plain(torch, lambda: (M.zero_(), assemble(var)), 5)
         extra[f"mass_{nm}_ms"] = round(mm, 4)
@@ -544,9 +638,27 @@ def bench_mass(args, torch, pcg, scalar=False, f64=False):
         t0 = time.perf_counter()
         run_oracle(m2)
         sec = time.perf_counter() - t0
-        cpu = dict(value=round(m2 / sec, 1), unit="particles/s", cores=1, kind="oracle",
-                   sample=f"first {m2} of {cnt} particles: fp64 per-particle outer products, "
-                          f"{sec:.1f} s, 1 thread")
+        single = (m2, sec, f"first {m2} of {cnt} particles: fp64 per-particle outer products, "
+                           f"{sec:.1f} s, 1 thread")
+        from oracle import parallel
+
+        nth = parallel.thread_count(M.numel() * 8)
+        m3 = int(min(cnt, m2 * nth))
+
+        def run_par():
+            xs = [a[:m3] for a in wl.x]
+            t0 = time.perf_counter()
+            if scalar:
+                parallel.mass(n, xs, wl.q[:m3], wl.w[:m3], nth)
+            else:
+                parallel.mass(n, xs, wl.q[:m3], wl.w[:m3], nth, B=[b[:m3] for b in wl.B],
+                              beta=wl.beta[:m3])
+            sec = time.perf_counter() - t0
+            return m3, sec, (f"first {m3} of {cnt} particles: fp64 per-particle outer products "
+                             f"on {nth} threads (per-thread ranges, private fp64 M added in "
+                             f"thread order), {sec:.1f} s")
+
+        cpu = cpu_baseline(single, run_par, nth, "particles/s")
     if scalar:
         config = dict(workload="scalar 3-D CIC mass matrix (coefficient q w) 64^3, 64 ppc "
                                "(cell sort + MFMA assembly)",
@@ -656,9 +768,12 @@ def bench_mass_tsc(args, torch, pcg, tensor=False):
     roof = roofline_entry(kt, kname, flops_per_launch=flops)
     if roof:
         roof["traffic"] = measured_traffic(kname, wname)
-    kernels = {nm: dict(avg_us=round(kk["avg_us"], 2),
-                        launches_per_step=kk["launches"] / args.steps) for nm, kk in kt.items()}
+    kernels = kernel_table(kt, args.steps, {}, gated=True)
     extra = {}
+    progress("timing with cold caches")
+    evict = torch.empty(EVICT_BYTES, dtype=torch.uint8, device=dev)
+    extra["cold_step_ms"] = time_cold(torch, step, args.steps, evict)
+    del evict
     for nm, var in (("valu", pcg.PCG_MASS_VALU), ("mfma", pcg.PCG_MASS_MFMA)):
         extra[f"mass_{nm}_ms"] = round(time_plain(torch, lambda: (M.zero_(), assemble(var)), 5), 4)
     extra["mfma_speedup_vs_valu"] = round(extra["mass_valu_ms"] / extra["mass_mfma_ms"], 2)
@@ -683,9 +798,27 @@ def bench_mass_tsc(args, torch, pcg, tensor=False):
         t0 = time.perf_counter()
         run_oracle(m2)
         sec = time.perf_counter() - t0
-        cpu = dict(value=round(m2 / sec, 1), unit="particles/s", cores=1, kind="oracle",
-                   sample=f"first {m2} of {cnt} particles: fp64 per-particle 27 x 27 outer "
-                          f"products, {sec:.1f} s, 1 thread")
+        single = (m2, sec, f"first {m2} of {cnt} particles: fp64 per-particle 27 x 27 outer "
+                           f"products, {sec:.1f} s, 1 thread")
+        from oracle import parallel
+
+        nth = parallel.thread_count(M.numel() * 8)
+        m3 = int(min(cnt, m2 * nth))
+
+        def run_par():
+            xs = [a[:m3] for a in wl.x]
+            t0 = time.perf_counter()
+            if tensor:
+                parallel.mass(n, xs, wl.q[:m3], wl.w[:m3], nth, B=[b[:m3] for b in wl.B],
+                              beta=wl.beta[:m3], order=2)
+            else:
+                parallel.mass(n, xs, wl.q[:m3], wl.w[:m3], nth, order=2)
+            sec = time.perf_counter() - t0
+            return m3, sec, (f"first {m3} of {cnt} particles: fp64 per-particle 27 x 27 outer "
+                             f"products on {nth} threads (per-thread ranges, private fp64 M "
+                             f"added in thread order), {sec:.1f} s")
+
+        cpu = cpu_baseline(single, run_par, nth, "particles/s")
     kind = "ECSIM 3-D TSC mass matrix" if tensor else "scalar 3-D TSC mass matrix (coefficient q w)"
     config = dict(workload=f"{kind} 64^3, 64 ppc (support-group sort + MFMA assembly)",
                   particles=cnt, grid=n,
@@ -750,9 +883,23 @@ def bench_sweep_grad(args, torch, pcg):
         oracle.sweep1d_grad(s.nb, s.x0[:m2], s.v[:m2], T, s.dt, s.hw,
                             2.0 * (Ho - target.cpu().numpy()))
         sec = time.perf_counter() - t0
-        cpu = dict(value=round(m2 * T / sec, 1), unit="particle-steps/s", cores=1,
-                   kind="oracle", sample=f"first {m2} of {n} particles, forward + reverse, "
-                                         f"{sec:.1f} s, 1 thread")
+        single = (m2 * T, sec, f"first {m2} of {n} particles, forward + reverse, {sec:.1f} s, "
+                               "1 thread")
+        from oracle import parallel
+
+        nth = parallel.thread_count(1)
+        m3 = int(min(n, m2 * nth))
+        tg = target.cpu().numpy()
+
+        def run_par():
+            t0 = time.perf_counter()
+            parallel.sweep_loss_grad(s.nb, s.x0[:m3], s.v[:m3], T, s.dt, s.hw, tg, nth)
+            sec = time.perf_counter() - t0
+            return m3 * T, sec, (f"first {m3} of {n} particles, forward + reverse on {nth} "
+                                 f"threads (per-thread ranges, histograms added in thread "
+                                 f"order), {sec:.1f} s")
+
+        cpu = cpu_baseline(single, run_par, nth, "particle-steps/s")
     config = dict(workload="1-D windowed sweep loss gradient: 10^7 particles, 50 steps, 1024 "
                            "bins (forward, seed, reverse gather)",
                   particles=n, steps=T, bins=s.nb)

@@ -42,3 +42,19 @@ def test_measured_traffic_follows_the_source_digest(monkeypatch):
     assert bench.measured_traffic("deposit_regroup", "no_such_workload") is None
     monkeypatch.setattr(profsummary, "source_digest", lambda k: "changed")
     assert bench.measured_traffic("deposit_regroup", "cic3d_128_ppc32") is None
+
+
+def test_kernel_table_marks_gated_launches():
+    """Launches of the general sort that a step enqueues behind the incremental
+    one carry no bytes, so no per-kernel rate can exceed the HBM peak by
+    counting work a gated launch never did."""
+    kt = {"deposit_regroup": dict(avg_us=1000.0, launches=20),
+          "sort_permute": dict(avg_us=6.0, launches=20),
+          "sort_hist": dict(avg_us=6.0, launches=40)}
+    alg = {"deposit_regroup": 4.3e9, "sort_permute": 4.5e9}
+    tab = bench.kernel_table(kt, 20, alg, gated=True)
+    assert "GBps" not in tab["sort_permute"] and "gated" in tab["sort_permute"]
+    assert tab["sort_hist"]["launches_per_step"] == 2.0
+    assert tab["deposit_regroup"]["GBps"] == 4300.0
+    for e in tab.values():
+        assert e.get("GBps", 0.0) <= bench.HBM_PEAK_GBS

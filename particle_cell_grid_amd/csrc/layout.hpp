@@ -127,69 +127,96 @@ __global__ __launch_bounds__(CHUNK_SCAN_BLOCK) void k_chunk_scan3(
     write_tile_chunks(map, map_len, c0, tile_items(off, t, n_part, chunk), t, off, n_part);
 }
 
-// Tiles up to which one work-group computes the whole layout in one launch.
-constexpr uint32_t CHUNK_ONE_BLOCK_MAX = 16384;
-constexpr int CHUNK_TPT = 4;  // tiles per thread per round of the one-launch layout
+// Tiles up to which the whole layout is computed in one launch.
+constexpr uint32_t CHUNK_PAR_MAX = 8192;
+constexpr int CHUNK_PAR_TPT = CHUNK_PAR_MAX / CHUNK_SCAN_BLOCK;  // tiles per thread
+constexpr uint32_t CHUNK_PAR_BLOCKS = 64;  // most work-groups of that launch
 
-// The whole layout in one work-group (ntiles <= CHUNK_ONE_BLOCK_MAX), and,
-// if `flag` is given, whether off is a partition of [0, n_part): *flag = 0 if
-// off[0] = 0, off is non-decreasing and off[ntiles] = n_part, else 1.
-__global__ __launch_bounds__(CHUNK_SCAN_BLOCK) void k_chunk_layout_one(
+// The whole layout in one launch (ntiles <= CHUNK_PAR_MAX), on several
+// work-groups.  Each work-group computes the prefix of the tiles' work items
+// into LDS (the same prefix in every work-group: a few KB of offsets each),
+// then writes its share of the map entries, finding each entry's tile by
+// binary search in the prefix.  Work-group 0 also writes cum[] and, if `flag`
+// is given, whether off is a partition of [0, n_part): *flag = 0 if off[0] = 0,
+// off is non-decreasing and off[ntiles] = n_part, else 1.
+__global__ __launch_bounds__(CHUNK_SCAN_BLOCK) void k_chunk_layout_par(
     const uint32_t *__restrict__ off, uint32_t ntiles, int64_t n_part, uint32_t chunk,
     uint32_t *__restrict__ cum, ChunkEntry *__restrict__ map, uint32_t map_len,
     const uint32_t *gate, uint32_t gate_run, uint32_t *flag)
 {
     if (gate && *gate != gate_run)
         return;
-    __shared__ uint32_t s_carry, s_bad;
-    if (threadIdx.x == 0) {
-        s_carry = 0;
+    __shared__ uint32_t s_cum[CHUNK_PAR_MAX + 1];
+    __shared__ uint32_t s_bad;
+    if (threadIdx.x == 0)
         s_bad = 0;
+    const bool check = flag && blockIdx.x == 0;
+    const uint32_t t0 = threadIdx.x * CHUNK_PAR_TPT;
+    uint32_t items[CHUNK_PAR_TPT], sum = 0;
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < CHUNK_PAR_TPT; ++j) {
+        const uint32_t t = t0 + j;
+        items[j] = t < ntiles ? tile_items(off, t, n_part, chunk) : 0u;
+        sum += items[j];
+        if (check && t < ntiles)
+            bad = bad || (t == 0 ? off[0] != 0u : off[t] < off[t - 1]);
     }
+    __syncthreads();  // s_bad is cleared
+    if (bad)
+        atomicOr(&s_bad, 1u);
+    uint32_t total;
+    uint32_t c = block_exclusive_1024(sum, &total);
+#pragma unroll
+    for (int j = 0; j < CHUNK_PAR_TPT; ++j) {
+        const uint32_t t = t0 + j;
+        if (t < ntiles)
+            s_cum[t] = c;
+        c += items[j];
+    }
+    if (threadIdx.x == 0)
+        s_cum[ntiles] = total;
     __syncthreads();
-    for (uint32_t base = 0; base < ntiles; base += CHUNK_SCAN_BLOCK * CHUNK_TPT) {
-        const uint32_t t0 = base + threadIdx.x * CHUNK_TPT;
-        uint32_t items[CHUNK_TPT], sum = 0;
-        bool bad = false;
-#pragma unroll
-        for (int j = 0; j < CHUNK_TPT; ++j) {
-            const uint32_t t = t0 + j;
-            items[j] = t < ntiles ? tile_items(off, t, n_part, chunk) : 0u;
-            sum += items[j];
-            if (flag && t < ntiles)
-                bad = bad || (t == 0 ? off[0] != 0u : off[t] < off[t - 1]);
+    if (blockIdx.x == 0) {
+        for (uint32_t t = threadIdx.x; t <= ntiles; t += CHUNK_SCAN_BLOCK)
+            cum[t] = s_cum[t];
+        if (check && threadIdx.x == 0) {
+            bool b = s_bad != 0u || (int64_t)off[ntiles] != n_part;
+            b = b || (ntiles == 0 ? off[0] != 0u : off[ntiles] < off[ntiles - 1]);
+            *flag = b ? 1u : 0u;
         }
-        if (bad)
-            atomicOr(&s_bad, 1u);
-        uint32_t total;
-        const uint32_t ex = block_exclusive_1024(sum, &total);
-        uint32_t c = s_carry + ex;
-#pragma unroll
-        for (int j = 0; j < CHUNK_TPT; ++j) {
-            const uint32_t t = t0 + j;
-            if (t < ntiles) {
-                cum[t] = c;
-                write_tile_chunks(map, map_len, c, items[j], t, off, n_part);
-                c += items[j];
-            }
-        }
-        __syncthreads();  // s_carry read and wsum reused below
-        if (threadIdx.x == 0)
-            s_carry += total;
-        __syncthreads();
     }
-    if (threadIdx.x == 0) {
-        cum[ntiles] = s_carry;
-        if (flag) {
-            bool bad = s_bad != 0u || (int64_t)off[ntiles] != n_part;
-            bad = bad || (ntiles == 0 ? off[0] != 0u : off[ntiles] < off[ntiles - 1]);
-            *flag = bad ? 1u : 0u;
+    const uint32_t nent = min(total, map_len);
+    for (uint32_t e = blockIdx.x * CHUNK_SCAN_BLOCK + threadIdx.x; e < nent;
+         e += gridDim.x * CHUNK_SCAN_BLOCK) {
+        // the tile t with s_cum[t] <= e < s_cum[t + 1] (s_cum[0] = 0 <= e < total)
+        uint32_t lo = 0, hi = ntiles;
+        while (hi - lo > 1) {
+            const uint32_t mid = (lo + hi) / 2;
+            if (s_cum[mid] <= e)
+                lo = mid;
+            else
+                hi = mid;
         }
+        const uint32_t n = s_cum[lo + 1] - s_cum[lo], j = e - s_cum[lo];
+        const uint64_t p0 = std::min<uint64_t>(off[lo], (uint64_t)n_part);
+        const uint64_t p1 = std::min<uint64_t>(off[lo + 1], (uint64_t)n_part);
+        const uint64_t len = p1 > p0 ? p1 - p0 : 0;
+        map[e] = ChunkEntry{lo, (uint32_t)(p0 + len * j / n), (uint32_t)(p0 + len * (j + 1) / n),
+                            0u};
     }
 }
 
+// Work-groups of the one-launch layout for a map of map_len entries.
+inline uint32_t chunk_par_blocks(uint32_t map_len)
+{
+    return std::max<uint32_t>(1u, std::min<uint32_t>(CHUNK_PAR_BLOCKS,
+                                                     (map_len + CHUNK_SCAN_BLOCK - 1) /
+                                                         CHUNK_SCAN_BLOCK));
+}
+
 // Enqueues the layout: cum[0..ntiles] and map[0..min(cum[ntiles], map_len)),
-// in one launch for up to CHUNK_ONE_BLOCK_MAX tiles, else in three passes
+// in one launch for up to CHUNK_PAR_MAX tiles, else in three passes
 // (part needs ceil(ntiles / CHUNK_SCAN_BLOCK) entries).  With a gate, the
 // kernels return at once unless *gate == gate_run.
 inline pcg_status launch_chunk_layout(const char *name, const uint32_t *off, uint32_t ntiles,
@@ -197,10 +224,10 @@ inline pcg_status launch_chunk_layout(const char *name, const uint32_t *off, uin
                                       uint32_t *part, ChunkEntry *map, uint32_t map_len,
                                       const uint32_t *gate, uint32_t gate_run, hipStream_t st)
 {
-    if (ntiles <= CHUNK_ONE_BLOCK_MAX)
-        return launch(name, k_chunk_layout_one, dim3(1), dim3(CHUNK_SCAN_BLOCK), 0, st, off,
-                      ntiles, n_part, chunk, cum, map, map_len, gate, gate_run,
-                      (uint32_t *)nullptr);
+    if (ntiles <= CHUNK_PAR_MAX)
+        return launch(name, k_chunk_layout_par, dim3(chunk_par_blocks(map_len)),
+                      dim3(CHUNK_SCAN_BLOCK), 0, st, off, ntiles, n_part, chunk, cum, map,
+                      map_len, gate, gate_run, (uint32_t *)nullptr);
     const uint32_t nb = (ntiles + CHUNK_SCAN_BLOCK - 1) / CHUNK_SCAN_BLOCK;
     PCG_TRY(launch(name, k_chunk_scan1, dim3(nb), dim3(CHUNK_SCAN_BLOCK), 0, st, off, ntiles,
                    n_part, chunk, cum, part, gate, gate_run));

@@ -79,23 +79,28 @@ __global__ __launch_bounds__(SORT_BLOCK) void k_radix_hist(const uint32_t *__res
         return;
     constexpr uint32_t R = 1u << BITS;
     __shared__ uint32_t hist[R];
-    for (uint32_t d = threadIdx.x; d < R; d += SORT_BLOCK)
-        hist[d] = 0;
-    __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * SORT_TILE;
+    // the launch may have fewer work-groups than key blocks: each takes every
+    // gridDim.x-th block (a small grid keeps a gated-off launch cheap)
+    for (uint32_t vb = blockIdx.x; vb < nblocks; vb += gridDim.x) {
+        for (uint32_t d = threadIdx.x; d < R; d += SORT_BLOCK)
+            hist[d] = 0;
+        __syncthreads();
+        const int64_t base = (int64_t)vb * SORT_TILE;
 #pragma unroll 4
-    for (int j = 0; j < SORT_IPT; ++j) {
-        const int64_t idx = base + (int64_t)j * SORT_BLOCK + threadIdx.x;
-        const bool valid = idx < count;
-        const uint32_t digit = valid ? (keys[idx] >> shift) & (R - 1) : 0u;
-        const uint64_t peers = peer_mask<BITS>(digit, valid);
-        // the lowest lane of each peer group adds the group's size
-        if (valid && (peers & lanemask_lt()) == 0)
-            atomicAdd(&hist[digit], (uint32_t)__popcll(peers));
+        for (int j = 0; j < SORT_IPT; ++j) {
+            const int64_t idx = base + (int64_t)j * SORT_BLOCK + threadIdx.x;
+            const bool valid = idx < count;
+            const uint32_t digit = valid ? (keys[idx] >> shift) & (R - 1) : 0u;
+            const uint64_t peers = peer_mask<BITS>(digit, valid);
+            // the lowest lane of each peer group adds the group's size
+            if (valid && (peers & lanemask_lt()) == 0)
+                atomicAdd(&hist[digit], (uint32_t)__popcll(peers));
+        }
+        __syncthreads();
+        for (uint32_t d = threadIdx.x; d < R; d += SORT_BLOCK)
+            counts[(size_t)d * nblocks + vb] = hist[d];
+        __syncthreads();  // hist is cleared for the next block
     }
-    __syncthreads();
-    for (uint32_t d = threadIdx.x; d < R; d += SORT_BLOCK)
-        counts[(size_t)d * nblocks + blockIdx.x] = hist[d];
 }
 
 template <int BITS>
@@ -109,6 +114,9 @@ __global__ __launch_bounds__(SORT_BLOCK) void k_radix_scatter(
     constexpr uint32_t R = 1u << BITS;
     __shared__ uint16_t cnt[SORT_SLOTS][R];  // items of digit d in wave-slot s, then prefix
     __shared__ uint32_t gbase[R];
+    // virtual blocks, as in k_radix_hist
+    for (uint32_t vb = blockIdx.x; vb < nblocks; vb += gridDim.x) {
+    __syncthreads();  // the previous block is done with cnt and gbase
     {
         uint32_t *c32 = reinterpret_cast<uint32_t *>(&cnt[0][0]);
         constexpr int words = SORT_SLOTS * R / 2;
@@ -116,11 +124,11 @@ __global__ __launch_bounds__(SORT_BLOCK) void k_radix_scatter(
             c32[i] = 0;
     }
     for (uint32_t d = threadIdx.x; d < R; d += SORT_BLOCK)
-        gbase[d] = offsets[(size_t)d * nblocks + blockIdx.x];
+        gbase[d] = offsets[(size_t)d * nblocks + vb];
     __syncthreads();
 
     const int wave = threadIdx.x / WAVE;
-    const int64_t base = (int64_t)blockIdx.x * SORT_TILE;
+    const int64_t base = (int64_t)vb * SORT_TILE;
     uint32_t key[SORT_IPT], val[SORT_IPT];
     uint16_t rank[SORT_IPT];
 #pragma unroll
@@ -158,6 +166,7 @@ __global__ __launch_bounds__(SORT_BLOCK) void k_radix_scatter(
                 vals_out[dst] = val[j];
             }
         }
+    }
     }
 }
 
@@ -205,17 +214,20 @@ __global__ __launch_bounds__(SCAN_BLOCK) void k_scan_reduce(const uint32_t *__re
 {
     if (gated_off(gate))
         return;
-    const size_t base = (size_t)blockIdx.x * SCAN_TILE;
-    uint32_t s = 0;
-    for (int j = 0; j < SCAN_IPT; ++j) {
-        const size_t idx = base + (size_t)j * SCAN_BLOCK + threadIdx.x;
-        if (idx < len)
-            s += in[idx];
+    const uint32_t nparts = (uint32_t)((len + SCAN_TILE - 1) / SCAN_TILE);
+    for (uint32_t part = blockIdx.x; part < nparts; part += gridDim.x) {
+        const size_t base = (size_t)part * SCAN_TILE;
+        uint32_t s = 0;
+        for (int j = 0; j < SCAN_IPT; ++j) {
+            const size_t idx = base + (size_t)j * SCAN_BLOCK + threadIdx.x;
+            if (idx < len)
+                s += in[idx];
+        }
+        uint32_t total;
+        block_exclusive_scan<SCAN_BLOCK>(s, &total);
+        if (threadIdx.x == 0)
+            partial[part] = total;
     }
-    uint32_t total;
-    block_exclusive_scan<SCAN_BLOCK>(s, &total);
-    if (threadIdx.x == 0)
-        partial[blockIdx.x] = total;
 }
 
 // Single work-group exclusive scan of the partial sums (in place).
@@ -245,22 +257,25 @@ __global__ __launch_bounds__(SCAN_BLOCK) void k_scan_down(uint32_t *__restrict__
 {
     if (gated_off(gate))
         return;
-    // thread t owns SCAN_IPT consecutive elements of the block's tile
-    const size_t base = (size_t)blockIdx.x * SCAN_TILE + (size_t)threadIdx.x * SCAN_IPT;
-    uint32_t v[SCAN_IPT];
-    uint32_t s = 0;
+    const uint32_t nparts = (uint32_t)((len + SCAN_TILE - 1) / SCAN_TILE);
+    for (uint32_t part = blockIdx.x; part < nparts; part += gridDim.x) {
+        // thread t owns SCAN_IPT consecutive elements of the part
+        const size_t base = (size_t)part * SCAN_TILE + (size_t)threadIdx.x * SCAN_IPT;
+        uint32_t v[SCAN_IPT];
+        uint32_t s = 0;
 #pragma unroll
-    for (int j = 0; j < SCAN_IPT; ++j) {
-        v[j] = (base + j < len) ? data[base + j] : 0u;
-        s += v[j];
-    }
-    uint32_t total;
-    uint32_t run = block_exclusive_scan<SCAN_BLOCK>(s, &total) + partial[blockIdx.x];
+        for (int j = 0; j < SCAN_IPT; ++j) {
+            v[j] = (base + j < len) ? data[base + j] : 0u;
+            s += v[j];
+        }
+        uint32_t total;
+        uint32_t run = block_exclusive_scan<SCAN_BLOCK>(s, &total) + partial[part];
 #pragma unroll
-    for (int j = 0; j < SCAN_IPT; ++j) {
-        if (base + j < len)
-            data[base + j] = run;
-        run += v[j];
+        for (int j = 0; j < SCAN_IPT; ++j) {
+            if (base + j < len)
+                data[base + j] = run;
+            run += v[j];
+        }
     }
 }
 
@@ -301,17 +316,28 @@ __global__ __launch_bounds__(1024) void k_scan_one(uint32_t *__restrict__ data, 
     }
 }
 
+// Work-groups of a general-path launch over n blocks of work: the kernels
+// loop over their blocks, so a launch behind the incremental path (gated,
+// nearly always returning at once) stays small; an ungated one fills the chip.
+inline uint32_t general_grid(int64_t n, const Gate &gate)
+{
+    const int64_t cap = (int64_t)device_cus() * (gate.flag ? 2 : 8);
+    return (uint32_t)std::max<int64_t>(1, std::min<int64_t>(n, cap));
+}
+
 pcg_status exclusive_scan(uint32_t *data, size_t len, uint32_t *partial, Gate gate,
                           hipStream_t st)
 {
     if (len <= SCAN_ONE_MAX)
         return launch("sort_scan", k_scan_one, dim3(1), dim3(1024), 0, st, data, len, gate);
     const uint32_t nparts = (uint32_t)((len + SCAN_TILE - 1) / SCAN_TILE);
-    PCG_TRY(launch("sort_scan_reduce", k_scan_reduce, dim3(nparts), dim3(SCAN_BLOCK), 0, st,
+    PCG_TRY(launch("sort_scan_reduce", k_scan_reduce, dim3(general_grid(nparts, gate)),
+                   dim3(SCAN_BLOCK), 0, st,
                    (const uint32_t *)data, len, partial, gate));
     PCG_TRY(launch("sort_scan_partials", k_scan_partials, dim3(1), dim3(1024), 0, st, partial,
                    nparts, gate));
-    PCG_TRY(launch("sort_scan_down", k_scan_down, dim3(nparts), dim3(SCAN_BLOCK), 0, st, data,
+    PCG_TRY(launch("sort_scan_down", k_scan_down, dim3(general_grid(nparts, gate)),
+                   dim3(SCAN_BLOCK), 0, st, data,
                    len, (const uint32_t *)partial, gate));
     return PCG_OK;
 }
@@ -891,10 +917,12 @@ pcg_status radix_pass(const SortPlan &p, int shift, const uint32_t *kin, const u
                       uint32_t *kout, uint32_t *vout, const SortBuffers &b, Gate gate,
                       hipStream_t st)
 {
-    PCG_TRY(launch("sort_hist", k_radix_hist<BITS>, dim3(p.nblocks), dim3(SORT_BLOCK), 0, st,
+    PCG_TRY(launch("sort_hist", k_radix_hist<BITS>, dim3(general_grid(p.nblocks, gate)),
+                   dim3(SORT_BLOCK), 0, st,
                    kin, p.count, shift, b.counts, p.nblocks, gate));
     PCG_TRY(exclusive_scan(b.counts, p.counts_len, b.partial, gate, st));
-    PCG_TRY(launch("sort_scatter", k_radix_scatter<BITS>, dim3(p.nblocks), dim3(SORT_BLOCK), 0,
+    PCG_TRY(launch("sort_scatter", k_radix_scatter<BITS>, dim3(general_grid(p.nblocks, gate)),
+                   dim3(SORT_BLOCK), 0,
                    st, kin, vin, kout, vout, p.count, shift, (const uint32_t *)b.counts,
                    p.nblocks, gate));
     return PCG_OK;
@@ -921,8 +949,7 @@ template <int DIM, int ORDER>
 pcg_status launch_keys(int64_t count, const float *const x[3], const KeyGeom &g, uint32_t *keys,
                        Gate gate, hipStream_t st)
 {
-    const int64_t blocks = std::min<int64_t>((count + 255) / 256, (int64_t)device_cus() * 32);
-    return launch("sort_keys", k_tile_keys<DIM, ORDER>, dim3((unsigned)std::max<int64_t>(blocks, 1)),
+    return launch("sort_keys", k_tile_keys<DIM, ORDER>, dim3(general_grid((count + 255) / 256, gate)),
                   dim3(256), 0, st, count, x[0], DIM > 1 ? x[1] : nullptr,
                   DIM > 2 ? x[2] : nullptr, g, keys, gate);
 }
@@ -957,13 +984,13 @@ pcg_status general_path(const pcg_grid *grid, int order, const SortPlan &p, cons
         kin = kout;
         vin = vout;
     }
-    const int64_t oblocks = std::min<int64_t>((count + 1 + 255) / 256, (int64_t)device_cus() * 32);
-    PCG_TRY(launch("sort_offsets", k_tile_offsets, dim3((unsigned)oblocks), dim3(256), 0, st,
+    PCG_TRY(launch("sort_offsets", k_tile_offsets, dim3(general_grid((count + 1 + 255) / 256, gate)),
+                   dim3(256), 0, st,
                    (const uint32_t *)final_keys, count, p.ntiles, tile_offsets, gate));
     if (arr.n > 0) {
-        const int64_t blocks = std::min<int64_t>((count + 256 * PERM_EPT - 1) / (256 * PERM_EPT),
-                                                 (int64_t)device_cus() * 32);
-        PCG_TRY(launch("sort_permute", k_permute, dim3((unsigned)blocks), dim3(256), 0, st, arr,
+        const int64_t blocks = (count + 256 * PERM_EPT - 1) / (256 * PERM_EPT);
+        PCG_TRY(launch("sort_permute", k_permute, dim3(general_grid(blocks, gate)), dim3(256), 0,
+                       st, arr,
                        (const uint32_t *)perm, count, gate));
     }
     return PCG_OK;
@@ -1110,11 +1137,12 @@ pcg_status tile_sort_impl(const pcg_grid *grid, int32_t order, int32_t T, int64_
         a.flag = b.flag;
         const uint32_t chunk = INC_CHUNK;
         const uint32_t nwork = p.nchunks_max;  // >= ntiles + ceil(count / chunk)
-        if (p.ntiles <= CHUNK_ONE_BLOCK_MAX) {
+        if (p.ntiles <= CHUNK_PAR_MAX) {
             // one launch: the chunk layout, and the flag set from the check
             // that prev is a partition
-            PCG_TRY(launch("sort_inc_chunks", k_chunk_layout_one, dim3(1), dim3(CHUNK_SCAN_BLOCK),
-                           0, st, prev->tile_offsets, p.ntiles, count, chunk, b.cum, b.cmap,
+            PCG_TRY(launch("sort_inc_chunks", k_chunk_layout_par,
+                           dim3(chunk_par_blocks(p.nchunks_max)), dim3(CHUNK_SCAN_BLOCK), 0, st,
+                           prev->tile_offsets, p.ntiles, count, chunk, b.cum, b.cmap,
                            p.nchunks_max, (const uint32_t *)nullptr, 0u, b.flag));
         } else {
             PCG_TRY(launch("sort_inc_flag", k_set_flag, dim3(1), dim3(64), 0, st, b.flag, 0u));

@@ -167,6 +167,24 @@ pcg_status deposit_currents(const pcg_grid *grid, const pcg_particles *particles
                             const pcg_tile *tile, float *J, unsigned long long *n_escaped,
                             void *workspace, size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation, arguments and results as deposit_currents, with no workspace
+ * argument.  The work-item map deposit_currents keeps in its workspace lives
+ * in a static device array of PCG_NOALLOC_SCRATCH_BYTES bytes instead (each
+ * GPU the library runs on holds one until the process ends; looked up once
+ * per device).  A layout whose map needs more (pcg_deposit_workspace_bytes()
+ * above the maximum; it takes about 20 bytes per tile and 16 per 2048
+ * partitioned particles, so 4096 tiles and 67M particles need 0.6 MB) returns
+ * PCG_EWORKSPACE before anything is enqueued.  Every call on one GPU shares
+ * that GPU's array, so calls that overlap on one GPU (different streams or
+ * host threads) race; calls in one stream order are safe.  The array holds no
+ * state from one call to the next that a call relies on. */
+#define PCG_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+pcg_status deposit_currents_noalloc(const pcg_grid *grid, const pcg_particles *particles,
+                                    int32_t order, const pcg_tile *tile, float *J,
+                                    unsigned long long *n_escaped, void *stream);
+
 /* Bytes of device workspace deposit_currents_regroup needs (0 if invalid). */
 size_t pcg_deposit_regroup_workspace_bytes(const pcg_grid *grid, const pcg_tile *tile,
                                            int64_t count);

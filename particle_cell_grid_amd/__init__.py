@@ -56,6 +56,9 @@ _lib.pcg_deposit_workspace_bytes.restype = C.c_size_t
 _lib.deposit_currents.argtypes = [_P(Grid), _P(Particles), C.c_int32, _P(Tile), C.c_void_p,
                                   C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
 _lib.deposit_currents.restype = C.c_int32
+_lib.deposit_currents_noalloc.argtypes = [_P(Grid), _P(Particles), C.c_int32, _P(Tile),
+                                          C.c_void_p, C.c_void_p, C.c_void_p]
+_lib.deposit_currents_noalloc.restype = C.c_int32
 _lib.pcg_deposit_regroup_workspace_bytes.argtypes = [_P(Grid), _P(Tile), C.c_int64]
 _lib.pcg_deposit_regroup_workspace_bytes.restype = C.c_size_t
 _lib.deposit_currents_regroup.argtypes = [_P(Grid), _P(Particles), C.c_int32, _P(Tile),
@@ -243,6 +246,21 @@ def deposit_currents(dim: int, n: Sequence[int], order: int, x: List[torch.Tenso
                                _ptr(n_escaped), _ptr(workspace) if need else None,
                                int(workspace.numel()) if need else 0, _stream())
     _check(st, "deposit_currents")
+    return J
+
+
+def deposit_currents_noalloc(dim: int, n: Sequence[int], order: int, x: List[torch.Tensor],
+                             v: List[torch.Tensor], q: torch.Tensor, w: torch.Tensor,
+                             J: torch.Tensor, layout: Optional[Layout] = None,
+                             n_escaped: Optional[torch.Tensor] = None):
+    """deposit_currents without a workspace: the library's static scratch."""
+    g = make_grid(dim, n)
+    P = _particles(q.numel(), x, v, q, w)
+    tile = layout.to_c() if layout is not None else None
+    st = _lib.deposit_currents_noalloc(C.byref(g), C.byref(P), int(order),
+                                       C.byref(tile) if tile is not None else None, _ptr(J),
+                                       _ptr(n_escaped), _stream())
+    _check(st, "deposit_currents_noalloc")
     return J
 
 

@@ -16,6 +16,7 @@
 // (order+1)^dim x 3 global atomics -- used with no layout and for the tail.
 #include <algorithm>
 #include <climits>
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -1271,6 +1272,39 @@ pcg_status regroup_hook(void *ctx, const IncGeom &inc, const uint32_t *off, uint
 }
 
 }  // namespace
+
+// Scratch of deposit_currents_noalloc: its work-item map, in a file-scope
+// device array (every GPU the library runs on holds its own copy until the
+// process ends).  Calls on one GPU share it, so calls that overlap on one GPU
+// race.
+constexpr size_t NOALLOC_SCRATCH_BYTES = PCG_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current (the host-side name is not an address).
+pcg_status noalloc_scratch(const char *who, void **out)
+{
+    static std::mutex mu;
+    static void *ptr[64] = {nullptr};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return fail(PCG_EHIP, "%s: no current HIP device", who);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(PCG_EHIP, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s", who,
+                        dev, hipGetErrorString(e));
+        ptr[dev] = p;
+    }
+    *out = ptr[dev];
+    return PCG_OK;
+}
+
+}  // namespace
 }  // namespace pcg
 
 using namespace pcg;
@@ -1301,6 +1335,37 @@ pcg_status deposit_currents(const pcg_grid *grid, const pcg_particles *particles
     PCG_TRY(dispatch(grid->dim, order, true, plan.a, 0, 0, plan.nwork, plan.block, plan.lds, st));
     // tail pass ([TD] "Coverage: the tail pass")
     return dispatch(grid->dim, order, false, plan.a, tile->n_partitioned, count, 0, 0, 0, st);
+}
+
+// The entry point that allocates nothing: the workspace deposit_currents would
+// take comes from a file-scope device array instead.  In host code the array's
+// name is only a stand-in for the symbol; its device address (one per GPU) is
+// looked up once per device and used everywhere host code passes the array.
+pcg_status deposit_currents_noalloc(const pcg_grid *grid, const pcg_particles *particles,
+                                    int32_t order, const pcg_tile *tile, float *J,
+                                    unsigned long long *n_escaped, void *stream)
+{
+    const char *who = "deposit_currents_noalloc";
+    clear_error();
+    void *ws = nullptr;
+    if (tile) {
+        const size_t need = deposit_workspace_bytes(grid, tile);
+        if (need > NOALLOC_SCRATCH_BYTES)
+            return fail(PCG_EWORKSPACE,
+                        "%s: the layout needs %zu bytes of scratch, above the static %zu bytes "
+                        "(fewer tiles or particles, or deposit_currents with a workspace)",
+                        who, need, (size_t)NOALLOC_SCRATCH_BYTES);
+        // every argument check before the first HIP call (the workspace
+        // pointer stands in for the scratch; nothing reads it here)
+        TiledPlan probe;
+        PCG_TRY(prepare_deposit(who, grid, particles, order, tile, J, n_escaped,
+                                reinterpret_cast<void *>(uintptr_t(256)), NOALLOC_SCRATCH_BYTES, 0,
+                                &probe));
+        PCG_TRY(noalloc_scratch(who, &ws));
+    }
+    // the rest is deposit_currents with the static scratch as its workspace
+    return deposit_currents(grid, particles, order, tile, J, n_escaped, ws,
+                            ws ? (size_t)NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 size_t pcg_deposit_regroup_workspace_bytes(const pcg_grid *grid, const pcg_tile *tile,

@@ -346,3 +346,24 @@ def test_mass_and_sweep_validation(lib):
     assert lg(1024, 10, FAKE, FAKE, 50, 0.02, 0.005, None, FAKE, FAKE, None) == EINVAL  # target
     assert lg(1024, 10, FAKE, FAKE, 50, 0.02, 0.005, FAKE, None, FAKE, None) == EINVAL  # H
     assert lg(1024, 10, FAKE, FAKE, 50, 0.02, 0.005, FAKE, FAKE, None, None) == EINVAL  # dx0
+
+
+def test_deposit_noalloc_validation(lib):
+    """The entry point with a static scratch: a layout whose map exceeds it is
+    refused with PCG_EWORKSPACE, and bad arguments with the deposit's codes,
+    before any HIP call."""
+    lib.pcg_last_error.restype = C.c_char_p
+    dn = lib.deposit_currents_noalloc
+    P = particles(1000)
+
+    def call(g, order=1, tile=None, J=C.c_void_p(FAKE), P=P):
+        return dn(C.byref(g), C.byref(P), order, C.byref(tile) if tile else None, J, None, None)
+
+    big = grid(3, [256, 256, 256])                    # 16.8M cell tiles: a 335 MB map
+    assert call(big, tile=Tile(1, 1, 0, 0, 1000, FAKE)) == EWORKSPACE
+    assert b"static" in lib.pcg_last_error()
+    g = grid(3, [64, 64, 64])
+    assert call(g, tile=Tile(8, 1, 1, 0, 1000, FAKE), J=None) == EINVAL
+    assert call(g, order=3, tile=Tile(8, 1, 1, 0, 1000, FAKE)) == EUNSUPPORTED
+    assert call(g, tile=Tile(8, 1, 1, 0, 1001, FAKE)) == EINVAL     # n_partitioned > count
+    assert call(grid(0, [1, 1, 1])) == EINVAL

@@ -262,35 +262,89 @@ constexpr uint32_t QUEUE_MAX = 512;  // entries per work-group (12 KiB)
 constexpr int MQ_WORDS = 9;
 constexpr uint32_t MOVE_QUEUE_MAX = 1024;  // entries per work-group (36 KiB)
 
+// A particle's support in a work-group's window: its first support node b
+// (unwrapped), the weights, the scratch start s (periodic offset of b from the
+// window's low edge) and whether the stencil leaves the window.
+template <int ORDER>
+struct Support {
+    float W[3][ORDER + 1];
+    int b[3];
+    int s[3];
+    bool esc;
+};
+
+template <int DIM, int ORDER>
+__device__ __attribute__((always_inline)) inline Support<ORDER> support_of(const DepArgs &a,
+                                                                           const TileCtx &c,
+                                                                           const float *xs)
+{
+    Support<ORDER> sp;
+    const int last = a.T - 1 + 2 * a.D;  // largest scratch start that keeps the stencil inside
+    sp.esc = false;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        sp.b[k] = 0;
+        sp.s[k] = 0;
+    }
+#pragma unroll
+    for (int k = 0; k < DIM; ++k) {
+        sp.b[k] = shape_axis_raw<ORDER>(xs[k], a.nf[k], sp.W[k]);
+        // b in [-1, n], origin in [0, n - T], so one wrap suffices
+        sp.s[k] = wrap_once(sp.b[k] - c.origin[k] + a.D, a.n[k]);
+        sp.esc |= sp.s[k] > last;
+    }
+    return sp;
+}
+
+// Direction (0..26) of the tile holding a particle's first support node,
+// relative to the work-group's tile, from the support's scratch start: along
+// each axis the tile below (0), the same (1) or above (2).  Valid when every
+// used axis has at least three tiles and D < T and the particle moved at most
+// one tile: then s < D or s >= n - T + D means the tile below (the second
+// after a periodic wrap), s < D + T the same tile, else the tile above.
+template <int DIM, int ORDER>
+__device__ inline int support_dir(const DepArgs &a, const Support<ORDER> &sp)
+{
+    int dir = 0, mul = 1;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        int d = 1;
+        if (k < DIM) {
+            const int sk = sp.s[k];
+            d = (sk < a.D || sk >= a.n[k] - a.T + a.D) ? 0 : (sk < a.D + a.T ? 1 : 2);
+        }
+        dir += mul * d;
+        mul *= 3;
+    }
+    return dir;
+}
+
 // One particle: its support, then either the LDS scratch (mode MODE) or, if
 // its stencil leaves the window or its amplitude is outside the admitted
 // range, global atomics.  `again` marks the fallback pass: particles that
 // went to global memory in the first pass are skipped.  Returns 1 for an
 // escape (stencil outside the window) on the first pass.
 template <int DIM, int ORDER, int MODE, int TEC>
-__device__ __attribute__((always_inline)) inline uint32_t deposit_one(const DepArgs &a, const TileCtx &c, const Scratch &sc,
-                                       const float *xs, const float *vv, float cq, float cw,
-                                       bool again)
+__device__ __attribute__((always_inline)) inline uint32_t deposit_supported(
+    const DepArgs &a, const TileCtx &c, const Scratch &sc, const Support<ORDER> &sp,
+    const float *xs, const float *vv, float cq, float cw, bool again)
 {
     constexpr int M = ORDER + 1;
     constexpr int MY = DIM > 1 ? M : 1, MZ = DIM > 2 ? M : 1;
     const int TE = TEC > 0 ? TEC : c.TE;
     const int vol = TEC > 0 ? (DIM == 3 ? TEC * TEC * TEC : (DIM == 2 ? TEC * TEC : TEC)) : c.vol;
-    const int last = a.T - 1 + 2 * a.D;  // largest scratch start that keeps the stencil inside
     const float qw = cq * cw;
-
     float W[3][M];
-    int b[3] = {0, 0, 0};
-    int s[3] = {0, 0, 0};
-    bool esc = false;
+    int b[3], s[3];
 #pragma unroll
-    for (int k = 0; k < DIM; ++k) {
-        b[k] = shape_axis_raw<ORDER>(xs[k], a.nf[k], W[k]);
-        // scratch start: periodic offset of the base node from the window's low
-        // edge (b in [-1, n], origin in [0, n - T], so one wrap suffices)
-        s[k] = wrap_once(b[k] - c.origin[k] + a.D, a.n[k]);
-        esc |= s[k] > last;
+    for (int k = 0; k < 3; ++k) {
+        b[k] = sp.b[k];
+        s[k] = sp.s[k];
+#pragma unroll
+        for (int j = 0; j < M; ++j)
+            W[k][j] = k < DIM ? sp.W[k][j] : 1.0f;
     }
+    const bool esc = sp.esc;
     const float qws = qw * c.scale;
     float amp[3] = {qws * vv[0], qws * vv[1], qws * vv[2]};
     const float amax = fmaxf(fabsf(amp[0]), fmaxf(fabsf(amp[1]), fabsf(amp[2])));
@@ -372,6 +426,15 @@ __device__ __attribute__((always_inline)) inline uint32_t deposit_one(const DepA
         }
     }
     return 0u;
+}
+
+template <int DIM, int ORDER, int MODE, int TEC>
+__device__ __attribute__((always_inline)) inline uint32_t deposit_one(const DepArgs &a, const TileCtx &c, const Scratch &sc,
+                                       const float *xs, const float *vv, float cq, float cw,
+                                       bool again)
+{
+    const Support<ORDER> sp = support_of<DIM, ORDER>(a, c, xs);
+    return deposit_supported<DIM, ORDER, MODE, TEC>(a, c, sc, sp, xs, vv, cq, cw, again);
 }
 
 // Global node index of scratch node i of the window (periodic wrap).
@@ -741,6 +804,12 @@ __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
         }
         uint32_t *run = s_run[MOVE ? wave : 0];
         uint32_t esc_count = 0;
+        // the direction from the support's window position (support_dir)
+        // where every used axis has three tiles or more
+        bool fastdir = a.D < a.T;
+#pragma unroll
+        for (int k = 0; k < DIM; ++k)
+            fastdir = fastdir && a.nt[k] >= 3;
         for (uint32_t j = wave; j < nsub; j += nwaves) {
             uint32_t clo, chi;
             if (move) {
@@ -778,11 +847,13 @@ __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
                 for (int u = 0; u < UW; ++u) {
                     const uint32_t p = base + u * WAVE + lane;
                     const bool valid = p < chi;
+                    const Support<ORDER> sp = support_of<DIM, ORDER>(a, cx, gx[u]);
                     if (move) {
                         // wave-uniform: the slot comes from the whole wave's
                         // directions
-                        const int d = particle_dir<DIM, ORDER>(gx[u][0], gx[u][1], gx[u][2],
-                                                               m.inc.g, tsc);
+                        const int d = fastdir ? support_dir<DIM, ORDER>(a, sp)
+                                              : particle_dir<DIM, ORDER>(gx[u][0], gx[u][1],
+                                                                         gx[u][2], m.inc.g, tsc);
                         const bool ok = valid && d >= 0;  // d < 0 cannot occur: flag clear
                         const uint32_t pos = walk_slot(run, d, ok);
                         if (ok && pos < (uint64_t)m.inc.count) {
@@ -820,8 +891,8 @@ __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
                         }
                     }
                     if (valid)
-                        esc_count += deposit_one<DIM, ORDER, MODE, TEC>(a, cx, sc, gx[u], gv[u],
-                                                                        gq[u], gw[u], false);
+                        esc_count += deposit_supported<DIM, ORDER, MODE, TEC>(
+                            a, cx, sc, sp, gx[u], gv[u], gq[u], gw[u], false);
                 }
             }
         }

@@ -137,18 +137,36 @@ __device__ inline int particle_dir(float x0, float x1, float x2, const KeyGeom &
 // slot of each lane's particle (lanes with ok set; dir in [0, NDIR)), from the
 // wave's next free slot per direction run[] in LDS, advanced past this step.
 // Particles keep their order within each direction, so the slots are those of
-// a stable counting sort.  Wave-uniform control flow only.
+// a stable counting sort.  Most particles stay in their tile: one ballot ranks
+// those, and the few leavers are ranked one direction at a time (a loop over
+// the distinct directions present, wave-uniform).  Wave-uniform control flow
+// only.
 __device__ inline uint32_t walk_slot(uint32_t *run, int dir, bool ok)
 {
-    const uint32_t d = ok ? (uint32_t)dir : 0u;
-    const uint64_t peers = peer_mask<5>(d, ok);
-    const uint32_t rank = (uint32_t)__popcll(peers & lanemask_lt());
-    const uint32_t before = run[d];
+    const uint64_t lt = lanemask_lt();
+    const bool stays = ok && dir == DIR_STAY;
+    const uint64_t stay = __ballot(stays);
+    uint64_t left = __ballot(ok && dir != DIR_STAY);
+    const uint32_t stay_base = run[DIR_STAY];
+    uint32_t pos = stay_base + (uint32_t)__popcll(stay & lt);
+    while (left) {
+        const int l = __builtin_amdgcn_readfirstlane(__ffsll((long long)left) - 1);
+        const int d0 = __builtin_amdgcn_readlane(dir, l);
+        const bool mine = ok && dir == d0;
+        const uint64_t m = __ballot(mine);
+        const uint32_t b = run[d0];
+        if (mine)
+            pos = b + (uint32_t)__popcll(m & lt);
+        __builtin_amdgcn_wave_barrier();
+        if (lane_id() == l)
+            run[d0] = b + (uint32_t)__popcll(m);
+        __builtin_amdgcn_wave_barrier();
+        left &= ~m;
+    }
+    if (lane_id() == 0 && stay)
+        run[DIR_STAY] = stay_base + (uint32_t)__popcll(stay);
     __builtin_amdgcn_wave_barrier();
-    if (ok && rank == 0)
-        run[d] = before + (uint32_t)__popcll(peers);
-    __builtin_amdgcn_wave_barrier();
-    return before + rank;
+    return pos;
 }
 
 // Output slot base of every direction of incremental chunk `chunk` (global

@@ -439,11 +439,18 @@ def bench_zigzag(args, torch, pcg):
     def deposit():
         pcg.deposit_currents_zigzag(n, x, xpd, q, w, J, lay, esc)
 
-    def step():
+    def unfused():
         J.zero_()
         deposit()
         pcg.pcg_tile_sort(3, n, 1, T, x, cur, outs=nxt, want_perm=False, want_keys=False,
                           tile_offsets=off1, workspace=sws, prev=lay)
+
+    def step():
+        # deposit with the layout of the previous positions and regroup by the
+        # new ones, in one pass over the particle arrays
+        J.zero_()
+        pcg.deposit_currents_zigzag_regroup(n, x, xpd, q, w, J, lay, cur, outs=nxt,
+                                            tile_offsets=off1, workspace=sws)
 
     progress("timing steps")
     ms, wall, kt = time_steps(torch, pcg, step, args.steps, args.warmup)
@@ -456,14 +463,23 @@ def bench_zigzag(args, torch, pcg):
     alg = {
         # x, x_prev, q, w read once + J read-modify-write
         "zigzag_tiled": cnt * 8 * 4 + 2 * jbytes,
+        # the same, plus every field written once to its new slot
+        "zigzag_regroup": cnt * 2 * 8 * 4 + 2 * jbytes,
         "sort_inc_count": cnt * 3 * 4,
         "sort_inc_move": cnt * 2 * 8 * 4,
     }
     kernels = kernel_table(kt, args.steps, alg, gated=True)
-    roof = roofline_entry(kt, "zigzag_tiled", bytes_per_launch=alg["zigzag_tiled"])
+    roof = roofline_entry(kt, "zigzag_regroup", bytes_per_launch=alg["zigzag_regroup"])
     if roof:
-        roof["traffic"] = measured_traffic("zigzag_tiled", "zigzag3d_128_ppc32")
+        roof["traffic"] = measured_traffic("zigzag_regroup", "zigzag3d_128_ppc32")
     extra = dict(escaped_particles=n_esc)
+    extra["unfused_step_ms"] = round(time_plain(torch, unfused, args.steps), 4)
+    _, _, kt_dep = time_steps(torch, pcg, lambda: (J.zero_(), deposit()), args.steps, 1)
+    extra["deposit_roofline"] = roofline_entry(kt_dep, "zigzag_tiled",
+                                               bytes_per_launch=alg["zigzag_tiled"])
+    if extra["deposit_roofline"]:
+        extra["deposit_roofline"]["traffic"] = measured_traffic("zigzag_tiled",
+                                                                "zigzag3d_128_ppc32")
     progress("timing the step with cold caches")
     evict = torch.empty(EVICT_BYTES, dtype=torch.uint8, device=dev)
     extra["cold_step_ms"] = time_cold(torch, step, args.steps, evict)
@@ -512,8 +528,8 @@ def bench_zigzag(args, torch, pcg):
     config = dict(workload="3-D charge-conserving zigzag current deposit + tile sort, 128^3 "
                            "periodic, 32 ppc, each particle moved by its velocity",
                   particles=cnt, grid=n, tile=T, drift=D,
-                  step="zero J + tiled zigzag deposit with the layout of the previous "
-                       "positions + incremental tile sort on the new positions")
+                  step="zero J + fused tiled zigzag deposit (layout of the previous "
+                       "positions) and regroup (incremental tile sort on the new positions)")
     return dict(value=cnt / (ms * 1e-3), ms=ms, wall=wall, dtype="f32", config=config,
                 roofline=roof, kernels=kernels, extra=extra, cpu=cpu, unit="particles/s")
 

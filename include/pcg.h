@@ -253,6 +253,37 @@ pcg_status deposit_currents_zigzag(const pcg_grid *grid, const pcg_particles *pa
                                    const float *const x_prev[3], const pcg_tile *tile, float *J,
                                    unsigned long long *n_escaped, void *stream);
 
+/* The zigzag deposit and the next sort in one pass over the particle data
+ * ([TD] "How a tile deposit runs" followed by "The tile-based spatial sort",
+ * the sort at the end of a step): the same results as
+ *     deposit_currents_zigzag(grid, particles, x_prev, tile, J, n_escaped, ...);
+ *     pcg_tile_sort(grid, 1, tile->T, particles->count, particles->x,
+ *                   n_arrays, in_arrays, out_arrays, NULL, NULL,
+ *                   tile_offsets, tile, ...);
+ * (J and n_escaped accumulated as there; out_arrays and tile_offsets equal to
+ * the sort's, bit for bit).  When `tile` covers every particle, in_arrays are
+ * exactly x[0..3), x_prev[0..3), q, w of the deposit, in that order, and the
+ * window holds int64 sums, the deposit kernel makes the sort's move from the
+ * values it has loaded (one work-group per tile, its waves walking the sort's
+ * chunks in order), so the particle arrays are read once instead of twice.
+ * `tile` is the layout the particles are grouped by (required); the sort uses
+ * it as `prev`, and a particle that moved further than one tile, or a layout
+ * that is not a partition, sends the regrouping to the general sort path
+ * (decided on the device; the deposit is unaffected).  Otherwise the two
+ * calls run one after the other.  in_arrays / out_arrays as in pcg_tile_sort
+ * (out of place); tile_offsets: device uint32 [ntiles + 1], the new layout,
+ * distinct from tile->tile_offsets.  workspace: at least
+ * pcg_sort_workspace_bytes(grid, count, tile->T) bytes, 256-byte aligned.
+ * Errors: as for the two calls; every check runs before anything is
+ * enqueued. */
+pcg_status deposit_currents_zigzag_regroup(const pcg_grid *grid, const pcg_particles *particles,
+                                           const float *const x_prev[3], const pcg_tile *tile,
+                                           float *J, unsigned long long *n_escaped,
+                                           int32_t n_arrays, const float *const in_arrays[],
+                                           float *const out_arrays[], uint32_t *tile_offsets,
+                                           void *workspace, size_t workspace_bytes,
+                                           void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* ECSIM mass matrix  ([MM] §2.1 Eq.(4)-(6), §2.2 Eq.(9)-(11), §3)           */
 /* ------------------------------------------------------------------------ */

@@ -69,6 +69,11 @@ _lib.deposit_currents_regroup.restype = C.c_int32
 _lib.deposit_currents_zigzag.argtypes = [_P(Grid), _P(Particles), C.c_void_p, _P(Tile),
                                          C.c_void_p, C.c_void_p, C.c_void_p]
 _lib.deposit_currents_zigzag.restype = C.c_int32
+_lib.deposit_currents_zigzag_regroup.argtypes = [_P(Grid), _P(Particles), C.c_void_p,
+                                                 _P(Tile), C.c_void_p, C.c_void_p, C.c_int32,
+                                                 C.c_void_p, C.c_void_p, C.c_void_p,
+                                                 C.c_void_p, C.c_size_t, C.c_void_p]
+_lib.deposit_currents_zigzag_regroup.restype = C.c_int32
 _lib.pcg_mass_workspace_bytes.argtypes = [_P(Grid)]
 _lib.pcg_mass_workspace_bytes.restype = C.c_size_t
 _lib.assemble_mass_matrix.argtypes = [_P(Grid), _P(Particles), C.c_void_p, C.c_void_p, _P(Tile),
@@ -319,6 +324,40 @@ def deposit_currents_zigzag(n: Sequence[int], x: List[torch.Tensor], x_prev: Lis
                                       _ptr(n_escaped), _stream())
     _check(st, "deposit_currents_zigzag")
     return J
+
+
+def deposit_currents_zigzag_regroup(n: Sequence[int], x: List[torch.Tensor],
+                                    x_prev: List[torch.Tensor], q: torch.Tensor,
+                                    w: torch.Tensor, J: torch.Tensor, layout: Layout,
+                                    arrays: Sequence[torch.Tensor],
+                                    outs: Optional[List[torch.Tensor]] = None,
+                                    tile_offsets: Optional[torch.Tensor] = None,
+                                    n_escaped: Optional[torch.Tensor] = None,
+                                    workspace: Optional[torch.Tensor] = None):
+    """J += the zigzag current of each move from x_prev to x with `layout`, and
+    `arrays` regrouped by the tiles of x into `outs` / `tile_offsets` (the next
+    layout), in one pass.  Returns (tile_offsets, outs)."""
+    g = make_grid(3, n)
+    count = int(q.numel())
+    P = _particles(count, x, None, q, w)
+    xp = (C.c_void_p * 3)(*[x_prev[k].data_ptr() for k in range(3)])
+    tile = layout.to_c()
+    dev = q.device
+    if tile_offsets is None:
+        tile_offsets = torch.empty(ntiles(3, n, layout.T) + 1, dtype=torch.int32, device=dev)
+    if outs is None:
+        outs = [torch.empty_like(a) for a in arrays]
+    need = pcg_sort_workspace_bytes(3, n, count, layout.T)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    na = len(arrays)
+    ins = (C.c_void_p * max(na, 1))(*[a.data_ptr() for a in arrays])
+    ous = (C.c_void_p * max(na, 1))(*[o.data_ptr() for o in outs])
+    st = _lib.deposit_currents_zigzag_regroup(C.byref(g), C.byref(P), xp, C.byref(tile), _ptr(J),
+                                              _ptr(n_escaped), na, ins, ous, _ptr(tile_offsets),
+                                              _ptr(workspace), int(workspace.numel()), _stream())
+    _check(st, "deposit_currents_zigzag_regroup")
+    return tile_offsets, outs
 
 
 def pcg_mass_workspace_bytes(n: Sequence[int]) -> int:

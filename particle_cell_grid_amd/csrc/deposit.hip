@@ -73,13 +73,6 @@ struct MoveArgs {
     uint32_t group;       // incremental chunks per deposit work item
 };
 
-// Start of chunk c of a tile slice of L particles split into nch balanced
-// chunks (the split of the incremental sort).
-__device__ inline uint32_t chunk_start(uint32_t c, uint32_t L, uint32_t nch)
-{
-    return (uint32_t)(((uint64_t)L * c) / nch);
-}
-
 // One axis of the shape: first support node b, unwrapped (in [-1, n] for a
 // coordinate clamped into [0, n]), and order+1 weights.
 template <int ORDER>

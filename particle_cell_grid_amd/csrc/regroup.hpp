@@ -169,6 +169,13 @@ __device__ inline uint32_t walk_slot(uint32_t *run, int dir, bool ok)
     return pos;
 }
 
+// Start of chunk c of a tile slice of L particles split into nch balanced
+// chunks (the split of the incremental sort).
+__device__ inline uint32_t chunk_start(uint32_t c, uint32_t L, uint32_t nch)
+{
+    return (uint32_t)(((uint64_t)L * c) / nch);
+}
+
 // Output slot base of every direction of incremental chunk `chunk` (global
 // chunk number) of source tile `tile`: off[new tile] + the tile's prefix among
 // the new tile's sources + the chunk's prefix among the tile's chunks.

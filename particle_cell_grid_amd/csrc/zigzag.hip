@@ -24,6 +24,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "regroup.hpp"
 
 namespace pcg {
 namespace {
@@ -224,6 +225,81 @@ __device__ inline unsigned long long to_fixed(float x)
     return (unsigned long long)(long long)(int32_t)x;
 }
 
+// One particle's 24 contributions into the window (ws: its first node per
+// axis, unwrapped; TE nodes per axis), scaled by 2^k_scale when FIXED; a
+// particle whose stencil does not fit (a move over more than a neighbouring
+// cell, or a layout more than D cells stale) goes to global memory on the
+// first pass and is skipped on a second.  Returns 1 for such an escape on the
+// first pass.
+template <bool FIXED, typename Acc>
+__device__ __attribute__((always_inline)) inline uint32_t window_add(
+    const ZzArgs &m, Acc *win, int TE, int vol, const int *ws, Move mv, int k_scale, bool first)
+{
+    const int stride[3] = {1, TE, TE * TE};
+    // the stencil fits if its last node lies in the window
+    int l0[3];
+    bool fits = true;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const int64_t d = window_coord(mv.lo[k], ws[k], m.n[k]);
+        l0[k] = (int)d;
+        fits = fits && d >= 0 && mv.ext[k] >= 1 && mv.ext[k] <= 2 && d + mv.ext[k] < TE;
+    }
+    if (!fits) {
+        if (first)
+            deposit_global(m, mv);
+        return first ? 1u : 0u;
+    }
+    if (FIXED)
+        mv.qw = ldexpf(mv.qw, k_scale);  // every contribution comes out scaled
+    // window slot of each segment's cell corner
+    int base[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+        base[s] = (l0[0] + mv.cell[s][0] - mv.lo[0]) +
+                  TE * ((l0[1] + mv.cell[s][1] - mv.lo[1]) + TE * (l0[2] + mv.cell[s][2] - mv.lo[2]));
+    auto add = [&](int s, int c, int j, float v) {
+        const int k1 = c == 0 ? 1 : 0, k2 = c == 2 ? 1 : 2;
+        Acc *a = &win[base[s] + c * vol + (j & 1) * stride[k1] + (j >> 1) * stride[k2]];
+        if constexpr (FIXED)
+            atomicAdd(a, to_fixed(v));
+        else
+            atomicAdd(a, v);
+    };
+    // a move that crosses no cell boundary is one segment when FIXED
+    // (make_move<true>); its second, empty one is not added
+    const bool same = mv.cell[0][0] == mv.cell[1][0] && mv.cell[0][1] == mv.cell[1][1] &&
+                      mv.cell[0][2] == mv.cell[1][2];
+    for_each_in_segment(mv, 0, [&](int c, int j, const int *, float v) { add(0, c, j, v); });
+    if (!(FIXED && same))
+        for_each_in_segment(mv, 1, [&](int c, int j, const int *, float v) { add(1, c, j, v); });
+    return 0u;
+}
+
+// Adds the window to J (one atomic per non-zero slot, periodic wrap).
+template <bool FIXED, typename Acc>
+__device__ inline void flush_window(const ZzArgs &m, const Acc *win, int TE, int vol,
+                                    const int *ws, int k_scale)
+{
+    const int64_t ng = (int64_t)m.n[0] * m.n[1] * m.n[2];
+    for (int i = threadIdx.x; i < 3 * vol; i += blockDim.x) {
+        const Acc a = win[i];
+        if (a == 0)
+            continue;
+        float v;
+        if constexpr (FIXED)
+            v = (float)ldexp((double)(long long)a, -k_scale);
+        else
+            v = a;
+        const int c = i / vol, r = i - c * vol;
+        const int lx = r % TE, ly = (r / TE) % TE, lz = r / (TE * TE);
+        const int64_t idx = wrapn(ws[0] + lx, m.n[0]) +
+                            (int64_t)m.n[0] * (wrapn(ws[1] + ly, m.n[1]) +
+                                               (int64_t)m.n[1] * wrapn(ws[2] + lz, m.n[2]));
+        atomic_add_f32(&m.J[c * ng + idx], v);
+    }
+}
+
 // One work-group per tile.  FIXED: the window holds int64 sums of the
 // contributions scaled by 2^k (exact and independent of the order of the adds;
 // LDS integer atomics run over twenty times the rate of float ones on this
@@ -248,7 +324,6 @@ __global__ __launch_bounds__(512) void k_zigzag_tiled(ZzArgs m)
     __shared__ float red[8];  // one per wave
     const int TE = TEC ? TEC : m.TE;
     const int vol = TE * TE * TE;
-    const int stride[3] = {1, TE, TE * TE};
     const uint32_t t = blockIdx.x;
     const int tc[3] = {(int)(t % (uint32_t)m.nt[0]), (int)((t / (uint32_t)m.nt[0]) % (uint32_t)m.nt[1]),
                        (int)(t / ((uint32_t)m.nt[0] * (uint32_t)m.nt[1]))};
@@ -275,51 +350,9 @@ __global__ __launch_bounds__(512) void k_zigzag_tiled(ZzArgs m)
             const Raw cur = next;
             if (p + blockDim.x < hi)
                 next = load_raw(m, p + blockDim.x);
-            Move mv = make_move<FIXED>(cur);
+            const Move mv = make_move<FIXED>(cur);
             seen = fmaxf(seen, fabsf(mv.qw));
-            // the stencil fits if its last node lies in the window (a move over
-            // more than a neighbouring cell is sent to global memory)
-            int l0[3];
-            bool fits = true;
-#pragma unroll
-            for (int k = 0; k < 3; ++k) {
-                const int64_t d = window_coord(mv.lo[k], ws[k], m.n[k]);
-                l0[k] = (int)d;
-                fits = fits && d >= 0 && mv.ext[k] >= 1 && mv.ext[k] <= 2 && d + mv.ext[k] < TE;
-            }
-            if (!fits) {
-                if (first) {
-                    deposit_global(m, mv);
-                    ++escaped;
-                }
-                continue;
-            }
-            if (FIXED)
-                mv.qw = ldexpf(mv.qw, k_scale);  // every contribution comes out scaled
-            // window slot of each segment's cell corner
-            int base[2];
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                base[s] = (l0[0] + mv.cell[s][0] - mv.lo[0]) +
-                          TE * ((l0[1] + mv.cell[s][1] - mv.lo[1]) +
-                                TE * (l0[2] + mv.cell[s][2] - mv.lo[2]));
-            auto add = [&](int s, int c, int j, float v) {
-                const int k1 = c == 0 ? 1 : 0, k2 = c == 2 ? 1 : 2;
-                Acc *a = &win[base[s] + c * vol + (j & 1) * stride[k1] + (j >> 1) * stride[k2]];
-                if constexpr (FIXED)
-                    atomicAdd(a, to_fixed(v));
-                else
-                    atomicAdd(a, v);
-            };
-            // a move that crosses no cell boundary is one segment when FIXED
-            // (above); its second, empty one is not added
-            const bool same = mv.cell[0][0] == mv.cell[1][0] && mv.cell[0][1] == mv.cell[1][1] &&
-                              mv.cell[0][2] == mv.cell[1][2];
-            for_each_in_segment(mv, 0, [&](int c, int j, const int *, float v) { add(0, c, j, v); });
-            if (!(FIXED && same))
-                for_each_in_segment(mv, 1, [&](int c, int j, const int *, float v) {
-                    add(1, c, j, v);
-                });
+            escaped += window_add<FIXED>(m, win, TE, vol, ws, mv, k_scale, first);
         }
         __syncthreads();
         return seen;
@@ -346,25 +379,223 @@ __global__ __launch_bounds__(512) void k_zigzag_tiled(ZzArgs m)
         k_scale = fixed_scale(seen);
     }
 
-    const int64_t ng = (int64_t)m.n[0] * m.n[1] * m.n[2];
-    for (int i = threadIdx.x; i < 3 * vol; i += blockDim.x) {
-        const Acc a = win[i];
-        if (a == 0)
-            continue;
-        float v;
-        if constexpr (FIXED)
-            v = (float)ldexp((double)(long long)a, -k_scale);
-        else
-            v = a;
-        const int c = i / vol, r = i - c * vol;
-        const int lx = r % TE, ly = (r / TE) % TE, lz = r / (TE * TE);
-        const int64_t idx = wrapn(ws[0] + lx, m.n[0]) +
-                            (int64_t)m.n[0] * (wrapn(ws[1] + ly, m.n[1]) +
-                                               (int64_t)m.n[1] * wrapn(ws[2] + lz, m.n[2]));
-        atomic_add_f32(&m.J[c * ng + idx], v);
-    }
+    flush_window<FIXED>(m, win, TE, vol, ws, k_scale);
     if (m.n_escaped && escaped)
         atomicAdd(m.n_escaped, (unsigned long long)escaped);
+}
+
+// ------------------------------------------------------------------ fused pass
+
+// The regrouping half of the fused pass: every particle the deposit loads is
+// also written to its slot in the next layout (keyed on the new positions),
+// the slot the incremental tile sort's move stage would give it.
+struct ZzMoveArgs {
+    IncGeom inc;
+    const uint32_t *off;  // the new tile offsets
+    float *out[8];        // new arrays of x[0..3), x_prev[0..3), q, w
+    uint32_t mcap;        // entries of the LDS queue of particles that change tile
+};
+
+constexpr int ZZ_MQ_WORDS = 9;               // new slot, then the eight fields
+constexpr uint32_t ZZ_MOVE_QUEUE_MAX = 1024;  // entries per work-group (36 KiB)
+constexpr int ZZ_WAVES = 8;                  // most waves of a work-group
+constexpr int ZZ_UW = 2;                     // particles per lane in flight in the walk
+
+// One work-group per tile of the layout the particles are grouped by; its
+// waves walk the tile's incremental chunks in order (wave j takes chunks j,
+// j + waves, ...), 64 ZZ_UW particles at a time.  Each particle gets its slot
+// in the new layout from its direction and the wave's running count per
+// direction (walk_slot, a stable counting sort), is stored there (or staged in
+// LDS if it changes tile, and written with the work-group's other leavers
+// after the walk), and is deposited into the window as k_zigzag_tiled<true>
+// does.  If the device flag says the incremental path does not hold, the
+// kernel deposits only (the general sort then regroups).  The scale check and
+// rerun are those of k_zigzag_tiled; the rerun deposits without moving.
+template <int TEC>
+__global__ __launch_bounds__(ZZ_WAVES * WAVE) void k_zigzag_regroup(ZzArgs m, ZzMoveArgs mv)
+{
+    using Acc = unsigned long long;
+    extern __shared__ __align__(8) unsigned char lds_raw[];
+    Acc *win = reinterpret_cast<Acc *>(lds_raw);  // [3][TE][TE][TE]
+    const int TE = TEC ? TEC : m.TE;
+    const int vol = TE * TE * TE;
+    float *mq = reinterpret_cast<float *>(lds_raw + (size_t)3 * vol * sizeof(Acc));
+    __shared__ float red[ZZ_WAVES];
+    __shared__ uint32_t s_run[ZZ_WAVES][32];
+    __shared__ uint32_t s_mn;
+    const uint32_t t = blockIdx.x;
+    int tc[3];
+    tile_coords(t, mv.inc.g, tc);
+    int ws[3];  // window start (unwrapped node index)
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+        ws[k] = tc[k] * m.T - m.D - 1;
+    const int64_t lo = std::min<int64_t>(m.offsets[t], m.n_part);
+    const int64_t hi = std::max<int64_t>(lo, std::min<int64_t>(m.offsets[t + 1], m.n_part));
+    const bool move = *mv.inc.flag == 0u;  // the same value in every lane
+    if (threadIdx.x == 0)
+        s_mn = 0;
+    // the scale: twice the largest |q w| of the first particle of every thread
+    float first_qw = 0.0f;
+    if (lo + (int64_t)threadIdx.x < hi)
+        first_qw = fabsf(m.q[lo + threadIdx.x] * m.w[lo + threadIdx.x]);
+    const float assumed = 2.0f * block_max(first_qw, red);
+    int k_scale = fixed_scale(assumed);
+    for (int i = threadIdx.x; i < 3 * vol; i += blockDim.x)
+        win[i] = 0;
+    __syncthreads();
+
+    uint32_t escaped = 0;
+    float seen = 0.0f;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), lane = lane_id();
+    const int nwaves = blockDim.x / WAVE;
+    const uint32_t p0 = (uint32_t)lo, L = (uint32_t)(hi - lo);
+    uint32_t nch = (L + INC_CHUNK - 1) / INC_CHUNK, g0 = 0;
+    if (move) {
+        g0 = mv.inc.cum[t];
+        nch = mv.inc.cum[t + 1] - g0;
+    }
+    uint32_t *run = s_run[wave];
+    for (uint32_t j = wave; j < nch; j += nwaves) {
+        const uint32_t clo = p0 + chunk_start(j, L, nch), chi = p0 + chunk_start(j + 1, L, nch);
+        if (clo >= chi)
+            continue;
+        if (move) {
+            if (lane < NDIR)
+                run[lane] = move_base(mv.inc, mv.off, t, g0 + j, lane);
+            __builtin_amdgcn_wave_barrier();
+        }
+        // no branch around the loads: a lane past the chunk reloads its last
+        // particle (never used)
+        Raw nx[ZZ_UW];
+        auto load_group = [&](uint32_t base) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < ZZ_UW; ++u)
+                nx[u] = load_raw(m, min(base + u * WAVE + lane, chi - 1));
+        };
+        load_group(clo);
+        for (uint32_t base = clo; base < chi; base += ZZ_UW * WAVE) {
+            Raw cur[ZZ_UW];
+#pragma unroll
+            for (int u = 0; u < ZZ_UW; ++u)
+                cur[u] = nx[u];
+            load_group(base + ZZ_UW * WAVE);
+#pragma unroll
+            for (int u = 0; u < ZZ_UW; ++u)
+                asm volatile("" ::"v"(cur[u].a[0]), "v"(cur[u].a[1]), "v"(cur[u].a[2]),
+                             "v"(cur[u].b[0]), "v"(cur[u].b[1]), "v"(cur[u].b[2]), "v"(cur[u].q),
+                             "v"(cur[u].w));
+#pragma unroll
+            for (int u = 0; u < ZZ_UW; ++u) {
+                const uint32_t p = base + u * WAVE + lane;
+                const bool valid = p < chi;
+                if (move) {
+                    // wave-uniform: the slot comes from the whole wave's directions
+                    const int d = particle_dir<3, 1>(cur[u].b[0], cur[u].b[1], cur[u].b[2],
+                                                     mv.inc.g, tc);
+                    const bool ok = valid && d >= 0;  // d < 0 cannot occur: the flag is clear
+                    const uint32_t pos = walk_slot(run, d, ok);
+                    if (ok && pos < (uint64_t)mv.inc.count) {
+                        const float f[8] = {cur[u].b[0], cur[u].b[1], cur[u].b[2], cur[u].a[0],
+                                            cur[u].a[1], cur[u].a[2], cur[u].q, cur[u].w};
+                        bool staged = false;
+                        if (d != DIR_STAY && mv.mcap) {
+                            const uint32_t slot = atomicAdd(&s_mn, 1u);
+                            if (slot < mv.mcap) {
+                                float *e = mq + (size_t)slot * ZZ_MQ_WORDS;
+                                reinterpret_cast<uint32_t *>(e)[0] = pos;
+#pragma unroll
+                                for (int k = 0; k < 8; ++k)
+                                    e[1 + k] = f[k];
+                                staged = true;
+                            }
+                        }
+                        if (!staged) {
+#pragma unroll
+                            for (int k = 0; k < 8; ++k)
+                                mv.out[k][pos] = f[k];
+                        }
+                    }
+                }
+                if (valid) {
+                    const Move mm = make_move<true>(cur[u]);
+                    seen = fmaxf(seen, fabsf(mm.qw));
+                    escaped += window_add<true>(m, win, TE, vol, ws, mm, k_scale, true);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // the staged leavers, one per thread
+    {
+        const uint32_t n = min(s_mn, mv.mcap);
+        for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
+            const float *e = mq + (size_t)i * ZZ_MQ_WORDS;
+            const uint32_t pos = reinterpret_cast<const uint32_t *>(e)[0];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                mv.out[k][pos] = e[1 + k];
+        }
+    }
+    const float seen_all = block_max(seen, red);
+    if (seen_all > assumed) {
+        // the bound may not have held: deposit again with the true maximum
+        // (no moves: those are done; escapes, already deposited, skipped)
+        k_scale = fixed_scale(seen_all);
+        for (int i = threadIdx.x; i < 3 * vol; i += blockDim.x)
+            win[i] = 0;
+        __syncthreads();
+        for (int64_t p = lo + threadIdx.x; p < hi; p += blockDim.x)
+            window_add<true>(m, win, TE, vol, ws, make_move<true>(load_raw(m, p)), k_scale, false);
+        __syncthreads();
+    }
+    flush_window<true>(m, win, TE, vol, ws, k_scale);
+    if (m.n_escaped && escaped)
+        atomicAdd(m.n_escaped, (unsigned long long)escaped);
+}
+
+// The fused pass's move hook: it replaces the incremental sort's move kernel.
+struct ZzRegroupCtx {
+    ZzArgs m;
+    size_t lds;       // window bytes
+    uint32_t ntiles;
+};
+
+pcg_status zz_regroup_hook(void *ctx, const IncGeom &inc, const uint32_t *off, uint32_t,
+                           const PermArgs &arr, hipStream_t st)
+{
+    const ZzRegroupCtx &c = *static_cast<const ZzRegroupCtx *>(ctx);
+    ZzMoveArgs mv{};
+    mv.inc = inc;
+    mv.off = off;
+    for (int k = 0; k < 8 && k < arr.n; ++k)
+        mv.out[k] = arr.out[k];
+    // one wave per incremental chunk of an average tile, up to ZZ_WAVES
+    const int64_t per_tile = c.m.n_part / std::max<int64_t>(1, c.ntiles);
+    const int waves = (int)std::max<int64_t>(
+        1, std::min<int64_t>(ZZ_WAVES, (per_tile + INC_CHUNK - 1) / INC_CHUNK));
+    auto kern = c.m.TE == 7    ? k_zigzag_regroup<7>
+                : c.m.TE == 9  ? k_zigzag_regroup<9>
+                : c.m.TE == 11 ? k_zigzag_regroup<11>
+                : c.m.TE == 13 ? k_zigzag_regroup<13>
+                               : k_zigzag_regroup<0>;
+    size_t stat = 2048;  // above the kernel's static LDS (run counts, reductions)
+    {
+        hipFuncAttributes fa{};
+        if (hipFuncGetAttributes(&fa, (const void *)kern) == hipSuccess)
+            stat = (size_t)fa.sharedSizeBytes;
+    }
+    const size_t limit = 160 * 1024 - stat;
+    const size_t at = (c.lds + 15) / 16 * 16;
+    mv.mcap = at < limit ? (uint32_t)std::min<size_t>(ZZ_MOVE_QUEUE_MAX,
+                                                      (limit - at) / (ZZ_MQ_WORDS * 4))
+                         : 0u;
+    const size_t lds = at + (size_t)mv.mcap * ZZ_MQ_WORDS * 4;
+    if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds) != hipSuccess)
+        return fail(PCG_EHIP, "deposit_currents_zigzag_regroup: cannot raise dynamic LDS to %zu "
+                    "bytes", lds);
+    return launch("zigzag_regroup", kern, dim3(c.ntiles), dim3(waves * WAVE), lds, st, c.m, mv);
 }
 
 }  // namespace
@@ -372,13 +603,22 @@ __global__ __launch_bounds__(512) void k_zigzag_tiled(ZzArgs m)
 
 using namespace pcg;
 
-extern "C" pcg_status deposit_currents_zigzag(const pcg_grid *grid, const pcg_particles *particles,
-                                              const float *const x_prev[3], const pcg_tile *tile,
-                                              float *J, unsigned long long *n_escaped,
-                                              void *stream)
+namespace pcg {
+namespace {
+
+// A validated zigzag deposit: its arguments, and for a layout the window's
+// LDS bytes and accumulator kind.
+struct ZzPlan {
+    ZzArgs m{};
+    size_t lds = 0;
+    bool fixed = true;
+    bool tiled = false;
+};
+
+pcg_status prepare_zigzag(const char *who, const pcg_grid *grid, const pcg_particles *particles,
+                          const float *const x_prev[3], const pcg_tile *tile, float *J,
+                          unsigned long long *n_escaped, ZzPlan *plan)
 {
-    const char *who = "deposit_currents_zigzag";
-    clear_error();
     PCG_TRY(check_grid(grid, who));
     if (grid->dim != 3)
         return fail(PCG_EUNSUPPORTED, "%s: only 3-D grids (dim = %d)", who, grid->dim);
@@ -394,7 +634,7 @@ extern "C" pcg_status deposit_currents_zigzag(const pcg_grid *grid, const pcg_pa
         if (!particles->q || !particles->w)
             return fail(PCG_EINVAL, "%s: q or w is NULL", who);
     }
-    ZzArgs m{};
+    ZzArgs &m = plan->m;
     for (int k = 0; k < 3; ++k) {
         m.n[k] = grid->n[k];
         m.x[k] = particles->x[k];
@@ -404,8 +644,7 @@ extern "C" pcg_status deposit_currents_zigzag(const pcg_grid *grid, const pcg_pa
     m.w = particles->w;
     m.J = J;
     m.n_escaped = n_escaped;
-    size_t lds = 0;
-    bool fixed = true;
+    plan->tiled = tile != nullptr;
     if (tile) {
         if (tile->order != 1)
             return fail(PCG_EINVAL, "%s: the layout must be keyed on CIC cells (order 1, not %d)",
@@ -426,13 +665,13 @@ extern "C" pcg_status deposit_currents_zigzag(const pcg_grid *grid, const pcg_pa
         m.T = tile->T;
         m.D = tile->drift;
         m.TE = (int)te;
-        lds = (size_t)3 * m.TE * m.TE * m.TE * sizeof(unsigned long long);
-        fixed = lds <= ZZ_LDS_MAX;
-        if (!fixed)
-            lds /= 2;  // fp32 sums
-        if (lds > ZZ_LDS_MAX)
+        plan->lds = (size_t)3 * m.TE * m.TE * m.TE * sizeof(unsigned long long);
+        plan->fixed = plan->lds <= ZZ_LDS_MAX;
+        if (!plan->fixed)
+            plan->lds /= 2;  // fp32 sums
+        if (plan->lds > ZZ_LDS_MAX)
             return fail(PCG_ELDS, "%s: window of %zu bytes exceeds the LDS (T = %d, D = %d)",
-                        who, lds, tile->T, tile->drift);
+                        who, plan->lds, tile->T, tile->drift);
         for (int k = 0; k < 3; ++k)
             m.nt[k] = grid->n[k] / tile->T;
         if ((int64_t)m.nt[0] * m.nt[1] * m.nt[2] >= (int64_t(1) << 31))
@@ -441,35 +680,114 @@ extern "C" pcg_status deposit_currents_zigzag(const pcg_grid *grid, const pcg_pa
         m.offsets = tile->tile_offsets;
         m.n_part = tile->n_partitioned;
     }
+    return PCG_OK;
+}
+
+pcg_status launch_zigzag_flat(const ZzArgs &m, int64_t begin, int64_t end, hipStream_t st)
+{
+    if (end <= begin)
+        return PCG_OK;
+    const int64_t blocks = std::min<int64_t>((end - begin + 255) / 256, (int64_t)device_cus() * 32);
+    return launch("zigzag_flat", k_zigzag_flat, dim3((unsigned)blocks), dim3(256), 0, st, m, begin,
+                  end);
+}
+
+pcg_status launch_zigzag_tiled(const ZzPlan &p, hipStream_t st)
+{
+    const ZzArgs &m = p.m;
+    if (m.n_part <= 0)
+        return PCG_OK;
+    // window edges of tiles 4 and 8 with drift 0 and 1 are compiled in
+    auto kern = !p.fixed       ? k_zigzag_tiled<false, 0>
+                : m.TE == 7  ? k_zigzag_tiled<true, 7>
+                : m.TE == 9  ? k_zigzag_tiled<true, 9>
+                : m.TE == 11 ? k_zigzag_tiled<true, 11>
+                : m.TE == 13 ? k_zigzag_tiled<true, 13>
+                             : k_zigzag_tiled<true, 0>;
+    if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)p.lds) != hipSuccess)
+        return fail(PCG_EHIP, "deposit_currents_zigzag: cannot raise dynamic LDS to %zu bytes",
+                    p.lds);
+    const int64_t ntiles = (int64_t)m.nt[0] * m.nt[1] * m.nt[2];
+    // a window that leaves room for few work-groups per CU gets wider ones
+    const unsigned block = p.lds > 32 * 1024 ? 512 : 256;
+    return launch(p.fixed ? "zigzag_tiled" : "zigzag_tiled_f32", kern, dim3((unsigned)ntiles),
+                  dim3(block), p.lds, st, m);
+}
+
+}  // namespace
+}  // namespace pcg
+
+extern "C" pcg_status deposit_currents_zigzag(const pcg_grid *grid, const pcg_particles *particles,
+                                              const float *const x_prev[3], const pcg_tile *tile,
+                                              float *J, unsigned long long *n_escaped,
+                                              void *stream)
+{
+    const char *who = "deposit_currents_zigzag";
+    clear_error();
+    ZzPlan plan;
+    PCG_TRY(prepare_zigzag(who, grid, particles, x_prev, tile, J, n_escaped, &plan));
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t count = particles->count;
     if (count == 0)
         return PCG_OK;
-    auto flat = [&](int64_t begin, int64_t end) -> pcg_status {
-        if (end <= begin)
-            return PCG_OK;
-        const int64_t blocks =
-            std::min<int64_t>((end - begin + 255) / 256, (int64_t)device_cus() * 32);
-        return launch("zigzag_flat", k_zigzag_flat, dim3((unsigned)blocks), dim3(256), 0, st, m,
-                      begin, end);
-    };
     if (!tile)
-        return flat(0, count);
-    if (m.n_part > 0) {
-        // window edges of tiles 4 and 8 with drift 0 and 1 are compiled in
-        auto kern = !fixed         ? k_zigzag_tiled<false, 0>
-                    : m.TE == 7  ? k_zigzag_tiled<true, 7>
-                    : m.TE == 9  ? k_zigzag_tiled<true, 9>
-                    : m.TE == 11 ? k_zigzag_tiled<true, 11>
-                    : m.TE == 13 ? k_zigzag_tiled<true, 13>
-                                 : k_zigzag_tiled<true, 0>;
-        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)lds) != hipSuccess)
-            return fail(PCG_EHIP, "%s: cannot raise dynamic LDS to %zu bytes", who, lds);
-        const int64_t ntiles = (int64_t)m.nt[0] * m.nt[1] * m.nt[2];
-        // a window that leaves room for few work-groups per CU gets wider ones
-        const unsigned block = lds > 32 * 1024 ? 512 : 256;
-        PCG_TRY(launch(fixed ? "zigzag_tiled" : "zigzag_tiled_f32", kern, dim3((unsigned)ntiles),
-                       dim3(block), lds, st, m));
+        return launch_zigzag_flat(plan.m, 0, count, st);
+    PCG_TRY(launch_zigzag_tiled(plan, st));
+    return launch_zigzag_flat(plan.m, tile->n_partitioned, count, st);
+}
+
+extern "C" pcg_status deposit_currents_zigzag_regroup(
+    const pcg_grid *grid, const pcg_particles *particles, const float *const x_prev[3],
+    const pcg_tile *tile, float *J, unsigned long long *n_escaped, int32_t n_arrays,
+    const float *const in_arrays[], float *const out_arrays[], uint32_t *tile_offsets,
+    void *workspace, size_t workspace_bytes, void *stream)
+{
+    const char *who = "deposit_currents_zigzag_regroup";
+    clear_error();
+    if (!tile)
+        return fail(PCG_EINVAL, "%s: tile is NULL (the pass needs the current layout)", who);
+    ZzPlan plan;
+    PCG_TRY(prepare_zigzag(who, grid, particles, x_prev, tile, J, n_escaped, &plan));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t count = particles->count;
+    // the sort's own checks, before anything is enqueued
+    const size_t need = sort_workspace_bytes(grid, count, tile->T);
+    if (!workspace || workspace_bytes < need || need == 0)
+        return fail(PCG_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, need,
+                    workspace_bytes);
+    if (!tile_offsets)
+        return fail(PCG_EINVAL, "%s: tile_offsets is NULL", who);
+    if ((const void *)tile_offsets == (const void *)tile->tile_offsets)
+        return fail(PCG_EINVAL, "%s: tile_offsets must differ from the layout's offsets", who);
+    if (n_arrays < 0 || n_arrays > MAX_ARRAYS)
+        return fail(PCG_EINVAL, "%s: n_arrays = %d not in [0, %d]", who, n_arrays, MAX_ARRAYS);
+    for (int i = 0; i < n_arrays && count > 0; ++i) {
+        if (!in_arrays || !out_arrays || !in_arrays[i] || !out_arrays[i])
+            return fail(PCG_EINVAL, "%s: array %d is NULL", who, i);
+        if ((const void *)in_arrays[i] == (const void *)out_arrays[i])
+            return fail(PCG_EINVAL, "%s: array %d is moved in place (out == in)", who, i);
     }
-    return flat(tile->n_partitioned, count);
+    bool canon = in_arrays && n_arrays == 8 && plan.fixed && tile->n_partitioned == count;
+    for (int k = 0; canon && k < 3; ++k)
+        canon = in_arrays[k] == particles->x[k] && in_arrays[3 + k] == x_prev[k];
+    canon = canon && in_arrays[6] == particles->q && in_arrays[7] == particles->w;
+    if (!canon) {
+        // a tail, fp32 window sums, or other arrays than exactly (x, x_prev,
+        // q, w): the deposit, then the sort with its own move
+        PCG_TRY(deposit_currents_zigzag(grid, particles, x_prev, tile, J, n_escaped, stream));
+        return tile_sort_impl(grid, 1, tile->T, count, particles->x, n_arrays, in_arrays,
+                              out_arrays, nullptr, nullptr, tile_offsets, tile, workspace,
+                              workspace_bytes, st, nullptr, nullptr);
+    }
+    ZzRegroupCtx ctx{plan.m, plan.lds, (uint32_t)((int64_t)plan.m.nt[0] * plan.m.nt[1] *
+                                                  plan.m.nt[2])};
+    const MoveHook hook{zz_regroup_hook, &ctx};
+    bool taken = false;
+    PCG_TRY(tile_sort_impl(grid, 1, tile->T, count, particles->x, n_arrays, in_arrays, out_arrays,
+                           nullptr, nullptr, tile_offsets, tile, workspace, workspace_bytes, st,
+                           &hook, &taken));
+    if (!taken && count > 0)  // cannot happen with n_partitioned == count; never skip the deposit
+        return deposit_currents_zigzag(grid, particles, x_prev, tile, J, n_escaped, stream);
+    return PCG_OK;
 }

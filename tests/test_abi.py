@@ -42,6 +42,7 @@ def test_header_declares_the_entry_points():
               "assemble_mass_matrix_f64",
               "assemble_mass_matrix_scalar_f64", "deposit_sweep1d", "deposit_sweep1d_grad",
               "deposit_sweep1d_loss_grad", "deposit_currents_zigzag",
+              "deposit_currents_zigzag_regroup", "deposit_currents_noalloc",
               "pcg_status_string", "pcg_last_error", "pcg_version", "pcg_timing_enable",
               "pcg_timing_reset", "pcg_timing_read", "pcg_timing_names"]:
         assert n in names
@@ -176,6 +177,32 @@ def test_zigzag_validation(lib):
     assert call(big, tile=Tile(1, 1, 1, 0, 1000, FAKE)) == EINVAL  # 2^33 tiles: one launch
     # no particles: nothing to check beyond the grid, nothing launched
     assert call(g, P=particles(0), xp=None) == 0
+
+
+def test_zigzag_regroup_validation(lib):
+    lib.pcg_last_error.restype = C.c_char_p
+    zr = lib.deposit_currents_zigzag_regroup
+    lib.pcg_sort_workspace_bytes.restype = C.c_size_t
+    P = particles(1000)
+    xp = (C.c_void_p * 3)(FAKE, FAKE, FAKE)
+    arrs = (C.c_void_p * 8)(*([FAKE] * 8))
+    outs = (C.c_void_p * 8)(*([FAKE + 64] * 8))
+    g = grid(3, [64, 64, 64])
+    need = lib.pcg_sort_workspace_bytes(C.byref(g), C.c_int64(1000), 8)
+
+    def call(g=g, tile=Tile(8, 1, 0, 0, 1000, FAKE), ws=C.c_void_p(FAKE * 256), wsb=need,
+             off=C.c_void_p(FAKE * 2), na=8):
+        return zr(C.byref(g), C.byref(P), xp, C.byref(tile) if tile else None, C.c_void_p(FAKE),
+                  None, na, arrs, outs, off, ws, C.c_size_t(wsb), None)
+
+    assert call(tile=None) == EINVAL                                # the layout is required
+    assert call(g=grid(2, [8, 8])) == EUNSUPPORTED
+    assert call(tile=Tile(8, 2, 0, 0, 1000, FAKE)) == EINVAL       # keyed with TSC
+    assert call(wsb=need - 1) == EWORKSPACE
+    assert call(ws=None) == EWORKSPACE
+    assert call(off=None) == EINVAL
+    assert call(off=C.c_void_p(FAKE)) == EINVAL                     # same as the layout's
+    assert call(na=17) == EINVAL
 
 
 def test_deposit_workspace_size(lib):

@@ -200,3 +200,131 @@ def test_full_size_parity(orc, D):
         tot = float((qw * (x[c].astype(np.float64) - xp[c])).sum())
         scale = float(np.abs(qw * (x[c].astype(np.float64) - xp[c])).sum())
         assert abs(float(J[c].astype(np.float64).sum()) - tot) <= 1e-6 * scale
+
+
+# ---------------------------------------------------------------- fused pass
+
+def _run_fused(n, T, D, x, xp, q, w, off, n_part=None, arrays=None):
+    """deposit_currents_zigzag_regroup with the layout `off` (the particles'
+    current grouping): J, escapes, the new offsets and the regrouped arrays."""
+    xs, xps = [dev(a) for a in x], [dev(a) for a in xp]
+    qd, wd = dev(q), dev(w)
+    arrs = xs + xps + [qd, wd] if arrays is None else [dev(a) for a in arrays]
+    J = _J(n)
+    esc = torch.zeros(1, dtype=torch.int64, device=DEV)
+    lay = _layout(T, D, off, x[0].size if n_part is None else n_part)
+    say("zigzag fused", n, T, D, x[0].size, n_part, len(arrs))
+    off_new, outs = pcg.deposit_currents_zigzag_regroup(n, xs, xps, qd, wd, J, lay, arrs,
+                                                        n_escaped=esc)
+    torch.cuda.synchronize()
+    return (J.cpu().numpy(), int(esc.item()), off_new.cpu().numpy().view(np.uint32),
+            [o.cpu().numpy() for o in outs])
+
+
+def _check_fused(orc, n, T, D, key, x, xp, q, w, off, got, arrays=None):
+    """J vs the oracle; escapes vs the window rule; the new layout and every
+    regrouped array bit for bit against the oracle's stable sort of x."""
+    J, esc, off_new, outs = got
+    assert rel_max_err(J, orc.deposit_zigzag(n, x, xp, q, w)) <= TOL
+    assert esc == _expected_escapes(n, T, D, key, x, xp)
+    _, p, o = orc.tile_sort(3, n, 1, T, x)
+    assert np.array_equal(off_new, o)
+    src = [*x, *xp, q, w] if arrays is None else arrays
+    for a, b in zip(outs, src):
+        assert np.array_equal(a.view(np.uint32), b[p].view(np.uint32))
+    return esc
+
+
+def _grouped_by_prev(orc, n, T, x, xp, q, w):
+    """The particles grouped by the tiles of their previous positions (wrapped
+    into the grid), as the last step's sort left them."""
+    key = [np.mod(a, np.float32(n[k])).astype(np.float32) for k, a in enumerate(xp)]
+    key = [np.where(a >= n[k], np.float32(0), a) for k, a in enumerate(key)]
+    _, p, off = orc.tile_sort(3, n, 1, T, key)
+    p = p.astype(np.int64)
+    return [a[p] for a in key], [a[p] for a in x], [a[p] for a in xp], q[p], w[p], off
+
+
+@pytest.mark.parametrize("n,T,D", [
+    ([32, 32, 32], 8, 0),
+    ([32, 32, 32], 8, 1),
+    ([32, 32, 32], 4, 0),
+    ([24, 16, 32], 8, 2),
+    ([32, 32, 32], 16, 1),   # fp32 window sums: deposit, then the sort's own move
+])
+def test_fused_matches_oracle(orc, n, T, D):
+    x, xp, q, w = _inputs(n, 6, seed=770 + T + D)
+    key, x, xp, q, w, off = _grouped_by_prev(orc, n, T, x, xp, q, w)
+    got = _run_fused(n, T, D, x, xp, q, w, off)
+    _check_fused(orc, n, T, D, key, x, xp, q, w, off, got)
+    moved = orc.tile_keys(3, n, 1, T, x) != orc.tile_keys(3, n, 1, T, key)
+    assert moved.sum() > 0       # particles change tile: the move's leaver path ran
+
+
+def test_fused_heavy_tiles_and_queue_overflow(orc):
+    """Tiles of edge 2 holding 2400 particles, most of which change tile: more
+    leavers than the work-group's LDS queue (1024) takes; then one tile of
+    204,800 particles (100 chunks for 8 waves)."""
+    n = [8, 8, 8]
+    x, xp, q, w = _inputs(n, 300, seed=781)
+    key, x, xp, q, w, off = _grouped_by_prev(orc, n, 2, x, xp, q, w)
+    leavers = orc.tile_keys(3, n, 1, 2, x) != orc.tile_keys(3, n, 1, 2, key)
+    assert leavers.sum() > 64 * 1100   # over 1024 per tile on average
+    _check_fused(orc, n, 2, 0, key, x, xp, q, w, off, _run_fused(n, 2, 0, x, xp, q, w, off))
+    x, xp, q, w = _inputs([8, 8, 8], 400, seed=782)
+    key, x, xp, q, w, off = _grouped_by_prev(orc, [8, 8, 8], 8, x, xp, q, w)
+    assert np.diff(off.astype(np.int64)).max() > 16 * 2048
+    _check_fused(orc, [8, 8, 8], 8, 1, key, x, xp, q, w, off,
+                 _run_fused([8, 8, 8], 8, 1, x, xp, q, w, off))
+
+
+def test_fused_stale_layout_falls_back_to_the_general_sort(orc):
+    """A layout three tiles stale: the deposit takes the escape valve for most
+    particles and the device flag hands the regrouping to the radix path."""
+    n, T = [32, 32, 32], 4
+    x, xp, q, w = _inputs(n, 3, seed=783)
+    key = [np.mod(a + np.float32(3 * T), np.float32(n[k])).astype(np.float32)
+           for k, a in enumerate(x)]
+    _, p, off = orc.tile_sort(3, n, 1, T, key)
+    p = p.astype(np.int64)
+    key, x, xp, q, w = [a[p] for a in key], [a[p] for a in x], [a[p] for a in xp], q[p], w[p]
+    esc = _check_fused(orc, n, T, 1, key, x, xp, q, w, off, _run_fused(n, T, 1, x, xp, q, w, off))
+    assert esc > x[0].size // 2
+
+
+def test_fused_tail_and_other_arrays(orc):
+    """A tail, and arrays other than exactly (x, x_prev, q, w): the deposit and
+    the sort run one after the other, with the same results."""
+    n, T = [32, 32, 32], 8
+    x, xp, q, w = _inputs(n, 3, seed=784)
+    key, x, xp, q, w, off = _grouped_by_prev(orc, n, T, x, xp, q, w)
+    cnt = x[0].size
+    got = _run_fused(n, T, 0, x, xp, q, w, off, n_part=cnt - 321)
+    J, esc, off_new, outs = got
+    assert rel_max_err(J, orc.deposit_zigzag(n, x, xp, q, w)) <= TOL
+    _, p, o = orc.tile_sort(3, n, 1, T, x)
+    assert np.array_equal(off_new, o)
+    ids = np.arange(cnt, dtype=np.int32).view(np.float32)
+    arrays = [q, ids, *x, w]
+    got = _run_fused(n, T, 0, x, xp, q, w, off, arrays=arrays)
+    _check_fused(orc, n, T, 0, key, x, xp, q, w, off, got, arrays=arrays)
+
+
+def test_fused_empty(orc):
+    n = [8, 8, 8]
+    e = np.zeros(0, np.float32)
+    J, esc, off_new, outs = _run_fused(n, 4, 0, [e] * 3, [e] * 3, e, e, np.zeros(9, np.uint32))
+    assert not J.any() and esc == 0 and not off_new.any()
+
+
+def test_fused_full_size_step(orc):
+    """The zigzag step the benchmark times, at full size (67.1M particles,
+    128^3, T = 8, drift 0): J vs the oracle over the whole array; the new
+    layout and all eight regrouped arrays bit for bit."""
+    wl = full_workload("cic3d_128_ppc32")
+    n, T = wl.n, 8
+    xp = synthetic.previous_positions(wl.x, scale_v=1.0, v=wl.v)
+    key, x, xp, q, w, off = _grouped_by_prev(orc, n, T, wl.x, xp, wl.q, wl.w)
+    got = _run_fused(n, T, 0, x, xp, q, w, off)
+    esc = _check_fused(orc, n, T, 0, key, x, xp, q, w, off, got)
+    assert esc == 0

@@ -1036,16 +1036,23 @@ pcg_status launch_tiled_mode(DepArgs a, const MoveArgs &m, uint32_t nwork, int b
     const size_t packed = packed_bytes(vol, ncell), fixed = vol * 24, flt = vol * 12;
     // The queues (globally deposited particles; in the fused pass, particles
     // that change tile) follow the first pass's scratch, as large as the LDS
-    // left allows (none: no queue).  They may reach into the 64-bit scratch,
-    // which is used only after they are drained, or instead of them.
+    // left allows (none: no queue) and in proportion to the work-group's
+    // waves (64 and 128 entries per wave), so that work-groups of one or two
+    // waves over small tiles keep their LDS small and many of them fit a CU.
+    // They may reach into the 64-bit scratch, which is used only after they
+    // are drained, or instead of them.
+    const size_t waves = (size_t)std::max(1, block / WAVE);
     auto with_queues = [&](size_t first, size_t rest, size_t limit) {
         size_t at = (first + 15) / 16 * 16;
         auto room = [&](size_t bytes) { return limit > at ? (limit - at) / bytes : 0; };
         a.qoff = (uint32_t)at;
-        a.qcap = (uint32_t)std::min<size_t>(QUEUE_MAX, room(QUEUE_FLOATS * 4));
+        a.qcap = (uint32_t)std::min<size_t>(std::min<size_t>(QUEUE_MAX, 64 * waves),
+                                            room(QUEUE_FLOATS * 4));
         at += (size_t)a.qcap * QUEUE_FLOATS * 4;
         a.moff = (uint32_t)at;
-        a.mcap = MOVE ? (uint32_t)std::min<size_t>(MOVE_QUEUE_MAX, room(MQ_WORDS * 4)) : 0u;
+        a.mcap = MOVE ? (uint32_t)std::min<size_t>(std::min<size_t>(MOVE_QUEUE_MAX, 128 * waves),
+                                                   room(MQ_WORDS * 4))
+                      : 0u;
         at += (size_t)a.mcap * MQ_WORDS * 4;
         return std::max(at, rest);
     };

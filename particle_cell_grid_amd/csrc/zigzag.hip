@@ -396,10 +396,19 @@ struct ZzMoveArgs {
     uint32_t mcap;        // entries of the LDS queue of particles that change tile
 };
 
-constexpr int ZZ_MQ_WORDS = 9;               // new slot, then the eight fields
-constexpr uint32_t ZZ_MOVE_QUEUE_MAX = 1024;  // entries per work-group (36 KiB)
-constexpr int ZZ_WAVES = 8;                  // most waves of a work-group
-constexpr int ZZ_UW = 2;                     // particles per lane in flight in the walk
+#ifndef PCG_ZZ_MQ
+#define PCG_ZZ_MQ 1024
+#endif
+#ifndef PCG_ZZ_UW
+#define PCG_ZZ_UW 2
+#endif
+#ifndef PCG_ZZ_WAVES
+#define PCG_ZZ_WAVES 8
+#endif
+constexpr int ZZ_MQ_WORDS = 9;                     // new slot, then the eight fields
+constexpr uint32_t ZZ_MOVE_QUEUE_MAX = PCG_ZZ_MQ;  // entries per work-group (36 KiB)
+constexpr int ZZ_WAVES = PCG_ZZ_WAVES;             // most waves of a work-group
+constexpr int ZZ_UW = PCG_ZZ_UW;                   // particles per lane in flight in the walk
 
 // One work-group per tile of the layout the particles are grouped by; its
 // waves walk the tile's incremental chunks in order (wave j takes chunks j,
@@ -587,8 +596,11 @@ pcg_status zz_regroup_hook(void *ctx, const IncGeom &inc, const uint32_t *off, u
     }
     const size_t limit = 160 * 1024 - stat;
     const size_t at = (c.lds + 15) / 16 * 16;
-    mv.mcap = at < limit ? (uint32_t)std::min<size_t>(ZZ_MOVE_QUEUE_MAX,
-                                                      (limit - at) / (ZZ_MQ_WORDS * 4))
+    // 128 entries per wave at most, so that small work-groups over small
+    // tiles keep their LDS small and many fit a CU
+    mv.mcap = at < limit ? (uint32_t)std::min<size_t>(
+                               std::min<size_t>(ZZ_MOVE_QUEUE_MAX, 128 * (size_t)waves),
+                               (limit - at) / (ZZ_MQ_WORDS * 4))
                          : 0u;
     const size_t lds = at + (size_t)mv.mcap * ZZ_MQ_WORDS * 4;
     if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -845,8 +845,8 @@ __global__ __launch_bounds__(512) void k_deposit_tiled(DepArgs a, MoveArgs m)
                         // wave-uniform: the slot comes from the whole wave's
                         // directions
                         const int d = fastdir ? support_dir<DIM, ORDER>(a, sp)
-                                              : particle_dir<DIM, ORDER>(gx[u][0], gx[u][1],
-                                                                         gx[u][2], m.inc.g, tsc);
+                                              : tile_dir<DIM, ORDER>(gx[u][0], gx[u][1], gx[u][2],
+                                                                     m.inc.g, tsc);
                         const bool ok = valid && d >= 0;  // d < 0 cannot occur: flag clear
                         const uint32_t pos = walk_slot(run, d, ok);
                         if (ok && pos < (uint64_t)m.inc.count) {

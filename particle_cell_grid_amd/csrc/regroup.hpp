@@ -26,6 +26,7 @@ struct KeyGeom {
     int nt[3];
     int T;
     int T_shift;  // log2(T) if T is a power of two, else -1
+    int pow2;     // every used axis has n and n / T >= 4 powers of two (and T too)
 };
 
 // Tile coordinate of a particle along one axis: the tile holding its first
@@ -131,6 +132,44 @@ __device__ inline int particle_dir(float x0, float x1, float x2, const KeyGeom &
         mul *= 3;
     }
     return far ? -1 : dir;
+}
+
+// particle_dir where n, T and n / T >= 4 are powers of two on every used axis
+// (KeyGeom::pow2; four tiles or more keep -1, 0, +1 apart): the periodic wraps of the node and of the tile difference
+// are masks, some 28 vector instructions per particle instead of about 66.
+// The first support node is floor(x) (CIC) or floor(x - 1/2) (TSC: the node
+// below when the fraction is under 1/2; x - 1/2 is exact or rounds only for
+// x < 1/4, where the floor is -1 either way), x clamped into [0, n] as in
+// tile_coord, so both give the same tile.
+template <int DIM, int ORDER>
+__device__ inline int particle_dir_pow2(float x0, float x1, float x2, const KeyGeom &g,
+                                        const int *sc)
+{
+    const float xs[3] = {x0, x1, x2};
+    int dir = 0, mul = 1;
+    uint32_t worst = 0;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        uint32_t d = 1;  // unused axes: direction 0
+        if (k < DIM) {
+            const float xf = clamp_coord(xs[k], g.nf[k]);
+            const int b = (int)floorf(ORDER == 2 ? xf - 0.5f : xf);
+            const uint32_t t = ((uint32_t)b & (uint32_t)(g.n[k] - 1)) >> g.T_shift;
+            d = (t - (uint32_t)sc[k] + 1u) & (uint32_t)(g.nt[k] - 1);
+            worst = max(worst, d);
+        }
+        dir += mul * (int)d;
+        mul *= 3;
+    }
+    return worst > 2u ? -1 : dir;
+}
+
+// The direction of a particle: particle_dir_pow2 where the geometry allows.
+template <int DIM, int ORDER>
+__device__ inline int tile_dir(float x0, float x1, float x2, const KeyGeom &g, const int *sc)
+{
+    return g.pow2 ? particle_dir_pow2<DIM, ORDER>(x0, x1, x2, g, sc)
+                  : particle_dir<DIM, ORDER>(x0, x1, x2, g, sc);
 }
 
 // One 64-particle step of a wave's in-order walk through a chunk: the new

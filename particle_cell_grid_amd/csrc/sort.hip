@@ -472,7 +472,7 @@ __global__ __launch_bounds__(256) void k_inc_count(IncGeom a, const float *x0, c
 #pragma unroll
         for (int e = 0; e < COUNT_EPT; ++e) {
             const bool valid = b + e * stride < hi;
-            int dir = particle_dir<DIM, ORDER>(c[e][0], c[e][1], c[e][2], a.g, sc);
+            int dir = tile_dir<DIM, ORDER>(c[e][0], c[e][1], c[e][2], a.g, sc);
             far |= valid && dir < 0;
             const bool ok = valid && dir >= 0;
             // most particles stay in their tile: one ballot counts those, and
@@ -652,7 +652,7 @@ __global__ __launch_bounds__(MOVE_WAVES * WAVE) void k_inc_move(
         }
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
-            dir[e] = particle_dir<DIM, ORDER>(c[e][0], c[e][1], c[e][2], a.g, sc);
+            dir[e] = tile_dir<DIM, ORDER>(c[e][0], c[e][1], c[e][2], a.g, sc);
             ok[e] = p[e] < r.hi && dir[e] >= 0;  // dir < 0 cannot occur: the flag is clear
             pos[e] = walk_slot(run, dir[e], ok[e]);
             ok[e] = ok[e] && pos[e] < (uint64_t)a.count;
@@ -779,7 +779,7 @@ __global__ __launch_bounds__(MOVE_WAVES * WAVE) void k_inc_move_small(
         }
 #pragma unroll
         for (int j = 0; j < K; ++j) {
-            dir[j] = particle_dir<DIM, ORDER>(c[j][0], c[j][1], c[j][2], a.g, sc[j]);
+            dir[j] = tile_dir<DIM, ORDER>(c[j][0], c[j][1], c[j][2], a.g, sc[j]);
             ok[j] = p[j] < hi[j] && dir[j] >= 0;  // dir < 0 cannot occur: the flag is clear
             pos[j] = walk_slot(s_run[wave][j], dir[j], ok[j]);
             ok[j] = ok[j] && pos[j] < (uint64_t)a.count;
@@ -1111,6 +1111,10 @@ pcg_status tile_sort_impl(const pcg_grid *grid, int32_t order, int32_t T, int64_
     for (int s = 0; s < 31; ++s)
         if ((1 << s) == T)
             g.T_shift = s;
+    auto is_pow2 = [](int v) { return v > 0 && (v & (v - 1)) == 0; };
+    g.pow2 = g.T_shift >= 0;
+    for (int k = 0; k < grid->dim; ++k)
+        g.pow2 = g.pow2 && is_pow2(grid->n[k]) && is_pow2(g.nt[k]) && g.nt[k] >= 4;
     PermArgs arr{};
     for (int i = 0; i < n_arrays; ++i) {
         arr.in[i] = in_arrays[i];

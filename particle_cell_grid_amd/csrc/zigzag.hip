@@ -500,7 +500,7 @@ __global__ __launch_bounds__(ZZ_WAVES * WAVE) void k_zigzag_regroup(ZzArgs m, Zz
                 const bool valid = p < chi;
                 if (move) {
                     // wave-uniform: the slot comes from the whole wave's directions
-                    const int d = particle_dir<3, 1>(cur[u].b[0], cur[u].b[1], cur[u].b[2],
+                    const int d = tile_dir<3, 1>(cur[u].b[0], cur[u].b[1], cur[u].b[2],
                                                      mv.inc.g, tc);
                     const bool ok = valid && d >= 0;  // d < 0 cannot occur: the flag is clear
                     const uint32_t pos = walk_slot(run, d, ok);

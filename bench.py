@@ -361,9 +361,11 @@ def bench_deposit(args, torch, pcg, name):
     progress("timing the deposit alone")
     dep_ms, _, kt_dep = time_steps(torch, pcg, lambda: (J.zero_(), deposit()), args.steps, 1)
     roof = roofline_entry(kt_dep, "deposit_tiled", bytes_per_launch=alg["deposit_tiled"])
+    # traffic records are kept per tile size for the blob (its T is swept)
+    tkey = f"{name}_T{T}" if name == "tsc3d_128_blob" else name
     for r in (roof, roof_dom):
         if r:
-            r["traffic"] = measured_traffic(r["kernel"], name)
+            r["traffic"] = measured_traffic(r["kernel"], tkey)
     extra["deposit_only_particles_per_s"] = round(cnt / (dep_ms * 1e-3), 1)
     extra["deposit_only_ms"] = round(dep_ms, 4)
     if not args.no_flat:

@@ -164,3 +164,9 @@ def full_size_checks(orc, wl, M, tol):
 def _check_tol(M, ref, tol):
     assert rel_frob_err(M, ref) <= tol
     assert np.abs(M - ref).max() <= tol * np.abs(ref).max()
+
+
+def component_errors(J, ref):
+    """Per component c of a current: max |J_c - ref_c| / max |ref_c| (the
+    deposit tolerance applied to each component on its own)."""
+    return [rel_max_err(J[c], ref[c]) for c in range(J.shape[0])]

@@ -230,10 +230,13 @@ __device__ inline unsigned long long to_fixed(float x)
 // particle whose stencil does not fit (a move over more than a neighbouring
 // cell, or a layout more than D cells stale) goes to global memory on the
 // first pass and is skipped on a second.  Returns 1 for such an escape on the
-// first pass.
+// first pass.  When FIXED, a particle with |q w| above qlim (the bound the
+// scale was chosen for) adds nothing: its contributions might not fit an int32,
+// and the tile is deposited again at a scale that holds it.
 template <bool FIXED, typename Acc>
 __device__ __attribute__((always_inline)) inline uint32_t window_add(
-    const ZzArgs &m, Acc *win, int TE, int vol, const int *ws, Move mv, int k_scale, bool first)
+    const ZzArgs &m, Acc *win, int TE, int vol, const int *ws, Move mv, int k_scale, bool first,
+    float qlim)
 {
     const int stride[3] = {1, TE, TE * TE};
     // the stencil fits if its last node lies in the window
@@ -250,6 +253,8 @@ __device__ __attribute__((always_inline)) inline uint32_t window_add(
             deposit_global(m, mv);
         return first ? 1u : 0u;
     }
+    if (FIXED && !(fabsf(mv.qw) <= qlim))
+        return 0u;
     if (FIXED)
         mv.qw = ldexpf(mv.qw, k_scale);  // every contribution comes out scaled
     // window slot of each segment's cell corner
@@ -304,9 +309,11 @@ __device__ inline void flush_window(const ZzArgs &m, const Acc *win, int TE, int
 // contributions scaled by 2^k (exact and independent of the order of the adds;
 // LDS integer atomics run over twenty times the rate of float ones on this
 // chip).  A particle whose move stays within neighbouring cells on every axis
-// has |F'| <= 1 and 0 <= w <= 1 per segment, so it adds at most 2 (13/12) |q w|
-// to any node (both segments, summed before the add); k is chosen so that this
-// bound, scaled, is below 2^31.  Each add then converts one int32, and a node
+// has |F'| <= 1 and 0 <= w <= 1 per segment, so one segment adds at most
+// (13/12) |q w| to a node, and a move within one cell (its two segments merged
+// into one add) at most twice that; k is chosen so that 2 (13/12) |q w|,
+// scaled, is below 2^31, and particles above the assumed max|q w| add nothing
+// until the tile runs again.  Each add then converts one int32, and a node
 // sum of fewer than 2^31 particles' adds stays below 2^62.  max|q w| is taken
 // as twice the largest of the first particle of every thread, and checked
 // after the pass against every particle seen; a tile that breaks it is cleared
@@ -337,7 +344,7 @@ __global__ __launch_bounds__(512) void k_zigzag_tiled(ZzArgs m)
 
     // one pass over the tile's particles at scale 2^k_scale; returns the
     // largest |q w| this thread saw
-    auto deposit_pass = [&](int k_scale, bool first) -> float {
+    auto deposit_pass = [&](int k_scale, bool first, float qlim) -> float {
         for (int i = threadIdx.x; i < 3 * vol; i += blockDim.x)
             win[i] = 0;
         __syncthreads();
@@ -352,7 +359,7 @@ __global__ __launch_bounds__(512) void k_zigzag_tiled(ZzArgs m)
                 next = load_raw(m, p + blockDim.x);
             const Move mv = make_move<FIXED>(cur);
             seen = fmaxf(seen, fabsf(mv.qw));
-            escaped += window_add<FIXED>(m, win, TE, vol, ws, mv, k_scale, first);
+            escaped += window_add<FIXED>(m, win, TE, vol, ws, mv, k_scale, first, qlim);
         }
         __syncthreads();
         return seen;
@@ -369,7 +376,7 @@ __global__ __launch_bounds__(512) void k_zigzag_tiled(ZzArgs m)
     }
     // at most two passes: the second runs with the true maximum, which holds
     for (bool first = true;; first = false) {
-        const float seen_here = deposit_pass(k_scale, first);
+        const float seen_here = deposit_pass(k_scale, first, assumed);
         if (!FIXED)
             break;
         const float seen = block_max(seen_here, red);
@@ -529,7 +536,7 @@ __global__ __launch_bounds__(ZZ_WAVES * WAVE) void k_zigzag_regroup(ZzArgs m, Zz
                 if (valid) {
                     const Move mm = make_move<true>(cur[u]);
                     seen = fmaxf(seen, fabsf(mm.qw));
-                    escaped += window_add<true>(m, win, TE, vol, ws, mm, k_scale, true);
+                    escaped += window_add<true>(m, win, TE, vol, ws, mm, k_scale, true, assumed);
                 }
             }
         }
@@ -555,7 +562,8 @@ __global__ __launch_bounds__(ZZ_WAVES * WAVE) void k_zigzag_regroup(ZzArgs m, Zz
             win[i] = 0;
         __syncthreads();
         for (int64_t p = lo + threadIdx.x; p < hi; p += blockDim.x)
-            window_add<true>(m, win, TE, vol, ws, make_move<true>(load_raw(m, p)), k_scale, false);
+            window_add<true>(m, win, TE, vol, ws, make_move<true>(load_raw(m, p)), k_scale, false,
+                             seen_all);
         __syncthreads();
     }
     flush_window<true>(m, win, TE, vol, ws, k_scale);

@@ -281,6 +281,24 @@ def test_fused_heavy_tiles_and_queue_overflow(orc):
                  _run_fused([8, 8, 8], 8, 1, x, xp, q, w, off))
 
 
+@pytest.mark.parametrize("heavy_w", [40.0, 1e5])
+def test_fused_scale_redo(orc, heavy_w):
+    """The fused step's tiles take their fixed-point scale from the first
+    particle of each thread; one heavy particle per tile past its first 512
+    makes every tile deposit again at its true maximum (no second move).  At
+    w = 1e5 the first scale would put that particle's contributions far past
+    the int32 range, so it must add nothing on the first pass."""
+    n, T, D = [32, 32, 32], 8, 1
+    x, xp, q, w = _inputs(n, 6, seed=786)
+    key, x, xp, q, w, off = _grouped_by_prev(orc, n, T, x, xp, q, w)
+    w = np.full_like(w, 0.5)
+    heavy = [int(off[t]) + 600 for t in range(off.size - 1) if off[t + 1] - off[t] > 600]
+    assert len(heavy) == off.size - 1
+    w[heavy] = heavy_w
+    say("zigzag fused scale redo", n, T, D, x[0].size, heavy_w)
+    _check_fused(orc, n, T, D, key, x, xp, q, w, off, _run_fused(n, T, D, x, xp, q, w, off))
+
+
 def test_fused_stale_layout_falls_back_to_the_general_sort(orc):
     """A layout three tiles stale: the deposit takes the escape valve for most
     particles and the device flag hands the regrouping to the radix path."""

@@ -104,6 +104,28 @@ __device__ inline void atomic_add_f32(float *p, float v)
     __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The chip's work-groups are dealt to its 8 XCDs (each with its own L2) in
+// turn: block b runs on XCD b % 8.  xcd_item(b, run) gives each XCD runs of
+// `run` consecutive work items instead of every 8th one, so that items next to
+// each other in a layout (neighbouring tiles, whose windows overlap in J) run
+// on one XCD at about the same time.  A bijection of the naturals: a grid
+// rounded up by xcd_grid covers every item below it exactly once.  run = 0:
+// the plain order.
+constexpr uint32_t NXCD = 8;
+
+__device__ inline uint32_t xcd_item(uint32_t b, uint32_t run)
+{
+    if (run == 0)
+        return b;
+    const uint32_t j = b % NXCD, k = b / NXCD;
+    return (k / run) * (NXCD * run) + j * run + k % run;
+}
+
+inline uint32_t xcd_grid(uint32_t items, uint32_t run)
+{
+    return run ? (uint32_t)align_up(items, (size_t)NXCD * run) : items;
+}
+
 // One entry of a chunk map (a work item of a tile layout): the chunk's tile
 // and particle range [lo, hi).
 struct alignas(16) ChunkEntry {

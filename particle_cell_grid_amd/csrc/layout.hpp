@@ -256,8 +256,10 @@ __device__ inline ChunkRange find_chunk(uint32_t item, const uint32_t *cum, cons
 {
     ChunkRange r{UINT_MAX, item, 0, 0};
     const uint32_t total = cum[ntiles];
+    if (item >= total)
+        return r;
     const ChunkEntry e = map[item];
-    if (item >= total || e.tile >= ntiles || e.hi <= e.lo)
+    if (e.tile >= ntiles || e.hi <= e.lo)
         return r;
     r.tile = e.tile;
     r.lo = e.lo;

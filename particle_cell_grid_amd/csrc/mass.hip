@@ -442,9 +442,14 @@ __device__ inline void cell_moments(const MassArgs &m, WaveScratch<R> &ws, int l
                     cp[i] = ws.s.c[slot(i)];
                 }
                 __builtin_amdgcn_sched_barrier(0);
+                R cw[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
-                    acc00 = mfma16x4(wa[i], cp[i] * wa[i], acc00);
+                    cw[i] = cp[i] * wa[i];
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    acc00 = mfma16x4(wa[i], cw[i], acc00);
             } else {
                 const int batches = (nb + 7) >> 3;
                 for (int bt = 0; bt < batches; ++bt) {
@@ -483,11 +488,27 @@ __device__ inline void cell_moments(const MassArgs &m, WaveScratch<R> &ws, int l
                         cp[i] = ws.s.c[q];
                     }
                     // keep the reads ahead of the products (the scheduler would
-                    // otherwise interleave them and wait once per step)
+                    // otherwise interleave them and wait once per step), and
+                    // the operand products ahead of the matrix instructions:
+                    // a product issued just before the instruction that reads
+                    // it costs wait states, and on this chip matrix and vector
+                    // instructions of a SIMD do not overlap
+                    __builtin_amdgcn_sched_barrier(0);
+                    R A0[G], A1[G], B0[G], B1[G];
+#pragma unroll
+                    for (int i = 0; i < G; ++i) {
+                        A0[i] = uu[i].x * wa[i];
+                        A1[i] = uu[i].y * wa[i];
+                        B0[i] = cp[i] * A0[i];
+                        B1[i] = cp[i] * A1[i];
+                    }
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int i = 0; i < G; ++i)
-                        mfma_batch(wa[i], uu[i], cp[i]);
+                    for (int i = 0; i < G; ++i) {
+                        acc00 = mfma16x4(A0[i], B0[i], acc00);
+                        acc01 = mfma16x4(A0[i], B1[i], acc01);
+                        acc11 = mfma16x4(A1[i], B1[i], acc11);
+                    }
                 }
             } else {
                 const int batches = (nb + 3) >> 2;

@@ -209,15 +209,33 @@ __global__ __launch_bounds__(TSC_WAVES * WAVE) void k_mass_tsc_group(TscArgs m)
         wave_sync();
         const int nb = (int)std::min<int64_t>(64, hi - base);
         if (MFMA) {
+            // four 4-particle steps at a time: their operands are read first
+            // (one LDS round trip), then the products, then the twelve matrix
+            // instructions back to back; rows past the slice are staged as
+            // zero, so a group's steps past nb add nothing
             const int steps = (nb + 3) >> 2;
-            for (int i = 0; i < steps; ++i) {
-                const int q = 4 * i + kk;
-                const float a0 = ws.s.W[q][r], a1 = ws.s.W[q][16 + r];
-                const float cq = ws.s.c[q];
-                const float b0 = cq * a0, b1 = cq * a1;
-                acc00 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc00, 0, 0, 0);
-                acc01 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc01, 0, 0, 0);
-                acc11 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc11, 0, 0, 0);
+            for (int i0 = 0; i0 < steps; i0 += 4) {
+                float a0[4], a1[4], cq[4], b0[4], b1[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int q = 4 * (i0 + j) + kk;
+                    a0[j] = ws.s.W[q][r];
+                    a1[j] = ws.s.W[q][16 + r];
+                    cq[j] = ws.s.c[q];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    b0[j] = cq[j] * a0[j];
+                    b1[j] = cq[j] * a1[j];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc00 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[j], b0[j], acc00, 0, 0, 0);
+                    acc01 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[j], b1[j], acc01, 0, 0, 0);
+                    acc11 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[j], b1[j], acc11, 0, 0, 0);
+                }
             }
         } else {
             for (int q = 0; q < nb; ++q) {

@@ -261,8 +261,13 @@ __device__ __attribute__((always_inline)) inline uint32_t window_add(
     int base[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-        base[s] = (l0[0] + mv.cell[s][0] - mv.lo[0]) +
-                  TE * ((l0[1] + mv.cell[s][1] - mv.lo[1]) + TE * (l0[2] + mv.cell[s][2] - mv.lo[2]));
+        // every term is in [0, TE) once the stencil fits: 24-bit multiplies
+        // (full rate; a 32-bit one issues at a quarter of it)
+        base[s] = (int)((unsigned)(l0[0] + mv.cell[s][0] - mv.lo[0]) +
+                        __umul24((unsigned)TE,
+                                 (unsigned)(l0[1] + mv.cell[s][1] - mv.lo[1]) +
+                                     __umul24((unsigned)TE,
+                                              (unsigned)(l0[2] + mv.cell[s][2] - mv.lo[2]))));
     auto add = [&](int s, int c, int j, float v) {
         const int k1 = c == 0 ? 1 : 0, k2 = c == 2 ? 1 : 2;
         Acc *a = &win[base[s] + c * vol + (j & 1) * stride[k1] + (j >> 1) * stride[k2]];

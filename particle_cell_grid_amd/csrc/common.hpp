@@ -94,6 +94,14 @@ __device__ inline int wrap_index(int x, int n)
     return r < 0 ? r + n : r;
 }
 
+// a * b + c for a, b, c >= 0 and a, b < 2^24 (an index within a tile's
+// window): a 24-bit multiply issues at the full rate, a 32-bit one (or the
+// 64-bit multiply-add the compiler may pick) at a quarter of it.
+__device__ inline int mad24(int a, int b, int c)
+{
+    return (int)(__umul24((unsigned)a, (unsigned)b) + (unsigned)c);
+}
+
 // Clamp a coordinate into [0, n] (NaN -> 0) so a broken precondition can never
 // produce an out-of-range index; exact for valid input.
 __device__ inline float clamp_coord(float x, float n) { return fminf(fmaxf(x, 0.0f), n); }

@@ -377,10 +377,12 @@ __device__ __attribute__((always_inline)) inline uint32_t deposit_supported(
 #pragma unroll
         for (int ax = 0; ax < M; ++ax)
             ampx[k][ax] = amp[k] * W[0][ax];
-    const int sbase = DIM == 3 ? (s[2] * TE + s[1]) * TE + s[0] : (DIM == 2 ? s[1] * TE + s[0] : s[0]);
+    // window offsets: in [0, TE) on this path
+    const int sbase = DIM == 3 ? mad24(mad24(s[2], TE, s[1]), TE, s[0])
+                               : (DIM == 2 ? mad24(s[1], TE, s[0]) : s[0]);
     if (MODE == ACC_PACKED) {
-        const int cell = DIM == 3 ? (s[2] * c.cedge + s[1]) * c.cedge + s[0]
-                                  : (DIM == 2 ? s[1] * c.cedge + s[0] : s[0]);
+        const int cell = DIM == 3 ? mad24(mad24(s[2], c.cedge, s[1]), c.cedge, s[0])
+                                  : (DIM == 2 ? mad24(s[1], c.cedge, s[0]) : s[0]);
         __hip_atomic_fetch_add(&sc.cnt[cell], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
 #pragma unroll

@@ -427,7 +427,7 @@ __global__ __launch_bounds__(256) void k_inc_validate(const uint32_t *__restrict
 // work-group (LDS).  Launched with 256 threads and 4 particles per lane for
 // chunks of thousands of particles, with one wave and one particle per lane
 // for small ones.
-template <int DIM, int ORDER, int COUNT_EPT>
+template <int DIM, int ORDER, int COUNT_EPT, bool POW2>
 __global__ __launch_bounds__(256) void k_inc_count(IncGeom a, const float *x0, const float *x1,
                                                    const float *x2)
 {
@@ -449,30 +449,33 @@ __global__ __launch_bounds__(256) void k_inc_count(IncGeom a, const float *x0, c
     int sc[3];
     tile_coords(s_tile, a.g, sc);
     const uint32_t lo = s_lo, hi = s_hi, stride = blockDim.x;
-    // clamped loads: no branch around them, so the next batch stays in flight
+    // clamped loads: no branch around them, so the next batch stays in flight;
+    // addressed from the chunk's first particle (uniform) by a 32-bit offset,
+    // which needs no 64-bit address arithmetic per lane
+    const float *c0 = x0 + lo, *c1 = DIM > 1 ? x1 + lo : nullptr, *c2 = DIM > 2 ? x2 + lo : nullptr;
+    const uint32_t last = hi - 1 - lo;
     float c[COUNT_EPT][3], nc[COUNT_EPT][3];
+    auto at = [](const float *base, uint32_t q) {
+        return *reinterpret_cast<const float *>(reinterpret_cast<const char *>(base) + q * 4u);
+    };
     auto load = [&](uint32_t b, float (*dst)[3]) {
 #pragma unroll
         for (int e = 0; e < COUNT_EPT; ++e) {
-            const uint32_t q = min(b + e * stride, hi - 1);
-            dst[e][0] = x0[q];
-            dst[e][1] = DIM > 1 ? x1[q] : 0.f;
-            dst[e][2] = DIM > 2 ? x2[q] : 0.f;
+            const uint32_t q = min(b - lo + e * stride, last);  // below a chunk's length
+            dst[e][0] = at(c0, q);
+            dst[e][1] = DIM > 1 ? at(c1, q) : 0.f;
+            dst[e][2] = DIM > 2 ? at(c2, q) : 0.f;
         }
     };
     bool far = false;
-    load(lo + threadIdx.x, nc);
-    for (uint32_t b = lo + threadIdx.x; b - threadIdx.x < hi; b += COUNT_EPT * stride) {
-#pragma unroll
-        for (int e = 0; e < COUNT_EPT; ++e)
-#pragma unroll
-            for (int k = 0; k < 3; ++k)
-                c[e][k] = nc[e][k];
-        load(b + COUNT_EPT * stride, nc);
+    auto classify = [&](uint32_t b, float (*cx)[3]) {
 #pragma unroll
         for (int e = 0; e < COUNT_EPT; ++e) {
             const bool valid = b + e * stride < hi;
-            int dir = tile_dir<DIM, ORDER>(c[e][0], c[e][1], c[e][2], a.g, sc);
+            // the geometry test is a template argument here: a per-particle
+            // uniform branch would split the batch's straight-line code
+            const int dir = POW2 ? particle_dir_pow2<DIM, ORDER>(cx[e][0], cx[e][1], cx[e][2], a.g, sc)
+                                 : particle_dir<DIM, ORDER>(cx[e][0], cx[e][1], cx[e][2], a.g, sc);
             far |= valid && dir < 0;
             const bool ok = valid && dir >= 0;
             // most particles stay in their tile: one ballot counts those, and
@@ -483,6 +486,18 @@ __global__ __launch_bounds__(256) void k_inc_count(IncGeom a, const float *x0, c
             if (ok && dir != DIR_STAY)
                 atomicAdd(&s_cnt[dir], 1u);
         }
+    };
+    // two batch buffers in turn (no register copies): the next batch loads
+    // while this one is classified
+    const uint32_t step = COUNT_EPT * stride;
+    load(lo + threadIdx.x, c);
+    for (uint32_t b = lo + threadIdx.x; b - threadIdx.x < hi; b += 2 * step) {
+        load(b + step, nc);
+        classify(b, c);
+        if (b + step - threadIdx.x >= hi)
+            break;
+        load(b + 2 * step, c);
+        classify(b + step, nc);
     }
     if (__ballot(far))
         if (lane_id() == 0)
@@ -1005,12 +1020,11 @@ pcg_status incremental_launch(const IncGeom &a, const float *const key_x[3], uin
     const float *x1 = DIM > 1 ? key_x[1] : nullptr, *x2 = DIM > 2 ? key_x[2] : nullptr;
     // a work-group per chunk: 256 threads when a tile's slice averages a
     // chunk or more, one wave when chunks are small
-    if (a.count / std::max<int64_t>(1, a.ntiles) >= (int64_t)INC_CHUNK)
-        PCG_TRY(launch("sort_inc_count", k_inc_count<DIM, ORDER, 4>, dim3(nwork), dim3(256), 0, st,
-                       a, key_x[0], x1, x2));
-    else
-        PCG_TRY(launch("sort_inc_count", k_inc_count<DIM, ORDER, 1>, dim3(nwork), dim3(64), 0, st,
-                       a, key_x[0], x1, x2));
+    const bool big = a.count / std::max<int64_t>(1, a.ntiles) >= (int64_t)INC_CHUNK;
+    auto kern = big ? (a.g.pow2 ? k_inc_count<DIM, ORDER, 4, true> : k_inc_count<DIM, ORDER, 4, false>)
+                    : (a.g.pow2 ? k_inc_count<DIM, ORDER, 1, true> : k_inc_count<DIM, ORDER, 1, false>);
+    PCG_TRY(launch("sort_inc_count", kern, dim3(nwork), dim3(big ? 256 : 64), 0, st, a, key_x[0],
+                   x1, x2));
     PCG_TRY(launch("sort_inc_chunk_prefix", k_inc_chunk_prefix,
                    dim3((a.ntiles * NDIR + 255) / 256), dim3(256), 0, st, a));
     PCG_TRY(launch("sort_inc_tiles", k_inc_tiles, dim3((a.ntiles + 1 + 2047) / 2048 * 8),

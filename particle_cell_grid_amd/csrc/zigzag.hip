@@ -432,7 +432,7 @@ constexpr int ZZ_UW = PCG_ZZ_UW;                   // particles per lane in flig
 // does.  If the device flag says the incremental path does not hold, the
 // kernel deposits only (the general sort then regroups).  The scale check and
 // rerun are those of k_zigzag_tiled; the rerun deposits without moving.
-template <int TEC>
+template <int TEC, bool FAST>
 __global__ __launch_bounds__(ZZ_WAVES * WAVE) void k_zigzag_regroup(ZzArgs m, ZzMoveArgs mv)
 {
     using Acc = unsigned long long;
@@ -487,20 +487,34 @@ __global__ __launch_bounds__(ZZ_WAVES * WAVE) void k_zigzag_regroup(ZzArgs m, Zz
             __builtin_amdgcn_wave_barrier();
         }
         // no branch around the loads: a lane past the chunk reloads its last
-        // particle (never used)
-        Raw nx[ZZ_UW];
-        auto load_group = [&](uint32_t base) __attribute__((always_inline)) {
+        // particle (never used).  FAST: every array is under 4 GiB, so each
+        // element is a 32-bit byte offset from its array's (uniform) base, with
+        // no 64-bit address arithmetic per lane
+        auto load_one = [&](uint32_t p) __attribute__((always_inline)) {
+            if constexpr (FAST) {
+                auto at = [p](const float *base) {
+                    return *reinterpret_cast<const float *>(reinterpret_cast<const char *>(base) +
+                                                            p * 4u);
+                };
+                Raw r;
 #pragma unroll
-            for (int u = 0; u < ZZ_UW; ++u)
-                nx[u] = load_raw(m, min(base + u * WAVE + lane, chi - 1));
+                for (int k = 0; k < 3; ++k) {
+                    r.a[k] = at(m.xp[k]);
+                    r.b[k] = at(m.x[k]);
+                }
+                r.q = at(m.q);
+                r.w = at(m.w);
+                return r;
+            } else {
+                return load_raw(m, p);
+            }
         };
-        load_group(clo);
-        for (uint32_t base = clo; base < chi; base += ZZ_UW * WAVE) {
-            Raw cur[ZZ_UW];
+        auto load_group = [&](uint32_t base, Raw *dst) __attribute__((always_inline)) {
 #pragma unroll
             for (int u = 0; u < ZZ_UW; ++u)
-                cur[u] = nx[u];
-            load_group(base + ZZ_UW * WAVE);
+                dst[u] = load_one(min(base + u * WAVE + lane, chi - 1));
+        };
+        auto group = [&](uint32_t base, Raw *cur) __attribute__((always_inline)) {
 #pragma unroll
             for (int u = 0; u < ZZ_UW; ++u)
                 asm volatile("" ::"v"(cur[u].a[0]), "v"(cur[u].a[1]), "v"(cur[u].a[2]),
@@ -512,8 +526,10 @@ __global__ __launch_bounds__(ZZ_WAVES * WAVE) void k_zigzag_regroup(ZzArgs m, Zz
                 const bool valid = p < chi;
                 if (move) {
                     // wave-uniform: the slot comes from the whole wave's directions
-                    const int d = tile_dir<3, 1>(cur[u].b[0], cur[u].b[1], cur[u].b[2],
-                                                     mv.inc.g, tc);
+                    const int d =
+                        FAST ? particle_dir_pow2<3, 1>(cur[u].b[0], cur[u].b[1], cur[u].b[2],
+                                                       mv.inc.g, tc)
+                             : tile_dir<3, 1>(cur[u].b[0], cur[u].b[1], cur[u].b[2], mv.inc.g, tc);
                     const bool ok = valid && d >= 0;  // d < 0 cannot occur: the flag is clear
                     const uint32_t pos = walk_slot(run, d, ok);
                     if (ok && pos < (uint64_t)mv.inc.count) {
@@ -533,8 +549,13 @@ __global__ __launch_bounds__(ZZ_WAVES * WAVE) void k_zigzag_regroup(ZzArgs m, Zz
                         }
                         if (!staged) {
 #pragma unroll
-                            for (int k = 0; k < 8; ++k)
-                                mv.out[k][pos] = f[k];
+                            for (int k = 0; k < 8; ++k) {
+                                if constexpr (FAST)
+                                    *reinterpret_cast<float *>(reinterpret_cast<char *>(mv.out[k]) +
+                                                               pos * 4u) = f[k];
+                                else
+                                    mv.out[k][pos] = f[k];
+                            }
                         }
                     }
                 }
@@ -544,6 +565,19 @@ __global__ __launch_bounds__(ZZ_WAVES * WAVE) void k_zigzag_regroup(ZzArgs m, Zz
                     escaped += window_add<true>(m, win, TE, vol, ws, mm, k_scale, true, assumed);
                 }
             }
+        };
+        // two groups of registers in turn (no copies): the next group loads
+        // while this one is deposited
+        Raw ga[ZZ_UW], gb[ZZ_UW];
+        constexpr uint32_t STEP = ZZ_UW * WAVE;
+        load_group(clo, ga);
+        for (uint32_t base = clo; base < chi; base += 2 * STEP) {
+            load_group(base + STEP, gb);
+            group(base, ga);
+            if (base + STEP >= chi)
+                break;
+            load_group(base + 2 * STEP, ga);
+            group(base + STEP, gb);
         }
     }
     __syncthreads();
@@ -596,11 +630,15 @@ pcg_status zz_regroup_hook(void *ctx, const IncGeom &inc, const uint32_t *off, u
     const int64_t per_tile = c.m.n_part / std::max<int64_t>(1, c.ntiles);
     const int waves = (int)std::max<int64_t>(
         1, std::min<int64_t>(ZZ_WAVES, (per_tile + INC_CHUNK - 1) / INC_CHUNK));
-    auto kern = c.m.TE == 7    ? k_zigzag_regroup<7>
-                : c.m.TE == 9  ? k_zigzag_regroup<9>
-                : c.m.TE == 11 ? k_zigzag_regroup<11>
-                : c.m.TE == 13 ? k_zigzag_regroup<13>
-                               : k_zigzag_regroup<0>;
+    // the fast variant: power-of-two geometry (masked tile directions) and
+    // arrays under 4 GiB (32-bit byte offsets)
+    const bool fast = inc.g.pow2 && inc.count <= ((int64_t)1 << 30);
+    auto pick = [fast](auto k_fast, auto k_gen) { return fast ? k_fast : k_gen; };
+    auto kern = c.m.TE == 7    ? pick(k_zigzag_regroup<7, true>, k_zigzag_regroup<7, false>)
+                : c.m.TE == 9  ? pick(k_zigzag_regroup<9, true>, k_zigzag_regroup<9, false>)
+                : c.m.TE == 11 ? pick(k_zigzag_regroup<11, true>, k_zigzag_regroup<11, false>)
+                : c.m.TE == 13 ? pick(k_zigzag_regroup<13, true>, k_zigzag_regroup<13, false>)
+                               : pick(k_zigzag_regroup<0, true>, k_zigzag_regroup<0, false>);
     size_t stat = 2048;  // above the kernel's static LDS (run counts, reductions)
     {
         hipFuncAttributes fa{};

@@ -11,12 +11,15 @@
 // block T[a][b] = sum_p c_p W_a(p) W_b(p) (c = q w) is one product over the
 // group's particles: rows padded to 32 and computed as the three tiles (0,0),
 // (0,1), (1,1) of v_mfma_f32_16x16x4_f32 per 4 particles (T is symmetric, so
-// tile (1,0) is tile (0,1) transposed).  The block is added to M with device
-// atomics, 729 per group ([MM] §3.4).
+// tile (1,0) is tile (0,1) transposed).  [MM] §3.4 adds each block to M with
+// device atomics, 729 per group; the MFMA variant here sums the blocks of a
+// brick of 4 x 4 x 2 groups in an LDS patch of fixed-point node rows first and
+// adds the patch to M once (about 250 atomics per group, each node row of 125
+// floats by consecutive lanes).
 //
-// Variants: MFMA, VALU (each lane sums its node pairs over the staged
-// particles) and FLAT (one thread per particle, 729 atomics; also the unsorted
-// tail).  A particle found in a slice whose group it does not belong to (a
+// Variants: MFMA (bricks), VALU (one wave per group, each lane summing its
+// node pairs over the staged particles, 729 atomics per group) and FLAT (one
+// thread per particle, 729 atomics; also the unsorted tail).  A particle found in a slice whose group it does not belong to (a
 // stale layout) is deposited by its own lane with the flat path.
 //
 // The tensor (ECSIM) matrix with TSC weights ([MM] Eq.(4)-(5); §4.1 Fig. 9)
@@ -152,45 +155,46 @@ __device__ inline void wave_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One wave per group: group = the wave's global index (groups are the support
-// base nodes, linear index gx + n_x (gy + n_y gz)).
-template <bool MFMA>
-__global__ __launch_bounds__(TSC_WAVES * WAVE) void k_mass_tsc_group(TscArgs m)
-{
-    __shared__ TscScratch scratch[TSC_WAVES];
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), lane = lane_id();
-    TscScratch &ws = scratch[wave];
-    // neighbouring groups (which share M rows) on one XCD: blocks are dealt to
-    // the 8 XCDs round-robin
-    const uint32_t nblocks = (m.ngroups + TSC_WAVES - 1) / TSC_WAVES;
-    const uint32_t per = (nblocks + 7) / 8;
-    const uint32_t blk = (blockIdx.x % 8) * per + blockIdx.x / 8;
-    const uint32_t g = blk * TSC_WAVES + wave;
-    if (blk >= nblocks || g >= m.ngroups)
-        return;
-    const int64_t lo = std::min<int64_t>(m.offsets[g], m.n_part);
-    const int64_t hi = std::min<int64_t>(m.offsets[g + 1], m.n_part);
-    if (hi <= lo)
-        return;
-    int gb[3];
-    gb[0] = (int)(g % (uint32_t)m.n[0]);
-    gb[1] = (int)((g / (uint32_t)m.n[0]) % (uint32_t)m.n[1]);
-    gb[2] = (int)(g / ((uint32_t)m.n[0] * (uint32_t)m.n[1]));
+// The 27 x 27 block of one group (support base gb, wrapped; slice [lo, hi))
+// into ws.Tm (rows and columns 0..26), one wave.  MFMA: the three 16x16 tiles
+// on the matrix cores; VALU: each lane sums its node pairs pr = lane + 64 k
+// into tv.  A particle of the slice that does not belong to the group (a stale
+// layout) is deposited by its own lane with global atomics.
+constexpr int TSC_PAIRS = (TSC_NODES * TSC_NODES + WAVE - 1) / WAVE;  // pairs per lane
 
+// A particle's five inputs, as loaded (slot lo + lane of a slice, clamped).
+struct TscRaw {
+    float x[3], q, w;
+};
+
+__device__ inline TscRaw tsc_load(const TscArgs &m, int64_t lo, int64_t hi, int lane)
+{
+    const int64_t p = std::min<int64_t>(lo + lane, hi - 1);  // clamped
+    TscRaw r;
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+        r.x[k] = ld(m.x[k], p);
+    r.q = ld(m.q, p);
+    r.w = ld(m.w, p);
+    return r;
+}
+
+template <bool MFMA>
+__device__ inline void tsc_group_block(const TscArgs &m, TscScratch &ws, int lane, const int *gb,
+                                       int64_t lo, int64_t hi, float *tv,
+                                       const TscRaw *first = nullptr)
+{
     const int r = lane & 15, kk = lane >> 4;
     floatx4 acc00 = {0, 0, 0, 0}, acc01 = {0, 0, 0, 0}, acc11 = {0, 0, 0, 0};
-    // VALU: lane owns node pairs lane + 64 k (k < 12; 729 pairs)
-    constexpr int PAIRS = (TSC_NODES * TSC_NODES + WAVE - 1) / WAVE;
-    float tv[PAIRS];
 #pragma unroll
-    for (int k = 0; k < PAIRS; ++k)
+    for (int k = 0; k < TSC_PAIRS; ++k)
         tv[k] = 0.0f;
 
     for (int64_t base = lo; base < hi; base += 64) {
-        const int64_t p = std::min<int64_t>(base + lane, hi - 1);  // clamped
         const bool valid = base + lane < hi;
-        const TscParticle P =
-            tsc_particle(m, ld(m.x[0], p), ld(m.x[1], p), ld(m.x[2], p), ld(m.q, p), ld(m.w, p));
+        // the first batch may come loaded by the caller (a batch ahead)
+        const TscRaw in = (first && base == lo) ? *first : tsc_load(m, base, hi, lane);
+        const TscParticle P = tsc_particle(m, in.x[0], in.x[1], in.x[2], in.q, in.w);
         const bool home = P.base[0] == gb[0] && P.base[1] == gb[1] && P.base[2] == gb[2];
         const bool take = valid && home;
         if (valid && !home)
@@ -241,7 +245,7 @@ __global__ __launch_bounds__(TSC_WAVES * WAVE) void k_mass_tsc_group(TscArgs m)
             for (int q = 0; q < nb; ++q) {
                 const float cq = ws.s.c[q];
 #pragma unroll
-                for (int k = 0; k < PAIRS; ++k) {
+                for (int k = 0; k < TSC_PAIRS; ++k) {
                     const int pr = lane + WAVE * k;
                     if (pr < TSC_NODES * TSC_NODES)
                         tv[k] += cq * ws.s.W[q][pr / TSC_NODES] * ws.s.W[q][pr % TSC_NODES];
@@ -263,14 +267,185 @@ __global__ __launch_bounds__(TSC_WAVES * WAVE) void k_mass_tsc_group(TscArgs m)
         }
         wave_sync();
     }
+}
+
+// Group coordinates of linear group index g (gx + n_x (gy + n_y gz)).
+__device__ inline void group_coords(const TscArgs &m, uint32_t g, int *gb)
+{
+    gb[0] = (int)(g % (uint32_t)m.n[0]);
+    gb[1] = (int)((g / (uint32_t)m.n[0]) % (uint32_t)m.n[1]);
+    gb[2] = (int)(g / ((uint32_t)m.n[0] * (uint32_t)m.n[1]));
+}
+
+// One wave per group: group = the wave's global index (groups are the support
+// base nodes, linear index gx + n_x (gy + n_y gz)); its 729 node pairs go to M
+// with device atomics.
+template <bool MFMA>
+__global__ __launch_bounds__(TSC_WAVES * WAVE) void k_mass_tsc_group(TscArgs m)
+{
+    __shared__ TscScratch scratch[TSC_WAVES];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), lane = lane_id();
+    TscScratch &ws = scratch[wave];
+    // neighbouring groups (which share M rows) on one XCD: blocks are dealt to
+    // the 8 XCDs round-robin
+    const uint32_t nblocks = (m.ngroups + TSC_WAVES - 1) / TSC_WAVES;
+    const uint32_t per = (nblocks + 7) / 8;
+    const uint32_t blk = (blockIdx.x % 8) * per + blockIdx.x / 8;
+    const uint32_t g = blk * TSC_WAVES + wave;
+    if (blk >= nblocks || g >= m.ngroups)
+        return;
+    const int64_t lo = std::min<int64_t>(m.offsets[g], m.n_part);
+    const int64_t hi = std::min<int64_t>(m.offsets[g + 1], m.n_part);
+    if (hi <= lo)
+        return;
+    int gb[3];
+    group_coords(m, g, gb);
+    float tv[TSC_PAIRS];
+    tsc_group_block<MFMA>(m, ws, lane, gb, lo, hi, tv);
 #pragma unroll
-    for (int k = 0; k < PAIRS; ++k) {
+    for (int k = 0; k < TSC_PAIRS; ++k) {
         const int pr = lane + WAVE * k;
         if (pr < TSC_NODES * TSC_NODES) {
             const int a = pr / TSC_NODES, b = pr % TSC_NODES;
             const float v = MFMA ? ws.Tm[a][b] : tv[k];
             atomic_add_f32(&m.M[(size_t)tsc_node(m, gb, a) * TSC_OFFS + tsc_offset(a, b)], v);
         }
+    }
+}
+
+// The same matrix with the groups of a brick of TB_X x TB_Y x TB_Z bases per
+// work-group: each group's block is added into an LDS patch of the brick's
+// (TB + 2)^3 nodes x 125 offsets in 32-bit fixed point (integer LDS atomics,
+// exact and order-independent), and the patch goes to M once, each node row of
+// 125 floats by consecutive lanes: some 36 cache-line atomics per group instead
+// of about 240 when every group adds its 729 values to M itself.  The scale
+// 2^k keeps every partial sum of a patch entry below 2^30: a particle adds at
+// most (3/4)^2 |q w| to an entry, so 2^k (9/16) sum|q w| over the brick's
+// particles < 2^30 bounds them all (products are rounded to the nearest unit,
+// 2^-k, so the error of an entry is at most half a unit per particle).
+constexpr int TB_X = 4, TB_Y = 4, TB_Z = 2;
+constexpr int TP_X = TB_X + 2, TP_Y = TB_Y + 2, TP_Z = TB_Z + 2;
+constexpr int TP_NODES = TP_X * TP_Y * TP_Z;
+constexpr size_t TSC_PATCH_BYTES = (size_t)TP_NODES * TSC_OFFS * 4;
+constexpr int TSC_BRICK_WAVES = 8;
+
+__global__ __launch_bounds__(TSC_BRICK_WAVES * WAVE) void k_mass_tsc_brick(TscArgs m)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    int *patch = reinterpret_cast<int *>(smem);  // [TP_NODES][125]
+    __shared__ TscScratch scratch[TSC_BRICK_WAVES];
+    __shared__ float red[TSC_BRICK_WAVES];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), lane = lane_id();
+    TscScratch &ws = scratch[wave];
+    const int nbx = (m.n[0] + TB_X - 1) / TB_X, nby = (m.n[1] + TB_Y - 1) / TB_Y;
+    const int bi = (int)(blockIdx.x % (uint32_t)nbx);
+    const int bj = (int)((blockIdx.x / (uint32_t)nbx) % (uint32_t)nby);
+    const int bk = (int)(blockIdx.x / ((uint32_t)nbx * (uint32_t)nby));
+    const int org[3] = {bi * TB_X, bj * TB_Y, bk * TB_Z};
+    const int cnt[3] = {min(TB_X, m.n[0] - org[0]), min(TB_Y, m.n[1] - org[1]),
+                        min(TB_Z, m.n[2] - org[2])};
+    const int ngb = cnt[0] * cnt[1] * cnt[2];
+    for (int i = threadIdx.x; i < TP_NODES * TSC_OFFS; i += blockDim.x)
+        patch[i] = 0;
+    // the brick's local group j: base org + (j % cnt0, (j / cnt0) % cnt1, j / (cnt0 cnt1))
+    auto local = [&](int j, int *lg) {
+        lg[0] = j % cnt[0];
+        lg[1] = (j / cnt[0]) % cnt[1];
+        lg[2] = j / (cnt[0] * cnt[1]);
+    };
+    auto slice = [&](const int *lg, int64_t &lo, int64_t &hi) {
+        const uint32_t g = (uint32_t)(org[0] + lg[0]) +
+                           (uint32_t)m.n[0] * ((uint32_t)(org[1] + lg[1]) +
+                                               (uint32_t)m.n[1] * (uint32_t)(org[2] + lg[2]));
+        lo = std::min<int64_t>(m.offsets[g], m.n_part);
+        hi = std::max<int64_t>(lo, std::min<int64_t>(m.offsets[g + 1], m.n_part));
+    };
+    // sum |q w| over the brick's particles (every wave its groups)
+    float sum = 0.0f;
+    for (int j = wave; j < ngb; j += TSC_BRICK_WAVES) {
+        int lg[3];
+        local(j, lg);
+        int64_t lo, hi;
+        slice(lg, lo, hi);
+        for (int64_t p = lo + lane; p < hi; p += WAVE)
+            sum += fabsf(ld(m.q, p) * ld(m.w, p));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        sum += __shfl_xor(sum, off);
+    if (lane == 0)
+        red[wave] = sum;
+    __syncthreads();
+    float total = 0.0f;
+#pragma unroll
+    for (int w = 0; w < TSC_BRICK_WAVES; ++w)
+        total += red[w];
+    if (total == 0.0f)
+        return;  // no particle adds anything (every wave sees the same total)
+    // 2^k (9/16) total < 2^30: half the int32 range, which covers the fp32
+    // rounding of the sum and the half unit each rounded product may add
+    int e = 0;
+    frexpf(0.5625f * total, &e);  // value < 2^e
+    const int k_scale = max(-126, min(126, 30 - e));
+    const float scale = ldexpf(1.0f, k_scale), inv_scale = ldexpf(1.0f, -k_scale);
+
+    // each group's first batch is loaded while the wave's previous group is
+    // computed
+    int64_t nlo = 0, nhi = 0;
+    TscRaw nxt{};
+    if (wave < ngb) {
+        int lg[3];
+        local(wave, lg);
+        slice(lg, nlo, nhi);
+        if (nhi > nlo)
+            nxt = tsc_load(m, nlo, nhi, lane);
+    }
+    for (int j = wave; j < ngb; j += TSC_BRICK_WAVES) {
+        int lg[3];
+        local(j, lg);
+        const int64_t lo = nlo, hi = nhi;
+        const TscRaw cur = nxt;
+        if (j + TSC_BRICK_WAVES < ngb) {
+            int ln3[3];
+            local(j + TSC_BRICK_WAVES, ln3);
+            slice(ln3, nlo, nhi);
+            if (nhi > nlo)
+                nxt = tsc_load(m, nlo, nhi, lane);
+        }
+        if (hi <= lo)
+            continue;
+        int gb[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            gb[k] = org[k] + lg[k];
+        float tv[TSC_PAIRS];
+        tsc_group_block<true>(m, ws, lane, gb, lo, hi, tv, &cur);
+#pragma unroll
+        for (int k = 0; k < TSC_PAIRS; ++k) {
+            const int pr = lane + WAVE * k;
+            if (pr < TSC_NODES * TSC_NODES) {
+                const int a = pr / TSC_NODES, b = pr % TSC_NODES;
+                const int ln = (lg[0] + a % 3) + TP_X * ((lg[1] + (a / 3) % 3) + TP_Y * (lg[2] + a / 9));
+                atomicAdd(&patch[ln * TSC_OFFS + tsc_offset(a, b)],
+                          __float2int_rn(ws.Tm[a][b] * scale));
+            }
+        }
+        wave_sync();  // Tm is the next group's staging area
+    }
+    __syncthreads();
+    // the patch to M: node rows of 125 floats, consecutive threads on
+    // consecutive offsets; entries no group touched stay zero and are skipped
+    for (int i = threadIdx.x; i < TP_NODES * TSC_OFFS; i += blockDim.x) {
+        const int v = patch[i];
+        if (v == 0)
+            continue;
+        const int ln = i / TSC_OFFS, o = i - ln * TSC_OFFS;
+        const int lx = ln % TP_X, ly = (ln / TP_X) % TP_Y, lz = ln / (TP_X * TP_Y);
+        const int gx = wrap_add(org[0], lx, m.n[0]);
+        const int gy = wrap_add(org[1], ly, m.n[1]);
+        const int gz = wrap_add(org[2], lz, m.n[2]);
+        const size_t node = (size_t)gx + (size_t)m.n[0] * ((size_t)gy + (size_t)m.n[1] * gz);
+        atomic_add_f32(&m.M[node * TSC_OFFS + o], (float)v * inv_scale);
     }
 }
 
@@ -354,8 +529,7 @@ struct TscTensorStage {
     float u[64][4];
     float c[64];
 };
-// pairs per lane (729 over 64 lanes), flushed in two halves
-constexpr int TSC_PAIRS = (TSC_NODES * TSC_NODES + WAVE - 1) / WAVE;
+// pairs per lane (729 over 64 lanes: TSC_PAIRS), flushed in two halves
 constexpr int TSC_HALF = (TSC_PAIRS + 1) / 2;
 union TscTensorScratch {
     TscTensorStage s;
@@ -620,10 +794,23 @@ pcg_status assemble_tsc(const char *who, const pcg_grid *grid, const pcg_particl
             PCG_TRY(launch(valu ? "mass_tsc_tensor_valu" : "mass_tsc_tensor_mfma",
                            valu ? k_mass_tsc_tensor_group<false> : k_mass_tsc_tensor_group<true>,
                            dim3(blocks), dim3(TSC_WAVES * WAVE), 0, st, m));
-        else
-            PCG_TRY(launch(valu ? "mass_tsc_valu" : "mass_tsc_mfma",
-                           valu ? k_mass_tsc_group<false> : k_mass_tsc_group<true>, dim3(blocks),
+        else if (valu)
+            PCG_TRY(launch("mass_tsc_valu", k_mass_tsc_group<false>, dim3(blocks),
                            dim3(TSC_WAVES * WAVE), 0, st, m));
+        else {
+            static const bool lds_ok =
+                hipFuncSetAttribute((const void *)k_mass_tsc_brick,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)TSC_PATCH_BYTES) == hipSuccess;
+            if (!lds_ok)
+                return fail(PCG_EHIP, "%s: cannot raise dynamic LDS to %zu bytes", who,
+                            TSC_PATCH_BYTES);
+            const uint32_t bricks = (uint32_t)(((grid->n[0] + TB_X - 1) / TB_X) *
+                                               ((grid->n[1] + TB_Y - 1) / TB_Y) *
+                                               ((grid->n[2] + TB_Z - 1) / TB_Z));
+            PCG_TRY(launch("mass_tsc_mfma", k_mass_tsc_brick, dim3(bricks),
+                           dim3(TSC_BRICK_WAVES * WAVE), TSC_PATCH_BYTES, st, m));
+        }
     }
     return flat(groups->n_partitioned, count);
 }

@@ -72,6 +72,32 @@ def test_tsc_mass_ragged_stale_and_tail(orc, variant):
     _check(M, orc.mass_matrix_scalar_tsc(n, s.x, s.q, s.w))
 
 
+@pytest.mark.parametrize("scale", [1e-20, 1e15])
+def test_tsc_mass_charge_scale(orc, scale):
+    """The matrix-core path sums each brick of support groups in fixed point
+    whose unit follows the brick's sum |q w|: charges far from 1 keep their
+    relative precision."""
+    wl = synthetic.mass_workload([8, 7, 6], 24, seed=85)
+    s, off = _grouped(orc, wl)
+    s.w = (s.w.astype(np.float64) * scale).astype(np.float32)
+    _check(_run(wl.n, s, off, pcg.PCG_MASS_MFMA), orc.mass_matrix_scalar_tsc(wl.n, s.x, s.q, s.w))
+
+
+def test_tsc_mass_adds_to_M(orc):
+    """M += the matrix: a non-zero M keeps its values under the additions."""
+    wl = synthetic.mass_workload([6, 5, 7], 16, seed=86)
+    s, off = _grouped(orc, wl)
+    init = np.random.default_rng(87).standard_normal((7, 5, 6, 125)).astype(np.float32)
+    M = torch.from_numpy(init.copy()).to(DEV)
+    groups = pcg.Layout(T=1, order=2, tile_offsets=dev(off.view(np.int32)), n_partitioned=s.count,
+                        drift=0)
+    pcg.assemble_mass_matrix_scalar_tsc(wl.n, [dev(a) for a in s.x], dev(s.q), dev(s.w), M, groups,
+                                        pcg.PCG_MASS_MFMA)
+    torch.cuda.synchronize()
+    ref = orc.mass_matrix_scalar_tsc(wl.n, s.x, s.q, s.w)
+    _check(M.cpu().numpy().astype(np.float64) - init, ref)
+
+
 def test_tsc_mass_no_layout_is_flat(orc):
     wl = synthetic.mass_workload([5, 6, 7], 9, seed=82)
     _check(_run(wl.n, wl, None, pcg.PCG_MASS_AUTO, use_layout=False),

@@ -182,7 +182,7 @@ __device__ inline TscRaw tsc_load(const TscArgs &m, int64_t lo, int64_t hi, int 
 template <bool MFMA>
 __device__ inline void tsc_group_block(const TscArgs &m, TscScratch &ws, int lane, const int *gb,
                                        int64_t lo, int64_t hi, float *tv,
-                                       const TscRaw *first = nullptr)
+                                       const TscRaw *ahead = nullptr)
 {
     const int r = lane & 15, kk = lane >> 4;
     floatx4 acc00 = {0, 0, 0, 0}, acc01 = {0, 0, 0, 0}, acc11 = {0, 0, 0, 0};
@@ -192,8 +192,10 @@ __device__ inline void tsc_group_block(const TscArgs &m, TscScratch &ws, int lan
 
     for (int64_t base = lo; base < hi; base += 64) {
         const bool valid = base + lane < hi;
-        // the first batch may come loaded by the caller (a batch ahead)
-        const TscRaw in = (first && base == lo) ? *first : tsc_load(m, base, hi, lane);
+        // the first two batches may come loaded by the caller (ahead[0], [1])
+        const TscRaw in = (ahead && base == lo)        ? ahead[0]
+                          : (ahead && base == lo + 64) ? ahead[1]
+                                                       : tsc_load(m, base, hi, lane);
         const TscParticle P = tsc_particle(m, in.x[0], in.x[1], in.x[2], in.q, in.w);
         const bool home = P.base[0] == gb[0] && P.base[1] == gb[1] && P.base[2] == gb[2];
         const bool take = valid && home;
@@ -389,29 +391,28 @@ __global__ __launch_bounds__(TSC_BRICK_WAVES * WAVE) void k_mass_tsc_brick(TscAr
     const int k_scale = max(-126, min(126, 30 - e));
     const float scale = ldexpf(1.0f, k_scale), inv_scale = ldexpf(1.0f, -k_scale);
 
-    // each group's first batch is loaded while the wave's previous group is
-    // computed
+    // the first two batches of each group (most groups hold 50 to 80
+    // particles) are loaded while the wave's previous group is computed
     int64_t nlo = 0, nhi = 0;
-    TscRaw nxt{};
-    if (wave < ngb) {
+    TscRaw nxt[2] = {};
+    auto prefetch = [&](int j) {
         int lg[3];
-        local(wave, lg);
+        local(j, lg);
         slice(lg, nlo, nhi);
         if (nhi > nlo)
-            nxt = tsc_load(m, nlo, nhi, lane);
-    }
+            nxt[0] = tsc_load(m, nlo, nhi, lane);
+        if (nhi > nlo + 64)
+            nxt[1] = tsc_load(m, nlo + 64, nhi, lane);
+    };
+    if (wave < ngb)
+        prefetch(wave);
     for (int j = wave; j < ngb; j += TSC_BRICK_WAVES) {
         int lg[3];
         local(j, lg);
         const int64_t lo = nlo, hi = nhi;
-        const TscRaw cur = nxt;
-        if (j + TSC_BRICK_WAVES < ngb) {
-            int ln3[3];
-            local(j + TSC_BRICK_WAVES, ln3);
-            slice(ln3, nlo, nhi);
-            if (nhi > nlo)
-                nxt = tsc_load(m, nlo, nhi, lane);
-        }
+        const TscRaw cur[2] = {nxt[0], nxt[1]};
+        if (j + TSC_BRICK_WAVES < ngb)
+            prefetch(j + TSC_BRICK_WAVES);
         if (hi <= lo)
             continue;
         int gb[3];
@@ -419,7 +420,7 @@ __global__ __launch_bounds__(TSC_BRICK_WAVES * WAVE) void k_mass_tsc_brick(TscAr
         for (int k = 0; k < 3; ++k)
             gb[k] = org[k] + lg[k];
         float tv[TSC_PAIRS];
-        tsc_group_block<true>(m, ws, lane, gb, lo, hi, tv, &cur);
+        tsc_group_block<true>(m, ws, lane, gb, lo, hi, tv, cur);
 #pragma unroll
         for (int k = 0; k < TSC_PAIRS; ++k) {
             const int pr = lane + WAVE * k;

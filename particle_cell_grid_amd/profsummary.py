@@ -85,7 +85,7 @@ def tap_name(kernel):
              "k_permute": "sort_permute", "k_tile_keys": "sort_keys",
              "k_sweep1d": "sweep1d", "k_sweep1d_grad": "sweep1d_grad",
              "k_zigzag_tiled": "zigzag_tiled", "k_zigzag_flat": "zigzag_flat",
-             "k_zigzag_regroup": "zigzag_regroup"}
+             "k_zigzag_regroup": "zigzag_regroup", "k_mass_tsc_brick": "mass_tsc_mfma"}
     return table.get(base)
 
 

@@ -361,13 +361,16 @@ __device__ inline void wave_sync()
 
 // Stages one particle (raw values, valid = the slot is inside the cell's slice)
 // into the lane's row.  A particle that lies in another cell (a stale layout)
-// is staged as zero and reported through *stray: the follow-up pass deposits it.
+// is staged with c = 0 and reported through *stray: the follow-up pass
+// deposits it.
 template <bool SC, typename R>
 __device__ inline void stage_raw(const MassArgs &m, Stage<R> &s, int lane, const RawParticle &r,
                                  bool valid, const int *cell, bool *stray)
 {
     // computed for every lane (an empty slot holds zeros), then selected:
-    // no divergent branches
+    // no divergent branches.  Only c is zeroed for a slot that is not the
+    // cell's: every product of the moments takes c once, and the weights and
+    // u of a loaded particle are finite
     const Particle<R> P = make_particle<R>(m, r);
     const bool home = P.base[0] == cell[0] && P.base[1] == cell[1] && P.base[2] == cell[2];
     const bool take = valid && home;
@@ -375,10 +378,10 @@ __device__ inline void stage_raw(const MassArgs &m, Stage<R> &s, int lane, const
     R W[8], u[4];
 #pragma unroll
     for (int a = 0; a < 8; ++a)
-        W[a] = take ? P.W[a] : (R)0;
+        W[a] = P.W[a];
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-        u[k] = take ? P.u[k] : (R)0;
+        u[k] = P.u[k];
     const R c = take ? P.c : (R)0;
     if constexpr (sizeof(R) == 4) {
         float4 *w4 = reinterpret_cast<float4 *>(s.W[lane]);

@@ -205,12 +205,14 @@ __device__ inline void tsc_group_block(const TscArgs &m, TscScratch &ws, int lan
 #pragma unroll
         for (int a = 0; a < 32; a += 4) {
             float4 v4;
-            v4.x = take && a + 0 < TSC_NODES ? P.W[a + 0] : 0.0f;
-            v4.y = take && a + 1 < TSC_NODES ? P.W[a + 1] : 0.0f;
-            v4.z = take && a + 2 < TSC_NODES ? P.W[a + 2] : 0.0f;
-            v4.w = take && a + 3 < TSC_NODES ? P.W[a + 3] : 0.0f;
+            v4.x = a + 0 < TSC_NODES ? P.W[a + 0] : 0.0f;
+            v4.y = a + 1 < TSC_NODES ? P.W[a + 1] : 0.0f;
+            v4.z = a + 2 < TSC_NODES ? P.W[a + 2] : 0.0f;
+            v4.w = a + 3 < TSC_NODES ? P.W[a + 3] : 0.0f;
             *reinterpret_cast<float4 *>(&ws.s.W[lane][a]) = v4;
         }
+        // only c is zeroed for a slot outside the group: every product takes
+        // c once, and the weights of a loaded particle are finite
         ws.s.c[lane] = take ? P.c : 0.0f;
         wave_sync();
         const int nb = (int)std::min<int64_t>(64, hi - base);
@@ -594,15 +596,14 @@ __global__ __launch_bounds__(TSC_WAVES * WAVE) void k_mass_tsc_tensor_group(TscA
 #pragma unroll
         for (int a = 0; a < 32; a += 4) {
             float4 v4;
-            v4.x = take && a + 0 < TSC_NODES ? P.W[a + 0] : 0.0f;
-            v4.y = take && a + 1 < TSC_NODES ? P.W[a + 1] : 0.0f;
-            v4.z = take && a + 2 < TSC_NODES ? P.W[a + 2] : 0.0f;
-            v4.w = take && a + 3 < TSC_NODES ? P.W[a + 3] : 0.0f;
+            v4.x = a + 0 < TSC_NODES ? P.W[a + 0] : 0.0f;
+            v4.y = a + 1 < TSC_NODES ? P.W[a + 1] : 0.0f;
+            v4.z = a + 2 < TSC_NODES ? P.W[a + 2] : 0.0f;
+            v4.w = a + 3 < TSC_NODES ? P.W[a + 3] : 0.0f;
             *reinterpret_cast<float4 *>(&ws.s.W[lane][a]) = v4;
         }
-        *reinterpret_cast<float4 *>(ws.s.u[lane]) =
-            take ? make_float4(u[0], u[1], u[2], u[3]) : make_float4(0, 0, 0, 0);
-        ws.s.c[lane] = take ? c : 0.0f;
+        *reinterpret_cast<float4 *>(ws.s.u[lane]) = make_float4(u[0], u[1], u[2], u[3]);
+        ws.s.c[lane] = take ? c : 0.0f;  // the factor of every product (see above)
         wave_sync();
         const int nb = (int)std::min<int64_t>(64, hi - base);
         if (MFMA) {

@@ -292,6 +292,11 @@ pcg_status deposit_currents_zigzag_regroup(const pcg_grid *grid, const pcg_parti
 #define PCG_MASS_MFMA 1   /* per-cell contraction on fp32 MFMA (16x16x4)           */
 #define PCG_MASS_VALU 2   /* the same per-cell contraction with vector FMAs         */
 #define PCG_MASS_FLAT 3   /* one thread per particle, 576 global atomics each      */
+/* OR'ed into a variant of any assemble_mass_matrix* call: M is set to the
+ * matrix instead of added to.  With a layout (MFMA, VALU) the CIC column
+ * kernels then store each row of M without reading it; the other paths clear
+ * M first.  The tail and stray particles still add after the rows are set. */
+#define PCG_MASS_OVERWRITE 16
 
 /* Bytes of device workspace assemble_mass_matrix needs with a cell layout
  * (MFMA and VALU variants). */
@@ -313,7 +318,8 @@ size_t pcg_mass_workspace_bytes(const pcg_grid *grid);
  *   cell it is not in is deposited by the flat path after that; the tail
  *   [n_partitioned, count) likewise.  Calls that write the same M on
  *   different streams race.
- * variant: PCG_MASS_*; VALU and MFMA need `cells`.
+ * variant: PCG_MASS_*, optionally OR'ed with PCG_MASS_OVERWRITE; VALU and
+ *   MFMA need `cells`.
  * workspace: device memory of at least pcg_mass_workspace_bytes() bytes,
  *   256-byte aligned, needed when `cells` is given (may be NULL otherwise);
  *   contents undefined on entry and exit. */
@@ -349,9 +355,12 @@ pcg_status assemble_mass_matrix_scalar(const pcg_grid *grid, const pcg_particles
  * groups: a T = 1, order = 2 layout from pcg_tile_sort (group = the particles
  *   sharing one TSC support base, [MM] §3.3), or NULL (flat path).  With it,
  *   each group's 27 x 27 block is one product over its particles on the matrix
- *   cores (PCG_MASS_MFMA) or vector FMAs (PCG_MASS_VALU), added to M with
- *   device atomics ([MM] §3.4).  A particle in a slice whose group it is not in,
- *   and the tail [n_partitioned, count), take the flat path (729 atomics each).
+ *   cores (PCG_MASS_MFMA) or vector FMAs (PCG_MASS_VALU).  MFMA sums the blocks
+ *   of 4 x 4 x 2 groups in LDS (32-bit fixed point, its unit set by the
+ *   brick's sum of |q w|: q w must be finite) and adds each node row to M once
+ *   with device atomics; VALU adds every block with device atomics ([MM]
+ *   §3.4).  A particle in a slice whose group it is not in, and the tail
+ *   [n_partitioned, count), take the flat path (729 atomics each).
  * No workspace.  Calls that write the same M on different streams race.
  * Errors: PCG_EINVAL for n_k < 5, a NULL array, a count outside [0, 2^30), a
  *   layout that is not T = 1, order = 2, or MFMA/VALU without a layout;

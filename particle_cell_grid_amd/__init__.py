@@ -27,6 +27,7 @@ if not os.path.exists(LIB_PATH):
 _lib = C.CDLL(LIB_PATH)
 
 PCG_MASS_AUTO, PCG_MASS_MFMA, PCG_MASS_VALU, PCG_MASS_FLAT = 0, 1, 2, 3
+PCG_MASS_OVERWRITE = 16  # OR'ed into a variant: M = the matrix, not M += the matrix
 
 
 class Grid(C.Structure):
@@ -378,10 +379,10 @@ def assemble_mass_matrix(n: Sequence[int], x: List[torch.Tensor], B: List[torch.
                          beta: torch.Tensor, q: torch.Tensor, w: torch.Tensor, M: torch.Tensor,
                          cells: Optional[Layout] = None, variant: int = PCG_MASS_AUTO,
                          workspace: Optional[torch.Tensor] = None):
-    """M[nz, ny, nx, 27, 3, 3] += the ECSIM CIC mass matrix, in M's dtype (fp32, or
-    fp64: the fp64 entry point).  With a cell layout a workspace of
-    pcg_mass_workspace_bytes() is needed; one is taken from torch's allocator
-    when none is given."""
+    """M[nz, ny, nx, 27, 3, 3] += the ECSIM CIC mass matrix (M = it with
+    PCG_MASS_OVERWRITE OR'ed into variant), in M's dtype (fp32, or fp64: the fp64
+    entry point).  With a cell layout a workspace of pcg_mass_workspace_bytes()
+    is needed; one is taken from torch's allocator when none is given."""
     g = make_grid(3, n)
     P = _particles(q.numel(), x, None, q, w)
     bp = (C.c_void_p * 3)(*[b.data_ptr() for b in B])

@@ -99,6 +99,7 @@ struct MassArgs {
     const uint32_t *cell_offsets;
     int64_t n_part;
     uint32_t ncells;
+    int overwrite;  // the column kernel stores its rows of M without reading them
 };
 
 template <typename R>
@@ -865,7 +866,7 @@ __global__ __launch_bounds__(COL_WAVES * WAVE) void k_mass_column(MassArgs m, Co
 #pragma unroll
                 for (int q = 0; q < COL_ROW_PER_THREAD; ++q) {
                     const int r = threadIdx.x + q * COL_WAVES * WAVE;
-                    v[ly][q] = ly < BY && r < BX * ROW ? dst[r] : (R)0;
+                    v[ly][q] = ly < BY && r < BX * ROW && !m.overwrite ? dst[r] : (R)0;
                 }
             }
             // one wait for all of them, so that the stores below need none
@@ -920,6 +921,16 @@ __global__ __launch_bounds__(256) void k_mass_strays(MassArgs m, const uint32_t 
 }
 
 __global__ void k_mass_clear_flag(uint32_t *flag) { *flag = 0u; }
+
+// M = 0 ahead of a path that only adds (the overwrite flag without the column
+// kernel).
+template <typename R>
+__global__ __launch_bounds__(256) void k_mass_zero(R *__restrict__ M, int64_t len)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < len; i += stride)
+        M[i] = (R)0;
+}
 
 }  // namespace
 }  // namespace pcg
@@ -976,6 +987,8 @@ pcg_status assemble(const char *who, const pcg_grid *grid, const pcg_particles *
                         who, k, grid->n[k]);
     if (!particles || !M)
         return fail(PCG_EINVAL, "%s: particles or M is NULL", who);
+    const bool overwrite = (variant & PCG_MASS_OVERWRITE) != 0;
+    variant &= ~PCG_MASS_OVERWRITE;
     if (variant < PCG_MASS_AUTO || variant > PCG_MASS_FLAT)
         return fail(PCG_EINVAL, "%s: unknown variant %d", who, variant);
     const int64_t count = particles->count;
@@ -1002,8 +1015,18 @@ pcg_status assemble(const char *who, const pcg_grid *grid, const pcg_particles *
     m.M = M;
     m.ncells = (uint32_t)((int64_t)grid->n[0] * grid->n[1] * grid->n[2]);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    // M = 0 (overwrite) where the column kernel will not set every row; run
+    // only once the arguments have passed every check
+    auto zero = [&]() -> pcg_status {
+        if (!overwrite)
+            return PCG_OK;
+        const int64_t len = (int64_t)m.ncells * row_floats<SC>();
+        const int64_t blocks = std::min<int64_t>((len + 255) / 256, (int64_t)device_cus() * 16);
+        return launch("mass_zero", k_mass_zero<R>, dim3((unsigned)blocks), dim3(256), 0, st,
+                      M, len);
+    };
     if (count == 0)
-        return PCG_OK;
+        return zero();
     auto flat = [&](int64_t begin, int64_t end) -> pcg_status {
         if (end <= begin)
             return PCG_OK;
@@ -1012,8 +1035,10 @@ pcg_status assemble(const char *who, const pcg_grid *grid, const pcg_particles *
         return launch(kernel_name<SC, R>(2), k_mass_flat<SC, R>, dim3((unsigned)blocks),
                       dim3(256), 0, st, m, begin, end);
     };
-    if (variant == PCG_MASS_FLAT || (!cells && variant == PCG_MASS_AUTO))
+    if (variant == PCG_MASS_FLAT || (!cells && variant == PCG_MASS_AUTO)) {
+        PCG_TRY(zero());
         return flat(0, count);
+    }
     if (!cells)
         return fail(PCG_EINVAL, "%s: the %s variant needs a cell layout", who,
                     variant == PCG_MASS_VALU ? "VALU" : "MFMA");
@@ -1037,6 +1062,9 @@ pcg_status assemble(const char *who, const pcg_grid *grid, const pcg_particles *
     cg.ncol[2] = (grid->n[2] + col_z<SC>() - 1) / col_z<SC>();
     cg.nwork = (uint32_t)cg.ncol[0] * cg.ncol[1] * cg.ncol[2];
     cg.stray_flag = static_cast<uint32_t *>(workspace);
+    if (m.n_part == 0)
+        PCG_TRY(zero());
+    m.overwrite = overwrite ? 1 : 0;  // the column kernel sets every row
     if (m.n_part > 0) {
         PCG_TRY(launch("mass_clear_flag", k_mass_clear_flag, dim3(1), dim3(1), 0, st,
                        cg.stray_flag));

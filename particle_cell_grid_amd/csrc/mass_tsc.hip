@@ -710,6 +710,14 @@ __global__ __launch_bounds__(TSC_WAVES * WAVE) void k_mass_tsc_tensor_group(TscA
     }
 }
 
+// M = 0 ahead of the additions (PCG_MASS_OVERWRITE).
+__global__ __launch_bounds__(256) void k_mass_tsc_zero(float *__restrict__ M, int64_t len)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < len; i += stride)
+        M[i] = 0.0f;
+}
+
 }  // namespace
 }  // namespace pcg
 
@@ -734,6 +742,8 @@ pcg_status assemble_tsc(const char *who, const pcg_grid *grid, const pcg_particl
                         who, k, grid->n[k]);
     if (!particles || !M)
         return fail(PCG_EINVAL, "%s: particles or M is NULL", who);
+    const bool overwrite = (variant & PCG_MASS_OVERWRITE) != 0;
+    variant &= ~PCG_MASS_OVERWRITE;
     if (variant < PCG_MASS_AUTO || variant > PCG_MASS_FLAT)
         return fail(PCG_EINVAL, "%s: unknown variant %d", who, variant);
     const int64_t count = particles->count;
@@ -771,6 +781,14 @@ pcg_status assemble_tsc(const char *who, const pcg_grid *grid, const pcg_particl
     m.M = M;
     m.ngroups = (uint32_t)((int64_t)grid->n[0] * grid->n[1] * grid->n[2]);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (overwrite) {
+        // every path here adds to M: clear it first (the arguments have
+        // passed every check)
+        const int64_t len = (int64_t)m.ngroups * TSC_OFFS * (TENSOR ? 9 : 1);
+        const int64_t blocks = std::min<int64_t>((len + 255) / 256, (int64_t)device_cus() * 16);
+        PCG_TRY(launch("mass_tsc_zero", k_mass_tsc_zero, dim3((unsigned)blocks), dim3(256), 0, st,
+                       M, len));
+    }
     if (count == 0)
         return PCG_OK;
     auto flat = [&](int64_t begin, int64_t end) -> pcg_status {

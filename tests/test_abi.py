@@ -394,3 +394,36 @@ def test_deposit_noalloc_validation(lib):
     assert call(g, order=3, tile=Tile(8, 1, 1, 0, 1000, FAKE)) == EUNSUPPORTED
     assert call(g, tile=Tile(8, 1, 1, 0, 1001, FAKE)) == EINVAL     # n_partitioned > count
     assert call(grid(0, [1, 1, 1])) == EINVAL
+
+
+def test_mass_constants_match_the_header(lib):
+    """The binding's PCG_MASS_* values are the header's (the overwrite flag too)."""
+    import sys
+
+    sys.path.insert(0, ROOT)
+    import particle_cell_grid_amd as pcg
+
+    defs = {m.group(1): int(m.group(2))
+            for m in re.finditer(r"#define (PCG_MASS_\w+) (\d+)", open(HEADER).read())}
+    assert "PCG_MASS_OVERWRITE" in defs and len(defs) == 5
+    for name, value in defs.items():
+        assert getattr(pcg, name) == value
+
+
+def test_mass_overwrite_flag_validation(lib):
+    """With the overwrite flag the checks are those without it, all before
+    anything is enqueued (M is never touched on an error)."""
+    sm = lib.assemble_mass_matrix_scalar
+    sm.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
+                   C.c_size_t, C.c_void_p]
+    g8 = C.byref(grid(3, [8, 8, 8]))
+    P = particles(100)
+    c1 = Tile(1, 1, 0, 0, 100, FAKE)
+    OVER = 16
+    assert sm(g8, C.byref(P), None, 7 | OVER, FAKE, FAKE, 256, None) == EINVAL
+    assert sm(g8, C.byref(P), None, 2 | OVER, FAKE, FAKE, 256, None) == EINVAL   # VALU needs cells
+    assert sm(g8, C.byref(P), C.byref(c1), 1 | OVER, FAKE, None, 0, None) == EWORKSPACE
+    tm = lib.assemble_mass_matrix_scalar_tsc
+    tm.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p]
+    assert tm(g8, C.byref(P), None, 1 | OVER, FAKE, None) == EINVAL           # MFMA needs groups
+    assert tm(g8, C.byref(P), None, 7 | OVER, FAKE, None) == EINVAL

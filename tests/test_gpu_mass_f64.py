@@ -21,10 +21,12 @@ TOL = 1e-12
 VARIANTS = [pcg.PCG_MASS_MFMA, pcg.PCG_MASS_VALU, pcg.PCG_MASS_FLAT]
 
 
-def _run(wl, perm, off, variant, scalar, n_part=None):
+def _run(wl, perm, off, variant, scalar, n_part=None, M0=None):
     s = wl.take(perm.astype(np.int64)) if perm is not None else wl
     shape = (wl.n[2], wl.n[1], wl.n[0], 27) + (() if scalar else (3, 3))
     M = torch.zeros(shape, dtype=torch.float64, device=DEV)
+    if M0 is not None:
+        M.copy_(torch.from_numpy(M0.reshape(shape)))
     cells = pcg.Layout(T=1, order=1, tile_offsets=dev(off.view(np.int32)),
                        n_partitioned=wl.count if n_part is None else n_part, drift=0)
     say("mass f64", "scalar" if scalar else "tensor", wl.n, wl.count, variant, n_part)
@@ -119,3 +121,17 @@ def test_f64_scalar_mass_full_size_64(orc):
     want = node_row_sums(wl.n, s.x, 1, [qw])
     scale = node_row_sums(wl.n, s.x, 1, [np.abs(qw)])
     say("row sums: worst error / bound", check_row_sums(block_row_sums(M), want, scale, TOL))
+
+
+@pytest.mark.parametrize("scalar", [False, True])
+def test_f64_mass_overwrite(orc, scalar):
+    """PCG_MASS_OVERWRITE in fp64: the column kernel stores every row of M
+    without reading it."""
+    wl = synthetic.mass_workload([8, 6, 7], 16, seed=78)
+    _, perm, off = orc.tile_sort(3, wl.n, 1, 1, wl.x)
+    s = wl.take(perm.astype(np.int64))
+    size = 7 * 6 * 8 * 27 * (1 if scalar else 9)
+    M0 = np.random.default_rng(79).standard_normal(size)
+    M = _run(s, None, off, pcg.PCG_MASS_MFMA | pcg.PCG_MASS_OVERWRITE, scalar, M0=M0)
+    ref = _ref(orc, wl.n, s, scalar)
+    assert rel_frob_err(M, ref) <= TOL

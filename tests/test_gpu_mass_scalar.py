@@ -120,3 +120,20 @@ def test_scalar_mass_full_size_64(orc):
         mo = offs.index((-dx, -dy, -dz))
         rolled = np.roll(M[..., mo], shift=(-dz, -dy, -dx), axis=(0, 1, 2))
         assert np.abs(M[..., o] - rolled).max() <= 1e-5 * scale
+
+
+@pytest.mark.parametrize("variant", [pcg.PCG_MASS_MFMA, pcg.PCG_MASS_FLAT])
+def test_scalar_mass_overwrite(orc, variant):
+    """PCG_MASS_OVERWRITE on the scalar matrix: M's previous values are gone,
+    a tail still adds after the rows are set."""
+    wl = synthetic.mass_workload([9, 8, 10], 12, seed=68)
+    _, perm, off = orc.tile_sort(3, wl.n, 1, 1, wl.x)
+    s = wl.take(perm.astype(np.int64))
+    M = torch.from_numpy(np.random.default_rng(69).standard_normal(
+        (10, 8, 9, 27)).astype(np.float32)).to(DEV)
+    cells = pcg.Layout(T=1, order=1, tile_offsets=dev(off.view(np.int32)),
+                       n_partitioned=s.count - 200, drift=0)
+    pcg.assemble_mass_matrix_scalar(wl.n, [dev(a) for a in s.x], dev(s.q), dev(s.w), M, cells,
+                                    variant | pcg.PCG_MASS_OVERWRITE)
+    torch.cuda.synchronize()
+    _check(M.cpu().numpy(), orc.mass_matrix_scalar(wl.n, s.x, s.q, s.w))

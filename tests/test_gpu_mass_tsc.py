@@ -98,6 +98,21 @@ def test_tsc_mass_adds_to_M(orc):
     _check(M.cpu().numpy().astype(np.float64) - init, ref)
 
 
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_tsc_mass_overwrite(orc, variant):
+    """PCG_MASS_OVERWRITE: M is cleared before the additions, on every path."""
+    wl = synthetic.mass_workload([6, 7, 5], 16, seed=88)
+    s, off = _grouped(orc, wl)
+    M = torch.from_numpy(np.random.default_rng(89).standard_normal(
+        (5, 7, 6, 125)).astype(np.float32)).to(DEV)
+    groups = pcg.Layout(T=1, order=2, tile_offsets=dev(off.view(np.int32)), n_partitioned=s.count,
+                        drift=0)
+    pcg.assemble_mass_matrix_scalar_tsc(wl.n, [dev(a) for a in s.x], dev(s.q), dev(s.w), M, groups,
+                                        variant | pcg.PCG_MASS_OVERWRITE)
+    torch.cuda.synchronize()
+    _check(M.cpu().numpy(), orc.mass_matrix_scalar_tsc(wl.n, s.x, s.q, s.w))
+
+
 def test_tsc_mass_no_layout_is_flat(orc):
     wl = synthetic.mass_workload([5, 6, 7], 9, seed=82)
     _check(_run(wl.n, wl, None, pcg.PCG_MASS_AUTO, use_layout=False),

@@ -7,6 +7,12 @@ under _build/) and the objects are linked into the shared library.
 
 Flags: -O3, C++17, gfx950 only, and packed-FP32 instruction selection turned
 off (``-target-feature -packed-fp32-ops``) so hipcc never emits v_pk_*_f32.
+
+``build_asan()`` (``build.py --asan``) makes a debug copy,
+``_build/asan/libpcg_asan.so``, whose HOST code is built with AddressSanitizer
+and UndefinedBehaviorSanitizer; the device code is compiled as usual (no GPU
+sanitizer).  It is for CPU runs of the argument checks: load it into a process
+started with ``asan_runtime()`` in ``LD_PRELOAD``.
 """
 import glob
 import os
@@ -31,14 +37,23 @@ def sources():
     return sorted(glob.glob(os.path.join(HERE, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every .hip source to an object (in parallel), then link libpcg.so."""
+# host-only sanitizer flags (each -fsanitize= behind -Xarch_host, so the
+# device compile never sees them)
+ASAN_HOST = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+    "-Xarch_host", "-g",
+]
+ASAN_DIR = os.path.join(HERE, "_build", "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libpcg_asan.so")
+
+
+def _build(out: str, obj_dir: str, extra: list, verbose: bool) -> str:
     from concurrent.futures import ThreadPoolExecutor
 
-    obj_dir = os.path.join(HERE, "_build")
     os.makedirs(obj_dir, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", HERE]
-    compile_flags = [f for f in FLAGS if f != "-shared"]
+    compile_flags = [f for f in FLAGS if f != "-shared"] + extra
 
     def compile_one(src):
         obj = os.path.join(obj_dir, os.path.basename(src)[:-4] + ".o")
@@ -51,14 +66,61 @@ def build(verbose: bool = False) -> str:
     srcs = sources()
     with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(compile_one, srcs))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *objs, "-o", tmp]
+    tmp = out + ".tmp"
+    link_extra = ["-shared-libasan"] if extra else []
+    cmd = [HIPCC, *FLAGS, *extra, *link_extra, *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every .hip source to an object (in parallel), then link libpcg.so."""
+    return _build(LIB, os.path.join(HERE, "_build"), [], verbose)
+
+
+def source_digest() -> str:
+    """sha256 over the sources and the public header (names and bytes)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for p in sources() + sorted(glob.glob(os.path.join(HERE, "*.hpp"))) + [
+            os.path.join(ROOT, "include", "pcg.h"), os.path.abspath(__file__)]:
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def build_asan(verbose: bool = False) -> str:
+    """Build (or reuse, when the sources are unchanged) the sanitizer copy."""
+    stamp = os.path.join(ASAN_DIR, "digest")
+    digest = source_digest()
+    if os.path.exists(ASAN_LIB) and os.path.exists(stamp) and open(stamp).read() == digest:
+        return ASAN_LIB
+    _build(ASAN_LIB, ASAN_DIR, ASAN_HOST, verbose)
+    with open(stamp, "w") as f:
+        f.write(digest)
+    return ASAN_LIB
+
+
+def host_clang() -> str:
+    """The clang that hipcc drives for host code."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "lib", "llvm", "bin",
+                         "clang")
+    return clang if os.path.exists(clang) else "/opt/rocm/llvm/bin/clang"
+
+
+def asan_runtime() -> str:
+    """The ASan runtime of hipcc's host compiler, for LD_PRELOAD."""
+    return subprocess.check_output(
+        [host_clang(), "-print-file-name=libclang_rt.asan-x86_64.so"], text=True).strip()
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--asan" in sys.argv:
+        print(build_asan(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -8,7 +8,8 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-LIB = os.path.join(ROOT, "particle_cell_grid_amd", "libpcg.so")
+# PCG_LIB names another build of the library to check (the sanitizer build)
+LIB = os.environ.get("PCG_LIB") or os.path.join(ROOT, "particle_cell_grid_amd", "libpcg.so")
 HEADER = os.path.join(ROOT, "include", "pcg.h")
 
 EINVAL, EUNSUPPORTED, ELDS, EWORKSPACE = -1, -2, -3, -4

@@ -795,8 +795,17 @@ def bench_mass_tsc(args, torch, pcg, tensor=False):
         extra[f"mass_{nm}_ms"] = round(time_plain(
             torch, lambda: assemble(var | pcg.PCG_MASS_OVERWRITE), 5), 4)
     extra["mfma_speedup_vs_valu"] = round(extra["mass_valu_ms"] / extra["mass_mfma_ms"], 2)
-    if tensor:  # the scalar matrix sums bricks of groups in LDS first
-        extra["flush_atomics_per_launch"] = 729 * 9 * nc
+    # device atomics of the brick flush, at most: every node pair that a
+    # brick's groups reach (5 b + 4 per axis for b groups), x 9 components for
+    # the tensor; entries that stay zero are skipped
+    edge = (2, 2, 2) if tensor else (4, 4, 2)
+    per_brick = 9 if tensor else 1
+    bricks = 1
+    for k in range(3):
+        bricks *= -(-n[k] // edge[k])
+        per_brick *= 5 * edge[k] + 4
+    extra["flush_atomics_per_launch_max"] = bricks * per_brick
+    extra["flush_atomics_per_group_max"] = round(bricks * per_brick / nc, 1)
     cpu = None
     if not args.no_cpu_baseline:
         import oracle

@@ -22,15 +22,15 @@
 // thread per particle, 729 atomics; also the unsorted tail).  A particle found in a slice whose group it does not belong to (a
 // stale layout) is deposited by its own lane with the flat path.
 //
-// The tensor (ECSIM) matrix with TSC weights ([MM] Eq.(4)-(5); §4.1 Fig. 9)
-// uses the moments of the CIC kernels: with u = (1, omega) and
-// c = q w / (1 + |omega|^2), T_kl[a][b] = sum_p c u_k u_l W_a W_b (k <= l) and
-//   M^ij = delta_ij T_00 + eps_ijk T_0(k+1) + T_(i+1)(j+1).
-// Each T_kl is a symmetric 27 x 27 matrix: tiles (0,0), (0,1), (1,1), i.e.
-// 30 products of 16x16x4 per 4 particles, accumulators in place (120 AGPRs).
-// The block (729 node pairs x 9 components) is added to M with 6561 atomics,
-// staged in LDS so that consecutive lanes add consecutive floats of M (a lane
-// per pair would put 36 bytes between neighbouring lanes' addresses).
+// The tensor (ECSIM) matrix with TSC weights ([MM] Eq.(4)-(5); §4.1 Fig. 9):
+// M^ij = sum_p c_p alpha'^ij_p W_a W_b with c = q w / (1 + |omega|^2) and
+// alpha' = I + omega omega^T + the rotation terms.  Each of the nine
+// components is a symmetric 27 x 27 block per group, so the MFMA variant runs
+// three 16x16x4 tiles per component (27 matrix instructions per 4 particles)
+// and sums the upper triangles of a brick of 2 x 2 x 2 groups in an LDS patch
+// that keeps one entry per unordered node pair (see the brick kernel).  The
+// VALU variant forms the ten moments u_k u_l (u = (1, omega)) per lane and
+// node pair and adds each group's 6561 values to M itself.
 #include <algorithm>
 
 #include "common.hpp"
@@ -69,6 +69,21 @@ struct TscParticle {
     float c;
 };
 
+// Axis k of a particle's support: the wrapped base node and the three weights.
+__device__ inline int tsc_axis(const TscArgs &m, float xk, int k, float *wk)
+{
+    const float x = clamp_coord(xk, m.nf[k]);
+    const float fl = floorf(x);
+    const bool low = x - fl < 0.5f;
+    const float b = low ? fl - 1.0f : fl;
+    const float t = x - (b + 1.0f);
+    const int bi = (int)b;  // in [-1, n]
+    wk[0] = 0.5f * (0.5f - t) * (0.5f - t);
+    wk[1] = 0.75f - t * t;
+    wk[2] = 0.5f * (0.5f + t) * (0.5f + t);
+    return bi < 0 ? bi + m.n[k] : (bi >= m.n[k] ? bi - m.n[k] : bi);
+}
+
 __device__ inline TscParticle tsc_particle(const TscArgs &m, float x0, float x1, float x2,
                                            float q, float w)
 {
@@ -76,18 +91,8 @@ __device__ inline TscParticle tsc_particle(const TscArgs &m, float x0, float x1,
     const float xs[3] = {x0, x1, x2};
     float wk[3][3];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-        const float x = clamp_coord(xs[k], m.nf[k]);
-        const float fl = floorf(x);
-        const bool low = x - fl < 0.5f;
-        const float b = low ? fl - 1.0f : fl;
-        const float t = x - (b + 1.0f);
-        const int bi = (int)b;  // in [-1, n]
-        P.base[k] = bi < 0 ? bi + m.n[k] : (bi >= m.n[k] ? bi - m.n[k] : bi);
-        wk[k][0] = 0.5f * (0.5f - t) * (0.5f - t);
-        wk[k][1] = 0.75f - t * t;
-        wk[k][2] = 0.5f * (0.5f + t) * (0.5f + t);
-    }
+    for (int k = 0; k < 3; ++k)
+        P.base[k] = tsc_axis(m, xs[k], k, wk[k]);
 #pragma unroll
     for (int a = 0; a < TSC_NODES; ++a)
         P.W[a] = wk[0][a % 3] * wk[1][(a / 3) % 3] * wk[2][a / 9];
@@ -527,6 +532,11 @@ __global__ __launch_bounds__(256) void k_mass_tsc_tensor_flat(TscArgs m, int64_t
     }
 }
 
+// The VALU variant: one wave per group, each lane summing the nine components
+// of its node pairs (lane + 64 k) over the staged particles; the block goes to
+// M with 6561 device atomics, staged in LDS so that consecutive lanes add
+// consecutive floats of M (a lane per pair would put 36 bytes between
+// neighbouring lanes' addresses).
 struct TscTensorStage {
     float W[64][32];
     float u[64][4];
@@ -536,7 +546,6 @@ struct TscTensorStage {
 constexpr int TSC_HALF = (TSC_PAIRS + 1) / 2;
 union TscTensorScratch {
     TscTensorStage s;
-    float Tm[32][33];
     float F[WAVE * TSC_HALF * 9];  // one half's blocks, pair-major
 };
 
@@ -544,8 +553,7 @@ union TscTensorScratch {
 __device__ constexpr int MOM_K[10] = {0, 0, 0, 0, 1, 1, 1, 2, 2, 3};
 __device__ constexpr int MOM_L[10] = {0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
 
-template <bool MFMA>
-__global__ __launch_bounds__(TSC_WAVES * WAVE) void k_mass_tsc_tensor_group(TscArgs m)
+__global__ __launch_bounds__(TSC_WAVES * WAVE) void k_mass_tsc_tensor_valu(TscArgs m)
 {
     __shared__ TscTensorScratch scratch[TSC_WAVES];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), lane = lane_id();
@@ -561,22 +569,12 @@ __global__ __launch_bounds__(TSC_WAVES * WAVE) void k_mass_tsc_tensor_group(TscA
     if (hi <= lo)
         return;
     int gb[3];
-    gb[0] = (int)(g % (uint32_t)m.n[0]);
-    gb[1] = (int)((g / (uint32_t)m.n[0]) % (uint32_t)m.n[1]);
-    gb[2] = (int)(g / ((uint32_t)m.n[0] * (uint32_t)m.n[1]));
+    group_coords(m, g, gb);
 
-    const int r = lane & 15, kk = lane >> 4;
-    // MFMA: acc[3 mom + t], tiles t = (0,0), (0,1), (1,1) of moment mom
-    floatx4 acc[30];
+    // lane owns node pairs lane + 64 k (k < 12) and their 9 components
+    float tv[TSC_PAIRS][9];
 #pragma unroll
-    for (int i = 0; i < 30; ++i)
-        acc[i] = floatx4{0, 0, 0, 0};
-    // VALU: lane owns node pairs lane + 64 k (k < 12) and their 9 components
-    constexpr int PAIRS = TSC_PAIRS;
-    constexpr int VPAIRS = MFMA ? 1 : PAIRS;
-    float tv[VPAIRS][9];
-#pragma unroll
-    for (int k = 0; k < VPAIRS; ++k)
+    for (int k = 0; k < TSC_PAIRS; ++k)
 #pragma unroll
         for (int ij = 0; ij < 9; ++ij)
             tv[k][ij] = 0.0f;
@@ -603,98 +601,37 @@ __global__ __launch_bounds__(TSC_WAVES * WAVE) void k_mass_tsc_tensor_group(TscA
             *reinterpret_cast<float4 *>(&ws.s.W[lane][a]) = v4;
         }
         *reinterpret_cast<float4 *>(ws.s.u[lane]) = make_float4(u[0], u[1], u[2], u[3]);
-        ws.s.c[lane] = take ? c : 0.0f;  // the factor of every product (see above)
+        ws.s.c[lane] = take ? c : 0.0f;  // the factor of every product
         wave_sync();
         const int nb = (int)std::min<int64_t>(64, hi - base);
-        if (MFMA) {
-            const int steps = (nb + 3) >> 2;
-            for (int i = 0; i < steps; ++i) {
-                const int qq = 4 * i + kk;
-                const float w0 = ws.s.W[qq][r], w1 = ws.s.W[qq][16 + r];
-                const float4 uq = *reinterpret_cast<const float4 *>(ws.s.u[qq]);
-                const float cq = ws.s.c[qq];
-                const float uk[4] = {uq.x, uq.y, uq.z, uq.w};
-                float a0[4], a1[4], b0[4], b1[4];
+        for (int qq = 0; qq < nb; ++qq) {
+            const float cq = ws.s.c[qq];
+            const float4 uq = *reinterpret_cast<const float4 *>(ws.s.u[qq]);
+            const float uk[4] = {uq.x, uq.y, uq.z, uq.w};
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    a0[k] = uk[k] * w0;
-                    a1[k] = uk[k] * w1;
-                    b0[k] = cq * a0[k];
-                    b1[k] = cq * a1[k];
-                }
+            for (int k2 = 0; k2 < TSC_PAIRS; ++k2) {
+                const int pr = lane + WAVE * k2;
+                if (pr < TSC_NODES * TSC_NODES) {
+                    const float wab = cq * ws.s.W[qq][pr / TSC_NODES] * ws.s.W[qq][pr % TSC_NODES];
 #pragma unroll
-                for (int mo = 0; mo < 10; ++mo) {
-                    const int k = MOM_K[mo], l = MOM_L[mo];
-                    acc[3 * mo + 0] =
-                        __builtin_amdgcn_mfma_f32_16x16x4f32(a0[k], b0[l], acc[3 * mo + 0], 0, 0, 0);
-                    acc[3 * mo + 1] =
-                        __builtin_amdgcn_mfma_f32_16x16x4f32(a0[k], b1[l], acc[3 * mo + 1], 0, 0, 0);
-                    acc[3 * mo + 2] =
-                        __builtin_amdgcn_mfma_f32_16x16x4f32(a1[k], b1[l], acc[3 * mo + 2], 0, 0, 0);
-                }
-            }
-        } else {
-            for (int qq = 0; qq < nb; ++qq) {
-                const float cq = ws.s.c[qq];
-                const float4 uq = *reinterpret_cast<const float4 *>(ws.s.u[qq]);
-                const float uk[4] = {uq.x, uq.y, uq.z, uq.w};
-#pragma unroll
-                for (int k2 = 0; k2 < VPAIRS; ++k2) {
-                    const int pr = lane + WAVE * k2;
-                    if (pr < TSC_NODES * TSC_NODES) {
-                        const float wab =
-                            cq * ws.s.W[qq][pr / TSC_NODES] * ws.s.W[qq][pr % TSC_NODES];
-#pragma unroll
-                        for (int mo = 0; mo < 10; ++mo)
-                            add_moment(MOM_K[mo], MOM_L[mo], wab * uk[MOM_K[mo]] * uk[MOM_L[mo]],
-                                       tv[k2]);
-                    }
+                    for (int mo = 0; mo < 10; ++mo)
+                        add_moment(MOM_K[mo], MOM_L[mo], wab * uk[MOM_K[mo]] * uk[MOM_L[mo]],
+                                   tv[k2]);
                 }
             }
         }
     }
     wave_sync();
-    // per half of the lane's pairs (lane + 64 (h TSC_HALF + k2)): the blocks,
-    // from the moments through LDS (MFMA) or from the lane's sums (VALU), then
-    // the half's 64 TSC_HALF x 9 floats flushed with consecutive lanes on
-    // consecutive values v: pair 64 h TSC_HALF + v / 9, component v % 9
+    // per half of the lane's pairs (lane + 64 (h TSC_HALF + k2)): the half's
+    // 64 TSC_HALF x 9 floats flushed with consecutive lanes on consecutive
+    // values v: pair 64 h TSC_HALF + v / 9, component v % 9
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        float blk[TSC_HALF][9];
 #pragma unroll
         for (int k2 = 0; k2 < TSC_HALF; ++k2)
 #pragma unroll
             for (int ij = 0; ij < 9; ++ij)
-                blk[k2][ij] = MFMA ? 0.0f : tv[(h * TSC_HALF + k2) % VPAIRS][ij];
-        if (MFMA) {
-            // register i of this lane holds D[4 (lane / 16) + i][lane % 16];
-            // tile (1,0) is tile (0,1) transposed
-#pragma unroll
-            for (int mo = 0; mo < 10; ++mo) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 4 * kk + i, col = r;
-                    ws.Tm[row][col] = acc[3 * mo + 0][i];
-                    ws.Tm[row][16 + col] = acc[3 * mo + 1][i];
-                    ws.Tm[16 + col][row] = acc[3 * mo + 1][i];
-                    ws.Tm[16 + row][16 + col] = acc[3 * mo + 2][i];
-                }
-                wave_sync();
-#pragma unroll
-                for (int k2 = 0; k2 < TSC_HALF; ++k2) {
-                    const int pr = lane + WAVE * (h * TSC_HALF + k2);
-                    if (h * TSC_HALF + k2 < PAIRS && pr < TSC_NODES * TSC_NODES)
-                        add_moment(MOM_K[mo], MOM_L[mo], ws.Tm[pr / TSC_NODES][pr % TSC_NODES],
-                                   blk[k2]);
-                }
-                wave_sync();
-            }
-        }
-#pragma unroll
-        for (int k2 = 0; k2 < TSC_HALF; ++k2)
-#pragma unroll
-            for (int ij = 0; ij < 9; ++ij)
-                ws.F[(k2 * WAVE + lane) * 9 + ij] = blk[k2][ij];
+                ws.F[(k2 * WAVE + lane) * 9 + ij] = tv[h * TSC_HALF + k2][ij];
         wave_sync();
         for (int v = lane; v < WAVE * TSC_HALF * 9; v += WAVE) {
             const int pl = v / 9, ij = v - 9 * pl;
@@ -707,6 +644,326 @@ __global__ __launch_bounds__(TSC_WAVES * WAVE) void k_mass_tsc_tensor_group(TscA
             }
         }
         wave_sync();
+    }
+}
+
+// ------------------------------------------------- tensor matrix in bricks
+//
+// Each component of the tensor matrix is itself a scalar-type matrix,
+// M^ij_{g g'} = sum_p c_p alpha'^ij_p W_g(p) W_g'(p) with c = q w / (1 + |omega|^2)
+// and alpha' = I + omega omega^T plus the rotation (+omega_z at (x,y), -omega_y
+// at (x,z), ... as in add_moment): nine symmetric 27 x 27 blocks per group,
+// three 16x16x4 tiles each (A = W_a, B = c alpha'^ij W_b), 27 matrix
+// instructions per 4 particles and no moments to combine afterwards.  A
+// work-group takes a brick of 2 x 2 x 2 groups and sums their blocks in an LDS
+// patch of 32-bit fixed-point values, scaled as in k_mass_tsc_brick (|alpha^ij|
+// <= 1: alpha is the inverse of I - [omega]x, whose singular values are >= 1).
+// The brick's groups reach nodes 0..3 (local) per axis and a node pair
+// (la, lb) of an axis occurs iff |la - lb| <= 2: 14 pairs per axis, 2744 node
+// pairs.  As every component block is symmetric in its two nodes, the patch
+// keeps one of (A, B) and (B, A), the one whose offset B - A is >= 0 in
+// (z, y, x) order ("canonical"): 1404 pairs x 9 components, 50.5 KB, so two
+// work-groups share a CU.  A group adds only its blocks' upper triangles (node
+// b >= a in support order, which is exactly the canonical half), and the
+// flush writes every pair of the brick, reading the canonical entry:
+// 3087 device atomics per group instead of 6561, in runs of consecutive M
+// floats.
+constexpr int TT_B = 2;                  // groups per brick edge
+constexpr int TT_N = TT_B + 2;           // patch nodes per axis
+constexpr int TT_ALL = 5 * TT_B + 4;     // per axis: node pairs with |la - lb| <= 2
+constexpr int TT_POS = 2 * TT_B + 1;     //   ... with lb > la
+constexpr int TT_NN = 3 * TT_B + 3;      //   ... with lb >= la
+constexpr int TT_FULL = TT_ALL * TT_ALL * TT_ALL;
+constexpr int TT_ZBLK = TT_POS * TT_ALL + TT_N * TT_NN;
+constexpr int TT_HALF = TT_POS * TT_ALL * TT_ALL + TT_N * TT_ZBLK;
+constexpr int TT_UPPER = TSC_NODES * (TSC_NODES + 1) / 2;  // pairs a <= b of a support
+constexpr int TT_UP_LANE = (TT_UPPER + WAVE - 1) / WAVE;    // per lane
+constexpr int TT_WAVES = 4;
+constexpr size_t TT_PATCH_BYTES = (size_t)TT_HALF * 9 * sizeof(int);
+static_assert(TT_B == 2, "the per-axis closed forms below are for bricks of edge 2");
+
+// Per-axis pair indices (la, lb in 0..3): every pair, ordered by la then lb;
+// the pairs with lb > la; the pairs with lb >= la.
+__host__ __device__ constexpr int tt_all(int la, int lb)
+{
+    return 4 * la - (la > 0) - (la == 3) + lb;
+}
+__host__ __device__ constexpr int tt_pos(int la, int lb) { return la + lb - 1; }
+__host__ __device__ constexpr int tt_nn(int la, int lb) { return la == 3 ? 8 : 2 * la + lb; }
+
+// Patch index of the canonical pair (A, B): offset in z > 0; else in y > 0;
+// else in x >= 0.
+__host__ __device__ constexpr int tt_half(int ax, int ay, int az, int bx, int by, int bz)
+{
+    return bz > az ? (tt_pos(az, bz) * TT_ALL + tt_all(ay, by)) * TT_ALL + tt_all(ax, bx)
+                   : TT_POS * TT_ALL * TT_ALL + az * TT_ZBLK +
+                         (by > ay ? tt_pos(ay, by) * TT_ALL + tt_all(ax, bx)
+                                  : TT_POS * TT_ALL + ay * TT_NN + tt_nn(ax, bx));
+}
+
+// Every canonical pair of the 4^3 patch nodes (offsets -2..2) has its own
+// index below TT_HALF, and none is left over.
+constexpr bool tt_half_is_a_bijection()
+{
+    bool seen[TT_HALF] = {};
+    int count = 0;
+    for (int A = 0; A < TT_N * TT_N * TT_N; ++A)
+        for (int o = 0; o < TSC_OFFS; ++o) {
+            const int ax = A % TT_N, ay = (A / TT_N) % TT_N, az = A / (TT_N * TT_N);
+            const int dx = o % 5 - 2, dy = (o / 5) % 5 - 2, dz = o / 25 - 2;
+            const int bx = ax + dx, by = ay + dy, bz = az + dz;
+            if (bx < 0 || bx >= TT_N || by < 0 || by >= TT_N || bz < 0 || bz >= TT_N)
+                continue;
+            if (!(dz > 0 || (dz == 0 && (dy > 0 || (dy == 0 && dx >= 0)))))
+                continue;
+            const int h = tt_half(ax, ay, az, bx, by, bz);
+            if (h < 0 || h >= TT_HALF || seen[h])
+                return false;
+            seen[h] = true;
+            ++count;
+        }
+    return count == TT_HALF;
+}
+static_assert(tt_half_is_a_bijection(), "patch index of the canonical pairs");
+
+struct TtTables {
+    // node pair f of the brick (x pair fastest, pairs by tt_all per axis):
+    // canonical patch index | local node A (ax + 4 ay + 16 az) << 11 | offset o << 17
+    uint32_t dec[TT_FULL];
+    // support pair u (a <= b, row-major): a | b << 5
+    uint16_t up[TT_UPPER];
+    // group cell c = cx + 2 cy + 4 cz of the brick, support pair u: patch index
+    uint16_t h[8][TT_UPPER];
+};
+
+constexpr TtTables tt_tables()
+{
+    TtTables t{};
+    int la[TT_ALL] = {}, lb[TT_ALL] = {};
+    for (int a = 0; a < TT_N; ++a)
+        for (int b = 0; b < TT_N; ++b)
+            if (a - b <= 2 && b - a <= 2) {
+                la[tt_all(a, b)] = a;
+                lb[tt_all(a, b)] = b;
+            }
+    for (int f = 0; f < TT_FULL; ++f) {
+        const int p[3] = {f % TT_ALL, (f / TT_ALL) % TT_ALL, f / (TT_ALL * TT_ALL)};
+        const int A[3] = {la[p[0]], la[p[1]], la[p[2]]}, B[3] = {lb[p[0]], lb[p[1]], lb[p[2]]};
+        const int d[3] = {B[0] - A[0], B[1] - A[1], B[2] - A[2]};
+        const bool canon = d[2] > 0 || (d[2] == 0 && (d[1] > 0 || (d[1] == 0 && d[0] >= 0)));
+        const int h = canon ? tt_half(A[0], A[1], A[2], B[0], B[1], B[2])
+                            : tt_half(B[0], B[1], B[2], A[0], A[1], A[2]);
+        const int o = (d[0] + 2) + 5 * (d[1] + 2) + 25 * (d[2] + 2);
+        t.dec[f] = (uint32_t)h | (uint32_t)(A[0] + TT_N * A[1] + TT_N * TT_N * A[2]) << 11 |
+                   (uint32_t)o << 17;
+    }
+    int u = 0;
+    for (int a = 0; a < TSC_NODES; ++a)
+        for (int b = a; b < TSC_NODES; ++b, ++u) {
+            t.up[u] = (uint16_t)(a | b << 5);
+            for (int c = 0; c < 8; ++c) {
+                const int cx = c & 1, cy = (c >> 1) & 1, cz = c >> 2;
+                t.h[c][u] = (uint16_t)tt_half(cx + a % 3, cy + (a / 3) % 3, cz + a / 9,
+                                              cx + b % 3, cy + (b / 3) % 3, cz + b / 9);
+            }
+        }
+    return t;
+}
+__device__ constexpr TtTables TT = tt_tables();
+
+// Per-wave LDS: one staged batch of 64 particles, each the nine axis weights
+// (x0..2 y0..2 z0..2 at 0..8) and c alpha'^ij (at 12..20); reused for one
+// component's 32 x 32 block once the batches are done.
+union __attribute__((aligned(16))) TtScratch {
+    float v[64][24];
+    float Tm[32][33];
+};
+
+__global__ __launch_bounds__(TT_WAVES * WAVE, 2) void k_mass_tsc_tensor_brick(TscArgs m)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    int *patch = reinterpret_cast<int *>(smem);  // [TT_HALF][9]
+    __shared__ TtScratch scratch[TT_WAVES];
+    __shared__ float red[TT_WAVES];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), lane = lane_id();
+    TtScratch &ws = scratch[wave];
+    const int nbx = (m.n[0] + TT_B - 1) / TT_B, nby = (m.n[1] + TT_B - 1) / TT_B;
+    const int bi = (int)(blockIdx.x % (uint32_t)nbx);
+    const int bj = (int)((blockIdx.x / (uint32_t)nbx) % (uint32_t)nby);
+    const int bk = (int)(blockIdx.x / ((uint32_t)nbx * (uint32_t)nby));
+    const int org[3] = {bi * TT_B, bj * TT_B, bk * TT_B};
+    const int cnt[3] = {min(TT_B, m.n[0] - org[0]), min(TT_B, m.n[1] - org[1]),
+                        min(TT_B, m.n[2] - org[2])};
+    const int ngb = cnt[0] * cnt[1] * cnt[2];
+    {
+        int4 *p4 = reinterpret_cast<int4 *>(patch);
+        for (int i = threadIdx.x; i < TT_HALF * 9 / 4; i += blockDim.x)
+            p4[i] = int4{0, 0, 0, 0};
+    }
+    static_assert(TT_HALF * 9 % 4 == 0, "patch cleared as int4");
+    auto local = [&](int j, int *lg) {
+        lg[0] = j % cnt[0];
+        lg[1] = (j / cnt[0]) % cnt[1];
+        lg[2] = j / (cnt[0] * cnt[1]);
+    };
+    auto slice = [&](const int *lg, int64_t &lo, int64_t &hi) {
+        const uint32_t g = (uint32_t)(org[0] + lg[0]) +
+                           (uint32_t)m.n[0] * ((uint32_t)(org[1] + lg[1]) +
+                                               (uint32_t)m.n[1] * (uint32_t)(org[2] + lg[2]));
+        lo = std::min<int64_t>(m.offsets[g], m.n_part);
+        hi = std::max<int64_t>(lo, std::min<int64_t>(m.offsets[g + 1], m.n_part));
+    };
+    float sum = 0.0f;
+    for (int j = wave; j < ngb; j += TT_WAVES) {
+        int lg[3];
+        local(j, lg);
+        int64_t lo, hi;
+        slice(lg, lo, hi);
+        for (int64_t p = lo + lane; p < hi; p += WAVE)
+            sum += fabsf(ld(m.q, p) * ld(m.w, p));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        sum += __shfl_xor(sum, off);
+    if (lane == 0)
+        red[wave] = sum;
+    __syncthreads();
+    float total = 0.0f;
+#pragma unroll
+    for (int w = 0; w < TT_WAVES; ++w)
+        total += red[w];
+    if (total == 0.0f)
+        return;  // nothing to add (every wave sees the same total)
+    // a particle adds at most (9/16) |q w| to an entry: 2^k (9/16) total < 2^30
+    int e = 0;
+    frexpf(0.5625f * total, &e);
+    const int k_scale = max(-126, min(126, 30 - e));
+    const float scale = ldexpf(1.0f, k_scale), inv_scale = ldexpf(1.0f, -k_scale);
+
+    const int r = lane & 15, kk = lane >> 4;
+    // the lane's rows of the MFMA operands: node r and node 16 + r (< 27 for r < 11)
+    const int ra[3] = {r % 3, 3 + (r / 3) % 3, 6 + r / 9};
+    const int s16 = r < 11 ? 16 + r : 0;
+    const int sa[3] = {s16 % 3, 3 + (s16 / 3) % 3, 6 + s16 / 9};
+    // the lane's support pairs (upper triangle) and where their values sit in Tm
+    int tma[TT_UP_LANE];
+#pragma unroll
+    for (int k = 0; k < TT_UP_LANE; ++k) {
+        const int u = min(lane + WAVE * k, TT_UPPER - 1);
+        const int ab = TT.up[u];
+        tma[k] = (ab & 31) * 33 + (ab >> 5);
+    }
+
+    for (int j = wave; j < ngb; j += TT_WAVES) {
+        int lg[3];
+        local(j, lg);
+        int64_t lo, hi;
+        slice(lg, lo, hi);
+        if (hi <= lo)
+            continue;
+        const int gb[3] = {org[0] + lg[0], org[1] + lg[1], org[2] + lg[2]};
+        floatx4 acc[27];
+#pragma unroll
+        for (int i = 0; i < 27; ++i)
+            acc[i] = floatx4{0, 0, 0, 0};
+        for (int64_t base = lo; base < hi; base += 64) {
+            const int64_t p = std::min<int64_t>(base + lane, hi - 1);  // clamped
+            const bool valid = base + lane < hi;
+            const float x0 = ld(m.x[0], p), x1 = ld(m.x[1], p), x2 = ld(m.x[2], p);
+            const float q = ld(m.q, p), w = ld(m.w, p);
+            const float bt = ld(m.beta, p);
+            const float o0 = bt * ld(m.B[0], p), o1 = bt * ld(m.B[1], p), o2 = bt * ld(m.B[2], p);
+            float wk[3][3];
+            const int b0 = tsc_axis(m, x0, 0, wk[0]), b1 = tsc_axis(m, x1, 1, wk[1]),
+                      b2 = tsc_axis(m, x2, 2, wk[2]);
+            const bool home = b0 == gb[0] && b1 == gb[1] && b2 == gb[2];
+            const float c = q * w / (1.0f + (o0 * o0 + o1 * o1 + o2 * o2));
+            if (valid && !home) {  // stale layout: this lane deposits it alone
+                const float u[4] = {1.0f, o0, o1, o2};
+                tsc_tensor_global(m, tsc_particle(m, x0, x1, x2, q, w), u, c);
+            }
+            // c alpha'^ij, or 0 for a slot outside the group (the weights of a
+            // loaded particle are finite, so its products vanish)
+            const float cc = valid && home ? c : 0.0f;
+            wave_sync();
+            float4 *row = reinterpret_cast<float4 *>(ws.v[lane]);
+            row[0] = make_float4(wk[0][0], wk[0][1], wk[0][2], wk[1][0]);
+            row[1] = make_float4(wk[1][1], wk[1][2], wk[2][0], wk[2][1]);
+            row[2] = make_float4(wk[2][2], 0.0f, 0.0f, 0.0f);
+            row[3] = make_float4(cc * (1.0f + o0 * o0), cc * (o2 + o0 * o1),
+                                 cc * (o0 * o2 - o1), cc * (o1 * o0 - o2));
+            row[4] = make_float4(cc * (1.0f + o1 * o1), cc * (o0 + o1 * o2),
+                                 cc * (o1 + o2 * o0), cc * (o2 * o1 - o0));
+            row[5] = make_float4(cc * (1.0f + o2 * o2), 0.0f, 0.0f, 0.0f);
+            wave_sync();
+            const int nb = (int)std::min<int64_t>(64, hi - base);
+            const int steps = (nb + 3) >> 2;
+            for (int i = 0; i < steps; ++i) {
+                const float *sv = ws.v[4 * i + kk];
+                const float wr = sv[ra[0]] * sv[ra[1]] * sv[ra[2]];
+                const float wsv = r < 11 ? sv[sa[0]] * sv[sa[1]] * sv[sa[2]] : 0.0f;
+                const float4 c0 = *reinterpret_cast<const float4 *>(sv + 12);
+                const float4 c1 = *reinterpret_cast<const float4 *>(sv + 16);
+                const float ca[9] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w, sv[20]};
+                float bb0[9], bb1[9];
+#pragma unroll
+                for (int ij = 0; ij < 9; ++ij) {
+                    bb0[ij] = ca[ij] * wr;
+                    bb1[ij] = ca[ij] * wsv;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ij = 0; ij < 9; ++ij) {
+                    acc[3 * ij + 0] =
+                        __builtin_amdgcn_mfma_f32_16x16x4f32(wr, bb0[ij], acc[3 * ij + 0], 0, 0, 0);
+                    acc[3 * ij + 1] =
+                        __builtin_amdgcn_mfma_f32_16x16x4f32(wr, bb1[ij], acc[3 * ij + 1], 0, 0, 0);
+                    acc[3 * ij + 2] =
+                        __builtin_amdgcn_mfma_f32_16x16x4f32(wsv, bb1[ij], acc[3 * ij + 2], 0, 0, 0);
+                }
+            }
+        }
+        // the group's upper triangles into the patch, one component at a time
+        const int cell = lg[0] + 2 * lg[1] + 4 * lg[2];
+        int hk[TT_UP_LANE];
+#pragma unroll
+        for (int k = 0; k < TT_UP_LANE; ++k)
+            hk[k] = TT.h[cell][min(lane + WAVE * k, TT_UPPER - 1)] * 9;
+        const float *tm = &ws.Tm[0][0];
+#pragma unroll
+        for (int ij = 0; ij < 9; ++ij) {
+            wave_sync();
+            // register i of this lane holds D[4 (lane / 16) + i][lane % 16]
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rw = 4 * kk + i;
+                ws.Tm[rw][r] = acc[3 * ij + 0][i];
+                ws.Tm[rw][16 + r] = acc[3 * ij + 1][i];
+                ws.Tm[16 + rw][16 + r] = acc[3 * ij + 2][i];
+            }
+            wave_sync();
+#pragma unroll
+            for (int k = 0; k < TT_UP_LANE; ++k)
+                if (lane + WAVE * k < TT_UPPER)
+                    atomicAdd(&patch[hk[k] + ij], __float2int_rn(tm[tma[k]] * scale));
+        }
+        wave_sync();  // Tm is the next group's staging area
+    }
+    __syncthreads();
+    // every node pair of the brick, read from its canonical entry; consecutive
+    // threads on consecutive floats of M (components, then offsets of a row)
+    for (int i = threadIdx.x; i < TT_FULL * 9; i += blockDim.x) {
+        const int f = i / 9, ij = i - 9 * f;
+        const uint32_t d = TT.dec[f];
+        const int v = patch[(int)(d & 2047u) * 9 + ij];
+        if (v == 0)
+            continue;
+        const int A = (int)((d >> 11) & 63u), o = (int)(d >> 17);
+        const int gx = wrap_add(org[0], A % TT_N, m.n[0]);
+        const int gy = wrap_add(org[1], (A / TT_N) % TT_N, m.n[1]);
+        const int gz = wrap_add(org[2], A / (TT_N * TT_N), m.n[2]);
+        const size_t node = (size_t)gx + (size_t)m.n[0] * ((size_t)gy + (size_t)m.n[1] * gz);
+        atomic_add_f32(&m.M[(node * TSC_OFFS + o) * 9 + ij], (float)v * inv_scale);
     }
 }
 
@@ -810,11 +1067,23 @@ pcg_status assemble_tsc(const char *who, const pcg_grid *grid, const pcg_particl
         const uint32_t nblocks = (m.ngroups + TSC_WAVES - 1) / TSC_WAVES;
         const uint32_t blocks = (nblocks + 7) / 8 * 8;
         const bool valu = variant == PCG_MASS_VALU;
-        if (TENSOR)
-            PCG_TRY(launch(valu ? "mass_tsc_tensor_valu" : "mass_tsc_tensor_mfma",
-                           valu ? k_mass_tsc_tensor_group<false> : k_mass_tsc_tensor_group<true>,
-                           dim3(blocks), dim3(TSC_WAVES * WAVE), 0, st, m));
-        else if (valu)
+        if (TENSOR && valu)
+            PCG_TRY(launch("mass_tsc_tensor_valu", k_mass_tsc_tensor_valu, dim3(blocks),
+                           dim3(TSC_WAVES * WAVE), 0, st, m));
+        else if (TENSOR) {
+            static const bool lds_ok =
+                hipFuncSetAttribute((const void *)k_mass_tsc_tensor_brick,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)TT_PATCH_BYTES) == hipSuccess;
+            if (!lds_ok)
+                return fail(PCG_EHIP, "%s: cannot raise dynamic LDS to %zu bytes", who,
+                            TT_PATCH_BYTES);
+            const uint32_t bricks = (uint32_t)(((grid->n[0] + TT_B - 1) / TT_B) *
+                                               ((grid->n[1] + TT_B - 1) / TT_B) *
+                                               ((grid->n[2] + TT_B - 1) / TT_B));
+            PCG_TRY(launch("mass_tsc_tensor_mfma", k_mass_tsc_tensor_brick, dim3(bricks),
+                           dim3(TT_WAVES * WAVE), TT_PATCH_BYTES, st, m));
+        } else if (valu)
             PCG_TRY(launch("mass_tsc_valu", k_mass_tsc_group<false>, dim3(blocks),
                            dim3(TSC_WAVES * WAVE), 0, st, m));
         else {

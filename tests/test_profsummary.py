@@ -24,7 +24,8 @@ from particle_cell_grid_amd import profsummary as ps
     ("k_mass_tsc_group<true>", "mass_tsc_mfma"),
     ("k_mass_tsc_group<false>", "mass_tsc_valu"),
     ("k_mass_tsc_brick", "mass_tsc_mfma"),
-    ("k_mass_tsc_tensor_group<true>", "mass_tsc_tensor_mfma"),
+    ("k_mass_tsc_tensor_brick", "mass_tsc_tensor_mfma"),
+    ("k_mass_tsc_tensor_valu", "mass_tsc_tensor_valu"),
     ("k_mass_tsc_flat", "mass_tsc_flat"),
     ("k_mass_tsc_tensor_flat", "mass_tsc_tensor_flat"),
     ("k_sweep1d", "sweep1d"),

@@ -779,6 +779,26 @@ union __attribute__((aligned(16))) TtScratch {
     float Tm[32][33];
 };
 
+// A particle's nine inputs, as loaded (slot base + lane of a slice, clamped).
+struct TtRaw {
+    float x[3], q, w, B[3], beta;
+};
+
+__device__ inline TtRaw tt_load(const TscArgs &m, int64_t base, int64_t hi, int lane)
+{
+    const int64_t p = std::min<int64_t>(base + lane, hi - 1);  // clamped
+    TtRaw r;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        r.x[k] = ld(m.x[k], p);
+        r.B[k] = ld(m.B[k], p);
+    }
+    r.q = ld(m.q, p);
+    r.w = ld(m.w, p);
+    r.beta = ld(m.beta, p);
+    return r;
+}
+
 __global__ __launch_bounds__(TT_WAVES * WAVE, 2) void k_mass_tsc_tensor_brick(TscArgs m)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -813,13 +833,28 @@ __global__ __launch_bounds__(TT_WAVES * WAVE, 2) void k_mass_tsc_tensor_brick(Ts
         lo = std::min<int64_t>(m.offsets[g], m.n_part);
         hi = std::max<int64_t>(lo, std::min<int64_t>(m.offsets[g + 1], m.n_part));
     };
+    // a wave's groups are j = wave and wave + TT_WAVES; their first batches are
+    // loaded up front and serve the sum of |q w| as well
+    static_assert(TT_B * TT_B * TT_B <= 2 * TT_WAVES, "two groups per wave at most");
+    int64_t glo[2] = {0, 0}, ghi[2] = {0, 0};
+    TtRaw first[2] = {};
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int j = wave + TT_WAVES * t;
+        if (j < ngb) {
+            int lg[3];
+            local(j, lg);
+            slice(lg, glo[t], ghi[t]);
+            if (ghi[t] > glo[t])
+                first[t] = tt_load(m, glo[t], ghi[t], lane);
+        }
+    }
     float sum = 0.0f;
-    for (int j = wave; j < ngb; j += TT_WAVES) {
-        int lg[3];
-        local(j, lg);
-        int64_t lo, hi;
-        slice(lg, lo, hi);
-        for (int64_t p = lo + lane; p < hi; p += WAVE)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        if (glo[t] + lane < ghi[t])
+            sum += fabsf(first[t].q * first[t].w);
+        for (int64_t p = glo[t] + WAVE + lane; p < ghi[t]; p += WAVE)
             sum += fabsf(ld(m.q, p) * ld(m.w, p));
     }
 #pragma unroll
@@ -854,25 +889,24 @@ __global__ __launch_bounds__(TT_WAVES * WAVE, 2) void k_mass_tsc_tensor_brick(Ts
         tma[k] = (ab & 31) * 33 + (ab >> 5);
     }
 
-    for (int j = wave; j < ngb; j += TT_WAVES) {
+    for (int t = 0; t < 2; ++t) {
+        const int j = wave + TT_WAVES * t;
+        const int64_t lo = glo[t], hi = ghi[t];
+        if (j >= ngb || hi <= lo)
+            continue;
         int lg[3];
         local(j, lg);
-        int64_t lo, hi;
-        slice(lg, lo, hi);
-        if (hi <= lo)
-            continue;
+        const TtRaw cur = t == 0 ? first[0] : first[1];
         const int gb[3] = {org[0] + lg[0], org[1] + lg[1], org[2] + lg[2]};
         floatx4 acc[27];
 #pragma unroll
         for (int i = 0; i < 27; ++i)
             acc[i] = floatx4{0, 0, 0, 0};
         for (int64_t base = lo; base < hi; base += 64) {
-            const int64_t p = std::min<int64_t>(base + lane, hi - 1);  // clamped
             const bool valid = base + lane < hi;
-            const float x0 = ld(m.x[0], p), x1 = ld(m.x[1], p), x2 = ld(m.x[2], p);
-            const float q = ld(m.q, p), w = ld(m.w, p);
-            const float bt = ld(m.beta, p);
-            const float o0 = bt * ld(m.B[0], p), o1 = bt * ld(m.B[1], p), o2 = bt * ld(m.B[2], p);
+            const TtRaw in = base == lo ? cur : tt_load(m, base, hi, lane);
+            const float x0 = in.x[0], x1 = in.x[1], x2 = in.x[2], q = in.q, w = in.w;
+            const float o0 = in.beta * in.B[0], o1 = in.beta * in.B[1], o2 = in.beta * in.B[2];
             float wk[3][3];
             const int b0 = tsc_axis(m, x0, 0, wk[0]), b1 = tsc_axis(m, x1, 1, wk[1]),
                       b2 = tsc_axis(m, x2, 2, wk[2]);
@@ -950,20 +984,37 @@ __global__ __launch_bounds__(TT_WAVES * WAVE, 2) void k_mass_tsc_tensor_brick(Ts
         wave_sync();  // Tm is the next group's staging area
     }
     __syncthreads();
-    // every node pair of the brick, read from its canonical entry; consecutive
-    // threads on consecutive floats of M (components, then offsets of a row)
-    for (int i = threadIdx.x; i < TT_FULL * 9; i += blockDim.x) {
-        const int f = i / 9, ij = i - 9 * f;
-        const uint32_t d = TT.dec[f];
-        const int v = patch[(int)(d & 2047u) * 9 + ij];
-        if (v == 0)
-            continue;
-        const int A = (int)((d >> 11) & 63u), o = (int)(d >> 17);
-        const int gx = wrap_add(org[0], A % TT_N, m.n[0]);
-        const int gy = wrap_add(org[1], (A / TT_N) % TT_N, m.n[1]);
-        const int gz = wrap_add(org[2], A / (TT_N * TT_N), m.n[2]);
-        const size_t node = (size_t)gx + (size_t)m.n[0] * ((size_t)gy + (size_t)m.n[1] * gz);
-        atomic_add_f32(&m.M[(node * TSC_OFFS + o) * 9 + ij], (float)v * inv_scale);
+    // every node pair of the brick, read from its canonical entry: thread t <
+    // 252 takes component t % 9 of the pairs f = t / 9 + 28 k, so consecutive
+    // threads add consecutive floats of M (components, then offsets of a row);
+    // seven pairs at a time, their table entries and patch values read first
+    constexpr int FL_PAIRS = 28, FL_UNROLL = 7;
+    static_assert(TT_FULL % (FL_PAIRS * FL_UNROLL) == 0, "flush rounds");
+    static_assert(TT_WAVES * WAVE >= 9 * FL_PAIRS, "flush threads");
+    if (threadIdx.x < 9 * FL_PAIRS) {
+        const int ij = threadIdx.x % 9, f0 = threadIdx.x / 9;
+        for (int f1 = f0; f1 < TT_FULL; f1 += FL_PAIRS * FL_UNROLL) {
+            uint32_t d[FL_UNROLL];
+            int v[FL_UNROLL];
+#pragma unroll
+            for (int u = 0; u < FL_UNROLL; ++u)
+                d[u] = TT.dec[f1 + FL_PAIRS * u];
+#pragma unroll
+            for (int u = 0; u < FL_UNROLL; ++u)
+                v[u] = patch[(int)(d[u] & 2047u) * 9 + ij];
+#pragma unroll
+            for (int u = 0; u < FL_UNROLL; ++u) {
+                if (v[u] == 0)
+                    continue;
+                const int A = (int)((d[u] >> 11) & 63u), o = (int)(d[u] >> 17);
+                const int gx = wrap_add(org[0], A % TT_N, m.n[0]);
+                const int gy = wrap_add(org[1], (A / TT_N) % TT_N, m.n[1]);
+                const int gz = wrap_add(org[2], A / (TT_N * TT_N), m.n[2]);
+                const size_t node =
+                    (size_t)gx + (size_t)m.n[0] * ((size_t)gy + (size_t)m.n[1] * gz);
+                atomic_add_f32(&m.M[(node * TSC_OFFS + o) * 9 + ij], (float)v[u] * inv_scale);
+            }
+        }
     }
 }
 

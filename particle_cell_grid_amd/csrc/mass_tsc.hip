@@ -677,7 +677,6 @@ constexpr int TT_FULL = TT_ALL * TT_ALL * TT_ALL;
 constexpr int TT_ZBLK = TT_POS * TT_ALL + TT_N * TT_NN;
 constexpr int TT_HALF = TT_POS * TT_ALL * TT_ALL + TT_N * TT_ZBLK;
 constexpr int TT_UPPER = TSC_NODES * (TSC_NODES + 1) / 2;  // pairs a <= b of a support
-constexpr int TT_UP_LANE = (TT_UPPER + WAVE - 1) / WAVE;    // per lane
 constexpr int TT_WAVES = 4;
 constexpr size_t TT_PATCH_BYTES = (size_t)TT_HALF * 9 * sizeof(int);
 static_assert(TT_B == 2, "the per-axis closed forms below are for bricks of edge 2");
@@ -730,9 +729,8 @@ struct TtTables {
     // node pair f of the brick (x pair fastest, pairs by tt_all per axis):
     // canonical patch index | local node A (ax + 4 ay + 16 az) << 11 | offset o << 17
     uint32_t dec[TT_FULL];
-    // support pair u (a <= b, row-major): a | b << 5
-    uint16_t up[TT_UPPER];
-    // group cell c = cx + 2 cy + 4 cz of the brick, support pair u: patch index
+    // group cell c = cx + 2 cy + 4 cz of the brick, support pair u (a <= b,
+    // row-major: u = 27 a - a (a - 1) / 2 + b - a): patch index
     uint16_t h[8][TT_UPPER];
 };
 
@@ -760,7 +758,6 @@ constexpr TtTables tt_tables()
     int u = 0;
     for (int a = 0; a < TSC_NODES; ++a)
         for (int b = a; b < TSC_NODES; ++b, ++u) {
-            t.up[u] = (uint16_t)(a | b << 5);
             for (int c = 0; c < 8; ++c) {
                 const int cx = c & 1, cy = (c >> 1) & 1, cz = c >> 2;
                 t.h[c][u] = (uint16_t)tt_half(cx + a % 3, cy + (a / 3) % 3, cz + a / 9,
@@ -772,11 +769,9 @@ constexpr TtTables tt_tables()
 __device__ constexpr TtTables TT = tt_tables();
 
 // Per-wave LDS: one staged batch of 64 particles, each the nine axis weights
-// (x0..2 y0..2 z0..2 at 0..8) and c alpha'^ij (at 12..20); reused for one
-// component's 32 x 32 block once the batches are done.
-union __attribute__((aligned(16))) TtScratch {
+// (x0..2 y0..2 z0..2 at 0..8) and c alpha'^ij (at 12..20).
+struct __attribute__((aligned(16))) TtScratch {
     float v[64][24];
-    float Tm[32][33];
 };
 
 // A particle's nine inputs, as loaded (slot base + lane of a slice, clamped).
@@ -880,14 +875,23 @@ __global__ __launch_bounds__(TT_WAVES * WAVE, 2) void k_mass_tsc_tensor_brick(Ts
     const int ra[3] = {r % 3, 3 + (r / 3) % 3, 6 + r / 9};
     const int s16 = r < 11 ? 16 + r : 0;
     const int sa[3] = {s16 % 3, 3 + (s16 / 3) % 3, 6 + s16 / 9};
-    // the lane's support pairs (upper triangle) and where their values sit in Tm
-    int tma[TT_UP_LANE];
+    // The lane's twelve accumulator values per component: slot 4 t + i holds
+    // entry (a, b) of tile t (0: (0,0), 1: (0,1), 2: (1,1)), a = 16 (t == 2) +
+    // 4 (lane / 16) + i, b = 16 (t >= 1) + lane % 16.  The slots on or above
+    // the diagonal of the 27 x 27 block go to the patch straight from the
+    // registers; their support pair index u (upper triangle, row-major) is
+    // fixed per lane.
+    int up[12];
+    uint32_t live = 0;
 #pragma unroll
-    for (int k = 0; k < TT_UP_LANE; ++k) {
-        const int u = min(lane + WAVE * k, TT_UPPER - 1);
-        const int ab = TT.up[u];
-        tma[k] = (ab & 31) * 33 + (ab >> 5);
-    }
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int a = (t == 2 ? 16 : 0) + 4 * kk + i, b = (t >= 1 ? 16 : 0) + r;
+            const bool ok = a <= b && b < TSC_NODES;
+            live |= ok ? 1u << (4 * t + i) : 0u;
+            up[4 * t + i] = ok ? a * TSC_NODES - a * (a - 1) / 2 + (b - a) : 0;
+        }
 
     for (int t = 0; t < 2; ++t) {
         const int j = wave + TT_WAVES * t;
@@ -957,31 +961,19 @@ __global__ __launch_bounds__(TT_WAVES * WAVE, 2) void k_mass_tsc_tensor_brick(Ts
                 }
             }
         }
-        // the group's upper triangles into the patch, one component at a time
+        // the group's upper triangles into the patch, from the accumulators
         const int cell = lg[0] + 2 * lg[1] + 4 * lg[2];
-        int hk[TT_UP_LANE];
+        int hs[12];
 #pragma unroll
-        for (int k = 0; k < TT_UP_LANE; ++k)
-            hk[k] = TT.h[cell][min(lane + WAVE * k, TT_UPPER - 1)] * 9;
-        const float *tm = &ws.Tm[0][0];
+        for (int sl = 0; sl < 12; ++sl)
+            hs[sl] = TT.h[cell][up[sl]] * 9;
 #pragma unroll
-        for (int ij = 0; ij < 9; ++ij) {
-            wave_sync();
-            // register i of this lane holds D[4 (lane / 16) + i][lane % 16]
+        for (int ij = 0; ij < 9; ++ij)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rw = 4 * kk + i;
-                ws.Tm[rw][r] = acc[3 * ij + 0][i];
-                ws.Tm[rw][16 + r] = acc[3 * ij + 1][i];
-                ws.Tm[16 + rw][16 + r] = acc[3 * ij + 2][i];
-            }
-            wave_sync();
-#pragma unroll
-            for (int k = 0; k < TT_UP_LANE; ++k)
-                if (lane + WAVE * k < TT_UPPER)
-                    atomicAdd(&patch[hk[k] + ij], __float2int_rn(tm[tma[k]] * scale));
-        }
-        wave_sync();  // Tm is the next group's staging area
+            for (int sl = 0; sl < 12; ++sl)
+                if (live & (1u << sl))
+                    atomicAdd(&patch[hs[sl] + ij],
+                              __float2int_rn(acc[3 * ij + sl / 4][sl % 4] * scale));
     }
     __syncthreads();
     // every node pair of the brick, read from its canonical entry: thread t <

@@ -143,14 +143,13 @@ __global__ __launch_bounds__(256) void k_mass_tsc_flat(TscArgs m, int64_t begin,
 }
 
 // Per-wave LDS: one staged 64-particle batch (rows padded to 32 nodes, the pads
-// zero), reused for the 32 x 32 block once the batches are done.
+// zero).
 struct TscStage {
     float W[64][32];
     float c[64];
 };
-union TscScratch {
+struct TscScratch {
     TscStage s;
-    float Tm[32][33];
 };
 
 __device__ inline void wave_sync()
@@ -160,11 +159,13 @@ __device__ inline void wave_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// The 27 x 27 block of one group (support base gb, wrapped; slice [lo, hi))
-// into ws.Tm (rows and columns 0..26), one wave.  MFMA: the three 16x16 tiles
-// on the matrix cores; VALU: each lane sums its node pairs pr = lane + 64 k
-// into tv.  A particle of the slice that does not belong to the group (a stale
-// layout) is deposited by its own lane with global atomics.
+// The 27 x 27 block of one group (support base gb, wrapped; slice [lo, hi)),
+// one wave.  MFMA: the three 16x16 tiles (0,0), (0,1), (1,1) on the matrix
+// cores, left in acc00, acc01, acc11 (register i of a lane holds entry
+// (4 (lane / 16) + i, lane % 16) of its tile); VALU: each lane sums its node
+// pairs pr = lane + 64 k into tv.  A particle of the slice that does not belong
+// to the group (a stale layout) is deposited by its own lane with global
+// atomics.
 constexpr int TSC_PAIRS = (TSC_NODES * TSC_NODES + WAVE - 1) / WAVE;  // pairs per lane
 
 // A particle's five inputs, as loaded (slot lo + lane of a slice, clamped).
@@ -186,11 +187,14 @@ __device__ inline TscRaw tsc_load(const TscArgs &m, int64_t lo, int64_t hi, int 
 
 template <bool MFMA>
 __device__ inline void tsc_group_block(const TscArgs &m, TscScratch &ws, int lane, const int *gb,
-                                       int64_t lo, int64_t hi, float *tv,
+                                       int64_t lo, int64_t hi, float *tv, floatx4 &acc00,
+                                       floatx4 &acc01, floatx4 &acc11,
                                        const TscRaw *ahead = nullptr)
 {
     const int r = lane & 15, kk = lane >> 4;
-    floatx4 acc00 = {0, 0, 0, 0}, acc01 = {0, 0, 0, 0}, acc11 = {0, 0, 0, 0};
+    acc00 = floatx4{0, 0, 0, 0};
+    acc01 = floatx4{0, 0, 0, 0};
+    acc11 = floatx4{0, 0, 0, 0};
 #pragma unroll
     for (int k = 0; k < TSC_PAIRS; ++k)
         tv[k] = 0.0f;
@@ -262,20 +266,7 @@ __device__ inline void tsc_group_block(const TscArgs &m, TscScratch &ws, int lan
             }
         }
     }
-    wave_sync();
-    if (MFMA) {
-        // register i of this lane holds D[4 (lane / 16) + i][lane % 16]; tile
-        // (1,0) is filled as tile (0,1) transposed
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 4 * kk + i, col = r;
-            ws.Tm[row][col] = acc00[i];
-            ws.Tm[row][16 + col] = acc01[i];
-            ws.Tm[16 + col][row] = acc01[i];
-            ws.Tm[16 + row][16 + col] = acc11[i];
-        }
-        wave_sync();
-    }
+    wave_sync();  // the staging area is free for the next group
 }
 
 // Group coordinates of linear group index g (gx + n_x (gy + n_y gz)).
@@ -286,11 +277,10 @@ __device__ inline void group_coords(const TscArgs &m, uint32_t g, int *gb)
     gb[2] = (int)(g / ((uint32_t)m.n[0] * (uint32_t)m.n[1]));
 }
 
-// One wave per group: group = the wave's global index (groups are the support
-// base nodes, linear index gx + n_x (gy + n_y gz)); its 729 node pairs go to M
-// with device atomics.
-template <bool MFMA>
-__global__ __launch_bounds__(TSC_WAVES * WAVE) void k_mass_tsc_group(TscArgs m)
+// VALU variant, one wave per group: group = the wave's global index (groups
+// are the support base nodes, linear index gx + n_x (gy + n_y gz)); its 729
+// node pairs go to M with device atomics.
+__global__ __launch_bounds__(TSC_WAVES * WAVE) void k_mass_tsc_valu(TscArgs m)
 {
     __shared__ TscScratch scratch[TSC_WAVES];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), lane = lane_id();
@@ -310,14 +300,15 @@ __global__ __launch_bounds__(TSC_WAVES * WAVE) void k_mass_tsc_group(TscArgs m)
     int gb[3];
     group_coords(m, g, gb);
     float tv[TSC_PAIRS];
-    tsc_group_block<MFMA>(m, ws, lane, gb, lo, hi, tv);
+    floatx4 unused[3];
+    tsc_group_block<false>(m, ws, lane, gb, lo, hi, tv, unused[0], unused[1], unused[2]);
 #pragma unroll
     for (int k = 0; k < TSC_PAIRS; ++k) {
         const int pr = lane + WAVE * k;
         if (pr < TSC_NODES * TSC_NODES) {
             const int a = pr / TSC_NODES, b = pr % TSC_NODES;
-            const float v = MFMA ? ws.Tm[a][b] : tv[k];
-            atomic_add_f32(&m.M[(size_t)tsc_node(m, gb, a) * TSC_OFFS + tsc_offset(a, b)], v);
+            atomic_add_f32(&m.M[(size_t)tsc_node(m, gb, a) * TSC_OFFS + tsc_offset(a, b)],
+                           tv[k]);
         }
     }
 }
@@ -411,6 +402,28 @@ __global__ __launch_bounds__(TSC_BRICK_WAVES * WAVE) void k_mass_tsc_brick(TscAr
         if (nhi > nlo + 64)
             nxt[1] = tsc_load(m, nlo + 64, nhi, lane);
     };
+    // The lane's accumulator entries: slot 4 t + i is entry (a, b) of tile t
+    // (0: (0,0), 1: (0,1), 2: (1,1)), a = 16 (t == 2) + 4 (lane / 16) + i,
+    // b = 16 (t >= 1) + lane % 16; slot 12 + i is the transposed entry (b, a)
+    // of tile (0,1), which stands for tile (1,0).  Each goes to the patch
+    // straight from the registers, at a fixed offset from the group's row.
+    const int r = lane & 15, kk = lane >> 4;
+    auto patch_node = [](int a) { return a % 3 + TP_X * ((a / 3) % 3 + TP_Y * (a / 9)); };
+    int cst[16];
+    uint32_t live = 0;
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int a = (t == 2 ? 16 : 0) + 4 * kk + i, b = (t >= 1 ? 16 : 0) + r;
+            const bool ok = a < TSC_NODES && b < TSC_NODES;
+            live |= ok ? 1u << (4 * t + i) : 0u;
+            cst[4 * t + i] = ok ? patch_node(a) * TSC_OFFS + tsc_offset(a, b) : 0;
+            if (t == 1) {
+                live |= ok ? 1u << (12 + i) : 0u;
+                cst[12 + i] = ok ? patch_node(b) * TSC_OFFS + tsc_offset(b, a) : 0;
+            }
+        }
     if (wave < ngb)
         prefetch(wave);
     for (int j = wave; j < ngb; j += TSC_BRICK_WAVES) {
@@ -427,18 +440,14 @@ __global__ __launch_bounds__(TSC_BRICK_WAVES * WAVE) void k_mass_tsc_brick(TscAr
         for (int k = 0; k < 3; ++k)
             gb[k] = org[k] + lg[k];
         float tv[TSC_PAIRS];
-        tsc_group_block<true>(m, ws, lane, gb, lo, hi, tv, cur);
+        floatx4 acc[3];
+        tsc_group_block<true>(m, ws, lane, gb, lo, hi, tv, acc[0], acc[1], acc[2], cur);
+        int *row = patch + (lg[0] + TP_X * (lg[1] + TP_Y * lg[2])) * TSC_OFFS;
 #pragma unroll
-        for (int k = 0; k < TSC_PAIRS; ++k) {
-            const int pr = lane + WAVE * k;
-            if (pr < TSC_NODES * TSC_NODES) {
-                const int a = pr / TSC_NODES, b = pr % TSC_NODES;
-                const int ln = (lg[0] + a % 3) + TP_X * ((lg[1] + (a / 3) % 3) + TP_Y * (lg[2] + a / 9));
-                atomicAdd(&patch[ln * TSC_OFFS + tsc_offset(a, b)],
-                          __float2int_rn(ws.Tm[a][b] * scale));
-            }
-        }
-        wave_sync();  // Tm is the next group's staging area
+        for (int sl = 0; sl < 16; ++sl)
+            if (live & (1u << sl))
+                atomicAdd(&row[cst[sl]],
+                          __float2int_rn((sl < 12 ? acc[sl / 4][sl % 4] : acc[1][sl - 12]) * scale));
     }
     __syncthreads();
     // the patch to M: node rows of 125 floats, consecutive threads on
@@ -1127,7 +1136,7 @@ pcg_status assemble_tsc(const char *who, const pcg_grid *grid, const pcg_particl
             PCG_TRY(launch("mass_tsc_tensor_mfma", k_mass_tsc_tensor_brick, dim3(bricks),
                            dim3(TT_WAVES * WAVE), TT_PATCH_BYTES, st, m));
         } else if (valu)
-            PCG_TRY(launch("mass_tsc_valu", k_mass_tsc_group<false>, dim3(blocks),
+            PCG_TRY(launch("mass_tsc_valu", k_mass_tsc_valu, dim3(blocks),
                            dim3(TSC_WAVES * WAVE), 0, st, m));
         else {
             static const bool lds_ok =

@@ -56,6 +56,8 @@ struct TscArgs {
     const uint32_t *offsets;
     int64_t n_part;
     uint32_t ngroups;
+    uint32_t nbricks;  // brick kernels: bricks of the grid
+    uint32_t xcd_run;  // brick kernels: bricks per XCD run (xcd_item); 0: plain order
 };
 
 // One particle's TSC support: wrapped base node per axis and the 27 weights,
@@ -687,7 +689,11 @@ constexpr int TT_ZBLK = TT_POS * TT_ALL + TT_N * TT_NN;
 constexpr int TT_HALF = TT_POS * TT_ALL * TT_ALL + TT_N * TT_ZBLK;
 constexpr int TT_UPPER = TSC_NODES * (TSC_NODES + 1) / 2;  // pairs a <= b of a support
 constexpr int TT_WAVES = 4;
-constexpr size_t TT_PATCH_BYTES = (size_t)TT_HALF * 9 * sizeof(int);
+// a patch entry: the nine components as five 64-bit words, components 2 w and
+// 2 w + 1 packed in word w (the last word holds component 8 alone)
+constexpr int TT_WORDS = 5;
+constexpr size_t TT_PATCH_BYTES = (size_t)TT_HALF * TT_WORDS * sizeof(unsigned long long);
+constexpr uint32_t TT_XCD_RUN = 64;
 static_assert(TT_B == 2, "the per-axis closed forms below are for bricks of edge 2");
 
 // Per-axis pair indices (la, lb in 0..3): every pair, ordered by la then lb;
@@ -777,11 +783,21 @@ constexpr TtTables tt_tables()
 }
 __device__ constexpr TtTables TT = tt_tables();
 
-// Per-wave LDS: one staged batch of 64 particles, each the nine axis weights
-// (x0..2 y0..2 z0..2 at 0..8) and c alpha'^ij (at 12..20).
+// Per-wave LDS: one staged batch of 64 particles, each c alpha'^ij (at 0..8)
+// and the nine axis weights (x0..2 y0..2 z0..2 at 9..17); rows of 20 floats, so
+// that the lanes' 16-byte writes of a row cover all banks.
+constexpr int TT_ROW = 20, TT_AXW = 9;
 struct __attribute__((aligned(16))) TtScratch {
-    float v[64][24];
+    float v[64][TT_ROW];
 };
+
+// One of the two sums of a patch word: the low one (signed 32-bit), or the
+// high one, the word less the low sum shifted down.
+__device__ inline int tt_split(unsigned long long word, int high)
+{
+    const int lo = (int)(uint32_t)word;
+    return high ? (int)((long long)(word - (unsigned long long)(long long)lo) >> 32) : lo;
+}
 
 // A particle's nine inputs, as loaded (slot base + lane of a slice, clamped).
 struct TtRaw {
@@ -806,25 +822,32 @@ __device__ inline TtRaw tt_load(const TscArgs &m, int64_t base, int64_t hi, int 
 __global__ __launch_bounds__(TT_WAVES * WAVE, 2) void k_mass_tsc_tensor_brick(TscArgs m)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    int *patch = reinterpret_cast<int *>(smem);  // [TT_HALF][9]
+    // [TT_HALF][TT_WORDS]: two 32-bit fixed-point sums per word, added as one
+    // 64-bit integer (the low sum signed: the high one gets its borrow back
+    // when the word is split, as every partial sum stays below 2^30)
+    unsigned long long *patch = reinterpret_cast<unsigned long long *>(smem);
     __shared__ TtScratch scratch[TT_WAVES];
     __shared__ float red[TT_WAVES];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), lane = lane_id();
     TtScratch &ws = scratch[wave];
+    // runs of neighbouring bricks (which add to the same rows of M) on one XCD
+    const uint32_t brick = xcd_item(blockIdx.x, m.xcd_run);
+    if (brick >= m.nbricks)
+        return;
     const int nbx = (m.n[0] + TT_B - 1) / TT_B, nby = (m.n[1] + TT_B - 1) / TT_B;
-    const int bi = (int)(blockIdx.x % (uint32_t)nbx);
-    const int bj = (int)((blockIdx.x / (uint32_t)nbx) % (uint32_t)nby);
-    const int bk = (int)(blockIdx.x / ((uint32_t)nbx * (uint32_t)nby));
+    const int bi = (int)(brick % (uint32_t)nbx);
+    const int bj = (int)((brick / (uint32_t)nbx) % (uint32_t)nby);
+    const int bk = (int)(brick / ((uint32_t)nbx * (uint32_t)nby));
     const int org[3] = {bi * TT_B, bj * TT_B, bk * TT_B};
     const int cnt[3] = {min(TT_B, m.n[0] - org[0]), min(TT_B, m.n[1] - org[1]),
                         min(TT_B, m.n[2] - org[2])};
     const int ngb = cnt[0] * cnt[1] * cnt[2];
     {
         int4 *p4 = reinterpret_cast<int4 *>(patch);
-        for (int i = threadIdx.x; i < TT_HALF * 9 / 4; i += blockDim.x)
+        for (int i = threadIdx.x; i < TT_HALF * TT_WORDS / 2; i += blockDim.x)
             p4[i] = int4{0, 0, 0, 0};
     }
-    static_assert(TT_HALF * 9 % 4 == 0, "patch cleared as int4");
+    static_assert(TT_HALF * TT_WORDS % 2 == 0, "patch cleared as int4");
     auto local = [&](int j, int *lg) {
         lg[0] = j % cnt[0];
         lg[1] = (j / cnt[0]) % cnt[1];
@@ -881,9 +904,9 @@ __global__ __launch_bounds__(TT_WAVES * WAVE, 2) void k_mass_tsc_tensor_brick(Ts
 
     const int r = lane & 15, kk = lane >> 4;
     // the lane's rows of the MFMA operands: node r and node 16 + r (< 27 for r < 11)
-    const int ra[3] = {r % 3, 3 + (r / 3) % 3, 6 + r / 9};
+    const int ra[3] = {TT_AXW + r % 3, TT_AXW + 3 + (r / 3) % 3, TT_AXW + 6 + r / 9};
     const int s16 = r < 11 ? 16 + r : 0;
-    const int sa[3] = {s16 % 3, 3 + (s16 / 3) % 3, 6 + s16 / 9};
+    const int sa[3] = {TT_AXW + s16 % 3, TT_AXW + 3 + (s16 / 3) % 3, TT_AXW + 6 + s16 / 9};
     // The lane's twelve accumulator values per component: slot 4 t + i holds
     // entry (a, b) of tile t (0: (0,0), 1: (0,1), 2: (1,1)), a = 16 (t == 2) +
     // 4 (lane / 16) + i, b = 16 (t >= 1) + lane % 16.  The slots on or above
@@ -934,14 +957,13 @@ __global__ __launch_bounds__(TT_WAVES * WAVE, 2) void k_mass_tsc_tensor_brick(Ts
             const float cc = valid && home ? c : 0.0f;
             wave_sync();
             float4 *row = reinterpret_cast<float4 *>(ws.v[lane]);
-            row[0] = make_float4(wk[0][0], wk[0][1], wk[0][2], wk[1][0]);
-            row[1] = make_float4(wk[1][1], wk[1][2], wk[2][0], wk[2][1]);
-            row[2] = make_float4(wk[2][2], 0.0f, 0.0f, 0.0f);
-            row[3] = make_float4(cc * (1.0f + o0 * o0), cc * (o2 + o0 * o1),
+            row[0] = make_float4(cc * (1.0f + o0 * o0), cc * (o2 + o0 * o1),
                                  cc * (o0 * o2 - o1), cc * (o1 * o0 - o2));
-            row[4] = make_float4(cc * (1.0f + o1 * o1), cc * (o0 + o1 * o2),
+            row[1] = make_float4(cc * (1.0f + o1 * o1), cc * (o0 + o1 * o2),
                                  cc * (o1 + o2 * o0), cc * (o2 * o1 - o0));
-            row[5] = make_float4(cc * (1.0f + o2 * o2), 0.0f, 0.0f, 0.0f);
+            row[2] = make_float4(cc * (1.0f + o2 * o2), wk[0][0], wk[0][1], wk[0][2]);
+            row[3] = make_float4(wk[1][0], wk[1][1], wk[1][2], wk[2][0]);
+            row[4] = make_float4(wk[2][1], wk[2][2], 0.0f, 0.0f);
             wave_sync();
             const int nb = (int)std::min<int64_t>(64, hi - base);
             const int steps = (nb + 3) >> 2;
@@ -949,9 +971,9 @@ __global__ __launch_bounds__(TT_WAVES * WAVE, 2) void k_mass_tsc_tensor_brick(Ts
                 const float *sv = ws.v[4 * i + kk];
                 const float wr = sv[ra[0]] * sv[ra[1]] * sv[ra[2]];
                 const float wsv = r < 11 ? sv[sa[0]] * sv[sa[1]] * sv[sa[2]] : 0.0f;
-                const float4 c0 = *reinterpret_cast<const float4 *>(sv + 12);
-                const float4 c1 = *reinterpret_cast<const float4 *>(sv + 16);
-                const float ca[9] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w, sv[20]};
+                const float4 c0 = *reinterpret_cast<const float4 *>(sv);
+                const float4 c1 = *reinterpret_cast<const float4 *>(sv + 4);
+                const float ca[9] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w, sv[8]};
                 float bb0[9], bb1[9];
 #pragma unroll
                 for (int ij = 0; ij < 9; ++ij) {
@@ -975,14 +997,19 @@ __global__ __launch_bounds__(TT_WAVES * WAVE, 2) void k_mass_tsc_tensor_brick(Ts
         int hs[12];
 #pragma unroll
         for (int sl = 0; sl < 12; ++sl)
-            hs[sl] = TT.h[cell][up[sl]] * 9;
+            hs[sl] = TT.h[cell][up[sl]] * TT_WORDS;
+        auto fix = [&](int ij, int sl) {
+            return (long long)__float2int_rn(acc[3 * ij + sl / 4][sl % 4] * scale);
+        };
 #pragma unroll
-        for (int ij = 0; ij < 9; ++ij)
+        for (int w = 0; w < TT_WORDS; ++w)
 #pragma unroll
             for (int sl = 0; sl < 12; ++sl)
-                if (live & (1u << sl))
-                    atomicAdd(&patch[hs[sl] + ij],
-                              __float2int_rn(acc[3 * ij + sl / 4][sl % 4] * scale));
+                if (live & (1u << sl)) {
+                    const long long hi = 2 * w + 1 < 9 ? fix(2 * w + 1, sl) : 0;
+                    atomicAdd(&patch[hs[sl] + w],
+                              (unsigned long long)(hi * 4294967296LL + fix(2 * w, sl)));
+                }
     }
     __syncthreads();
     // every node pair of the brick, read from its canonical entry: thread t <
@@ -1002,7 +1029,7 @@ __global__ __launch_bounds__(TT_WAVES * WAVE, 2) void k_mass_tsc_tensor_brick(Ts
                 d[u] = TT.dec[f1 + FL_PAIRS * u];
 #pragma unroll
             for (int u = 0; u < FL_UNROLL; ++u)
-                v[u] = patch[(int)(d[u] & 2047u) * 9 + ij];
+                v[u] = tt_split(patch[(int)(d[u] & 2047u) * TT_WORDS + ij / 2], ij & 1);
 #pragma unroll
             for (int u = 0; u < FL_UNROLL; ++u) {
                 if (v[u] == 0)
@@ -1130,11 +1157,13 @@ pcg_status assemble_tsc(const char *who, const pcg_grid *grid, const pcg_particl
             if (!lds_ok)
                 return fail(PCG_EHIP, "%s: cannot raise dynamic LDS to %zu bytes", who,
                             TT_PATCH_BYTES);
-            const uint32_t bricks = (uint32_t)(((grid->n[0] + TT_B - 1) / TT_B) *
-                                               ((grid->n[1] + TT_B - 1) / TT_B) *
-                                               ((grid->n[2] + TT_B - 1) / TT_B));
-            PCG_TRY(launch("mass_tsc_tensor_mfma", k_mass_tsc_tensor_brick, dim3(bricks),
-                           dim3(TT_WAVES * WAVE), TT_PATCH_BYTES, st, m));
+            m.nbricks = (uint32_t)(((grid->n[0] + TT_B - 1) / TT_B) *
+                                   ((grid->n[1] + TT_B - 1) / TT_B) *
+                                   ((grid->n[2] + TT_B - 1) / TT_B));
+            m.xcd_run = TT_XCD_RUN;
+            PCG_TRY(launch("mass_tsc_tensor_mfma", k_mass_tsc_tensor_brick,
+                           dim3(xcd_grid(m.nbricks, m.xcd_run)), dim3(TT_WAVES * WAVE),
+                           TT_PATCH_BYTES, st, m));
         } else if (valu)
             PCG_TRY(launch("mass_tsc_valu", k_mass_tsc_valu, dim3(blocks),
                            dim3(TSC_WAVES * WAVE), 0, st, m));

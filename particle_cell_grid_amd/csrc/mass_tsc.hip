@@ -145,9 +145,10 @@ __global__ __launch_bounds__(256) void k_mass_tsc_flat(TscArgs m, int64_t begin,
 }
 
 // Per-wave LDS: one staged 64-particle batch (rows padded to 32 nodes, the pads
-// zero).
+// zero; 36 floats apart, so that the lanes' 16-byte writes of their rows, and
+// the reads of four rows at a time, spread over the banks).
 struct TscStage {
-    float W[64][32];
+    float W[64][36];
     float c[64];
 };
 struct TscScratch {
@@ -362,6 +363,21 @@ __global__ __launch_bounds__(TSC_BRICK_WAVES * WAVE) void k_mass_tsc_brick(TscAr
         lo = std::min<int64_t>(m.offsets[g], m.n_part);
         hi = std::max<int64_t>(lo, std::min<int64_t>(m.offsets[g + 1], m.n_part));
     };
+    // the first two batches of each group (most groups hold 50 to 80
+    // particles) are loaded while the wave's previous group is computed
+    int64_t nlo = 0, nhi = 0;
+    TscRaw nxt[2] = {};
+    auto prefetch = [&](int j) {
+        int lg[3];
+        local(j, lg);
+        slice(lg, nlo, nhi);
+        if (nhi > nlo)
+            nxt[0] = tsc_load(m, nlo, nhi, lane);
+        if (nhi > nlo + 64)
+            nxt[1] = tsc_load(m, nlo + 64, nhi, lane);
+    };
+    if (wave < ngb)
+        prefetch(wave);  // in flight during the sum below
     // sum |q w| over the brick's particles (every wave its groups)
     float sum = 0.0f;
     for (int j = wave; j < ngb; j += TSC_BRICK_WAVES) {
@@ -391,19 +407,6 @@ __global__ __launch_bounds__(TSC_BRICK_WAVES * WAVE) void k_mass_tsc_brick(TscAr
     const int k_scale = max(-126, min(126, 30 - e));
     const float scale = ldexpf(1.0f, k_scale), inv_scale = ldexpf(1.0f, -k_scale);
 
-    // the first two batches of each group (most groups hold 50 to 80
-    // particles) are loaded while the wave's previous group is computed
-    int64_t nlo = 0, nhi = 0;
-    TscRaw nxt[2] = {};
-    auto prefetch = [&](int j) {
-        int lg[3];
-        local(j, lg);
-        slice(lg, nlo, nhi);
-        if (nhi > nlo)
-            nxt[0] = tsc_load(m, nlo, nhi, lane);
-        if (nhi > nlo + 64)
-            nxt[1] = tsc_load(m, nlo + 64, nhi, lane);
-    };
     // The lane's accumulator entries: slot 4 t + i is entry (a, b) of tile t
     // (0: (0,0), 1: (0,1), 2: (1,1)), a = 16 (t == 2) + 4 (lane / 16) + i,
     // b = 16 (t >= 1) + lane % 16; slot 12 + i is the transposed entry (b, a)
@@ -426,8 +429,6 @@ __global__ __launch_bounds__(TSC_BRICK_WAVES * WAVE) void k_mass_tsc_brick(TscAr
                 cst[12 + i] = ok ? patch_node(b) * TSC_OFFS + tsc_offset(b, a) : 0;
             }
         }
-    if (wave < ngb)
-        prefetch(wave);
     for (int j = wave; j < ngb; j += TSC_BRICK_WAVES) {
         int lg[3];
         local(j, lg);

@@ -332,6 +332,40 @@ constexpr int TP_NODES = TP_X * TP_Y * TP_Z;
 constexpr size_t TSC_PATCH_BYTES = (size_t)TP_NODES * TSC_OFFS * 4;
 constexpr int TSC_BRICK_WAVES = 8;
 
+// The patch entries a brick's groups can reach: node pairs at most 2 apart on
+// every axis (5 b + 4 per axis for b groups), as (row, offset) in row-major
+// order, so consecutive entries are consecutive floats of M.  Entry: patch
+// index | lx << 15 | ly << 18 | lz << 21 | o << 23 (the row's local node, the
+// offset).
+constexpr int TS_FULL = (5 * TB_X + 4) * (5 * TB_Y + 4) * (5 * TB_Z + 4);
+struct TsTable {
+    uint32_t e[TS_FULL];
+    int count;
+};
+constexpr TsTable ts_table()
+{
+    TsTable t{};
+    for (int lz = 0; lz < TP_Z; ++lz)
+        for (int ly = 0; ly < TP_Y; ++ly)
+            for (int lx = 0; lx < TP_X; ++lx)
+                for (int o = 0; o < TSC_OFFS; ++o) {
+                    const int mx = lx + o % 5 - 2, my = ly + (o / 5) % 5 - 2, mz = lz + o / 25 - 2;
+                    if (mx < 0 || mx >= TP_X || my < 0 || my >= TP_Y || mz < 0 || mz >= TP_Z)
+                        continue;
+                    const int ln = lx + TP_X * (ly + TP_Y * lz);
+                    if (t.count < TS_FULL)
+                        t.e[t.count] = (uint32_t)(ln * TSC_OFFS + o) | (uint32_t)lx << 15 |
+                                       (uint32_t)ly << 18 | (uint32_t)lz << 21 |
+                                       (uint32_t)o << 23;
+                    ++t.count;
+                }
+    return t;
+}
+static_assert(ts_table().count == TS_FULL, "reachable patch entries");
+static_assert(TP_NODES * TSC_OFFS <= (1 << 15) && TP_X <= 8 && TP_Y <= 8 && TP_Z <= 4,
+              "fields of a patch entry");
+__device__ constexpr TsTable TS = ts_table();
+
 __global__ __launch_bounds__(TSC_BRICK_WAVES * WAVE) void k_mass_tsc_brick(TscArgs m)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -453,19 +487,32 @@ __global__ __launch_bounds__(TSC_BRICK_WAVES * WAVE) void k_mass_tsc_brick(TscAr
                           __float2int_rn((sl < 12 ? acc[sl / 4][sl % 4] : acc[1][sl - 12]) * scale));
     }
     __syncthreads();
-    // the patch to M: node rows of 125 floats, consecutive threads on
-    // consecutive offsets; entries no group touched stay zero and are skipped
-    for (int i = threadIdx.x; i < TP_NODES * TSC_OFFS; i += blockDim.x) {
-        const int v = patch[i];
-        if (v == 0)
-            continue;
-        const int ln = i / TSC_OFFS, o = i - ln * TSC_OFFS;
-        const int lx = ln % TP_X, ly = (ln / TP_X) % TP_Y, lz = ln / (TP_X * TP_Y);
-        const int gx = wrap_add(org[0], lx, m.n[0]);
-        const int gy = wrap_add(org[1], ly, m.n[1]);
-        const int gz = wrap_add(org[2], lz, m.n[2]);
-        const size_t node = (size_t)gx + (size_t)m.n[0] * ((size_t)gy + (size_t)m.n[1] * gz);
-        atomic_add_f32(&m.M[node * TSC_OFFS + o], (float)v * inv_scale);
+    // the patch to M: the reachable entries, consecutive threads on consecutive
+    // floats of M; four entries at a time, their table words and patch values
+    // read first; entries no group touched stay zero and are skipped
+    constexpr int FL_UNROLL = 4;
+    for (int f0 = threadIdx.x; f0 < TS_FULL; f0 += FL_UNROLL * blockDim.x) {
+        uint32_t e[FL_UNROLL];
+        int v[FL_UNROLL];
+#pragma unroll
+        for (int u = 0; u < FL_UNROLL; ++u) {
+            const int f = f0 + u * (int)blockDim.x;
+            e[u] = f < TS_FULL ? TS.e[f] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < FL_UNROLL; ++u)
+            v[u] = f0 + u * (int)blockDim.x < TS_FULL ? patch[e[u] & 0x7fffu] : 0;
+#pragma unroll
+        for (int u = 0; u < FL_UNROLL; ++u) {
+            if (v[u] == 0)
+                continue;
+            const int gx = wrap_add(org[0], (int)((e[u] >> 15) & 7u), m.n[0]);
+            const int gy = wrap_add(org[1], (int)((e[u] >> 18) & 7u), m.n[1]);
+            const int gz = wrap_add(org[2], (int)((e[u] >> 21) & 3u), m.n[2]);
+            const size_t node =
+                (size_t)gx + (size_t)m.n[0] * ((size_t)gy + (size_t)m.n[1] * gz);
+            atomic_add_f32(&m.M[node * TSC_OFFS + (e[u] >> 23)], (float)v[u] * inv_scale);
+        }
     }
 }
 

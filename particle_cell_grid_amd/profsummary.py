@@ -62,8 +62,8 @@ def tap_name(kernel):
     last = targs[-1].strip() if targs else ""
     if base == "k_deposit_tiled":
         return "deposit_regroup" if last == "true" else "deposit_tiled"
-    if base == "k_mass_tsc_group":
-        return "mass_tsc_mfma" if last == "true" else "mass_tsc_valu"
+    if base == "k_mass_tsc_brick":
+        return "mass_tsc_tensor_mfma" if last == "true" else "mass_tsc_mfma"
     if base == "k_zigzag_tiled":
         # <fixed point, window edge>
         return "zigzag_tiled" if targs and targs[0].strip() == "true" else "zigzag_tiled_f32"
@@ -83,8 +83,7 @@ def tap_name(kernel):
              "k_permute": "sort_permute", "k_tile_keys": "sort_keys",
              "k_sweep1d": "sweep1d", "k_sweep1d_grad": "sweep1d_grad",
              "k_zigzag_tiled": "zigzag_tiled", "k_zigzag_flat": "zigzag_flat",
-             "k_zigzag_regroup": "zigzag_regroup", "k_mass_tsc_brick": "mass_tsc_mfma",
-             "k_mass_tsc_tensor_brick": "mass_tsc_tensor_mfma",
+             "k_zigzag_regroup": "zigzag_regroup", "k_mass_tsc_valu": "mass_tsc_valu",
              "k_mass_tsc_tensor_valu": "mass_tsc_tensor_valu"}
     return table.get(base)
 

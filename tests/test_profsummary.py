@@ -21,10 +21,9 @@ from particle_cell_grid_amd import profsummary as ps
     ("k_mass_column<false, true, double>", "mass_scalar_valu_f64"),
     ("k_mass_flat<false, float>", "mass_flat"),
     ("k_mass_strays<true, double>", "mass_scalar_strays_f64"),
-    ("k_mass_tsc_group<true>", "mass_tsc_mfma"),
-    ("k_mass_tsc_group<false>", "mass_tsc_valu"),
-    ("k_mass_tsc_brick", "mass_tsc_mfma"),
-    ("k_mass_tsc_tensor_brick", "mass_tsc_tensor_mfma"),
+    ("k_mass_tsc_brick<false>", "mass_tsc_mfma"),
+    ("k_mass_tsc_brick<true>", "mass_tsc_tensor_mfma"),
+    ("k_mass_tsc_valu", "mass_tsc_valu"),
     ("k_mass_tsc_tensor_valu", "mass_tsc_tensor_valu"),
     ("k_mass_tsc_flat", "mass_tsc_flat"),
     ("k_mass_tsc_tensor_flat", "mass_tsc_tensor_flat"),

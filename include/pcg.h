@@ -357,9 +357,9 @@ pcg_status assemble_mass_matrix_scalar(const pcg_grid *grid, const pcg_particles
  *   each group's 27 x 27 block is one product over its particles on the matrix
  *   cores (PCG_MASS_MFMA) or vector FMAs (PCG_MASS_VALU).  MFMA sums the blocks
  *   of 4 x 4 x 2 groups in LDS (32-bit fixed point, its unit set by the
- *   brick's sum of |q w|: q w must be finite) and adds each node row to M once
- *   with device atomics; VALU adds every block with device atomics ([MM]
- *   §3.4).  A particle in a slice whose group it is not in, and the tail
+ *   brick's sum of |q w|: q w must be finite) and adds the brick's node pairs
+ *   to M once with device atomics; VALU adds every block with device atomics
+ *   ([MM] §3.4).  A particle in a slice whose group it is not in, and the tail
  *   [n_partitioned, count), take the flat path (729 atomics each).
  * No workspace.  Calls that write the same M on different streams race.
  * Errors: PCG_EINVAL for n_k < 5, a NULL array, a count outside [0, 2^30), a
@@ -377,9 +377,12 @@ pcg_status assemble_mass_matrix_scalar_tsc(const pcg_grid *grid, const pcg_parti
  * M: device fp32 [n_z][n_y][n_x][125][3][3], accumulated; offsets as for
  *   assemble_mass_matrix_scalar_tsc.
  * B[3], beta: as for assemble_mass_matrix.  groups, variant, strays, tail and
- *   errors: as for assemble_mass_matrix_scalar_tsc; per group the ten moment
- *   matrices of the CIC kernels (27 x 27 each) are formed and the 9-component
- *   block is added with 6561 device atomics ([MM] §3.4).  No workspace. */
+ *   errors: as for assemble_mass_matrix_scalar_tsc.  MFMA forms the nine
+ *   component blocks (27 x 27 each) per group and sums those of 2 x 2 x 2
+ *   groups in LDS (32-bit fixed point as above: q w, B and beta must be
+ *   finite) before adding them to M; VALU forms the ten moment matrices of the
+ *   CIC kernels per group and adds the 9-component block with 6561 device
+ *   atomics ([MM] §3.4).  No workspace. */
 pcg_status assemble_mass_matrix_tsc(const pcg_grid *grid, const pcg_particles *particles,
                                     const float *const B[3], const float *beta,
                                     const pcg_tile *groups, int32_t variant, float *M,

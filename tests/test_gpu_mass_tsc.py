@@ -225,3 +225,46 @@ def test_tsc_tensor_mass_full_size_64(orc):
     rs = block_row_sums(M)
     got = np.stack([rs[0] + rs[4] + rs[8], rs[1] - rs[3], rs[2] + rs[6]])
     say("row sums: worst error / bound", check_row_sums(got, want, scale, TOL))
+
+
+@pytest.mark.parametrize("scale", [1e-20, 1e15])
+def test_tsc_tensor_mass_charge_scale(orc, scale):
+    """The tensor bricks sum in fixed point whose unit follows the brick's
+    sum |q w| as well: charges far from 1 keep their relative precision."""
+    wl = synthetic.mass_workload([7, 6, 5], 24, seed=94)
+    s, off = _grouped(orc, wl)
+    s.w = (s.w.astype(np.float64) * scale).astype(np.float32)
+    _check(_run_tensor(wl.n, s, off, pcg.PCG_MASS_MFMA),
+           orc.mass_matrix_tsc(wl.n, s.x, s.B, s.q, s.w, s.beta))
+
+
+@pytest.mark.parametrize("field", [0.05, 20.0])
+def test_tsc_tensor_mass_field_strength(orc, field):
+    """Weak and strong rotation (|omega| from about 0.05 to 20 times the
+    default): the rotation and omega omega^T terms of alpha dominate in turn,
+    and both halves of every packed patch word carry large values."""
+    wl = synthetic.mass_workload([5, 7, 6], 32, seed=95)
+    wl.B = [(b.astype(np.float64) * field).astype(np.float32) for b in wl.B]
+    s, off = _grouped(orc, wl)
+    _check(_run_tensor(wl.n, s, off, pcg.PCG_MASS_MFMA),
+           orc.mass_matrix_tsc(wl.n, wl.x, wl.B, wl.q, wl.w, wl.beta))
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_tsc_tensor_mass_overwrite_and_add(orc, variant):
+    """M += the matrix on a non-zero M, and PCG_MASS_OVERWRITE clears it first,
+    on every path; grid edges of 9, 7, 5 leave partial bricks on every axis."""
+    wl = synthetic.mass_workload([9, 7, 5], 12, seed=96)
+    s, off = _grouped(orc, wl)
+    ref = orc.mass_matrix_tsc(wl.n, s.x, s.B, s.q, s.w, s.beta)
+    init = np.random.default_rng(97).standard_normal((5, 7, 9, 125, 3, 3)).astype(np.float32)
+    groups = pcg.Layout(T=1, order=2, tile_offsets=dev(off.view(np.int32)), n_partitioned=s.count,
+                        drift=0)
+    for flags in (0, pcg.PCG_MASS_OVERWRITE):
+        M = torch.from_numpy(init.copy()).to(DEV)
+        say("mass tsc tensor on a non-zero M", wl.n, s.count, variant, flags)
+        pcg.assemble_mass_matrix_tsc(wl.n, [dev(a) for a in s.x], [dev(b) for b in s.B],
+                                     dev(s.beta), dev(s.q), dev(s.w), M, groups, variant | flags)
+        torch.cuda.synchronize()
+        got = M.cpu().numpy().astype(np.float64)
+        _check(got if flags else got - init, ref)

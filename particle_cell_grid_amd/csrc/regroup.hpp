@@ -61,8 +61,10 @@ struct IncGeom {
     const uint32_t *cum;  // [ntiles + 1] chunk numbering of the source slices
     const ChunkEntry *map;  // [nchunks] source tile and range of each chunk
     uint32_t *cnt;        // [nchunks][NDIR] particles per direction; then prefix over chunks
-    uint32_t *tcnt;       // [ntiles][NDIR] per source tile
-    uint32_t *tpre;       // [ntiles][NDIR] prefix over a new tile's sources
+    // per tile, direction-major, so that threads of consecutive tiles touch
+    // consecutive words:
+    uint32_t *tcnt;       // [NDIR][ntiles] per source tile
+    uint32_t *tpre;       // [NDIR][ntiles] prefix over a new tile's sources
     uint32_t *flag;       // non-zero: the general path takes over
 };
 
@@ -224,7 +226,7 @@ __device__ inline uint32_t move_base(const IncGeom &a, const uint32_t *off, uint
     int sc[3];
     tile_coords(tile, a.g, sc);
     const uint32_t t = dest_tile(sc, dir, a.g);
-    return off[t] + a.tpre[(size_t)tile * NDIR + dir] + a.cnt[(size_t)chunk * NDIR + dir];
+    return off[t] + a.tpre[(size_t)dir * a.ntiles + tile] + a.cnt[(size_t)chunk * NDIR + dir];
 }
 
 // The move stage of the incremental path, replaceable by a caller of

@@ -507,24 +507,36 @@ __global__ __launch_bounds__(256) void k_inc_count(IncGeom a, const float *x0, c
         a.cnt[(size_t)blockIdx.x * NDIR + threadIdx.x] = s_cnt[threadIdx.x];
 }
 
-// Thread per (source tile, direction): exclusive prefix of the counts over the
-// tile's chunks (in place) and the tile's total.
+// Per (source tile, direction): exclusive prefix of the counts over the tile's
+// chunks (in place) and the tile's total.  A work-group takes PREFIX_TILES
+// tiles: the prefixes run tile-major (consecutive threads on one chunk's
+// consecutive counts), the totals go through LDS and out direction-major
+// (consecutive threads on consecutive tiles).  8 tiles (one item per thread)
+// where tiles hold several chunks, 16 where most hold one.
+template <int PREFIX_TILES>
 __global__ __launch_bounds__(256) void k_inc_chunk_prefix(IncGeom a)
 {
     if (*a.flag != 0u)
         return;
-    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= a.ntiles * (uint32_t)NDIR)
-        return;
-    const uint32_t s = i / NDIR, d = i % NDIR;
-    uint32_t run = 0;
-    for (uint32_t c = a.cum[s]; c < a.cum[s + 1]; ++c) {
-        const size_t j = (size_t)c * NDIR + d;
-        const uint32_t v = a.cnt[j];
-        a.cnt[j] = run;
-        run += v;
+    __shared__ uint32_t tot[NDIR][PREFIX_TILES];
+    const uint32_t s0 = blockIdx.x * PREFIX_TILES;
+    const uint32_t nt = min((uint32_t)PREFIX_TILES, a.ntiles - s0);
+    for (uint32_t i = threadIdx.x; i < nt * NDIR; i += blockDim.x) {
+        const uint32_t sl = i / NDIR, d = i % NDIR, s = s0 + sl;
+        uint32_t run = 0;
+        for (uint32_t c = a.cum[s]; c < a.cum[s + 1]; ++c) {
+            const size_t j = (size_t)c * NDIR + d;
+            const uint32_t v = a.cnt[j];
+            a.cnt[j] = run;
+            run += v;
+        }
+        tot[d][sl] = run;
     }
-    a.tcnt[i] = run;
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < nt * NDIR; i += blockDim.x) {
+        const uint32_t d = i / nt, sl = i % nt;
+        a.tcnt[(size_t)d * a.ntiles + s0 + sl] = tot[d][sl];
+    }
 }
 
 // The distinct source coordinates of new-tile coordinate tc on one axis of nt
@@ -604,8 +616,9 @@ __global__ __launch_bounds__(256) void k_inc_tiles(IncGeom a, uint32_t *__restri
                 const int q = ix + 3 * iy + 9 * iz;
                 const bool ok = ix < nx && iy < ny && iz < nz;
                 const int c[3] = {cx[ok ? ix : 0], cy[ok ? iy : 0], cz[ok ? iz : 0]};
-                jj[q] = (size_t)tile_index(c, a.g) * NDIR + dx[ok ? ix : 0] + 3 * dy[ok ? iy : 0] +
-                        9 * dz[ok ? iz : 0];
+                jj[q] = (size_t)(dx[ok ? ix : 0] + 3 * dy[ok ? iy : 0] + 9 * dz[ok ? iz : 0]) *
+                            a.ntiles +
+                        tile_index(c, a.g);
                 v[q] = ok ? a.tcnt[jj[q]] : 0u;
             }
     uint32_t run = 0;
@@ -1025,8 +1038,8 @@ pcg_status incremental_launch(const IncGeom &a, const float *const key_x[3], uin
                     : (a.g.pow2 ? k_inc_count<DIM, ORDER, 1, true> : k_inc_count<DIM, ORDER, 1, false>);
     PCG_TRY(launch("sort_inc_count", kern, dim3(nwork), dim3(big ? 256 : 64), 0, st, a, key_x[0],
                    x1, x2));
-    PCG_TRY(launch("sort_inc_chunk_prefix", k_inc_chunk_prefix,
-                   dim3((a.ntiles * NDIR + 255) / 256), dim3(256), 0, st, a));
+    PCG_TRY(launch("sort_inc_chunk_prefix", big ? k_inc_chunk_prefix<8> : k_inc_chunk_prefix<16>,
+                   dim3((a.ntiles + (big ? 8 : 16) - 1) / (big ? 8 : 16)), dim3(256), 0, st, a));
     PCG_TRY(launch("sort_inc_tiles", k_inc_tiles, dim3((a.ntiles + 1 + 2047) / 2048 * 8),
                    dim3(256), 0, st, a, tile_offsets));
     PCG_TRY(exclusive_scan(tile_offsets, (size_t)a.ntiles + 1, b.partial, Gate{b.flag, 0u}, st));

@@ -943,8 +943,8 @@ def bench_sweep_grad(args, torch, pcg):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
-              "supported (the multi-GPU split is a design note only)", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(splitting the grid over GPUs is described, not implemented)", file=sys.stderr)
         sys.exit(2)
     import torch
 

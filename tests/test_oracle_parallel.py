@@ -1,4 +1,4 @@
-"""The all-cores driver of the oracle (the benchmark's CPU baseline) gives the
+"""The all-cores runner of the oracle (the benchmark's CPU baseline) gives the
 single-threaded oracle's results: the same stable sort bit for bit, and the
 same sums up to fp64 rounding order."""
 import numpy as np

@@ -268,3 +268,25 @@ def test_tsc_tensor_mass_overwrite_and_add(orc, variant):
         torch.cuda.synchronize()
         got = M.cpu().numpy().astype(np.float64)
         _check(got if flags else got - init, ref)
+
+
+@pytest.mark.parametrize("tensor", [False, True])
+def test_tsc_mass_long_x_graded_weights(orc, tensor):
+    """41 nodes along x: 11 scalar bricks or 21 tensor ones per row, the last one
+    partial, and weights that grow along x by a factor of 100, so that
+    neighbouring bricks, which add to the same node pairs, sum in fixed point of
+    different units; the light end holds the tolerance against its own largest
+    value."""
+    wl = synthetic.mass_workload([41, 6, 5], 12, seed=98)
+    grow = 10.0 ** (2.0 * wl.x[0].astype(np.float64) / 41)
+    wl.w = (wl.w.astype(np.float64) * grow).astype(np.float32)
+    s, off = _grouped(orc, wl)
+    if tensor:
+        M = _run_tensor(wl.n, s, off, pcg.PCG_MASS_MFMA)
+        ref = orc.mass_matrix_tsc(wl.n, s.x, s.B, s.q, s.w, s.beta)
+    else:
+        M = _run(wl.n, s, off, pcg.PCG_MASS_MFMA)
+        ref = orc.mass_matrix_scalar_tsc(wl.n, s.x, s.q, s.w)
+    _check(M, ref)
+    lo = (slice(None), slice(None), slice(2, 8))  # node columns x = 2 .. 7
+    assert np.abs(M[lo] - ref[lo]).max() <= TOL * np.abs(ref[lo]).max()

@@ -290,3 +290,41 @@ def test_tsc_mass_long_x_graded_weights(orc, tensor):
     _check(M, ref)
     lo = (slice(None), slice(None), slice(2, 8))  # node columns x = 2 .. 7
     assert np.abs(M[lo] - ref[lo]).max() <= TOL * np.abs(ref[lo]).max()
+
+
+@pytest.mark.parametrize("tensor", [False, True])
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("case", ["empty", "all_tail"])
+def test_tsc_mass_empty_and_all_tail(orc, tensor, variant, case):
+    """No particles: M keeps its values when added to and is all zeros with
+    PCG_MASS_OVERWRITE.  A layout that covers none of the particles (every one
+    in the unsorted tail): the matrix still comes out whole."""
+    wl = synthetic.mass_workload([6, 5, 7], 10, seed=99)
+    s, off = _grouped(orc, wl)
+    n_part = 0
+    if case == "empty":
+        s = s.take(np.arange(0))
+        off = np.zeros_like(off)
+    shape = (7, 5, 6, 125, 3, 3) if tensor else (7, 5, 6, 125)
+    init = np.random.default_rng(100).standard_normal(shape).astype(np.float32)
+    groups = pcg.Layout(T=1, order=2, tile_offsets=dev(off.view(np.int32)), n_partitioned=n_part,
+                        drift=0)
+    if s.count:
+        ref = (orc.mass_matrix_tsc(wl.n, s.x, s.B, s.q, s.w, s.beta) if tensor
+               else orc.mass_matrix_scalar_tsc(wl.n, s.x, s.q, s.w))
+    for flags in (0, pcg.PCG_MASS_OVERWRITE):
+        M = torch.from_numpy(init.copy()).to(DEV)
+        say("mass tsc", case, "tensor" if tensor else "scalar", variant, flags)
+        if tensor:
+            pcg.assemble_mass_matrix_tsc(wl.n, [dev(a) for a in s.x], [dev(b) for b in s.B],
+                                         dev(s.beta), dev(s.q), dev(s.w), M, groups,
+                                         variant | flags)
+        else:
+            pcg.assemble_mass_matrix_scalar_tsc(wl.n, [dev(a) for a in s.x], dev(s.q), dev(s.w),
+                                                M, groups, variant | flags)
+        torch.cuda.synchronize()
+        got = M.cpu().numpy().astype(np.float64)
+        if not s.count:
+            assert np.array_equal(got, np.zeros_like(got) if flags else init)
+        else:
+            _check(got if flags else got - init, ref)

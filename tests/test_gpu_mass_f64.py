@@ -135,3 +135,32 @@ def test_f64_mass_overwrite(orc, scalar):
     M = _run(s, None, off, pcg.PCG_MASS_MFMA | pcg.PCG_MASS_OVERWRITE, scalar, M0=M0)
     ref = _ref(orc, wl.n, s, scalar)
     assert rel_frob_err(M, ref) <= TOL
+
+
+@pytest.mark.parametrize("scalar", [False, True])
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("case", ["empty", "all_tail"])
+def test_f64_mass_empty_and_all_tail(orc, scalar, variant, case):
+    """No particles: M keeps its values when added to and is all zeros with
+    PCG_MASS_OVERWRITE; a layout that covers none of the particles (all in the
+    unsorted tail) still gives the whole matrix, in fp64 on every path."""
+    wl = synthetic.mass_workload([7, 6, 5], 12, seed=120)
+    _, perm, off = orc.tile_sort(3, wl.n, 1, 1, wl.x)
+    s = wl.take(perm.astype(np.int64))
+    if case == "empty":
+        s = s.take(np.arange(0))
+        off = np.zeros_like(off)
+    size = 5 * 6 * 7 * 27 * (1 if scalar else 9)
+    M0 = np.random.default_rng(121).standard_normal(size)
+    for flags in (0, pcg.PCG_MASS_OVERWRITE):
+        M = _run(s, None, off, variant | flags, scalar, n_part=0, M0=M0)
+        init = M0.reshape(M.shape)
+        if not s.count:
+            assert np.array_equal(M, np.zeros_like(M) if flags else init)
+        else:
+            ref = _ref(orc, wl.n, s, scalar)
+            got = M if flags else M - init
+            assert rel_frob_err(got, ref) <= TOL
+            # adding to a non-zero M rounds against its values, not the matrix's
+            bound = TOL * (np.abs(ref).max() + (0 if flags else np.abs(init).max()))
+            assert np.abs(got - ref).max() <= bound

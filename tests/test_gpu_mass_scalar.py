@@ -137,3 +137,31 @@ def test_scalar_mass_overwrite(orc, variant):
                                     variant | pcg.PCG_MASS_OVERWRITE)
     torch.cuda.synchronize()
     _check(M.cpu().numpy(), orc.mass_matrix_scalar(wl.n, s.x, s.q, s.w))
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("case", ["empty", "all_tail"])
+def test_scalar_mass_empty_and_all_tail(orc, variant, case):
+    """No particles: M keeps its values when added to and is all zeros with
+    PCG_MASS_OVERWRITE; a layout that covers none of the particles (all in the
+    unsorted tail) still gives the whole matrix, on every path."""
+    wl = synthetic.mass_workload([7, 6, 5], 12, seed=122)
+    _, perm, off = orc.tile_sort(3, wl.n, 1, 1, wl.x)
+    s = wl.take(perm.astype(np.int64))
+    if case == "empty":
+        s = s.take(np.arange(0))
+        off = np.zeros_like(off)
+    init = np.random.default_rng(123).standard_normal((5, 6, 7, 27)).astype(np.float32)
+    cells = pcg.Layout(T=1, order=1, tile_offsets=dev(off.view(np.int32)), n_partitioned=0,
+                       drift=0)
+    for flags in (0, pcg.PCG_MASS_OVERWRITE):
+        M = torch.from_numpy(init.copy()).to(DEV)
+        say("mass scalar", case, variant, flags)
+        pcg.assemble_mass_matrix_scalar(wl.n, [dev(a) for a in s.x], dev(s.q), dev(s.w), M, cells,
+                                        variant | flags)
+        torch.cuda.synchronize()
+        got = M.cpu().numpy().astype(np.float64)
+        if not s.count:
+            assert np.array_equal(got, np.zeros_like(got) if flags else init)
+        else:
+            _check(got if flags else got - init, orc.mass_matrix_scalar(wl.n, s.x, s.q, s.w))

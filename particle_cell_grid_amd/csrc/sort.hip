@@ -24,7 +24,7 @@
 //   k_tile_keys; LSD radix sort of (key, index) in ceil(bits/8) passes of
 //   <= 8 bits (per-block digit histograms, a scan, a stable scatter ranking
 //   each wave's keys with ballot peer masks); k_tile_offsets from key
-//   transitions; k_permute gathers the SoA arrays.
+//   transitions; k_permute moves the SoA arrays to their slots.
 // Both paths are enqueued when `prev` is given; a device flag makes the kernels
 // of the path not taken return at once, so the call stays asynchronous.
 #include <algorithm>
@@ -50,10 +50,13 @@ template <int DIM, int ORDER>
 __global__ __launch_bounds__(256) void k_tile_keys(int64_t count, const float *__restrict__ x0,
                                                    const float *__restrict__ x1,
                                                    const float *__restrict__ x2, KeyGeom g,
-                                                   uint32_t *__restrict__ keys, Gate gate)
+                                                   uint32_t *__restrict__ keys,
+                                                   uint32_t *__restrict__ same, Gate gate)
 {
     if (gated_off(gate))
         return;
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        *same = 0u;  // counted by the first histogram pass
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
         const float *xs[3] = {x0, x1, x2};
@@ -73,12 +76,16 @@ template <int BITS>
 __global__ __launch_bounds__(SORT_BLOCK) void k_radix_hist(const uint32_t *__restrict__ keys,
                                                            int64_t count, int shift,
                                                            uint32_t *__restrict__ counts,
-                                                           uint32_t nblocks, Gate gate)
+                                                           uint32_t nblocks,
+                                                           uint32_t *__restrict__ same, Gate gate)
 {
     if (gated_off(gate))
         return;
     constexpr uint32_t R = 1u << BITS;
     __shared__ uint32_t hist[R];
+    // same (first pass only): particles whose key equals that of the particle
+    // before them in the input (within a wave), the input's measure of order
+    uint32_t eq = 0;
     // the launch may have fewer work-groups than key blocks: each takes every
     // gridDim.x-th block (a small grid keeps a gated-off launch cheap)
     for (uint32_t vb = blockIdx.x; vb < nblocks; vb += gridDim.x) {
@@ -90,7 +97,13 @@ __global__ __launch_bounds__(SORT_BLOCK) void k_radix_hist(const uint32_t *__res
         for (int j = 0; j < SORT_IPT; ++j) {
             const int64_t idx = base + (int64_t)j * SORT_BLOCK + threadIdx.x;
             const bool valid = idx < count;
-            const uint32_t digit = valid ? (keys[idx] >> shift) & (R - 1) : 0u;
+            const uint32_t key = valid ? keys[idx] : 0u;
+            const uint32_t digit = (key >> shift) & (R - 1);
+            if (same) {
+                const uint32_t before = __shfl_up(key, 1, WAVE);
+                const bool vb = __shfl_up((int)valid, 1, WAVE) != 0;
+                eq += (lane_id() > 0 && valid && vb && before == key) ? 1u : 0u;
+            }
             const uint64_t peers = peer_mask<BITS>(digit, valid);
             // the lowest lane of each peer group adds the group's size
             if (valid && (peers & lanemask_lt()) == 0)
@@ -101,16 +114,35 @@ __global__ __launch_bounds__(SORT_BLOCK) void k_radix_hist(const uint32_t *__res
             counts[(size_t)d * nblocks + vb] = hist[d];
         __syncthreads();  // hist is cleared for the next block
     }
+    if (same) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1)
+            eq += (uint32_t)__shfl_xor((int)eq, o, WAVE);
+        if (lane_id() == 0 && eq)
+            atomicAdd(same, eq);
+    }
+}
+
+// The arrays are moved by scatter (out[rank[i]] = in[i]) when at least half
+// of the input's neighbours share a key (a re-sort of nearly ordered
+// particles: reads and most writes consecutive), else by gather (out[i] =
+// in[perm[i]]: an unordered input would scatter its writes over whole lines).
+__device__ inline bool permute_by_scatter(const uint32_t *same, int64_t count)
+{
+    return 2 * (int64_t)*same >= count;
 }
 
 template <int BITS>
 __global__ __launch_bounds__(SORT_BLOCK) void k_radix_scatter(
     const uint32_t *__restrict__ keys_in, const uint32_t *__restrict__ vals_in,
     uint32_t *__restrict__ keys_out, uint32_t *__restrict__ vals_out, int64_t count, int shift,
-    const uint32_t *__restrict__ offsets, uint32_t nblocks, Gate gate)
+    const uint32_t *__restrict__ offsets, uint32_t nblocks, uint32_t *__restrict__ rank_out,
+    const uint32_t *__restrict__ same, Gate gate)
 {
     if (gated_off(gate))
         return;
+    if (rank_out && !permute_by_scatter(same, count))
+        rank_out = nullptr;
     constexpr uint32_t R = 1u << BITS;
     __shared__ uint16_t cnt[SORT_SLOTS][R];  // items of digit d in wave-slot s, then prefix
     __shared__ uint32_t gbase[R];
@@ -164,6 +196,9 @@ __global__ __launch_bounds__(SORT_BLOCK) void k_radix_scatter(
             if (dst < (uint64_t)count) {  // always true for a consistent histogram
                 keys_out[dst] = key[j];
                 vals_out[dst] = val[j];
+                // the last pass: where each input element goes
+                if (rank_out && val[j] < (uint64_t)count)
+                    rank_out[val[j]] = dst;
             }
         }
     }
@@ -360,32 +395,46 @@ __global__ __launch_bounds__(256) void k_tile_offsets(const uint32_t *__restrict
     }
 }
 
-constexpr int PERM_EPT = 4;  // elements per thread: all index loads, then all gathers
+constexpr int PERM_EPT = 4;  // elements per thread: all rank loads, then the arrays
 
+// The sort's permutation applied to the SoA arrays, in one of two forms
+// chosen on the device (permute_by_scatter): out[k][rank[i]] = in[k][i], each
+// array read in order, rank the inverse permutation from the last radix pass;
+// or out[k][i] = in[k][perm[i]].  Where most particles keep their order (a
+// re-sort), the first reads and writes consecutive words but for the few
+// movers, while a gather would read every particle that changed tile from its
+// old tile's range; for an unordered input the gather's scattered reads cost
+// less than scattered writes.
 __global__ __launch_bounds__(256) void k_permute(PermArgs a, const uint32_t *__restrict__ perm,
-                                                 int64_t count, Gate gate)
+                                                 const uint32_t *__restrict__ rank,
+                                                 const uint32_t *__restrict__ same, int64_t count,
+                                                 Gate gate)
 {
     if (gated_off(gate))
         return;
+    const bool scatter = permute_by_scatter(same, count);
+    const uint32_t *__restrict__ idx = scatter ? rank : perm;
     for (int64_t blk = blockIdx.x; blk * 256 * PERM_EPT < count; blk += gridDim.x) {
     const int64_t i0 = (blk * PERM_EPT) * 256 + threadIdx.x;
-    uint32_t p[PERM_EPT];
+    uint32_t r[PERM_EPT];
 #pragma unroll
     for (int e = 0; e < PERM_EPT; ++e) {
         const int64_t i = i0 + e * 256;
-        // perm is a permutation of [0, count); the clamp only keeps a broken one in bounds
-        p[e] = i < count ? min(perm[i], (uint32_t)(count - 1)) : 0u;
+        // a permutation of [0, count); the clamp only keeps a broken one in bounds
+        r[e] = i < count ? min(idx[i], (uint32_t)(count - 1)) : 0u;
     }
     for (int k = 0; k < a.n; ++k) {
         float v[PERM_EPT];
 #pragma unroll
-        for (int e = 0; e < PERM_EPT; ++e)
-            v[e] = a.in[k][p[e]];
+        for (int e = 0; e < PERM_EPT; ++e) {
+            const int64_t i = i0 + e * 256;
+            v[e] = i < count ? a.in[k][scatter ? i : r[e]] : 0.0f;
+        }
 #pragma unroll
         for (int e = 0; e < PERM_EPT; ++e) {
             const int64_t i = i0 + e * 256;
             if (i < count)
-                a.out[k][i] = v[e];
+                a.out[k][scatter ? r[e] : i] = v[e];
         }
     }
     }
@@ -900,6 +949,7 @@ SortPlan make_plan(const pcg_grid *grid, int64_t count, int T)
 struct SortBuffers {
     uint32_t *k0, *ak, *av, *bv, *fk, *pm, *counts, *partial;
     uint32_t *flag, *cum, *cnt, *tcnt, *tpre, *cpart;
+    uint32_t *same;  // general path: neighbouring particles with equal keys
     ChunkEntry *cmap;
 };
 
@@ -917,6 +967,7 @@ size_t carve(const SortPlan &p, void *ws, SortBuffers *b)
     const size_t scan_len = std::max(p.counts_len, (size_t)p.ntiles + 1);
     b->partial = c.take<uint32_t>((scan_len + SCAN_TILE - 1) / SCAN_TILE + 1);
     b->flag = c.take<uint32_t>(1);
+    b->same = c.take<uint32_t>(1);
     b->cum = c.take<uint32_t>((size_t)p.ntiles + 1);
     b->cnt = c.take<uint32_t>((size_t)p.nchunks_max * NDIR);
     b->tcnt = c.take<uint32_t>((size_t)p.ntiles * NDIR);
@@ -942,44 +993,44 @@ pcg_status check_sort_args(const pcg_grid *grid, int64_t count, int T, const cha
 
 template <int BITS>
 pcg_status radix_pass(const SortPlan &p, int shift, const uint32_t *kin, const uint32_t *vin,
-                      uint32_t *kout, uint32_t *vout, const SortBuffers &b, Gate gate,
-                      hipStream_t st)
+                      uint32_t *kout, uint32_t *vout, uint32_t *rank, const SortBuffers &b,
+                      Gate gate, hipStream_t st)
 {
     PCG_TRY(launch("sort_hist", k_radix_hist<BITS>, dim3(general_grid(p.nblocks, gate)),
                    dim3(SORT_BLOCK), 0, st,
-                   kin, p.count, shift, b.counts, p.nblocks, gate));
+                   kin, p.count, shift, b.counts, p.nblocks, shift == 0 ? b.same : nullptr, gate));
     PCG_TRY(exclusive_scan(b.counts, p.counts_len, b.partial, gate, st));
     PCG_TRY(launch("sort_scatter", k_radix_scatter<BITS>, dim3(general_grid(p.nblocks, gate)),
                    dim3(SORT_BLOCK), 0,
                    st, kin, vin, kout, vout, p.count, shift, (const uint32_t *)b.counts,
-                   p.nblocks, gate));
+                   p.nblocks, rank, (const uint32_t *)b.same, gate));
     return PCG_OK;
 }
 
 pcg_status radix_pass_dispatch(int bits, const SortPlan &p, int shift, const uint32_t *kin,
                                const uint32_t *vin, uint32_t *kout, uint32_t *vout,
-                               const SortBuffers &b, Gate gate, hipStream_t st)
+                               uint32_t *rank, const SortBuffers &b, Gate gate, hipStream_t st)
 {
     switch (bits) {
-    case 1: return radix_pass<1>(p, shift, kin, vin, kout, vout, b, gate, st);
-    case 2: return radix_pass<2>(p, shift, kin, vin, kout, vout, b, gate, st);
-    case 3: return radix_pass<3>(p, shift, kin, vin, kout, vout, b, gate, st);
-    case 4: return radix_pass<4>(p, shift, kin, vin, kout, vout, b, gate, st);
-    case 5: return radix_pass<5>(p, shift, kin, vin, kout, vout, b, gate, st);
-    case 6: return radix_pass<6>(p, shift, kin, vin, kout, vout, b, gate, st);
-    case 7: return radix_pass<7>(p, shift, kin, vin, kout, vout, b, gate, st);
-    case 8: return radix_pass<8>(p, shift, kin, vin, kout, vout, b, gate, st);
+    case 1: return radix_pass<1>(p, shift, kin, vin, kout, vout, rank, b, gate, st);
+    case 2: return radix_pass<2>(p, shift, kin, vin, kout, vout, rank, b, gate, st);
+    case 3: return radix_pass<3>(p, shift, kin, vin, kout, vout, rank, b, gate, st);
+    case 4: return radix_pass<4>(p, shift, kin, vin, kout, vout, rank, b, gate, st);
+    case 5: return radix_pass<5>(p, shift, kin, vin, kout, vout, rank, b, gate, st);
+    case 6: return radix_pass<6>(p, shift, kin, vin, kout, vout, rank, b, gate, st);
+    case 7: return radix_pass<7>(p, shift, kin, vin, kout, vout, rank, b, gate, st);
+    case 8: return radix_pass<8>(p, shift, kin, vin, kout, vout, rank, b, gate, st);
     default: return fail(PCG_EUNSUPPORTED, "radix pass of %d bits", bits);
     }
 }
 
 template <int DIM, int ORDER>
 pcg_status launch_keys(int64_t count, const float *const x[3], const KeyGeom &g, uint32_t *keys,
-                       Gate gate, hipStream_t st)
+                       uint32_t *same, Gate gate, hipStream_t st)
 {
     return launch("sort_keys", k_tile_keys<DIM, ORDER>, dim3(general_grid((count + 255) / 256, gate)),
                   dim3(256), 0, st, count, x[0], DIM > 1 ? x[1] : nullptr,
-                  DIM > 2 ? x[2] : nullptr, g, keys, gate);
+                  DIM > 2 ? x[2] : nullptr, g, keys, same, gate);
 }
 
 pcg_status general_path(const pcg_grid *grid, int order, const SortPlan &p, const KeyGeom &g,
@@ -991,12 +1042,12 @@ pcg_status general_path(const pcg_grid *grid, int order, const SortPlan &p, cons
     const int key = grid->dim * 10 + order;
     pcg_status s = PCG_OK;
     switch (key) {
-    case 11: s = launch_keys<1, 1>(count, key_x, g, b.k0, gate, st); break;
-    case 12: s = launch_keys<1, 2>(count, key_x, g, b.k0, gate, st); break;
-    case 21: s = launch_keys<2, 1>(count, key_x, g, b.k0, gate, st); break;
-    case 22: s = launch_keys<2, 2>(count, key_x, g, b.k0, gate, st); break;
-    case 31: s = launch_keys<3, 1>(count, key_x, g, b.k0, gate, st); break;
-    case 32: s = launch_keys<3, 2>(count, key_x, g, b.k0, gate, st); break;
+    case 11: s = launch_keys<1, 1>(count, key_x, g, b.k0, b.same, gate, st); break;
+    case 12: s = launch_keys<1, 2>(count, key_x, g, b.k0, b.same, gate, st); break;
+    case 21: s = launch_keys<2, 1>(count, key_x, g, b.k0, b.same, gate, st); break;
+    case 22: s = launch_keys<2, 2>(count, key_x, g, b.k0, b.same, gate, st); break;
+    case 31: s = launch_keys<3, 1>(count, key_x, g, b.k0, b.same, gate, st); break;
+    case 32: s = launch_keys<3, 2>(count, key_x, g, b.k0, b.same, gate, st); break;
     }
     PCG_TRY(s);
     uint32_t *final_keys = sorted_keys ? sorted_keys : b.fk;
@@ -1004,11 +1055,16 @@ pcg_status general_path(const pcg_grid *grid, int order, const SortPlan &p, cons
         perm = b.pm;  // the last radix pass needs somewhere to put the permutation
     const uint32_t *kin = b.k0;
     const uint32_t *vin = nullptr;  // pass 0 ranks input indices
+    // the inverse permutation, written by the last pass (where the arrays will
+    // be moved by scatter) into the value buffer that pass does not read (b.bv
+    // after an even number of passes, else b.av)
+    uint32_t *rank = arr.n > 0 ? (p.passes % 2 == 0 ? b.bv : b.av) : nullptr;
     for (int pass = 0; pass < p.passes; ++pass) {
         const bool last = pass == p.passes - 1;
         uint32_t *kout = last ? final_keys : (pass % 2 == 0 ? b.ak : b.k0);
         uint32_t *vout = last ? perm : (pass % 2 == 0 ? b.av : b.bv);
-        PCG_TRY(radix_pass_dispatch(p.bits, p, pass * p.bits, kin, vin, kout, vout, b, gate, st));
+        PCG_TRY(radix_pass_dispatch(p.bits, p, pass * p.bits, kin, vin, kout, vout,
+                                    last ? rank : nullptr, b, gate, st));
         kin = kout;
         vin = vout;
     }
@@ -1018,8 +1074,8 @@ pcg_status general_path(const pcg_grid *grid, int order, const SortPlan &p, cons
     if (arr.n > 0) {
         const int64_t blocks = (count + 256 * PERM_EPT - 1) / (256 * PERM_EPT);
         PCG_TRY(launch("sort_permute", k_permute, dim3(general_grid(blocks, gate)), dim3(256), 0,
-                       st, arr,
-                       (const uint32_t *)perm, count, gate));
+                       st, arr, (const uint32_t *)perm, (const uint32_t *)rank,
+                       (const uint32_t *)b.same, count, gate));
     }
     return PCG_OK;
 }

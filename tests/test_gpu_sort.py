@@ -72,6 +72,22 @@ def test_sort_nearly_sorted_steady_state(orc):
     _check_sort(orc, 3, wl.n, 1, 8, s.x_next, s.x_next + s.v + [s.q, s.w])
 
 
+@pytest.mark.parametrize("ordered", [0.0, 0.4, 0.6, 1.0])
+def test_sort_moves_arrays_by_gather_or_scatter(orc, ordered):
+    """The arrays are moved by gather for an unordered input and by scatter
+    through the inverse permutation where at least half of the neighbouring
+    particles share a tile: inputs whose leading fraction `ordered` is in tile
+    order (the rest shuffled) fall on both sides of that choice, and every
+    array must come out exactly as the oracle's stable sort puts it."""
+    wl = synthetic.deposit_workload(3, [32, 32, 32], ppc=4, seed=131)
+    _, p, _ = orc.tile_sort(3, wl.n, 1, 8, wl.x)
+    order = p.astype(np.int64)
+    cut = int(ordered * order.size)
+    order[cut:] = np.random.default_rng(132).permutation(order[cut:])
+    s = wl.take(order)
+    _check_sort(orc, 3, wl.n, 1, 8, s.x, s.x + s.v + [s.q, s.w])
+
+
 def test_sort_deterministic_repeat(orc):
     wl = synthetic.deposit_workload(3, [32, 32, 32], ppc=4, seed=77)
     x = [dev(a) for a in wl.x]

@@ -24,7 +24,10 @@
 //   k_tile_keys; LSD radix sort of (key, index) in ceil(bits/8) passes of
 //   <= 8 bits (per-block digit histograms, a scan, a stable scatter ranking
 //   each wave's keys with ballot peer masks); k_tile_offsets from key
-//   transitions; k_permute moves the SoA arrays to their slots.
+//   transitions; k_permute moves the SoA arrays to their slots, by gather
+//   through the permutation, or (an input mostly in tile order, as counted by
+//   the first histogram pass) by scatter through its inverse, which the last
+//   scatter pass writes.
 // Both paths are enqueued when `prev` is given; a device flag makes the kernels
 // of the path not taken return at once, so the call stays asynchronous.
 #include <algorithm>
